@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""E8 encode+decode throughput of the HyperQuant hot path on one MI355X.
+
+Workload: the Llama-3.1-8B-shaped 32-layer stack (per layer q/o 4096x4096,
+k/v 1024x4096, gate/up 14336x4096, down 4096x14336; 6.98e9 bf16 weights,
+13.96 GB), entries N(0, 0.02^2) with 0.1% of input columns replaced by
+10 * Student-t(4) outliers, drawn on the GPU (seed per layer).  One step
+streams the whole stack: for each layer, encode its seven matrices (E8,
+4 bps, tile 256, auto scale, RHT seed = layer index), then decode them to
+bf16.  Inputs and output buffers are resident in HBM before timing starts.
+
+Prints one JSON line.  value = bf16 GB/s in = 2 * weights / step time.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+# Algorithmic bytes per 256-weight E8 tile (bf16 in / int8 idx / one coset
+# word / uint8 k / uint32 bits / fp32 scale).
+ENC_BYTES_PER_TILE = 512 + 256 + 4 + 1 + 4 + 4
+DEC_BYTES_PER_TILE = 256 + 4 + 4 + 512
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--bps", type=float, default=4.0)
+    ap.add_argument("--cpu-baseline", type=int, default=1,
+                    help="time the oracle on a sample of the workload (rank 0, N=1)")
+    ap.add_argument("--cpu-sample-stride", type=int, default=8,
+                    help="oracle sample: every k-th tile of layer 0")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------ CPU baseline
+
+def _oracle_chunk(args):
+    tiles, seed, bps = args
+    from threadpoolctl import threadpool_limits
+    from oracle import codec
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        e = codec.encode(tiles, "E8", 256, bps, rht_seed=seed)
+        codec.decode(e["idx"], e["coset"], e["scale"], "E8", 256, seed)
+        return time.perf_counter() - t0
+
+
+def cpu_baseline(stride, bps):
+    """The oracle (fp64 NumPy, unmodified) on every stride-th tile of a
+    host-drawn layer of the same shapes and distribution, spread over the
+    host's cores (one single-threaded process each)."""
+    import multiprocessing as mp
+
+    import numpy as np
+
+    import workloads
+    chunks = []
+    n_w = 0
+    for m in range(7):
+        bits = workloads.llama_matrix(m, layer=0)
+        t = workloads.bf16_bits_to_f64(bits.reshape(-1, 256)[::stride])
+        n_w += t.size
+        chunks.extend(np.array_split(t, max(1, len(t) // 2048)))
+    procs = min(os.cpu_count() or 1, 16)
+    ctx = mp.get_context("fork")
+    with ctx.Pool(procs) as pool:
+        t0 = time.perf_counter()
+        pool.map(_oracle_chunk, [(c, 0, bps) for c in chunks], chunksize=1)
+        wall = time.perf_counter() - t0
+    return {
+        "value": round(2.0 * n_w / wall / 1e9, 6),
+        "unit": "GB/s (bf16 in)",
+        "cores": procs,
+        "kind": "oracle",
+        "sample": "every %dth 256-weight tile of one host-drawn layer of the same "
+                  "shapes and distribution (%d weights), E8 4 bps encode + decode, "
+                  "%d single-threaded processes, %.1f s wall" % (stride, n_w, procs, wall),
+    }
+
+
+# ------------------------------------------------------------------- GPU
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(tiles are independent; see DESIGN.md for how it would shard)", file=sys.stderr)
+        sys.exit(2)
+
+    cpu = cpu_baseline(args.cpu_sample_stride, args.bps) if args.cpu_baseline else None
+
+    import torch
+
+    import workloads
+    from lattice_post_quantization_amd import hq
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    mats = []
+    for layer in range(args.layers):
+        row = []
+        for m, (name, rows, cols) in enumerate(workloads.LLAMA_LAYER):
+            x = workloads.llama_stack_torch(layer, m, dev)
+            nt = rows * cols // 256
+            enc = {
+                "scale": torch.empty(nt, dtype=torch.float32, device=dev),
+                "idx": torch.empty((rows, cols), dtype=torch.int8, device=dev),
+                "coset": torch.empty((nt, 1), dtype=torch.int32, device=dev),
+                "rice_k": torch.empty(nt, dtype=torch.uint8, device=dev),
+                "tile_bits": torch.empty(nt, dtype=torch.int32, device=dev),
+            }
+            y = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+            row.append((x, enc, y, nt))
+        mats.append(row)
+    torch.cuda.synchronize()
+    n_weights = sum(x.numel() for row in mats for (x, _, _, _) in row)
+    n_tiles = n_weights // 256
+
+    def step(ev=None):
+        for layer, row in enumerate(mats):
+            for i, (x, enc, y, nt) in enumerate(row):
+                if ev is not None:
+                    ev["enc"].append(torch.cuda.Event(enable_timing=True))
+                    ev["enc"][-1].record()
+                hq.hq_encode_tiles(x, "E8", 256, args.bps, layer, out=enc)
+                if ev is not None:
+                    ev["enc"].append(torch.cuda.Event(enable_timing=True))
+                    ev["enc"][-1].record()
+                    ev["enc_tiles"].append(nt)
+            for i, (x, enc, y, nt) in enumerate(row):
+                if ev is not None:
+                    ev["dec"].append(torch.cuda.Event(enable_timing=True))
+                    ev["dec"][-1].record()
+                hq.hq_decode_tiles(enc["idx"], enc["coset"], enc["scale"], "E8", 256, layer,
+                                   torch.bfloat16, out=y)
+                if ev is not None:
+                    ev["dec"].append(torch.cuda.Event(enable_timing=True))
+                    ev["dec"][-1].record()
+                    ev["dec_tiles"].append(nt)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: whole steps, bracketed by synchronisation
+    ev = {"enc": [], "dec": [], "enc_tiles": [], "dec_tiles": []}
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record()
+    for _ in range(args.steps):
+        step(ev)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    gpu_ms = t_start.elapsed_time(t_end)
+    ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
+
+    def kernel_stats(name, tiles_key, bytes_per_tile):
+        evs = ev[name]
+        durs = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(len(evs) // 2)]
+        tiles = ev[tiles_key]
+        tot_ms = sum(durs)
+        tot_bytes = sum(t * bytes_per_tile for t in tiles)
+        return {"launches": len(durs), "avg_us": 1e3 * tot_ms / len(durs),
+                "sum_ms_per_step": tot_ms / args.steps,
+                "gbs": tot_bytes / (tot_ms * 1e-3) / 1e9}
+
+    enc = kernel_stats("enc", "enc_tiles", ENC_BYTES_PER_TILE)
+    dec = kernel_stats("dec", "dec_tiles", DEC_BYTES_PER_TILE)
+    dominant = enc if enc["sum_ms_per_step"] >= dec["sum_ms_per_step"] else dec
+    dom_name = "encode" if dominant is enc else "decode"
+
+    value = 2.0 * n_weights / (ms_per_step * 1e-3) / 1e9
+    alg = (ENC_BYTES_PER_TILE + DEC_BYTES_PER_TILE) * n_tiles / (ms_per_step * 1e-3) / 1e9
+    out = {
+        "metric": "E8 encode+decode throughput, bf16 GB/s in and % of HBM peak (1 GPU)",
+        "value": round(value, 3),
+        "unit": "GB/s (bf16 in)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {
+            "workload": "llama3.1-8b-shaped 32-layer weight stack streamed through encode "
+                        "then decode (E8, tile 256, auto scale)",
+            "layers": args.layers, "weights": n_weights, "bps": args.bps, "tile": 256,
+            "lattice": "E8", "input": "bf16", "output": "bf16",
+        },
+        "pct_hbm_peak_algorithmic": round(100.0 * alg / HBM_PEAK_GBS, 3),
+        "algorithmic_gbs": round(alg, 2),
+        "roofline": {
+            "kernel": dom_name,
+            "bound": "hbm",
+            "achieved": round(dominant["gbs"], 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dominant["gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "kernels": {
+            "encode": {k: round(v, 3) for k, v in enc.items()},
+            "decode": {k: round(v, 3) for k, v in dec.items()},
+        },
+        "host_wall_ms_per_step": round(wall * 1e3 / args.steps, 3),
+        "gpu_event_ms_per_step": round(gpu_ms / args.steps, 3),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,219 @@
+/*
+ * hq.h - C ABI of the HyperQuant hot path on MI355X (gfx950).
+ *
+ * The method (sources are web pages, cited by title):
+ *   [arXiv abstract]  "HyperQuant: A Rate-Distortion-Optimal Quantization
+ *       Pipeline for Large Language and Diffusion Models", arXiv abstract as
+ *       shown on mlsanity.com (paper 2606.23406), enumerated ideas (i)-(iv).
+ *   [ICLR abstract]   "HyperQuant: A Near-Entropy-Optimal Lattice Quantization
+ *       Pipeline for Large Language and Diffusion Models", abstract on
+ *       acceptodds.com (iclr2027-3515).
+ *   [issue]           GitHub issue "HyperQuant: A Rate-Distortion-Optimal
+ *       Quantization Pipeline ... #9", section "Additional context".
+ *
+ * Pipeline per tile of n consecutive elements: random signs, Walsh-Hadamard
+ * rotation, per-tile scale, nearest point of the E8 / D4 / A2 / Z lattice,
+ * lossless strip of the membership-fixed bits, Rice rate; decode inverts it
+ * algebraically; the KV path adds a subtractive dither.
+ *
+ * Conventions for every entry point
+ *   - All array arguments are caller-allocated DEVICE pointers (hipMalloc or
+ *     equivalent) on the current HIP device; `p` is host memory read during
+ *     the call only.  The library allocates nothing on any path.
+ *   - Calls enqueue kernels on `stream` and return without synchronising.
+ *     The return code reports argument validation (HQ_EINVAL,
+ *     HQ_EUNSUPPORTED), the auto-scale index range bound (HQ_ERANGE) and
+ *     launch failure (HQ_EDEVICE).  Validation happens before any device
+ *     call; on a nonzero return nothing was enqueued.
+ *   - Data-dependent faults (non-finite input, an index outside int8 with an
+ *     explicit scale, a packed stream larger than its capacity) are OR-ed
+ *     into the optional device word `*status` (HQ_ST_* bits); the caller
+ *     reads it after synchronising.  Outputs of an affected tile are
+ *     unspecified.  `status` may be NULL.
+ *   - A call with zero tiles is a no-op returning HQ_OK.
+ *   - Stateless and reentrant.  Results are bitwise deterministic and, on
+ *     inputs whose Hadamard partial sums are exact in fp64 (every bf16 tile
+ *     whose magnitudes span less than 2^37), bit-identical to the fp64
+ *     definition below, ties included.
+ *
+ * Data layout
+ *   A matrix is row-major and contiguous; tile t is flat elements
+ *   [n t, n t + n), so cols must be a multiple of n.  idx holds one int8 per
+ *   element in the same order; coset holds hq_coset_words(p) uint32 words per
+ *   tile; scale, rice_k and tile_bits hold one entry per tile.
+ */
+#ifndef HQ_H
+#define HQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t hq_status;
+enum {
+  HQ_OK = 0,
+  HQ_EINVAL = -1,       /* bad argument (null pointer, size, tile, dtype)  */
+  HQ_ERANGE = -2,       /* auto scale cannot keep indices inside int8      */
+  HQ_EDEVICE = -3,      /* a HIP call or kernel launch failed              */
+  HQ_EUNSUPPORTED = -4  /* a valid combination this build does not offer   */
+};
+
+/* Lattice; the value is the lattice dimension. [arXiv abstract] item (ii). */
+typedef enum { HQ_Z = 1, HQ_A2 = 2, HQ_D4 = 4, HQ_E8 = 8 } hq_lattice;
+
+/* Element type of weight / KV / decoded arrays. */
+typedef enum { HQ_F32 = 0, HQ_BF16 = 1 } hq_dtype;
+
+/* hq_params.flags */
+enum {
+  HQ_SCALE_AUTO = 1u,   /* encode computes the scales (else reads them)    */
+  HQ_DITHER = 2u,       /* subtractive dither (E8 only; KV encode/decode)  */
+  HQ_WANT_COORDS = 4u   /* encode also writes full lattice coordinates     */
+};
+
+/* Device status bits (OR-ed into *status by kernels). */
+enum {
+  HQ_ST_NONFINITE = 1u,   /* NaN or Inf in the input of a tile            */
+  HQ_ST_OVERFLOW = 2u,    /* a stripped index left int8 (explicit scale)  */
+  HQ_ST_STREAM_FULL = 4u  /* hq_rate: packed stream exceeded capacity     */
+};
+
+typedef struct {
+  uint32_t struct_size;   /* must equal sizeof(hq_params)                   */
+  int32_t lattice;        /* hq_lattice                                     */
+  int32_t tile;           /* n: 256 (E8) or 128 (E8, D4, A2, Z)             */
+  float bps;              /* target rate R in bits per scalar, 0 < R <= 8   */
+  uint32_t rht_seed;      /* seed of the RHT sign vector                    */
+  uint32_t dither_seed;   /* HQ_DITHER only; must be < 2^24                 */
+  int64_t dither_base;    /* HQ_DITHER only: global index of vector 0       */
+  uint32_t flags;         /* HQ_SCALE_AUTO | HQ_DITHER | HQ_WANT_COORDS     */
+  uint32_t reserved;      /* must be 0                                      */
+} hq_params;
+
+/*
+ * hq_encode_tiles - forward pipeline on a row-major matrix.
+ *
+ * Passages: [arXiv abstract] items (i)-(iii); [ICLR abstract] (rotation,
+ * lattice, lossless strip, Rice).  Per tile t:
+ *   s      = sign vector: s_j = -1 iff bit 63 of SplitMix64(((seed) << 32) ^ j)
+ *   S      = H_n (s * x_t)                      (Sylvester Hadamard, exact)
+ *   Delta  = scale[t], or with HQ_SCALE_AUTO
+ *            bf16_rne(sqrt(sum x^2 / n) * sqrt(2 pi e) 2^-R / vol^(1/d)),
+ *            1 when that rounds to 0
+ *   u      = rne(S * (2^24 / (sqrt(n) * Delta))) * 2^-24    (quantizer input)
+ *   p      = nearest lattice point per block (ties: see the oracle's rules)
+ *   idx    = stripped integers: E8 (z0..z6, floor(z7/2)) with z = p - c/2,
+ *            D4 (z0, z1, z2, floor(z3/2)), A2 (a, b), Z (z)
+ *   coset  = one bit per E8 block / A2 pair, block j at bit j (LSB first)
+ *   rice_k = argmin_k sum(floor(zeta/2^k) + 1 + k), zeta = zigzag(idx)
+ *   tile_bits = 4 + coset bits + that minimum
+ *
+ * x       [rows*cols] of x_dtype (bf16 or fp32)
+ * scale   [n_tiles] fp32: output with HQ_SCALE_AUTO, input otherwise
+ * idx     [rows*cols] int8
+ * coset   [n_tiles * hq_coset_words(p)] uint32; may be NULL iff that is 0
+ * rice_k  [n_tiles] uint8,  tile_bits [n_tiles] uint32
+ * coords  [rows*cols] int16 iff HQ_WANT_COORDS (E8: 2p; A2: 2 * (a + c/2,
+ *         b + c/2); D4, Z: p), else ignored and may be NULL
+ * Errors: HQ_EINVAL (null pointer, rows or cols <= 0, cols % tile != 0,
+ * bad tile/lattice/dtype/bps/flags), HQ_ERANGE (auto scale with
+ * sqrt(n)/c(L,R) + 2 > 127), HQ_EUNSUPPORTED (HQ_DITHER here: use
+ * hq_kv_encode), HQ_EDEVICE.
+ */
+hq_status hq_encode_tiles(const hq_params* p, const void* x, int32_t x_dtype,
+                          int64_t rows, int64_t cols, float* scale, int8_t* idx,
+                          uint32_t* coset, uint8_t* rice_k, uint32_t* tile_bits,
+                          int16_t* coords, uint32_t* status, hipStream_t stream);
+
+/*
+ * hq_decode_tiles - inverse pipeline ([ICLR abstract]: decoding is
+ * algebraic, no codebook).  Per tile: unstrip (E8: z7 = 2 t7 + (z0+..+z6 mod
+ * 2)), point p, yhat = Delta p (HQ_DITHER: Delta (p - d) with the same
+ * dither_seed and dither_base as the encode), x = s * ((H_n yhat) / sqrt(n)),
+ * rounded to y_dtype (fp32: nearest; bf16: nearest even).
+ *
+ * idx [rows*cols] int8, coset as for encode, scale [n_tiles] fp32,
+ * y [rows*cols] of y_dtype.  Errors as for encode; HQ_DITHER requires E8.
+ */
+hq_status hq_decode_tiles(const hq_params* p, const int8_t* idx,
+                          const uint32_t* coset, const float* scale,
+                          int64_t rows, int64_t cols, void* y, int32_t y_dtype,
+                          uint32_t* status, hipStream_t stream);
+
+/*
+ * hq_rate - Rice rate and optional packing of stripped indices.
+ *
+ * Passages: [arXiv abstract] item (iii), [ICLR abstract] (Rice code; one
+ * itemized rate accounting), [issue] (packed Rice-coded index format).
+ * Per tile: rice_k and tile_bits as in hq_encode_tiles; *total_bits = sum of
+ * tile_bits (written, not accumulated).  If stream_words is not NULL the
+ * tiles are also packed: per tile, k (4 bits), the coset bits, then each code
+ * (floor(zeta/2^k) one-bits, a zero bit, the k low bits of zeta, LSB first);
+ * stream bit j is bit (j mod 32) of word j/32; each tile starts on a word
+ * boundary, zero padded; tile_word_offset[t] = sum over earlier tiles of
+ * ceil(tile_bits/32), tile_word_offset[n_tiles] = total words.  A tile that
+ * does not fit in capacity_words is not written and sets HQ_ST_STREAM_FULL.
+ *
+ * idx [n_tiles * tile] int8; coset as for encode (used only when packing);
+ * rice_k [n_tiles] uint8, tile_bits [n_tiles] uint32, total_bits: 1 uint64;
+ * tile_word_offset [n_tiles + 1] uint64 (required when packing);
+ * workspace: device scratch of at least hq_rate_workspace_bytes(n_tiles)
+ * bytes (required when packing, else may be NULL).
+ */
+hq_status hq_rate(const hq_params* p, const int8_t* idx, const uint32_t* coset,
+                  int64_t n_tiles, uint8_t* rice_k, uint32_t* tile_bits,
+                  uint64_t* total_bits, uint32_t* stream_words,
+                  uint64_t capacity_words, uint64_t* tile_word_offset,
+                  void* workspace, size_t workspace_bytes, uint32_t* status,
+                  hipStream_t stream);
+
+/*
+ * hq_kv_encode - encode KV-cache vectors ([ICLR abstract]: subtractive
+ * dither keeps each cached inner product unbiased per vector; [arXiv
+ * abstract] item (iv)).  The vectors are tiles of n = p->tile = head_dim
+ * (128 or 256), lattice E8.  With HQ_DITHER, vector v (global index
+ * dither_base + v) gets the dither d = w - Q_E8(w), w_i = 2^-23 *
+ * (SplitMix64((seed << 40) ^ ((v << 8) | i)) >> 40) - 1, and is encoded as
+ * Q_E8(u + d).  Without HQ_DITHER this is hq_encode_tiles on the vectors
+ * (the rotation-only control).  Outputs as for hq_encode_tiles; decode with
+ * hq_decode_tiles and the same flags, seed and base.
+ */
+hq_status hq_kv_encode(const hq_params* p, const void* kv, int32_t kv_dtype,
+                       int64_t n_vectors, float* scale, int8_t* idx,
+                       uint32_t* coset, uint8_t* rice_k, uint32_t* tile_bits,
+                       uint32_t* status, hipStream_t stream);
+
+/* Coset words per tile: E8 ceil(n/256), A2 ceil(n/64), D4 and Z 0;
+ * -1 on an invalid p. */
+int32_t hq_coset_words(const hq_params* p);
+
+/* Device workspace bytes hq_rate needs to pack n_tiles tiles. */
+size_t hq_rate_workspace_bytes(int64_t n_tiles);
+
+/* Static description of a status code (never NULL). */
+const char* hq_status_string(hq_status s);
+
+/* Host-side helpers (no device work; usable without a GPU). */
+
+/* SplitMix64 output for state `key` (Steele, Lea & Flood, OOPSLA 2014). */
+uint64_t hq_splitmix64(uint64_t key);
+
+/* Writes the n RHT signs (+1 / -1) for `seed` into host memory `out`. */
+hq_status hq_rht_signs(uint32_t seed, int32_t n, int8_t* out);
+
+/* The auto-scale constant c(L, R) = sqrt(2 pi e) 2^-R / vol^(1/d) for p. */
+hq_status hq_scale_constant(const hq_params* p, double* out);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int32_t hq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HQ_H */

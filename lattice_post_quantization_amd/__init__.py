@@ -1,0 +1,6 @@
+"""HyperQuant hot path on MI355X: HIP kernels behind a C ABI (include/hq.h)
+and a thin Python binding (hq.py)."""
+
+from .hq import (  # noqa: F401
+    HQError, hq_decode_tiles, hq_encode_tiles, hq_kv_encode, hq_rate, lib,
+)

@@ -1,0 +1,326 @@
+// C ABI of the HyperQuant hot path: argument validation, sign vectors,
+// kernel launches.  Every check that needs no device call runs first, so a
+// rejected call touches nothing on the GPU.
+//
+// Passages: [arXiv abstract] "HyperQuant: A Rate-Distortion-Optimal
+// Quantization Pipeline ..." ideas (i)-(iv); [ICLR abstract] "HyperQuant: A
+// Near-Entropy-Optimal Lattice Quantization Pipeline ..."; the statement of
+// the problem there (tile, lattice, target rate, per-tile scale and seed in;
+// lattice indices, coset bits, Rice parameters and bit lengths out) is the
+// shape of this interface.
+#include <math.h>
+#include <string.h>
+
+#include "hq.h"
+#include "hq_device.h"
+#include "hq_internal.h"
+
+namespace hq {
+int64_t rate_blocks(int64_t n_tiles, int tile);
+}
+
+namespace {
+
+using namespace hq;
+
+constexpr uint32_t kKnownFlags = HQ_SCALE_AUTO | HQ_DITHER | HQ_WANT_COORDS;
+
+bool lattice_ok(int32_t l) { return l == HQ_E8 || l == HQ_D4 || l == HQ_A2 || l == HQ_Z; }
+
+// Validates the parameter block; `need_range` adds the auto-scale bound.
+hq_status check_params(const hq_params* p) {
+  if (p == nullptr || p->struct_size != sizeof(hq_params)) return HQ_EINVAL;
+  if (!lattice_ok(p->lattice)) return HQ_EINVAL;
+  if (p->tile != 128 && p->tile != 256) return HQ_EINVAL;
+  if (!(p->bps > 0.0f) || !(p->bps <= 8.0f)) return HQ_EINVAL;
+  if ((p->flags & ~kKnownFlags) != 0 || p->reserved != 0) return HQ_EINVAL;
+  if (p->flags & HQ_DITHER) {
+    if (p->lattice != HQ_E8) return HQ_EUNSUPPORTED;
+    if (p->dither_seed >= (1u << 24)) return HQ_EINVAL;
+    if (p->dither_base < 0) return HQ_EINVAL;
+  }
+  return HQ_OK;
+}
+
+double vol_root(int32_t lattice) {
+  switch (lattice) {
+    case HQ_D4: return sqrt(sqrt(2.0));
+    case HQ_A2: return sqrt(sqrt(3.0) / 2.0);
+    default: return 1.0;
+  }
+}
+
+// c(L, R) = sqrt(2 pi e) 2^-R / vol^(1/d)   (high-resolution scale constant)
+double scale_constant(const hq_params* p) {
+  return sqrt(2.0 * M_PI * M_E) * pow(2.0, -(double)p->bps) / vol_root(p->lattice);
+}
+
+// Auto scale keeps |index| <= sqrt(n)/c + 2 inside int8.
+bool range_ok(const hq_params* p) {
+  return sqrt((double)p->tile) / scale_constant(p) + 2.0 <= 127.0;
+}
+
+int32_t coset_words(const hq_params* p) {
+  if (p->lattice == HQ_E8) return (p->tile / 8 + 31) / 32;
+  if (p->lattice == HQ_A2) return (p->tile / 2 + 31) / 32;
+  return 0;
+}
+
+int32_t coset_bits(const hq_params* p) {
+  if (p->lattice == HQ_E8) return p->tile / 8;
+  if (p->lattice == HQ_A2) return p->tile / 2;
+  return 0;
+}
+
+bool aligned16(const void* q) { return ((uintptr_t)q & 15u) == 0; }
+
+void make_signs(uint32_t seed, int n, uint32_t* out) {
+  for (int w = 0; w < 8; ++w) out[w] = 0;
+  for (int j = 0; j < n; ++j) {
+    const uint64_t h = splitmix64(((uint64_t)seed << 32) ^ (uint64_t)j);
+    if (h >> 63) out[j >> 5] |= 1u << (j & 31);
+  }
+}
+
+// Device-pointer check (one HIP query per pointer); clears the error a
+// failed query leaves behind.
+bool on_device(const void* q) {
+  if (q == nullptr) return false;
+  hipPointerAttribute_t attr;
+  memset(&attr, 0, sizeof(attr));
+  if (hipPointerGetAttributes(&attr, q) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged ||
+         attr.type == hipMemoryTypeUnified;
+}
+
+hq_status launched(hipError_t e) { return e == hipSuccess ? HQ_OK : HQ_EDEVICE; }
+
+// Shared validation of an encode-shaped call.
+hq_status check_encode(const hq_params* p, const void* x, int32_t x_dtype, int64_t rows,
+                       int64_t cols, const float* scale, const int8_t* idx,
+                       const uint32_t* coset, const uint8_t* rice_k,
+                       const uint32_t* tile_bits, const int16_t* coords) {
+  hq_status st = check_params(p);
+  if (st != HQ_OK) return st;
+  if (x_dtype != HQ_F32 && x_dtype != HQ_BF16) return HQ_EINVAL;
+  if (rows < 0 || cols < 0) return HQ_EINVAL;
+  if (cols % p->tile != 0) return HQ_EINVAL;
+  if (x == nullptr || scale == nullptr || idx == nullptr || rice_k == nullptr ||
+      tile_bits == nullptr)
+    return HQ_EINVAL;
+  if (coset_words(p) > 0 && coset == nullptr) return HQ_EINVAL;
+  if ((p->flags & HQ_WANT_COORDS) && coords == nullptr) return HQ_EINVAL;
+  if (!aligned16(x) || !aligned16(idx) || ((p->flags & HQ_WANT_COORDS) && !aligned16(coords)))
+    return HQ_EINVAL;
+  if (rows > 0 && cols > 0 && rows > INT64_MAX / cols) return HQ_EINVAL;
+  if ((p->flags & HQ_SCALE_AUTO) && !range_ok(p)) return HQ_ERANGE;
+  return HQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hq_status hq_encode_tiles(const hq_params* p, const void* x, int32_t x_dtype, int64_t rows,
+                          int64_t cols, float* scale, int8_t* idx, uint32_t* coset,
+                          uint8_t* rice_k, uint32_t* tile_bits, int16_t* coords,
+                          uint32_t* status, hipStream_t stream) {
+  hq_status st = check_encode(p, x, x_dtype, rows, cols, scale, idx, coset, rice_k, tile_bits,
+                              coords);
+  if (st != HQ_OK) return st;
+  if (p->flags & HQ_DITHER) return HQ_EUNSUPPORTED;
+  const int64_t n_tiles = rows * cols / p->tile;
+  if (n_tiles == 0) return HQ_OK;
+  if (!on_device(x) || !on_device(scale) || !on_device(idx) || !on_device(rice_k) ||
+      !on_device(tile_bits) || (coset_words(p) > 0 && !on_device(coset)) ||
+      ((p->flags & HQ_WANT_COORDS) && !on_device(coords)) ||
+      (status != nullptr && !on_device(status)))
+    return HQ_EINVAL;
+  EncodeLaunch a;
+  memset(&a, 0, sizeof(a));
+  a.x = x;
+  a.in_bf16 = x_dtype == HQ_BF16;
+  a.n_tiles = n_tiles;
+  a.lattice = p->lattice;
+  a.tile = p->tile;
+  a.scale = scale;
+  a.auto_scale = (p->flags & HQ_SCALE_AUTO) != 0;
+  a.idx = idx;
+  a.coset = coset;
+  a.rice_k = rice_k;
+  a.tile_bits = tile_bits;
+  a.coords = (p->flags & HQ_WANT_COORDS) ? coords : nullptr;
+  a.status = status;
+  make_signs(p->rht_seed, p->tile, a.signs);
+  a.c = scale_constant(p);
+  a.sqrt_n = sqrt((double)p->tile);
+  return launched(launch_encode(a, stream));
+}
+
+hq_status hq_kv_encode(const hq_params* p, const void* kv, int32_t kv_dtype, int64_t n_vectors,
+                       float* scale, int8_t* idx, uint32_t* coset, uint8_t* rice_k,
+                       uint32_t* tile_bits, uint32_t* status, hipStream_t stream) {
+  hq_status st = check_params(p);
+  if (st != HQ_OK) return st;
+  if (p->lattice != HQ_E8) return HQ_EUNSUPPORTED;
+  if (p->flags & HQ_WANT_COORDS) return HQ_EUNSUPPORTED;
+  if (n_vectors < 0) return HQ_EINVAL;
+  st = check_encode(p, kv, kv_dtype, n_vectors, p->tile, scale, idx, coset, rice_k, tile_bits,
+                    nullptr);
+  if (st != HQ_OK) return st;
+  if ((p->flags & HQ_DITHER) && p->dither_base + n_vectors > ((int64_t)1 << 32))
+    return HQ_EINVAL;
+  if (n_vectors == 0) return HQ_OK;
+  if (!on_device(kv) || !on_device(scale) || !on_device(idx) || !on_device(rice_k) ||
+      !on_device(tile_bits) || !on_device(coset) || (status != nullptr && !on_device(status)))
+    return HQ_EINVAL;
+  EncodeLaunch a;
+  memset(&a, 0, sizeof(a));
+  a.x = kv;
+  a.in_bf16 = kv_dtype == HQ_BF16;
+  a.n_tiles = n_vectors;
+  a.lattice = HQ_E8;
+  a.tile = p->tile;
+  a.scale = scale;
+  a.auto_scale = (p->flags & HQ_SCALE_AUTO) != 0;
+  a.idx = idx;
+  a.coset = coset;
+  a.rice_k = rice_k;
+  a.tile_bits = tile_bits;
+  a.coords = nullptr;
+  a.status = status;
+  make_signs(p->rht_seed, p->tile, a.signs);
+  a.c = scale_constant(p);
+  a.sqrt_n = sqrt((double)p->tile);
+  a.dither = (p->flags & HQ_DITHER) != 0;
+  a.dither_seed = p->dither_seed;
+  a.dither_base = p->dither_base;
+  return launched(launch_encode(a, stream));
+}
+
+hq_status hq_decode_tiles(const hq_params* p, const int8_t* idx, const uint32_t* coset,
+                          const float* scale, int64_t rows, int64_t cols, void* y,
+                          int32_t y_dtype, uint32_t* status, hipStream_t stream) {
+  hq_status st = check_params(p);
+  if (st != HQ_OK) return st;
+  if (y_dtype != HQ_F32 && y_dtype != HQ_BF16) return HQ_EINVAL;
+  if (rows < 0 || cols < 0 || cols % p->tile != 0) return HQ_EINVAL;
+  if (idx == nullptr || scale == nullptr || y == nullptr) return HQ_EINVAL;
+  if (coset_words(p) > 0 && coset == nullptr) return HQ_EINVAL;
+  if (!aligned16(idx) || !aligned16(y)) return HQ_EINVAL;
+  if (rows > 0 && cols > 0 && rows > INT64_MAX / cols) return HQ_EINVAL;
+  const int64_t n_tiles = rows * cols / p->tile;
+  if ((p->flags & HQ_DITHER) && p->dither_base + n_tiles > ((int64_t)1 << 32))
+    return HQ_EINVAL;
+  if (n_tiles == 0) return HQ_OK;
+  if (!on_device(idx) || !on_device(scale) || !on_device(y) ||
+      (coset_words(p) > 0 && !on_device(coset)) || (status != nullptr && !on_device(status)))
+    return HQ_EINVAL;
+  DecodeLaunch a;
+  memset(&a, 0, sizeof(a));
+  a.idx = idx;
+  a.coset = coset;
+  a.scale = scale;
+  a.n_tiles = n_tiles;
+  a.lattice = p->lattice;
+  a.tile = p->tile;
+  a.y = y;
+  a.out_bf16 = y_dtype == HQ_BF16;
+  a.status = status;
+  make_signs(p->rht_seed, p->tile, a.signs);
+  a.inv_sqrt_n = 1.0 / sqrt((double)p->tile);
+  a.dither = (p->flags & HQ_DITHER) != 0;
+  a.dither_seed = p->dither_seed;
+  a.dither_base = p->dither_base;
+  return launched(launch_decode(a, stream));
+}
+
+size_t hq_rate_workspace_bytes(int64_t n_tiles) {
+  if (n_tiles <= 0) return 0;
+  return (size_t)((n_tiles + 15) / 16) * sizeof(uint64_t);
+}
+
+hq_status hq_rate(const hq_params* p, const int8_t* idx, const uint32_t* coset, int64_t n_tiles,
+                  uint8_t* rice_k, uint32_t* tile_bits, uint64_t* total_bits,
+                  uint32_t* stream_words, uint64_t capacity_words, uint64_t* tile_word_offset,
+                  void* workspace, size_t workspace_bytes, uint32_t* status,
+                  hipStream_t stream) {
+  hq_status st = check_params(p);
+  if (st != HQ_OK) return st;
+  if (n_tiles < 0) return HQ_EINVAL;
+  if (idx == nullptr || rice_k == nullptr || tile_bits == nullptr || total_bits == nullptr)
+    return HQ_EINVAL;
+  if (!aligned16(idx) || ((uintptr_t)total_bits & 7u)) return HQ_EINVAL;
+  const bool pack = stream_words != nullptr;
+  if (pack) {
+    if (tile_word_offset == nullptr || workspace == nullptr) return HQ_EINVAL;
+    if (coset_words(p) > 0 && coset == nullptr) return HQ_EINVAL;
+    if (workspace_bytes < hq_rate_workspace_bytes(n_tiles)) return HQ_EINVAL;
+    if (((uintptr_t)workspace & 7u) || ((uintptr_t)tile_word_offset & 7u)) return HQ_EINVAL;
+  }
+  if (n_tiles > INT64_MAX / p->tile) return HQ_EINVAL;
+  if (n_tiles == 0) return HQ_OK;
+  if (!on_device(idx) || !on_device(rice_k) || !on_device(tile_bits) || !on_device(total_bits) ||
+      (status != nullptr && !on_device(status)))
+    return HQ_EINVAL;
+  if (pack && (!on_device(stream_words) || !on_device(tile_word_offset) ||
+               !on_device(workspace) || (coset_words(p) > 0 && !on_device(coset))))
+    return HQ_EINVAL;
+  RateLaunch a;
+  memset(&a, 0, sizeof(a));
+  a.idx = idx;
+  a.coset = coset;
+  a.n_tiles = n_tiles;
+  a.tile = p->tile;
+  a.coset_bits = coset_bits(p);
+  a.coset_words = coset_words(p);
+  a.rice_k = rice_k;
+  a.tile_bits = tile_bits;
+  a.total_bits = total_bits;
+  a.stream = pack ? stream_words : nullptr;
+  a.capacity = capacity_words;
+  a.tile_word_offset = tile_word_offset;
+  a.block_words = pack ? static_cast<uint64_t*>(workspace) : nullptr;
+  a.status = status;
+  return launched(launch_rate(a, stream));
+}
+
+int32_t hq_coset_words(const hq_params* p) {
+  if (check_params(p) != HQ_OK) return -1;
+  return coset_words(p);
+}
+
+const char* hq_status_string(hq_status s) {
+  switch (s) {
+    case HQ_OK: return "ok";
+    case HQ_EINVAL: return "invalid argument";
+    case HQ_ERANGE: return "auto scale would overflow the int8 indices";
+    case HQ_EDEVICE: return "HIP call or kernel launch failed";
+    case HQ_EUNSUPPORTED: return "unsupported parameter combination";
+    default: return "unknown status";
+  }
+}
+
+uint64_t hq_splitmix64(uint64_t key) { return splitmix64(key); }
+
+hq_status hq_rht_signs(uint32_t seed, int32_t n, int8_t* out) {
+  if (out == nullptr || n <= 0 || n > 256) return HQ_EINVAL;
+  for (int j = 0; j < n; ++j)
+    out[j] = (splitmix64(((uint64_t)seed << 32) ^ (uint64_t)j) >> 63) ? -1 : 1;
+  return HQ_OK;
+}
+
+hq_status hq_scale_constant(const hq_params* p, double* out) {
+  hq_status st = check_params(p);
+  if (st != HQ_OK) return st;
+  if (out == nullptr) return HQ_EINVAL;
+  *out = scale_constant(p);
+  return HQ_OK;
+}
+
+int32_t hq_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Launch descriptors shared by the C ABI (hq_api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hq {
+
+constexpr int kBlock = 256;         // threads per block, every kernel
+constexpr int kElemsPerLane = 16;   // tile elements held by one lane
+
+struct EncodeLaunch {
+  const void* x;
+  int in_bf16;
+  int64_t n_tiles;
+  int lattice;          // 8, 4, 2, 1
+  int tile;             // 128 or 256
+  float* scale;
+  int auto_scale;
+  int8_t* idx;
+  uint32_t* coset;
+  uint8_t* rice_k;
+  uint32_t* tile_bits;
+  int16_t* coords;      // nullptr unless requested
+  uint32_t* status;     // may be nullptr
+  uint32_t signs[8];    // bit j set: sign of element j is -1
+  double c;             // auto-scale constant c(L, R)
+  double sqrt_n;        // fp64 sqrt(tile)
+  int dither;
+  uint32_t dither_seed;
+  int64_t dither_base;
+};
+
+struct DecodeLaunch {
+  const int8_t* idx;
+  const uint32_t* coset;
+  const float* scale;
+  int64_t n_tiles;
+  int lattice;
+  int tile;
+  void* y;
+  int out_bf16;
+  uint32_t* status;
+  uint32_t signs[8];
+  double inv_sqrt_n;    // fp64 1/sqrt(tile)
+  int dither;
+  uint32_t dither_seed;
+  int64_t dither_base;
+};
+
+struct RateLaunch {
+  const int8_t* idx;
+  const uint32_t* coset;
+  int64_t n_tiles;
+  int tile;
+  int coset_bits;       // per tile
+  int coset_words;      // per tile
+  uint8_t* rice_k;
+  uint32_t* tile_bits;
+  uint64_t* total_bits;
+  uint32_t* stream;     // nullptr: rate only
+  uint64_t capacity;
+  uint64_t* tile_word_offset;
+  uint64_t* block_words;   // workspace: one uint64 per rate block
+  uint32_t* status;
+};
+
+hipError_t launch_encode(const EncodeLaunch& a, hipStream_t s);
+hipError_t launch_decode(const DecodeLaunch& a, hipStream_t s);
+hipError_t launch_rate(const RateLaunch& a, hipStream_t s);
+
+// tiles handled by one rate/pack block
+constexpr int kRateTilesPerBlock = 16;
+
+}  // namespace hq

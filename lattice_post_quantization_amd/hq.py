@@ -1,0 +1,298 @@
+"""Python binding of libhq.so (the HyperQuant hot path on MI355X).
+
+Argument marshalling only: every step of the path runs in the HIP kernels
+behind the C ABI declared in include/hq.h.  PyTorch provides device memory and
+the current HIP stream.  The names mirror the C entry points.
+
+The library must be built first (`python -m lattice_post_quantization_amd.build`);
+a missing library raises instead of falling back to anything else.
+"""
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime first, so libhq.so binds to the same one
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhq.so")
+
+HQ_OK, HQ_EINVAL, HQ_ERANGE, HQ_EDEVICE, HQ_EUNSUPPORTED = 0, -1, -2, -3, -4
+HQ_Z, HQ_A2, HQ_D4, HQ_E8 = 1, 2, 4, 8
+HQ_F32, HQ_BF16 = 0, 1
+HQ_SCALE_AUTO, HQ_DITHER, HQ_WANT_COORDS = 1, 2, 4
+HQ_ST_NONFINITE, HQ_ST_OVERFLOW, HQ_ST_STREAM_FULL = 1, 2, 4
+
+LATTICES = {"E8": HQ_E8, "D4": HQ_D4, "A2": HQ_A2, "Z": HQ_Z}
+
+
+class HQError(RuntimeError):
+    def __init__(self, code, what):
+        self.code = code
+        super().__init__("%s: %s (%d)" % (what, status_string(code), code))
+
+
+class Params(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("lattice", ctypes.c_int32),
+        ("tile", ctypes.c_int32),
+        ("bps", ctypes.c_float),
+        ("rht_seed", ctypes.c_uint32),
+        ("dither_seed", ctypes.c_uint32),
+        ("dither_base", ctypes.c_int64),
+        ("flags", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
+    ]
+
+
+def make_params(lattice="E8", tile=256, bps=4.0, rht_seed=0, flags=0,
+                dither_seed=0, dither_base=0):
+    lat = LATTICES[lattice] if isinstance(lattice, str) else int(lattice)
+    return Params(ctypes.sizeof(Params), lat, int(tile), float(bps), int(rht_seed),
+                  int(dither_seed), int(dither_base), int(flags), 0)
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I32, _I64, _U32, _U64, _SZ = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
+                               ctypes.c_uint64, ctypes.c_size_t)
+_PP = ctypes.POINTER(Params)
+
+_SIGNATURES = {
+    "hq_encode_tiles": (_I32, [_PP, _P, _I32, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "hq_decode_tiles": (_I32, [_PP, _P, _P, _P, _I64, _I64, _P, _I32, _P, _P]),
+    "hq_rate": (_I32, [_PP, _P, _P, _I64, _P, _P, _P, _P, _U64, _P, _P, _SZ, _P, _P]),
+    "hq_kv_encode": (_I32, [_PP, _P, _I32, _I64, _P, _P, _P, _P, _P, _P, _P]),
+    "hq_coset_words": (_I32, [_PP]),
+    "hq_rate_workspace_bytes": (_SZ, [_I64]),
+    "hq_status_string": (ctypes.c_char_p, [_I32]),
+    "hq_splitmix64": (_U64, [_U64]),
+    "hq_rht_signs": (_I32, [_U32, _I32, _P]),
+    "hq_scale_constant": (_I32, [_PP, ctypes.POINTER(ctypes.c_double)]),
+    "hq_version": (_I32, []),
+}
+
+
+def lib():
+    """The loaded libhq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libhq.so is not built (%s); run "
+                               "python -m lattice_post_quantization_amd.build" % LIB_PATH)
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = l
+    return _lib
+
+
+def status_string(code):
+    return lib().hq_status_string(int(code)).decode()
+
+
+def _check(code, what):
+    if code != HQ_OK:
+        raise HQError(code, what)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(dt):
+    if dt == torch.bfloat16:
+        return HQ_BF16
+    if dt == torch.float32:
+        return HQ_F32
+    raise ValueError("dtype must be bfloat16 or float32")
+
+
+def _device_tensor(t, name):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError("%s must be a CUDA (HIP) tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def coset_words(lattice="E8", tile=256):
+    p = make_params(lattice, tile)
+    return int(lib().hq_coset_words(ctypes.byref(p)))
+
+
+def rate_workspace_bytes(n_tiles):
+    return int(lib().hq_rate_workspace_bytes(int(n_tiles)))
+
+
+def rht_signs(seed, n):
+    import numpy as np
+    out = np.zeros(n, np.int8)
+    _check(lib().hq_rht_signs(int(seed), int(n), out.ctypes.data_as(ctypes.c_void_p)),
+           "hq_rht_signs")
+    return out
+
+
+def scale_constant(lattice, bps):
+    p = make_params(lattice, 256 if lattice == "E8" else 128, bps)
+    out = ctypes.c_double()
+    _check(lib().hq_scale_constant(ctypes.byref(p), ctypes.byref(out)), "hq_scale_constant")
+    return out.value
+
+
+def splitmix64(key):
+    return int(lib().hq_splitmix64(int(key)))
+
+
+def hq_encode_tiles(x, lattice="E8", tile=256, bps=4.0, rht_seed=0, scale=None,
+                    want_coords=False, status=None, out=None):
+    """Encode a row-major (rows, cols) bf16/fp32 device matrix.
+
+    scale=None selects auto scales (returned); otherwise a float32 device
+    tensor of per-tile scales.  Returns a dict of device tensors: scale,
+    idx (int8, like x), coset (int32 words, (n_tiles, w)), rice_k (uint8),
+    tile_bits (int32 holding uint32), coords (int16, if requested).
+    `out` may supply preallocated tensors under the same keys."""
+    _device_tensor(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D (rows, cols)")
+    rows, cols = x.shape
+    dev = x.device
+    n_tiles = rows * cols // tile if cols % tile == 0 else 0
+    w = coset_words(lattice, tile)
+    o = dict(out or {})
+    flags = (HQ_SCALE_AUTO if scale is None else 0) | (HQ_WANT_COORDS if want_coords else 0)
+    if scale is None:
+        scale = o.get("scale")
+        if scale is None:
+            scale = torch.empty(n_tiles, dtype=torch.float32, device=dev)
+    else:
+        _device_tensor(scale, "scale")
+    idx = o.get("idx")
+    if idx is None:
+        idx = torch.empty((rows, cols), dtype=torch.int8, device=dev)
+    coset = o.get("coset")
+    if coset is None:
+        coset = torch.empty((n_tiles, max(w, 1)), dtype=torch.int32, device=dev)
+    rice_k = o.get("rice_k")
+    if rice_k is None:
+        rice_k = torch.empty(n_tiles, dtype=torch.uint8, device=dev)
+    tile_bits = o.get("tile_bits")
+    if tile_bits is None:
+        tile_bits = torch.empty(n_tiles, dtype=torch.int32, device=dev)
+    coords = None
+    if want_coords:
+        coords = o.get("coords")
+        if coords is None:
+            coords = torch.empty((rows, cols), dtype=torch.int16, device=dev)
+    p = make_params(lattice, tile, bps, rht_seed, flags)
+    code = lib().hq_encode_tiles(ctypes.byref(p), _ptr(x), _dtype_code(x.dtype), rows, cols,
+                                 _ptr(scale), _ptr(idx), _ptr(coset), _ptr(rice_k),
+                                 _ptr(tile_bits), _ptr(coords), _ptr(status), _stream(dev))
+    _check(code, "hq_encode_tiles")
+    res = {"scale": scale, "idx": idx, "coset": coset, "rice_k": rice_k, "tile_bits": tile_bits}
+    if want_coords:
+        res["coords"] = coords
+    return res
+
+
+def hq_decode_tiles(idx, coset, scale, lattice="E8", tile=256, rht_seed=0,
+                    out_dtype=torch.bfloat16, dither_seed=None, dither_base=0,
+                    status=None, out=None):
+    """Decode stripped indices back to weights (rows, cols) of out_dtype."""
+    _device_tensor(idx, "idx")
+    _device_tensor(scale, "scale")
+    if coset is not None:
+        _device_tensor(coset, "coset")
+    rows, cols = idx.shape
+    y = out if out is not None else torch.empty((rows, cols), dtype=out_dtype, device=idx.device)
+    flags = HQ_DITHER if dither_seed is not None else 0
+    p = make_params(lattice, tile, 4.0, rht_seed, flags,
+                    0 if dither_seed is None else dither_seed, dither_base)
+    code = lib().hq_decode_tiles(ctypes.byref(p), _ptr(idx), _ptr(coset), _ptr(scale), rows, cols,
+                                 _ptr(y), _dtype_code(y.dtype), _ptr(status), _stream(idx.device))
+    _check(code, "hq_decode_tiles")
+    return y
+
+
+def hq_rate(idx, coset, lattice="E8", tile=256, pack=False, capacity_words=None,
+            status=None, out=None):
+    """Rice parameters and bit lengths per tile; optionally the packed stream.
+
+    Returns dict: rice_k, tile_bits, total_bits (int64 device scalar) and, when
+    packing, stream (int32 words), tile_word_offset (int64, n_tiles + 1)."""
+    _device_tensor(idx, "idx")
+    dev = idx.device
+    n_tiles = idx.numel() // tile
+    o = dict(out or {})
+    rice_k = o.get("rice_k")
+    if rice_k is None:
+        rice_k = torch.empty(n_tiles, dtype=torch.uint8, device=dev)
+    tile_bits = o.get("tile_bits")
+    if tile_bits is None:
+        tile_bits = torch.empty(n_tiles, dtype=torch.int32, device=dev)
+    total = o.get("total_bits")
+    if total is None:
+        total = torch.empty(1, dtype=torch.int64, device=dev)
+    stream = offs = ws = None
+    if pack:
+        if capacity_words is None:
+            # the optimal k never costs more than k = 8: 4 + coset + 9 n bits
+            capacity_words = n_tiles * ((4 + tile // 2 + 9 * tile + 31) // 32)
+        stream = o.get("stream")
+        if stream is None:
+            stream = torch.empty(max(int(capacity_words), 1), dtype=torch.int32, device=dev)
+        offs = torch.empty(n_tiles + 1, dtype=torch.int64, device=dev)
+        ws = torch.empty(max(rate_workspace_bytes(n_tiles), 8), dtype=torch.uint8, device=dev)
+    p = make_params(lattice, tile, 4.0)
+    code = lib().hq_rate(ctypes.byref(p), _ptr(idx), _ptr(coset), n_tiles, _ptr(rice_k),
+                         _ptr(tile_bits), _ptr(total), _ptr(stream),
+                         int(capacity_words or 0), _ptr(offs), _ptr(ws),
+                         0 if ws is None else ws.numel(), _ptr(status), _stream(dev))
+    _check(code, "hq_rate")
+    res = {"rice_k": rice_k, "tile_bits": tile_bits, "total_bits": total}
+    if pack:
+        res["stream"] = stream
+        res["tile_word_offset"] = offs
+    return res
+
+
+def hq_kv_encode(kv, bps=4.0, rht_seed=0, dither_seed=None, dither_base=0, status=None,
+                 out=None):
+    """Encode KV vectors (n_vectors, head_dim) with E8 and auto scales;
+    dither_seed=None gives the rotation-only control."""
+    _device_tensor(kv, "kv")
+    if kv.dim() != 2:
+        raise ValueError("kv must be 2-D (n_vectors, head_dim)")
+    n_vec, hd = kv.shape
+    dev = kv.device
+    o = dict(out or {})
+    scale = o.get("scale")
+    if scale is None:
+        scale = torch.empty(n_vec, dtype=torch.float32, device=dev)
+    idx = o.get("idx")
+    if idx is None:
+        idx = torch.empty((n_vec, hd), dtype=torch.int8, device=dev)
+    coset = o.get("coset")
+    if coset is None:
+        coset = torch.empty((n_vec, coset_words("E8", hd)), dtype=torch.int32, device=dev)
+    rice_k = o.get("rice_k")
+    if rice_k is None:
+        rice_k = torch.empty(n_vec, dtype=torch.uint8, device=dev)
+    tile_bits = o.get("tile_bits")
+    if tile_bits is None:
+        tile_bits = torch.empty(n_vec, dtype=torch.int32, device=dev)
+    flags = HQ_SCALE_AUTO | (HQ_DITHER if dither_seed is not None else 0)
+    p = make_params("E8", hd, bps, rht_seed, flags,
+                    0 if dither_seed is None else dither_seed, dither_base)
+    code = lib().hq_kv_encode(ctypes.byref(p), _ptr(kv), _dtype_code(kv.dtype), n_vec,
+                              _ptr(scale), _ptr(idx), _ptr(coset), _ptr(rice_k), _ptr(tile_bits),
+                              _ptr(status), _stream(dev))
+    _check(code, "hq_kv_encode")
+    return {"scale": scale, "idx": idx, "coset": coset, "rice_k": rice_k, "tile_bits": tile_bits}

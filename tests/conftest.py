@@ -27,3 +27,16 @@ def read_golden(name):
 @pytest.fixture(scope="session")
 def golden():
     return read_golden
+
+
+def pytest_collection_modifyitems(config, items):
+    """GPU tests are skipped, with a reason, on a machine without a GPU."""
+    if not any("gpu" in it.keywords for it in items):
+        return
+    import torch
+    if torch.cuda.is_available():
+        return
+    skip = pytest.mark.skip(reason="no GPU visible to torch")
+    for it in items:
+        if "gpu" in it.keywords:
+            it.add_marker(skip)

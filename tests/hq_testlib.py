@@ -1,0 +1,92 @@
+"""Helpers shared by the GPU parity tests: host<->device transfer and the
+comparison rules (indices bit-exact except at oracle near-ties, decoded values
+within 1e-5 * Delta, Rice results exact on matching tiles)."""
+
+import numpy as np
+import torch
+
+from oracle import codec, rice
+
+NEAR_TIE = 1e-6          # oracle margin below which a block counts as a near-tie
+NEAR_TIE_CAP = 1e-5      # largest allowed fraction of excused blocks
+
+
+def bf16_device(bits, shape=None):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    if shape is not None:
+        t = t.reshape(shape)
+    return t.cuda()
+
+
+def f32_device(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def u32(t):
+    return host(t).view(np.uint32)
+
+
+def bf16_host_bits(t):
+    return host(t.view(torch.int16)).view(np.uint16)
+
+
+def tile_rows(gpu_array, n, tiles=None):
+    a = np.asarray(gpu_array).reshape(-1, n)
+    return a if tiles is None else a[tiles]
+
+
+def compare_indices(g_idx, g_coset, ora, lattice, n, label=""):
+    """Block-level comparison.  Returns (mismatch blocks, near-tie blocks,
+    total blocks, tiles whose indices all match)."""
+    d = codec.DIM[lattice]
+    T = ora["idx"].shape[0]
+    gi = np.asarray(g_idx, np.int64).reshape(T, n // d, d)
+    oi = ora["idx"].reshape(T, n // d, d)
+    bad = np.any(gi != oi, axis=-1)
+    if codec.coset_bits_per_tile(lattice, n):
+        gc = codec.unpack_cosets(np.asarray(g_coset).reshape(T, -1).astype(np.uint32), lattice, n)
+        oc = codec.unpack_cosets(ora["coset"], lattice, n)
+        bad |= gc != oc
+    near = ora["margin"] < NEAR_TIE
+    assert np.all(near[bad]), "%s: %d index mismatches outside near-ties" % (label, np.sum(bad & ~near))
+    assert bad.sum() <= NEAR_TIE_CAP * bad.size, "%s: too many near-tie mismatches" % label
+    tiles_ok = ~np.any(bad, axis=1)
+    return int(bad.sum()), int(near.sum()), int(bad.size), tiles_ok
+
+
+def compare_decoded(g_vals, o_vals, scale, out_bf16, exact, label=""):
+    """|gpu - oracle| <= 1e-5 * Delta (+ half a bf16 ulp of the oracle for
+    bf16 outputs); `exact` additionally demands bit equality."""
+    g = np.asarray(g_vals, np.float64)
+    o = np.asarray(o_vals, np.float64)
+    tol = 1e-5 * np.asarray(scale, np.float64)[:, None]
+    if out_bf16:
+        ulp = np.abs(o) * 2.0 ** -7
+        tol = tol + 0.5 * ulp
+    err = np.abs(g - o)
+    assert np.all(err <= tol), "%s: max err / Delta %.3g" % (label, np.max(err / np.asarray(scale)[:, None]))
+    if exact:
+        assert np.array_equal(g, o), "%s: %d values differ" % (label, int(np.sum(g != o)))
+
+
+def oracle_decode_like_gpu(g_idx, g_coset, g_scale, lattice, n, seed, out_bf16,
+                           dither_seed=None, dither_base=0):
+    """Oracle decode of the GPU's own indices, rounded like the output."""
+    T = np.asarray(g_idx).size // n
+    x = codec.decode(np.asarray(g_idx, np.int64).reshape(T, n),
+                     np.asarray(g_coset).reshape(T, -1).astype(np.uint32) if g_coset is not None
+                     else np.zeros((T, 0), np.uint32),
+                     np.asarray(g_scale, np.float64), lattice, n, seed,
+                     dither_seed=dither_seed, dither_base=dither_base)
+    if out_bf16:
+        return codec.bf16_rne(x)
+    return x.astype(np.float32).astype(np.float64)
+
+
+def rice_pack_oracle(idx, coset_words, lattice, n):
+    return rice.pack(np.asarray(idx, np.int64), coset_words,
+                     codec.coset_bits_per_tile(lattice, n))

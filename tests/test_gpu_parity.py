@@ -1,0 +1,295 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Every oracle input is generated here from seeds; nothing the oracle sees comes
+from the GPU.  Encode parity compares the GPU's encode of x with the oracle's
+encode of the same x; decode and rate parity feed the oracle's indices to
+both sides.  Indices must match bit for bit except at oracle near-ties
+(margin < 1e-6, at most a 1e-5 fraction); decoded values within 1e-5 * Delta
+(bit-exact where the arithmetic is exact); Rice results exact.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import codec
+import hq_testlib as T
+
+pytestmark = pytest.mark.gpu
+
+from lattice_post_quantization_amd import hq  # noqa: E402  (fails loudly if unbuilt)
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def midpoint_close(pre, rel=1e-9):
+    """Tiles whose fp64 pre-rounding scale sits within rel of a bf16 midpoint."""
+    m, e = np.frexp(np.asarray(pre, np.float64))
+    t = m * 256.0
+    return np.abs(t - np.floor(t) - 0.5) < rel * t
+
+
+def oracle_pre_scale(X, lattice, bps):
+    n = X.shape[1]
+    return np.sqrt(np.sum(X * X, axis=1) / n) * codec.scale_constant(lattice, bps)
+
+
+def check_encode(x_host, x_dev, lattice, n, bps, seed, tiles=None, label=""):
+    """Auto-scale encode on the GPU (all tiles) vs the oracle (all or the
+    sampled tiles).  Returns the oracle result of the compared tiles."""
+    g = hq.hq_encode_tiles(x_dev, lattice, n, bps, seed, want_coords=True)
+    torch.cuda.synchronize()
+    X = codec.tiles(x_host, n)
+    if tiles is not None:
+        X = X[tiles]
+    ora = codec.encode(X, lattice, n, bps, rht_seed=seed)
+    gs = T.tile_rows(T.host(g["scale"]), 1, None).reshape(-1)
+    gs = gs if tiles is None else gs[tiles]
+    skip = midpoint_close(oracle_pre_scale(X, lattice, bps))
+    assert np.array_equal(gs.astype(np.float64)[~skip], ora["scale"][~skip]), label + " scales"
+    same = gs.astype(np.float64) == ora["scale"]
+    gi = T.tile_rows(T.host(g["idx"]), n, tiles)
+    gc = T.tile_rows(T.u32(g["coset"]), g["coset"].shape[1], tiles)
+    keep = np.nonzero(same)[0]
+    sub = {k: (v[keep] if isinstance(v, np.ndarray) and v.shape[:1] == (len(X),) else v)
+           for k, v in ora.items()}
+    bad, near, total, ok = T.compare_indices(gi[keep], gc[keep], sub, lattice, n, label)
+    gk = T.host(g["rice_k"]).reshape(-1)
+    gb = T.u32(g["tile_bits"]).reshape(-1)
+    if tiles is not None:
+        gk, gb = gk[tiles], gb[tiles]
+    assert np.array_equal(gk[keep][ok], sub["rice_k"][ok]), label + " rice_k"
+    assert np.array_equal(gb[keep][ok], sub["tile_bits"][ok]), label + " tile_bits"
+    gco = T.tile_rows(T.host(g["coords"]), n, tiles)
+    assert np.array_equal(gco[keep][ok], sub["coords"][ok]), label + " coords"
+    say("%s: tiles %d, scale-boundary skips %d, blocks %d, mismatches %d, near-ties %d"
+        % (label, len(X), int(skip.sum()), total, bad, near))
+    return ora
+
+
+def check_decode(ora, lattice, n, seed, label="", exact=True, dither_seed=None, dither_base=0):
+    Tn = ora["idx"].shape[0]
+    idx = torch.from_numpy(ora["idx"].astype(np.int8)).cuda()
+    cw = ora["coset"].astype(np.uint32)
+    coset = torch.from_numpy(cw.view(np.int32)).cuda() if cw.size else None
+    scale = torch.from_numpy(ora["scale"].astype(np.float32)).cuda()
+    for out_dtype, bf in ((torch.float32, False), (torch.bfloat16, True)):
+        y = hq.hq_decode_tiles(idx, coset, scale, lattice, n, seed, out_dtype,
+                               dither_seed=dither_seed, dither_base=dither_base)
+        torch.cuda.synchronize()
+        g = (T.host(y) if not bf else codec.bf16_from_bits(T.bf16_host_bits(y))).reshape(Tn, n)
+        o = T.oracle_decode_like_gpu(ora["idx"], cw if cw.size else None, ora["scale"],
+                                     lattice, n, seed, bf, dither_seed, dither_base)
+        T.compare_decoded(g, o, ora["scale"], bf, exact, "%s decode %s" % (label, out_dtype))
+
+
+def check_rate(ora, lattice, n, label=""):
+    idx = torch.from_numpy(ora["idx"].astype(np.int8)).cuda()
+    cw = ora["coset"].astype(np.uint32)
+    coset = torch.from_numpy(cw.view(np.int32)).cuda() if cw.size else None
+    r = hq.hq_rate(idx, coset, lattice, n, pack=True)
+    torch.cuda.synchronize()
+    k, tb, total, words, off = codec.rate(ora["idx"], cw, lattice, n)
+    assert np.array_equal(T.host(r["rice_k"]).astype(np.int64), k), label + " k"
+    assert np.array_equal(T.u32(r["tile_bits"]).astype(np.int64), tb), label + " bits"
+    assert int(T.host(r["total_bits"])[0]) == total, label + " total"
+    goff = T.host(r["tile_word_offset"])
+    assert np.array_equal(goff, off), label + " offsets"
+    assert np.array_equal(T.u32(r["stream"])[:off[-1]], words), label + " stream"
+
+
+# ------------------------------------------------------------------ tests
+
+def test_small_fp32_e8_full_parity():
+    """1024x1024 fp32 N(0,1), tiles of 256, RHT seed 1, E8 at 4 bps."""
+    x = workloads.small_fp32()
+    say("case: small fp32 E8/256 R=4 seed 1")
+    ora = check_encode(x, T.f32_device(x), "E8", 256, 4.0, 1, label="small_fp32")
+    check_decode(ora, "E8", 256, 1, "small_fp32")
+    check_rate(ora, "E8", 256, "small_fp32")
+    # explicit oracle scales give the same indices
+    g = hq.hq_encode_tiles(T.f32_device(x), "E8", 256, 4.0, 1,
+                           scale=torch.from_numpy(ora["scale"].astype(np.float32)).cuda())
+    torch.cuda.synchronize()
+    T.compare_indices(T.host(g["idx"]).reshape(-1, 256), T.u32(g["coset"]), ora, "E8", 256,
+                      "small_fp32 explicit")
+
+
+@pytest.mark.parametrize("lattice,n", [("E8", 256), ("E8", 128), ("D4", 128), ("D4", 256),
+                                       ("A2", 128), ("A2", 256), ("Z", 128), ("Z", 256)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_lattices_tile_sizes_ragged(lattice, n, dtype):
+    """Every lattice x tile size on a small bf16 / fp32 matrix whose tile
+    count leaves a ragged final block."""
+    rows, cols = 37, 6 * n          # 222 tiles: not a multiple of 16 or 32
+    rng = np.random.default_rng(21)
+    w = rng.standard_normal((rows, cols)) * 0.02
+    w[:, 5] *= 300.0                # an outlier column
+    if dtype == "bf16":
+        bits = workloads.f32_to_bf16_bits(w.astype(np.float32))
+        xh = workloads.bf16_bits_to_f64(bits)
+        xd = T.bf16_device(bits, (rows, cols))
+    else:
+        xh = w.astype(np.float32)
+        xd = T.f32_device(xh)
+    for bps in (2.0, 4.0):
+        label = "%s/%d %s R=%g" % (lattice, n, dtype, bps)
+        say("case:", label)
+        ora = check_encode(xh, xd, lattice, n, bps, 7, label=label)
+        check_decode(ora, lattice, n, 7, label, exact=(lattice != "A2"))
+        check_rate(ora, lattice, n, label)
+
+
+@pytest.mark.parametrize("bps", [3.0, 4.0, 5.0])
+def test_llama_layer_parity(bps):
+    """One Llama-3.1-8B-shaped layer in bf16 (outlier columns): k in full,
+    the other six projections on every 61st tile, at 3, 4 and 5 bps."""
+    for m, (name, rows, cols) in enumerate(workloads.LLAMA_LAYER):
+        bits = workloads.llama_matrix(m, layer=0)
+        xd = T.bf16_device(bits, (rows, cols))
+        xh = workloads.bf16_bits_to_f64(bits)
+        n_tiles = rows * cols // 256
+        tiles = None if name == "k" else np.arange(0, n_tiles, 61)
+        label = "layer0.%s R=%g" % (name, bps)
+        say("case:", label)
+        ora = check_encode(xh, xd, "E8", 256, bps, 0, tiles=tiles, label=label)
+        if name in ("k", "down"):
+            check_decode(ora, "E8", 256, 0, label)
+            check_rate(ora, "E8", 256, label)
+        del xd
+
+
+def test_lattice_sweep_matrix():
+    """The 4096x14336 bf16 sweep matrix: D4, A2, Z (tile 128) and E8 (tile
+    256) at 2, 3, 4 bps; every 97th tile against the oracle; full-matrix MSE
+    against the normalized-second-moment prediction."""
+    bits = workloads.sweep_matrix()
+    rows, cols = bits.shape
+    xd = T.bf16_device(bits, (rows, cols))
+    xh = workloads.bf16_bits_to_f64(bits)
+    G = {"E8": 929 / 12960, "D4": 13 / (120 * math.sqrt(2)), "A2": 5 / (36 * math.sqrt(3)),
+         "Z": 1 / 12}
+    var = float(torch.mean(xd.double() ** 2))
+    for lattice, n in (("D4", 128), ("A2", 128), ("Z", 128), ("E8", 256)):
+        for bps in (2.0, 3.0, 4.0):
+            label = "sweep %s/%d R=%g" % (lattice, n, bps)
+            say("case:", label)
+            tiles = np.arange(0, rows * cols // n, 97)
+            ora = check_encode(xh, xd, lattice, n, bps, 1, tiles=tiles, label=label)
+            check_decode(ora, lattice, n, 1, label, exact=(lattice != "A2"))
+            g = hq.hq_encode_tiles(xd, lattice, n, bps, 1)
+            y = hq.hq_decode_tiles(g["idx"], g["coset"], g["scale"], lattice, n, 1, torch.float32)
+            mse = float(torch.mean((y.double() - xd.double()) ** 2)) / var
+            pred = 2 * math.pi * math.e * G[lattice] * 2 ** (-2 * bps)
+            say("  mse/var %.4e  prediction %.4e  ratio %.3f" % (mse, pred, mse / pred))
+            assert 0.75 < mse / pred < 1.3
+
+
+def test_kv_dither_parity_and_unbiasedness():
+    """K and V [8, 32768, 128] bf16 with per-channel offsets; E8, 4 bps,
+    subtractive dither (seed 2); every 509th vector against the oracle, a
+    contiguous block through the dithered decoder, and the mean query-key
+    error over 4096 queries."""
+    kb, vb = workloads.kv_layer()
+    nvec = kb.shape[0] * kb.shape[1]
+    for name, bits, base in (("K", kb, 0), ("V", vb, nvec)):
+        xd = T.bf16_device(bits, (nvec, 128))
+        xh = workloads.bf16_bits_to_f64(bits).reshape(nvec, 128)
+        say("case: kv", name)
+        g = hq.hq_kv_encode(xd, 4.0, 1, dither_seed=2, dither_base=base)
+        torch.cuda.synchronize()
+        sample = np.arange(0, nvec, 509)[:300]
+        # the oracle encodes each sampled vector with its own global index
+        parts = [codec.encode(xh[i:i + 1], "E8", 128, 4.0, rht_seed=1, dither_seed=2,
+                              dither_base=base + int(i)) for i in sample]
+        ora = {k: np.concatenate([o[k] for o in parts])
+               for k in ("scale", "idx", "coset", "rice_k", "tile_bits", "margin")}
+        assert np.array_equal(T.host(g["scale"])[sample].astype(np.float64), ora["scale"])
+        T.compare_indices(T.host(g["idx"])[sample], T.u32(g["coset"])[sample], ora, "E8", 128,
+                          "kv %s" % name)
+        assert np.array_equal(T.host(g["rice_k"])[sample], ora["rice_k"])
+        assert np.array_equal(T.u32(g["tile_bits"])[sample], ora["tile_bits"])
+        # contiguous block through both dithered decoders
+        blk = slice(1000, 1512)
+        ora = codec.encode(xh[blk], "E8", 128, 4.0, rht_seed=1, dither_seed=2,
+                           dither_base=base + 1000)
+        check_decode(ora, "E8", 128, 1, "kv %s" % name, exact=True, dither_seed=2,
+                     dither_base=base + 1000)
+    # unbiasedness of q . (k_hat - k)
+    xd = T.bf16_device(kb, (nvec, 128))
+    q = torch.from_numpy(workloads.kv_queries()).cuda()
+    res = {}
+    for mode, ds in (("dither", 2), ("rotation-only", None)):
+        g = hq.hq_kv_encode(xd, 4.0, 1, dither_seed=ds, dither_base=0)
+        y = hq.hq_decode_tiles(g["idx"], g["coset"], g["scale"], "E8", 128, 1, torch.float32,
+                               dither_seed=ds, dither_base=0)
+        err = (y.double() - xd.double()).reshape(8, -1, 128)
+        qbar = q.mean(0)
+        stat = float((err.mean(1) @ qbar).mean())            # mean over h, j, t of q_j . e
+        per_tok = (err @ qbar).reshape(-1)
+        se = float(per_tok.std() / math.sqrt(per_tok.numel()))
+        # per-query bias z-scores b_j = q_j . mean(e) against their null spread
+        e2 = err.reshape(-1, 128)
+        b = q @ e2.mean(0)
+        null_sd = torch.sqrt((q * q) @ (e2.var(0) / e2.shape[0]))
+        z = (b / null_sd).abs()
+        res[mode] = (stat, se, float(z.mean()), float(z.max()))
+        say("  %s: mean q.e %.3e  SE %.3e  per-query |z| mean %.2f max %.2f" % ((mode,) + res[mode]))
+    stat, se, _, _ = res["dither"]
+    assert abs(stat) <= 4 * se
+
+
+def test_edge_cases_and_status_bits():
+    dev = torch.device("cuda")
+    # empty input: no-op
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device=dev)
+    g = hq.hq_encode_tiles(x, "E8", 256, 4.0, 0)
+    assert g["idx"].numel() == 0
+    # zero tiles -> scale 1, zero indices; a single tile; odd shapes
+    x = torch.zeros((1, 512), dtype=torch.bfloat16, device=dev)
+    g = hq.hq_encode_tiles(x, "E8", 256, 4.0, 0)
+    torch.cuda.synchronize()
+    assert np.all(T.host(g["scale"]) == 1.0) and not T.host(g["idx"]).any()
+    # non-finite input sets the status bit
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    x = torch.randn((2, 256), device=dev).to(torch.bfloat16)
+    x[1, 17] = float("nan")
+    hq.hq_encode_tiles(x, "E8", 256, 4.0, 0, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & hq.HQ_ST_NONFINITE
+    # an explicit scale far too small overflows the int8 indices
+    st.zero_()
+    x = torch.randn((1, 256), device=dev).to(torch.bfloat16)
+    hq.hq_encode_tiles(x, "E8", 256, 4.0, 0, scale=torch.full((1,), 1e-4, device=dev),
+                       status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & hq.HQ_ST_OVERFLOW
+    # a packed stream with too little capacity
+    st.zero_()
+    x = torch.randn((4, 1024), device=dev).to(torch.bfloat16)
+    g = hq.hq_encode_tiles(x, "E8", 256, 4.0, 0)
+    r = hq.hq_rate(g["idx"], g["coset"], "E8", 256, pack=True, capacity_words=40, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & hq.HQ_ST_STREAM_FULL
+    # auto scale outside the int8 range is refused before launch
+    with pytest.raises(hq.HQError) as e:
+        hq.hq_encode_tiles(x, "E8", 256, 6.0, 0)
+    assert e.value.code == hq.HQ_ERANGE
+
+
+def test_bitwise_determinism():
+    bits = workloads.llama_matrix(1, layer=3)
+    xd = T.bf16_device(bits, bits.shape)
+    a = hq.hq_encode_tiles(xd, "E8", 256, 4.0, 3)
+    b = hq.hq_encode_tiles(xd, "E8", 256, 4.0, 3)
+    ya = hq.hq_decode_tiles(a["idx"], a["coset"], a["scale"], "E8", 256, 3)
+    yb = hq.hq_decode_tiles(b["idx"], b["coset"], b["scale"], "E8", 256, 3)
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+    assert torch.equal(ya.view(torch.int16), yb.view(torch.int16))
