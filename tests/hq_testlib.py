@@ -58,33 +58,36 @@ def compare_indices(g_idx, g_coset, ora, lattice, n, label=""):
     return int(bad.sum()), int(near.sum()), int(bad.size), tiles_ok
 
 
-def compare_decoded(g_vals, o_vals, scale, out_bf16, exact, label=""):
-    """|gpu - oracle| <= 1e-5 * Delta (+ half a bf16 ulp of the oracle for
-    bf16 outputs); `exact` additionally demands bit equality."""
+def compare_decoded(g_vals, o_round, o_raw, scale, out_bf16, exact, label=""):
+    """|gpu - oracle fp64| <= 1e-5 * Delta, plus half a bf16 ulp of the
+    oracle value for bf16 outputs (the output rounding); `exact` additionally
+    demands bit equality with the identically rounded oracle value."""
     g = np.asarray(g_vals, np.float64)
-    o = np.asarray(o_vals, np.float64)
+    raw = np.asarray(o_raw, np.float64)
     tol = 1e-5 * np.asarray(scale, np.float64)[:, None]
     if out_bf16:
-        ulp = np.abs(o) * 2.0 ** -7
-        tol = tol + 0.5 * ulp
-    err = np.abs(g - o)
-    assert np.all(err <= tol), "%s: max err / Delta %.3g" % (label, np.max(err / np.asarray(scale)[:, None]))
+        tol = tol + 0.5 * np.abs(raw) * 2.0 ** -7
+    err = np.abs(g - raw)
+    assert np.all(err <= tol), "%s: max err / Delta %.3g" % (
+        label, np.max(err / np.asarray(scale)[:, None]))
     if exact:
+        o = np.asarray(o_round, np.float64)
         assert np.array_equal(g, o), "%s: %d values differ" % (label, int(np.sum(g != o)))
 
 
-def oracle_decode_like_gpu(g_idx, g_coset, g_scale, lattice, n, seed, out_bf16,
+def oracle_decode_like_gpu(idx, coset, scale, lattice, n, seed, out_bf16,
                            dither_seed=None, dither_base=0):
-    """Oracle decode of the GPU's own indices, rounded like the output."""
-    T = np.asarray(g_idx).size // n
-    x = codec.decode(np.asarray(g_idx, np.int64).reshape(T, n),
-                     np.asarray(g_coset).reshape(T, -1).astype(np.uint32) if g_coset is not None
+    """Oracle decode of the given (oracle) indices: (value rounded like the
+    output, unrounded fp64 value)."""
+    T = np.asarray(idx).size // n
+    x = codec.decode(np.asarray(idx, np.int64).reshape(T, n),
+                     np.asarray(coset).reshape(T, -1).astype(np.uint32) if coset is not None
                      else np.zeros((T, 0), np.uint32),
-                     np.asarray(g_scale, np.float64), lattice, n, seed,
+                     np.asarray(scale, np.float64), lattice, n, seed,
                      dither_seed=dither_seed, dither_base=dither_base)
     if out_bf16:
-        return codec.bf16_rne(x)
-    return x.astype(np.float32).astype(np.float64)
+        return codec.bf16_rne(x), x
+    return x.astype(np.float32).astype(np.float64), x
 
 
 def rice_pack_oracle(idx, coset_words, lattice, n):

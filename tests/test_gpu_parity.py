@@ -83,9 +83,9 @@ def check_decode(ora, lattice, n, seed, label="", exact=True, dither_seed=None, 
                                dither_seed=dither_seed, dither_base=dither_base)
         torch.cuda.synchronize()
         g = (T.host(y) if not bf else codec.bf16_from_bits(T.bf16_host_bits(y))).reshape(Tn, n)
-        o = T.oracle_decode_like_gpu(ora["idx"], cw if cw.size else None, ora["scale"],
-                                     lattice, n, seed, bf, dither_seed, dither_base)
-        T.compare_decoded(g, o, ora["scale"], bf, exact, "%s decode %s" % (label, out_dtype))
+        o, raw = T.oracle_decode_like_gpu(ora["idx"], cw if cw.size else None, ora["scale"],
+                                          lattice, n, seed, bf, dither_seed, dither_base)
+        T.compare_decoded(g, o, raw, ora["scale"], bf, exact, "%s decode %s" % (label, out_dtype))
 
 
 def check_rate(ora, lattice, n, label=""):
