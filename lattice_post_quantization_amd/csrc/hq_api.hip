@@ -108,6 +108,7 @@ hq_status check_encode(const hq_params* p, const void* x, int32_t x_dtype, int64
   if (x_dtype != HQ_F32 && x_dtype != HQ_BF16) return HQ_EINVAL;
   if (rows < 0 || cols < 0) return HQ_EINVAL;
   if (cols % p->tile != 0) return HQ_EINVAL;
+  if (rows == 0 || cols == 0) return HQ_OK;   // zero tiles: a no-op, buffers unused
   if (x == nullptr || scale == nullptr || idx == nullptr || rice_k == nullptr ||
       tile_bits == nullptr)
     return HQ_EINVAL;
@@ -208,6 +209,7 @@ hq_status hq_decode_tiles(const hq_params* p, const int8_t* idx, const uint32_t*
   if (st != HQ_OK) return st;
   if (y_dtype != HQ_F32 && y_dtype != HQ_BF16) return HQ_EINVAL;
   if (rows < 0 || cols < 0 || cols % p->tile != 0) return HQ_EINVAL;
+  if (rows == 0 || cols == 0) return HQ_OK;   // zero tiles: a no-op
   if (idx == nullptr || scale == nullptr || y == nullptr) return HQ_EINVAL;
   if (coset_words(p) > 0 && coset == nullptr) return HQ_EINVAL;
   if (!aligned16(idx) || !aligned16(y)) return HQ_EINVAL;
@@ -251,6 +253,7 @@ hq_status hq_rate(const hq_params* p, const int8_t* idx, const uint32_t* coset, 
   hq_status st = check_params(p);
   if (st != HQ_OK) return st;
   if (n_tiles < 0) return HQ_EINVAL;
+  if (n_tiles == 0) return HQ_OK;   // zero tiles: a no-op (nothing is written)
   if (idx == nullptr || rice_k == nullptr || tile_bits == nullptr || total_bits == nullptr)
     return HQ_EINVAL;
   if (!aligned16(idx) || ((uintptr_t)total_bits & 7u)) return HQ_EINVAL;

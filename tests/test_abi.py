@@ -158,3 +158,19 @@ def test_no_cpu_fallback_in_the_binding():
     src = open(hq.__file__).read()
     assert "oracle" not in src.replace("oracle-free", "")
     assert not math.isnan(hq.scale_constant("E8", 4.0))
+
+
+def test_zero_tiles_is_a_noop_even_with_null_buffers():
+    lib = hq.lib()
+    p = hq.make_params("E8", 256, 4.0, 0, hq.HQ_SCALE_AUTO)
+    assert lib.hq_encode_tiles(ctypes.byref(p), None, 1, 0, 256, None, None, None, None, None,
+                               None, None, None) == hq.HQ_OK
+    assert lib.hq_decode_tiles(ctypes.byref(p), None, None, None, 0, 256, None, 1, None,
+                               None) == hq.HQ_OK
+    assert lib.hq_rate(ctypes.byref(p), None, None, 0, None, None, None, None, 0, None, None, 0,
+                       None, None) == hq.HQ_OK
+    assert lib.hq_kv_encode(ctypes.byref(p), None, 1, 0, None, None, None, None, None, None,
+                            None) == hq.HQ_OK
+    # still validated: a negative size or a bad tile is an error
+    assert lib.hq_encode_tiles(ctypes.byref(p), None, 1, 0, 100, None, None, None, None, None,
+                               None, None, None) == hq.HQ_EINVAL
