@@ -196,6 +196,7 @@ hipError_t launch_lat(const DecodeLaunch& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t s) {
+  if (e8_fast_decode_ok(a)) return launch_decode_e8_fast(a, s);
   switch (a.lattice) {
     case 8: return launch_lat<8>(a, s);
     case 4: return launch_lat<4>(a, s);

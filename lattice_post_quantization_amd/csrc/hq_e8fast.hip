@@ -1,0 +1,566 @@
+// Fast path for the headline configuration: E8, tile 256, bf16 weights in,
+// bf16 or fp32 weights out, no dither.  Same results as the generic kernels,
+// bit for bit; laid out for gfx950.
+//
+// Passages: [arXiv abstract] "HyperQuant: A Rate-Distortion-Optimal
+// Quantization Pipeline ..." ideas (i)-(iii); [ICLR abstract] "HyperQuant: A
+// Near-Entropy-Optimal Lattice Quantization Pipeline ..." (Walsh-Hadamard
+// rotation per tile, E8 by default, lossless strip, Rice code, algebraic
+// decoding).
+//
+// Work mapping.  A wave holds 16 tiles.  Lane (t, r) = lane t + 16 r of the
+// wave holds elements [64 r, 64 r + 64) of tile t, so a tile spans the four
+// 16-lane rows and every lane keeps 64 elements in registers.  Element bits
+// 0-5 are register bits: six Walsh-Hadamard stages run inside the lane.
+// Element bits 6 and 7 are the row bits; v_permlane16_swap / v_permlane32_swap
+// exchange a row bit with a register bit (one instruction per dword pair),
+// after which those two stages also run in registers.  Reductions over a tile
+// use the same swaps.  No LDS traffic apart from a 512-byte sign table.
+#include "hq.h"
+#include "hq_device.h"
+#include "hq_internal.h"
+
+namespace hq {
+namespace {
+
+// 1.5 * 2^52: adding it to |q| < 2^51 rounds q to an integer (ties to even)
+// that sits in the low mantissa bits.
+constexpr double kMagic = 6755399441055744.0;
+
+__device__ inline void swap16(uint32_t& a, uint32_t& b) {
+  auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+
+__device__ inline void swap32(uint32_t& a, uint32_t& b) {
+  auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+
+template <bool ROW32>
+__device__ inline void swap_f64(double& a, double& b) {
+  uint64_t ua = (uint64_t)__double_as_longlong(a), ub = (uint64_t)__double_as_longlong(b);
+  uint32_t alo = (uint32_t)ua, ahi = (uint32_t)(ua >> 32);
+  uint32_t blo = (uint32_t)ub, bhi = (uint32_t)(ub >> 32);
+  if (ROW32) {
+    swap32(alo, blo);
+    swap32(ahi, bhi);
+  } else {
+    swap16(alo, blo);
+    swap16(ahi, bhi);
+  }
+  a = __longlong_as_double((long long)(((uint64_t)ahi << 32) | alo));
+  b = __longlong_as_double((long long)(((uint64_t)bhi << 32) | blo));
+}
+
+// Sum / OR of a value over the four lanes (rows) that hold one tile.
+__device__ inline uint32_t tile_sum_u32(uint32_t v) {
+  uint32_t a = v, b = v;
+  swap16(a, b);
+  v = a + b;
+  a = v;
+  b = v;
+  swap32(a, b);
+  return a + b;
+}
+
+__device__ inline uint32_t tile_or_u32(uint32_t v) {
+  uint32_t a = v, b = v;
+  swap16(a, b);
+  v = a | b;
+  a = v;
+  b = v;
+  swap32(a, b);
+  return a | b;
+}
+
+__device__ inline double tile_sum_f64(double v) {
+  double a = v, b = v;
+  swap_f64<false>(a, b);
+  v = a + b;
+  a = v;
+  b = v;
+  swap_f64<true>(a, b);
+  return a + b;
+}
+
+// Sign table: for row r and element pair p (elements 64 r + 2p, 64 r + 2p + 1)
+// the bf16-pair XOR mask (bit 15: first element, bit 31: second).
+__device__ inline void fill_sign_table(uint32_t* tab, const uint32_t* signs) {
+  for (int i = threadIdx.x; i < 128; i += kBlock) {
+    const int e = 2 * i;   // row r = i / 32, pair p = i % 32 -> element 64 r + 2 p = 2 i
+    uint32_t w0 = signs[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) w0 = ((e >> 5) == k) ? signs[k] : w0;
+    const uint32_t b0 = (w0 >> (e & 31)) & 1u, b1 = (w0 >> ((e + 1) & 31)) & 1u;
+    tab[i] = (b0 << 15) | (b1 << 31);
+  }
+}
+
+// ------------------------------------------------------------------ E8 block
+// Nearest E8 point for one block of grid values U (units of 2^-24), exact.
+// Fast path: with F_i = U_i mod 2^24, I_i = floor(U_i / 2^24), B_i = |F_i - 2^23|
+// (distance to the nearest half-integer; the distance to the nearest integer
+// is 2^23 - B_i), and no coordinate exactly on an integer or half-integer:
+//   integer coset a_i = I_i + [F_i > 2^23], half coset b_i = I_i (+ 1/2),
+//   parity fixes on the first max/min of B, coset choice by
+//   D = 2^25 - sum B + [odd a] 2 min B - [odd b] (2^24 - 2 max B) > 0.
+// Blocks with a coordinate on an integer or half-integer take the general
+// decoder (rare; same results).  Writes the stored integers (z0..z6,
+// floor(z7/2)) and returns the coset bit.
+__device__ inline int e8_block(const int32_t* U, int32_t* s) {
+  int32_t I[8], E[8];
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  int32_t sumB = 0, xi = 0, xe = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int32_t F = U[i] & 0xFFFFFF;
+    I[i] = U[i] >> 24;
+    E[i] = kHalf - F;
+    const uint32_t B = (uint32_t)(E[i] < 0 ? -E[i] : E[i]);
+    sumB += (int32_t)B;
+    const uint32_t k1 = (B << 3) | (uint32_t)i, k2 = (B << 3) | (uint32_t)(7 - i);
+    kmin = k1 < kmin ? k1 : kmin;
+    kmax = k2 > kmax ? k2 : kmax;
+    xi ^= I[i];
+    xe ^= E[i];
+  }
+  const int32_t bmin = (int32_t)(kmin >> 3), bmax = (int32_t)(kmax >> 3);
+  if (bmin == 0 || bmax == kHalf) {
+    int32_t z[8];
+    const int c = e8_nearest(U, z);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s[i] = (i == 7) ? (z[i] >> 1) : z[i];
+    return c;
+  }
+  const int ja = (int)(kmin & 7u), jb = 7 - (int)(kmax & 7u);
+  const int odd_b = xi & 1, odd_a = (xi ^ (int32_t)((uint32_t)xe >> 31)) & 1;
+  const int32_t D = (1 << 25) - sumB + (odd_a ? 2 * bmin : 0) -
+                    (odd_b ? (1 << 24) - 2 * bmax : 0);
+  const int c = D > 0;
+  const int jf = c ? jb : ja;
+  const int fodd = c ? odd_b : odd_a;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int32_t up = (int32_t)((uint32_t)E[i] >> 31);   // F_i > 2^23
+    int32_t z = I[i] + (c ? 0 : up);
+    // coset a: move towards u (+1 when u_j is above a_j); coset b: likewise
+    const int32_t step = c ? (up ? 1 : -1) : (up ? -1 : 1);
+    z += (fodd && i == jf) ? step : 0;
+    s[i] = (i == 7) ? (z >> 1) : z;
+  }
+  return c;
+}
+
+__device__ inline uint32_t pack4(const int32_t* s) {
+  return ((uint32_t)s[0] & 0xFFu) | (((uint32_t)s[1] & 0xFFu) << 8) |
+         (((uint32_t)s[2] & 0xFFu) << 16) | ((uint32_t)s[3] << 24);
+}
+
+// zigzag of four int8 values held in a dword, bytewise
+__device__ inline uint32_t zigzag4(uint32_t d) {
+  const uint32_t sgn = (d >> 7) & 0x01010101u;
+  return ((d << 1) & 0xFEFEFEFEu) ^ (sgn * 0xFFu);
+}
+
+__device__ inline uint32_t byte_sum(uint32_t d, uint32_t acc) {
+  return __builtin_amdgcn_sad_u8(d, 0u, acc);
+}
+
+__global__ __launch_bounds__(kBlock) void encode_e8_fast(EncodeLaunch a) {
+  __shared__ uint32_t sign_tab[128];
+  fill_sign_table(sign_tab, a.signs);
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int t = lane & 15, row = lane >> 4;
+  const int64_t group = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+  if (group * 16 >= a.n_tiles) return;               // whole wave past the end
+  const int64_t tile_raw = group * 16 + t;
+  const bool live = tile_raw < a.n_tiles;
+  const int64_t tile = live ? tile_raw : a.n_tiles - 1;   // ragged end: recompute a valid tile
+
+  // ---- load 64 bf16 (128 bytes) and apply the RHT signs in the bf16 domain
+  const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) +
+                                                    tile * 256 + row * 64);
+  uint32_t w[32];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint4 q = src[k];
+    w[4 * k] = q.x; w[4 * k + 1] = q.y; w[4 * k + 2] = q.z; w[4 * k + 3] = q.w;
+  }
+  const uint4* st = reinterpret_cast<const uint4*>(sign_tab + row * 32);
+  double v[64];
+  double ss = 0.0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint4 m = st[k];
+    const uint32_t mm[4] = {m.x, m.y, m.z, m.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t d = w[4 * k + j] ^ mm[j];
+      const double lo = (double)__uint_as_float(d << 16);
+      const double hi = (double)__uint_as_float(d & 0xFFFF0000u);
+      v[8 * k + 2 * j] = lo;
+      v[8 * k + 2 * j + 1] = hi;
+      ss = fma(lo, lo, ss);
+      ss = fma(hi, hi, ss);
+    }
+  }
+
+  // ---- scale: bf16_rne(rms * c) (auto) or the caller's; the norm bound
+  // sqrt(sum x^2)/Delta < 126 keeps every grid value in range
+  ss = tile_sum_f64(ss);
+  uint32_t status = 0;
+  float delta;
+  if (a.auto_scale) {
+    delta = bf16_round_to_f32(sqrt(ss / 256.0) * a.c);
+    if (delta == 0.0f) delta = 1.0f;
+  } else {
+    delta = a.scale[tile];
+    if (!(delta > 0.0f) || !isfinite(delta)) status |= HQ_ST_NONFINITE;
+  }
+  if (!isfinite(ss)) status |= HQ_ST_NONFINITE;
+  if (!(sqrt(ss) < 126.0 * (double)delta)) status |= HQ_ST_OVERFLOW;
+  const double K = 16777216.0 / (a.sqrt_n * (double)delta);
+
+  // ---- Walsh-Hadamard: element bits 0-5 in registers
+#pragma unroll
+  for (int h = 1; h < 64; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      if (!(i & h)) {
+        const double x = v[i], y = v[i + h];
+        v[i] = x + y;
+        v[i + h] = x - y;
+      }
+    }
+  }
+  // element bit 6 (row bit 0) <-> register bit 5, then butterfly
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    swap_f64<false>(v[i], v[i + 32]);
+    const double x = v[i], y = v[i + 32];
+    v[i] = x + y;
+    v[i + 32] = x - y;
+  }
+  // element bit 7 (row bit 1) <-> register bit 4, then butterfly
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    if (!(i & 16)) {
+      swap_f64<true>(v[i], v[i + 16]);
+      const double x = v[i], y = v[i + 16];
+      v[i] = x + y;
+      v[i + 16] = x - y;
+    }
+  }
+  // Now register i holds element bits (i0 i1 i2 i3 | i4 = b7 | i5 = b6) and the
+  // lane's row bits hold (r0 = b5, r1 = b4).
+
+  // ---- quantizer input U = rne(S K) (units of 2^-24), stored integers
+  uint32_t packed[16];
+  uint32_t cbits = 0;
+  const int r0 = row & 1, r1 = row >> 1;
+#pragma unroll
+  for (int blk = 0; blk < 8; ++blk) {
+    int32_t U[8], s[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      // two roundings, never fused: q = RN(S K), then RN(q + 1.5 2^52)
+      const double m = __dadd_rn(__dmul_rn(v[8 * blk + i], K), kMagic);
+      U[i] = (int32_t)(uint32_t)(uint64_t)__double_as_longlong(m);
+    }
+    const int c = e8_block(U, s);
+    // tile block index = b3 + 2 b4 + 4 b5 + 8 b6 + 16 b7
+    const int bpos = (blk & 1) + 2 * r1 + 4 * r0 + 8 * (blk >> 2) + 16 * ((blk >> 1) & 1);
+    cbits |= (uint32_t)c << bpos;
+    packed[2 * blk] = pack4(s);
+    packed[2 * blk + 1] = pack4(s + 4);
+  }
+  const uint32_t coset_word = tile_or_u32(cbits);
+
+  // ---- Rice parameter: k = argmin_k sum(floor(zeta/2^k)) + 256 (1 + k).
+  // With S = sum zeta and kt the smallest k with S <= 256 * 2^(k+1), only
+  // kt - 1 .. kt + 2 can be optimal (convexity bound); k >= 9 never is.
+  uint32_t zz[16];
+  uint32_t S = 0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    zz[q] = zigzag4(packed[q]);
+    S = byte_sum(zz[q], S);
+  }
+  S = tile_sum_u32(S);
+  int kt = 0;
+  while (kt < 8 && S > (256u << (kt + 1))) ++kt;
+  int kc[4];
+  uint32_t R[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int k = kt - 1 + j;
+    kc[j] = k < 0 ? 0 : (k > 8 ? 8 : k);
+    const uint32_t mask = ((1u << kc[j]) - 1u) * 0x01010101u;
+    uint32_t r = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) r = byte_sum(zz[q] & mask, r);
+    R[j] = r;
+  }
+  uint32_t best = 0xFFFFFFFFu;
+  int bk = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t Rk = tile_sum_u32(R[j]);
+    const uint32_t L = ((S - Rk) >> kc[j]) + 256u * (uint32_t)(1 + kc[j]);
+    if (L < best) { best = L; bk = kc[j]; }
+  }
+
+  // ---- restore natural element order (undo the two swaps) and store
+#pragma unroll
+  for (int q = 0; q < 16; ++q)
+    if (!(q & 4)) swap32(packed[q], packed[q + 4]);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) swap16(packed[q], packed[q + 8]);
+  if (live) {
+    uint4* dst = reinterpret_cast<uint4*>(a.idx + tile * 256 + row * 64);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      dst[k] = make_uint4(packed[4 * k], packed[4 * k + 1], packed[4 * k + 2], packed[4 * k + 3]);
+    if (row == 0) {
+      if (a.auto_scale) a.scale[tile] = delta;
+      a.coset[tile] = coset_word;
+      a.rice_k[tile] = (uint8_t)bk;
+      a.tile_bits[tile] = 4u + 32u + best;
+      if (status) set_status(a.status, status);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ decode
+// Integer Hadamard on P = 2p in packed int16 pairs (2 elements per register);
+// exact while sum |P| <= 32767, which every tile of encoder output satisfies
+// (|P_i| stays far below that bound); otherwise the tile runs the same
+// transform in fp32 (exact for |values| < 2^24).  Then
+// x = s * (H P) * (Delta / 32) is exact in fp32 and rounded once to the output.
+
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+__device__ inline s16x2 as_s16x2(uint32_t u) { return __builtin_bit_cast(s16x2, u); }
+__device__ inline uint32_t as_u32(s16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// in-dword butterfly: (lo, hi) -> (lo + hi, lo - hi)
+__device__ inline uint32_t half_butterfly(uint32_t x) {
+  const s16x2 p = as_s16x2(x);
+  const s16x2 hh = __builtin_shufflevector(p, p, 1, 1);
+  const s16x2 ll = __builtin_shufflevector(p, p, 0, 0);
+  return as_u32(hh * (s16x2){1, -1} + ll);
+}
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(kBlock) void decode_e8_fast(DecodeLaunch a) {
+  __shared__ uint32_t sign_tab[128];
+  fill_sign_table(sign_tab, a.signs);
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int t = lane & 15, row = lane >> 4;
+  const int64_t group = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+  if (group * 16 >= a.n_tiles) return;
+  const int64_t tile_raw = group * 16 + t;
+  const bool live = tile_raw < a.n_tiles;
+  const int64_t tile = live ? tile_raw : a.n_tiles - 1;
+
+  const uint4* src = reinterpret_cast<const uint4*>(a.idx + tile * 256 + row * 64);
+  uint32_t d[16];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint4 q = src[k];
+    d[4 * k] = q.x; d[4 * k + 1] = q.y; d[4 * k + 2] = q.z; d[4 * k + 3] = q.w;
+  }
+  const uint32_t cw = a.coset[tile] >> (8 * row);   // this lane's 8 blocks
+  const float dsc = a.scale[tile] * 0.03125f;        // Delta / 32, exact
+
+  // bound for the int16 path: sum |P| <= 4 sum|stored| + 320 (|z7| <= 2|t7| + 1)
+  uint32_t sabs = 0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) sabs = __builtin_amdgcn_sad_u8(d[q] ^ 0x80808080u, 0x80808080u, sabs);
+  sabs = tile_sum_u32(sabs);
+  const bool small = sabs <= 8111u;
+
+  // ---- unstrip into P = 2z + c as int16 pairs: P2[m] = (P_2m, P_2m+1)
+  uint32_t P2[32];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const uint32_t d0 = d[2 * b], d1 = d[2 * b + 1];
+    uint32_t x = d0 ^ (d1 & 0x00FFFFFFu);
+    x ^= x >> 16;
+    x ^= x >> 8;
+    const uint32_t par = x & 1u;
+    const uint32_t c = (cw >> b) & 1u;
+    // sign-extended int16 pairs (z0,z1) (z2,z3) from d0 and (z4,z5) (z6,t7) from d1
+    const uint32_t e0 = d0 << 8, e1 = d1 << 8;
+    const uint32_t p01 = __builtin_amdgcn_perm(d0, e0, 0x0A050804u);
+    const uint32_t p23 = __builtin_amdgcn_perm(d0, e0, 0x0B070906u);
+    const uint32_t p45 = __builtin_amdgcn_perm(d1, e1, 0x0A050804u);
+    const uint32_t p67 = __builtin_amdgcn_perm(d1, e1, 0x0B070906u);
+    const s16x2 cc = (s16x2){(short)c, (short)c};
+    // z7 = 2 t7 + par: P7 = 4 t7 + 2 par + c
+    const s16x2 c7 = (s16x2){(short)c, (short)(c + 2 * par)};
+    P2[4 * b] = as_u32(as_s16x2(p01) * (s16x2){2, 2} + cc);
+    P2[4 * b + 1] = as_u32(as_s16x2(p23) * (s16x2){2, 2} + cc);
+    P2[4 * b + 2] = as_u32(as_s16x2(p45) * (s16x2){2, 2} + cc);
+    P2[4 * b + 3] = as_u32(as_s16x2(p67) * (s16x2){2, 4} + c7);
+  }
+
+  float y[64];
+  if (small) {
+    // element bit 0: inside each dword
+#pragma unroll
+    for (int m = 0; m < 32; ++m) P2[m] = half_butterfly(P2[m]);
+    // element bits 1-5: dword index bits 0-4
+#pragma unroll
+    for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+      for (int m = 0; m < 32; ++m) {
+        if (!(m & h)) {
+          const s16x2 x = as_s16x2(P2[m]), z = as_s16x2(P2[m + h]);
+          P2[m] = as_u32(x + z);
+          P2[m + h] = as_u32(x - z);
+        }
+      }
+    }
+    // element bit 6 (row bit 0) <-> dword bit 4; element bit 7 (row bit 1) <-> dword bit 3
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      swap16(P2[m], P2[m + 16]);
+      const s16x2 x = as_s16x2(P2[m]), z = as_s16x2(P2[m + 16]);
+      P2[m] = as_u32(x + z);
+      P2[m + 16] = as_u32(x - z);
+    }
+#pragma unroll
+    for (int m = 0; m < 32; ++m) {
+      if (!(m & 8)) {
+        swap32(P2[m], P2[m + 8]);
+        const s16x2 x = as_s16x2(P2[m]), z = as_s16x2(P2[m + 8]);
+        P2[m] = as_u32(x + z);
+        P2[m + 8] = as_u32(x - z);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < 32; ++m) {
+      y[2 * m] = (float)(short)(P2[m] & 0xFFFFu) * dsc;
+      y[2 * m + 1] = (float)((int32_t)P2[m] >> 16) * dsc;
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < 32; ++m) {
+      y[2 * m] = (float)(short)(P2[m] & 0xFFFFu);
+      y[2 * m + 1] = (float)((int32_t)P2[m] >> 16);
+    }
+#pragma unroll
+    for (int h = 1; h < 64; h <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 64; ++i) {
+        if (!(i & h)) {
+          const float x = y[i], z = y[i + h];
+          y[i] = x + z;
+          y[i + h] = x - z;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      uint32_t p = __float_as_uint(y[i]), q = __float_as_uint(y[i + 32]);
+      swap16(p, q);
+      const float x = __uint_as_float(p), z = __uint_as_float(q);
+      y[i] = x + z;
+      y[i + 32] = x - z;
+    }
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      if (!(i & 16)) {
+        uint32_t p = __float_as_uint(y[i]), q = __float_as_uint(y[i + 16]);
+        swap32(p, q);
+        const float x = __uint_as_float(p), z = __uint_as_float(q);
+        y[i] = x + z;
+        y[i + 16] = x - z;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 64; ++i) y[i] *= dsc;
+  }
+  // Register i now holds element bits (i0 .. i3, i4 = b7, i5 = b6); rows (b5, b4).
+
+  const uint4* st = reinterpret_cast<const uint4*>(sign_tab + row * 32);
+  if constexpr (OUT_BF16) {
+    uint32_t o[32];
+#pragma unroll
+    for (int m = 0; m < 32; ++m) {
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      const bf16x2 pr = {(__bf16)y[2 * m], (__bf16)y[2 * m + 1]};
+      o[m] = __builtin_bit_cast(uint32_t, pr);
+    }
+    // undo the swaps: dword bit 3 <-> row bit 1, dword bit 4 <-> row bit 0
+#pragma unroll
+    for (int m = 0; m < 32; ++m)
+      if (!(m & 8)) swap32(o[m], o[m + 8]);
+#pragma unroll
+    for (int m = 0; m < 16; ++m) swap16(o[m], o[m + 16]);
+    if (live) {
+      uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.y) + tile * 256 + row * 64);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint4 sm = st[k];
+        dst[k] = make_uint4(o[4 * k] ^ sm.x, o[4 * k + 1] ^ sm.y, o[4 * k + 2] ^ sm.z,
+                            o[4 * k + 3] ^ sm.w);
+      }
+    }
+  } else {
+    uint32_t o[64];
+#pragma unroll
+    for (int i = 0; i < 64; ++i) o[i] = __float_as_uint(y[i]);
+#pragma unroll
+    for (int i = 0; i < 64; ++i)
+      if (!(i & 16)) swap32(o[i], o[i + 16]);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) swap16(o[i], o[i + 32]);
+    if (live) {
+      uint4* dst = reinterpret_cast<uint4*>(static_cast<float*>(a.y) + tile * 256 + row * 64);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const uint32_t sm = sign_tab[row * 32 + 2 * k], sn = sign_tab[row * 32 + 2 * k + 1];
+        dst[k] = make_uint4(o[4 * k] ^ (sm << 16), o[4 * k + 1] ^ (sm & 0x80000000u),
+                            o[4 * k + 2] ^ (sn << 16), o[4 * k + 3] ^ (sn & 0x80000000u));
+      }
+    }
+  }
+}
+
+}  // namespace
+
+bool e8_fast_encode_ok(const EncodeLaunch& a) {
+  return a.lattice == 8 && a.tile == 256 && a.in_bf16 && !a.dither && a.coords == nullptr;
+}
+
+bool e8_fast_decode_ok(const DecodeLaunch& a) {
+  return a.lattice == 8 && a.tile == 256 && !a.dither;
+}
+
+hipError_t launch_encode_e8_fast(const EncodeLaunch& a, hipStream_t s) {
+  const int64_t groups = (a.n_tiles + 15) / 16;
+  const int64_t blocks = (groups + kBlock / 64 - 1) / (kBlock / 64);
+  hipLaunchKernelGGL(encode_e8_fast, dim3((unsigned)blocks), dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_e8_fast(const DecodeLaunch& a, hipStream_t s) {
+  const int64_t groups = (a.n_tiles + 15) / 16;
+  const int64_t blocks = (groups + kBlock / 64 - 1) / (kBlock / 64);
+  if (a.out_bf16)
+    hipLaunchKernelGGL(decode_e8_fast<true>, dim3((unsigned)blocks), dim3(kBlock), 0, s, a);
+  else
+    hipLaunchKernelGGL(decode_e8_fast<false>, dim3((unsigned)blocks), dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace hq

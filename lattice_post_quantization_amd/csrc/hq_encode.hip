@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeLaunch a) {
   int32_t U[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    double q = rint(v[i] * ((LAT == 2 && (i & 1)) ? K3 : K));
+    double q = rint(__dmul_rn(v[i], (LAT == 2 && (i & 1)) ? K3 : K));
     if (!(fabs(q) <= kUClamp)) {
       st |= HQ_ST_OVERFLOW;
       q = (q > 0.0) ? kUClamp : -kUClamp;
@@ -299,6 +299,7 @@ hipError_t launch_lat(const EncodeLaunch& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_encode(const EncodeLaunch& a, hipStream_t s) {
+  if (e8_fast_encode_ok(a)) return launch_encode_e8_fast(a, s);
   switch (a.lattice) {
     case 8: return launch_lat<8>(a, s);
     case 4: return launch_lat<4>(a, s);

@@ -69,6 +69,12 @@ hipError_t launch_encode(const EncodeLaunch& a, hipStream_t s);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t s);
 hipError_t launch_rate(const RateLaunch& a, hipStream_t s);
 
+// fast path for E8 / tile 256 / bf16 input (encode) and E8 / tile 256 (decode)
+bool e8_fast_encode_ok(const EncodeLaunch& a);
+bool e8_fast_decode_ok(const DecodeLaunch& a);
+hipError_t launch_encode_e8_fast(const EncodeLaunch& a, hipStream_t s);
+hipError_t launch_decode_e8_fast(const DecodeLaunch& a, hipStream_t s);
+
 // tiles handled by one rate/pack block
 constexpr int kRateTilesPerBlock = 16;
 

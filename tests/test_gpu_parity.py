@@ -41,34 +41,41 @@ def oracle_pre_scale(X, lattice, bps):
 
 def check_encode(x_host, x_dev, lattice, n, bps, seed, tiles=None, label=""):
     """Auto-scale encode on the GPU (all tiles) vs the oracle (all or the
-    sampled tiles).  Returns the oracle result of the compared tiles."""
-    g = hq.hq_encode_tiles(x_dev, lattice, n, bps, seed, want_coords=True)
-    torch.cuda.synchronize()
+    sampled tiles), through both device paths: the plain call (the fast
+    kernel where one exists) and a call that also exports coordinates (the
+    generic kernel).  Returns the oracle result of the compared tiles."""
     X = codec.tiles(x_host, n)
     if tiles is not None:
         X = X[tiles]
     ora = codec.encode(X, lattice, n, bps, rht_seed=seed)
-    gs = T.tile_rows(T.host(g["scale"]), 1, None).reshape(-1)
-    gs = gs if tiles is None else gs[tiles]
     skip = midpoint_close(oracle_pre_scale(X, lattice, bps))
-    assert np.array_equal(gs.astype(np.float64)[~skip], ora["scale"][~skip]), label + " scales"
-    same = gs.astype(np.float64) == ora["scale"]
-    gi = T.tile_rows(T.host(g["idx"]), n, tiles)
-    gc = T.tile_rows(T.u32(g["coset"]), g["coset"].shape[1], tiles)
-    keep = np.nonzero(same)[0]
-    sub = {k: (v[keep] if isinstance(v, np.ndarray) and v.shape[:1] == (len(X),) else v)
-           for k, v in ora.items()}
-    bad, near, total, ok = T.compare_indices(gi[keep], gc[keep], sub, lattice, n, label)
-    gk = T.host(g["rice_k"]).reshape(-1)
-    gb = T.u32(g["tile_bits"]).reshape(-1)
-    if tiles is not None:
-        gk, gb = gk[tiles], gb[tiles]
-    assert np.array_equal(gk[keep][ok], sub["rice_k"][ok]), label + " rice_k"
-    assert np.array_equal(gb[keep][ok], sub["tile_bits"][ok]), label + " tile_bits"
-    gco = T.tile_rows(T.host(g["coords"]), n, tiles)
-    assert np.array_equal(gco[keep][ok], sub["coords"][ok]), label + " coords"
-    say("%s: tiles %d, scale-boundary skips %d, blocks %d, mismatches %d, near-ties %d"
-        % (label, len(X), int(skip.sum()), total, bad, near))
+    for coords in (False, True):
+        g = hq.hq_encode_tiles(x_dev, lattice, n, bps, seed, want_coords=coords)
+        torch.cuda.synchronize()
+        path = "generic" if coords else "default"
+        gs = T.host(g["scale"]).reshape(-1)
+        gs = gs if tiles is None else gs[tiles]
+        assert np.array_equal(gs.astype(np.float64)[~skip], ora["scale"][~skip]), \
+            label + " scales (%s)" % path
+        same = gs.astype(np.float64) == ora["scale"]
+        gi = T.tile_rows(T.host(g["idx"]), n, tiles)
+        gc = T.tile_rows(T.u32(g["coset"]), g["coset"].shape[1], tiles)
+        keep = np.nonzero(same)[0]
+        sub = {k: (v[keep] if isinstance(v, np.ndarray) and v.shape[:1] == (len(X),) else v)
+               for k, v in ora.items()}
+        bad, near, total, ok = T.compare_indices(gi[keep], gc[keep], sub, lattice, n,
+                                                 "%s (%s)" % (label, path))
+        gk = T.host(g["rice_k"]).reshape(-1)
+        gb = T.u32(g["tile_bits"]).reshape(-1)
+        if tiles is not None:
+            gk, gb = gk[tiles], gb[tiles]
+        assert np.array_equal(gk[keep][ok], sub["rice_k"][ok]), label + " rice_k (%s)" % path
+        assert np.array_equal(gb[keep][ok], sub["tile_bits"][ok]), label + " bits (%s)" % path
+        if coords:
+            gco = T.tile_rows(T.host(g["coords"]), n, tiles)
+            assert np.array_equal(gco[keep][ok], sub["coords"][ok]), label + " coords"
+        say("%s [%s]: tiles %d, scale-boundary skips %d, blocks %d, mismatches %d, near-ties %d"
+            % (label, path, len(X), int(skip.sum()), total, bad, near))
     return ora
 
 
