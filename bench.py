@@ -127,41 +127,49 @@ def main():
     n_weights = sum(x.numel() for row in mats for (x, _, _, _) in row)
     n_tiles = n_weights // 256
 
-    def step(ev=None):
+    n_calls = sum(len(row) for row in mats)
+    # events for the timed region are created up front (creation is a host
+    # call that would otherwise sit between kernel launches)
+    ev = {"enc": [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_calls * args.steps)],
+          "dec": [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_calls * args.steps)],
+          "enc_tiles": [], "dec_tiles": []}
+    cursor = {"enc": 0, "dec": 0}
+
+    def mark(kind):
+        if ev is not None and cursor[kind] < len(ev[kind]):
+            ev[kind][cursor[kind]].record()
+            cursor[kind] += 1
+
+    def step(timed):
         for layer, row in enumerate(mats):
             for i, (x, enc, y, nt) in enumerate(row):
-                if ev is not None:
-                    ev["enc"].append(torch.cuda.Event(enable_timing=True))
-                    ev["enc"][-1].record()
+                if timed:
+                    mark("enc")
                 hq.hq_encode_tiles(x, "E8", 256, args.bps, layer, out=enc)
-                if ev is not None:
-                    ev["enc"].append(torch.cuda.Event(enable_timing=True))
-                    ev["enc"][-1].record()
+                if timed:
+                    mark("enc")
                     ev["enc_tiles"].append(nt)
             for i, (x, enc, y, nt) in enumerate(row):
-                if ev is not None:
-                    ev["dec"].append(torch.cuda.Event(enable_timing=True))
-                    ev["dec"][-1].record()
+                if timed:
+                    mark("dec")
                 hq.hq_decode_tiles(enc["idx"], enc["coset"], enc["scale"], "E8", 256, layer,
                                    torch.bfloat16, out=y)
-                if ev is not None:
-                    ev["dec"].append(torch.cuda.Event(enable_timing=True))
-                    ev["dec"][-1].record()
+                if timed:
+                    mark("dec")
                     ev["dec_tiles"].append(nt)
 
     for _ in range(args.warmup):
-        step()
+        step(False)
     torch.cuda.synchronize()
 
     # timed region: whole steps, bracketed by synchronisation
-    ev = {"enc": [], "dec": [], "enc_tiles": [], "dec_tiles": []}
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     t_start.record()
     for _ in range(args.steps):
-        step(ev)
+        step(True)
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
@@ -169,7 +177,7 @@ def main():
     ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
 
     def kernel_stats(name, tiles_key, bytes_per_tile):
-        evs = ev[name]
+        evs = ev[name][:cursor[name]]
         durs = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(len(evs) // 2)]
         tiles = ev[tiles_key]
         tot_ms = sum(durs)

@@ -20,6 +20,8 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
+    # every rounding step is the one written: no fused multiply-add contraction
+    "-ffp-contract=off",
     # no packed fp32 instructions in any kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",

@@ -110,22 +110,34 @@ __device__ inline void fill_sign_table(uint32_t* tab, const uint32_t* signs) {
 // Blocks with a coordinate on an integer or half-integer take the general
 // decoder (rare; same results).  Writes the stored integers (z0..z6,
 // floor(z7/2)) and returns the coset bit.
+__device__ inline uint32_t sad_u32(uint32_t a, uint32_t b) {
+  uint32_t r;
+  __asm__("v_sad_u32 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 __device__ inline int e8_block(const int32_t* U, int32_t* s) {
-  int32_t I[8], E[8];
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  int32_t sumB = 0, xi = 0, xe = 0;
+  int32_t I[8];
+  uint32_t up[8], k1[8], k2[8];
+  uint32_t sumB = 0, upc = 0;
+  int32_t xi = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int32_t F = U[i] & 0xFFFFFF;
+    const uint32_t F = (uint32_t)U[i] & 0xFFFFFFu;
     I[i] = U[i] >> 24;
-    E[i] = kHalf - F;
-    const uint32_t B = (uint32_t)(E[i] < 0 ? -E[i] : E[i]);
-    sumB += (int32_t)B;
-    const uint32_t k1 = (B << 3) | (uint32_t)i, k2 = (B << 3) | (uint32_t)(7 - i);
-    kmin = k1 < kmin ? k1 : kmin;
-    kmax = k2 > kmax ? k2 : kmax;
+    const uint32_t B = sad_u32(F, (uint32_t)kHalf);       // |F - 2^23|
+    up[i] = ((uint32_t)kHalf - F) >> 31;                   // F > 2^23
+    k1[i] = (B << 3) | (uint32_t)i;
+    k2[i] = (B << 3) | (uint32_t)(7 - i);
+    sumB += B;
+    upc += up[i];
     xi ^= I[i];
-    xe ^= E[i];
+  }
+  uint32_t kmin = k1[0], kmax = k2[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) {
+    kmin = k1[i] < kmin ? k1[i] : kmin;
+    kmax = k2[i] > kmax ? k2[i] : kmax;
   }
   const int32_t bmin = (int32_t)(kmin >> 3), bmax = (int32_t)(kmax >> 3);
   if (bmin == 0 || bmax == kHalf) {
@@ -136,19 +148,24 @@ __device__ inline int e8_block(const int32_t* U, int32_t* s) {
     return c;
   }
   const int ja = (int)(kmin & 7u), jb = 7 - (int)(kmax & 7u);
-  const int odd_b = xi & 1, odd_a = (xi ^ (int32_t)((uint32_t)xe >> 31)) & 1;
-  const int32_t D = (1 << 25) - sumB + (odd_a ? 2 * bmin : 0) -
+  const int odd_b = xi & 1, odd_a = (xi ^ (int32_t)upc) & 1;
+  const int32_t D = (1 << 25) - (int32_t)sumB + (odd_a ? 2 * bmin : 0) -
                     (odd_b ? (1 << 24) - 2 * bmax : 0);
   const int c = D > 0;
+  const uint32_t nc = (uint32_t)(1 - c);
   const int jf = c ? jb : ja;
-  const int fodd = c ? odd_b : odd_a;
+  const uint32_t oh = (uint32_t)(c ? odd_b : odd_a) << jf;    // one-hot flip position
+  // the flipped coordinate moves towards u: coset a: +1 unless it was
+  // rounded up; coset b: +1 when u lies above the half-integer
+  uint32_t upmask = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) upmask |= up[i] << i;
+  const int32_t upj = (int32_t)((upmask >> jf) & 1u);
+  const int32_t step = c ? (2 * upj - 1) : (1 - 2 * upj);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int32_t up = (int32_t)((uint32_t)E[i] >> 31);   // F_i > 2^23
-    int32_t z = I[i] + (c ? 0 : up);
-    // coset a: move towards u (+1 when u_j is above a_j); coset b: likewise
-    const int32_t step = c ? (up ? 1 : -1) : (up ? -1 : 1);
-    z += (fodd && i == jf) ? step : 0;
+    int32_t z = (int32_t)((uint32_t)I[i] + up[i] * nc);
+    z += (int32_t)((oh >> i) & 1u) * step;
     s[i] = (i == 7) ? (z >> 1) : z;
   }
   return c;
@@ -169,28 +186,40 @@ __device__ inline uint32_t byte_sum(uint32_t d, uint32_t acc) {
   return __builtin_amdgcn_sad_u8(d, 0u, acc);
 }
 
-__global__ __launch_bounds__(kBlock) void encode_e8_fast(EncodeLaunch a) {
-  __shared__ uint32_t sign_tab[128];
-  fill_sign_table(sign_tab, a.signs);
-  __syncthreads();
-
-  const int lane = threadIdx.x & 63;
-  const int t = lane & 15, row = lane >> 4;
-  const int64_t group = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
-  if (group * 16 >= a.n_tiles) return;               // whole wave past the end
-  const int64_t tile_raw = group * 16 + t;
-  const bool live = tile_raw < a.n_tiles;
-  const int64_t tile = live ? tile_raw : a.n_tiles - 1;   // ragged end: recompute a valid tile
-
-  // ---- load 64 bf16 (128 bytes) and apply the RHT signs in the bf16 domain
-  const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) +
-                                                    tile * 256 + row * 64);
-  uint32_t w[32];
+// Staged loads.  A wave's 16 tiles are 8 KB of contiguous bf16, read with
+// eight direct-to-LDS loads of 1 KB each (instruction k covers tiles 2k and
+// 2k + 1, so every load is fully coalesced).  Lane l = 16 r + b of
+// instruction k fetches row r, 16-byte chunk j = (b/2 - k) mod 8 of tile
+// 2k + (b & 1) and the hardware stores it at LDS slot 64 k + l; lane (t, r)
+// later finds chunk j of its tile at slot 64 (t/2) + 16 r + ((t + 2j) mod 16),
+// so each 16-lane row reads 16 different bank groups.
+__device__ inline void enc_prefetch(const EncodeLaunch& a, int64_t group, uint4* buf, int lane) {
+  const int r = lane >> 4, b = lane & 15;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const uint4 q = src[k];
-    w[4 * k] = q.x; w[4 * k + 1] = q.y; w[4 * k + 2] = q.z; w[4 * k + 3] = q.w;
+    const int j = ((b >> 1) - k) & 7;
+    int64_t tile = group * 16 + 2 * k + (b & 1);
+    tile = tile < a.n_tiles ? tile : a.n_tiles - 1;   // ragged end: reread a valid tile
+    const uint16_t* src = static_cast<const uint16_t*>(a.x) + tile * 256 + r * 64 + j * 8;
+    __builtin_amdgcn_global_load_lds(src, buf + 64 * k, 16, 0, 0);
   }
+}
+
+__device__ inline void enc_take(const uint4* buf, int t, int r, uint32_t* w) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint4 q = buf[64 * (t >> 1) + 16 * r + ((t + 2 * j) & 15)];
+    w[4 * j] = q.x; w[4 * j + 1] = q.y; w[4 * j + 2] = q.z; w[4 * j + 3] = q.w;
+  }
+}
+
+// One group of 16 tiles held by a wave (w: this lane's 64 bf16 of its tile).
+__device__ inline void enc_group(const EncodeLaunch& a, const uint32_t* sign_tab, int64_t group,
+                                 int t, int row, const uint32_t* w) {
+  const int64_t tile_raw = group * 16 + t;
+  const bool live = tile_raw < a.n_tiles;
+  const int64_t tile = live ? tile_raw : a.n_tiles - 1;
+
   const uint4* st = reinterpret_cast<const uint4*>(sign_tab + row * 32);
   double v[64];
   double ss = 0.0;
@@ -336,6 +365,36 @@ __global__ __launch_bounds__(kBlock) void encode_e8_fast(EncodeLaunch a) {
   }
 }
 
+// Persistent waves: each wave walks groups of 16 tiles with a grid-wide
+// stride; the next group streams into the wave's LDS buffer while the
+// current one is computed.
+__global__ __launch_bounds__(kBlock) void encode_e8_fast(EncodeLaunch a) {
+  __shared__ uint32_t sign_tab[128];
+  __shared__ uint4 stage[kBlock / 64][512];
+  fill_sign_table(sign_tab, a.signs);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int t = lane & 15, row = lane >> 4;
+  uint4* buf = stage[threadIdx.x >> 6];
+  const int64_t n_groups = (a.n_tiles + 15) / 16;
+  const int64_t stride = (int64_t)gridDim.x * (kBlock / 64);
+  int64_t g = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+  if (g >= n_groups) return;
+  enc_prefetch(a, g, buf, lane);
+  for (;;) {
+    uint32_t w[32];
+    enc_take(buf, t, row, w);
+    // every lane's reads of the buffer complete before it is refilled
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int64_t gn = g + stride;
+    const bool more = gn < n_groups;   // uniform across the wave
+    if (more) enc_prefetch(a, gn, buf, lane);
+    enc_group(a, sign_tab, g, t, row, w);
+    if (!more) break;
+    g = gn;
+  }
+}
+
 // ------------------------------------------------------------------ decode
 // Integer Hadamard on P = 2p in packed int16 pairs (2 elements per register);
 // exact while sum |P| <= 32767, which every tile of encoder output satisfies
@@ -356,29 +415,48 @@ __device__ inline uint32_t half_butterfly(uint32_t x) {
   return as_u32(hh * (s16x2){1, -1} + ll);
 }
 
-template <bool OUT_BF16>
-__global__ __launch_bounds__(kBlock) void decode_e8_fast(DecodeLaunch a) {
-  __shared__ uint32_t sign_tab[128];
-  fill_sign_table(sign_tab, a.signs);
-  __syncthreads();
+// Staged loads as in the encoder: a wave's 16 tiles are 4 KB of int8
+// indices, four 1 KB direct-to-LDS loads (instruction k covers tiles 4k ..
+// 4k + 3).  Lane l = 16 r + b of instruction k fetches row r, chunk
+// j = (b/4 - k) mod 4 of tile 4k + (b & 3) into slot 64 k + l; lane (t, r)
+// reads chunk j of its tile from slot 64 (t/4) + 16 r + ((t + 4j) mod 16).
+struct DecIn {
+  uint32_t cw;
+  float scale;
+};
 
-  const int lane = threadIdx.x & 63;
-  const int t = lane & 15, row = lane >> 4;
-  const int64_t group = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
-  if (group * 16 >= a.n_tiles) return;
+__device__ inline void dec_prefetch(const DecodeLaunch& a, int64_t group, uint4* buf, int lane,
+                                    int t, DecIn& in) {
+  const int r = lane >> 4, b = lane & 15;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int j = ((b >> 2) - k) & 3;
+    int64_t tile = group * 16 + 4 * k + (b & 3);
+    tile = tile < a.n_tiles ? tile : a.n_tiles - 1;
+    __builtin_amdgcn_global_load_lds(a.idx + tile * 256 + r * 64 + j * 16, buf + 64 * k, 16, 0, 0);
+  }
+  int64_t tile = group * 16 + t;
+  tile = tile < a.n_tiles ? tile : a.n_tiles - 1;
+  in.cw = a.coset[tile];
+  in.scale = a.scale[tile];
+}
+
+__device__ inline void dec_take(const uint4* buf, int t, int r, uint32_t* d) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint4 q = buf[64 * (t >> 2) + 16 * r + ((t + 4 * j) & 15)];
+    d[4 * j] = q.x; d[4 * j + 1] = q.y; d[4 * j + 2] = q.z; d[4 * j + 3] = q.w;
+  }
+}
+
+template <bool OUT_BF16>
+__device__ inline void dec_group(const DecodeLaunch& a, const uint32_t* sign_tab, int64_t group,
+                                 int t, int row, const uint32_t* d, const DecIn& in) {
   const int64_t tile_raw = group * 16 + t;
   const bool live = tile_raw < a.n_tiles;
   const int64_t tile = live ? tile_raw : a.n_tiles - 1;
-
-  const uint4* src = reinterpret_cast<const uint4*>(a.idx + tile * 256 + row * 64);
-  uint32_t d[16];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint4 q = src[k];
-    d[4 * k] = q.x; d[4 * k + 1] = q.y; d[4 * k + 2] = q.z; d[4 * k + 3] = q.w;
-  }
-  const uint32_t cw = a.coset[tile] >> (8 * row);   // this lane's 8 blocks
-  const float dsc = a.scale[tile] * 0.03125f;        // Delta / 32, exact
+  const uint32_t cw = in.cw >> (8 * row);        // this lane's 8 blocks
+  const float dsc = in.scale * 0.03125f;         // Delta / 32, exact
 
   // bound for the int16 path: sum |P| <= 4 sum|stored| + 320 (|z7| <= 2|t7| + 1)
   uint32_t sabs = 0;
@@ -536,6 +614,36 @@ __global__ __launch_bounds__(kBlock) void decode_e8_fast(DecodeLaunch a) {
   }
 }
 
+template <bool OUT_BF16>
+__global__ __launch_bounds__(kBlock) void decode_e8_fast(DecodeLaunch a) {
+  __shared__ uint32_t sign_tab[128];
+  __shared__ uint4 stage[kBlock / 64][256];
+  fill_sign_table(sign_tab, a.signs);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int t = lane & 15, row = lane >> 4;
+  uint4* buf = stage[threadIdx.x >> 6];
+  const int64_t n_groups = (a.n_tiles + 15) / 16;
+  const int64_t stride = (int64_t)gridDim.x * (kBlock / 64);
+  int64_t g = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+  if (g >= n_groups) return;
+  DecIn cur;
+  dec_prefetch(a, g, buf, lane, t, cur);
+  for (;;) {
+    uint32_t d[16];
+    dec_take(buf, t, row, d);
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int64_t gn = g + stride;
+    const bool more = gn < n_groups;
+    DecIn nxt;
+    if (more) dec_prefetch(a, gn, buf, lane, t, nxt);
+    dec_group<OUT_BF16>(a, sign_tab, g, t, row, d, cur);
+    if (!more) break;
+    cur = nxt;
+    g = gn;
+  }
+}
+
 }  // namespace
 
 bool e8_fast_encode_ok(const EncodeLaunch& a) {
@@ -546,20 +654,58 @@ bool e8_fast_decode_ok(const DecodeLaunch& a) {
   return a.lattice == 8 && a.tile == 256 && !a.dither;
 }
 
-hipError_t launch_encode_e8_fast(const EncodeLaunch& a, hipStream_t s) {
-  const int64_t groups = (a.n_tiles + 15) / 16;
+namespace {
+
+int device_cus() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Resident blocks of a kernel on the whole device (persistent grid size).
+template <typename K>
+int64_t resident_blocks(K kernel, int& cache) {
+  if (cache == 0) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0) != hipSuccess ||
+        per_cu <= 0)
+      per_cu = 1;
+    cache = per_cu;
+  }
+  return (int64_t)cache * device_cus();
+}
+
+int64_t persistent_grid(int64_t n_tiles, int64_t resident) {
+  const int64_t groups = (n_tiles + 15) / 16;
   const int64_t blocks = (groups + kBlock / 64 - 1) / (kBlock / 64);
+  return blocks < resident ? blocks : resident;
+}
+
+}  // namespace
+
+hipError_t launch_encode_e8_fast(const EncodeLaunch& a, hipStream_t s) {
+  static int occ = 0;
+  const int64_t blocks = persistent_grid(a.n_tiles, resident_blocks(encode_e8_fast, occ));
   hipLaunchKernelGGL(encode_e8_fast, dim3((unsigned)blocks), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_e8_fast(const DecodeLaunch& a, hipStream_t s) {
-  const int64_t groups = (a.n_tiles + 15) / 16;
-  const int64_t blocks = (groups + kBlock / 64 - 1) / (kBlock / 64);
-  if (a.out_bf16)
+  static int occ_bf16 = 0, occ_f32 = 0;
+  if (a.out_bf16) {
+    const int64_t blocks = persistent_grid(a.n_tiles, resident_blocks(decode_e8_fast<true>, occ_bf16));
     hipLaunchKernelGGL(decode_e8_fast<true>, dim3((unsigned)blocks), dim3(kBlock), 0, s, a);
-  else
+  } else {
+    const int64_t blocks = persistent_grid(a.n_tiles, resident_blocks(decode_e8_fast<false>, occ_f32));
     hipLaunchKernelGGL(decode_e8_fast<false>, dim3((unsigned)blocks), dim3(kBlock), 0, s, a);
+  }
   return hipGetLastError();
 }
 
