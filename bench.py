@@ -6,8 +6,9 @@ k/v 1024x4096, gate/up 14336x4096, down 4096x14336; 6.98e9 bf16 weights,
 13.96 GB), entries N(0, 0.02^2) with 0.1% of input columns replaced by
 10 * Student-t(4) outliers, drawn on the GPU (seed per layer).  One step
 streams the whole stack: for each layer, encode its seven matrices (E8,
-4 bps, tile 256, auto scale, RHT seed = layer index), then decode them to
-bf16.  Inputs and output buffers are resident in HBM before timing starts.
+4 bps, tile 256, auto scale, RHT seed = layer index) with one batched call,
+then decode them to bf16 with another.  Inputs and output buffers are
+resident in HBM before timing starts.
 
 Prints one JSON line.  value = bf16 GB/s in = 2 * weights / step time.
 """
@@ -107,56 +108,43 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    mats = []
+    layers = []
     for layer in range(args.layers):
-        row = []
-        for m, (name, rows, cols) in enumerate(workloads.LLAMA_LAYER):
-            x = workloads.llama_stack_torch(layer, m, dev)
-            nt = rows * cols // 256
-            enc = {
-                "scale": torch.empty(nt, dtype=torch.float32, device=dev),
-                "idx": torch.empty((rows, cols), dtype=torch.int8, device=dev),
-                "coset": torch.empty((nt, 1), dtype=torch.int32, device=dev),
-                "rice_k": torch.empty(nt, dtype=torch.uint8, device=dev),
-                "tile_bits": torch.empty(nt, dtype=torch.int32, device=dev),
-            }
-            y = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
-            row.append((x, enc, y, nt))
-        mats.append(row)
+        xs = [workloads.llama_stack_torch(layer, m, dev) for m in range(len(workloads.LLAMA_LAYER))]
+        encs = hq.hq_encode_batch(xs, "E8", 256, args.bps, layer)       # output buffers
+        ys = [torch.empty_like(x) for x in xs]
+        layers.append((xs, encs, ys))
     torch.cuda.synchronize()
-    n_weights = sum(x.numel() for row in mats for (x, _, _, _) in row)
+    n_weights = sum(x.numel() for xs, _, _ in layers for x in xs)
     n_tiles = n_weights // 256
+    tiles_per_layer = [sum(x.numel() for x in xs) // 256 for xs, _, _ in layers]
 
-    n_calls = sum(len(row) for row in mats)
     # events for the timed region are created up front (creation is a host
     # call that would otherwise sit between kernel launches)
-    ev = {"enc": [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_calls * args.steps)],
-          "dec": [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_calls * args.steps)],
+    n_ev = 2 * len(layers) * args.steps
+    ev = {"enc": [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)],
+          "dec": [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)],
           "enc_tiles": [], "dec_tiles": []}
     cursor = {"enc": 0, "dec": 0}
 
     def mark(kind):
-        if ev is not None and cursor[kind] < len(ev[kind]):
-            ev[kind][cursor[kind]].record()
-            cursor[kind] += 1
+        ev[kind][cursor[kind]].record()
+        cursor[kind] += 1
 
     def step(timed):
-        for layer, row in enumerate(mats):
-            for i, (x, enc, y, nt) in enumerate(row):
-                if timed:
-                    mark("enc")
-                hq.hq_encode_tiles(x, "E8", 256, args.bps, layer, out=enc)
-                if timed:
-                    mark("enc")
-                    ev["enc_tiles"].append(nt)
-            for i, (x, enc, y, nt) in enumerate(row):
-                if timed:
-                    mark("dec")
-                hq.hq_decode_tiles(enc["idx"], enc["coset"], enc["scale"], "E8", 256, layer,
-                                   torch.bfloat16, out=y)
-                if timed:
-                    mark("dec")
-                    ev["dec_tiles"].append(nt)
+        # one launch encodes a layer's seven projections, one launch decodes them
+        for layer, (xs, encs, ys) in enumerate(layers):
+            if timed:
+                mark("enc")
+            hq.hq_encode_batch(xs, "E8", 256, args.bps, layer, outs=encs)
+            if timed:
+                mark("enc")
+                ev["enc_tiles"].append(tiles_per_layer[layer])
+                mark("dec")
+            hq.hq_decode_batch(encs, "E8", 256, layer, torch.bfloat16, outs=ys)
+            if timed:
+                mark("dec")
+                ev["dec_tiles"].append(tiles_per_layer[layer])
 
     for _ in range(args.warmup):
         step(False)

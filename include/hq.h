@@ -188,6 +188,44 @@ hq_status hq_kv_encode(const hq_params* p, const void* kv, int32_t kv_dtype,
                        uint32_t* coset, uint8_t* rice_k, uint32_t* tile_bits,
                        uint32_t* status, hipStream_t stream);
 
+/*
+ * Batched calls.  A transformer layer's projections share one parameter
+ * block (lattice, tile, rate, RHT seed, flags); encoding or decoding them in
+ * one call lets the library cover several matrices with one persistent
+ * launch (up to 8 matrices per launch on the E8 / tile 256 path), which
+ * keeps the GPU full on small matrices and removes per-matrix launch gaps.
+ * Results are bit-identical to one hq_encode_tiles / hq_decode_tiles call per
+ * item.  `items` is a host array of `count` descriptors read during the call;
+ * every item is validated as the single call would be, and nothing is
+ * enqueued unless all of them pass.  HQ_WANT_COORDS and HQ_DITHER are not
+ * accepted here (HQ_EUNSUPPORTED).  Same passages as the single calls.
+ */
+typedef struct {
+  const void* x;          /* [rows*cols] of x_dtype                     */
+  int64_t rows, cols;
+  float* scale;           /* [n_tiles]: out with HQ_SCALE_AUTO, else in */
+  int8_t* idx;            /* [rows*cols]                                */
+  uint32_t* coset;        /* [n_tiles * hq_coset_words(p)]              */
+  uint8_t* rice_k;        /* [n_tiles]                                  */
+  uint32_t* tile_bits;    /* [n_tiles]                                  */
+} hq_encode_item;
+
+typedef struct {
+  const int8_t* idx;      /* [rows*cols]                                */
+  const uint32_t* coset;  /* [n_tiles * hq_coset_words(p)]              */
+  const float* scale;     /* [n_tiles]                                  */
+  int64_t rows, cols;
+  void* y;                /* [rows*cols] of y_dtype                     */
+} hq_decode_item;
+
+hq_status hq_encode_batch(const hq_params* p, int32_t x_dtype, int32_t count,
+                          const hq_encode_item* items, uint32_t* status,
+                          hipStream_t stream);
+
+hq_status hq_decode_batch(const hq_params* p, int32_t y_dtype, int32_t count,
+                          const hq_decode_item* items, uint32_t* status,
+                          hipStream_t stream);
+
 /* Coset words per tile: E8 ceil(n/256), A2 ceil(n/64), D4 and Z 0;
  * -1 on an invalid p. */
 int32_t hq_coset_words(const hq_params* p);

@@ -240,6 +240,140 @@ hq_status hq_decode_tiles(const hq_params* p, const int8_t* idx, const uint32_t*
   return launched(launch_decode(a, stream));
 }
 
+hq_status hq_encode_batch(const hq_params* p, int32_t x_dtype, int32_t count,
+                          const hq_encode_item* items, uint32_t* status, hipStream_t stream) {
+  hq_status st = check_params(p);
+  if (st != HQ_OK) return st;
+  if (p->flags & (HQ_WANT_COORDS | HQ_DITHER)) return HQ_EUNSUPPORTED;
+  if (count < 0 || (count > 0 && items == nullptr)) return HQ_EINVAL;
+  for (int32_t i = 0; i < count; ++i) {
+    const hq_encode_item& it = items[i];
+    st = check_encode(p, it.x, x_dtype, it.rows, it.cols, it.scale, it.idx, it.coset, it.rice_k,
+                      it.tile_bits, nullptr);
+    if (st != HQ_OK) return st;
+  }
+  for (int32_t i = 0; i < count; ++i) {
+    const hq_encode_item& it = items[i];
+    if (it.rows == 0 || it.cols == 0) continue;
+    if (!on_device(it.x) || !on_device(it.scale) || !on_device(it.idx) || !on_device(it.rice_k) ||
+        !on_device(it.tile_bits) || (coset_words(p) > 0 && !on_device(it.coset)))
+      return HQ_EINVAL;
+  }
+  if (status != nullptr && !on_device(status)) return HQ_EINVAL;
+  EncodeLaunch a;
+  memset(&a, 0, sizeof(a));
+  a.in_bf16 = x_dtype == HQ_BF16;
+  a.lattice = p->lattice;
+  a.tile = p->tile;
+  a.auto_scale = (p->flags & HQ_SCALE_AUTO) != 0;
+  a.status = status;
+  make_signs(p->rht_seed, p->tile, a.signs);
+  a.c = scale_constant(p);
+  a.sqrt_n = sqrt((double)p->tile);
+  if (e8_fast_encode_ok(a)) {
+    EncBatch b;
+    memset(&b, 0, sizeof(b));
+    for (int32_t i = 0; i <= count; ++i) {
+      const bool flush = (i == count) || b.n == kMaxItems;
+      if (flush && b.n > 0) {
+        for (int k = b.n; k < kMaxItems; ++k) b.it[k] = b.it[0];
+        if (launch_encode_e8_fast(a, b, stream) != hipSuccess) return HQ_EDEVICE;
+        memset(&b, 0, sizeof(b));
+      }
+      if (i == count) break;
+      const hq_encode_item& it = items[i];
+      const int64_t nt = it.rows * it.cols / p->tile;
+      if (nt == 0) continue;
+      b.it[b.n] = EncItem{it.x, it.idx, it.scale, it.coset, it.rice_k, it.tile_bits, nt,
+                          b.n_groups};
+      b.n_groups += (nt + 15) / 16;
+      b.n += 1;
+    }
+    return HQ_OK;
+  }
+  for (int32_t i = 0; i < count; ++i) {
+    const hq_encode_item& it = items[i];
+    const int64_t nt = it.rows * it.cols / p->tile;
+    if (nt == 0) continue;
+    a.x = it.x;
+    a.n_tiles = nt;
+    a.scale = it.scale;
+    a.idx = it.idx;
+    a.coset = it.coset;
+    a.rice_k = it.rice_k;
+    a.tile_bits = it.tile_bits;
+    a.coords = nullptr;
+    if (launch_encode(a, stream) != hipSuccess) return HQ_EDEVICE;
+  }
+  return HQ_OK;
+}
+
+hq_status hq_decode_batch(const hq_params* p, int32_t y_dtype, int32_t count,
+                          const hq_decode_item* items, uint32_t* status, hipStream_t stream) {
+  hq_status st = check_params(p);
+  if (st != HQ_OK) return st;
+  if (p->flags & (HQ_WANT_COORDS | HQ_DITHER)) return HQ_EUNSUPPORTED;
+  if (y_dtype != HQ_F32 && y_dtype != HQ_BF16) return HQ_EINVAL;
+  if (count < 0 || (count > 0 && items == nullptr)) return HQ_EINVAL;
+  for (int32_t i = 0; i < count; ++i) {
+    const hq_decode_item& it = items[i];
+    if (it.rows < 0 || it.cols < 0 || it.cols % p->tile != 0) return HQ_EINVAL;
+    if (it.rows == 0 || it.cols == 0) continue;
+    if (it.idx == nullptr || it.scale == nullptr || it.y == nullptr) return HQ_EINVAL;
+    if (coset_words(p) > 0 && it.coset == nullptr) return HQ_EINVAL;
+    if (!aligned16(it.idx) || !aligned16(it.y)) return HQ_EINVAL;
+    if (it.rows > INT64_MAX / it.cols) return HQ_EINVAL;
+  }
+  for (int32_t i = 0; i < count; ++i) {
+    const hq_decode_item& it = items[i];
+    if (it.rows == 0 || it.cols == 0) continue;
+    if (!on_device(it.idx) || !on_device(it.scale) || !on_device(it.y) ||
+        (coset_words(p) > 0 && !on_device(it.coset)))
+      return HQ_EINVAL;
+  }
+  if (status != nullptr && !on_device(status)) return HQ_EINVAL;
+  DecodeLaunch a;
+  memset(&a, 0, sizeof(a));
+  a.lattice = p->lattice;
+  a.tile = p->tile;
+  a.out_bf16 = y_dtype == HQ_BF16;
+  a.status = status;
+  make_signs(p->rht_seed, p->tile, a.signs);
+  a.inv_sqrt_n = 1.0 / sqrt((double)p->tile);
+  if (e8_fast_decode_ok(a)) {
+    DecBatch b;
+    memset(&b, 0, sizeof(b));
+    for (int32_t i = 0; i <= count; ++i) {
+      const bool flush = (i == count) || b.n == kMaxItems;
+      if (flush && b.n > 0) {
+        for (int k = b.n; k < kMaxItems; ++k) b.it[k] = b.it[0];
+        if (launch_decode_e8_fast(a, b, stream) != hipSuccess) return HQ_EDEVICE;
+        memset(&b, 0, sizeof(b));
+      }
+      if (i == count) break;
+      const hq_decode_item& it = items[i];
+      const int64_t nt = it.rows * it.cols / p->tile;
+      if (nt == 0) continue;
+      b.it[b.n] = DecItem{it.idx, it.coset, it.scale, it.y, nt, b.n_groups};
+      b.n_groups += (nt + 15) / 16;
+      b.n += 1;
+    }
+    return HQ_OK;
+  }
+  for (int32_t i = 0; i < count; ++i) {
+    const hq_decode_item& it = items[i];
+    const int64_t nt = it.rows * it.cols / p->tile;
+    if (nt == 0) continue;
+    a.idx = it.idx;
+    a.coset = it.coset;
+    a.scale = it.scale;
+    a.n_tiles = nt;
+    a.y = it.y;
+    if (launch_decode(a, stream) != hipSuccess) return HQ_EDEVICE;
+  }
+  return HQ_OK;
+}
+
 size_t hq_rate_workspace_bytes(int64_t n_tiles) {
   if (n_tiles <= 0) return 0;
   return (size_t)((n_tiles + 15) / 16) * sizeof(uint64_t);

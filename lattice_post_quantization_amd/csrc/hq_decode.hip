@@ -196,7 +196,15 @@ hipError_t launch_lat(const DecodeLaunch& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t s) {
-  if (e8_fast_decode_ok(a)) return launch_decode_e8_fast(a, s);
+  if (e8_fast_decode_ok(a)) {
+    DecBatch b;
+    b.n = 1;
+    b.pad = 0;
+    b.n_groups = (a.n_tiles + 15) / 16;
+    b.it[0] = DecItem{a.idx, a.coset, a.scale, a.y, a.n_tiles, 0};
+    for (int i = 1; i < kMaxItems; ++i) b.it[i] = b.it[0];
+    return launch_decode_e8_fast(a, b, s);
+  }
   switch (a.lattice) {
     case 8: return launch_lat<8>(a, s);
     case 4: return launch_lat<4>(a, s);

@@ -193,14 +193,14 @@ __device__ inline uint32_t byte_sum(uint32_t d, uint32_t acc) {
 // 2k + (b & 1) and the hardware stores it at LDS slot 64 k + l; lane (t, r)
 // later finds chunk j of its tile at slot 64 (t/2) + 16 r + ((t + 2j) mod 16),
 // so each 16-lane row reads 16 different bank groups.
-__device__ inline void enc_prefetch(const EncodeLaunch& a, int64_t group, uint4* buf, int lane) {
+__device__ inline void enc_prefetch(const EncItem& it, int64_t group, uint4* buf, int lane) {
   const int r = lane >> 4, b = lane & 15;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int j = ((b >> 1) - k) & 7;
     int64_t tile = group * 16 + 2 * k + (b & 1);
-    tile = tile < a.n_tiles ? tile : a.n_tiles - 1;   // ragged end: reread a valid tile
-    const uint16_t* src = static_cast<const uint16_t*>(a.x) + tile * 256 + r * 64 + j * 8;
+    tile = tile < it.n_tiles ? tile : it.n_tiles - 1;   // ragged end: reread a valid tile
+    const uint16_t* src = static_cast<const uint16_t*>(it.x) + tile * 256 + r * 64 + j * 8;
     __builtin_amdgcn_global_load_lds(src, buf + 64 * k, 16, 0, 0);
   }
 }
@@ -214,11 +214,11 @@ __device__ inline void enc_take(const uint4* buf, int t, int r, uint32_t* w) {
 }
 
 // One group of 16 tiles held by a wave (w: this lane's 64 bf16 of its tile).
-__device__ inline void enc_group(const EncodeLaunch& a, const uint32_t* sign_tab, int64_t group,
-                                 int t, int row, const uint32_t* w) {
+__device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const uint32_t* sign_tab,
+                                 int64_t group, int t, int row, const uint32_t* w) {
   const int64_t tile_raw = group * 16 + t;
-  const bool live = tile_raw < a.n_tiles;
-  const int64_t tile = live ? tile_raw : a.n_tiles - 1;
+  const bool live = tile_raw < it.n_tiles;
+  const int64_t tile = live ? tile_raw : it.n_tiles - 1;
 
   const uint4* st = reinterpret_cast<const uint4*>(sign_tab + row * 32);
   double v[64];
@@ -248,7 +248,7 @@ __device__ inline void enc_group(const EncodeLaunch& a, const uint32_t* sign_tab
     delta = bf16_round_to_f32(sqrt(ss / 256.0) * a.c);
     if (delta == 0.0f) delta = 1.0f;
   } else {
-    delta = a.scale[tile];
+    delta = it.scale[tile];
     if (!(delta > 0.0f) || !isfinite(delta)) status |= HQ_ST_NONFINITE;
   }
   if (!isfinite(ss)) status |= HQ_ST_NONFINITE;
@@ -351,15 +351,15 @@ __device__ inline void enc_group(const EncodeLaunch& a, const uint32_t* sign_tab
 #pragma unroll
   for (int q = 0; q < 8; ++q) swap16(packed[q], packed[q + 8]);
   if (live) {
-    uint4* dst = reinterpret_cast<uint4*>(a.idx + tile * 256 + row * 64);
+    uint4* dst = reinterpret_cast<uint4*>(it.idx + tile * 256 + row * 64);
 #pragma unroll
     for (int k = 0; k < 4; ++k)
       dst[k] = make_uint4(packed[4 * k], packed[4 * k + 1], packed[4 * k + 2], packed[4 * k + 3]);
     if (row == 0) {
-      if (a.auto_scale) a.scale[tile] = delta;
-      a.coset[tile] = coset_word;
-      a.rice_k[tile] = (uint8_t)bk;
-      a.tile_bits[tile] = 4u + 32u + best;
+      if (a.auto_scale) it.scale[tile] = delta;
+      it.coset[tile] = coset_word;
+      it.rice_k[tile] = (uint8_t)bk;
+      it.tile_bits[tile] = 4u + 32u + best;
       if (status) set_status(a.status, status);
     }
   }
@@ -368,30 +368,43 @@ __device__ inline void enc_group(const EncodeLaunch& a, const uint32_t* sign_tab
 // Persistent waves: each wave walks groups of 16 tiles with a grid-wide
 // stride; the next group streams into the wave's LDS buffer while the
 // current one is computed.
-__global__ __launch_bounds__(kBlock) void encode_e8_fast(EncodeLaunch a) {
+// Item holding global group g (items are few; the index is wave-uniform).
+template <typename B>
+__device__ inline int item_of(const B& b, int64_t g) {
+  int i = 0;
+#pragma unroll
+  for (int k = 1; k < kMaxItems; ++k)
+    if (k < b.n && g >= b.it[k].group0) i = k;
+  return i;
+}
+
+__global__ __launch_bounds__(kBlock) void encode_e8_fast(EncodeLaunch a, EncBatch b) {
   __shared__ uint32_t sign_tab[128];
   __shared__ uint4 stage[kBlock / 64][512];
   fill_sign_table(sign_tab, a.signs);
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int t = lane & 15, row = lane >> 4;
-  uint4* buf = stage[threadIdx.x >> 6];
-  const int64_t n_groups = (a.n_tiles + 15) / 16;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint4* buf = stage[wave];
   const int64_t stride = (int64_t)gridDim.x * (kBlock / 64);
-  int64_t g = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
-  if (g >= n_groups) return;
-  enc_prefetch(a, g, buf, lane);
+  int64_t g = (int64_t)blockIdx.x * (kBlock / 64) + wave;
+  if (g >= b.n_groups) return;
+  int ic = item_of(b, g);
+  enc_prefetch(b.it[ic], g - b.it[ic].group0, buf, lane);
   for (;;) {
     uint32_t w[32];
     enc_take(buf, t, row, w);
     // every lane's reads of the buffer complete before it is refilled
     __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const int64_t gn = g + stride;
-    const bool more = gn < n_groups;   // uniform across the wave
-    if (more) enc_prefetch(a, gn, buf, lane);
-    enc_group(a, sign_tab, g, t, row, w);
+    const bool more = gn < b.n_groups;   // uniform across the wave
+    const int in = more ? item_of(b, gn) : ic;
+    if (more) enc_prefetch(b.it[in], gn - b.it[in].group0, buf, lane);
+    enc_group(a, b.it[ic], sign_tab, g - b.it[ic].group0, t, row, w);
     if (!more) break;
     g = gn;
+    ic = in;
   }
 }
 
@@ -425,20 +438,20 @@ struct DecIn {
   float scale;
 };
 
-__device__ inline void dec_prefetch(const DecodeLaunch& a, int64_t group, uint4* buf, int lane,
-                                    int t, DecIn& in) {
+__device__ inline void dec_prefetch(const DecItem& it, int64_t group, uint4* buf, int lane, int t,
+                                    DecIn& in) {
   const int r = lane >> 4, b = lane & 15;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int j = ((b >> 2) - k) & 3;
     int64_t tile = group * 16 + 4 * k + (b & 3);
-    tile = tile < a.n_tiles ? tile : a.n_tiles - 1;
-    __builtin_amdgcn_global_load_lds(a.idx + tile * 256 + r * 64 + j * 16, buf + 64 * k, 16, 0, 0);
+    tile = tile < it.n_tiles ? tile : it.n_tiles - 1;
+    __builtin_amdgcn_global_load_lds(it.idx + tile * 256 + r * 64 + j * 16, buf + 64 * k, 16, 0, 0);
   }
   int64_t tile = group * 16 + t;
-  tile = tile < a.n_tiles ? tile : a.n_tiles - 1;
-  in.cw = a.coset[tile];
-  in.scale = a.scale[tile];
+  tile = tile < it.n_tiles ? tile : it.n_tiles - 1;
+  in.cw = it.coset[tile];
+  in.scale = it.scale[tile];
 }
 
 __device__ inline void dec_take(const uint4* buf, int t, int r, uint32_t* d) {
@@ -450,11 +463,11 @@ __device__ inline void dec_take(const uint4* buf, int t, int r, uint32_t* d) {
 }
 
 template <bool OUT_BF16>
-__device__ inline void dec_group(const DecodeLaunch& a, const uint32_t* sign_tab, int64_t group,
-                                 int t, int row, const uint32_t* d, const DecIn& in) {
+__device__ inline void dec_group(const DecItem& it, const uint32_t* sign_tab, int64_t group, int t,
+                                 int row, const uint32_t* d, const DecIn& in) {
   const int64_t tile_raw = group * 16 + t;
-  const bool live = tile_raw < a.n_tiles;
-  const int64_t tile = live ? tile_raw : a.n_tiles - 1;
+  const bool live = tile_raw < it.n_tiles;
+  const int64_t tile = live ? tile_raw : it.n_tiles - 1;
   const uint32_t cw = in.cw >> (8 * row);        // this lane's 8 blocks
   const float dsc = in.scale * 0.03125f;         // Delta / 32, exact
 
@@ -585,7 +598,7 @@ __device__ inline void dec_group(const DecodeLaunch& a, const uint32_t* sign_tab
 #pragma unroll
     for (int m = 0; m < 16; ++m) swap16(o[m], o[m + 16]);
     if (live) {
-      uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.y) + tile * 256 + row * 64);
+      uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(it.y) + tile * 256 + row * 64);
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const uint4 sm = st[k];
@@ -603,7 +616,7 @@ __device__ inline void dec_group(const DecodeLaunch& a, const uint32_t* sign_tab
 #pragma unroll
     for (int i = 0; i < 32; ++i) swap16(o[i], o[i + 32]);
     if (live) {
-      uint4* dst = reinterpret_cast<uint4*>(static_cast<float*>(a.y) + tile * 256 + row * 64);
+      uint4* dst = reinterpret_cast<uint4*>(static_cast<float*>(it.y) + tile * 256 + row * 64);
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const uint32_t sm = sign_tab[row * 32 + 2 * k], sn = sign_tab[row * 32 + 2 * k + 1];
@@ -615,32 +628,35 @@ __device__ inline void dec_group(const DecodeLaunch& a, const uint32_t* sign_tab
 }
 
 template <bool OUT_BF16>
-__global__ __launch_bounds__(kBlock) void decode_e8_fast(DecodeLaunch a) {
+__global__ __launch_bounds__(kBlock) void decode_e8_fast(DecodeLaunch a, DecBatch b) {
   __shared__ uint32_t sign_tab[128];
   __shared__ uint4 stage[kBlock / 64][256];
   fill_sign_table(sign_tab, a.signs);
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int t = lane & 15, row = lane >> 4;
-  uint4* buf = stage[threadIdx.x >> 6];
-  const int64_t n_groups = (a.n_tiles + 15) / 16;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint4* buf = stage[wave];
   const int64_t stride = (int64_t)gridDim.x * (kBlock / 64);
-  int64_t g = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
-  if (g >= n_groups) return;
+  int64_t g = (int64_t)blockIdx.x * (kBlock / 64) + wave;
+  if (g >= b.n_groups) return;
+  int ic = item_of(b, g);
   DecIn cur;
-  dec_prefetch(a, g, buf, lane, t, cur);
+  dec_prefetch(b.it[ic], g - b.it[ic].group0, buf, lane, t, cur);
   for (;;) {
     uint32_t d[16];
     dec_take(buf, t, row, d);
     __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const int64_t gn = g + stride;
-    const bool more = gn < n_groups;
+    const bool more = gn < b.n_groups;
+    const int in = more ? item_of(b, gn) : ic;
     DecIn nxt;
-    if (more) dec_prefetch(a, gn, buf, lane, t, nxt);
-    dec_group<OUT_BF16>(a, sign_tab, g, t, row, d, cur);
+    if (more) dec_prefetch(b.it[in], gn - b.it[in].group0, buf, lane, t, nxt);
+    dec_group<OUT_BF16>(b.it[ic], sign_tab, g - b.it[ic].group0, t, row, d, cur);
     if (!more) break;
     cur = nxt;
     g = gn;
+    ic = in;
   }
 }
 
@@ -690,21 +706,21 @@ int64_t persistent_grid(int64_t n_tiles, int64_t resident) {
 
 }  // namespace
 
-hipError_t launch_encode_e8_fast(const EncodeLaunch& a, hipStream_t s) {
+hipError_t launch_encode_e8_fast(const EncodeLaunch& a, const EncBatch& b, hipStream_t s) {
   static int occ = 0;
-  const int64_t blocks = persistent_grid(a.n_tiles, resident_blocks(encode_e8_fast, occ));
-  hipLaunchKernelGGL(encode_e8_fast, dim3((unsigned)blocks), dim3(kBlock), 0, s, a);
+  const int64_t blocks = persistent_grid(b.n_groups * 16, resident_blocks(encode_e8_fast, occ));
+  hipLaunchKernelGGL(encode_e8_fast, dim3((unsigned)blocks), dim3(kBlock), 0, s, a, b);
   return hipGetLastError();
 }
 
-hipError_t launch_decode_e8_fast(const DecodeLaunch& a, hipStream_t s) {
+hipError_t launch_decode_e8_fast(const DecodeLaunch& a, const DecBatch& b, hipStream_t s) {
   static int occ_bf16 = 0, occ_f32 = 0;
   if (a.out_bf16) {
-    const int64_t blocks = persistent_grid(a.n_tiles, resident_blocks(decode_e8_fast<true>, occ_bf16));
-    hipLaunchKernelGGL(decode_e8_fast<true>, dim3((unsigned)blocks), dim3(kBlock), 0, s, a);
+    const int64_t blocks = persistent_grid(b.n_groups * 16, resident_blocks(decode_e8_fast<true>, occ_bf16));
+    hipLaunchKernelGGL(decode_e8_fast<true>, dim3((unsigned)blocks), dim3(kBlock), 0, s, a, b);
   } else {
-    const int64_t blocks = persistent_grid(a.n_tiles, resident_blocks(decode_e8_fast<false>, occ_f32));
-    hipLaunchKernelGGL(decode_e8_fast<false>, dim3((unsigned)blocks), dim3(kBlock), 0, s, a);
+    const int64_t blocks = persistent_grid(b.n_groups * 16, resident_blocks(decode_e8_fast<false>, occ_f32));
+    hipLaunchKernelGGL(decode_e8_fast<false>, dim3((unsigned)blocks), dim3(kBlock), 0, s, a, b);
   }
   return hipGetLastError();
 }

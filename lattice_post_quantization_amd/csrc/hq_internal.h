@@ -69,11 +69,50 @@ hipError_t launch_encode(const EncodeLaunch& a, hipStream_t s);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t s);
 hipError_t launch_rate(const RateLaunch& a, hipStream_t s);
 
-// fast path for E8 / tile 256 / bf16 input (encode) and E8 / tile 256 (decode)
+// Fast path for E8 / tile 256 / bf16 input (encode) and E8 / tile 256
+// (decode).  One launch covers up to kMaxItems matrices that share the
+// parameters; groups of 16 tiles are numbered across the items.
+constexpr int kMaxItems = 8;
+
+struct EncItem {
+  const void* x;
+  int8_t* idx;
+  float* scale;
+  uint32_t* coset;
+  uint8_t* rice_k;
+  uint32_t* tile_bits;
+  int64_t n_tiles;
+  int64_t group0;       // first global group of this item
+};
+
+struct EncBatch {
+  int32_t n;
+  int32_t pad;
+  int64_t n_groups;
+  EncItem it[kMaxItems];
+};
+
+struct DecItem {
+  const int8_t* idx;
+  const uint32_t* coset;
+  const float* scale;
+  void* y;
+  int64_t n_tiles;
+  int64_t group0;
+};
+
+struct DecBatch {
+  int32_t n;
+  int32_t pad;
+  int64_t n_groups;
+  DecItem it[kMaxItems];
+};
+
 bool e8_fast_encode_ok(const EncodeLaunch& a);
 bool e8_fast_decode_ok(const DecodeLaunch& a);
-hipError_t launch_encode_e8_fast(const EncodeLaunch& a, hipStream_t s);
-hipError_t launch_decode_e8_fast(const DecodeLaunch& a, hipStream_t s);
+// a: shared parameters (its per-matrix fields are ignored); b: the matrices
+hipError_t launch_encode_e8_fast(const EncodeLaunch& a, const EncBatch& b, hipStream_t s);
+hipError_t launch_decode_e8_fast(const DecodeLaunch& a, const DecBatch& b, hipStream_t s);
 
 // tiles handled by one rate/pack block
 constexpr int kRateTilesPerBlock = 16;

@@ -52,6 +52,17 @@ def make_params(lattice="E8", tile=256, bps=4.0, rht_seed=0, flags=0,
                   int(dither_seed), int(dither_base), int(flags), 0)
 
 
+class EncodeItem(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("scale", ctypes.c_void_p), ("idx", ctypes.c_void_p), ("coset", ctypes.c_void_p),
+                ("rice_k", ctypes.c_void_p), ("tile_bits", ctypes.c_void_p)]
+
+
+class DecodeItem(ctypes.Structure):
+    _fields_ = [("idx", ctypes.c_void_p), ("coset", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("y", ctypes.c_void_p)]
+
+
 _lib = None
 _P = ctypes.c_void_p
 _I32, _I64, _U32, _U64, _SZ = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
@@ -63,6 +74,8 @@ _SIGNATURES = {
     "hq_decode_tiles": (_I32, [_PP, _P, _P, _P, _I64, _I64, _P, _I32, _P, _P]),
     "hq_rate": (_I32, [_PP, _P, _P, _I64, _P, _P, _P, _P, _U64, _P, _P, _SZ, _P, _P]),
     "hq_kv_encode": (_I32, [_PP, _P, _I32, _I64, _P, _P, _P, _P, _P, _P, _P]),
+    "hq_encode_batch": (_I32, [_PP, _I32, _I32, _P, _P, _P]),
+    "hq_decode_batch": (_I32, [_PP, _I32, _I32, _P, _P, _P]),
     "hq_coset_words": (_I32, [_PP]),
     "hq_rate_workspace_bytes": (_SZ, [_I64]),
     "hq_status_string": (ctypes.c_char_p, [_I32]),
@@ -296,3 +309,73 @@ def hq_kv_encode(kv, bps=4.0, rht_seed=0, dither_seed=None, dither_base=0, statu
                               _ptr(status), _stream(dev))
     _check(code, "hq_kv_encode")
     return {"scale": scale, "idx": idx, "coset": coset, "rice_k": rice_k, "tile_bits": tile_bits}
+
+
+def _addr(t):
+    return None if t is None else t.data_ptr()
+
+
+def hq_encode_batch(xs, lattice="E8", tile=256, bps=4.0, rht_seed=0, outs=None, status=None):
+    """hq_encode_tiles on every matrix of `xs` (same dtype, device and
+    parameters) in one call; auto scales.  `outs` may give, per matrix, the
+    preallocated dict hq_encode_tiles would return.  Returns a list of dicts."""
+    if not xs:
+        return []
+    dev = xs[0].device
+    dt = xs[0].dtype
+    res = []
+    for i, x in enumerate(xs):
+        _device_tensor(x, "x")
+        if x.dim() != 2 or x.dtype != dt or x.device != dev:
+            raise ValueError("batched matrices must be 2-D with one dtype and device")
+        rows, cols = x.shape
+        nt = rows * cols // tile if cols % tile == 0 else 0
+        o = dict(outs[i]) if outs is not None else {}
+        w = max(coset_words(lattice, tile), 1)
+        o.setdefault("scale", None)
+        res.append({
+            "scale": o["scale"] if o["scale"] is not None else
+            torch.empty(nt, dtype=torch.float32, device=dev),
+            "idx": o.get("idx") if o.get("idx") is not None else
+            torch.empty((rows, cols), dtype=torch.int8, device=dev),
+            "coset": o.get("coset") if o.get("coset") is not None else
+            torch.empty((nt, w), dtype=torch.int32, device=dev),
+            "rice_k": o.get("rice_k") if o.get("rice_k") is not None else
+            torch.empty(nt, dtype=torch.uint8, device=dev),
+            "tile_bits": o.get("tile_bits") if o.get("tile_bits") is not None else
+            torch.empty(nt, dtype=torch.int32, device=dev),
+        })
+    items = (EncodeItem * len(xs))()
+    for i, (x, r) in enumerate(zip(xs, res)):
+        items[i] = EncodeItem(_addr(x), x.shape[0], x.shape[1], _addr(r["scale"]), _addr(r["idx"]),
+                              _addr(r["coset"]), _addr(r["rice_k"]), _addr(r["tile_bits"]))
+    p = make_params(lattice, tile, bps, rht_seed, HQ_SCALE_AUTO)
+    code = lib().hq_encode_batch(ctypes.byref(p), _dtype_code(dt), len(xs), ctypes.byref(items),
+                                 _ptr(status), _stream(dev))
+    _check(code, "hq_encode_batch")
+    return res
+
+
+def hq_decode_batch(encs, lattice="E8", tile=256, rht_seed=0, out_dtype=torch.bfloat16,
+                    outs=None, status=None):
+    """hq_decode_tiles on every encoded matrix of `encs` (dicts with idx,
+    coset, scale) in one call.  Returns the list of decoded tensors."""
+    if not encs:
+        return []
+    dev = encs[0]["idx"].device
+    ys = []
+    items = (DecodeItem * len(encs))()
+    for i, e in enumerate(encs):
+        _device_tensor(e["idx"], "idx")
+        rows, cols = e["idx"].shape
+        y = outs[i] if outs is not None else torch.empty((rows, cols), dtype=out_dtype, device=dev)
+        if y.dtype != out_dtype:
+            raise ValueError("output dtype mismatch")
+        ys.append(y)
+        items[i] = DecodeItem(_addr(e["idx"]), _addr(e["coset"]), _addr(e["scale"]), rows, cols,
+                              _addr(y))
+    p = make_params(lattice, tile, 4.0, rht_seed, 0)
+    code = lib().hq_decode_batch(ctypes.byref(p), _dtype_code(out_dtype), len(encs),
+                                 ctypes.byref(items), _ptr(status), _stream(dev))
+    _check(code, "hq_decode_batch")
+    return ys

@@ -174,3 +174,26 @@ def test_zero_tiles_is_a_noop_even_with_null_buffers():
     # still validated: a negative size or a bad tile is an error
     assert lib.hq_encode_tiles(ctypes.byref(p), None, 1, 0, 100, None, None, None, None, None,
                                None, None, None) == hq.HQ_EINVAL
+
+
+def test_batch_validation():
+    lib = hq.lib()
+    p = hq.make_params("E8", 256, 4.0, 0, hq.HQ_SCALE_AUTO)
+    items = (hq.EncodeItem * 2)()
+    items[0] = hq.EncodeItem(4096, 4, 256, 4096, 4096, 4096, 4096, 4096)
+    items[1] = hq.EncodeItem(4096, 4, 100, 4096, 4096, 4096, 4096, 4096)   # cols % tile
+    assert lib.hq_encode_batch(ctypes.byref(p), 1, 2, ctypes.byref(items), None, None) == hq.HQ_EINVAL
+    assert lib.hq_encode_batch(ctypes.byref(p), 1, 1, None, None, None) == hq.HQ_EINVAL
+    assert lib.hq_encode_batch(ctypes.byref(p), 1, 0, None, None, None) == hq.HQ_OK
+    pc = hq.make_params("E8", 256, 4.0, 0, hq.HQ_SCALE_AUTO | hq.HQ_WANT_COORDS)
+    assert lib.hq_encode_batch(ctypes.byref(pc), 1, 1, ctypes.byref(items), None,
+                               None) == hq.HQ_EUNSUPPORTED
+    # empty items are skipped by validation, host pointers are refused
+    items[1] = hq.EncodeItem(None, 0, 256, None, None, None, None, None)
+    assert lib.hq_encode_batch(ctypes.byref(p), 1, 1, ctypes.byref(items, ctypes.sizeof(hq.EncodeItem)),
+                               None, None) == hq.HQ_OK
+    assert lib.hq_encode_batch(ctypes.byref(p), 1, 2, ctypes.byref(items), None, None) == hq.HQ_EINVAL
+    d = (hq.DecodeItem * 1)()
+    d[0] = hq.DecodeItem(4096, 4096, 4096, 4, 250, 4096)
+    assert lib.hq_decode_batch(ctypes.byref(p), 1, 1, ctypes.byref(d), None, None) == hq.HQ_EINVAL
+    assert lib.hq_decode_batch(ctypes.byref(p), 5, 1, ctypes.byref(d), None, None) == hq.HQ_EINVAL
