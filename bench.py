@@ -41,6 +41,9 @@ def parse():
                     help="time the oracle on a sample of the workload (rank 0, N=1)")
     ap.add_argument("--cpu-sample-stride", type=int, default=8,
                     help="oracle sample: every k-th tile of layer 0")
+    ap.add_argument("--copy-ref-mib", type=int, default=0,
+                    help="before timing, copy a buffer of this many MiB once (a kernel of "
+                         "known traffic that scales the profiler's byte counters)")
     return ap.parse_args()
 
 
@@ -118,6 +121,13 @@ def main():
     n_weights = sum(x.numel() for xs, _, _ in layers for x in xs)
     n_tiles = n_weights // 256
     tiles_per_layer = [sum(x.numel() for x in xs) // 256 for xs, _, _ in layers]
+
+    if args.copy_ref_mib > 0:
+        src = torch.ones(args.copy_ref_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # events for the timed region are created up front (creation is a host
     # call that would otherwise sit between kernel launches)
