@@ -27,6 +27,71 @@ namespace {
 // that sits in the low mantissa bits.
 constexpr double kMagic = 6755399441055744.0;
 
+// Raw buffer over [base, base + bytes): the hardware drops stores whose
+// offset falls outside and returns zeros for such loads, which replaces
+// per-lane bounds branches around the memory operations of a ragged last
+// group.  Offsets are 32-bit, so each buffer covers one group.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline __amdgpu_buffer_rsrc_t out_rsrc(void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ inline lds_void* lds_ptr(uint4* p) { return (lds_void*)p; }
+
+__device__ inline void store16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t a, uint32_t b,
+                               uint32_t c, uint32_t d) {
+  __builtin_amdgcn_raw_buffer_store_b128((u32x4){a, b, c, d}, r, (int)off, 0, 0);
+}
+
+// Tiles of a group that exist (the last group of a matrix may be short).
+__device__ inline uint32_t live_tiles(int64_t n_tiles, int64_t group) {
+  const int64_t n = n_tiles - group * 16;
+  return (uint32_t)(n < 16 ? n : 16);
+}
+
+// Lanes of one wave exchange data through LDS.  LDS instructions of a wave
+// execute in order, so no wait is needed; the fences (no instruction at
+// wavefront scope) keep the compiler from moving or reusing LDS accesses
+// across the exchange.
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Coalesced store of a group's output.  Lane (t, r) holds CPL 16-byte chunks:
+// chunk k lies at byte r * 16 CPL + 16 k of tile t, and tiles are
+// 64 CPL bytes apart.  The wave writes them, 4 KB (256 chunks) per pass,
+// into a 4 KB LDS buffer and reads them back so that each store instruction
+// covers 1 KB of contiguous output.  Chunk c of a pass sits at LDS slot
+// c ^ ((c >> 4) & 15), which keeps both sides free of bank conflicts.
+template <int CPL>
+__device__ inline void store_group(__amdgpu_buffer_rsrc_t rs, const uint4* chunk, uint4* ost,
+                                   int t, int row) {
+  constexpr int kTilesPerPass = 256 / (4 * CPL);
+  const int lane = row * 16 + t;
+#pragma unroll
+  for (int h = 0; h < 16 / kTilesPerPass; ++h) {
+    wave_lds_sync();
+    if (t / kTilesPerPass == h) {
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) {
+        const int c = (t % kTilesPerPass) * 4 * CPL + row * CPL + k;
+        ost[c ^ ((c >> 4) & 15)] = chunk[k];
+      }
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = 64 * i + lane;
+      const uint4 q = ost[c ^ ((c >> 4) & 15)];
+      store16(rs, (uint32_t)(h * 4096 + 16 * c), q.x, q.y, q.z, q.w);
+    }
+  }
+}
+
 __device__ inline void swap16(uint32_t& a, uint32_t& b) {
   auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
   a = r[0];
@@ -193,32 +258,49 @@ __device__ inline uint32_t byte_sum(uint32_t d, uint32_t acc) {
 // 2k + (b & 1) and the hardware stores it at LDS slot 64 k + l; lane (t, r)
 // later finds chunk j of its tile at slot 64 (t/2) + 16 r + ((t + 2j) mod 16),
 // so each 16-lane row reads 16 different bank groups.
-__device__ inline void enc_prefetch(const EncItem& it, int64_t group, uint4* buf, int lane) {
+// With a caller-supplied scale, a ninth load brings the group's 16 scales to
+// the 256 bytes after the bf16 data (lanes 16-63 repeat them).  Lane offsets
+// are relative to the group's first tile; tiles past the end read as zeros.
+constexpr int kEncStage = 512 + 16;   // uint4 per wave
+
+__device__ inline void enc_prefetch(const EncItem& it, int64_t group, uint4* buf, int lane,
+                                    bool scale_in) {
   const int r = lane >> 4, b = lane & 15;
+  const uint32_t live = live_tiles(it.n_tiles, group);
+  // bytes past the group's live tiles read as zero (their results are dropped)
+  const auto rs = out_rsrc(static_cast<uint16_t*>(const_cast<void*>(it.x)) + group * 16 * 256,
+                           live * 512u);
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int j = ((b >> 1) - k) & 7;
-    int64_t tile = group * 16 + 2 * k + (b & 1);
-    tile = tile < it.n_tiles ? tile : it.n_tiles - 1;   // ragged end: reread a valid tile
-    const uint16_t* src = static_cast<const uint16_t*>(it.x) + tile * 256 + r * 64 + j * 8;
-    __builtin_amdgcn_global_load_lds(src, buf + 64 * k, 16, 0, 0);
+    const int off = (2 * k + (b & 1)) * 512 + r * 128 + j * 16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr(buf + 64 * k), 16, off, 0, 0, 0);
   }
+  if (scale_in)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(out_rsrc(it.scale + group * 16, live * 4u),
+                                             lds_ptr(buf + 512), 4, b * 4, 0, 0, 0);
 }
 
-__device__ inline void enc_take(const uint4* buf, int t, int r, uint32_t* w) {
+__device__ inline void enc_take(const uint4* buf, int t, int r, uint32_t* w, float& scale) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const uint4 q = buf[64 * (t >> 1) + 16 * r + ((t + 2 * j) & 15)];
     w[4 * j] = q.x; w[4 * j + 1] = q.y; w[4 * j + 2] = q.z; w[4 * j + 3] = q.w;
   }
+  scale = reinterpret_cast<const float*>(buf + 512)[t];
+}
+
+// Per-tile results are written by the 16 lanes of row 0; other lanes get an
+// offset past the end of the buffer, which the hardware drops.
+__device__ inline uint32_t row0_offset(int t, int row, int size) {
+  return row == 0 ? (uint32_t)(t * size) : 0x40000000u;
 }
 
 // One group of 16 tiles held by a wave (w: this lane's 64 bf16 of its tile).
+// (scale_in: the caller's scale of this lane's tile when not automatic.)
 __device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const uint32_t* sign_tab,
-                                 int64_t group, int t, int row, const uint32_t* w) {
-  const int64_t tile_raw = group * 16 + t;
-  const bool live = tile_raw < it.n_tiles;
-  const int64_t tile = live ? tile_raw : it.n_tiles - 1;
+                                 int64_t group, int t, int row, const uint32_t* w, float scale_in,
+                                 uint4* ost) {
 
   const uint4* st = reinterpret_cast<const uint4*>(sign_tab + row * 32);
   double v[64];
@@ -248,7 +330,7 @@ __device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const
     delta = bf16_round_to_f32(sqrt(ss / 256.0) * a.c);
     if (delta == 0.0f) delta = 1.0f;
   } else {
-    delta = it.scale[tile];
+    delta = scale_in;
     if (!(delta > 0.0f) || !isfinite(delta)) status |= HQ_ST_NONFINITE;
   }
   if (!isfinite(ss)) status |= HQ_ST_NONFINITE;
@@ -350,19 +432,23 @@ __device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const
     if (!(q & 4)) swap32(packed[q], packed[q + 4]);
 #pragma unroll
   for (int q = 0; q < 8; ++q) swap16(packed[q], packed[q + 8]);
-  if (live) {
-    uint4* dst = reinterpret_cast<uint4*>(it.idx + tile * 256 + row * 64);
+  const uint32_t live = live_tiles(it.n_tiles, group);
+  const int64_t tile0 = group * 16;
+  uint4 ch[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      dst[k] = make_uint4(packed[4 * k], packed[4 * k + 1], packed[4 * k + 2], packed[4 * k + 3]);
-    if (row == 0) {
-      if (a.auto_scale) it.scale[tile] = delta;
-      it.coset[tile] = coset_word;
-      it.rice_k[tile] = (uint8_t)bk;
-      it.tile_bits[tile] = 4u + 32u + best;
-      if (status) set_status(a.status, status);
-    }
-  }
+  for (int k = 0; k < 4; ++k)
+    ch[k] = make_uint4(packed[4 * k], packed[4 * k + 1], packed[4 * k + 2], packed[4 * k + 3]);
+  store_group<4>(out_rsrc(it.idx + tile0 * 256, live * 256u), ch, ost, t, row);
+  if (a.auto_scale)
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(delta), out_rsrc(it.scale + tile0, live * 4u),
+                                          (int)row0_offset(t, row, 4), 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b32(coset_word, out_rsrc(it.coset + tile0, live * 4u),
+                                        (int)row0_offset(t, row, 4), 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b8((uint8_t)bk, out_rsrc(it.rice_k + tile0, live),
+                                       (int)row0_offset(t, row, 1), 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b32(4u + 32u + best, out_rsrc(it.tile_bits + tile0, live * 4u),
+                                        (int)row0_offset(t, row, 4), 0, 0);
+  if (status && row == 0 && (uint32_t)t < live) set_status(a.status, status);
 }
 
 // Persistent waves: each wave walks groups of 16 tiles with a grid-wide
@@ -378,33 +464,42 @@ __device__ inline int item_of(const B& b, int64_t g) {
   return i;
 }
 
+// The loop body ends with reading the next group from LDS, after this
+// group's stores; the last iteration prefetches its own group again (an L2
+// hit) so that no branch surrounds the memory operations.
 __global__ __launch_bounds__(kBlock) void encode_e8_fast(EncodeLaunch a, EncBatch b) {
   __shared__ uint32_t sign_tab[128];
-  __shared__ uint4 stage[kBlock / 64][512];
+  __shared__ uint4 stage[kBlock / 64][kEncStage];
+  __shared__ uint4 ostage[kBlock / 64][256];
   fill_sign_table(sign_tab, a.signs);
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int t = lane & 15, row = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint4* buf = stage[wave];
+  const bool scale_in = !a.auto_scale;
   const int64_t stride = (int64_t)gridDim.x * (kBlock / 64);
   int64_t g = (int64_t)blockIdx.x * (kBlock / 64) + wave;
   if (g >= b.n_groups) return;
   int ic = item_of(b, g);
-  enc_prefetch(b.it[ic], g - b.it[ic].group0, buf, lane);
+  uint32_t w[32];
+  float sc;
+  enc_prefetch(b.it[ic], g - b.it[ic].group0, buf, lane, scale_in);
+  enc_take(buf, t, row, w, sc);
   for (;;) {
-    uint32_t w[32];
-    enc_take(buf, t, row, w);
     // every lane's reads of the buffer complete before it is refilled
     __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const int64_t gn = g + stride;
     const bool more = gn < b.n_groups;   // uniform across the wave
-    const int in = more ? item_of(b, gn) : ic;
-    if (more) enc_prefetch(b.it[in], gn - b.it[in].group0, buf, lane);
-    enc_group(a, b.it[ic], sign_tab, g - b.it[ic].group0, t, row, w);
+    const int64_t gp = more ? gn : g;
+    const int ip = more ? item_of(b, gn) : ic;
+    enc_prefetch(b.it[ip], gp - b.it[ip].group0, buf, lane, scale_in);
+    enc_group(a, b.it[ic], sign_tab, g - b.it[ic].group0, t, row, w, sc, ostage[wave]);
+    __builtin_amdgcn_sched_barrier(0);
+    enc_take(buf, t, row, w, sc);
     if (!more) break;
     g = gn;
-    ic = in;
+    ic = ip;
   }
 }
 
@@ -433,41 +528,46 @@ __device__ inline uint32_t half_butterfly(uint32_t x) {
 // 4k + 3).  Lane l = 16 r + b of instruction k fetches row r, chunk
 // j = (b/4 - k) mod 4 of tile 4k + (b & 3) into slot 64 k + l; lane (t, r)
 // reads chunk j of its tile from slot 64 (t/4) + 16 r + ((t + 4j) mod 16).
+// Two more loads bring the group's coset words and scales (lanes 0-15; the
+// other lanes repeat them) to the 512 bytes after the indices.
+constexpr int kDecStage = 256 + 32;   // uint4 per wave
+
 struct DecIn {
   uint32_t cw;
   float scale;
 };
 
-__device__ inline void dec_prefetch(const DecItem& it, int64_t group, uint4* buf, int lane, int t,
-                                    DecIn& in) {
+__device__ inline void dec_prefetch(const DecItem& it, int64_t group, uint4* buf, int lane) {
   const int r = lane >> 4, b = lane & 15;
+  const uint32_t live = live_tiles(it.n_tiles, group);
+  const auto rs = out_rsrc(const_cast<int8_t*>(it.idx) + group * 16 * 256, live * 256u);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int j = ((b >> 2) - k) & 3;
-    int64_t tile = group * 16 + 4 * k + (b & 3);
-    tile = tile < it.n_tiles ? tile : it.n_tiles - 1;
-    __builtin_amdgcn_global_load_lds(it.idx + tile * 256 + r * 64 + j * 16, buf + 64 * k, 16, 0, 0);
+    const int off = (4 * k + (b & 3)) * 256 + r * 64 + j * 16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr(buf + 64 * k), 16, off, 0, 0, 0);
   }
-  int64_t tile = group * 16 + t;
-  tile = tile < it.n_tiles ? tile : it.n_tiles - 1;
-  in.cw = it.coset[tile];
-  in.scale = it.scale[tile];
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      out_rsrc(const_cast<uint32_t*>(it.coset) + group * 16, live * 4u), lds_ptr(buf + 256), 4,
+      b * 4, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      out_rsrc(const_cast<float*>(it.scale) + group * 16, live * 4u), lds_ptr(buf + 272), 4,
+      b * 4, 0, 0, 0);
 }
 
-__device__ inline void dec_take(const uint4* buf, int t, int r, uint32_t* d) {
+__device__ inline void dec_take(const uint4* buf, int t, int r, uint32_t* d, DecIn& in) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const uint4 q = buf[64 * (t >> 2) + 16 * r + ((t + 4 * j) & 15)];
     d[4 * j] = q.x; d[4 * j + 1] = q.y; d[4 * j + 2] = q.z; d[4 * j + 3] = q.w;
   }
+  in.cw = reinterpret_cast<const uint32_t*>(buf + 256)[t];
+  in.scale = reinterpret_cast<const float*>(buf + 272)[t];
 }
 
 template <bool OUT_BF16>
 __device__ inline void dec_group(const DecItem& it, const uint32_t* sign_tab, int64_t group, int t,
-                                 int row, const uint32_t* d, const DecIn& in) {
-  const int64_t tile_raw = group * 16 + t;
-  const bool live = tile_raw < it.n_tiles;
-  const int64_t tile = live ? tile_raw : it.n_tiles - 1;
+                                 int row, const uint32_t* d, const DecIn& in, uint4* ost) {
   const uint32_t cw = in.cw >> (8 * row);        // this lane's 8 blocks
   const float dsc = in.scale * 0.03125f;         // Delta / 32, exact
 
@@ -597,15 +697,16 @@ __device__ inline void dec_group(const DecItem& it, const uint32_t* sign_tab, in
       if (!(m & 8)) swap32(o[m], o[m + 8]);
 #pragma unroll
     for (int m = 0; m < 16; ++m) swap16(o[m], o[m + 16]);
-    if (live) {
-      uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(it.y) + tile * 256 + row * 64);
+    uint4 ch[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const uint4 sm = st[k];
-        dst[k] = make_uint4(o[4 * k] ^ sm.x, o[4 * k + 1] ^ sm.y, o[4 * k + 2] ^ sm.z,
-                            o[4 * k + 3] ^ sm.w);
-      }
+    for (int k = 0; k < 8; ++k) {
+      const uint4 sm = st[k];
+      ch[k] = make_uint4(o[4 * k] ^ sm.x, o[4 * k + 1] ^ sm.y, o[4 * k + 2] ^ sm.z,
+                         o[4 * k + 3] ^ sm.w);
     }
+    store_group<8>(out_rsrc(static_cast<uint16_t*>(it.y) + group * 16 * 256,
+                            live_tiles(it.n_tiles, group) * 512u),
+                   ch, ost, t, row);
   } else {
     uint32_t o[64];
 #pragma unroll
@@ -615,22 +716,29 @@ __device__ inline void dec_group(const DecItem& it, const uint32_t* sign_tab, in
       if (!(i & 16)) swap32(o[i], o[i + 16]);
 #pragma unroll
     for (int i = 0; i < 32; ++i) swap16(o[i], o[i + 32]);
-    if (live) {
-      uint4* dst = reinterpret_cast<uint4*>(static_cast<float*>(it.y) + tile * 256 + row * 64);
+    uint4 ch[16];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const uint32_t sm = sign_tab[row * 32 + 2 * k], sn = sign_tab[row * 32 + 2 * k + 1];
-        dst[k] = make_uint4(o[4 * k] ^ (sm << 16), o[4 * k + 1] ^ (sm & 0x80000000u),
-                            o[4 * k + 2] ^ (sn << 16), o[4 * k + 3] ^ (sn & 0x80000000u));
-      }
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t sm = sign_tab[row * 32 + 2 * k], sn = sign_tab[row * 32 + 2 * k + 1];
+      ch[k] = make_uint4(o[4 * k] ^ (sm << 16), o[4 * k + 1] ^ (sm & 0x80000000u),
+                         o[4 * k + 2] ^ (sn << 16), o[4 * k + 3] ^ (sn & 0x80000000u));
     }
+    store_group<16>(out_rsrc(static_cast<float*>(it.y) + group * 16 * 256,
+                             live_tiles(it.n_tiles, group) * 1024u),
+                    ch, ost, t, row);
   }
 }
 
+// Persistent waves as in the encoder.  The loop body ends with reading the
+// next group from LDS, after this group's stores, so the wait for the
+// prefetch never includes those stores; the last iteration prefetches its
+// own group again (an L2 hit) to keep the loop free of branches around
+// memory operations.
 template <bool OUT_BF16>
 __global__ __launch_bounds__(kBlock) void decode_e8_fast(DecodeLaunch a, DecBatch b) {
   __shared__ uint32_t sign_tab[128];
-  __shared__ uint4 stage[kBlock / 64][256];
+  __shared__ uint4 stage[kBlock / 64][kDecStage];
+  __shared__ uint4 ostage[kBlock / 64][256];
   fill_sign_table(sign_tab, a.signs);
   __syncthreads();
   const int lane = threadIdx.x & 63;
@@ -641,22 +749,24 @@ __global__ __launch_bounds__(kBlock) void decode_e8_fast(DecodeLaunch a, DecBatc
   int64_t g = (int64_t)blockIdx.x * (kBlock / 64) + wave;
   if (g >= b.n_groups) return;
   int ic = item_of(b, g);
-  DecIn cur;
-  dec_prefetch(b.it[ic], g - b.it[ic].group0, buf, lane, t, cur);
+  uint32_t d[16];
+  DecIn in;
+  dec_prefetch(b.it[ic], g - b.it[ic].group0, buf, lane);
+  dec_take(buf, t, row, d, in);
   for (;;) {
-    uint32_t d[16];
-    dec_take(buf, t, row, d);
+    // every lane's reads of the buffer complete before it is refilled
     __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     const int64_t gn = g + stride;
-    const bool more = gn < b.n_groups;
-    const int in = more ? item_of(b, gn) : ic;
-    DecIn nxt;
-    if (more) dec_prefetch(b.it[in], gn - b.it[in].group0, buf, lane, t, nxt);
-    dec_group<OUT_BF16>(b.it[ic], sign_tab, g - b.it[ic].group0, t, row, d, cur);
+    const bool more = gn < b.n_groups;   // uniform across the wave
+    const int64_t gp = more ? gn : g;
+    const int ip = more ? item_of(b, gn) : ic;
+    dec_prefetch(b.it[ip], gp - b.it[ip].group0, buf, lane);
+    dec_group<OUT_BF16>(b.it[ic], sign_tab, g - b.it[ic].group0, t, row, d, in, ostage[wave]);
+    __builtin_amdgcn_sched_barrier(0);
+    dec_take(buf, t, row, d, in);
     if (!more) break;
-    cur = nxt;
     g = gn;
-    ic = in;
+    ic = ip;
   }
 }
 
