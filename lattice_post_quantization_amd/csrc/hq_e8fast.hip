@@ -172,67 +172,109 @@ __device__ inline void fill_sign_table(uint32_t* tab, const uint32_t* signs) {
 //   integer coset a_i = I_i + [F_i > 2^23], half coset b_i = I_i (+ 1/2),
 //   parity fixes on the first max/min of B, coset choice by
 //   D = 2^25 - sum B + [odd a] 2 min B - [odd b] (2^24 - 2 max B) > 0.
+// Bit 24 of U_i is the parity of I_i and bit 23 is [F_i > 2^23], so both
+// parities come from the XOR of the eight U_i.  The stored integers are
+// built as bytes: the top byte of U_i is I_i; coset a adds the bit-23 bits
+// and the parity flip adds +/-1 to one byte.  The bytes carry a bias of 128
+// while they are added to, so no byte carries into the next (a tile without
+// the overflow flag has |u_i| < 126, keeping every biased byte in 0..255).
+// The last coordinate is stored halved, from U_7 + [coset a] 2^23 with its
+// flip applied before halving.
 // Blocks with a coordinate on an integer or half-integer take the general
 // decoder (rare; same results).  Writes the stored integers (z0..z6,
-// floor(z7/2)) and returns the coset bit.
+// floor(z7/2)) as two dwords of int8 and returns the coset bit.
 __device__ inline uint32_t sad_u32(uint32_t a, uint32_t b) {
   uint32_t r;
   __asm__("v_sad_u32 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
   return r;
 }
 
-__device__ inline int e8_block(const int32_t* U, int32_t* s) {
-  int32_t I[8];
-  uint32_t up[8], k1[8], k2[8];
-  uint32_t sumB = 0, upc = 0;
-  int32_t xi = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t F = (uint32_t)U[i] & 0xFFFFFFu;
-    I[i] = U[i] >> 24;
-    const uint32_t B = sad_u32(F, (uint32_t)kHalf);       // |F - 2^23|
-    up[i] = ((uint32_t)kHalf - F) >> 31;                   // F > 2^23
-    k1[i] = (B << 3) | (uint32_t)i;
-    k2[i] = (B << 3) | (uint32_t)(7 - i);
-    sumB += B;
-    upc += up[i];
-    xi ^= I[i];
+// |a - 2^26| + C (C an inline constant)
+template <int C>
+__device__ inline uint32_t sad26(uint32_t a) {
+  uint32_t r;
+  __asm__("v_sad_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(1u << 26), "i"(C));
+  return r;
+}
+
+__device__ inline uint32_t min3u(uint32_t a, uint32_t b, uint32_t c) {
+  const uint32_t m = a < b ? a : b;
+  return m < c ? m : c;
+}
+__device__ inline uint32_t max3u(uint32_t a, uint32_t b, uint32_t c) {
+  const uint32_t m = a > b ? a : b;
+  return m > c ? m : c;
+}
+
+// top bytes of four dwords, in order, as one dword
+__device__ inline uint32_t top_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return __builtin_amdgcn_perm(b, a, 0x0C0C0703u) | __builtin_amdgcn_perm(d, c, 0x07030C0Cu);
+}
+
+// byte 2 of four dwords, in order
+__device__ inline uint32_t third_bytes(int32_t a, int32_t b, int32_t c, int32_t d) {
+  return __builtin_amdgcn_perm((uint32_t)b, (uint32_t)a, 0x0C0C0602u) |
+         __builtin_amdgcn_perm((uint32_t)d, (uint32_t)c, 0x06020C0Cu);
+}
+
+__device__ inline uint32_t pack4(const int32_t* s);
+
+__device__ inline int e8_block(const int32_t* U, uint32_t& p0, uint32_t& p1) {
+  // keys (B << 3) + i and (B << 3) + 7 - i: |8F - 2^26| plus the index
+  uint32_t k1[8], k2[8];
+#define HQ_E8_KEYS(i)                                             \
+  {                                                               \
+    const uint32_t F8 = ((uint32_t)U[i] << 3) & 0x07FFFFFFu;      \
+    k1[i] = sad26<i>(F8);                                         \
+    k2[i] = sad26<7 - i>(F8);                                     \
   }
-  uint32_t kmin = k1[0], kmax = k2[0];
-#pragma unroll
-  for (int i = 1; i < 8; ++i) {
-    kmin = k1[i] < kmin ? k1[i] : kmin;
-    kmax = k2[i] > kmax ? k2[i] : kmax;
-  }
+  HQ_E8_KEYS(0) HQ_E8_KEYS(1) HQ_E8_KEYS(2) HQ_E8_KEYS(3)
+  HQ_E8_KEYS(4) HQ_E8_KEYS(5) HQ_E8_KEYS(6) HQ_E8_KEYS(7)
+#undef HQ_E8_KEYS
+  const uint32_t kmin = min3u(min3u(k1[0], k1[1], k1[2]), min3u(k1[3], k1[4], k1[5]),
+                              k1[6] < k1[7] ? k1[6] : k1[7]);
+  const uint32_t kmax = max3u(max3u(k2[0], k2[1], k2[2]), max3u(k2[3], k2[4], k2[5]),
+                              k2[6] > k2[7] ? k2[6] : k2[7]);
   const int32_t bmin = (int32_t)(kmin >> 3), bmax = (int32_t)(kmax >> 3);
   if (bmin == 0 || bmax == kHalf) {
     int32_t z[8];
     const int c = e8_nearest(U, z);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s[i] = (i == 7) ? (z[i] >> 1) : z[i];
+    z[7] >>= 1;
+    p0 = pack4(z);
+    p1 = pack4(z + 4);
     return c;
   }
-  const int ja = (int)(kmin & 7u), jb = 7 - (int)(kmax & 7u);
-  const int odd_b = xi & 1, odd_a = (xi ^ (int32_t)upc) & 1;
+  const uint32_t sumB =
+      (((k1[0] + k1[1] + k1[2]) + (k1[3] + k1[4] + k1[5]) + (k1[6] + k1[7])) - 28u) >> 3;
+  const uint32_t X = ((uint32_t)U[0] ^ (uint32_t)U[1] ^ (uint32_t)U[2]) ^
+                     ((uint32_t)U[3] ^ (uint32_t)U[4] ^ (uint32_t)U[5]) ^
+                     ((uint32_t)U[6] ^ (uint32_t)U[7]);
+  const int odd_b = (int)((X >> 24) & 1u);                 // sum I odd
+  const int odd_a = (int)(((X >> 23) ^ (X >> 24)) & 1u);   // sum (I + up) odd
   const int32_t D = (1 << 25) - (int32_t)sumB + (odd_a ? 2 * bmin : 0) -
                     (odd_b ? (1 << 24) - 2 * bmax : 0);
   const int c = D > 0;
-  const uint32_t nc = (uint32_t)(1 - c);
-  const int jf = c ? jb : ja;
-  const uint32_t oh = (uint32_t)(c ? odd_b : odd_a) << jf;    // one-hot flip position
-  // the flipped coordinate moves towards u: coset a: +1 unless it was
-  // rounded up; coset b: +1 when u lies above the half-integer
-  uint32_t upmask = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) upmask |= up[i] << i;
-  const int32_t upj = (int32_t)((upmask >> jf) & 1u);
-  const int32_t step = c ? (2 * upj - 1) : (1 - 2 * upj);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int32_t z = (int32_t)((uint32_t)I[i] + up[i] * nc);
-    z += (int32_t)((oh >> i) & 1u) * step;
-    s[i] = (i == 7) ? (z >> 1) : z;
-  }
+  const uint32_t jf = c ? 7u - (kmax & 7u) : (kmin & 7u);
+  const int odd = c ? odd_b : odd_a;
+  // byte k of Gq: byte 2 of U_{4q+k}, whose bit 7 is [F > 2^23]
+  const uint32_t G0 = third_bytes(U[0], U[1], U[2], U[3]);
+  const uint32_t G1 = third_bytes(U[4], U[5], U[6], U[7]);
+  const uint32_t upj = (uint32_t)((((uint64_t)G1 << 32) | G0) >> (8 * jf + 7)) & 1u;
+  // The flipped coordinate moves away from u's rounding in coset a (-1 when
+  // rounded up) and towards u in coset b (+1 when u lies above the
+  // half-integer).
+  const bool neg = ((uint32_t)c ^ upj) != 0u;
+  const uint32_t jo = odd ? jf : 8u;                       // 8: no flip
+  const int32_t s7 = (int32_t)((uint32_t)U[7] + (c ? 0u : (uint32_t)kHalf) +
+                               (jo == 7u ? (neg ? 0xFF000000u : 0x01000000u) : 0u)) >> 1;
+  const uint32_t d = (neg ? 0xFFFFFFFFu : 1u) << (8u * (jo & 3u));
+  const uint32_t up0 = c ? 0u : (G0 >> 7) & 0x01010101u;
+  const uint32_t up1 = c ? 0u : (G1 >> 7) & 0x00010101u;
+  constexpr uint32_t kBias = 0x80808080u;
+  p0 = ((top_bytes((uint32_t)U[0], (uint32_t)U[1], (uint32_t)U[2], (uint32_t)U[3]) ^ kBias) + up0 +
+        (jo < 4u ? d : 0u)) ^ kBias;
+  p1 = ((top_bytes((uint32_t)U[4], (uint32_t)U[5], (uint32_t)U[6], (uint32_t)s7) ^ kBias) + up1 +
+        (jo - 4u < 3u ? d : 0u)) ^ kBias;
   return c;
 }
 
@@ -376,19 +418,17 @@ __device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const
   const int r0 = row & 1, r1 = row >> 1;
 #pragma unroll
   for (int blk = 0; blk < 8; ++blk) {
-    int32_t U[8], s[8];
+    int32_t U[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       // two roundings, never fused: q = RN(S K), then RN(q + 1.5 2^52)
       const double m = __dadd_rn(__dmul_rn(v[8 * blk + i], K), kMagic);
       U[i] = (int32_t)(uint32_t)(uint64_t)__double_as_longlong(m);
     }
-    const int c = e8_block(U, s);
+    const int c = e8_block(U, packed[2 * blk], packed[2 * blk + 1]);
     // tile block index = b3 + 2 b4 + 4 b5 + 8 b6 + 16 b7
     const int bpos = (blk & 1) + 2 * r1 + 4 * r0 + 8 * (blk >> 2) + 16 * ((blk >> 1) & 1);
     cbits |= (uint32_t)c << bpos;
-    packed[2 * blk] = pack4(s);
-    packed[2 * blk + 1] = pack4(s + 4);
   }
   const uint32_t coset_word = tile_or_u32(cbits);
 
