@@ -283,10 +283,12 @@ __device__ inline uint32_t pack4(const int32_t* s) {
          (((uint32_t)s[2] & 0xFFu) << 16) | ((uint32_t)s[3] << 24);
 }
 
-// zigzag of four int8 values held in a dword, bytewise
+// zigzag of four int8 values held in a dword, bytewise: 2z, or its
+// complement for negative z.  v_perm selectors 8-11 replicate the sign bits
+// of bytes 1, 3, 5, 7 of {d << 8, d}, i.e. of bytes 1, 3, 0, 2 of d.
 __device__ inline uint32_t zigzag4(uint32_t d) {
-  const uint32_t sgn = (d >> 7) & 0x01010101u;
-  return ((d << 1) & 0xFEFEFEFEu) ^ (sgn * 0xFFu);
+  const uint32_t neg = __builtin_amdgcn_perm(d << 8, d, 0x090B080Au);
+  return ((d << 1) & 0xFEFEFEFEu) ^ neg;
 }
 
 __device__ inline uint32_t byte_sum(uint32_t d, uint32_t acc) {
@@ -432,9 +434,13 @@ __device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const
   }
   const uint32_t coset_word = tile_or_u32(cbits);
 
-  // ---- Rice parameter: k = argmin_k sum(floor(zeta/2^k)) + 256 (1 + k).
-  // With S = sum zeta and kt the smallest k with S <= 256 * 2^(k+1), only
-  // kt - 1 .. kt + 2 can be optimal (convexity bound); k >= 9 never is.
+  // ---- Rice parameter: k = argmin_k L(k), L(k) = Q_k + 256 (1 + k),
+  // Q_k = sum floor(zeta / 2^k).  L is convex: L(k+1) - L(k) = 256 - D_k with
+  // D_k = Q_k - Q_{k+1} = sum floor((zeta + 2^k) / 2^(k+1)), which falls
+  // with k, so the first minimum is the smallest k with D_k <= 256.  D_k lies
+  // within 128 of S / 2^(k+1) (S = sum zeta), so with kt the smallest k with
+  // S <= 256 * 2^(k+1): D_{kt+1} <= 256, and D_k > 256 for k <= kt - 2
+  // (strictly, so no smaller k ties).  Only kt - 1, kt, kt + 1 remain.
   uint32_t zz[16];
   uint32_t S = 0;
 #pragma unroll
@@ -445,10 +451,10 @@ __device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const
   S = tile_sum_u32(S);
   int kt = 0;
   while (kt < 8 && S > (256u << (kt + 1))) ++kt;
-  int kc[4];
-  uint32_t R[4];
+  int kc[3];
+  uint32_t R[3];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 3; ++j) {
     int k = kt - 1 + j;
     kc[j] = k < 0 ? 0 : (k > 8 ? 8 : k);
     const uint32_t mask = ((1u << kc[j]) - 1u) * 0x01010101u;
@@ -460,7 +466,7 @@ __device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const
   uint32_t best = 0xFFFFFFFFu;
   int bk = 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 3; ++j) {
     const uint32_t Rk = tile_sum_u32(R[j]);
     const uint32_t L = ((S - Rk) >> kc[j]) + 256u * (uint32_t)(1 + kc[j]);
     if (L < best) { best = L; bk = kc[j]; }
