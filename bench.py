@@ -62,6 +62,9 @@ def parse():
                     help="time the oracle on a sample of the workload (rank 0, N=1)")
     ap.add_argument("--cpu-sample-stride", type=int, default=4,
                     help="oracle sample: every k-th tile of layer 0")
+    ap.add_argument("--secondary", type=int, default=1,
+                    help="after the timed steps, also time the pack pass and the KV path "
+                         "(reported beside the headline, never in it)")
     ap.add_argument("--copy-ref-mib", type=int, default=0,
                     help="before timing, copy a buffer of this many MiB once (a kernel of "
                          "known traffic that scales the profiler's byte counters)")
@@ -115,6 +118,78 @@ def cpu_baseline(stride, bps):
 
 
 # ------------------------------------------------------------------- GPU
+
+def time_calls(fn, reps, warm=2):
+    """Average milliseconds of fn() over reps calls, HIP events on the
+    current stream (fn launches on it)."""
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def secondary(layer0, bps, dev):
+    """Steps outside the headline: the rate + pack pass over one layer's
+    indices (its own pass over the encoder's output) and the KV path (dithered
+    E8 encode and decode of one layer's K and V cache, [8, 32768, 128] each)."""
+    import numpy as np
+    import torch
+
+    import workloads
+    from lattice_post_quantization_amd import hq
+    _, encs, _ = layer0
+    outs = [hq.hq_rate(e["idx"], e["coset"], "E8", 256, pack=True) for e in encs]
+
+    def pack_layer():
+        for e, o in zip(encs, outs):
+            hq.hq_rate(e["idx"], e["coset"], "E8", 256, pack=True, out=o)
+
+    ms = time_calls(pack_layer, 10)
+    torch.cuda.synchronize()
+    tiles = sum(e["idx"].numel() for e in encs) // 256
+    words = sum(int(o["tile_word_offset"][-1].item()) for o in outs)
+    # the method reads idx + coset once and writes k, bits, offsets and the
+    # words (this implementation reads the indices twice: rate, then pack)
+    alg = tiles * (256 + 4) + tiles * (1 + 4 + 8) + 4 * words
+    pack = {"workload": "rate + pack of one Llama-3.1-8B-shaped layer's E8 indices "
+                        "(seven calls, %d tiles)" % tiles,
+            "us": round(ms * 1e3, 2), "algorithmic_gbs": round(alg / (ms * 1e-3) / 1e9, 1),
+            "stream_bits_per_weight": round(32.0 * words / (tiles * 256), 4)}
+
+    kb, vb = workloads.kv_layer()
+    kvs = [torch.from_numpy(a.reshape(-1, 128).view(np.int16)).to(dev).view(torch.bfloat16)
+           for a in (kb, vb)]
+    n_vec = sum(t.shape[0] for t in kvs)
+    encs_kv = [hq.hq_kv_encode(t, bps, 1, dither_seed=2) for t in kvs]
+    ys = [torch.empty_like(t) for t in kvs]
+
+    def kv_enc():
+        for t, o in zip(kvs, encs_kv):
+            hq.hq_kv_encode(t, bps, 1, dither_seed=2, out=o)
+
+    def kv_dec():
+        for o, y in zip(encs_kv, ys):
+            hq.hq_decode_tiles(o["idx"], o["coset"], o["scale"], "E8", 128, 1, torch.bfloat16,
+                               dither_seed=2, out=y)
+
+    ms_e = time_calls(kv_enc, 10)
+    ms_d = time_calls(kv_dec, 10)
+    # per 128-vector: 256 B in / 128 B idx + 4 coset + 1 k + 4 bits + 4 scale
+    kv = {"workload": "dithered E8 encode and decode of K and V [8, 32768, 128] bf16 "
+                      "(%d vectors of 128, 4 bps)" % n_vec,
+          "encode_us": round(ms_e * 1e3, 2), "decode_us": round(ms_d * 1e3, 2),
+          "encode_algorithmic_gbs": round(n_vec * (256 + 141) / (ms_e * 1e-3) / 1e9, 1),
+          "decode_algorithmic_gbs": round(n_vec * (128 + 8 + 256) / (ms_d * 1e-3) / 1e9, 1)}
+    return {"pack": pack, "kv": kv}
+
 
 def main():
     args = parse()
@@ -216,6 +291,8 @@ def main():
         t = MEASURED_TRAFFIC[dom_name]
         traffic = round((t["read"] + t["write"]) * tiles_per_launch)
 
+    extra = secondary(layers[0], args.bps, dev) if args.secondary else None
+
     value = 2.0 * n_weights / (ms_per_step * 1e-3) / 1e9
     alg = (ENC_BYTES_PER_TILE + DEC_BYTES_PER_TILE) * n_tiles / (ms_per_step * 1e-3) / 1e9
     out = {
@@ -258,6 +335,7 @@ def main():
         "host_wall_ms_per_step": round(wall * 1e3 / args.steps, 3),
         "gpu_event_ms_per_step": round(gpu_ms / args.steps, 3),
         "cpu_baseline": cpu,
+        "secondary": extra,
     }
     print(json.dumps(out), flush=True)
 

@@ -261,8 +261,12 @@ def hq_rate(idx, coset, lattice="E8", tile=256, pack=False, capacity_words=None,
         stream = o.get("stream")
         if stream is None:
             stream = torch.empty(max(int(capacity_words), 1), dtype=torch.int32, device=dev)
-        offs = torch.empty(n_tiles + 1, dtype=torch.int64, device=dev)
-        ws = torch.empty(max(rate_workspace_bytes(n_tiles), 8), dtype=torch.uint8, device=dev)
+        offs = o.get("tile_word_offset")
+        if offs is None:
+            offs = torch.empty(n_tiles + 1, dtype=torch.int64, device=dev)
+        ws = o.get("workspace")
+        if ws is None:
+            ws = torch.empty(max(rate_workspace_bytes(n_tiles), 8), dtype=torch.uint8, device=dev)
     p = make_params(lattice, tile, 4.0)
     code = lib().hq_rate(ctypes.byref(p), _ptr(idx), _ptr(coset), n_tiles, _ptr(rice_k),
                          _ptr(tile_bits), _ptr(total), _ptr(stream),
@@ -273,6 +277,7 @@ def hq_rate(idx, coset, lattice="E8", tile=256, pack=False, capacity_words=None,
     if pack:
         res["stream"] = stream
         res["tile_word_offset"] = offs
+        res["workspace"] = ws
     return res
 
 

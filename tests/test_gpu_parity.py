@@ -335,3 +335,49 @@ def test_batched_calls_match_single_calls_and_oracle():
                               256, "batch item %d" % i)
             yo = codec.bf16_rne(codec.decode(ora["idx"], ora["coset"], ora["scale"], "E8", 256, 9))
             assert np.array_equal(T.bf16_host_bits(y).reshape(-1, 256), codec.bf16_bits(yo)), i
+
+
+def test_stack_sampled_parity_as_benchmarked():
+    """The 32-layer Llama-3.1-8B-shaped stack exactly as bench.py runs it:
+    each layer drawn on the GPU, one batched encode of its seven matrices and
+    one batched decode (E8, tile 256, 4 bps, RHT seed = layer index).  Every
+    4099th tile of every matrix is copied to the host and checked against the
+    oracle: scale, indices and cosets, Rice k and bits, and the decoded bf16
+    of tiles whose indices match."""
+    dev = torch.device("cuda")
+    stride = 4099
+    n_checked = 0
+    for layer in range(32):
+        say("case: stack layer %d" % layer)
+        xs = [workloads.llama_stack_torch(layer, m, dev) for m in range(len(workloads.LLAMA_LAYER))]
+        encs = hq.hq_encode_batch(xs, "E8", 256, 4.0, layer)
+        ys = hq.hq_decode_batch(encs, "E8", 256, layer, torch.bfloat16)
+        torch.cuda.synchronize()
+        parts = {k: [] for k in ("x", "scale", "idx", "coset", "rice_k", "tile_bits", "y")}
+        for x, e, y in zip(xs, encs, ys):
+            sel = torch.arange(0, x.numel() // 256, stride, device=dev)
+            parts["x"].append(T.bf16_host_bits(x.view(-1, 256)[sel]))
+            parts["scale"].append(T.host(e["scale"].view(-1)[sel]))
+            parts["idx"].append(T.host(e["idx"].view(-1, 256)[sel]))
+            parts["coset"].append(T.u32(e["coset"].view(-1, 1)[sel]))
+            parts["rice_k"].append(T.host(e["rice_k"].view(-1)[sel]))
+            parts["tile_bits"].append(T.u32(e["tile_bits"].view(-1)[sel]))
+            parts["y"].append(T.bf16_host_bits(y.view(-1, 256)[sel]))
+        del xs, encs, ys
+        g = {k: np.concatenate(v) for k, v in parts.items()}
+        X = workloads.bf16_bits_to_f64(g["x"]).reshape(-1, 256)
+        ora = codec.encode(X, "E8", 256, 4.0, rht_seed=layer)
+        skip = midpoint_close(oracle_pre_scale(X, "E8", 4.0))
+        assert np.array_equal(g["scale"].astype(np.float64)[~skip], ora["scale"][~skip]), layer
+        keep = np.nonzero(g["scale"].astype(np.float64) == ora["scale"])[0]
+        sub = {k: (v[keep] if isinstance(v, np.ndarray) and v.shape[:1] == (len(X),) else v)
+               for k, v in ora.items()}
+        _, _, _, ok = T.compare_indices(g["idx"][keep], g["coset"][keep], sub, "E8", 256,
+                                        "stack layer %d" % layer)
+        assert np.array_equal(g["rice_k"][keep][ok].astype(np.int64), sub["rice_k"][ok]), layer
+        assert np.array_equal(g["tile_bits"][keep][ok].astype(np.int64), sub["tile_bits"][ok]), layer
+        yo = codec.bf16_rne(codec.decode(sub["idx"][ok], sub["coset"][ok], sub["scale"][ok],
+                                         "E8", 256, layer))
+        assert np.array_equal(g["y"][keep][ok].reshape(-1, 256), codec.bf16_bits(yo)), layer
+        n_checked += len(X)
+    say("stack: %d sampled tiles checked" % n_checked)
