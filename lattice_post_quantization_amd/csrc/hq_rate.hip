@@ -8,15 +8,17 @@
 // packed, Rice-coded lattice-index checkpoint format).
 //
 // Three kernels:
-//   rate_kernel  per tile: zigzag, k = argmin payload, tile_bits; per block:
-//                the sum of ceil(tile_bits/32) into the workspace; the total
-//                bit count is accumulated with one 64-bit atomic per block.
+//   rate_kernel  per tile (16 indices per lane): zigzag bytewise, k from
+//                byte sums over three candidates, tile_bits; per block the
+//                sum of ceil(tile_bits/32) into the workspace; the total bit
+//                count is accumulated with one 64-bit atomic per block.
 //   scan_kernel  one block: exclusive prefix sum of the per-block word sums.
-//   pack_kernel  per tile: code lengths -> in-tile exclusive scan (lanes and
-//                lane groups) -> bit positions; codes are OR-ed into an LDS
-//                copy of the tile's words, which is then stored at the
-//                tile's word offset.  Tiles are word aligned, so no two
-//                tiles share a word.
+//   pack_kernel  per tile: each lane's payload length from byte sums, an
+//                exclusive scan over the tile's lanes gives its first bit;
+//                the lane then streams its 16 codes through a 64-bit window
+//                and ORs whole words into an LDS copy of the tile, which is
+//                stored at the tile's word offset.  Tiles are word aligned,
+//                so no two tiles share a word.
 #include "hq.h"
 #include "hq_device.h"
 #include "hq_internal.h"
@@ -24,46 +26,101 @@
 namespace hq {
 namespace {
 
-template <int G, typename T>
-__device__ inline T group_sum(T v) {
-#pragma unroll
-  for (int m = 1; m < G; m <<= 1) v += __shfl_xor(v, m, G);
-  return v;
+// The G lanes of a tile (G = 8 or 16) lie in one 16-lane DPP row, so sums
+// and scans over them use DPP moves (VALU, no LDS round trip).
+template <int CTRL>
+__device__ inline uint32_t dpp(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
 }
 
-// Inclusive scan across a lane group of width G (Hillis-Steele on shuffles).
 template <int G>
-__device__ inline uint32_t group_inclusive_scan(uint32_t v, int r) {
-#pragma unroll
-  for (int d = 1; d < G; d <<= 1) {
-    uint32_t p = __shfl_up(v, d, G);
-    if (r >= d) v += p;
+__device__ inline uint32_t row_sum(uint32_t x) {
+  x += dpp<0xB1>(x);                    // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);                    // quad_perm [2,3,0,1]
+  x += dpp<0x141>(x);                   // row_half_mirror: the other quad of the half row
+  if (G == 16) x += dpp<0x140>(x);      // row_mirror: the other half row
+  return x;
+}
+
+// Inclusive scan over the G lanes of a group (lane r of the group).
+template <int G>
+__device__ inline uint32_t row_incl_scan(uint32_t x, int r) {
+  uint32_t v = dpp<0x111>(x);           // row_shr:1
+  x += r >= 1 ? v : 0u;
+  v = dpp<0x112>(x);                    // row_shr:2
+  x += r >= 2 ? v : 0u;
+  v = dpp<0x114>(x);                    // row_shr:4
+  x += r >= 4 ? v : 0u;
+  if (G == 16) {
+    v = dpp<0x118>(x);                  // row_shr:8
+    x += r >= 8 ? v : 0u;
   }
-  return v;
+  return x;
 }
 
-template <int N>
-__device__ inline void load_zeta(const int8_t* idx, int64_t e0, uint32_t* zz) {
-  const uint4 q = *reinterpret_cast<const uint4*>(idx + e0);
-  const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-  for (int i = 0; i < 16; ++i) zz[i] = zigzag((int32_t)(int8_t)(qw[i >> 2] >> (8 * (i & 3))));
+// Zigzag of four int8 values held in a dword, bytewise: 2z, or its
+// complement for negative z (v_perm selectors 8-11 replicate the sign bits of
+// bytes 1, 3, 5, 7 of {d << 8, d}, i.e. of bytes 1, 3, 0, 2 of d).
+__device__ inline uint32_t zigzag4(uint32_t d) {
+  return ((d << 1) & 0xFEFEFEFEu) ^ __builtin_amdgcn_perm(d << 8, d, 0x090B080Au);
 }
 
-// k = argmin_k sum(floor(zeta/2^k) + 1 + k), first minimum; returns the payload.
+__device__ inline uint32_t byte_sum(uint32_t d, uint32_t acc) {
+  return __builtin_amdgcn_sad_u8(d, 0u, acc);
+}
+
+// This lane's 16 zigzagged indices of a tile as 4 dwords of bytes.
+__device__ inline void zeta4(const uint4 q, uint32_t* zz) {
+  zz[0] = zigzag4(q.x);
+  zz[1] = zigzag4(q.y);
+  zz[2] = zigzag4(q.z);
+  zz[3] = zigzag4(q.w);
+}
+
+__device__ inline uint4 load16(const int8_t* idx, int64_t e0) {
+  return *reinterpret_cast<const uint4*>(idx + e0);
+}
+
+// k = argmin_k L(k), L(k) = sum floor(zeta / 2^k) + N (1 + k), first minimum.
+// L is convex in k: L(k+1) - L(k) = N - D_k with D_k = sum floor((zeta + 2^k)
+// / 2^(k+1)) non-increasing in k and within N/2 of S / 2^(k+1), S = sum zeta.
+// With kt the smallest k with S <= N 2^(k+1), D_{kt+1} <= N and D_k > N for
+// k <= kt - 2, so the first minimum is one of kt - 1, kt, kt + 1 (zeta <= 255
+// keeps kt <= 7).  Sums over the tile's G lanes; returns the payload bits.
 template <int G, int N>
 __device__ inline uint32_t best_k(const uint32_t* zz, int& bk) {
+  uint32_t S = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) S = byte_sum(zz[j], S);
+  S = row_sum<G>(S);
+  int kt = 0;
+  while (kt < 8 && S > ((uint32_t)N << (kt + 1))) ++kt;
   uint32_t best = 0xFFFFFFFFu;
   bk = 0;
 #pragma unroll
-  for (int k = 0; k < 9; ++k) {
-    uint32_t p = 0;
+  for (int c = 0; c < 3; ++c) {
+    int k = kt - 1 + c;
+    k = k < 0 ? 0 : (k > 8 ? 8 : k);
+    const uint32_t mask = ((1u << k) - 1u) * 0x01010101u;
+    uint32_t R = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) p += zz[i] >> k;
-    const uint32_t L = group_sum<G>(p) + (uint32_t)N * (uint32_t)(1 + k);
+    for (int j = 0; j < 4; ++j) R = byte_sum(zz[j] & mask, R);
+    R = row_sum<G>(R);
+    const uint32_t L = ((S - R) >> k) + (uint32_t)N * (uint32_t)(1 + k);
     if (L < best) { best = L; bk = k; }
   }
   return best;
+}
+
+// Block b covers the contiguous tiles [b * span, (b + 1) * span), span a
+// multiple of the TPB tiles one pass of the block handles; the pack kernel
+// uses the same partition.  Few blocks keep the total's atomics few.
+template <int N>
+__device__ inline int64_t block_span(int64_t n_tiles) {
+  constexpr int TPB = kBlock / (N / kElemsPerLane);
+  const int64_t passes = (n_tiles + TPB - 1) / TPB;
+  const int64_t per_block = (passes + gridDim.x - 1) / gridDim.x;
+  return per_block * TPB;
 }
 
 template <int N>
@@ -73,19 +130,31 @@ __global__ __launch_bounds__(kBlock) void rate_kernel(RateLaunch a) {
   __shared__ uint64_t blk_words[kBlock / 64];
   __shared__ uint64_t blk_bits[kBlock / 64];
   const int r = threadIdx.x % G;
-  const int64_t tile = (int64_t)blockIdx.x * TPB + threadIdx.x / G;
+  const int64_t span = block_span<N>(a.n_tiles);
+  const int64_t first = (int64_t)blockIdx.x * span;
+  const int64_t end = first + span < a.n_tiles ? first + span : a.n_tiles;
   uint64_t words = 0, bits = 0;
-  if (tile < a.n_tiles) {
-    uint32_t zz[16];
-    load_zeta<N>(a.idx, tile * N + (int64_t)r * kElemsPerLane, zz);
+  // the next pass's indices are loaded while this pass is computed
+  auto fetch = [&](int64_t t0) {
+    const int64_t tile = t0 + threadIdx.x / G;
+    const int64_t tl = tile < end ? tile : end - 1;   // whole groups stay convergent
+    return load16(a.idx, tl * N + (int64_t)r * kElemsPerLane);
+  };
+  uint4 nxt = first < end ? fetch(first) : make_uint4(0, 0, 0, 0);
+  for (int64_t t0 = first; t0 < end; t0 += TPB) {
+    const int64_t tile = t0 + threadIdx.x / G;
+    const bool live = tile < end;
+    uint32_t zz[4];
+    zeta4(nxt, zz);
+    if (t0 + TPB < end) nxt = fetch(t0 + TPB);
     int bk;
     const uint32_t pay = best_k<G, N>(zz, bk);
     const uint32_t tb = 4u + (uint32_t)a.coset_bits + pay;
-    if (r == 0) {
+    if (live && r == 0) {
       a.rice_k[tile] = (uint8_t)bk;
       a.tile_bits[tile] = tb;
-      words = (tb + 31u) / 32u;
-      bits = tb;
+      words += (tb + 31u) / 32u;
+      bits += tb;
     }
   }
   // block sums (lane 0 of each group contributes)
@@ -109,29 +178,30 @@ __global__ __launch_bounds__(kBlock) void rate_kernel(RateLaunch a) {
 
 __global__ void zero_u64_kernel(uint64_t* p) { *p = 0; }
 
-// Exclusive scan of n values in place, one block of kBlock threads.
-__global__ __launch_bounds__(kBlock) void scan_kernel(uint64_t* v, int64_t n) {
-  __shared__ uint64_t part[kBlock];
+// Exclusive scan of n values in place, one block: each thread scans a
+// contiguous chunk, the chunk totals are scanned in LDS.
+constexpr int kScanThreads = 1024;
+
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(uint64_t* v, int64_t n) {
+  __shared__ uint64_t part[kScanThreads];
   const int t = threadIdx.x;
-  const int64_t chunk = (n + kBlock - 1) / kBlock;
+  const int64_t chunk = (n + kScanThreads - 1) / kScanThreads;
   const int64_t lo = t * chunk;
   const int64_t hi = (lo + chunk < n) ? lo + chunk : n;
   uint64_t s = 0;
   for (int64_t i = lo; i < hi; ++i) s += v[i];
   part[t] = s;
   __syncthreads();
-  if (t == 0) {
-    uint64_t run = 0;
-    for (int i = 0; i < kBlock; ++i) {
-      uint64_t x = part[i];
-      part[i] = run;
-      run += x;
-    }
+  // Hillis-Steele inclusive scan of the chunk totals
+  for (int d = 1; d < kScanThreads; d <<= 1) {
+    const uint64_t add = t >= d ? part[t - d] : 0;
+    __syncthreads();
+    part[t] += add;
+    __syncthreads();
   }
-  __syncthreads();
-  uint64_t run = part[t];
+  uint64_t run = part[t] - s;
   for (int64_t i = lo; i < hi; ++i) {
-    uint64_t x = v[i];
+    const uint64_t x = v[i];
     v[i] = run;
     run += x;
   }
@@ -144,104 +214,158 @@ struct PackBound {
   static constexpr int kWords = (kMaxBits + 31) / 32;
 };
 
-__device__ inline void lds_set_bits(uint32_t* w, uint32_t pos, uint32_t nbits, uint32_t value) {
-  // value has nbits <= 32 significant bits, LSB first at bit position pos
-  if (nbits == 0) return;
-  const uint32_t wi = pos >> 5, sh = pos & 31;
-  atomicOr(&w[wi], value << sh);
-  if (sh + nbits > 32) atomicOr(&w[wi + 1], value >> (32 - sh));
-}
+// Bit writer over a tile's LDS words.  acc holds stream bits from bit
+// position 32 * wp on; an counts them.  Full words are OR-ed out (the first
+// and last words of a lane's range are shared with its neighbours).
+struct BitWriter {
+  uint32_t* w;
+  uint64_t acc;
+  uint32_t an;
+  uint32_t wp;
 
-__device__ inline void lds_set_ones(uint32_t* w, uint32_t pos, uint32_t count) {
-  while (count > 0) {
-    const uint32_t wi = pos >> 5, sh = pos & 31;
-    const uint32_t take = (32 - sh < count) ? 32 - sh : count;
-    const uint32_t mask = (take == 32) ? 0xFFFFFFFFu : (((1u << take) - 1u) << sh);
-    atomicOr(&w[wi], mask);
-    pos += take;
-    count -= take;
+  __device__ inline void drain() {
+    while (an >= 32u) {
+      atomicOr(&w[wp], (uint32_t)acc);
+      acc >>= 32;
+      an -= 32u;
+      ++wp;
+    }
   }
-}
+  // nbits <= 32 bits of v (higher bits zero)
+  __device__ inline void put(uint32_t v, uint32_t nbits) {
+    acc |= (uint64_t)v << an;
+    an += nbits;
+    drain();
+  }
+  __device__ inline void flush() {
+    if (an > 0u) atomicOr(&w[wp], (uint32_t)acc);
+  }
+};
 
 template <int N>
 __global__ __launch_bounds__(kBlock) void pack_kernel(RateLaunch a) {
   constexpr int G = N / kElemsPerLane;
   constexpr int TPB = kBlock / G;
   constexpr int W = PackBound<N>::kWords;
-  __shared__ uint32_t buf[TPB * W];
-  __shared__ uint64_t toff[TPB + 1];
+  __shared__ uint32_t buf[TPB * W + 1];   // one spare word past the last tile
+  __shared__ uint32_t nw[TPB];
   const int r = threadIdx.x % G;
   const int slot = threadIdx.x / G;
-  const int64_t tile0 = (int64_t)blockIdx.x * TPB;
-  const int64_t tile = tile0 + slot;
-
-  for (int i = threadIdx.x; i < TPB * W; i += kBlock) buf[i] = 0;
-  if (threadIdx.x == 0) {
-    // tile word offsets inside this block (serial over TPB tiles)
-    uint64_t run = a.block_words[blockIdx.x];
-    for (int s = 0; s < TPB; ++s) {
-      toff[s] = run;
-      const int64_t t = tile0 + s;
-      if (t < a.n_tiles) run += (a.tile_bits[t] + 31u) / 32u;
+  const int64_t span = block_span<N>(a.n_tiles);
+  const int64_t first = (int64_t)blockIdx.x * span;
+  const int64_t end = first + span < a.n_tiles ? first + span : a.n_tiles;
+  uint64_t base = a.block_words[blockIdx.x];   // first word of this pass's tiles
+  // the next pass's indices, k and bit count are loaded during this pass
+  uint4 nq = make_uint4(0, 0, 0, 0);
+  uint32_t nk = 0, ntb = 0;
+  auto fetch = [&](int64_t t0) {
+    const int64_t tile = t0 + slot;
+    if (tile < end) {
+      nq = load16(a.idx, tile * N + (int64_t)r * kElemsPerLane);
+      nk = a.rice_k[tile];
+      ntb = a.tile_bits[tile];
     }
-    toff[TPB] = run;
-  }
-  __syncthreads();
-  const bool live = tile < a.n_tiles;
-  uint32_t* tw = buf + slot * W;
-  uint32_t tb = 0, nwords = 0;
-  if (live) {
-    tb = a.tile_bits[tile];
-    nwords = (tb + 31u) / 32u;
-    const int k = a.rice_k[tile];
-    uint32_t zz[16];
-    load_zeta<N>(a.idx, tile * N + (int64_t)r * kElemsPerLane, zz);
-    uint32_t lens[16], lane_total = 0;
+  };
+  if (first < end) fetch(first);
+  for (int64_t t0 = first; t0 < end; t0 += TPB) {
+    const int64_t tile = t0 + slot;
+    const bool live = tile < end;
+    const uint4 cq = nq;
+    const uint32_t ck = nk, tb = live ? ntb : 0u;
+    if (t0 + TPB < end) fetch(t0 + TPB);
+    for (int i = threadIdx.x; i < TPB * W; i += kBlock) buf[i] = 0;
+    const uint32_t nwords = (tb + 31u) / 32u;
+    if (r == 0) nw[slot] = nwords;
+    __syncthreads();
+    uint64_t off = base;
+    for (int s = 0; s < slot; ++s) off += nw[s];
+    uint32_t pass_words = 0;
+    for (int s = 0; s < TPB; ++s) pass_words += nw[s];
+    // every lane runs the scan (DPP moves read neighbouring lanes)
+    uint32_t k = 0;
+    uint32_t zz[4] = {0u, 0u, 0u, 0u};
+    if (live) {
+      k = ck;
+      zeta4(cq, zz);
+    }
+    // this lane's payload bits: sum floor(zeta / 2^k) + 16 (1 + k)
+    const uint32_t m = (0xFFu >> k) * 0x01010101u;
+    uint32_t qs = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      lens[i] = (zz[i] >> k) + 1u + (uint32_t)k;
-      lane_total += lens[i];
-    }
-    const uint32_t incl = group_inclusive_scan<G>(lane_total, r);
-    uint32_t pos = 4u + (uint32_t)a.coset_bits + incl - lane_total;
-    if (r == 0) {
-      lds_set_bits(tw, 0, 4, (uint32_t)k);
-      for (int j = 0; j < a.coset_words; ++j) {
-        const int nb = a.coset_bits - 32 * j;
-        const uint32_t cw = a.coset[tile * a.coset_words + j];
-        lds_set_bits(tw, 4u + 32u * j, nb < 32 ? nb : 32,
-                     nb < 32 ? (cw & ((1u << nb) - 1u)) : cw);
+    for (int j = 0; j < 4; ++j) qs = byte_sum((zz[j] >> k) & m, qs);
+    const uint32_t T = live ? qs + 16u * (1u + k) : 0u;
+    const uint32_t pos = 4u + (uint32_t)a.coset_bits + row_incl_scan<G>(T, r) - T;
+    if (live) {
+      uint32_t* tw = buf + slot * W;
+      if (r == 0) {
+        // header: k (4 bits), then the coset bits
+        BitWriter h{tw, (uint64_t)k, 4u, 0u};
+        for (int j = 0; j < a.coset_words; ++j) {
+          const int nb = a.coset_bits - 32 * j;
+          const uint32_t cw = a.coset[tile * a.coset_words + j];
+          h.put(nb < 32 ? (cw & ((1u << nb) - 1u)) : cw, nb < 32 ? (uint32_t)nb : 32u);
+        }
+        h.flush();
+      }
+      const uint32_t rmask = (1u << k) - 1u;
+      uint32_t pb = pos;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t zeta = __builtin_amdgcn_ubfe(zz[i >> 2], 8 * (i & 3), 8);
+        const uint32_t q = zeta >> k, rem = zeta & rmask, len = q + 1u + k;
+        if (len <= 32u) {
+          // q ones, a zero, the k low bits: ((2 rem + 1) << q) - 1, at bit pb
+          const uint32_t c = (((rem << 1) | 1u) << q) - 1u;
+          const uint64_t v = (uint64_t)c << (pb & 31u);
+          uint32_t* w = tw + (pb >> 5);
+          atomicOr(w, (uint32_t)v);
+          atomicOr(w + 1, (uint32_t)(v >> 32));
+        } else {
+          BitWriter bw{tw, 0, pb & 31u, pb >> 5};
+          uint32_t qq = q;
+          while (qq > 0u) {
+            const uint32_t t = qq < 32u ? qq : 32u;
+            bw.put(t == 32u ? 0xFFFFFFFFu : (1u << t) - 1u, t);
+            qq -= t;
+          }
+          bw.put(rem << 1, 1u + k);
+          bw.flush();
+        }
+        pb += len;
       }
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t qv = zz[i] >> k;
-      lds_set_ones(tw, pos, qv);
-      if (k > 0) lds_set_bits(tw, pos + qv + 1u, (uint32_t)k, zz[i] & ((1u << k) - 1u));
-      pos += lens[i];
+    __syncthreads();
+    if (live) {
+      if (r == 0) a.tile_word_offset[tile] = off;
+      if (tile == a.n_tiles - 1 && r == 0) a.tile_word_offset[a.n_tiles] = off + nwords;
+      if (off + nwords <= a.capacity) {
+        const uint32_t* tw = buf + slot * W;
+        for (uint32_t j = r; j < nwords; j += G) a.stream[off + j] = tw[j];
+      } else if (r == 0) {
+        set_status(a.status, HQ_ST_STREAM_FULL);
+      }
     }
+    base += pass_words;
+    __syncthreads();   // the buffer and nw are reused by the next pass
   }
-  __syncthreads();
-  if (live) {
-    const uint64_t off = toff[slot];
-    if (r == 0) a.tile_word_offset[tile] = off;
-    if (tile == a.n_tiles - 1 && r == 0) a.tile_word_offset[a.n_tiles] = toff[slot] + nwords;
-    if (off + nwords <= a.capacity) {
-      for (uint32_t j = r; j < nwords; j += G) a.stream[off + j] = tw[j];
-    } else if (r == 0) {
-      set_status(a.status, HQ_ST_STREAM_FULL);
-    }
-  }
+}
+
+constexpr int64_t kMaxRateBlocks = 2048;
+
+template <int N>
+int64_t n_blocks(int64_t n_tiles) {
+  constexpr int TPB = kBlock / (N / kElemsPerLane);
+  const int64_t passes = (n_tiles + TPB - 1) / TPB;
+  return passes < kMaxRateBlocks ? passes : kMaxRateBlocks;
 }
 
 template <int N>
 hipError_t launch_n(const RateLaunch& a, hipStream_t s) {
-  constexpr int TPB = kBlock / (N / kElemsPerLane);
-  const int64_t blocks = (a.n_tiles + TPB - 1) / TPB;
+  const int64_t blocks = n_blocks<N>(a.n_tiles);
   hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(1), 0, s, a.total_bits);
   hipLaunchKernelGGL(rate_kernel<N>, dim3((unsigned)blocks), dim3(kBlock), 0, s, a);
   if (a.stream != nullptr) {
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kBlock), 0, s, a.block_words, blocks);
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a.block_words, blocks);
     hipLaunchKernelGGL(pack_kernel<N>, dim3((unsigned)blocks), dim3(kBlock), 0, s, a);
   }
   return hipGetLastError();
