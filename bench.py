@@ -138,8 +138,9 @@ def time_calls(fn, reps, warm=2):
 
 def secondary(layer0, bps, dev):
     """Steps outside the headline: the rate + pack pass over one layer's
-    indices (its own pass over the encoder's output) and the KV path (dithered
-    E8 encode and decode of one layer's K and V cache, [8, 32768, 128] each)."""
+    indices (its own pass over the encoder's output), the stream decoder on
+    the result, and the KV path (dithered E8 encode and decode of one layer's
+    K and V cache, [8, 32768, 128] each)."""
     import numpy as np
     import torch
 
@@ -163,6 +164,22 @@ def secondary(layer0, bps, dev):
                         "(seven calls, %d tiles)" % tiles,
             "us": round(ms * 1e3, 2), "algorithmic_gbs": round(alg / (ms * 1e-3) / 1e9, 1),
             "stream_bits_per_weight": round(32.0 * words / (tiles * 256), 4)}
+
+    # the stream decoder on the same streams
+    unp = [hq.hq_unpack(o["stream"], o["tile_word_offset"], "E8", 256) for o in outs]
+
+    def unpack_layer():
+        for o, u in zip(outs, unp):
+            hq.hq_unpack(o["stream"], o["tile_word_offset"], "E8", 256, out=u)
+
+    ms_u = time_calls(unpack_layer, 10)
+    torch.cuda.synchronize()
+    same = all(torch.equal(u["idx"].view(-1), e["idx"].view(-1)) for u, e in zip(unp, encs))
+    # reads the words and offsets, writes idx, coset and k
+    alg_u = 4 * words + 8 * (tiles + len(encs)) + tiles * (256 + 4 + 1)
+    unpack = {"workload": "Rice stream decode of the same layer's packed streams (seven calls)",
+              "us": round(ms_u * 1e3, 2), "algorithmic_gbs": round(alg_u / (ms_u * 1e-3) / 1e9, 1),
+              "round_trip_exact": bool(same)}
 
     kb, vb = workloads.kv_layer()
     kvs = [torch.from_numpy(a.reshape(-1, 128).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -188,7 +205,7 @@ def secondary(layer0, bps, dev):
           "encode_us": round(ms_e * 1e3, 2), "decode_us": round(ms_d * 1e3, 2),
           "encode_algorithmic_gbs": round(n_vec * (256 + 141) / (ms_e * 1e-3) / 1e9, 1),
           "decode_algorithmic_gbs": round(n_vec * (128 + 8 + 256) / (ms_d * 1e-3) / 1e9, 1)}
-    return {"pack": pack, "kv": kv}
+    return {"pack": pack, "unpack": unpack, "kv": kv}
 
 
 def main():

@@ -80,7 +80,9 @@ enum {
 enum {
   HQ_ST_NONFINITE = 1u,   /* NaN or Inf in the input of a tile            */
   HQ_ST_OVERFLOW = 2u,    /* a stripped index left int8 (explicit scale)  */
-  HQ_ST_STREAM_FULL = 4u  /* hq_rate: packed stream exceeded capacity     */
+  HQ_ST_STREAM_FULL = 4u, /* hq_rate: packed stream exceeded capacity     */
+  HQ_ST_CORRUPT = 8u      /* hq_unpack: a tile's codes overran its words,
+                             or decoded to a value outside int8           */
 };
 
 typedef struct {
@@ -171,6 +173,33 @@ hq_status hq_rate(const hq_params* p, const int8_t* idx, const uint32_t* coset,
                   uint64_t capacity_words, uint64_t* tile_word_offset,
                   void* workspace, size_t workspace_bytes, uint32_t* status,
                   hipStream_t stream);
+
+/*
+ * hq_unpack - decode a packed stream back to stripped indices, coset words
+ * and Rice parameters: the inverse of the packing done by hq_rate.
+ *
+ * Passages: [issue] "Additional context" (a packed, Rice-coded lattice-index
+ * checkpoint format, to be read back), [arXiv abstract] item (iii) and
+ * [ICLR abstract] (the Rice code itself).  The layout is the one written by
+ * hq_rate: per tile k (4 bits), the coset bits, then per index a run of
+ * floor(zeta/2^k) one-bits, a zero bit and the k low bits of zeta (LSB
+ * first), with zeta the zigzag map of the index; stream bit j is bit
+ * (j mod 32) of word j/32; tile t occupies words [tile_word_offset[t],
+ * tile_word_offset[t + 1]).  Any k in 0..15 is accepted.
+ *
+ * stream_words: the words (device, read only within the tiles' ranges);
+ * tile_word_offset [n_tiles + 1] uint64 (device); idx [n_tiles * tile] int8
+ * out; coset [n_tiles * hq_coset_words(p)] uint32 out (NULL iff that is 0);
+ * rice_k [n_tiles] uint8 out, or NULL.  Only lattice and tile of p are used.
+ * A tile whose codes run past its words, whose word range is reversed, or
+ * that decodes an index outside int8 sets HQ_ST_CORRUPT; its outputs are
+ * unspecified and no word outside its range is read.  idx must be 16-byte
+ * aligned.
+ */
+hq_status hq_unpack(const hq_params* p, const uint32_t* stream_words,
+                    const uint64_t* tile_word_offset, int64_t n_tiles,
+                    int8_t* idx, uint32_t* coset, uint8_t* rice_k,
+                    uint32_t* status, hipStream_t stream);
 
 /*
  * hq_kv_encode - encode KV-cache vectors ([ICLR abstract]: subtractive

@@ -27,7 +27,8 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
     "-I", INCLUDE, "-I", CSRC,
 ]
-SOURCES = ["hq_encode.hip", "hq_decode.hip", "hq_e8fast.hip", "hq_rate.hip", "hq_api.hip"]
+SOURCES = ["hq_encode.hip", "hq_decode.hip", "hq_e8fast.hip", "hq_rate.hip", "hq_unpack.hip",
+           "hq_api.hip"]
 
 
 def _compile(src):

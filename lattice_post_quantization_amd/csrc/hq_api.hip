@@ -425,6 +425,38 @@ hq_status hq_rate(const hq_params* p, const int8_t* idx, const uint32_t* coset, 
   return launched(launch_rate(a, stream));
 }
 
+hq_status hq_unpack(const hq_params* p, const uint32_t* stream_words,
+                    const uint64_t* tile_word_offset, int64_t n_tiles, int8_t* idx,
+                    uint32_t* coset, uint8_t* rice_k, uint32_t* status, hipStream_t stream) {
+  hq_status st = check_params(p);
+  if (st != HQ_OK) return st;
+  if (n_tiles < 0) return HQ_EINVAL;
+  if (n_tiles == 0) return HQ_OK;   // zero tiles: a no-op (nothing is read or written)
+  if (stream_words == nullptr || tile_word_offset == nullptr || idx == nullptr) return HQ_EINVAL;
+  if (coset_words(p) > 0 && coset == nullptr) return HQ_EINVAL;
+  if (!aligned16(idx) || ((uintptr_t)tile_word_offset & 7u) || ((uintptr_t)stream_words & 3u) ||
+      ((uintptr_t)coset & 3u))
+    return HQ_EINVAL;
+  if (n_tiles > INT64_MAX / p->tile) return HQ_EINVAL;
+  if (!on_device(stream_words) || !on_device(tile_word_offset) || !on_device(idx) ||
+      (coset_words(p) > 0 && !on_device(coset)) || (rice_k != nullptr && !on_device(rice_k)) ||
+      (status != nullptr && !on_device(status)))
+    return HQ_EINVAL;
+  UnpackLaunch a;
+  memset(&a, 0, sizeof(a));
+  a.stream = stream_words;
+  a.tile_word_offset = tile_word_offset;
+  a.n_tiles = n_tiles;
+  a.tile = p->tile;
+  a.coset_bits = coset_bits(p);
+  a.coset_words = coset_words(p);
+  a.idx = idx;
+  a.coset = coset_words(p) > 0 ? coset : nullptr;
+  a.rice_k = rice_k;
+  a.status = status;
+  return launched(launch_unpack(a, stream));
+}
+
 int32_t hq_coset_words(const hq_params* p) {
   if (check_params(p) != HQ_OK) return -1;
   return coset_words(p);

@@ -65,9 +65,23 @@ struct RateLaunch {
   uint32_t* status;
 };
 
+struct UnpackLaunch {
+  const uint32_t* stream;
+  const uint64_t* tile_word_offset;
+  int64_t n_tiles;
+  int tile;
+  int coset_bits;       // per tile
+  int coset_words;      // per tile
+  int8_t* idx;
+  uint32_t* coset;      // nullptr iff coset_words == 0
+  uint8_t* rice_k;      // may be nullptr
+  uint32_t* status;     // may be nullptr
+};
+
 hipError_t launch_encode(const EncodeLaunch& a, hipStream_t s);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t s);
 hipError_t launch_rate(const RateLaunch& a, hipStream_t s);
+hipError_t launch_unpack(const UnpackLaunch& a, hipStream_t s);
 
 // Fast path for E8 / tile 256 / bf16 input (encode) and E8 / tile 256
 // (decode).  One launch covers up to kMaxItems matrices that share the

@@ -20,7 +20,7 @@ HQ_OK, HQ_EINVAL, HQ_ERANGE, HQ_EDEVICE, HQ_EUNSUPPORTED = 0, -1, -2, -3, -4
 HQ_Z, HQ_A2, HQ_D4, HQ_E8 = 1, 2, 4, 8
 HQ_F32, HQ_BF16 = 0, 1
 HQ_SCALE_AUTO, HQ_DITHER, HQ_WANT_COORDS = 1, 2, 4
-HQ_ST_NONFINITE, HQ_ST_OVERFLOW, HQ_ST_STREAM_FULL = 1, 2, 4
+HQ_ST_NONFINITE, HQ_ST_OVERFLOW, HQ_ST_STREAM_FULL, HQ_ST_CORRUPT = 1, 2, 4, 8
 
 LATTICES = {"E8": HQ_E8, "D4": HQ_D4, "A2": HQ_A2, "Z": HQ_Z}
 
@@ -73,6 +73,7 @@ _SIGNATURES = {
     "hq_encode_tiles": (_I32, [_PP, _P, _I32, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P]),
     "hq_decode_tiles": (_I32, [_PP, _P, _P, _P, _I64, _I64, _P, _I32, _P, _P]),
     "hq_rate": (_I32, [_PP, _P, _P, _I64, _P, _P, _P, _P, _U64, _P, _P, _SZ, _P, _P]),
+    "hq_unpack": (_I32, [_PP, _P, _P, _I64, _P, _P, _P, _P, _P]),
     "hq_kv_encode": (_I32, [_PP, _P, _I32, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "hq_encode_batch": (_I32, [_PP, _I32, _I32, _P, _P, _P]),
     "hq_decode_batch": (_I32, [_PP, _I32, _I32, _P, _P, _P]),
@@ -279,6 +280,33 @@ def hq_rate(idx, coset, lattice="E8", tile=256, pack=False, capacity_words=None,
         res["tile_word_offset"] = offs
         res["workspace"] = ws
     return res
+
+
+def hq_unpack(stream, tile_word_offset, lattice="E8", tile=256, status=None, out=None):
+    """Decode a packed stream (as written by hq_rate) back to stripped
+    indices (n_tiles, tile) int8, coset words (n_tiles, words) int32 or None,
+    and rice_k (n_tiles,) uint8.  tile_word_offset: int64 (n_tiles + 1)."""
+    _device_tensor(stream, "stream")
+    _device_tensor(tile_word_offset, "tile_word_offset")
+    dev = stream.device
+    n_tiles = tile_word_offset.numel() - 1
+    o = dict(out or {})
+    idx = o.get("idx")
+    if idx is None:
+        idx = torch.empty((n_tiles, tile), dtype=torch.int8, device=dev)
+    nw = coset_words(lattice, tile)
+    coset = o.get("coset")
+    if coset is None and nw:
+        coset = torch.empty((n_tiles, nw), dtype=torch.int32, device=dev)
+    rice_k = o.get("rice_k")
+    if rice_k is None:
+        rice_k = torch.empty(n_tiles, dtype=torch.uint8, device=dev)
+    p = make_params(lattice, tile, 4.0)
+    code = lib().hq_unpack(ctypes.byref(p), _ptr(stream), _ptr(tile_word_offset), n_tiles,
+                           _ptr(idx), _ptr(coset if nw else None), _ptr(rice_k), _ptr(status),
+                           _stream(dev))
+    _check(code, "hq_unpack")
+    return {"idx": idx, "coset": coset if nw else None, "rice_k": rice_k}
 
 
 def hq_kv_encode(kv, bps=4.0, rht_seed=0, dither_seed=None, dither_base=0, status=None,

@@ -197,3 +197,24 @@ def test_batch_validation():
     d[0] = hq.DecodeItem(4096, 4096, 4096, 4, 250, 4096)
     assert lib.hq_decode_batch(ctypes.byref(p), 1, 1, ctypes.byref(d), None, None) == hq.HQ_EINVAL
     assert lib.hq_decode_batch(ctypes.byref(p), 5, 1, ctypes.byref(d), None, None) == hq.HQ_EINVAL
+
+
+def test_unpack_validation_codes():
+    lib = hq.lib()
+    p = hq.make_params("E8", 256, 4.0)
+    # zero tiles: a no-op, even with null buffers
+    assert lib.hq_unpack(ctypes.byref(p), None, None, 0, None, None, None, None, None) == hq.HQ_OK
+    # missing stream / offsets / indices, or coset words for E8
+    assert lib.hq_unpack(ctypes.byref(p), None, FAKE, 3, FAKE, FAKE, None, None, None) == hq.HQ_EINVAL
+    assert lib.hq_unpack(ctypes.byref(p), FAKE, None, 3, FAKE, FAKE, None, None, None) == hq.HQ_EINVAL
+    assert lib.hq_unpack(ctypes.byref(p), FAKE, FAKE, 3, None, FAKE, None, None, None) == hq.HQ_EINVAL
+    assert lib.hq_unpack(ctypes.byref(p), FAKE, FAKE, 3, FAKE, None, None, None, None) == hq.HQ_EINVAL
+    assert lib.hq_unpack(ctypes.byref(p), FAKE, FAKE, -1, FAKE, FAKE, None, None, None) == hq.HQ_EINVAL
+    # host memory is not device memory
+    host = np.zeros(4096, np.uint8)
+    ptr = ctypes.c_void_p((host.ctypes.data + 255) // 256 * 256)
+    assert lib.hq_unpack(ctypes.byref(p), ptr, ptr, 1, ptr, ptr, None, None, None) == hq.HQ_EINVAL
+    # bad parameters
+    bad = hq.make_params("E8", 100, 4.0)
+    assert lib.hq_unpack(ctypes.byref(bad), FAKE, FAKE, 1, FAKE, FAKE, None, None,
+                         None) == hq.HQ_EINVAL

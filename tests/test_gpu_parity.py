@@ -381,3 +381,109 @@ def test_stack_sampled_parity_as_benchmarked():
         assert np.array_equal(g["y"][keep][ok].reshape(-1, 256), codec.bf16_bits(yo)), layer
         n_checked += len(X)
     say("stack: %d sampled tiles checked" % n_checked)
+
+
+def _stream_dev(words, off):
+    w = torch.from_numpy(np.ascontiguousarray(words, np.uint32).view(np.int32)).cuda()
+    if w.numel() == 0:
+        w = torch.zeros(1, dtype=torch.int32, device="cuda")
+    return w, torch.from_numpy(np.ascontiguousarray(off, np.int64)).cuda()
+
+
+def _check_unpacked(g, idx, coset_rows, k, lattice, n, label):
+    assert np.array_equal(T.host(g["idx"]).astype(np.int64), idx), label + " idx"
+    assert np.array_equal(T.host(g["rice_k"]).astype(np.int64), k), label + " k"
+    if coset_rows.shape[1]:
+        from oracle import rice
+        got = rice.coset_bit_rows(T.u32(g["coset"]), coset_rows.shape[1])
+        assert np.array_equal(got, coset_rows), label + " coset"
+
+
+@pytest.mark.parametrize("lattice,n", [("E8", 256), ("E8", 128), ("D4", 128), ("A2", 128),
+                                       ("A2", 256), ("Z", 256)])
+def test_unpack_parity(lattice, n):
+    """hq_unpack of the oracle's packed stream gives the oracle's indices,
+    coset bits and k (oracle unpack of the same words), on a ragged tile
+    count; hq_unpack of the GPU's own packed stream gives back the indices."""
+    from oracle import rice
+    rows, cols = 37, 6 * n          # 222 tiles: not a multiple of 64
+    rng = np.random.default_rng(41)
+    w = rng.standard_normal((rows, cols)) * 0.02
+    w[:, 3] *= 200.0
+    xh = workloads.bf16_bits_to_f64(workloads.f32_to_bf16_bits(w.astype(np.float32)))
+    cb = codec.coset_bits_per_tile(lattice, n)
+    for bps in (2.0, 4.0):
+        label = "unpack %s/%d R=%g" % (lattice, n, bps)
+        say("case:", label)
+        ora = codec.encode(xh, lattice, n, bps, rht_seed=7)
+        k, tb, total, words, off = codec.rate(ora["idx"], ora["coset"], lattice, n)
+        ref_idx, ref_cos, ref_k = rice.unpack(words, off, n, cb)
+        assert np.array_equal(ref_idx, ora["idx"])          # the oracle's own round trip
+        st = torch.zeros(1, dtype=torch.int32, device="cuda")
+        wd, od = _stream_dev(words, off)
+        g = hq.hq_unpack(wd, od, lattice, n, status=st)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0, label
+        _check_unpacked(g, ref_idx, ref_cos, ref_k, lattice, n, label)
+        # the GPU's own pack, unpacked on the GPU
+        cw = ora["coset"].astype(np.uint32)
+        r = hq.hq_rate(torch.from_numpy(ora["idx"].astype(np.int8)).cuda(),
+                       torch.from_numpy(cw.view(np.int32)).cuda() if cw.size else None,
+                       lattice, n, pack=True)
+        g2 = hq.hq_unpack(r["stream"], r["tile_word_offset"], lattice, n, status=st)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0, label
+        _check_unpacked(g2, ref_idx, ref_cos, ref_k, lattice, n, label + " (gpu pack)")
+
+
+def _forced_k_stream(idx, coset_rows, ks):
+    """Packed words of tiles coded with the given k (not the optimal one),
+    through the oracle's own tile bit-string writer."""
+    from oracle import rice
+    segs, off = [], [0]
+    for t in range(idx.shape[0]):
+        bits = rice._tile_bitstring(idx[t], coset_rows[t], int(ks[t]))
+        nwords = (bits.size + 31) // 32
+        padded = np.zeros(nwords * 32, np.uint8)
+        padded[:bits.size] = bits
+        segs.append(np.packbits(padded, bitorder="little").view("<u4"))
+        off.append(off[-1] + nwords)
+    return np.concatenate(segs).astype(np.uint32), np.asarray(off, np.int64)
+
+
+def test_unpack_any_k_long_codes_and_corrupt_tiles():
+    """Streams whose tiles use any k in 0..15 (long unary runs at k = 0,
+    wide remainders at k = 15) decode as the oracle's unpack does; a tile
+    whose words end early, or whose word range is reversed, sets
+    HQ_ST_CORRUPT without disturbing the other tiles."""
+    from oracle import rice
+    rng = np.random.default_rng(43)
+    n, nt = 256, 70
+    idx = rng.integers(-128, 128, size=(nt, n))
+    idx[::3] = rng.integers(-3, 4, size=idx[::3].shape)
+    cos = rng.integers(0, 2, size=(nt, 32)).astype(np.uint8)
+    ks = np.arange(nt) % 16
+    words, off = _forced_k_stream(idx, cos, ks)
+    ref_idx, ref_cos, ref_k = rice.unpack(words, off, n, 32)
+    assert np.array_equal(ref_idx, idx) and np.array_equal(ref_k, ks)
+    say("case: unpack forced k 0..15")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    wd, od = _stream_dev(words, off)
+    g = hq.hq_unpack(wd, od, "E8", n, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    _check_unpacked(g, ref_idx, ref_cos, ref_k, "E8", n, "forced k")
+    # last tile three words short; tile 9's range reversed (which also
+    # moves the start of tile 10)
+    say("case: unpack corrupt tiles")
+    bad_off = off.copy()
+    bad_off[-1] -= 3
+    bad_off[10] = bad_off[9] - 1
+    wd, od = _stream_dev(words, bad_off)
+    st.zero_()
+    g = hq.hq_unpack(wd, od, "E8", n, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & hq.HQ_ST_CORRUPT
+    good = np.ones(nt, bool)
+    good[[9, 10, nt - 1]] = False       # tile 10 now starts inside tile 8
+    assert np.array_equal(T.host(g["idx"]).astype(np.int64)[good], idx[good])
