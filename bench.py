@@ -181,6 +181,36 @@ def secondary(layer0, bps, dev):
               "us": round(ms_u * 1e3, 2), "algorithmic_gbs": round(alg_u / (ms_u * 1e-3) / 1e9, 1),
               "round_trip_exact": bool(same)}
 
+    # y = W x from the stored indices (m = 1) against a bf16 GEMV of the
+    # decoded weights (the same layer's seven matrices)
+    _, _, ys = layer0
+    xv = [torch.randn(e["idx"].shape[1], device=dev) for e in encs]
+    yv = [torch.empty(e["idx"].shape[0], device=dev) for e in encs]
+    wsp = [torch.empty(hq.lib().hq_gemv_workspace_bytes(e["idx"].shape[0], e["idx"].shape[1], 1),
+                       dtype=torch.uint8, device=dev) for e in encs]
+
+    def gemv_layer():
+        for e, x, y, w in zip(encs, xv, yv, wsp):
+            hq.hq_gemv(e["idx"], e["coset"], e["scale"], x, rht_seed=0, out=y.view(1, -1),
+                       workspace=w)
+
+    xb = [x.to(torch.bfloat16) for x in xv]
+
+    def bf16_layer():
+        for wm, x in zip(ys, xb):
+            torch.mv(wm, x)
+
+    ms_g = time_calls(gemv_layer, 10)
+    ms_b = time_calls(bf16_layer, 10)
+    rows_cols = [tuple(e["idx"].shape) for e in encs]
+    w_total = sum(r * c for r, c in rows_cols)
+    alg_g = w_total * (1 + 8 / 256) + sum(4 * (r + c) for r, c in rows_cols)
+    gemv = {"workload": "y = W x (one vector, fp32) for the same layer's seven matrices, "
+                        "from the E8 indices; beside torch.mv on the decoded bf16 weights",
+            "us": round(ms_g * 1e3, 2), "bf16_gemv_us": round(ms_b * 1e3, 2),
+            "speedup_vs_bf16": round(ms_b / ms_g, 3),
+            "algorithmic_gbs": round(alg_g / (ms_g * 1e-3) / 1e9, 1)}
+
     kb, vb = workloads.kv_layer()
     kvs = [torch.from_numpy(a.reshape(-1, 128).view(np.int16)).to(dev).view(torch.bfloat16)
            for a in (kb, vb)]
@@ -205,7 +235,7 @@ def secondary(layer0, bps, dev):
           "encode_us": round(ms_e * 1e3, 2), "decode_us": round(ms_d * 1e3, 2),
           "encode_algorithmic_gbs": round(n_vec * (256 + 141) / (ms_e * 1e-3) / 1e9, 1),
           "decode_algorithmic_gbs": round(n_vec * (128 + 8 + 256) / (ms_d * 1e-3) / 1e9, 1)}
-    return {"pack": pack, "unpack": unpack, "kv": kv}
+    return {"pack": pack, "unpack": unpack, "gemv": gemv, "kv": kv}
 
 
 def main():

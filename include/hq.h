@@ -202,6 +202,35 @@ hq_status hq_unpack(const hq_params* p, const uint32_t* stream_words,
                     uint32_t* status, hipStream_t stream);
 
 /*
+ * hq_gemv - y = W x for E8-coded weights, without forming W: the consumer
+ * of the format ([issue] "Is your feature request related to a problem?":
+ * decode must be usable at inference; [ICLR abstract]: algebraic decoding).
+ *
+ * W is the matrix hq_decode_tiles reconstructs (before its output rounding):
+ * tile t of row r is w = s (.) H P Delta / (2 sqrt(n)), P = 2p the stored
+ * lattice point.  Since H is symmetric, w . x_t = Delta / (2 sqrt(n)) *
+ * <P, H (s (.) x_t)>, so the kernel rotates each n-column slice of x once
+ * (into the workspace) and then needs only the stored indices of W.
+ *
+ * p: lattice E8, tile 128 or 256, rht_seed of the encode; no dither.
+ * idx [rows*cols] int8, coset [n_tiles] (E8/256) or [n_tiles] 16-bit words
+ * as for decode, scale [n_tiles] fp32 (tile t = row r, column slice t mod
+ * cols/n); x [m][cols] fp32 (m vectors, each contiguous), 1 <= m <= 8;
+ * y [m][rows] fp32 out; workspace: device scratch of at least
+ * hq_gemv_workspace_bytes(rows, cols, m) bytes, 16-byte aligned.  Results
+ * are fp32 sums of the products in a fixed order (deterministic).  Errors as for decode;
+ * HQ_EUNSUPPORTED for another lattice or HQ_DITHER.
+ */
+hq_status hq_gemv(const hq_params* p, const int8_t* idx, const uint32_t* coset,
+                  const float* scale, int64_t rows, int64_t cols, const float* x,
+                  int32_t m, float* y, void* workspace, size_t workspace_bytes,
+                  uint32_t* status, hipStream_t stream);
+
+/* Device workspace bytes hq_gemv needs for a rows x cols matrix and m
+   vectors (the rotated vectors and the partial sums of the column splits). */
+size_t hq_gemv_workspace_bytes(int64_t rows, int64_t cols, int32_t m);
+
+/*
  * hq_kv_encode - encode KV-cache vectors ([ICLR abstract]: subtractive
  * dither keeps each cached inner product unbiased per vector; [arXiv
  * abstract] item (iv)).  The vectors are tiles of n = p->tile = head_dim

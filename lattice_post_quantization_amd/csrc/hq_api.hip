@@ -457,6 +457,54 @@ hq_status hq_unpack(const hq_params* p, const uint32_t* stream_words,
   return launched(launch_unpack(a, stream));
 }
 
+size_t hq_gemv_workspace_bytes(int64_t rows, int64_t cols, int32_t m) {
+  if (rows <= 0 || cols <= 0 || m <= 0 || cols % 256 != 0) return 0;
+  int64_t splits, span;
+  gemv_split(rows, cols, splits, span);
+  // the rotated vectors, then the partial sums (16-byte aligned)
+  const size_t xr = ((size_t)cols * (size_t)m * sizeof(float) + 15) / 16 * 16;
+  return xr + (size_t)splits * (size_t)m * (size_t)rows * sizeof(float);
+}
+
+hq_status hq_gemv(const hq_params* p, const int8_t* idx, const uint32_t* coset,
+                  const float* scale, int64_t rows, int64_t cols, const float* x, int32_t m,
+                  float* y, void* workspace, size_t workspace_bytes, uint32_t* status,
+                  hipStream_t stream) {
+  (void)status;
+  hq_status st = check_params(p);
+  if (st != HQ_OK) return st;
+  if (p->lattice != HQ_E8 || p->tile != 256 || (p->flags & HQ_DITHER)) return HQ_EUNSUPPORTED;
+  if (rows < 0 || cols < 0 || cols % 256 != 0 || m < 1 || m > 8) return HQ_EINVAL;
+  if (rows == 0 || cols == 0) return HQ_OK;   // nothing to compute
+  if (idx == nullptr || coset == nullptr || scale == nullptr || x == nullptr || y == nullptr ||
+      workspace == nullptr)
+    return HQ_EINVAL;
+  if (rows > INT64_MAX / cols || workspace_bytes < hq_gemv_workspace_bytes(rows, cols, m))
+    return HQ_EINVAL;
+  if (!aligned16(idx) || !aligned16(x) || !aligned16(workspace) || ((uintptr_t)y & 3u) ||
+      ((uintptr_t)coset & 3u) || ((uintptr_t)scale & 3u))
+    return HQ_EINVAL;
+  if (!on_device(idx) || !on_device(coset) || !on_device(scale) || !on_device(x) ||
+      !on_device(y) || !on_device(workspace))
+    return HQ_EINVAL;
+  GemvLaunch a;
+  memset(&a, 0, sizeof(a));
+  a.idx = idx;
+  a.coset = coset;
+  a.scale = scale;
+  a.rows = rows;
+  a.cols = cols;
+  a.x = x;
+  a.m = m;
+  a.y = y;
+  a.xr = static_cast<float*>(workspace);
+  gemv_split(rows, cols, a.splits, a.span);
+  a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                    ((size_t)cols * (size_t)m * sizeof(float) + 15) / 16 * 16);
+  make_signs(p->rht_seed, p->tile, a.signs);
+  return launched(launch_gemv(a, stream));
+}
+
 int32_t hq_coset_words(const hq_params* p) {
   if (check_params(p) != HQ_OK) return -1;
   return coset_words(p);

@@ -78,10 +78,30 @@ struct UnpackLaunch {
   uint32_t* status;     // may be nullptr
 };
 
+struct GemvLaunch {
+  const int8_t* idx;
+  const uint32_t* coset;
+  const float* scale;
+  int64_t rows;
+  int64_t cols;         // multiple of 256 (E8, tile 256)
+  const float* x;       // [m][cols]
+  int m;                // 1..8
+  float* y;             // [m][rows]
+  float* xr;            // workspace: H (s (.) x) per 256-column slice, [m][cols]
+  float* part;          // workspace: partial sums [splits][m][rows]
+  int64_t splits;       // column splits
+  int64_t span;         // slices per split
+  uint32_t signs[8];
+};
+
+// Column splits of hq_gemv (splits * span >= cols / 256).
+void gemv_split(int64_t rows, int64_t cols, int64_t& splits, int64_t& span);
+
 hipError_t launch_encode(const EncodeLaunch& a, hipStream_t s);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t s);
 hipError_t launch_rate(const RateLaunch& a, hipStream_t s);
 hipError_t launch_unpack(const UnpackLaunch& a, hipStream_t s);
+hipError_t launch_gemv(const GemvLaunch& a, hipStream_t s);
 
 // Fast path for E8 / tile 256 / bf16 input (encode) and E8 / tile 256
 // (decode).  One launch covers up to kMaxItems matrices that share the

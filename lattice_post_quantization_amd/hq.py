@@ -74,6 +74,8 @@ _SIGNATURES = {
     "hq_decode_tiles": (_I32, [_PP, _P, _P, _P, _I64, _I64, _P, _I32, _P, _P]),
     "hq_rate": (_I32, [_PP, _P, _P, _I64, _P, _P, _P, _P, _U64, _P, _P, _SZ, _P, _P]),
     "hq_unpack": (_I32, [_PP, _P, _P, _I64, _P, _P, _P, _P, _P]),
+    "hq_gemv": (_I32, [_PP, _P, _P, _P, _I64, _I64, _P, _I32, _P, _P, _SZ, _P, _P]),
+    "hq_gemv_workspace_bytes": (_SZ, [_I64, _I64, _I32]),
     "hq_kv_encode": (_I32, [_PP, _P, _I32, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "hq_encode_batch": (_I32, [_PP, _I32, _I32, _P, _P, _P]),
     "hq_decode_batch": (_I32, [_PP, _I32, _I32, _P, _P, _P]),
@@ -307,6 +309,27 @@ def hq_unpack(stream, tile_word_offset, lattice="E8", tile=256, status=None, out
                            _stream(dev))
     _check(code, "hq_unpack")
     return {"idx": idx, "coset": coset if nw else None, "rice_k": rice_k}
+
+
+def hq_gemv(idx, coset, scale, x, rht_seed=0, out=None, workspace=None):
+    """y = W x for E8/256-coded weights W (rows, cols) given by idx, coset and
+    scale; x: fp32 (cols,) or (m, cols) with m <= 8; returns fp32 (rows,) or
+    (m, rows)."""
+    for t, name in ((idx, "idx"), (coset, "coset"), (scale, "scale"), (x, "x")):
+        _device_tensor(t, name)
+    rows, cols = idx.shape
+    xv = x.reshape(1, -1) if x.dim() == 1 else x
+    m = xv.shape[0]
+    dev = idx.device
+    y = out if out is not None else torch.empty((m, rows), dtype=torch.float32, device=dev)
+    nb = lib().hq_gemv_workspace_bytes(rows, cols, m)
+    ws = workspace if workspace is not None else torch.empty(max(nb, 16), dtype=torch.uint8,
+                                                             device=dev)
+    p = make_params("E8", 256, 4.0, rht_seed)
+    code = lib().hq_gemv(ctypes.byref(p), _ptr(idx), _ptr(coset), _ptr(scale), rows, cols,
+                         _ptr(xv), m, _ptr(y), _ptr(ws), ws.numel(), None, _stream(dev))
+    _check(code, "hq_gemv")
+    return y.reshape(-1) if x.dim() == 1 else y
 
 
 def hq_kv_encode(kv, bps=4.0, rht_seed=0, dither_seed=None, dither_base=0, status=None,

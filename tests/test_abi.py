@@ -218,3 +218,29 @@ def test_unpack_validation_codes():
     bad = hq.make_params("E8", 100, 4.0)
     assert lib.hq_unpack(ctypes.byref(bad), FAKE, FAKE, 1, FAKE, FAKE, None, None,
                          None) == hq.HQ_EINVAL
+
+
+def test_gemv_validation_codes():
+    lib = hq.lib()
+    p = hq.make_params("E8", 256, 4.0, 3)
+    # the rotated vectors and at least one split of partial sums
+    assert lib.hq_gemv_workspace_bytes(1024, 4096, 2) >= 4096 * 2 * 4 + 1024 * 2 * 4
+    assert lib.hq_gemv_workspace_bytes(1024, 4000, 2) == 0
+    # nothing to compute: a no-op
+    assert lib.hq_gemv(ctypes.byref(p), None, None, None, 0, 256, None, 1, None, None, 0, None,
+                       None) == hq.HQ_OK
+    # E8 with tile 256 only; no dither
+    for q in (hq.make_params("D4", 128, 4.0), hq.make_params("E8", 128, 4.0),
+              hq.make_params("E8", 256, 4.0, 0, hq.HQ_DITHER, 1)):
+        assert lib.hq_gemv(ctypes.byref(q), FAKE, FAKE, FAKE, 4, 256, FAKE, 1, FAKE, FAKE, 4096,
+                           None, None) == hq.HQ_EUNSUPPORTED
+    # m outside 1..8, columns not a multiple of 256, workspace too small, nulls
+    for mm in (0, 9):
+        assert lib.hq_gemv(ctypes.byref(p), FAKE, FAKE, FAKE, 4, 256, FAKE, mm, FAKE, FAKE, 1 << 20,
+                           None, None) == hq.HQ_EINVAL
+    assert lib.hq_gemv(ctypes.byref(p), FAKE, FAKE, FAKE, 4, 384, FAKE, 1, FAKE, FAKE, 1 << 20,
+                       None, None) == hq.HQ_EINVAL
+    assert lib.hq_gemv(ctypes.byref(p), FAKE, FAKE, FAKE, 4, 512, FAKE, 2, FAKE, FAKE, 100,
+                       None, None) == hq.HQ_EINVAL
+    assert lib.hq_gemv(ctypes.byref(p), FAKE, None, FAKE, 4, 512, FAKE, 1, FAKE, FAKE, 1 << 20,
+                       None, None) == hq.HQ_EINVAL

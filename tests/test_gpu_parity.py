@@ -487,3 +487,45 @@ def test_unpack_any_k_long_codes_and_corrupt_tiles():
     good = np.ones(nt, bool)
     good[[9, 10, nt - 1]] = False       # tile 10 now starts inside tile 8
     assert np.array_equal(T.host(g["idx"]).astype(np.int64)[good], idx[good])
+
+
+@pytest.mark.parametrize("m", [1, 3, 8])
+def test_gemv_parity(m):
+    """hq_gemv against the oracle: y = W x with W the oracle's fp64 decode of
+    the oracle's own encode (a ragged 37 x 1536 matrix and a Llama-shaped k
+    projection, 1024 x 4096, RHT seed 5), x seeded N(0, 1) in fp32.  Bound
+    for fp32: every product enters through at most (slices + 16) roundings
+    (the rotated input, the 4-term dot, the scale, the per-lane sum over the
+    slices, the 64-lane sum), so |y - y_ref| <= (slices + 16) 2^-24 B with
+    B = sum_t Delta/32 sum_j |P_j| |(H (s . x_t))_j|, computed here in fp64."""
+    from oracle import hadamard, splitmix
+    rng = np.random.default_rng(51 + m)
+    for rows, cols in ((37, 1536), (1024, 4096)):
+        label = "gemv %dx%d m=%d" % (rows, cols, m)
+        say("case:", label)
+        w = rng.standard_normal((rows, cols)) * 0.02
+        w[:, 7] *= 50.0
+        xh = workloads.bf16_bits_to_f64(workloads.f32_to_bf16_bits(w.astype(np.float32)))
+        ora = codec.encode(xh, "E8", 256, 4.0, rht_seed=5)
+        W = codec.decode(ora["idx"], ora["coset"], ora["scale"], "E8", 256, 5).reshape(rows, cols)
+        x = rng.standard_normal((m, cols)).astype(np.float32)
+        y_ref = x.astype(np.float64) @ W.T                                  # (m, rows)
+        T_ = cols // 256
+        P = np.abs(ora["coords"].reshape(rows, T_, 256).astype(np.float64))
+        signs = splitmix.rht_signs(5, 256)
+        xr = np.abs(hadamard.unnormalized_forward(x.astype(np.float64).reshape(m * T_, 256),
+                                                  signs)).reshape(m, T_, 256)
+        dl = ora["scale"].reshape(rows, T_) / 32.0
+        B = np.einsum("rt,rtj,vtj->vr", dl, P, xr)
+        tol = (T_ + 16) * 2.0 ** -24 * B
+        idx = torch.from_numpy(ora["idx"].astype(np.int8).reshape(rows, cols)).cuda()
+        cw = torch.from_numpy(ora["coset"].astype(np.uint32).view(np.int32)).cuda()
+        sc = torch.from_numpy(ora["scale"].astype(np.float32)).cuda()
+        y = hq.hq_gemv(idx, cw, sc, torch.from_numpy(x).cuda(), rht_seed=5)
+        torch.cuda.synchronize()
+        err = np.abs(T.host(y).astype(np.float64) - y_ref)
+        assert np.all(err <= tol), "%s: max err/tol %.3g" % (label, np.max(err / tol))
+        # one vector as a 1-D input
+        y1 = hq.hq_gemv(idx, cw, sc, torch.from_numpy(x[0]).cuda(), rht_seed=5)
+        torch.cuda.synchronize()
+        assert np.all(np.abs(T.host(y1) - y_ref[0]) <= tol[0]), label + " 1-D"
