@@ -229,12 +229,27 @@ def secondary(layer0, bps, dev):
 
     ms_e = time_calls(kv_enc, 10)
     ms_d = time_calls(kv_dec, 10)
+    # scores of 64 queries (shared by the heads) against all 8 x 32768
+    # compressed keys of the K cache in one call (dither index = key row)
+    nq, heads, seq = 64, 8, kb.shape[1]
+    qv = torch.randn(nq, 128, device=dev)
+    sc = torch.empty(nq, heads * seq, device=dev)
+    wsq = torch.empty(hq.lib().hq_kv_scores_workspace_bytes(nq), dtype=torch.uint8, device=dev)
+
+    def kv_scores():
+        hq.hq_kv_scores(qv, encs_kv[0], 1, dither_seed=2, dither_base=0, out=sc, workspace=wsq)
+
+    ms_s = time_calls(kv_scores, 10)
     # per 128-vector: 256 B in / 128 B idx + 4 coset + 1 k + 4 bits + 4 scale
     kv = {"workload": "dithered E8 encode and decode of K and V [8, 32768, 128] bf16 "
                       "(%d vectors of 128, 4 bps)" % n_vec,
           "encode_us": round(ms_e * 1e3, 2), "decode_us": round(ms_d * 1e3, 2),
           "encode_algorithmic_gbs": round(n_vec * (256 + 141) / (ms_e * 1e-3) / 1e9, 1),
-          "decode_algorithmic_gbs": round(n_vec * (128 + 8 + 256) / (ms_d * 1e-3) / 1e9, 1)}
+          "decode_algorithmic_gbs": round(n_vec * (128 + 8 + 256) / (ms_d * 1e-3) / 1e9, 1),
+          "scores_workload": "%d queries against all %d x %d compressed keys of the K cache, "
+                             "one call (dither regenerated per key)" % (nq, heads, seq),
+          "scores_us": round(ms_s * 1e3, 2),
+          "scores_gflops": round(2.0 * nq * heads * seq * 128 / (ms_s * 1e-3) / 1e9, 1)}
     return {"pack": pack, "unpack": unpack, "gemv": gemv, "kv": kv}
 
 

@@ -231,6 +231,34 @@ hq_status hq_gemv(const hq_params* p, const int8_t* idx, const uint32_t* coset,
 size_t hq_gemv_workspace_bytes(int64_t rows, int64_t cols, int32_t m);
 
 /*
+ * hq_kv_scores - attention scores of queries against one head's compressed
+ * keys: scores[j][k] = q_j . khat_k, khat_k the key hq_decode_tiles would
+ * reconstruct (dither subtracted), without forming khat.
+ *
+ * Passages: [ICLR abstract] (subtractive dither keeps each cached inner
+ * product unbiased; algebraic decoding), [arXiv abstract] ideas (i)-(iii).
+ * khat = s (.) H yhat / sqrt(n) with yhat = Delta (p - d), and H is
+ * symmetric, so q . khat = <H (s (.) q), yhat> / sqrt(n): the queries are
+ * rotated once (into the workspace) and each key's yhat is formed from its
+ * stored indices and regenerated dither.
+ *
+ * p: lattice E8, tile 128 (the head dimension), rht_seed of the encode;
+ * HQ_DITHER with the encode's dither_seed, and dither_base = global index of
+ * key 0 (as for hq_kv_encode), or no dither (rotation-only keys).
+ * q [n_q][128] fp32; idx [n_keys][128] int8, coset [n_keys] uint32 (16 coset
+ * bits), scale [n_keys] fp32 as written by hq_kv_encode; scores [n_q][n_keys]
+ * fp32 out; workspace: device scratch of at least
+ * hq_kv_scores_workspace_bytes(n_q) bytes.  fp32 arithmetic in a fixed order.
+ */
+hq_status hq_kv_scores(const hq_params* p, const float* q, int64_t n_q,
+                       const int8_t* idx, const uint32_t* coset, const float* scale,
+                       int64_t n_keys, float* scores, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
+/* Device workspace bytes hq_kv_scores needs for n_q queries. */
+size_t hq_kv_scores_workspace_bytes(int64_t n_q);
+
+/*
  * hq_kv_encode - encode KV-cache vectors ([ICLR abstract]: subtractive
  * dither keeps each cached inner product unbiased per vector; [arXiv
  * abstract] item (iv)).  The vectors are tiles of n = p->tile = head_dim

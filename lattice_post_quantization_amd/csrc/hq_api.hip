@@ -505,6 +505,50 @@ hq_status hq_gemv(const hq_params* p, const int8_t* idx, const uint32_t* coset,
   return launched(launch_gemv(a, stream));
 }
 
+size_t hq_kv_scores_workspace_bytes(int64_t n_q) {
+  if (n_q <= 0) return 0;
+  return (size_t)n_q * 128u * sizeof(float);
+}
+
+hq_status hq_kv_scores(const hq_params* p, const float* q, int64_t n_q, const int8_t* idx,
+                       const uint32_t* coset, const float* scale, int64_t n_keys, float* scores,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  hq_status st = check_params(p);
+  if (st != HQ_OK) return st;
+  if (p->lattice != HQ_E8 || p->tile != 128) return HQ_EUNSUPPORTED;
+  if (n_q < 0 || n_keys < 0) return HQ_EINVAL;
+  if (n_q == 0 || n_keys == 0) return HQ_OK;   // nothing to compute
+  if (q == nullptr || idx == nullptr || coset == nullptr || scale == nullptr ||
+      scores == nullptr || workspace == nullptr)
+    return HQ_EINVAL;
+  if (n_q > INT64_MAX / 128 || n_keys > INT64_MAX / n_q || n_q > 0x7FFFFFFF ||
+      workspace_bytes < hq_kv_scores_workspace_bytes(n_q))
+    return HQ_EINVAL;
+  if ((p->flags & HQ_DITHER) && p->dither_base + n_keys > ((int64_t)1 << 32)) return HQ_EINVAL;
+  if (!aligned16(q) || !aligned16(idx) || !aligned16(workspace) || ((uintptr_t)coset & 3u) ||
+      ((uintptr_t)scale & 3u) || ((uintptr_t)scores & 3u))
+    return HQ_EINVAL;
+  if (!on_device(q) || !on_device(idx) || !on_device(coset) || !on_device(scale) ||
+      !on_device(scores) || !on_device(workspace))
+    return HQ_EINVAL;
+  ScoreLaunch a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.n_q = n_q;
+  a.idx = idx;
+  a.coset = coset;
+  a.scale = scale;
+  a.n_keys = n_keys;
+  a.scores = scores;
+  a.qr = static_cast<float*>(workspace);
+  make_signs(p->rht_seed, p->tile, a.signs);
+  a.inv_sqrt_n = 1.0 / sqrt((double)p->tile);
+  a.dither = (p->flags & HQ_DITHER) != 0;
+  a.dither_seed = p->dither_seed;
+  a.dither_base = p->dither_base;
+  return launched(launch_scores(a, stream));
+}
+
 int32_t hq_coset_words(const hq_params* p) {
   if (check_params(p) != HQ_OK) return -1;
   return coset_words(p);

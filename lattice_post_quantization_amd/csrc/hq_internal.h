@@ -97,11 +97,28 @@ struct GemvLaunch {
 // Column splits of hq_gemv (splits * span >= cols / 256).
 void gemv_split(int64_t rows, int64_t cols, int64_t& splits, int64_t& span);
 
+struct ScoreLaunch {
+  const float* q;       // [n_q][128]
+  int64_t n_q;
+  const int8_t* idx;    // [n_keys][128]
+  const uint32_t* coset;
+  const float* scale;
+  int64_t n_keys;
+  float* scores;        // [n_q][n_keys]
+  float* qr;            // workspace: H (s (.) q), [n_q][128]
+  uint32_t signs[8];
+  double inv_sqrt_n;
+  int dither;
+  uint32_t dither_seed;
+  int64_t dither_base;
+};
+
 hipError_t launch_encode(const EncodeLaunch& a, hipStream_t s);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t s);
 hipError_t launch_rate(const RateLaunch& a, hipStream_t s);
 hipError_t launch_unpack(const UnpackLaunch& a, hipStream_t s);
 hipError_t launch_gemv(const GemvLaunch& a, hipStream_t s);
+hipError_t launch_scores(const ScoreLaunch& a, hipStream_t s);
 
 // Fast path for E8 / tile 256 / bf16 input (encode) and E8 / tile 256
 // (decode).  One launch covers up to kMaxItems matrices that share the

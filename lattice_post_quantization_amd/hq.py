@@ -76,6 +76,8 @@ _SIGNATURES = {
     "hq_unpack": (_I32, [_PP, _P, _P, _I64, _P, _P, _P, _P, _P]),
     "hq_gemv": (_I32, [_PP, _P, _P, _P, _I64, _I64, _P, _I32, _P, _P, _SZ, _P, _P]),
     "hq_gemv_workspace_bytes": (_SZ, [_I64, _I64, _I32]),
+    "hq_kv_scores": (_I32, [_PP, _P, _I64, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
+    "hq_kv_scores_workspace_bytes": (_SZ, [_I64]),
     "hq_kv_encode": (_I32, [_PP, _P, _I32, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "hq_encode_batch": (_I32, [_PP, _I32, _I32, _P, _P, _P]),
     "hq_decode_batch": (_I32, [_PP, _I32, _I32, _P, _P, _P]),
@@ -330,6 +332,27 @@ def hq_gemv(idx, coset, scale, x, rht_seed=0, out=None, workspace=None):
                          _ptr(xv), m, _ptr(y), _ptr(ws), ws.numel(), None, _stream(dev))
     _check(code, "hq_gemv")
     return y.reshape(-1) if x.dim() == 1 else y
+
+
+def hq_kv_scores(q, enc, rht_seed=0, dither_seed=None, dither_base=0, out=None,
+                 workspace=None):
+    """scores[j][k] = q_j . khat_k for queries q (n_q, 128) fp32 against keys
+    encoded by hq_kv_encode (enc: its dict); returns fp32 (n_q, n_keys)."""
+    _device_tensor(q, "q")
+    idx, coset, scale = enc["idx"], enc["coset"], enc["scale"]
+    n_q, n_keys = q.shape[0], idx.shape[0]
+    dev = q.device
+    sc = out if out is not None else torch.empty((n_q, n_keys), dtype=torch.float32, device=dev)
+    nb = lib().hq_kv_scores_workspace_bytes(n_q)
+    ws = workspace if workspace is not None else torch.empty(max(nb, 16), dtype=torch.uint8,
+                                                             device=dev)
+    flags = HQ_DITHER if dither_seed is not None else 0
+    p = make_params("E8", 128, 4.0, rht_seed, flags,
+                    0 if dither_seed is None else dither_seed, dither_base)
+    code = lib().hq_kv_scores(ctypes.byref(p), _ptr(q), n_q, _ptr(idx), _ptr(coset), _ptr(scale),
+                              n_keys, _ptr(sc), _ptr(ws), ws.numel(), _stream(dev))
+    _check(code, "hq_kv_scores")
+    return sc
 
 
 def hq_kv_encode(kv, bps=4.0, rht_seed=0, dither_seed=None, dither_base=0, status=None,

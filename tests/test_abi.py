@@ -244,3 +244,26 @@ def test_gemv_validation_codes():
                        None, None) == hq.HQ_EINVAL
     assert lib.hq_gemv(ctypes.byref(p), FAKE, None, FAKE, 4, 512, FAKE, 1, FAKE, FAKE, 1 << 20,
                        None, None) == hq.HQ_EINVAL
+
+
+def test_kv_scores_validation_codes():
+    lib = hq.lib()
+    p = hq.make_params("E8", 128, 4.0, 1, hq.HQ_DITHER, 2, 0)
+    assert lib.hq_kv_scores_workspace_bytes(40) == 40 * 128 * 4
+    # nothing to compute
+    assert lib.hq_kv_scores(ctypes.byref(p), None, 0, None, None, None, 5, None, None, 0,
+                            None) == hq.HQ_OK
+    assert lib.hq_kv_scores(ctypes.byref(p), None, 5, None, None, None, 0, None, None, 0,
+                            None) == hq.HQ_OK
+    # E8 with head dimension 128 only
+    for q in (hq.make_params("E8", 256, 4.0), hq.make_params("D4", 128, 4.0)):
+        assert lib.hq_kv_scores(ctypes.byref(q), FAKE, 4, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 1 << 20,
+                                None) == hq.HQ_EUNSUPPORTED
+    # null buffers, short workspace, dither index overflow
+    assert lib.hq_kv_scores(ctypes.byref(p), FAKE, 4, FAKE, None, FAKE, 4, FAKE, FAKE, 1 << 20,
+                            None) == hq.HQ_EINVAL
+    assert lib.hq_kv_scores(ctypes.byref(p), FAKE, 4, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 100,
+                            None) == hq.HQ_EINVAL
+    pb = hq.make_params("E8", 128, 4.0, 1, hq.HQ_DITHER, 2, 2**32 - 2)
+    assert lib.hq_kv_scores(ctypes.byref(pb), FAKE, 4, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 1 << 20,
+                            None) == hq.HQ_EINVAL

@@ -529,3 +529,64 @@ def test_gemv_parity(m):
         y1 = hq.hq_gemv(idx, cw, sc, torch.from_numpy(x[0]).cuda(), rht_seed=5)
         torch.cuda.synchronize()
         assert np.all(np.abs(T.host(y1) - y_ref[0]) <= tol[0]), label + " 1-D"
+
+
+@pytest.mark.parametrize("dither", [True, False])
+def test_kv_scores_parity(dither):
+    """hq_kv_scores against the oracle: q . khat with khat the oracle's fp64
+    decode (dither subtracted) of the oracle's encode of 300 seeded keys
+    (not a multiple of the 256 keys of a block; dither base 1000) for 40
+    queries (a full and a ragged chunk of 32).  Bound for fp32: each product
+    q~_i yhat_i passes through at most 136 roundings (the rotated query,
+    yhat's difference and scale, the 128-term sums, the final 1/sqrt(128)),
+    so |s - s_ref| <= 136 2^-24 sum_i |q~_i| |yhat_i| / sqrt(128), with
+    q~ = H (s . q) and yhat = Delta (p - d) computed here in fp64."""
+    from oracle import hadamard, splitmix
+    rng = np.random.default_rng(61 + int(dither))
+    nk, nq, base = 300, 40, 1000
+    k = rng.standard_normal((nk, 128))
+    k[:, [3, 77]] += 4.0                                # channel offsets
+    xh = workloads.bf16_bits_to_f64(workloads.f32_to_bf16_bits(k.astype(np.float32)))
+    ds = 2 if dither else None
+    say("case: kv scores dither=%s" % dither)
+    ora = codec.encode(xh, "E8", 128, 4.0, rht_seed=1, dither_seed=ds, dither_base=base)
+    khat = codec.decode(ora["idx"], ora["coset"], ora["scale"], "E8", 128, 1,
+                        dither_seed=ds, dither_base=base)
+    q = rng.standard_normal((nq, 128)).astype(np.float32)
+    ref = q.astype(np.float64) @ khat.T
+    p = codec.lattice_points(ora["idx"], ora["coset"], "E8", 128)
+    if dither:
+        p = p - codec.dither(ds, base, nk, 128)
+    yhat = ora["scale"][:, None] * p
+    qr = hadamard.unnormalized_forward(q.astype(np.float64), splitmix.rht_signs(1, 128))
+    tol = 136 * 2.0 ** -24 * (np.abs(qr) @ np.abs(yhat).T) / math.sqrt(128.0)
+    enc = {"idx": torch.from_numpy(ora["idx"].astype(np.int8)).cuda(),
+           "coset": torch.from_numpy(ora["coset"].astype(np.uint32).view(np.int32)).cuda(),
+           "scale": torch.from_numpy(ora["scale"].astype(np.float32)).cuda()}
+    g = hq.hq_kv_scores(torch.from_numpy(q).cuda(), enc, rht_seed=1, dither_seed=ds,
+                        dither_base=base)
+    torch.cuda.synchronize()
+    err = np.abs(T.host(g).astype(np.float64) - ref)
+    assert np.all(err <= tol), "max err/tol %.3g" % np.max(err / tol)
+
+
+@pytest.mark.parametrize("bps", [1.7, 2.5])
+def test_kv_low_rate_parity(bps):
+    """Low-rate KV operating points: 2048 K vectors (128, bf16, channel
+    offsets) encoded with the dither at 1.7 and 2.5 bps against the oracle
+    (every vector), and the dithered decode bit-exact against the oracle's."""
+    rng = np.random.default_rng(71)
+    k = rng.standard_normal((2048, 128))
+    k[:, [5, 90]] += 3.0
+    bits = workloads.f32_to_bf16_bits(k.astype(np.float32))
+    xh = workloads.bf16_bits_to_f64(bits)
+    say("case: kv low rate %g bps" % bps)
+    g = hq.hq_kv_encode(T.bf16_device(bits, (2048, 128)), bps, 1, dither_seed=9, dither_base=77)
+    torch.cuda.synchronize()
+    ora = codec.encode(xh, "E8", 128, bps, rht_seed=1, dither_seed=9, dither_base=77)
+    assert np.array_equal(T.host(g["scale"]).astype(np.float64), ora["scale"])
+    _, _, _, ok = T.compare_indices(T.host(g["idx"]), T.u32(g["coset"]), ora, "E8", 128,
+                                    "kv %g bps" % bps)
+    assert np.array_equal(T.host(g["rice_k"])[ok].astype(np.int64), ora["rice_k"][ok])
+    assert np.array_equal(T.u32(g["tile_bits"])[ok].astype(np.int64), ora["tile_bits"][ok])
+    check_decode(ora, "E8", 128, 1, "kv %g bps" % bps, exact=True, dither_seed=9, dither_base=77)
