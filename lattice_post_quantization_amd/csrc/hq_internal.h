@@ -165,6 +165,13 @@ bool e8_fast_decode_ok(const DecodeLaunch& a);
 hipError_t launch_encode_e8_fast(const EncodeLaunch& a, const EncBatch& b, hipStream_t s);
 hipError_t launch_decode_e8_fast(const DecodeLaunch& a, const DecBatch& b, hipStream_t s);
 
+// Fast path for E8 / tile 128 (KV vectors, with or without the dither):
+// bf16 input (encode), either output type (decode); groups of 32 tiles.
+bool e8_128_encode_ok(const EncodeLaunch& a);
+bool e8_128_decode_ok(const DecodeLaunch& a);
+hipError_t launch_encode_e8_128(const EncodeLaunch& a, hipStream_t s);
+hipError_t launch_decode_e8_128(const DecodeLaunch& a, hipStream_t s);
+
 // tiles handled by one rate/pack block
 constexpr int kRateTilesPerBlock = 16;
 

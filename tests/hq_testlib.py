@@ -59,14 +59,14 @@ def compare_indices(g_idx, g_coset, ora, lattice, n, label=""):
 
 
 def compare_decoded(g_vals, o_round, o_raw, scale, out_bf16, exact, label=""):
-    """|gpu - oracle fp64| <= 1e-5 * Delta, plus half a bf16 ulp of the
-    oracle value for bf16 outputs (the output rounding); `exact` additionally
-    demands bit equality with the identically rounded oracle value."""
+    """|gpu - oracle fp64| <= 1e-5 * Delta plus half an ulp of the output
+    type at the oracle value (the output rounding: bf16 or fp32); `exact`
+    additionally demands bit equality with the identically rounded oracle
+    value."""
     g = np.asarray(g_vals, np.float64)
     raw = np.asarray(o_raw, np.float64)
     tol = 1e-5 * np.asarray(scale, np.float64)[:, None]
-    if out_bf16:
-        tol = tol + 0.5 * np.abs(raw) * 2.0 ** -7
+    tol = tol + 0.5 * np.abs(raw) * (2.0 ** -7 if out_bf16 else 2.0 ** -23)
     err = np.abs(g - raw)
     assert np.all(err <= tol), "%s: max err / Delta %.3g" % (
         label, np.max(err / np.asarray(scale)[:, None]))

@@ -590,3 +590,73 @@ def test_kv_low_rate_parity(bps):
     assert np.array_equal(T.host(g["rice_k"])[ok].astype(np.int64), ora["rice_k"][ok])
     assert np.array_equal(T.u32(g["tile_bits"])[ok].astype(np.int64), ora["tile_bits"][ok])
     check_decode(ora, "E8", 128, 1, "kv %g bps" % bps, exact=True, dither_seed=9, dither_base=77)
+
+
+def test_e8_128_groups_edges():
+    """E8 / tile 128 on the edges of its 32-vector groups: dithered encodes
+    of 1, 31, 33 and 95 vectors (a zero vector among them) at dither offsets
+    up to 2^31; caller scales (arbitrary fp32 values); decode of arbitrary
+    int8 indices, whose Hadamard sums leave the int16 range, with and without
+    the dither; the status bits."""
+    rng = np.random.default_rng(41)
+    for nvec, base in ((1, 5), (31, 1000), (33, 77777), (95, 2 ** 31)):
+        x = rng.standard_normal((nvec, 128)) * 0.5 + 0.1
+        x[nvec // 2] = 0.0
+        bits = workloads.f32_to_bf16_bits(x.astype(np.float32))
+        xh = workloads.bf16_bits_to_f64(bits)
+        label = "kv %d vectors, dither base %d" % (nvec, base)
+        say("case:", label)
+        g = hq.hq_kv_encode(T.bf16_device(bits, (nvec, 128)), 4.0, 3, dither_seed=9,
+                            dither_base=base)
+        torch.cuda.synchronize()
+        ora = codec.encode(xh, "E8", 128, 4.0, rht_seed=3, dither_seed=9, dither_base=base)
+        skip = midpoint_close(oracle_pre_scale(xh, "E8", 4.0))
+        assert not skip.any()
+        assert np.array_equal(T.host(g["scale"]).astype(np.float64), ora["scale"]), label
+        _, _, _, ok = T.compare_indices(T.host(g["idx"]), T.u32(g["coset"]), ora, "E8", 128,
+                                        label)
+        assert np.array_equal(T.host(g["rice_k"])[ok].astype(np.int64), ora["rice_k"][ok])
+        assert np.array_equal(T.u32(g["tile_bits"])[ok].astype(np.int64), ora["tile_bits"][ok])
+        check_decode(ora, "E8", 128, 3, label, exact=True, dither_seed=9, dither_base=base)
+
+    # caller scales: the automatic ones times 1.37, rounded to fp32
+    x = rng.standard_normal((70, 128))
+    bits = workloads.f32_to_bf16_bits(x.astype(np.float32))
+    xh = workloads.bf16_bits_to_f64(bits)
+    sc = (codec.encode(xh, "E8", 128, 4.0, rht_seed=3)["scale"] * 1.37).astype(np.float32)
+    ora = codec.encode(xh, "E8", 128, 4.0, rht_seed=3, scale=sc.astype(np.float64))
+    say("case: E8/128 caller scales")
+    g = hq.hq_encode_tiles(T.bf16_device(bits, (70, 128)), "E8", 128, 4.0, 3,
+                           scale=torch.from_numpy(sc).cuda())
+    torch.cuda.synchronize()
+    _, _, _, ok = T.compare_indices(T.host(g["idx"]), T.u32(g["coset"]), ora, "E8", 128,
+                                    "caller scales")
+    assert np.array_equal(T.host(g["rice_k"])[ok].astype(np.int64), ora["rice_k"][ok])
+    assert np.array_equal(T.u32(g["tile_bits"])[ok].astype(np.int64), ora["tile_bits"][ok])
+    check_decode(ora, "E8", 128, 3, "caller scales", exact=True)
+
+    # arbitrary indices (bf16-valued scales keep every product exact)
+    n = 45
+    idx = rng.integers(-128, 128, size=(n, 128))
+    idx[0], idx[1] = 127, -128
+    idx[2:20] = rng.integers(-3, 4, size=(18, 128))
+    cw = rng.integers(0, 2 ** 16, size=(n, 1)).astype(np.uint32)
+    scale = codec.bf16_rne(2.0 ** rng.uniform(-8, 2, size=n))
+    arb = {"idx": idx, "coset": cw, "scale": scale}
+    say("case: E8/128 arbitrary indices")
+    check_decode(arb, "E8", 128, 5, "arbitrary indices", exact=True)
+    check_decode(arb, "E8", 128, 5, "arbitrary indices, dither", exact=True, dither_seed=4,
+                 dither_base=123)
+
+    # status bits
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kv = torch.randn((40, 128), device="cuda").to(torch.bfloat16)
+    kv[33, 100] = float("inf")
+    hq.hq_kv_encode(kv, 4.0, 0, dither_seed=1, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & hq.HQ_ST_NONFINITE
+    st.zero_()
+    hq.hq_encode_tiles(kv[:32].contiguous(), "E8", 128, 4.0, 0,
+                       scale=torch.full((32,), 1e-4, device="cuda"), status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == hq.HQ_ST_OVERFLOW
