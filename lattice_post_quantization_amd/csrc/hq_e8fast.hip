@@ -178,21 +178,34 @@ __device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const
 
   // ---- quantizer input U = rne(S K) (units of 2^-24), stored integers
   uint32_t packed[16];
-  uint32_t cbits = 0;
+  uint32_t cbits = 0, ties = 0;
+  int32_t U[64];
   const int r0 = row & 1, r1 = row >> 1;
+  // tile block index of register block blk = b3 + 2 b4 + 4 b5 + 8 b6 + 16 b7
+  auto bpos = [&](int blk) {
+    return (blk & 1) + 2 * r1 + 4 * r0 + 8 * (blk >> 2) + 16 * ((blk >> 1) & 1);
+  };
 #pragma unroll
   for (int blk = 0; blk < 8; ++blk) {
-    int32_t U[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       // two roundings, never fused: q = RN(S K), then RN(q + 1.5 2^52)
       const double m = __dadd_rn(__dmul_rn(v[8 * blk + i], K), kMagic);
-      U[i] = (int32_t)(uint32_t)(uint64_t)__double_as_longlong(m);
+      U[8 * blk + i] = (int32_t)(uint32_t)(uint64_t)__double_as_longlong(m);
     }
-    const int c = e8_block(U, packed[2 * blk], packed[2 * blk + 1]);
-    // tile block index = b3 + 2 b4 + 4 b5 + 8 b6 + 16 b7
-    const int bpos = (blk & 1) + 2 * r1 + 4 * r0 + 8 * (blk >> 2) + 16 * ((blk >> 1) & 1);
-    cbits |= (uint32_t)c << bpos;
+    int c;
+    ties |= e8_block_fast(U + 8 * blk, packed[2 * blk], packed[2 * blk + 1], c) << blk;
+    cbits |= (uint32_t)c << bpos(blk);
+  }
+  if (ties) {
+    // blocks with a coordinate exactly on a rounding boundary
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) {
+      if ((ties >> blk) & 1u) {
+        const int c = e8_block_exact(U + 8 * blk, packed[2 * blk], packed[2 * blk + 1]);
+        cbits = (cbits & ~(1u << bpos(blk))) | ((uint32_t)c << bpos(blk));
+      }
+    }
   }
   const uint32_t coset_word = tile_or_u32(cbits);
 
@@ -265,7 +278,7 @@ __device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const
 // The loop body ends with reading the next group from LDS, after this
 // group's stores; the last iteration prefetches its own group again (an L2
 // hit) so that no branch surrounds the memory operations.
-__global__ __launch_bounds__(kBlock) void encode_e8_fast(EncodeLaunch a, EncBatch b) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void encode_e8_fast(EncodeLaunch a, EncBatch b) {
   __shared__ uint32_t sign_tab[128];
   __shared__ uint4 stage[kBlock / 64][kEncStage];
   __shared__ uint4 ostage[kBlock / 64][256];

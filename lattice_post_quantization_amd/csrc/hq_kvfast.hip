@@ -52,7 +52,7 @@ __device__ inline double pair_sum_f64(double v) {
 }
 
 // d = w - Q_E8(w) for one block, on the 2^-24 grid (W = w 2^24), exact.  The
-// nearest point is decided as in e8_block; with off = [coset a] 2^23 the
+// nearest point is decided as in e8_block_fast; with off = [coset a] 2^23 the
 // coordinate's offset from its point is ((W + off) mod 2^24) - 2^23, and the
 // parity flip moves one coordinate's point by one.
 __device__ inline void e8_dither_block(const int32_t* W, int32_t* d24) {
@@ -212,8 +212,11 @@ __device__ inline void enc128_group(const EncodeLaunch& a, const uint32_t* sign_
   // register i now holds element (i mod 32) + 32 r + 64 (i / 32)
 
   uint32_t packed[16];
-  uint32_t cbits = 0;
+  uint32_t cbits = 0, ties = 0;
+  int32_t U[64];
   const uint64_t vec = (uint64_t)(a.dither_base + tile0 + t);
+  // tile block index of register block blk = element / 8
+  auto bpos = [&](int blk) { return (blk & 3) + 4 * r + 8 * (blk >> 2); };
 #pragma unroll
   for (int blk = 0; blk < 8; ++blk) {
     // the block's dither first (fewer registers live across the hash)
@@ -225,16 +228,31 @@ __device__ inline void enc128_group(const EncodeLaunch& a, const uint32_t* sign_
       for (int i = 0; i < 8; ++i) W[i] = dither_w(a.dither_seed, vec, e0 + (uint32_t)i);
       e8_dither_block(W, d24);
     }
-    int32_t U[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       // two roundings, never fused: q = RN(S K), then RN(q + 1.5 2^52)
       const double m = __dadd_rn(__dmul_rn(v[8 * blk + i], K), kMagic);
-      U[i] = (int32_t)(uint32_t)(uint64_t)__double_as_longlong(m) + d24[i];
+      U[8 * blk + i] = (int32_t)(uint32_t)(uint64_t)__double_as_longlong(m) + d24[i];
     }
-    const int c = e8_block(U, packed[2 * blk], packed[2 * blk + 1]);
-    // tile block index = element / 8 = (blk mod 4) + 4 r + 8 (blk / 4)
-    cbits |= (uint32_t)c << ((blk & 3) + 4 * r + 8 * (blk >> 2));
+    int c;
+    const uint32_t tie = e8_block_fast(U + 8 * blk, packed[2 * blk], packed[2 * blk + 1], c);
+    if constexpr (DITHER) {
+      // searched at once: the hash leaves no registers for deferring it
+      if (tie) c = e8_block_exact(U + 8 * blk, packed[2 * blk], packed[2 * blk + 1]);
+    } else {
+      ties |= tie << blk;
+    }
+    cbits |= (uint32_t)c << bpos(blk);
+  }
+  if (ties) {
+    // blocks with a coordinate exactly on a rounding boundary
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) {
+      if ((ties >> blk) & 1u) {
+        const int c = e8_block_exact(U + 8 * blk, packed[2 * blk], packed[2 * blk + 1]);
+        cbits = (cbits & ~(1u << bpos(blk))) | ((uint32_t)c << bpos(blk));
+      }
+    }
   }
   const uint32_t coset_word = pair_or_u32(cbits);
 

@@ -143,9 +143,12 @@ __device__ inline void fill_sign_table(uint32_t* tab, const uint32_t* signs) {
 // the overflow flag has |u_i| < 126, keeping every biased byte in 0..255).
 // The last coordinate is stored halved, from U_7 + [coset a] 2^23 with its
 // flip applied before halving.
-// Blocks with a coordinate on an integer or half-integer take the general
-// decoder (rare; same results).  Writes the stored integers (z0..z6,
-// floor(z7/2)) as two dwords of int8 and returns the coset bit.
+// Blocks with a coordinate on an integer or half-integer need the general
+// decoder (rare; same results): e8_block_fast then returns 1 and its other
+// results are meaningless, and e8_block_exact gives the answer.  Both write
+// the stored integers (z0..z6, floor(z7/2)) as two dwords of int8 and the
+// coset bit.  The fast decision has no branch, so the blocks of a lane can
+// be scheduled together and the rare search runs once, after all of them.
 __device__ inline uint32_t sad_u32(uint32_t a, uint32_t b) {
   uint32_t r;
   __asm__("v_sad_u32 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
@@ -182,7 +185,7 @@ __device__ inline uint32_t third_bytes(int32_t a, int32_t b, int32_t c, int32_t 
 
 __device__ inline uint32_t pack4(const int32_t* s);
 
-__device__ inline int e8_block(const int32_t* U, uint32_t& p0, uint32_t& p1) {
+__device__ inline uint32_t e8_block_fast(const int32_t* U, uint32_t& p0, uint32_t& p1, int& cs) {
   // keys (B << 3) + i and (B << 3) + 7 - i: |8F - 2^26| plus the index
   uint32_t k1[8], k2[8];
 #define HQ_E8_KEYS(i)                                             \
@@ -199,14 +202,7 @@ __device__ inline int e8_block(const int32_t* U, uint32_t& p0, uint32_t& p1) {
   const uint32_t kmax = max3u(max3u(k2[0], k2[1], k2[2]), max3u(k2[3], k2[4], k2[5]),
                               k2[6] > k2[7] ? k2[6] : k2[7]);
   const int32_t bmin = (int32_t)(kmin >> 3), bmax = (int32_t)(kmax >> 3);
-  if (bmin == 0 || bmax == kHalf) {
-    int32_t z[8];
-    const int c = e8_nearest(U, z);
-    z[7] >>= 1;
-    p0 = pack4(z);
-    p1 = pack4(z + 4);
-    return c;
-  }
+  const uint32_t tie = (uint32_t)(bmin == 0) | (uint32_t)(bmax == kHalf);
   const uint32_t sumB =
       (((k1[0] + k1[1] + k1[2]) + (k1[3] + k1[4] + k1[5]) + (k1[6] + k1[7])) - 28u) >> 3;
   const uint32_t X = ((uint32_t)U[0] ^ (uint32_t)U[1] ^ (uint32_t)U[2]) ^
@@ -238,12 +234,22 @@ __device__ inline int e8_block(const int32_t* U, uint32_t& p0, uint32_t& p1) {
         (jo < 4u ? d : 0u)) ^ kBias;
   p1 = ((top_bytes((uint32_t)U[4], (uint32_t)U[5], (uint32_t)U[6], (uint32_t)s7) ^ kBias) + up1 +
         (jo - 4u < 3u ? d : 0u)) ^ kBias;
-  return c;
+  cs = c;
+  return tie;
 }
 
 __device__ inline uint32_t pack4(const int32_t* s) {
   return ((uint32_t)s[0] & 0xFFu) | (((uint32_t)s[1] & 0xFFu) << 8) |
          (((uint32_t)s[2] & 0xFFu) << 16) | ((uint32_t)s[3] << 24);
+}
+
+__device__ inline int e8_block_exact(const int32_t* U, uint32_t& p0, uint32_t& p1) {
+  int32_t z[8];
+  const int c = e8_nearest(U, z);
+  z[7] >>= 1;
+  p0 = pack4(z);
+  p1 = pack4(z + 4);
+  return c;
 }
 
 // zigzag of four int8 values held in a dword, bytewise: 2z, or its
