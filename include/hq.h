@@ -212,14 +212,15 @@ hq_status hq_unpack(const hq_params* p, const uint32_t* stream_words,
  * <P, H (s (.) x_t)>, so the kernel rotates each n-column slice of x once
  * (into the workspace) and then needs only the stored indices of W.
  *
- * p: lattice E8, tile 128 or 256, rht_seed of the encode; no dither.
- * idx [rows*cols] int8, coset [n_tiles] (E8/256) or [n_tiles] 16-bit words
- * as for decode, scale [n_tiles] fp32 (tile t = row r, column slice t mod
- * cols/n); x [m][cols] fp32 (m vectors, each contiguous), 1 <= m <= 8;
- * y [m][rows] fp32 out; workspace: device scratch of at least
- * hq_gemv_workspace_bytes(rows, cols, m) bytes, 16-byte aligned.  Results
- * are fp32 sums of the products in a fixed order (deterministic).  Errors as for decode;
- * HQ_EUNSUPPORTED for another lattice or HQ_DITHER.
+ * p: lattice E8, tile 256, rht_seed of the encode; no dither.
+ * idx [rows*cols] int8 (cols a multiple of 256, at most 2^24), coset
+ * [n_tiles] words, scale [n_tiles] fp32 (tile t = row t / (cols/256),
+ * column slice t mod (cols/256)); x [m][cols] fp32 (m vectors, each
+ * contiguous), 1 <= m <= 8; y [m][rows] fp32 out; workspace: device
+ * scratch of at least hq_gemv_workspace_bytes(rows, cols, m) bytes,
+ * 16-byte aligned.  Results are fp32 sums of the products in a fixed order
+ * (deterministic).  Errors as for decode; HQ_EUNSUPPORTED for another
+ * lattice or tile, or HQ_DITHER.
  */
 hq_status hq_gemv(const hq_params* p, const int8_t* idx, const uint32_t* coset,
                   const float* scale, int64_t rows, int64_t cols, const float* x,
@@ -227,8 +228,36 @@ hq_status hq_gemv(const hq_params* p, const int8_t* idx, const uint32_t* coset,
                   uint32_t* status, hipStream_t stream);
 
 /* Device workspace bytes hq_gemv needs for a rows x cols matrix and m
-   vectors (the rotated vectors and the partial sums of the column splits). */
+   vectors (the rotated vectors, their 8-block sums, and the totals of the
+   column chunks when a row has more than one); 0 for invalid sizes. */
 size_t hq_gemv_workspace_bytes(int64_t rows, int64_t cols, int32_t m);
+
+/*
+ * hq_gemv_batch - hq_gemv for `count` matrices with the same m and the same
+ * p (a layer's projections), enqueued as three kernel launches per group of
+ * up to eight matrices instead of up to three per matrix.  Same passages,
+ * arguments per item and results (bit for bit) as one hq_gemv call per item.
+ * `items` is a host array read during the call; every item is validated and
+ * nothing is enqueued unless all pass.  The workspace (16-byte aligned, at
+ * least hq_gemv_batch_workspace_bytes(count, items, m) bytes) is divided
+ * among the items in order; an item with rows or cols 0 is skipped.
+ */
+typedef struct {
+  const int8_t* idx;      /* [rows*cols]                                */
+  const uint32_t* coset;  /* [n_tiles]                                  */
+  const float* scale;     /* [n_tiles]                                  */
+  int64_t rows, cols;
+  const float* x;         /* [m][cols]                                  */
+  float* y;               /* [m][rows]                                  */
+} hq_gemv_item;
+
+hq_status hq_gemv_batch(const hq_params* p, int32_t count, const hq_gemv_item* items,
+                        int32_t m, void* workspace, size_t workspace_bytes,
+                        uint32_t* status, hipStream_t stream);
+
+/* Device workspace bytes hq_gemv_batch needs (the sum over the items of
+   hq_gemv_workspace_bytes); 0 for invalid arguments. */
+size_t hq_gemv_batch_workspace_bytes(int32_t count, const hq_gemv_item* items, int32_t m);
 
 /*
  * hq_kv_scores - attention scores of queries against one head's compressed

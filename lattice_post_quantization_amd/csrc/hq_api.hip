@@ -458,51 +458,104 @@ hq_status hq_unpack(const hq_params* p, const uint32_t* stream_words,
 }
 
 size_t hq_gemv_workspace_bytes(int64_t rows, int64_t cols, int32_t m) {
-  if (rows <= 0 || cols <= 0 || m <= 0 || cols % 256 != 0) return 0;
-  int64_t splits, span;
-  gemv_split(rows, cols, splits, span);
-  // the rotated vectors, then the partial sums (16-byte aligned)
-  const size_t xr = ((size_t)cols * (size_t)m * sizeof(float) + 15) / 16 * 16;
-  return xr + (size_t)splits * (size_t)m * (size_t)rows * sizeof(float);
+  if (rows <= 0 || cols <= 0 || m <= 0 || m > 8 || cols % 256 != 0 || cols > kGemvMaxCols)
+    return 0;
+  return gemv_workspace(rows, cols, m);
+}
+
+namespace {
+
+// Argument checks of one hq_gemv matrix (device residency checked apart).
+hq_status check_gemv(const int8_t* idx, const uint32_t* coset, const float* scale, int64_t rows,
+                     int64_t cols, const float* x, const float* y) {
+  if (rows < 0 || cols < 0 || cols % 256 != 0 || cols > kGemvMaxCols) return HQ_EINVAL;
+  if (rows == 0 || cols == 0) return HQ_OK;   // nothing to compute
+  if (idx == nullptr || coset == nullptr || scale == nullptr || x == nullptr || y == nullptr)
+    return HQ_EINVAL;
+  if (rows > INT64_MAX / cols) return HQ_EINVAL;
+  if (!aligned16(idx) || !aligned16(x) || ((uintptr_t)y & 3u) || ((uintptr_t)coset & 3u) ||
+      ((uintptr_t)scale & 3u))
+    return HQ_EINVAL;
+  return HQ_OK;
+}
+
+bool gemv_on_device(const hq_gemv_item& it) {
+  return on_device(it.idx) && on_device(it.coset) && on_device(it.scale) && on_device(it.x) &&
+         on_device(it.y);
+}
+
+}  // namespace
+
+size_t hq_gemv_batch_workspace_bytes(int32_t count, const hq_gemv_item* items, int32_t m) {
+  if (count < 0 || (count > 0 && items == nullptr) || m < 1 || m > 8) return 0;
+  size_t total = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const hq_gemv_item& it = items[i];
+    if (it.rows < 0 || it.cols < 0 || it.cols % 256 != 0 || it.cols > kGemvMaxCols) return 0;
+    if (it.rows > 0 && it.cols > 0) total += gemv_workspace(it.rows, it.cols, m);
+  }
+  return total;
+}
+
+hq_status hq_gemv_batch(const hq_params* p, int32_t count, const hq_gemv_item* items, int32_t m,
+                        void* workspace, size_t workspace_bytes, uint32_t* status,
+                        hipStream_t stream) {
+  (void)status;
+  hq_status st = check_params(p);
+  if (st != HQ_OK) return st;
+  if (p->lattice != HQ_E8 || p->tile != 256 || (p->flags & HQ_DITHER)) return HQ_EUNSUPPORTED;
+  if (count < 0 || (count > 0 && items == nullptr) || m < 1 || m > 8) return HQ_EINVAL;
+  bool any = false;
+  for (int32_t i = 0; i < count; ++i) {
+    const hq_gemv_item& it = items[i];
+    st = check_gemv(it.idx, it.coset, it.scale, it.rows, it.cols, it.x, it.y);
+    if (st != HQ_OK) return st;
+    any = any || (it.rows > 0 && it.cols > 0);
+  }
+  if (!any) return HQ_OK;
+  if (workspace == nullptr || !aligned16(workspace) ||
+      workspace_bytes < hq_gemv_batch_workspace_bytes(count, items, m))
+    return HQ_EINVAL;
+  for (int32_t i = 0; i < count; ++i)
+    if (items[i].rows > 0 && items[i].cols > 0 && !gemv_on_device(items[i])) return HQ_EINVAL;
+  if (!on_device(workspace)) return HQ_EINVAL;
+  // launches of up to kGemvMaxItems matrices, each with its own workspace
+  // slice in item order
+  GemvBatch b;
+  memset(&b, 0, sizeof(b));
+  b.m = m;
+  make_signs(p->rht_seed, p->tile, b.signs);
+  char* ws = static_cast<char*>(workspace);
+  for (int32_t i = 0; i <= count; ++i) {
+    if ((i == count || b.n == kGemvMaxItems) && b.n > 0) {
+      char* base = ws;
+      for (int k = 0; k < b.n; ++k) ws += gemv_workspace(b.it[k].rows, b.it[k].cols, m);
+      gemv_layout(b, base);
+      if (launch_gemv(b, stream) != hipSuccess) return HQ_EDEVICE;
+      b.n = 0;
+    }
+    if (i == count) break;
+    const hq_gemv_item& it = items[i];
+    if (it.rows == 0 || it.cols == 0) continue;
+    GemvItem& g = b.it[b.n++];
+    memset(&g, 0, sizeof(g));
+    g.idx = it.idx;
+    g.coset = it.coset;
+    g.scale = it.scale;
+    g.rows = it.rows;
+    g.cols = it.cols;
+    g.x = it.x;
+    g.y = it.y;
+  }
+  return HQ_OK;
 }
 
 hq_status hq_gemv(const hq_params* p, const int8_t* idx, const uint32_t* coset,
                   const float* scale, int64_t rows, int64_t cols, const float* x, int32_t m,
                   float* y, void* workspace, size_t workspace_bytes, uint32_t* status,
                   hipStream_t stream) {
-  (void)status;
-  hq_status st = check_params(p);
-  if (st != HQ_OK) return st;
-  if (p->lattice != HQ_E8 || p->tile != 256 || (p->flags & HQ_DITHER)) return HQ_EUNSUPPORTED;
-  if (rows < 0 || cols < 0 || cols % 256 != 0 || m < 1 || m > 8) return HQ_EINVAL;
-  if (rows == 0 || cols == 0) return HQ_OK;   // nothing to compute
-  if (idx == nullptr || coset == nullptr || scale == nullptr || x == nullptr || y == nullptr ||
-      workspace == nullptr)
-    return HQ_EINVAL;
-  if (rows > INT64_MAX / cols || workspace_bytes < hq_gemv_workspace_bytes(rows, cols, m))
-    return HQ_EINVAL;
-  if (!aligned16(idx) || !aligned16(x) || !aligned16(workspace) || ((uintptr_t)y & 3u) ||
-      ((uintptr_t)coset & 3u) || ((uintptr_t)scale & 3u))
-    return HQ_EINVAL;
-  if (!on_device(idx) || !on_device(coset) || !on_device(scale) || !on_device(x) ||
-      !on_device(y) || !on_device(workspace))
-    return HQ_EINVAL;
-  GemvLaunch a;
-  memset(&a, 0, sizeof(a));
-  a.idx = idx;
-  a.coset = coset;
-  a.scale = scale;
-  a.rows = rows;
-  a.cols = cols;
-  a.x = x;
-  a.m = m;
-  a.y = y;
-  a.xr = static_cast<float*>(workspace);
-  gemv_split(rows, cols, a.splits, a.span);
-  a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                    ((size_t)cols * (size_t)m * sizeof(float) + 15) / 16 * 16);
-  make_signs(p->rht_seed, p->tile, a.signs);
-  return launched(launch_gemv(a, stream));
+  const hq_gemv_item it{idx, coset, scale, rows, cols, x, y};
+  return hq_gemv_batch(p, 1, &it, m, workspace, workspace_bytes, status, stream);
 }
 
 size_t hq_kv_scores_workspace_bytes(int64_t n_q) {

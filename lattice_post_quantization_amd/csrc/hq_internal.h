@@ -78,24 +78,46 @@ struct UnpackLaunch {
   uint32_t* status;     // may be nullptr
 };
 
-struct GemvLaunch {
+// One matrix of an hq_gemv batch.  The workspace pointers and the plan are
+// filled in by the API; wave0 / rot0 / red0 number the matrix's waves,
+// rotate waves and reduce elements across the batch.
+struct GemvItem {
   const int8_t* idx;
   const uint32_t* coset;
   const float* scale;
   int64_t rows;
-  int64_t cols;         // multiple of 256 (E8, tile 256)
+  int64_t cols;         // multiple of 256 (E8, tile 256), at most kGemvMaxCols
   const float* x;       // [m][cols]
-  int m;                // 1..8
   float* y;             // [m][rows]
   float* xr;            // workspace: H (s (.) x) per 256-column slice, [m][cols]
-  float* part;          // workspace: partial sums [splits][m][rows]
-  int64_t splits;       // column splits
-  int64_t span;         // slices per split
-  uint32_t signs[8];
+  float* xs;            // workspace: sums of xr over each 8-block, [m][cols / 8]
+  float* part;          // workspace: chunk totals [n_chunks][m][rows] (n_chunks > 1)
+  int64_t n_chunks;     // column chunks per row
+  int64_t rows_per_wave;
+  int64_t wave0;        // first gemv wave of this matrix
+  int64_t rot0;         // first rotate wave
+  int64_t red0;         // first reduce element
 };
 
-// Column splits of hq_gemv (splits * span >= cols / 256).
-void gemv_split(int64_t rows, int64_t cols, int64_t& splits, int64_t& span);
+constexpr int kGemvMaxItems = 8;   // matrices per launch
+
+struct GemvBatch {
+  int32_t n;            // matrices, 1..kGemvMaxItems
+  int32_t m;            // vectors, 1..8
+  int64_t n_waves;      // gemv waves of the batch
+  int64_t n_rot;        // rotate waves
+  int64_t n_red;        // reduce elements
+  uint32_t signs[8];
+  GemvItem it[kGemvMaxItems];
+};
+
+// Largest cols hq_gemv accepts, its work split (column chunks per row, rows
+// per wave) and the workspace one matrix needs.
+constexpr int64_t kGemvMaxCols = (int64_t)1 << 24;
+void gemv_plan(int64_t rows, int64_t cols, int m, int64_t& n_chunks, int64_t& rows_per_wave);
+size_t gemv_workspace(int64_t rows, int64_t cols, int m);
+// Fills the workspace pointers, the plan and the numbering of b.it[0 .. b.n).
+void gemv_layout(GemvBatch& b, char* workspace);
 
 struct ScoreLaunch {
   const float* q;       // [n_q][128]
@@ -117,7 +139,7 @@ hipError_t launch_encode(const EncodeLaunch& a, hipStream_t s);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t s);
 hipError_t launch_rate(const RateLaunch& a, hipStream_t s);
 hipError_t launch_unpack(const UnpackLaunch& a, hipStream_t s);
-hipError_t launch_gemv(const GemvLaunch& a, hipStream_t s);
+hipError_t launch_gemv(const GemvBatch& b, hipStream_t s);
 hipError_t launch_scores(const ScoreLaunch& a, hipStream_t s);
 
 // Fast path for E8 / tile 256 / bf16 input (encode) and E8 / tile 256

@@ -58,6 +58,12 @@ class EncodeItem(ctypes.Structure):
                 ("rice_k", ctypes.c_void_p), ("tile_bits", ctypes.c_void_p)]
 
 
+class GemvItem(ctypes.Structure):
+    _fields_ = [("idx", ctypes.c_void_p), ("coset", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("x", ctypes.c_void_p),
+                ("y", ctypes.c_void_p)]
+
+
 class DecodeItem(ctypes.Structure):
     _fields_ = [("idx", ctypes.c_void_p), ("coset", ctypes.c_void_p), ("scale", ctypes.c_void_p),
                 ("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("y", ctypes.c_void_p)]
@@ -76,6 +82,8 @@ _SIGNATURES = {
     "hq_unpack": (_I32, [_PP, _P, _P, _I64, _P, _P, _P, _P, _P]),
     "hq_gemv": (_I32, [_PP, _P, _P, _P, _I64, _I64, _P, _I32, _P, _P, _SZ, _P, _P]),
     "hq_gemv_workspace_bytes": (_SZ, [_I64, _I64, _I32]),
+    "hq_gemv_batch": (_I32, [_PP, _I32, _P, _I32, _P, _SZ, _P, _P]),
+    "hq_gemv_batch_workspace_bytes": (_SZ, [_I32, _P, _I32]),
     "hq_kv_scores": (_I32, [_PP, _P, _I64, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
     "hq_kv_scores_workspace_bytes": (_SZ, [_I64]),
     "hq_kv_encode": (_I32, [_PP, _P, _I32, _I64, _P, _P, _P, _P, _P, _P, _P]),
@@ -332,6 +340,41 @@ def hq_gemv(idx, coset, scale, x, rht_seed=0, out=None, workspace=None):
                          _ptr(xv), m, _ptr(y), _ptr(ws), ws.numel(), None, _stream(dev))
     _check(code, "hq_gemv")
     return y.reshape(-1) if x.dim() == 1 else y
+
+
+def hq_gemv_batch(mats, xs, rht_seed=0, outs=None, workspace=None):
+    """hq_gemv for several E8/256-coded matrices in one call: mats is a list
+    of dicts with idx, coset and scale, xs the matching fp32 inputs (all 1-D,
+    or all (m, cols) with the same m).  Returns the list of outputs."""
+    if len(mats) != len(xs):
+        raise ValueError("one input per matrix")
+    if not mats:
+        return []
+    dev = mats[0]["idx"].device
+    one_d = xs[0].dim() == 1
+    m = 1 if one_d else xs[0].shape[0]
+    items = (GemvItem * len(mats))()
+    ys = []
+    for i, (e, x) in enumerate(zip(mats, xs)):
+        for name in ("idx", "coset", "scale"):
+            _device_tensor(e[name], name)
+        _device_tensor(x, "x")
+        if (x.dim() == 1) != one_d or (not one_d and x.shape[0] != m):
+            raise ValueError("inputs must all be 1-D or all have the same m")
+        rows, cols = e["idx"].shape
+        y = outs[i] if outs is not None else torch.empty((m, rows), dtype=torch.float32,
+                                                          device=dev)
+        ys.append(y)
+        items[i] = GemvItem(_addr(e["idx"]), _addr(e["coset"]), _addr(e["scale"]), rows, cols,
+                            _addr(x), _addr(y))
+    nb = lib().hq_gemv_batch_workspace_bytes(len(mats), ctypes.byref(items), m)
+    ws = workspace if workspace is not None else torch.empty(max(nb, 16), dtype=torch.uint8,
+                                                             device=dev)
+    p = make_params("E8", 256, 4.0, rht_seed)
+    code = lib().hq_gemv_batch(ctypes.byref(p), len(mats), ctypes.byref(items), m, _ptr(ws),
+                               ws.numel(), None, _stream(dev))
+    _check(code, "hq_gemv_batch")
+    return [y.reshape(-1) for y in ys] if one_d else ys
 
 
 def hq_kv_scores(q, enc, rht_seed=0, dither_seed=None, dither_base=0, out=None,

@@ -223,9 +223,22 @@ def test_unpack_validation_codes():
 def test_gemv_validation_codes():
     lib = hq.lib()
     p = hq.make_params("E8", 256, 4.0, 3)
-    # the rotated vectors and at least one split of partial sums
-    assert lib.hq_gemv_workspace_bytes(1024, 4096, 2) >= 4096 * 2 * 4 + 1024 * 2 * 4
+    # at least the rotated vectors and their 8-block sums; invalid sizes 0
+    for m in (1, 2, 3, 8):
+        assert lib.hq_gemv_workspace_bytes(1024, 4096, m) >= (4096 + 512) * m * 4
     assert lib.hq_gemv_workspace_bytes(1024, 4000, 2) == 0
+    assert lib.hq_gemv_workspace_bytes(4, (1 << 24) + 256, 1) == 0
+    assert lib.hq_gemv_workspace_bytes(4, 256, 9) == 0
+    # a batch needs the sum of its items' workspaces
+    shapes = ((4096, 4096), (1024, 4096), (4096, 14336), (37, 1536))
+    items = (hq.GemvItem * len(shapes))()
+    for i, (r, c) in enumerate(shapes):
+        items[i] = hq.GemvItem(FAKE, FAKE, FAKE, r, c, FAKE, FAKE)
+    for m in (1, 2, 5):
+        assert lib.hq_gemv_batch_workspace_bytes(len(shapes), items, m) == sum(
+            lib.hq_gemv_workspace_bytes(r, c, m) for r, c in shapes)
+    items[3].cols = 1000
+    assert lib.hq_gemv_batch_workspace_bytes(len(shapes), items, 1) == 0
     # nothing to compute: a no-op
     assert lib.hq_gemv(ctypes.byref(p), None, None, None, 0, 256, None, 1, None, None, 0, None,
                        None) == hq.HQ_OK
@@ -238,12 +251,25 @@ def test_gemv_validation_codes():
     for mm in (0, 9):
         assert lib.hq_gemv(ctypes.byref(p), FAKE, FAKE, FAKE, 4, 256, FAKE, mm, FAKE, FAKE, 1 << 20,
                            None, None) == hq.HQ_EINVAL
-    assert lib.hq_gemv(ctypes.byref(p), FAKE, FAKE, FAKE, 4, 384, FAKE, 1, FAKE, FAKE, 1 << 20,
-                       None, None) == hq.HQ_EINVAL
+    for cols in (384, (1 << 24) + 256):
+        assert lib.hq_gemv(ctypes.byref(p), FAKE, FAKE, FAKE, 4, cols, FAKE, 1, FAKE, FAKE,
+                           1 << 40, None, None) == hq.HQ_EINVAL
     assert lib.hq_gemv(ctypes.byref(p), FAKE, FAKE, FAKE, 4, 512, FAKE, 2, FAKE, FAKE, 100,
                        None, None) == hq.HQ_EINVAL
     assert lib.hq_gemv(ctypes.byref(p), FAKE, None, FAKE, 4, 512, FAKE, 1, FAKE, FAKE, 1 << 20,
                        None, None) == hq.HQ_EINVAL
+    # the batch form: the same checks per item, nothing for an empty batch
+    assert lib.hq_gemv_batch(ctypes.byref(p), 0, None, 1, None, 0, None, None) == hq.HQ_OK
+    items = (hq.GemvItem * 2)()
+    items[0] = hq.GemvItem(FAKE, FAKE, FAKE, 4, 512, FAKE, FAKE)
+    items[1] = hq.GemvItem(FAKE, None, FAKE, 4, 512, FAKE, FAKE)
+    assert lib.hq_gemv_batch(ctypes.byref(p), 2, items, 1, FAKE, 1 << 20, None,
+                             None) == hq.HQ_EINVAL
+    assert lib.hq_gemv_batch(ctypes.byref(p), -1, items, 1, FAKE, 1 << 20, None,
+                             None) == hq.HQ_EINVAL
+    assert lib.hq_gemv_batch(ctypes.byref(p), 1, items, 9, FAKE, 1 << 20, None,
+                             None) == hq.HQ_EINVAL
+    assert lib.hq_gemv_batch(ctypes.byref(p), 1, items, 1, FAKE, 10, None, None) == hq.HQ_EINVAL
 
 
 def test_kv_scores_validation_codes():

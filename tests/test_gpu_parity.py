@@ -531,6 +531,30 @@ def test_gemv_parity(m):
         assert np.all(np.abs(T.host(y1) - y_ref[0]) <= tol[0]), label + " 1-D"
 
 
+@pytest.mark.parametrize("m", [1, 2, 3])
+def test_gemv_batch_matches_single_calls(m):
+    """hq_gemv_batch on ten matrices of mixed shapes (ragged row counts, one
+    and several column chunks per row; more than one launch group) gives
+    each matrix's hq_gemv result bit for bit."""
+    rng = np.random.default_rng(61 + m)
+    shapes = [(37, 1536), (64, 4096), (5, 256), (300, 14336), (129, 2048), (1, 768),
+              (77, 5120), (256, 1024), (3, 4096), (90, 512)]
+    mats, xs = [], []
+    for i, (rows, cols) in enumerate(shapes):
+        w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
+        bits = workloads.f32_to_bf16_bits(w)
+        say("case: gemv batch m=%d item %d %dx%d" % (m, i, rows, cols))
+        mats.append(hq.hq_encode_tiles(T.bf16_device(bits, (rows, cols)), "E8", 256, 4.0, 9))
+        x = rng.standard_normal((m, cols)).astype(np.float32)
+        xs.append(torch.from_numpy(x[0] if m == 1 else x).cuda())
+    ys = hq.hq_gemv_batch(mats, xs, rht_seed=9)
+    torch.cuda.synchronize()
+    for i, (e, x) in enumerate(zip(mats, xs)):
+        y1 = hq.hq_gemv(e["idx"], e["coset"], e["scale"], x, rht_seed=9)
+        torch.cuda.synchronize()
+        assert np.array_equal(T.host(ys[i]).view(np.uint32), T.host(y1).view(np.uint32)), i
+
+
 @pytest.mark.parametrize("dither", [True, False])
 def test_kv_scores_parity(dither):
     """hq_kv_scores against the oracle: q . khat with khat the oracle's fp64
