@@ -496,10 +496,10 @@ def test_gemv_parity(m):
     projection, 1024 x 4096, RHT seed 5), x seeded N(0, 1) in fp32.  Bound
     for fp32: a product passes at most 1 rounding of the rotated input, 9 of
     the block's multiply-add chain, 2 adding the coset term and the second
-    block, 1 of the scale, 3 adding a lane's (up to four) pieces, 6 of the
-    64-lane sum and (chunks - 1) of the chunk sum: at most 21 + chunks
-    <= slices + 16 for these shapes (chunks <= slices / 4 + 1, slices >= 6),
-    so |y - y_ref| <= (slices + 16) 2^-24 B with
+    block, 1 of the scale, (pieces - 1) adding a lane's 1024-column pieces,
+    6 of the 64-lane sum and (chunks - 1) of the chunk sum: 17 + pieces +
+    chunks in all, at most 22 here (pieces + chunks <= 5 for 6 and 16
+    slices at every m), so |y - y_ref| <= (slices + 16) 2^-24 B with
     B = sum_t Delta/32 sum_j |P_j| |(H (s . x_t))_j|, computed here in fp64."""
     from oracle import hadamard, splitmix
     rng = np.random.default_rng(51 + m)
