@@ -165,7 +165,8 @@ hq_status hq_decode_tiles(const hq_params* p, const int8_t* idx,
  * rice_k [n_tiles] uint8, tile_bits [n_tiles] uint32, total_bits: 1 uint64;
  * tile_word_offset [n_tiles + 1] uint64 (required when packing);
  * workspace: device scratch of at least hq_rate_workspace_bytes(n_tiles)
- * bytes (required when packing, else may be NULL).
+ * bytes, 8-byte aligned (required when packing; optional otherwise, where it
+ * replaces one 64-bit atomic per block on *total_bits by a per-block sum).
  */
 hq_status hq_rate(const hq_params* p, const int8_t* idx, const uint32_t* coset,
                   int64_t n_tiles, uint8_t* rice_k, uint32_t* tile_bits,

@@ -376,7 +376,8 @@ hq_status hq_decode_batch(const hq_params* p, int32_t y_dtype, int32_t count,
 
 size_t hq_rate_workspace_bytes(int64_t n_tiles) {
   if (n_tiles <= 0) return 0;
-  return (size_t)((n_tiles + 15) / 16) * sizeof(uint64_t);
+  // word and bit sums of each rate block
+  return 2 * (size_t)((n_tiles + 15) / 16) * sizeof(uint64_t);
 }
 
 hq_status hq_rate(const hq_params* p, const int8_t* idx, const uint32_t* coset, int64_t n_tiles,
@@ -406,6 +407,7 @@ hq_status hq_rate(const hq_params* p, const int8_t* idx, const uint32_t* coset, 
   if (pack && (!on_device(stream_words) || !on_device(tile_word_offset) ||
                !on_device(workspace) || (coset_words(p) > 0 && !on_device(coset))))
     return HQ_EINVAL;
+  if (!pack && workspace != nullptr && !on_device(workspace)) return HQ_EINVAL;
   RateLaunch a;
   memset(&a, 0, sizeof(a));
   a.idx = idx;
@@ -420,7 +422,11 @@ hq_status hq_rate(const hq_params* p, const int8_t* idx, const uint32_t* coset, 
   a.stream = pack ? stream_words : nullptr;
   a.capacity = capacity_words;
   a.tile_word_offset = tile_word_offset;
-  a.block_words = pack ? static_cast<uint64_t*>(workspace) : nullptr;
+  // with a workspace the block sums go there (no atomics); packing needs one
+  const bool ws = workspace != nullptr && workspace_bytes >= hq_rate_workspace_bytes(n_tiles) &&
+                  ((uintptr_t)workspace & 7u) == 0;
+  a.block_words = ws ? static_cast<uint64_t*>(workspace) : nullptr;
+  a.block_bits = ws ? static_cast<uint64_t*>(workspace) + (n_tiles + 15) / 16 : nullptr;
   a.status = status;
   return launched(launch_rate(a, stream));
 }

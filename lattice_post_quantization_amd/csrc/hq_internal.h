@@ -61,7 +61,8 @@ struct RateLaunch {
   uint32_t* stream;     // nullptr: rate only
   uint64_t capacity;
   uint64_t* tile_word_offset;
-  uint64_t* block_words;   // workspace: one uint64 per rate block
+  uint64_t* block_words;   // workspace: one uint64 per rate block (nullptr: none)
+  uint64_t* block_bits;    // workspace: bits per rate block
   uint32_t* status;
 };
 

@@ -10,9 +10,11 @@
 // Three kernels:
 //   rate_kernel  per tile (16 indices per lane): zigzag bytewise, k from
 //                byte sums over three candidates, tile_bits; per block the
-//                sum of ceil(tile_bits/32) into the workspace; the total bit
-//                count is accumulated with one 64-bit atomic per block.
-//   scan_kernel  one block: exclusive prefix sum of the per-block word sums.
+//                sums of ceil(tile_bits/32) and of tile_bits into the
+//                workspace (without a workspace, the bit total is
+//                accumulated with one 64-bit atomic per block instead).
+//   scan_kernel  one block: exclusive prefix sum of the per-block word sums,
+//                and the total of the per-block bit sums.
 //   pack_kernel  per tile: each lane's payload length from byte sums, an
 //                exclusive scan over the tile's lanes gives its first bit;
 //                the lane then streams its 16 codes through a 64-bit window
@@ -171,8 +173,12 @@ __global__ __launch_bounds__(kBlock) void rate_kernel(RateLaunch a) {
   if (threadIdx.x == 0) {
     uint64_t w = 0, b = 0;
     for (int i = 0; i < kBlock / 64; ++i) { w += blk_words[i]; b += blk_bits[i]; }
-    if (a.block_words != nullptr) a.block_words[blockIdx.x] = w;
-    atomicAdd((unsigned long long*)a.total_bits, (unsigned long long)b);
+    if (a.block_words != nullptr) {
+      a.block_words[blockIdx.x] = w;
+      a.block_bits[blockIdx.x] = b;
+    } else {
+      atomicAdd((unsigned long long*)a.total_bits, (unsigned long long)b);
+    }
   }
 }
 
@@ -182,16 +188,31 @@ __global__ void zero_u64_kernel(uint64_t* p) { *p = 0; }
 // contiguous chunk, the chunk totals are scanned in LDS.
 constexpr int kScanThreads = 1024;
 
-__global__ __launch_bounds__(kScanThreads) void scan_kernel(uint64_t* v, int64_t n) {
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(uint64_t* v, int64_t n,
+                                                            const uint64_t* bits,
+                                                            uint64_t* total_bits) {
   __shared__ uint64_t part[kScanThreads];
+  __shared__ uint64_t bsum[kScanThreads / 64];
   const int t = threadIdx.x;
   const int64_t chunk = (n + kScanThreads - 1) / kScanThreads;
   const int64_t lo = t * chunk;
   const int64_t hi = (lo + chunk < n) ? lo + chunk : n;
-  uint64_t s = 0;
-  for (int64_t i = lo; i < hi; ++i) s += v[i];
+  uint64_t s = 0, sb = 0;
+  for (int64_t i = lo; i < hi; ++i) {
+    s += v[i];
+    sb += bits[i];
+  }
   part[t] = s;
+  // the bit total (integer sums: the order does not matter)
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) sb += __shfl_xor(sb, m);
+  if ((t & 63) == 0) bsum[t >> 6] = sb;
   __syncthreads();
+  if (t == 0) {
+    uint64_t tot = 0;
+    for (int i = 0; i < kScanThreads / 64; ++i) tot += bsum[i];
+    *total_bits = tot;
+  }
   // Hillis-Steele inclusive scan of the chunk totals
   for (int d = 1; d < kScanThreads; d <<= 1) {
     const uint64_t add = t >= d ? part[t - d] : 0;
@@ -362,12 +383,14 @@ int64_t n_blocks(int64_t n_tiles) {
 template <int N>
 hipError_t launch_n(const RateLaunch& a, hipStream_t s) {
   const int64_t blocks = n_blocks<N>(a.n_tiles);
-  hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(1), 0, s, a.total_bits);
+  if (a.block_words == nullptr)
+    hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(1), 0, s, a.total_bits);
   hipLaunchKernelGGL(rate_kernel<N>, dim3((unsigned)blocks), dim3(kBlock), 0, s, a);
-  if (a.stream != nullptr) {
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a.block_words, blocks);
+  if (a.block_words != nullptr)
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a.block_words, blocks,
+                       a.block_bits, a.total_bits);
+  if (a.stream != nullptr)
     hipLaunchKernelGGL(pack_kernel<N>, dim3((unsigned)blocks), dim3(kBlock), 0, s, a);
-  }
   return hipGetLastError();
 }
 

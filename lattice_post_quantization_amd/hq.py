@@ -266,7 +266,7 @@ def hq_rate(idx, coset, lattice="E8", tile=256, pack=False, capacity_words=None,
     total = o.get("total_bits")
     if total is None:
         total = torch.empty(1, dtype=torch.int64, device=dev)
-    stream = offs = ws = None
+    stream = offs = None
     if pack:
         if capacity_words is None:
             # the optimal k never costs more than k = 8: 4 + coset + 9 n bits
@@ -277,20 +277,19 @@ def hq_rate(idx, coset, lattice="E8", tile=256, pack=False, capacity_words=None,
         offs = o.get("tile_word_offset")
         if offs is None:
             offs = torch.empty(n_tiles + 1, dtype=torch.int64, device=dev)
-        ws = o.get("workspace")
-        if ws is None:
-            ws = torch.empty(max(rate_workspace_bytes(n_tiles), 8), dtype=torch.uint8, device=dev)
+    ws = o.get("workspace")
+    if ws is None:
+        ws = torch.empty(max(rate_workspace_bytes(n_tiles), 8), dtype=torch.uint8, device=dev)
     p = make_params(lattice, tile, 4.0)
     code = lib().hq_rate(ctypes.byref(p), _ptr(idx), _ptr(coset), n_tiles, _ptr(rice_k),
                          _ptr(tile_bits), _ptr(total), _ptr(stream),
                          int(capacity_words or 0), _ptr(offs), _ptr(ws),
                          0 if ws is None else ws.numel(), _ptr(status), _stream(dev))
     _check(code, "hq_rate")
-    res = {"rice_k": rice_k, "tile_bits": tile_bits, "total_bits": total}
+    res = {"rice_k": rice_k, "tile_bits": tile_bits, "total_bits": total, "workspace": ws}
     if pack:
         res["stream"] = stream
         res["tile_word_offset"] = offs
-        res["workspace"] = ws
     return res
 
 
