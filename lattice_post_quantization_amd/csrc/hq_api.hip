@@ -16,7 +16,6 @@
 #include "hq_internal.h"
 
 namespace hq {
-int64_t rate_blocks(int64_t n_tiles, int tile);
 }
 
 namespace {
@@ -376,8 +375,8 @@ hq_status hq_decode_batch(const hq_params* p, int32_t y_dtype, int32_t count,
 
 size_t hq_rate_workspace_bytes(int64_t n_tiles) {
   if (n_tiles <= 0) return 0;
-  // word and bit sums of each rate block
-  return 2 * (size_t)((n_tiles + 15) / 16) * sizeof(uint64_t);
+  // word and bit sums of each rate block, word sums of each rate wave
+  return 6 * (size_t)rate_workspace_blocks(n_tiles) * sizeof(uint64_t);
 }
 
 hq_status hq_rate(const hq_params* p, const int8_t* idx, const uint32_t* coset, int64_t n_tiles,
@@ -426,7 +425,9 @@ hq_status hq_rate(const hq_params* p, const int8_t* idx, const uint32_t* coset, 
   const bool ws = workspace != nullptr && workspace_bytes >= hq_rate_workspace_bytes(n_tiles) &&
                   ((uintptr_t)workspace & 7u) == 0;
   a.block_words = ws ? static_cast<uint64_t*>(workspace) : nullptr;
-  a.block_bits = ws ? static_cast<uint64_t*>(workspace) + (n_tiles + 15) / 16 : nullptr;
+  const int64_t nb = rate_workspace_blocks(n_tiles);
+  a.block_bits = ws ? static_cast<uint64_t*>(workspace) + nb : nullptr;
+  a.wave_words = ws ? static_cast<uint64_t*>(workspace) + 2 * nb : nullptr;
   a.status = status;
   return launched(launch_rate(a, stream));
 }

@@ -61,8 +61,9 @@ struct RateLaunch {
   uint32_t* stream;     // nullptr: rate only
   uint64_t capacity;
   uint64_t* tile_word_offset;
-  uint64_t* block_words;   // workspace: one uint64 per rate block (nullptr: none)
+  uint64_t* block_words;   // workspace: words per rate block (nullptr: no workspace)
   uint64_t* block_bits;    // workspace: bits per rate block
+  uint64_t* wave_words;    // workspace: words per rate wave
   uint32_t* status;
 };
 
@@ -195,7 +196,8 @@ bool e8_128_decode_ok(const DecodeLaunch& a);
 hipError_t launch_encode_e8_128(const EncodeLaunch& a, hipStream_t s);
 hipError_t launch_decode_e8_128(const DecodeLaunch& a, hipStream_t s);
 
-// tiles handled by one rate/pack block
-constexpr int kRateTilesPerBlock = 16;
+// Rate blocks the hq_rate workspace provides for: per block a word sum and a
+// bit sum, per wave (4 per block) a word sum.
+int64_t rate_workspace_blocks(int64_t n_tiles);
 
 }  // namespace hq

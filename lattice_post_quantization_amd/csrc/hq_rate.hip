@@ -7,20 +7,23 @@
 // accounting); GitHub issue "HyperQuant ... #9", "Additional context" (a
 // packed, Rice-coded lattice-index checkpoint format).
 //
-// Three kernels:
+// Three kernels, each wave owning a contiguous span of tiles (the rate and
+// pack kernels use the same partition):
 //   rate_kernel  per tile (16 indices per lane): zigzag bytewise, k from
-//                byte sums over three candidates, tile_bits; per block the
-//                sums of ceil(tile_bits/32) and of tile_bits into the
-//                workspace (without a workspace, the bit total is
-//                accumulated with one 64-bit atomic per block instead).
+//                byte sums over three candidates, tile_bits; per wave the
+//                sum of ceil(tile_bits/32), per block the sums of
+//                ceil(tile_bits/32) and of tile_bits, into the workspace
+//                (without a workspace, the bit total is accumulated with one
+//                64-bit atomic per block instead).
 //   scan_kernel  one block: exclusive prefix sum of the per-block word sums,
 //                and the total of the per-block bit sums.
 //   pack_kernel  per tile: each lane's payload length from byte sums, an
 //                exclusive scan over the tile's lanes gives its first bit;
-//                the lane then streams its 16 codes through a 64-bit window
-//                and ORs whole words into an LDS copy of the tile, which is
-//                stored at the tile's word offset.  Tiles are word aligned,
-//                so no two tiles share a word.
+//                the lane then writes its 16 codes into the wave's LDS copy
+//                of the tile with OR operations, and the tile's lanes store
+//                its words at the tile's word offset.  Tiles are word
+//                aligned, so no two tiles share a word.  Only wave-level
+//                synchronisation: waves never wait for each other.
 #include "hq.h"
 #include "hq_device.h"
 #include "hq_internal.h"
@@ -114,41 +117,59 @@ __device__ inline uint32_t best_k(const uint32_t* zz, int& bk) {
   return best;
 }
 
-// Block b covers the contiguous tiles [b * span, (b + 1) * span), span a
-// multiple of the TPB tiles one pass of the block handles; the pack kernel
-// uses the same partition.  Few blocks keep the total's atomics few.
+// Waves of the rate and pack grids, and the tiles each covers: wave w owns
+// [w span, (w + 1) span), span a multiple of the TPW = 64 / G tiles one pass
+// of a wave handles.
+constexpr int64_t kMaxRateWaves = 8192;
+
 template <int N>
-__device__ inline int64_t block_span(int64_t n_tiles) {
-  constexpr int TPB = kBlock / (N / kElemsPerLane);
-  const int64_t passes = (n_tiles + TPB - 1) / TPB;
-  const int64_t per_block = (passes + gridDim.x - 1) / gridDim.x;
-  return per_block * TPB;
+__host__ __device__ inline int64_t rate_waves(int64_t n_tiles) {
+  constexpr int TPW = 64 / (N / kElemsPerLane);
+  const int64_t passes = (n_tiles + TPW - 1) / TPW;
+  return passes < kMaxRateWaves ? passes : kMaxRateWaves;
+}
+
+template <int N>
+__device__ inline int64_t wave_span(int64_t n_tiles) {
+  constexpr int TPW = 64 / (N / kElemsPerLane);
+  const int64_t passes = (n_tiles + TPW - 1) / TPW;
+  const int64_t waves = rate_waves<N>(n_tiles);
+  return (passes + waves - 1) / waves * TPW;
+}
+
+__device__ inline uint64_t wave_sum_u64(uint64_t x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m);
+  return x;
 }
 
 template <int N>
 __global__ __launch_bounds__(kBlock) void rate_kernel(RateLaunch a) {
   constexpr int G = N / kElemsPerLane;
-  constexpr int TPB = kBlock / G;
-  __shared__ uint64_t blk_words[kBlock / 64];
-  __shared__ uint64_t blk_bits[kBlock / 64];
-  const int r = threadIdx.x % G;
-  const int64_t span = block_span<N>(a.n_tiles);
-  const int64_t first = (int64_t)blockIdx.x * span;
+  constexpr int TPW = 64 / G;
+  __shared__ uint64_t blk[2][kBlock / 64];
+  const int lane = threadIdx.x & 63;
+  const int r = lane % G;
+  const int wl = threadIdx.x >> 6;
+  const int64_t wave = (int64_t)blockIdx.x * (kBlock / 64) + wl;
+  // waves past the last one have an empty span (the block still syncs)
+  const int64_t span = wave_span<N>(a.n_tiles);
+  const int64_t first = wave < rate_waves<N>(a.n_tiles) ? wave * span : a.n_tiles;
   const int64_t end = first + span < a.n_tiles ? first + span : a.n_tiles;
   uint64_t words = 0, bits = 0;
   // the next pass's indices are loaded while this pass is computed
   auto fetch = [&](int64_t t0) {
-    const int64_t tile = t0 + threadIdx.x / G;
+    const int64_t tile = t0 + lane / G;
     const int64_t tl = tile < end ? tile : end - 1;   // whole groups stay convergent
     return load16(a.idx, tl * N + (int64_t)r * kElemsPerLane);
   };
   uint4 nxt = first < end ? fetch(first) : make_uint4(0, 0, 0, 0);
-  for (int64_t t0 = first; t0 < end; t0 += TPB) {
-    const int64_t tile = t0 + threadIdx.x / G;
+  for (int64_t t0 = first; t0 < end; t0 += TPW) {
+    const int64_t tile = t0 + lane / G;
     const bool live = tile < end;
     uint32_t zz[4];
     zeta4(nxt, zz);
-    if (t0 + TPB < end) nxt = fetch(t0 + TPB);
+    if (t0 + TPW < end) nxt = fetch(t0 + TPW);
     int bk;
     const uint32_t pay = best_k<G, N>(zz, bk);
     const uint32_t tb = 4u + (uint32_t)a.coset_bits + pay;
@@ -159,20 +180,21 @@ __global__ __launch_bounds__(kBlock) void rate_kernel(RateLaunch a) {
       bits += tb;
     }
   }
-  // block sums (lane 0 of each group contributes)
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    words += __shfl_xor(words, m);
-    bits += __shfl_xor(bits, m);
-  }
-  if ((threadIdx.x & 63) == 0) {
-    blk_words[threadIdx.x >> 6] = words;
-    blk_bits[threadIdx.x >> 6] = bits;
+  words = wave_sum_u64(words);
+  bits = wave_sum_u64(bits);
+  if (lane == 0) {
+    if (a.wave_words != nullptr) a.wave_words[wave] = words;
+    blk[0][wl] = words;
+    blk[1][wl] = bits;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
     uint64_t w = 0, b = 0;
-    for (int i = 0; i < kBlock / 64; ++i) { w += blk_words[i]; b += blk_bits[i]; }
+#pragma unroll
+    for (int i = 0; i < kBlock / 64; ++i) {
+      w += blk[0][i];
+      b += blk[1][i];
+    }
     if (a.block_words != nullptr) {
       a.block_words[blockIdx.x] = w;
       a.block_bits[blockIdx.x] = b;
@@ -184,47 +206,54 @@ __global__ __launch_bounds__(kBlock) void rate_kernel(RateLaunch a) {
 
 __global__ void zero_u64_kernel(uint64_t* p) { *p = 0; }
 
-// Exclusive scan of n values in place, one block: each thread scans a
-// contiguous chunk, the chunk totals are scanned in LDS.
+// Exclusive scan of the n <= kMaxRateWaves / 4 per-block word sums in place,
+// and the total of the per-block bit sums; one block, kScanPer consecutive values
+// per thread (all loads issued at once), wave scans by shuffles and a scan of
+// the wave totals in LDS.
 constexpr int kScanThreads = 1024;
+constexpr int kScanPer = 2;
+static_assert(kScanThreads * kScanPer >= kMaxRateWaves / (kBlock / 64), "scan covers every rate block");
 
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(uint64_t* v, int64_t n,
                                                             const uint64_t* bits,
                                                             uint64_t* total_bits) {
-  __shared__ uint64_t part[kScanThreads];
-  __shared__ uint64_t bsum[kScanThreads / 64];
-  const int t = threadIdx.x;
-  const int64_t chunk = (n + kScanThreads - 1) / kScanThreads;
-  const int64_t lo = t * chunk;
-  const int64_t hi = (lo + chunk < n) ? lo + chunk : n;
+  __shared__ uint64_t wtot[kScanThreads / 64];
+  __shared__ uint64_t btot[kScanThreads / 64];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  uint64_t x[kScanPer];
   uint64_t s = 0, sb = 0;
-  for (int64_t i = lo; i < hi; ++i) {
-    s += v[i];
-    sb += bits[i];
+#pragma unroll
+  for (int i = 0; i < kScanPer; ++i) {
+    const int64_t j = (int64_t)t * kScanPer + i;
+    x[i] = j < n ? v[j] : 0;
+    sb += j < n ? bits[j] : 0;
+    s += x[i];
   }
-  part[t] = s;
-  // the bit total (integer sums: the order does not matter)
+  // inclusive scan over the wave, then over the wave totals
+  uint64_t inc = s;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint64_t y = __shfl_up(inc, d);
+    inc += lane >= d ? y : 0;
+  }
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) sb += __shfl_xor(sb, m);
-  if ((t & 63) == 0) bsum[t >> 6] = sb;
+  if (lane == 63) wtot[w] = inc;
+  if (lane == 0) btot[w] = sb;
   __syncthreads();
-  if (t == 0) {
-    uint64_t tot = 0;
-    for (int i = 0; i < kScanThreads / 64; ++i) tot += bsum[i];
-    *total_bits = tot;
+  uint64_t before = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < kScanThreads / 64; ++i) {
+    before += i < w ? wtot[i] : 0;
+    total += btot[i];
   }
-  // Hillis-Steele inclusive scan of the chunk totals
-  for (int d = 1; d < kScanThreads; d <<= 1) {
-    const uint64_t add = t >= d ? part[t - d] : 0;
-    __syncthreads();
-    part[t] += add;
-    __syncthreads();
-  }
-  uint64_t run = part[t] - s;
-  for (int64_t i = lo; i < hi; ++i) {
-    const uint64_t x = v[i];
-    v[i] = run;
-    run += x;
+  if (t == 0) *total_bits = total;
+  uint64_t run = before + inc - s;
+#pragma unroll
+  for (int i = 0; i < kScanPer; ++i) {
+    const int64_t j = (int64_t)t * kScanPer + i;
+    if (j < n) v[j] = run;
+    run += x[i];
   }
 }
 
@@ -263,45 +292,67 @@ struct BitWriter {
   }
 };
 
+// LDS words of one wave: its TPW tiles of at most W words each, plus a spare
+// word past the last tile (the two-word OR of a code may touch it).
+template <int N>
+constexpr int pack_lds_words() {
+  return 64 / (N / kElemsPerLane) * PackBound<N>::kWords + 1;
+}
+
 template <int N>
 __global__ __launch_bounds__(kBlock) void pack_kernel(RateLaunch a) {
   constexpr int G = N / kElemsPerLane;
-  constexpr int TPB = kBlock / G;
+  constexpr int TPW = 64 / G;
   constexpr int W = PackBound<N>::kWords;
-  __shared__ uint32_t buf[TPB * W + 1];   // one spare word past the last tile
-  __shared__ uint32_t nw[TPB];
-  const int r = threadIdx.x % G;
-  const int slot = threadIdx.x / G;
-  const int64_t span = block_span<N>(a.n_tiles);
-  const int64_t first = (int64_t)blockIdx.x * span;
+  __shared__ uint32_t lds[kBlock / 64][pack_lds_words<N>()];
+  const int lane = threadIdx.x & 63;
+  const int r = lane % G;
+  const int slot = lane / G;
+  const int64_t wave = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+  if (wave >= rate_waves<N>(a.n_tiles)) return;   // whole waves only
+  uint32_t* buf = lds[threadIdx.x >> 6];
+  const int64_t span = wave_span<N>(a.n_tiles);
+  const int64_t first = wave * span;
   const int64_t end = first + span < a.n_tiles ? first + span : a.n_tiles;
-  uint64_t base = a.block_words[blockIdx.x];   // first word of this pass's tiles
-  // the next pass's indices, k and bit count are loaded during this pass
-  uint4 nq = make_uint4(0, 0, 0, 0);
-  uint32_t nk = 0, ntb = 0;
-  auto fetch = [&](int64_t t0) {
-    const int64_t tile = t0 + slot;
-    if (tile < end) {
-      nq = load16(a.idx, tile * N + (int64_t)r * kElemsPerLane);
-      nk = a.rice_k[tile];
-      ntb = a.tile_bits[tile];
+  // first word of this pass's tiles: the block's offset, then the words of
+  // the block's earlier waves
+  uint64_t base = a.block_words[blockIdx.x];
+  for (int i = 0; i < (threadIdx.x >> 6); ++i) base += a.wave_words[(int64_t)blockIdx.x * (kBlock / 64) + i];
+  struct PassIn {
+    uint4 q;
+    uint32_t k, tb;
+  };
+  auto fetch = [&](int64_t t0, PassIn& in) {
+    if (t0 < end) {   // wave-uniform
+      const int64_t tile = t0 + slot;
+      if (tile < end) {
+        in.q = load16(a.idx, tile * N + (int64_t)r * kElemsPerLane);
+        in.k = a.rice_k[tile];
+        in.tb = a.tile_bits[tile];
+      }
     }
   };
-  if (first < end) fetch(first);
-  for (int64_t t0 = first; t0 < end; t0 += TPB) {
+  auto pass = [&](const PassIn& in, int64_t t0) {
+    if (t0 >= end) return;   // wave-uniform
     const int64_t tile = t0 + slot;
     const bool live = tile < end;
-    const uint4 cq = nq;
-    const uint32_t ck = nk, tb = live ? ntb : 0u;
-    if (t0 + TPB < end) fetch(t0 + TPB);
-    for (int i = threadIdx.x; i < TPB * W; i += kBlock) buf[i] = 0;
+    const uint4 cq = in.q;
+    const uint32_t ck = in.k, tb = live ? in.tb : 0u;
     const uint32_t nwords = (tb + 31u) / 32u;
-    if (r == 0) nw[slot] = nwords;
-    __syncthreads();
-    uint64_t off = base;
-    for (int s = 0; s < slot; ++s) off += nw[s];
-    uint32_t pass_words = 0;
-    for (int s = 0; s < TPB; ++s) pass_words += nw[s];
+    // word offsets of the pass's tiles: group g's count sits in lane g G
+    uint64_t off = base, pass_words = 0;
+#pragma unroll
+    for (int g = 0; g < TPW; ++g) {
+      const uint32_t ng = (uint32_t)__builtin_amdgcn_readlane((int)nwords, g * G);
+      off += g < slot ? ng : 0u;
+      pass_words += ng;
+    }
+    uint32_t* tw = buf + slot * W;
+    for (uint32_t j = r; j < nwords; j += G) tw[j] = 0u;
+    if (slot == TPW - 1 && r == 0) buf[TPW * W] = 0u;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // every lane runs the scan (DPP moves read neighbouring lanes)
     uint32_t k = 0;
     uint32_t zz[4] = {0u, 0u, 0u, 0u};
@@ -317,7 +368,6 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(RateLaunch a) {
     const uint32_t T = live ? qs + 16u * (1u + k) : 0u;
     const uint32_t pos = 4u + (uint32_t)a.coset_bits + row_incl_scan<G>(T, r) - T;
     if (live) {
-      uint32_t* tw = buf + slot * W;
       if (r == 0) {
         // header: k (4 bits), then the coset bits
         BitWriter h{tw, (uint64_t)k, 4u, 0u};
@@ -355,34 +405,38 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(RateLaunch a) {
         pb += len;
       }
     }
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (live) {
       if (r == 0) a.tile_word_offset[tile] = off;
       if (tile == a.n_tiles - 1 && r == 0) a.tile_word_offset[a.n_tiles] = off + nwords;
       if (off + nwords <= a.capacity) {
-        const uint32_t* tw = buf + slot * W;
         for (uint32_t j = r; j < nwords; j += G) a.stream[off + j] = tw[j];
       } else if (r == 0) {
         set_status(a.status, HQ_ST_STREAM_FULL);
       }
     }
     base += pass_words;
-    __syncthreads();   // the buffer and nw are reused by the next pass
+    // the LDS words are rewritten by the next pass
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  // the next pass's data are loaded while this pass is computed
+  PassIn nxt;
+  fetch(first, nxt);
+  for (int64_t t0 = first; t0 < end; t0 += TPW) {
+    const PassIn cur = nxt;
+    fetch(t0 + TPW, nxt);
+    pass(cur, t0);
   }
-}
-
-constexpr int64_t kMaxRateBlocks = 2048;
-
-template <int N>
-int64_t n_blocks(int64_t n_tiles) {
-  constexpr int TPB = kBlock / (N / kElemsPerLane);
-  const int64_t passes = (n_tiles + TPB - 1) / TPB;
-  return passes < kMaxRateBlocks ? passes : kMaxRateBlocks;
 }
 
 template <int N>
 hipError_t launch_n(const RateLaunch& a, hipStream_t s) {
-  const int64_t blocks = n_blocks<N>(a.n_tiles);
+  const int64_t waves = rate_waves<N>(a.n_tiles);
+  const int64_t blocks = (waves + kBlock / 64 - 1) / (kBlock / 64);
   if (a.block_words == nullptr)
     hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(1), 0, s, a.total_bits);
   hipLaunchKernelGGL(rate_kernel<N>, dim3((unsigned)blocks), dim3(kBlock), 0, s, a);
@@ -400,9 +454,11 @@ hipError_t launch_rate(const RateLaunch& a, hipStream_t s) {
   return a.tile == 256 ? launch_n<256>(a, s) : launch_n<128>(a, s);
 }
 
-int64_t rate_blocks(int64_t n_tiles, int tile) {
-  const int TPB = kBlock / (tile / kElemsPerLane);
-  return (n_tiles + TPB - 1) / TPB;
+int64_t rate_workspace_blocks(int64_t n_tiles) {
+  // at most one wave per 4 tiles (tile 256), capped, in blocks of 4 waves
+  int64_t w = (n_tiles + 3) / 4;
+  if (w > kMaxRateWaves) w = kMaxRateWaves;
+  return (w + kBlock / 64 - 1) / (kBlock / 64);
 }
 
 }  // namespace hq

@@ -62,7 +62,7 @@ def test_coset_words_and_workspace():
         for n in (128, 256):
             assert hq.coset_words(lat, n) == codec.coset_words_per_tile(lat, n)
     assert hq.rate_workspace_bytes(0) == 0
-    assert hq.rate_workspace_bytes(17) == 32    # word and bit sums of two 16-tile blocks
+    assert hq.rate_workspace_bytes(17) == 96    # two blocks: word and bit sums, four wave sums each
     bad = hq.make_params("E8", 64)
     assert hq.lib().hq_coset_words(ctypes.byref(bad)) == -1
 
