@@ -88,7 +88,8 @@ enum {
 typedef struct {
   uint32_t struct_size;   /* must equal sizeof(hq_params)                   */
   int32_t lattice;        /* hq_lattice                                     */
-  int32_t tile;           /* n: 256 (E8) or 128 (E8, D4, A2, Z)             */
+  int32_t tile;           /* n: 64, 128, 256 or 512, any lattice (at most  
+                             256 with HQ_DITHER, else HQ_EUNSUPPORTED)     */
   float bps;              /* target rate R in bits per scalar, 0 < R <= 8   */
   uint32_t rht_seed;      /* seed of the RHT sign vector                    */
   uint32_t dither_seed;   /* HQ_DITHER only; must be < 2^24                 */

@@ -30,11 +30,12 @@ bool lattice_ok(int32_t l) { return l == HQ_E8 || l == HQ_D4 || l == HQ_A2 || l 
 hq_status check_params(const hq_params* p) {
   if (p == nullptr || p->struct_size != sizeof(hq_params)) return HQ_EINVAL;
   if (!lattice_ok(p->lattice)) return HQ_EINVAL;
-  if (p->tile != 128 && p->tile != 256) return HQ_EINVAL;
+  if (p->tile != 64 && p->tile != 128 && p->tile != 256 && p->tile != kMaxTile) return HQ_EINVAL;
   if (!(p->bps > 0.0f) || !(p->bps <= 8.0f)) return HQ_EINVAL;
   if ((p->flags & ~kKnownFlags) != 0 || p->reserved != 0) return HQ_EINVAL;
   if (p->flags & HQ_DITHER) {
     if (p->lattice != HQ_E8) return HQ_EUNSUPPORTED;
+    if (p->tile > 256) return HQ_EUNSUPPORTED;   // the dither key holds coordinates < 256
     if (p->dither_seed >= (1u << 24)) return HQ_EINVAL;
     if (p->dither_base < 0) return HQ_EINVAL;
   }
@@ -73,8 +74,9 @@ int32_t coset_bits(const hq_params* p) {
 
 bool aligned16(const void* q) { return ((uintptr_t)q & 15u) == 0; }
 
+// out: (n + 31) / 32 words
 void make_signs(uint32_t seed, int n, uint32_t* out) {
-  for (int w = 0; w < 8; ++w) out[w] = 0;
+  for (int w = 0; w < (n + 31) / 32; ++w) out[w] = 0;
   for (int j = 0; j < n; ++j) {
     const uint64_t h = splitmix64(((uint64_t)seed << 32) ^ (uint64_t)j);
     if (h >> 63) out[j >> 5] |= 1u << (j & 31);

@@ -45,7 +45,7 @@ __device__ inline uint32_t lane_sign_mask(const DecodeLaunch& a, int r) {
   const int w = r >> 1;
   uint32_t s = a.signs[0];
 #pragma unroll
-  for (int k = 1; k < 8; ++k) s = (w == k) ? a.signs[k] : s;
+  for (int k = 1; k < kMaxTile / 32; ++k) s = (w == k) ? a.signs[k] : s;
   return (s >> (16 * (r & 1))) & 0xFFFFu;
 }
 
@@ -190,7 +190,12 @@ hipError_t launch_lat_n(const DecodeLaunch& a, hipStream_t s) {
 
 template <int LAT>
 hipError_t launch_lat(const DecodeLaunch& a, hipStream_t s) {
-  return a.tile == 256 ? launch_lat_n<LAT, 256>(a, s) : launch_lat_n<LAT, 128>(a, s);
+  switch (a.tile) {
+    case 64: return launch_lat_n<LAT, 64>(a, s);
+    case 128: return launch_lat_n<LAT, 128>(a, s);
+    case 256: return launch_lat_n<LAT, 256>(a, s);
+    default: return launch_lat_n<LAT, 512>(a, s);
+  }
 }
 
 }  // namespace

@@ -9,6 +9,8 @@ namespace hq {
 constexpr int kBlock = 256;         // threads per block, every kernel
 constexpr int kElemsPerLane = 16;   // tile elements held by one lane
 
+constexpr int kMaxTile = 512;       // largest tile (elements)
+
 struct EncodeLaunch {
   const void* x;
   int in_bf16;
@@ -23,7 +25,7 @@ struct EncodeLaunch {
   uint32_t* tile_bits;
   int16_t* coords;      // nullptr unless requested
   uint32_t* status;     // may be nullptr
-  uint32_t signs[8];    // bit j set: sign of element j is -1
+  uint32_t signs[kMaxTile / 32];   // bit j set: sign of element j is -1
   double c;             // auto-scale constant c(L, R)
   double sqrt_n;        // fp64 sqrt(tile)
   int dither;
@@ -41,7 +43,7 @@ struct DecodeLaunch {
   void* y;
   int out_bf16;
   uint32_t* status;
-  uint32_t signs[8];
+  uint32_t signs[kMaxTile / 32];
   double inv_sqrt_n;    // fp64 1/sqrt(tile)
   int dither;
   uint32_t dither_seed;

@@ -31,8 +31,9 @@
 namespace hq {
 namespace {
 
-// The G lanes of a tile (G = 8 or 16) lie in one 16-lane DPP row, so sums
-// and scans over them use DPP moves (VALU, no LDS round trip).
+// The G lanes of a tile (G = 4, 8, 16 or 32) are aligned lane groups: for
+// G <= 16 within one 16-lane DPP row, for G = 32 two neighbouring rows, so
+// sums and scans over them use DPP moves (VALU, no LDS round trip).
 template <int CTRL>
 __device__ inline uint32_t dpp(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
@@ -42,8 +43,9 @@ template <int G>
 __device__ inline uint32_t row_sum(uint32_t x) {
   x += dpp<0xB1>(x);                    // quad_perm [1,0,3,2]
   x += dpp<0x4E>(x);                    // quad_perm [2,3,0,1]
-  x += dpp<0x141>(x);                   // row_half_mirror: the other quad of the half row
-  if (G == 16) x += dpp<0x140>(x);      // row_mirror: the other half row
+  if (G >= 8) x += dpp<0x141>(x);       // row_half_mirror: the other quad of the half row
+  if (G >= 16) x += dpp<0x140>(x);      // row_mirror: the other half row
+  if (G == 32) x += __shfl_xor(x, 16);  // the other row of the pair
   return x;
 }
 
@@ -54,11 +56,17 @@ __device__ inline uint32_t row_incl_scan(uint32_t x, int r) {
   x += r >= 1 ? v : 0u;
   v = dpp<0x112>(x);                    // row_shr:2
   x += r >= 2 ? v : 0u;
-  v = dpp<0x114>(x);                    // row_shr:4
-  x += r >= 4 ? v : 0u;
-  if (G == 16) {
+  if (G >= 8) {
+    v = dpp<0x114>(x);                  // row_shr:4
+    x += r >= 4 ? v : 0u;
+  }
+  if (G >= 16) {
     v = dpp<0x118>(x);                  // row_shr:8
     x += r >= 8 ? v : 0u;
+  }
+  if (G == 32) {
+    v = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);   // row_bcast:15
+    x += r >= 16 ? v : 0u;
   }
   return x;
 }
@@ -451,12 +459,17 @@ hipError_t launch_n(const RateLaunch& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_rate(const RateLaunch& a, hipStream_t s) {
-  return a.tile == 256 ? launch_n<256>(a, s) : launch_n<128>(a, s);
+  switch (a.tile) {
+    case 64: return launch_n<64>(a, s);
+    case 128: return launch_n<128>(a, s);
+    case 256: return launch_n<256>(a, s);
+    default: return launch_n<512>(a, s);
+  }
 }
 
 int64_t rate_workspace_blocks(int64_t n_tiles) {
-  // at most one wave per 4 tiles (tile 256), capped, in blocks of 4 waves
-  int64_t w = (n_tiles + 3) / 4;
+  // at most one wave per 2 tiles (tile 512), capped, in blocks of 4 waves
+  int64_t w = (n_tiles + 1) / 2;
   if (w > kMaxRateWaves) w = kMaxRateWaves;
   return (w + kBlock / 64 - 1) / (kBlock / 64);
 }

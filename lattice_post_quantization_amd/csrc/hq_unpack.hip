@@ -336,10 +336,19 @@ __global__ __launch_bounds__(kUnpackBlock) void unpack_kernel(UnpackLaunch a) {
 
 hipError_t launch_unpack(const UnpackLaunch& a, hipStream_t s) {
   const int64_t blocks = (a.n_tiles + kUnpackBlock - 1) / kUnpackBlock;
-  if (a.tile == 256)
-    hipLaunchKernelGGL(unpack_kernel<256>, dim3((unsigned)blocks), dim3(kUnpackBlock), 0, s, a);
-  else
-    hipLaunchKernelGGL(unpack_kernel<128>, dim3((unsigned)blocks), dim3(kUnpackBlock), 0, s, a);
+  switch (a.tile) {
+    case 64:
+      hipLaunchKernelGGL(unpack_kernel<64>, dim3((unsigned)blocks), dim3(kUnpackBlock), 0, s, a);
+      break;
+    case 128:
+      hipLaunchKernelGGL(unpack_kernel<128>, dim3((unsigned)blocks), dim3(kUnpackBlock), 0, s, a);
+      break;
+    case 256:
+      hipLaunchKernelGGL(unpack_kernel<256>, dim3((unsigned)blocks), dim3(kUnpackBlock), 0, s, a);
+      break;
+    default:
+      hipLaunchKernelGGL(unpack_kernel<512>, dim3((unsigned)blocks), dim3(kUnpackBlock), 0, s, a);
+  }
   return hipGetLastError();
 }
 

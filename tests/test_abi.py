@@ -59,12 +59,15 @@ def test_coset_words_and_workspace():
     assert hq.coset_words("A2", 128) == 2 and hq.coset_words("A2", 256) == 4
     assert hq.coset_words("D4", 128) == 0 and hq.coset_words("Z", 256) == 0
     for lat in ("E8", "D4", "A2", "Z"):
-        for n in (128, 256):
+        for n in (64, 128, 256, 512):
             assert hq.coset_words(lat, n) == codec.coset_words_per_tile(lat, n)
     assert hq.rate_workspace_bytes(0) == 0
-    assert hq.rate_workspace_bytes(17) == 96    # two blocks: word and bit sums, four wave sums each
-    bad = hq.make_params("E8", 64)
-    assert hq.lib().hq_coset_words(ctypes.byref(bad)) == -1
+    # up to one wave per two tiles: 9 waves, 3 blocks of word and bit sums
+    # and four wave sums each
+    assert hq.rate_workspace_bytes(17) == 144
+    for n in (32, 96, 1024):
+        bad = hq.make_params("E8", n)
+        assert hq.lib().hq_coset_words(ctypes.byref(bad)) == -1
 
 
 def test_status_strings():
@@ -83,7 +86,10 @@ def test_encode_validation_codes():
     auto = hq.HQ_SCALE_AUTO
     assert _enc(P("E8", 256, 4.0, 0, auto), cols=100) == hq.HQ_EINVAL          # cols % tile
     assert _enc(P("E8", 256, 4.0, 0, auto), rows=-1) == hq.HQ_EINVAL
-    assert _enc(P("E8", 64, 4.0, 0, auto)) == hq.HQ_EINVAL                     # tile
+    for n in (32, 96, 1024):
+        assert _enc(P("E8", n, 4.0, 0, auto)) == hq.HQ_EINVAL                  # tile
+    # the dither key holds coordinates below 256
+    assert _enc(P("E8", 512, 4.0, 0, auto | hq.HQ_DITHER, 1), cols=512) == hq.HQ_EUNSUPPORTED
     assert _enc(P(3, 256, 4.0, 0, auto)) == hq.HQ_EINVAL                       # lattice
     for b in (0.0, -1.0, 9.0, float("nan")):
         assert _enc(P("E8", 256, b, 0, auto)) == hq.HQ_EINVAL                  # bps

@@ -127,8 +127,8 @@ def test_small_fp32_e8_full_parity():
                       "small_fp32 explicit")
 
 
-@pytest.mark.parametrize("lattice,n", [("E8", 256), ("E8", 128), ("D4", 128), ("D4", 256),
-                                       ("A2", 128), ("A2", 256), ("Z", 128), ("Z", 256)])
+@pytest.mark.parametrize("lattice,n", [(lat, n) for lat in ("E8", "D4", "A2", "Z")
+                                       for n in (64, 128, 256, 512)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_lattices_tile_sizes_ragged(lattice, n, dtype):
     """Every lattice x tile size on a small bf16 / fp32 matrix whose tile
@@ -400,7 +400,8 @@ def _check_unpacked(g, idx, coset_rows, k, lattice, n, label):
 
 
 @pytest.mark.parametrize("lattice,n", [("E8", 256), ("E8", 128), ("D4", 128), ("A2", 128),
-                                       ("A2", 256), ("Z", 256)])
+                                       ("A2", 256), ("Z", 256), ("E8", 64), ("E8", 512),
+                                       ("A2", 512), ("D4", 64)])
 def test_unpack_parity(lattice, n):
     """hq_unpack of the oracle's packed stream gives the oracle's indices,
     coset bits and k (oracle unpack of the same words), on a ragged tile
@@ -617,6 +618,27 @@ def test_kv_low_rate_parity(bps):
     assert np.array_equal(T.host(g["rice_k"])[ok].astype(np.int64), ora["rice_k"][ok])
     assert np.array_equal(T.u32(g["tile_bits"])[ok].astype(np.int64), ora["tile_bits"][ok])
     check_decode(ora, "E8", 128, 1, "kv %g bps" % bps, exact=True, dither_seed=9, dither_base=77)
+
+
+def test_kv_head_dim_64_dither_parity():
+    """Dithered E8 encode and decode of 300 KV vectors of 64 (tile 64,
+    generic kernels) against the oracle, every vector."""
+    rng = np.random.default_rng(83)
+    x = rng.standard_normal((300, 64))
+    x[:, 3] += 2.0
+    bits = workloads.f32_to_bf16_bits(x.astype(np.float32))
+    xh = workloads.bf16_bits_to_f64(bits)
+    say("case: kv head dim 64, dither")
+    g = hq.hq_kv_encode(T.bf16_device(bits, (300, 64)), 4.0, 2, dither_seed=5, dither_base=40)
+    torch.cuda.synchronize()
+    ora = codec.encode(xh, "E8", 64, 4.0, rht_seed=2, dither_seed=5, dither_base=40)
+    skip = midpoint_close(oracle_pre_scale(xh, "E8", 4.0))
+    assert not skip.any()
+    assert np.array_equal(T.host(g["scale"]).astype(np.float64), ora["scale"])
+    _, _, _, ok = T.compare_indices(T.host(g["idx"]), T.u32(g["coset"]), ora, "E8", 64, "kv 64")
+    assert np.array_equal(T.host(g["rice_k"])[ok].astype(np.int64), ora["rice_k"][ok])
+    assert np.array_equal(T.u32(g["tile_bits"])[ok].astype(np.int64), ora["tile_bits"][ok])
+    check_decode(ora, "E8", 64, 2, "kv 64", exact=True, dither_seed=5, dither_base=40)
 
 
 def test_e8_128_groups_edges():
