@@ -33,6 +33,18 @@ R5 Decode: x = s * ((H (Delta p)) * (1/sqrt(n))); output fp32 by rounding the
 R6 KV dither (E8 only): per vector v, w = the dither box sample, d = w - Q(w)
    per 8-block (uniform over the Voronoi cell); encode Q(u + d); decode
    Delta (p - d).
+R7 Per-tile rate control (a variant the pages list as a direction only):
+   instead of the fixed constant, each tile's scale is searched over bf16
+   values so that the tile fits a budget of floor(R n) bits (k field, coset
+   bits and Rice payload; the 16-bit scale is itemized apart).  A scale is
+   feasible when its indices fit int8 and tile_bits <= the budget.  The
+   search runs over the bf16 bit patterns (ordered like the values) from
+   the automatic scale's pattern a: lo = max(a - 1024, 0x0080),
+   hi = min(a + 1024, 0x7F7F) (eight binades each way, normal values only).
+   If hi is infeasible the tile takes hi; otherwise bisection with
+   mid = floor((lo + hi) / 2), keeping hi feasible, until hi - lo = 1, and
+   the tile takes hi.  All-zero and non-finite tiles keep the automatic
+   scale.
 """
 
 import math
@@ -228,12 +240,51 @@ def dither(dither_seed, dither_base, n_vectors, n):
 
 # ------------------------------------------------------------------ encode
 
+RC_SPAN = 1024        # bf16 patterns searched on each side of the automatic scale
+BF16_LOWEST_NORMAL_BITS, BF16_HIGHEST_BITS = 0x0080, 0x7F7F
+
+
+def rate_controlled_scale(X, S, lattice, bps):
+    """Reading R7: per-tile scales by bisection on bf16 patterns so that each
+    tile fits floor(R n) bits.  X: the tiles (T, n); S = H (s x), unnormalized."""
+    T, n = X.shape
+    base = auto_scale(X, lattice, bps)
+    budget = math.floor(bps * n)
+    cb = coset_bits_per_tile(lattice, n)
+    active = np.all(np.isfinite(X), axis=1) & (np.sum(X * X, axis=1) > 0.0)
+    a = bf16_bits(np.where(active, base, 1.0)).astype(np.int64)
+    lo = np.maximum(a - RC_SPAN, BF16_LOWEST_NORMAL_BITS)
+    hi = np.minimum(a + RC_SPAN, BF16_HIGHEST_BITS)
+    Sa = np.where(active[:, None], S, 0.0)   # inactive tiles: results unused
+
+    def feasible(codes):
+        delta = bf16_from_bits(codes.astype(np.uint16))
+        u = quantizer_input(Sa, delta, lattice)
+        z, c, _ = nearest(u, lattice)
+        idx = strip(z, c, lattice)
+        fits = ~np.any((idx < INT8_MIN) | (idx > INT8_MAX), axis=1)
+        _, tb = rice.tile_bits(np.clip(idx, INT8_MIN, INT8_MAX), cb)
+        return fits & (tb <= budget)
+
+    run = active & feasible(hi)
+    while True:
+        run = run & (hi - lo > 1)
+        if not run.any():
+            break
+        mid = (lo + hi) // 2
+        f = feasible(mid)
+        hi = np.where(run & f, mid, hi)
+        lo = np.where(run & ~f, mid, lo)
+    return np.where(active, bf16_from_bits(hi.astype(np.uint16)), base)
+
+
 def encode(x, lattice="E8", n=256, bps=4.0, rht_seed=0, scale=None,
-           dither_seed=None, dither_base=0):
+           dither_seed=None, dither_base=0, rate_control=False):
     """Encode a row-major matrix (or (V, n) KV vectors) tile by tile.
 
     scale: None for auto mode (reading R2) or explicit per-tile Delta values.
     dither_seed: None, or the KV dither seed (E8 only, reading R6).
+    rate_control: per-tile scales by reading R7 (scale must be None; no dither).
     Returns a dict of numpy arrays: scale (float64), idx (int64 (T, n)),
     coset (uint32 (T, words)), rice_k, tile_bits, coords, margin
     (T, blocks), overflow (bool (T,)), u (the quantizer input), S.
@@ -244,7 +295,12 @@ def encode(x, lattice="E8", n=256, bps=4.0, rht_seed=0, scale=None,
     T = X.shape[0]
     signs = splitmix.rht_signs(rht_seed, n)
     S = hadamard.unnormalized_forward(X, signs)
-    delta = auto_scale(X, lattice, bps) if scale is None else np.asarray(scale, np.float64)
+    if rate_control:
+        if scale is not None or dither_seed is not None:
+            raise ValueError("rate control chooses the scales itself, without a dither")
+        delta = rate_controlled_scale(X, S, lattice, bps)
+    else:
+        delta = auto_scale(X, lattice, bps) if scale is None else np.asarray(scale, np.float64)
     u = quantizer_input(S, delta, lattice)
     if dither_seed is not None:
         if lattice != "E8":
