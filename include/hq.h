@@ -73,7 +73,10 @@ typedef enum { HQ_F32 = 0, HQ_BF16 = 1 } hq_dtype;
 enum {
   HQ_SCALE_AUTO = 1u,   /* encode computes the scales (else reads them)    */
   HQ_DITHER = 2u,       /* subtractive dither (E8 only; KV encode/decode)  */
-  HQ_WANT_COORDS = 4u   /* encode also writes full lattice coordinates     */
+  HQ_WANT_COORDS = 4u,  /* encode also writes full lattice coordinates     */
+  HQ_RATE_CONTROL = 8u  /* encode: per-tile scales by bisection so that each
+                           tile fits floor(bps * tile) bits (see below);
+                           requires HQ_SCALE_AUTO; not with HQ_DITHER       */
 };
 
 /* Device status bits (OR-ed into *status by kernels). */
@@ -115,6 +118,15 @@ typedef struct {
  *   coset  = one bit per E8 block / A2 pair, block j at bit j (LSB first)
  *   rice_k = argmin_k sum(floor(zeta/2^k) + 1 + k), zeta = zigzag(idx)
  *   tile_bits = 4 + coset bits + that minimum
+ * With HQ_RATE_CONTROL (per-tile rate control, a variant the pages name as
+ * a direction only): Delta is searched over bf16 bit patterns within eight
+ * binades of the automatic one (patterns a -/+ 1024, kept among normal
+ * values) for the finest scale whose indices fit int8 and whose tile_bits
+ * <= floor(bps * n): the top of the window is probed first (if it does not
+ * fit, the tile takes it), then bisection with mid = floor((lo + hi) / 2)
+ * keeping the top feasible.  All-zero and non-finite tiles keep the
+ * automatic scale.  Generic kernels only (about a dozen candidate encodes per
+ * tile); no HQ_ERANGE check, since the search keeps the indices in range.
  *
  * x       [rows*cols] of x_dtype (bf16 or fp32)
  * scale   [n_tiles] fp32: output with HQ_SCALE_AUTO, input otherwise

@@ -22,7 +22,7 @@ namespace {
 
 using namespace hq;
 
-constexpr uint32_t kKnownFlags = HQ_SCALE_AUTO | HQ_DITHER | HQ_WANT_COORDS;
+constexpr uint32_t kKnownFlags = HQ_SCALE_AUTO | HQ_DITHER | HQ_WANT_COORDS | HQ_RATE_CONTROL;
 
 bool lattice_ok(int32_t l) { return l == HQ_E8 || l == HQ_D4 || l == HQ_A2 || l == HQ_Z; }
 
@@ -33,6 +33,10 @@ hq_status check_params(const hq_params* p) {
   if (p->tile != 64 && p->tile != 128 && p->tile != 256 && p->tile != kMaxTile) return HQ_EINVAL;
   if (!(p->bps > 0.0f) || !(p->bps <= 8.0f)) return HQ_EINVAL;
   if ((p->flags & ~kKnownFlags) != 0 || p->reserved != 0) return HQ_EINVAL;
+  if (p->flags & HQ_RATE_CONTROL) {
+    if (!(p->flags & HQ_SCALE_AUTO)) return HQ_EINVAL;     // the scales are outputs
+    if (p->flags & HQ_DITHER) return HQ_EUNSUPPORTED;
+  }
   if (p->flags & HQ_DITHER) {
     if (p->lattice != HQ_E8) return HQ_EUNSUPPORTED;
     if (p->tile > 256) return HQ_EUNSUPPORTED;   // the dither key holds coordinates < 256
@@ -99,6 +103,11 @@ bool on_device(const void* q) {
 
 hq_status launched(hipError_t e) { return e == hipSuccess ? HQ_OK : HQ_EDEVICE; }
 
+void set_rate_control(const hq_params* p, EncodeLaunch& a) {
+  a.rate_control = (p->flags & HQ_RATE_CONTROL) != 0;
+  a.rc_budget = (uint32_t)floor((double)p->bps * (double)p->tile);
+}
+
 // Shared validation of an encode-shaped call.
 hq_status check_encode(const hq_params* p, const void* x, int32_t x_dtype, int64_t rows,
                        int64_t cols, const float* scale, const int8_t* idx,
@@ -118,7 +127,9 @@ hq_status check_encode(const hq_params* p, const void* x, int32_t x_dtype, int64
   if (!aligned16(x) || !aligned16(idx) || ((p->flags & HQ_WANT_COORDS) && !aligned16(coords)))
     return HQ_EINVAL;
   if (rows > 0 && cols > 0 && rows > INT64_MAX / cols) return HQ_EINVAL;
-  if ((p->flags & HQ_SCALE_AUTO) && !range_ok(p)) return HQ_ERANGE;
+  // (rate control keeps the indices in range by itself)
+  if ((p->flags & HQ_SCALE_AUTO) && !(p->flags & HQ_RATE_CONTROL) && !range_ok(p))
+    return HQ_ERANGE;
   return HQ_OK;
 }
 
@@ -159,6 +170,7 @@ hq_status hq_encode_tiles(const hq_params* p, const void* x, int32_t x_dtype, in
   make_signs(p->rht_seed, p->tile, a.signs);
   a.c = scale_constant(p);
   a.sqrt_n = sqrt((double)p->tile);
+  set_rate_control(p, a);
   return launched(launch_encode(a, stream));
 }
 
@@ -197,6 +209,7 @@ hq_status hq_kv_encode(const hq_params* p, const void* kv, int32_t kv_dtype, int
   make_signs(p->rht_seed, p->tile, a.signs);
   a.c = scale_constant(p);
   a.sqrt_n = sqrt((double)p->tile);
+  set_rate_control(p, a);
   a.dither = (p->flags & HQ_DITHER) != 0;
   a.dither_seed = p->dither_seed;
   a.dither_base = p->dither_base;
@@ -271,7 +284,8 @@ hq_status hq_encode_batch(const hq_params* p, int32_t x_dtype, int32_t count,
   make_signs(p->rht_seed, p->tile, a.signs);
   a.c = scale_constant(p);
   a.sqrt_n = sqrt((double)p->tile);
-  if (e8_fast_encode_ok(a)) {
+  set_rate_control(p, a);
+  if (!a.rate_control && e8_fast_encode_ok(a)) {
     EncBatch b;
     memset(&b, 0, sizeof(b));
     for (int32_t i = 0; i <= count; ++i) {

@@ -75,6 +75,102 @@ __device__ inline uint32_t lane_sign_mask(const EncodeLaunch& a, int r) {
   return (s >> (16 * (r & 1))) & 0xFFFFu;
 }
 
+// Quantizer input on the 2^-24 grid for 16 rotated values: U = rne(S K)
+// (A2: odd coordinates with K3); magnitudes past kUClamp flag an overflow.
+template <int LAT>
+__device__ inline void grid_values(const double* v, double K, double K3, int32_t* U,
+                                   uint32_t& st) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    double q = rint(__dmul_rn(v[i], (LAT == 2 && (i & 1)) ? K3 : K));
+    if (!(fabs(q) <= kUClamp)) {
+      st |= HQ_ST_OVERFLOW;
+      q = (q > 0.0) ? kUClamp : -kUClamp;
+    }
+    U[i] = (int32_t)q;
+  }
+}
+
+// Nearest point and lossless strip of this lane's 16 grid values: stored
+// integers s, full coordinates crd (E8 and A2: 2p), coset bits of the
+// lane's blocks (E8) or pairs (A2).
+template <int LAT>
+__device__ inline void nearest_strip(const int32_t* U, int32_t* s, int16_t* crd, uint32_t& cbits) {
+  cbits = 0;
+  if constexpr (LAT == 8) {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      int32_t z[8];
+      const int c = e8_nearest(&U[8 * blk], z);
+      cbits |= (uint32_t)c << blk;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        s[8 * blk + i] = (i == 7) ? (z[i] >> 1) : z[i];
+        crd[8 * blk + i] = (int16_t)(2 * z[i] + c);
+      }
+    }
+  } else if constexpr (LAT == 4) {
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      int32_t z[4];
+      d_round<4>(&U[4 * blk], z);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[4 * blk + i] = (i == 3) ? (z[i] >> 1) : z[i];
+        crd[4 * blk + i] = (int16_t)z[i];
+      }
+    }
+  } else if constexpr (LAT == 2) {
+#pragma unroll
+    for (int pr = 0; pr < 8; ++pr) {
+      int32_t x0, x1;
+      const int c = a2_nearest(U[2 * pr], U[2 * pr + 1], x0, x1);
+      cbits |= (uint32_t)c << pr;
+      s[2 * pr] = x0;
+      s[2 * pr + 1] = x1;
+      crd[2 * pr] = (int16_t)(2 * x0 + c);
+      crd[2 * pr + 1] = (int16_t)(2 * x1 + c);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      int32_t R;
+      s[i] = rne_grid(U[i], R);
+      crd[i] = (int16_t)s[i];
+    }
+  }
+}
+
+// Rice parameter of the tile: k = argmin sum(floor(zeta/2^k) + 1 + k), first
+// minimum, over the int8 values of s (k >= 8 gives every zeta >> k = 0, so
+// k = 8 dominates k = 9..15).  Flags int8 overflow; returns the payload bits
+// and fills the lane's four packed index words.
+template <int G, int N>
+__device__ inline uint32_t rice_best(const int32_t* s, uint32_t& st, int& bk, uint32_t* packed) {
+  uint32_t Lp[9];
+#pragma unroll
+  for (int k = 0; k < 9; ++k) Lp[k] = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) packed[i] = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (s[i] < -128 || s[i] > 127) st |= HQ_ST_OVERFLOW;
+    const int32_t s8 = (int32_t)(int8_t)s[i];
+    packed[i >> 2] |= ((uint32_t)s8 & 0xFFu) << (8 * (i & 3));
+    const uint32_t zz = zigzag(s8);
+#pragma unroll
+    for (int k = 0; k < 9; ++k) Lp[k] += zz >> k;
+  }
+  uint32_t best = 0xFFFFFFFFu;
+  bk = 0;
+#pragma unroll
+  for (int k = 0; k < 9; ++k) {
+    const uint32_t L = group_sum<G>(Lp[k]) + (uint32_t)N * (uint32_t)(1 + k);
+    if (L < best) { best = L; bk = k; }
+  }
+  return best;
+}
+
 template <int LAT, int N, bool IN_BF16, bool DITHER>
 __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeLaunch a) {
   constexpr int G = N / kElemsPerLane;
@@ -126,25 +222,49 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeLaunch a) {
     delta = a.scale[tile];
     if (!(delta > 0.0f) || !isfinite(delta)) st |= HQ_ST_NONFINITE;
   }
-  const double t = a.sqrt_n * (double)delta;
-  const double K = 16777216.0 / t;
-  double K3 = K;
-  if (LAT == 2) K3 = 16777216.0 / (t * 1.7320508075688772);
-
   // ---- rotation
   fwht16<G>(v, r);
 
+  // ---- per-tile rate control: the finest bf16 scale, by bisection on its
+  // bit pattern within eight binades of the automatic one, at which the
+  // indices fit int8 and the tile fits the budget (every decision integer)
+  if constexpr (!DITHER) {
+    if (a.rate_control && group_or<G>(st) == 0u && ss > 0.0) {   // group-uniform
+      auto feasible = [&](uint32_t code) {
+        const double tq = a.sqrt_n * (double)__uint_as_float(code << 16);
+        int32_t Uq[16], sq[16];
+        int16_t cq[16];
+        uint32_t stq = 0, cbq, pq[4];
+        int bkq;
+        grid_values<LAT>(v, 16777216.0 / tq, 16777216.0 / (tq * 1.7320508075688772), Uq, stq);
+        nearest_strip<LAT>(Uq, sq, cq, cbq);
+        const uint32_t bits = 4u + (uint32_t)(N / LAT) * (Lat<LAT>::kCosetBits > 0 ? 1u : 0u) +
+                              rice_best<G, N>(sq, stq, bkq, pq);
+        return (group_or<G>(stq) & HQ_ST_OVERFLOW) == 0u && bits <= a.rc_budget;
+      };
+      const int32_t ac = (int32_t)(__float_as_uint(delta) >> 16);
+      int32_t lo = ac - kRcSpan > 0x0080 ? ac - kRcSpan : 0x0080;
+      int32_t hi = ac + kRcSpan < 0x7F7F ? ac + kRcSpan : 0x7F7F;
+      // probe hi first (infeasible: the tile takes hi), then the midpoints
+      // (one call site, so the search inlines)
+      int32_t probe = hi;
+      for (bool top = true;; top = false) {
+        const bool f = feasible((uint32_t)probe);
+        if (top && !f) break;
+        if (!top) (f ? hi : lo) = probe;
+        if (hi - lo <= 1) break;
+        probe = (lo + hi) / 2;
+      }
+      delta = __uint_as_float((uint32_t)hi << 16);
+    }
+  }
+  const double t = a.sqrt_n * (double)delta;
+  const double K = 16777216.0 / t;
+  const double K3 = 16777216.0 / (t * 1.7320508075688772);
+
   // ---- quantizer input on the 2^-24 grid
   int32_t U[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    double q = rint(__dmul_rn(v[i], (LAT == 2 && (i & 1)) ? K3 : K));
-    if (!(fabs(q) <= kUClamp)) {
-      st |= HQ_ST_OVERFLOW;
-      q = (q > 0.0) ? kUClamp : -kUClamp;
-    }
-    U[i] = (int32_t)q;
-  }
+  grid_values<LAT>(v, K, K3, U, st);
 
   if constexpr (DITHER) {
     // d = w - Q_E8(w), w = 2^-23 h - 1 with h the top 24 bits of the hash
@@ -166,67 +286,14 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeLaunch a) {
     }
   }
 
-  // ---- nearest point, strip, coordinates
+  // ---- nearest point, strip, coordinates; int8 indices and the Rice parameter
   int32_t s[16];
   int16_t crd[16];
-  uint32_t cbits = 0;
-  if constexpr (LAT == 8) {
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      int32_t z[8];
-      const int c = e8_nearest(&U[8 * blk], z);
-      cbits |= (uint32_t)c << blk;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        s[8 * blk + i] = (i == 7) ? (z[i] >> 1) : z[i];
-        crd[8 * blk + i] = (int16_t)(2 * z[i] + c);
-      }
-    }
-  } else if constexpr (LAT == 4) {
-#pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
-      int32_t z[4];
-      d_round<4>(&U[4 * blk], z);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s[4 * blk + i] = (i == 3) ? (z[i] >> 1) : z[i];
-        crd[4 * blk + i] = (int16_t)z[i];
-      }
-    }
-  } else if constexpr (LAT == 2) {
-#pragma unroll
-    for (int pr = 0; pr < 8; ++pr) {
-      int32_t x0, x1;
-      const int c = a2_nearest(U[2 * pr], U[2 * pr + 1], x0, x1);
-      cbits |= (uint32_t)c << pr;
-      s[2 * pr] = x0;
-      s[2 * pr + 1] = x1;
-      crd[2 * pr] = (int16_t)(2 * x0 + c);
-      crd[2 * pr + 1] = (int16_t)(2 * x1 + c);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      int32_t R;
-      s[i] = rne_grid(U[i], R);
-      crd[i] = (int16_t)s[i];
-    }
-  }
-
-  // ---- int8 indices and Rice partial sums: Lp[k] = sum(zeta >> k)
-  uint32_t packed[4] = {0, 0, 0, 0};
-  uint32_t Lp[9];
-#pragma unroll
-  for (int k = 0; k < 9; ++k) Lp[k] = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    if (s[i] < -128 || s[i] > 127) st |= HQ_ST_OVERFLOW;
-    const int32_t s8 = (int32_t)(int8_t)s[i];
-    packed[i >> 2] |= ((uint32_t)s8 & 0xFFu) << (8 * (i & 3));
-    const uint32_t zz = zigzag(s8);
-#pragma unroll
-    for (int k = 0; k < 9; ++k) Lp[k] += zz >> k;
-  }
+  uint32_t cbits;
+  nearest_strip<LAT>(U, s, crd, cbits);
+  uint32_t packed[4];
+  int bk;
+  const uint32_t best = rice_best<G, N>(s, st, bk, packed);
   *reinterpret_cast<uint4*>(a.idx + e0) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
   if (a.coords != nullptr) {
     uint32_t cw[8];
@@ -236,16 +303,6 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeLaunch a) {
     uint4* cp = reinterpret_cast<uint4*>(a.coords + e0);
     cp[0] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
     cp[1] = make_uint4(cw[4], cw[5], cw[6], cw[7]);
-  }
-
-  // ---- Rice parameter: k = argmin sum(floor(zeta/2^k) + 1 + k), first min.
-  // For k >= 8 every zeta >> k is 0, so k = 8 dominates k = 9..15.
-  uint32_t best = 0xFFFFFFFFu;
-  int bk = 0;
-#pragma unroll
-  for (int k = 0; k < 9; ++k) {
-    const uint32_t L = group_sum<G>(Lp[k]) + (uint32_t)N * (uint32_t)(1 + k);
-    if (L < best) { best = L; bk = k; }
   }
 
   // ---- coset words: lane r owns bits [r B, r B + B) of the tile's bit row
@@ -304,7 +361,7 @@ hipError_t launch_lat(const EncodeLaunch& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_encode(const EncodeLaunch& a, hipStream_t s) {
-  if (e8_fast_encode_ok(a)) {
+  if (!a.rate_control && e8_fast_encode_ok(a)) {
     EncBatch b;
     b.n = 1;
     b.pad = 0;
@@ -313,7 +370,7 @@ hipError_t launch_encode(const EncodeLaunch& a, hipStream_t s) {
     for (int i = 1; i < kMaxItems; ++i) b.it[i] = b.it[0];
     return launch_encode_e8_fast(a, b, s);
   }
-  if (e8_128_encode_ok(a)) return launch_encode_e8_128(a, s);
+  if (!a.rate_control && e8_128_encode_ok(a)) return launch_encode_e8_128(a, s);
   switch (a.lattice) {
     case 8: return launch_lat<8>(a, s);
     case 4: return launch_lat<4>(a, s);

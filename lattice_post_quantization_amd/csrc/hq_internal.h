@@ -31,7 +31,13 @@ struct EncodeLaunch {
   int dither;
   uint32_t dither_seed;
   int64_t dither_base;
+  int rate_control;     // per-tile scales by bisection (generic kernel)
+  uint32_t rc_budget;   // bits one tile may take: floor(bps * tile)
 };
+
+// bf16 bit patterns the rate control searches on each side of the
+// automatic scale (eight binades)
+constexpr int32_t kRcSpan = 1024;
 
 struct DecodeLaunch {
   const int8_t* idx;

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libhq.so")
 HQ_OK, HQ_EINVAL, HQ_ERANGE, HQ_EDEVICE, HQ_EUNSUPPORTED = 0, -1, -2, -3, -4
 HQ_Z, HQ_A2, HQ_D4, HQ_E8 = 1, 2, 4, 8
 HQ_F32, HQ_BF16 = 0, 1
-HQ_SCALE_AUTO, HQ_DITHER, HQ_WANT_COORDS = 1, 2, 4
+HQ_SCALE_AUTO, HQ_DITHER, HQ_WANT_COORDS, HQ_RATE_CONTROL = 1, 2, 4, 8
 HQ_ST_NONFINITE, HQ_ST_OVERFLOW, HQ_ST_STREAM_FULL, HQ_ST_CORRUPT = 1, 2, 4, 8
 
 LATTICES = {"E8": HQ_E8, "D4": HQ_D4, "A2": HQ_A2, "Z": HQ_Z}
@@ -177,14 +177,16 @@ def splitmix64(key):
 
 
 def hq_encode_tiles(x, lattice="E8", tile=256, bps=4.0, rht_seed=0, scale=None,
-                    want_coords=False, status=None, out=None):
+                    want_coords=False, status=None, out=None, rate_control=False):
     """Encode a row-major (rows, cols) bf16/fp32 device matrix.
 
     scale=None selects auto scales (returned); otherwise a float32 device
     tensor of per-tile scales.  Returns a dict of device tensors: scale,
     idx (int8, like x), coset (int32 words, (n_tiles, w)), rice_k (uint8),
     tile_bits (int32 holding uint32), coords (int16, if requested).
-    `out` may supply preallocated tensors under the same keys."""
+    `out` may supply preallocated tensors under the same keys.
+    rate_control: per-tile scales so that each tile fits floor(bps * tile)
+    bits (auto scales only; the chosen scales are returned)."""
     _device_tensor(x, "x")
     if x.dim() != 2:
         raise ValueError("x must be 2-D (rows, cols)")
@@ -193,7 +195,8 @@ def hq_encode_tiles(x, lattice="E8", tile=256, bps=4.0, rht_seed=0, scale=None,
     n_tiles = rows * cols // tile if cols % tile == 0 else 0
     w = coset_words(lattice, tile)
     o = dict(out or {})
-    flags = (HQ_SCALE_AUTO if scale is None else 0) | (HQ_WANT_COORDS if want_coords else 0)
+    flags = ((HQ_SCALE_AUTO if scale is None else 0) | (HQ_WANT_COORDS if want_coords else 0) |
+             (HQ_RATE_CONTROL if rate_control else 0))
     if scale is None:
         scale = o.get("scale")
         if scale is None:

@@ -88,6 +88,12 @@ def test_encode_validation_codes():
     assert _enc(P("E8", 256, 4.0, 0, auto), rows=-1) == hq.HQ_EINVAL
     for n in (32, 96, 1024):
         assert _enc(P("E8", n, 4.0, 0, auto)) == hq.HQ_EINVAL                  # tile
+    # rate control: the scales are outputs, no dither, no int8 range refusal
+    rc = hq.HQ_RATE_CONTROL
+    assert _enc(P("E8", 256, 4.0, 0, rc)) == hq.HQ_EINVAL
+    assert _enc(P("E8", 256, 4.0, 0, auto | rc | hq.HQ_DITHER, 1)) == hq.HQ_EUNSUPPORTED
+    assert _enc(P("E8", 256, 6.0, 0, auto)) == hq.HQ_ERANGE
+    assert _enc(P("E8", 256, 6.0, 0, auto | rc)) != hq.HQ_ERANGE
     # the dither key holds coordinates below 256
     assert _enc(P("E8", 512, 4.0, 0, auto | hq.HQ_DITHER, 1), cols=512) == hq.HQ_EUNSUPPORTED
     assert _enc(P(3, 256, 4.0, 0, auto)) == hq.HQ_EINVAL                       # lattice

@@ -620,6 +620,42 @@ def test_kv_low_rate_parity(bps):
     check_decode(ora, "E8", 128, 1, "kv %g bps" % bps, exact=True, dither_seed=9, dither_base=77)
 
 
+@pytest.mark.parametrize("lattice,n,dtype,bps", [("E8", 256, "bf16", 4.0), ("E8", 128, "f32", 3.0),
+                                                 ("D4", 128, "bf16", 4.0), ("A2", 64, "bf16", 3.5),
+                                                 ("Z", 512, "f32", 5.0)])
+def test_rate_control_parity(lattice, n, dtype, bps):
+    """Per-tile rate control (bisection on bf16 scales to floor(bps n) bits per
+    tile) against the oracle on a ragged matrix with outlier columns: the
+    chosen scales bit for bit, indices, k and bits, and every tile within
+    its budget; then the decoded values."""
+    rows, cols = 29, 5 * n
+    rng = np.random.default_rng(97)
+    w = rng.standard_normal((rows, cols)) * 0.02
+    w[:, 2] *= 80.0
+    w[3] = 0.0
+    if dtype == "bf16":
+        bits = workloads.f32_to_bf16_bits(w.astype(np.float32))
+        xh = workloads.bf16_bits_to_f64(bits)
+        xd = T.bf16_device(bits, (rows, cols))
+    else:
+        xh = w.astype(np.float32)
+        xd = T.f32_device(xh)
+    label = "rate control %s/%d %s R=%g" % (lattice, n, dtype, bps)
+    say("case:", label)
+    g = hq.hq_encode_tiles(xd, lattice, n, bps, 4, rate_control=True)
+    torch.cuda.synchronize()
+    ora = codec.encode(xh, lattice, n, bps, rht_seed=4, rate_control=True)
+    assert np.array_equal(T.host(g["scale"]).astype(np.float64), ora["scale"]), label
+    _, _, _, ok = T.compare_indices(T.host(g["idx"]).reshape(-1, n), T.u32(g["coset"]), ora,
+                                    lattice, n, label)
+    assert ok.all()
+    assert np.array_equal(T.host(g["rice_k"]).astype(np.int64), ora["rice_k"])
+    gb = T.u32(g["tile_bits"]).astype(np.int64)
+    assert np.array_equal(gb, ora["tile_bits"])
+    assert np.all(gb <= math.floor(bps * n))
+    check_decode(ora, lattice, n, 4, label, exact=(lattice != "A2"))
+
+
 def test_kv_head_dim_64_dither_parity():
     """Dithered E8 encode and decode of 300 KV vectors of 64 (tile 64,
     generic kernels) against the oracle, every vector."""
