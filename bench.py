@@ -31,15 +31,20 @@ DEC_BYTES_PER_TILE = 256 + 4 + 4 + 512
 
 # Measured HBM bytes per tile (rocprofv3 FETCH_SIZE and WRITE_SIZE per
 # dispatch, each scaled by what the same counter reads for a copy of known
-# size; the runs are summarised in profiles/).  They describe the kernels
+# size) and VALU lane-operations per weight (SQ_INSTS_VALU per dispatch x 64
+# lanes); the runs are summarised in profiles/.  They describe the kernels
 # built from the sources with this sha256 and are reported only while the
 # sources still match.
 KERNEL_SOURCES = ("hq_e8fast.hip", "hq_lanes.h", "hq_device.h", "hq_internal.h")
 MEASURED_TRAFFIC = {
-    "sources_sha256": "a11c09d9ed4bcec65a8ea0fd93c9ecd0ba4f7e986ea21e3606e069a44000efaf",
-    "encode": {"read": 514.08, "write": 272.46},
-    "decode": {"read": 265.45, "write": 512.00},
+    "sources_sha256": "6466746bac36a350b51239870a662df1724ec6fc6d8d3065056709edd1b09d0b",
+    "encode": {"read": 514.06, "write": 272.46},
+    "decode": {"read": 265.35, "write": 512.00},
+    "valu_lane_ops_per_weight": {"encode": 36.26, "decode": 11.90},
 }
+# VALU issue roof: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (a wave64 instruction
+# occupies a SIMD for 4 cycles; fp64 add / mul / fma issue at the same rate)
+VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
 
 
 def kernel_sources_sha256():
@@ -357,10 +362,16 @@ def main():
     dom_name = "encode" if dominant is enc else "decode"
 
     tiles_per_launch = sum(ev["enc_tiles"]) / len(ev["enc_tiles"])
-    traffic = None
+    traffic = alu = None
     if kernel_sources_sha256() == MEASURED_TRAFFIC["sources_sha256"]:
         t = MEASURED_TRAFFIC[dom_name]
         traffic = round((t["read"] + t["write"]) * tiles_per_launch)
+        # the same launches against the VALU issue roof
+        ops = MEASURED_TRAFFIC["valu_lane_ops_per_weight"][dom_name] * 256 * tiles_per_launch
+        achieved = ops / (dominant["avg_us"] * 1e-6)
+        alu = {"achieved": round(achieved / 1e12, 2), "peak": round(VALU_PEAK_LANE_OPS / 1e12, 2),
+               "unit": "T VALU lane-ops/s (issued)", "frac": round(achieved / VALU_PEAK_LANE_OPS, 4),
+               "lane_ops_per_weight": MEASURED_TRAFFIC["valu_lane_ops_per_weight"][dom_name]}
 
     extra = secondary(layers[0], args.bps, dev) if args.secondary else None
 
@@ -398,6 +409,7 @@ def main():
             "traffic_unit": "HBM bytes per launch (null: kernel changed since the counters)",
             "algorithmic_bytes_per_launch": round(
                 (ENC_BYTES_PER_TILE if dom_name == "encode" else DEC_BYTES_PER_TILE) * tiles_per_launch),
+            "alu_issue": alu,
         },
         "kernels": {
             "encode": {k: round(v, 3) for k, v in enc.items()},
