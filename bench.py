@@ -225,6 +225,39 @@ def secondary(layer0, bps, dev):
             "speedup_vs_bf16": round(ms_b / ms_g, 3),
             "algorithmic_gbs": round(alg_g / (ms_g * 1e-3) / 1e9, 1)}
 
+    # variants on the same layer's weights: per-tile rate control (the
+    # generic kernel searches about a dozen scales per tile) and tile 512
+    xs0, _, _ = layer0
+    rc = [hq.hq_encode_tiles(x, "E8", 256, bps, 0, rate_control=True) for x in xs0]
+
+    def rc_layer():
+        for x, o in zip(xs0, rc):
+            hq.hq_encode_tiles(x, "E8", 256, bps, 0, rate_control=True, out=o)
+
+    ms_rc = time_calls(rc_layer, 3)
+    torch.cuda.synchronize()
+    n_w = sum(x.numel() for x in xs0)
+    rc_bits = sum(float(o["tile_bits"].double().sum().item()) for o in rc) / n_w
+    e512 = [hq.hq_encode_tiles(x, "E8", 512, bps, 0) for x in xs0]
+    y512 = [torch.empty_like(x) for x in xs0]
+
+    def enc512():
+        for x, o in zip(xs0, e512):
+            hq.hq_encode_tiles(x, "E8", 512, bps, 0, out=o)
+
+    def dec512():
+        for o, y in zip(e512, y512):
+            hq.hq_decode_tiles(o["idx"], o["coset"], o["scale"], "E8", 512, 0, torch.bfloat16,
+                               out=y)
+
+    ms_e512, ms_d512 = time_calls(enc512, 5), time_calls(dec512, 5)
+    variants = {
+        "workload": "the same layer's seven matrices (bf16) through the generic kernels",
+        "rate_control_encode_us": round(ms_rc * 1e3, 1),
+        "rate_control_bits_per_weight": round(rc_bits, 4),
+        "tile512_encode_us": round(ms_e512 * 1e3, 1), "tile512_decode_us": round(ms_d512 * 1e3, 1),
+        "tile512_encode_gbs_bf16_in": round(2 * n_w / (ms_e512 * 1e-3) / 1e9, 1)}
+
     kb, vb = workloads.kv_layer()
     kvs = [torch.from_numpy(a.reshape(-1, 128).view(np.int16)).to(dev).view(torch.bfloat16)
            for a in (kb, vb)]
@@ -264,7 +297,7 @@ def secondary(layer0, bps, dev):
                              "one call (dither regenerated per key)" % (nq, heads, seq),
           "scores_us": round(ms_s * 1e3, 2),
           "scores_gflops": round(2.0 * nq * heads * seq * 128 / (ms_s * 1e-3) / 1e9, 1)}
-    return {"pack": pack, "unpack": unpack, "gemv": gemv, "kv": kv}
+    return {"pack": pack, "unpack": unpack, "gemv": gemv, "kv": kv, "variants": variants}
 
 
 def main():
