@@ -101,6 +101,9 @@ struct BitReader {
     nb -= n;
     return v;
   }
+  // this reader stops at the tile's last word, so an overrun shows as
+  // missing bits while decoding
+  __device__ inline bool overran() const { return false; }
 };
 
 // One Rice code: the zigzag value (garbage, with bad set, when the code runs
@@ -145,28 +148,37 @@ __device__ inline uint32_t read_code(BitReader<FromLds>& br, uint32_t k, bool& b
 // the staged segment, a refill that reads the next word unconditionally
 // (clamped into the segment) so that the value is first used one refill
 // later, and a fast path for a code that lies within the buffered bits.
+// The refill does not stop at the tile's last word: the words after it are
+// the wave's next tiles (or the repeated last staged word), so a code that
+// runs past its tile reads staged words only, and overran() reports it
+// once the tile is decoded.
 struct LdsReader {
   const lds_u32* lds;
-  uint32_t i, iend, last;   // next word, end of the tile, last staged word
+  uint32_t i0, i, iend, last;   // first and next word, end of the tile, last staged word
   uint64_t b;
   uint32_t nb;
-  uint32_t ahead;           // lds[i] (meaningful while i < iend)
+  uint32_t ahead;               // lds[min(i, last)]
 
-  __device__ inline void init(const lds_u32* seg, uint32_t i0, uint32_t i1, uint32_t n_staged) {
+  __device__ inline void init(const lds_u32* seg, uint32_t w0, uint32_t w1, uint32_t n_staged) {
     lds = seg;
-    i = i0;
-    iend = i1;
+    i0 = w0;
+    i = w0;
+    iend = w1;
     last = n_staged - 1u;
     b = 0;
     nb = 0;
-    ahead = lds[i0 < last ? i0 : last];
+    ahead = lds[w0 < last ? w0 : last];
   }
   __device__ inline void refill() {
-    const bool c = nb <= 32u && i < iend;
+    const bool c = nb <= 32u;
     b |= (uint64_t)(c ? ahead : 0u) << nb;
     nb += c ? 32u : 0u;
     i += c ? 1u : 0u;
     ahead = lds[i < last ? i : last];
+  }
+  // more bits consumed than the tile's words hold
+  __device__ inline bool overran() const {
+    return 32ull * (uint64_t)(i - i0) - nb > 32ull * (uint64_t)(iend - i0);
   }
   __device__ inline uint32_t take(uint32_t n) {   // n <= 32, at most nb
     n = n < nb ? n : nb;
@@ -177,11 +189,14 @@ struct LdsReader {
   }
 };
 
+// trailing zeros of x, 32 for x = 0 (one v_ffbl and a min)
+__device__ inline uint32_t ctz0(uint32_t x) { return x ? (uint32_t)__builtin_ctz(x) : 32u; }
+
 __device__ inline uint32_t read_code_lds(LdsReader& br, uint32_t k, bool& bad) {
   br.refill();
-  const uint32_t nlo = ~(uint32_t)br.b, nhi = ~(uint32_t)(br.b >> 32);
-  uint32_t z = nlo != 0u ? (uint32_t)__builtin_ctz(nlo)
-                         : (nhi != 0u ? 32u + (uint32_t)__builtin_ctz(nhi) : 64u);
+  // the run of ones: the first zero of the 64-bit buffer, without a branch
+  const uint32_t zl = ctz0(~(uint32_t)br.b), zh = 32u + ctz0(~(uint32_t)(br.b >> 32));
+  uint32_t z = zl < 32u ? zl : zh;
   if (z + 1u + k <= br.nb) {
     // common case: the whole code is buffered
     const uint32_t rem = (uint32_t)(br.b >> (z + 1u)) & ((1u << k) - 1u);
@@ -278,6 +293,7 @@ __device__ inline void decode_tiles(const UnpackLaunch& a, Reader& br, int64_t t
     }
     wave_lds_sync();
   }
+  bad |= br.overran();
 }
 
 template <int N>
