@@ -25,9 +25,9 @@
  *     HQ_EUNSUPPORTED), the auto-scale index range bound (HQ_ERANGE) and
  *     launch failure (HQ_EDEVICE).  Validation happens before any device
  *     call; on a nonzero return nothing was enqueued.
- *   - Data-dependent faults (non-finite input, an index outside int8 with an
- *     explicit scale, a packed stream larger than its capacity) are OR-ed
- *     into the optional device word `*status` (HQ_ST_* bits); the caller
+ *   - Data-dependent faults (non-finite input, a quantizer value |u| > 124
+ *     with an explicit scale, a packed stream larger than its capacity) are
+ *     OR-ed into the optional device word `*status` (HQ_ST_* bits); the caller
  *     reads it after synchronising.  Outputs of an affected tile are
  *     unspecified.  `status` may be NULL.
  *   - A call with zero tiles is a no-op returning HQ_OK.
@@ -82,7 +82,9 @@ enum {
 /* Device status bits (OR-ed into *status by kernels). */
 enum {
   HQ_ST_NONFINITE = 1u,   /* NaN or Inf in the input of a tile            */
-  HQ_ST_OVERFLOW = 2u,    /* a stripped index left int8 (explicit scale)  */
+  HQ_ST_OVERFLOW = 2u,    /* a grid value |u| passed 124, where encode
+                             clamps it (explicit scale; covers every
+                             index that would leave int8)                 */
   HQ_ST_STREAM_FULL = 4u, /* hq_rate: packed stream exceeded capacity     */
   HQ_ST_CORRUPT = 8u      /* hq_unpack: a tile's codes overran its words,
                              or decoded to a value outside int8           */

@@ -27,7 +27,7 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
     "-I", INCLUDE, "-I", CSRC,
 ]
-SOURCES = ["hq_encode.hip", "hq_decode.hip", "hq_e8fast.hip", "hq_kvfast.hip", "hq_rate.hip", "hq_unpack.hip",
+SOURCES = ["hq_encode.hip", "hq_decode.hip", "hq_e8fast.hip", "hq_fast128.hip", "hq_rate.hip", "hq_unpack.hip",
            "hq_gemv.hip", "hq_kvscore.hip", "hq_api.hip"]
 
 

@@ -210,7 +210,7 @@ hipError_t launch_decode(const DecodeLaunch& a, hipStream_t s) {
     for (int i = 1; i < kMaxItems; ++i) b.it[i] = b.it[0];
     return launch_decode_e8_fast(a, b, s);
   }
-  if (e8_128_decode_ok(a)) return launch_decode_e8_128(a, s);
+  if (fast128_decode_ok(a)) return launch_decode_fast128(a, s);
   switch (a.lattice) {
     case 8: return launch_lat<8>(a, s);
     case 4: return launch_lat<4>(a, s);

@@ -140,8 +140,9 @@ __device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const
     if (!(delta > 0.0f) || !isfinite(delta)) status |= HQ_ST_NONFINITE;
   }
   if (!isfinite(ss)) status |= HQ_ST_NONFINITE;
-  if (!(sqrt(ss) < 126.0 * (double)delta)) status |= HQ_ST_OVERFLOW;
-  const double K = 16777216.0 / (a.sqrt_n * (double)delta);
+  // |u_i| <= sqrt(sum x^2) / Delta: below 124 no grid value reaches the clamp
+  const bool big = !(sqrt(ss) < 124.0 * (double)delta);
+  double K = 16777216.0 / (a.sqrt_n * (double)delta);
 
   // ---- Walsh-Hadamard: element bits 0-5 in registers
 #pragma unroll
@@ -175,6 +176,21 @@ __device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const
   }
   // Now register i holds element bits (i0 i1 i2 i3 | i4 = b7 | i5 = b6) and the
   // lane's row bits hold (r0 = b5, r1 = b4).
+
+  // When some tile of the wave may pass the clamp, the generic encoder's
+  // clamped rint(S K) replaces S (and K becomes 1).
+  if (__builtin_amdgcn_ballot_w64(big) != 0) {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      double q = rint(__dmul_rn(v[i], K));
+      if (!(fabs(q) <= kUClamp)) {
+        status |= HQ_ST_OVERFLOW;
+        q = (q > 0.0) ? kUClamp : -kUClamp;
+      }
+      v[i] = q;
+    }
+    K = 1.0;
+  }
 
   // ---- quantizer input U = rne(S K) (units of 2^-24), stored integers
   uint32_t packed[16];
@@ -269,7 +285,7 @@ __device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const
                                        (int)row0_offset(t, row, 1), 0, 0);
   __builtin_amdgcn_raw_buffer_store_b32(4u + 32u + best, out_rsrc(it.tile_bits + tile0, live * 4u),
                                         (int)row0_offset(t, row, 4), 0, 0);
-  if (status && row == 0 && (uint32_t)t < live) set_status(a.status, status);
+  if (status && (uint32_t)t < live) set_status(a.status, status);
 }
 
 // Persistent waves: each wave walks groups of 16 tiles with a grid-wide

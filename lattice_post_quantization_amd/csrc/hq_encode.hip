@@ -370,7 +370,7 @@ hipError_t launch_encode(const EncodeLaunch& a, hipStream_t s) {
     for (int i = 1; i < kMaxItems; ++i) b.it[i] = b.it[0];
     return launch_encode_e8_fast(a, b, s);
   }
-  if (!a.rate_control && e8_128_encode_ok(a)) return launch_encode_e8_128(a, s);
+  if (!a.rate_control && fast128_encode_ok(a)) return launch_encode_fast128(a, s);
   switch (a.lattice) {
     case 8: return launch_lat<8>(a, s);
     case 4: return launch_lat<4>(a, s);

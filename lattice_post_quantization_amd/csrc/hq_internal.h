@@ -197,12 +197,12 @@ bool e8_fast_decode_ok(const DecodeLaunch& a);
 hipError_t launch_encode_e8_fast(const EncodeLaunch& a, const EncBatch& b, hipStream_t s);
 hipError_t launch_decode_e8_fast(const DecodeLaunch& a, const DecBatch& b, hipStream_t s);
 
-// Fast path for E8 / tile 128 (KV vectors, with or without the dither):
+// Fast path for tile 128, every lattice (E8 with or without the KV dither):
 // bf16 input (encode), either output type (decode); groups of 32 tiles.
-bool e8_128_encode_ok(const EncodeLaunch& a);
-bool e8_128_decode_ok(const DecodeLaunch& a);
-hipError_t launch_encode_e8_128(const EncodeLaunch& a, hipStream_t s);
-hipError_t launch_decode_e8_128(const DecodeLaunch& a, hipStream_t s);
+bool fast128_encode_ok(const EncodeLaunch& a);
+bool fast128_decode_ok(const DecodeLaunch& a);
+hipError_t launch_encode_fast128(const EncodeLaunch& a, hipStream_t s);
+hipError_t launch_decode_fast128(const DecodeLaunch& a, hipStream_t s);
 
 // Rate blocks the hq_rate workspace provides for: per block a word sum and a
 // bit sum, per wave (4 per block) a word sum.

@@ -745,3 +745,72 @@ def test_e8_128_groups_edges():
                        scale=torch.full((32,), 1e-4, device="cuda"), status=st)
     torch.cuda.synchronize()
     assert int(st.item()) == hq.HQ_ST_OVERFLOW
+
+
+@pytest.mark.parametrize("lattice,n", [("E8", 128), ("D4", 128), ("A2", 128), ("Z", 128),
+                                       ("E8", 256)])
+def test_fast_grid_clamp(lattice, n):
+    """Caller scales near the grid clamp: bf16 input (the tile-128 and the
+    E8 / tile-256 fast kernels) against fp32 input of the same values (the
+    generic kernel) and the oracle.  A tile A (s * h_k) (signs times Hadamard row k)
+    rotates to one coordinate of size ||x|| / Delta, so its scale puts the
+    largest grid value where wanted: HQ_ST_OVERFLOW is set iff some oracle
+    grid value passes 124 (the clamp), and the other tiles of the call, which
+    share the clamped grid of the spike's wave, match the oracle."""
+    from oracle import hadamard, splitmix
+    seed, bps = 3, 4.0
+    s = splitmix.rht_signs(seed, n)
+    H = hadamard.sylvester(n)
+    rng = np.random.default_rng(17)
+    for target in (123.5, 124.0 + 2.0 ** -20, 124.4, 125.9, 126.6, 131.0):
+        x = rng.standard_normal((40, n)) * 0.02
+        x[9] = s * H[77]                       # ||x|| = sqrt(n), one rotated coordinate
+        bits = workloads.f32_to_bf16_bits(x.astype(np.float32))
+        xh = workloads.bf16_bits_to_f64(bits)
+        sc = codec.auto_scale(xh, lattice, bps).astype(np.float32)
+        sc[9] = np.float32(math.sqrt(n) / target)
+        ora = codec.encode(xh, lattice, n, bps, rht_seed=seed, scale=sc.astype(np.float64))
+        U = np.rint(ora["u"] * 2.0 ** 24)
+        flagged = bool(np.any(np.abs(U) > 124 * 2 ** 24))
+        label = "%s/%d spike |u| = %g" % (lattice, n, target)
+        say("case:", label, "flag expected" if flagged else "no flag")
+        res = []
+        for xd in (T.bf16_device(bits, (40, n)), T.f32_device(xh)):
+            st = torch.zeros(1, dtype=torch.int32, device="cuda")
+            g = hq.hq_encode_tiles(xd, lattice, n, bps, seed, scale=torch.from_numpy(sc).cuda(),
+                                   status=st)
+            torch.cuda.synchronize()
+            res.append((int(st.item()), g))
+        for st_val, _ in res:
+            assert st_val == (hq.HQ_ST_OVERFLOW if flagged else 0), label
+        (_, gf), (_, gg) = res
+        has_coset = codec.coset_bits_per_tile(lattice, n) > 0
+        for key in ("idx", "rice_k", "tile_bits") + (("coset",) if has_coset else ()):
+            assert torch.equal(gf[key], gg[key]), "%s: fast and generic %s differ" % (label, key)
+        keep = np.ones(40, bool)
+        keep[9] = not flagged
+        sub = {k: (v[keep] if isinstance(v, np.ndarray) and v.shape[:1] == (40,) else v)
+               for k, v in ora.items()}
+        gc = T.u32(gf["coset"])[keep] if has_coset else None
+        _, _, _, ok = T.compare_indices(T.host(gf["idx"])[keep], gc, sub, lattice, n, label)
+        assert np.array_equal(T.host(gf["rice_k"])[keep][ok].astype(np.int64), sub["rice_k"][ok])
+        assert np.array_equal(T.u32(gf["tile_bits"])[keep][ok].astype(np.int64),
+                              sub["tile_bits"][ok])
+
+
+@pytest.mark.parametrize("lattice", ["E8", "D4", "A2", "Z"])
+def test_tile128_decode_scale_range(lattice):
+    """Tile 128 decode of oracle indices with scales from 2^-112 to 2^104:
+    waves whose scales stay within 2^-90 .. 2^90 round to bf16 through fp32
+    (to odd, then to nearest even), the others straight from fp64; both
+    against the oracle, bit for bit (A2 within its tolerance)."""
+    rng = np.random.default_rng(23)
+    n = 128
+    x = rng.standard_normal((100, n))
+    bits = workloads.f32_to_bf16_bits(x.astype(np.float32))
+    ora = codec.encode(workloads.bf16_bits_to_f64(bits), lattice, n, 4.0, rht_seed=6)
+    # first 64 tiles (two waves) in range, the rest spread over the extremes
+    e = np.concatenate([rng.uniform(-80, 80, 64), rng.uniform(-112, 104, 36)])
+    ora["scale"] = codec.bf16_rne(2.0 ** e)
+    say("case: %s/128 decode, scales 2^%.0f .. 2^%.0f" % (lattice, e.min(), e.max()))
+    check_decode(ora, lattice, n, 6, "%s/128 scale range" % lattice, exact=(lattice != "A2"))
