@@ -37,10 +37,10 @@ DEC_BYTES_PER_TILE = 256 + 4 + 4 + 512
 # sources still match.
 KERNEL_SOURCES = ("hq_e8fast.hip", "hq_lanes.h", "hq_device.h", "hq_internal.h")
 MEASURED_TRAFFIC = {
-    "sources_sha256": "6466746bac36a350b51239870a662df1724ec6fc6d8d3065056709edd1b09d0b",
-    "encode": {"read": 514.06, "write": 272.46},
-    "decode": {"read": 265.35, "write": 512.00},
-    "valu_lane_ops_per_weight": {"encode": 36.26, "decode": 11.90},
+    "sources_sha256": "f735f7c2b827e2077e840416f59f488f5bfb40fb4d0bf838af1793836e008ed4",
+    "encode": {"read": 513.85, "write": 269.33},
+    "decode": {"read": 265.38, "write": 512.00},
+    "valu_lane_ops_per_weight": {"encode": 36.51, "decode": 11.90},
 }
 # VALU issue roof: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (a wave64 instruction
 # occupies a SIMD for 4 cycles; fp64 add / mul / fma issue at the same rate)
@@ -144,8 +144,10 @@ def time_calls(fn, reps, warm=2):
 def secondary(layer0, bps, dev):
     """Steps outside the headline: the rate + pack pass over one layer's
     indices (its own pass over the encoder's output), the stream decoder on
-    the result, and the KV path (dithered E8 encode and decode of one layer's
-    K and V cache, [8, 32768, 128] each)."""
+    the result, GEMV from the indices, the variants (rate control, tile
+    512), the lattice sweep matrix through every lattice, and the KV path
+    (dithered E8 encode and decode of one layer's K and V cache,
+    [8, 32768, 128] each)."""
     import numpy as np
     import torch
 
@@ -258,6 +260,23 @@ def secondary(layer0, bps, dev):
         "tile512_encode_us": round(ms_e512 * 1e3, 1), "tile512_decode_us": round(ms_d512 * 1e3, 1),
         "tile512_encode_gbs_bf16_in": round(2 * n_w / (ms_e512 * 1e-3) / 1e9, 1)}
 
+    # the lattice sweep matrix (4096 x 14336 bf16 N(0, 0.02^2)): D4, A2 and Z
+    # at tile 128 and E8 at tiles 128 and 256, encode and decode at this rate
+    sw = workloads.sweep_matrix()
+    xs = torch.from_numpy(sw.view(np.int16)).to(dev).view(torch.bfloat16)
+    ys = torch.empty_like(xs)
+    sweep = {"workload": "one 4096x14336 bf16 N(0, 0.02^2) matrix (%d weights), %g bps, "
+                         "bf16 out" % (xs.numel(), bps)}
+    for lat, n in (("D4", 128), ("A2", 128), ("Z", 128), ("E8", 128), ("E8", 256)):
+        o = hq.hq_encode_tiles(xs, lat, n, bps, 1)
+        ms_se = time_calls(lambda: hq.hq_encode_tiles(xs, lat, n, bps, 1, out=o), 10)
+        ms_sd = time_calls(lambda: hq.hq_decode_tiles(o["idx"], o["coset"], o["scale"], lat, n,
+                                                      1, torch.bfloat16, out=ys), 10)
+        sweep["%s_%d" % (lat, n)] = {
+            "encode_us": round(ms_se * 1e3, 1), "decode_us": round(ms_sd * 1e3, 1),
+            "encode_gbs_bf16_in": round(2 * xs.numel() / (ms_se * 1e-3) / 1e9, 1)}
+    del xs, ys
+
     kb, vb = workloads.kv_layer()
     kvs = [torch.from_numpy(a.reshape(-1, 128).view(np.int16)).to(dev).view(torch.bfloat16)
            for a in (kb, vb)]
@@ -297,7 +316,8 @@ def secondary(layer0, bps, dev):
                              "one call (dither regenerated per key)" % (nq, heads, seq),
           "scores_us": round(ms_s * 1e3, 2),
           "scores_gflops": round(2.0 * nq * heads * seq * 128 / (ms_s * 1e-3) / 1e9, 1)}
-    return {"pack": pack, "unpack": unpack, "gemv": gemv, "kv": kv, "variants": variants}
+    return {"pack": pack, "unpack": unpack, "gemv": gemv, "kv": kv, "variants": variants,
+            "lattice_sweep": sweep}
 
 
 def main():
