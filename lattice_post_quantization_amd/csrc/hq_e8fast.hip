@@ -453,8 +453,8 @@ __device__ inline void dec_group(const DecItem& it, const uint32_t* sign_tab, in
     }
 #pragma unroll
     for (int m = 0; m < 32; ++m) {
-      y[2 * m] = (float)(short)(P2[m] & 0xFFFFu) * dsc;
-      y[2 * m + 1] = (float)((int32_t)P2[m] >> 16) * dsc;
+      y[2 * m] = (float)(short)(P2[m] & 0xFFFFu);
+      y[2 * m + 1] = (float)((int32_t)P2[m] >> 16);
     }
   } else {
 #pragma unroll
@@ -491,19 +491,33 @@ __device__ inline void dec_group(const DecItem& it, const uint32_t* sign_tab, in
         y[i + 16] = x - z;
       }
     }
-#pragma unroll
-    for (int i = 0; i < 64; ++i) y[i] *= dsc;
   }
-  // Register i now holds element bits (i0 .. i3, i4 = b7, i5 = b6); rows (b5, b4).
+  // Register i now holds element bits (i0 .. i3, i4 = b7, i5 = b6); rows (b5, b4),
+  // as the exact integer (H P)_e.
 
+  // ---- x = (H P)_e Delta / 32.  fp32 output: one rounding of the exact
+  // product.  bf16 output: the fp32 product is exact for a bf16-valued scale
+  // (|H P| < 2^16 times 8 significant bits) of normal magnitude, and one
+  // rounding to bf16 follows; a wave with any other scale (fp32 caller
+  // scales, outputs that could be subnormal) rounds from the exact fp64
+  // product as the generic decoder does.
   const uint4* st = reinterpret_cast<const uint4*>(sign_tab + row * 32);
   if constexpr (OUT_BF16) {
     uint32_t o[32];
+    const bool exact32 = (__float_as_uint(in.scale) & 0xFFFFu) == 0u && in.scale >= 0x1p-100f &&
+                         in.scale <= 0x1p100f;
+    if (__builtin_amdgcn_ballot_w64(!exact32) == 0) {
 #pragma unroll
-    for (int m = 0; m < 32; ++m) {
-      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-      const bf16x2 pr = {(__bf16)y[2 * m], (__bf16)y[2 * m + 1]};
-      o[m] = __builtin_bit_cast(uint32_t, pr);
+      for (int m = 0; m < 32; ++m) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 pr = {(__bf16)(y[2 * m] * dsc), (__bf16)(y[2 * m + 1] * dsc)};
+        o[m] = __builtin_bit_cast(uint32_t, pr);
+      }
+    } else {
+      const double dd = (double)in.scale * 0.03125;
+#pragma unroll
+      for (int m = 0; m < 32; ++m)
+        o[m] = f64_to_bf16((double)y[2 * m] * dd) | (f64_to_bf16((double)y[2 * m + 1] * dd) << 16);
     }
     // undo the swaps: dword bit 3 <-> row bit 1, dword bit 4 <-> row bit 0
 #pragma unroll
@@ -524,7 +538,7 @@ __device__ inline void dec_group(const DecItem& it, const uint32_t* sign_tab, in
   } else {
     uint32_t o[64];
 #pragma unroll
-    for (int i = 0; i < 64; ++i) o[i] = __float_as_uint(y[i]);
+    for (int i = 0; i < 64; ++i) o[i] = __float_as_uint(y[i] * dsc);
 #pragma unroll
     for (int i = 0; i < 64; ++i)
       if (!(i & 16)) swap32(o[i], o[i + 16]);

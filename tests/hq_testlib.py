@@ -59,14 +59,19 @@ def compare_indices(g_idx, g_coset, ora, lattice, n, label=""):
 
 
 def compare_decoded(g_vals, o_round, o_raw, scale, out_bf16, exact, label=""):
-    """|gpu - oracle fp64| <= 1e-5 * Delta plus half an ulp of the output
-    type at the oracle value (the output rounding: bf16 or fp32); `exact`
-    additionally demands bit equality with the identically rounded oracle
-    value."""
+    """|gpu - oracle fp64| <= 1e-5 * Delta plus the output rounding's own
+    error bound at the oracle value: half an ulp of bf16 or fp32, and below
+    the smallest normal the flush to zero of bf16 (up to 2^-126) or fp32's
+    subnormal spacing (2^-150); `exact` additionally demands bit equality
+    with the identically rounded oracle value."""
     g = np.asarray(g_vals, np.float64)
     raw = np.asarray(o_raw, np.float64)
     tol = 1e-5 * np.asarray(scale, np.float64)[:, None]
-    tol = tol + 0.5 * np.abs(raw) * (2.0 ** -7 if out_bf16 else 2.0 ** -23)
+    if out_bf16:
+        rnd = np.where(np.abs(raw) < 2.0 ** -126, 2.0 ** -126, 0.5 * np.abs(raw) * 2.0 ** -7)
+    else:
+        rnd = np.maximum(0.5 * np.abs(raw) * 2.0 ** -23, 2.0 ** -150)
+    tol = tol + rnd
     err = np.abs(g - raw)
     assert np.all(err <= tol), "%s: max err / Delta %.3g" % (
         label, np.max(err / np.asarray(scale)[:, None]))

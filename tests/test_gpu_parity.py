@@ -798,19 +798,31 @@ def test_fast_grid_clamp(lattice, n):
                               sub["tile_bits"][ok])
 
 
-@pytest.mark.parametrize("lattice", ["E8", "D4", "A2", "Z"])
-def test_tile128_decode_scale_range(lattice):
-    """Tile 128 decode of oracle indices with scales from 2^-112 to 2^104:
-    waves whose scales stay within 2^-90 .. 2^90 round to bf16 through fp32
-    (to odd, then to nearest even), the others straight from fp64; both
-    against the oracle, bit for bit (A2 within its tolerance)."""
+@pytest.mark.parametrize("lattice,n", [("E8", 128), ("D4", 128), ("A2", 128), ("Z", 128),
+                                       ("E8", 256)])
+def test_fast_decode_scale_range(lattice, n):
+    """Fast-kernel decode (tile 128, E8 / tile 256) of oracle indices under
+    caller scales: bf16-valued scales within 2^-80 .. 2^80, fp32 scales with
+    24 significant bits (the product with the Hadamard sums needs more than
+    fp32 holds), and bf16 scales from 2^-112 to 2^104 whose outputs leave the
+    range of the kernels' fp32 shortcuts; every case against the oracle, bit
+    for bit (A2 within its tolerance)."""
     rng = np.random.default_rng(23)
-    n = 128
-    x = rng.standard_normal((100, n))
+    T = 2100
+    x = rng.standard_normal((T, n))
     bits = workloads.f32_to_bf16_bits(x.astype(np.float32))
     ora = codec.encode(workloads.bf16_bits_to_f64(bits), lattice, n, 4.0, rht_seed=6)
-    # first 64 tiles (two waves) in range, the rest spread over the extremes
-    e = np.concatenate([rng.uniform(-80, 80, 64), rng.uniform(-112, 104, 36)])
-    ora["scale"] = codec.bf16_rne(2.0 ** e)
-    say("case: %s/128 decode, scales 2^%.0f .. 2^%.0f" % (lattice, e.min(), e.max()))
-    check_decode(ora, lattice, n, 6, "%s/128 scale range" % lattice, exact=(lattice != "A2"))
+    # 32 bf16 scales in range; 2000 fp32 scales (about one output in 2^16
+    # would round twice through an fp32 product); 68 bf16 scales at the
+    # extremes, the smallest (2^-126 .. 2^-118) giving subnormal outputs that
+    # flush to zero
+    sc = np.concatenate([codec.bf16_rne(2.0 ** rng.uniform(-80, 80, 32)),
+                         (2.0 ** rng.uniform(-40, 40, 2000)).astype(np.float32).astype(np.float64),
+                         codec.bf16_rne(2.0 ** rng.uniform(-126, -118, 34)),
+                         codec.bf16_rne(2.0 ** rng.uniform(-112, 104, 34))])
+    fp32 = sc[32:2032]
+    assert np.all(codec.bf16_bits(fp32).astype(np.uint32) << 16 !=
+                  fp32.astype(np.float32).view(np.uint32))
+    ora["scale"] = sc
+    say("case: %s/%d decode, bf16, fp32 and extreme scales" % (lattice, n))
+    check_decode(ora, lattice, n, 6, "%s/%d scale range" % (lattice, n), exact=(lattice != "A2"))
