@@ -167,9 +167,26 @@ def secondary(layer0, bps, dev):
     # the method reads idx + coset once and writes k, bits, offsets and the
     # words (this implementation reads the indices twice: rate, then pack)
     alg = tiles * (256 + 4) + tiles * (1 + 4 + 8) + 4 * words
+    # the same packing with the encoder's rice_k and tile_bits (HQ_RATE_GIVEN):
+    # reads idx + coset + k + bits once, writes the offsets and the words
+    outs_g = [hq.hq_rate(e["idx"], e["coset"], "E8", 256, pack=True, given=e) for e in encs]
+
+    def pack_layer_given():
+        for e, o in zip(encs, outs_g):
+            hq.hq_rate(e["idx"], e["coset"], "E8", 256, pack=True, out=o, given=e)
+
+    ms_gv = time_calls(pack_layer_given, 10)
+    torch.cuda.synchronize()
+    same_g = all(torch.equal(a["stream"][:int(a["tile_word_offset"][-1])],
+                             b["stream"][:int(b["tile_word_offset"][-1])])
+                 for a, b in zip(outs, outs_g))
+    alg_g = tiles * (256 + 4 + 1 + 4) + tiles * 8 + 4 * words
     pack = {"workload": "rate + pack of one Llama-3.1-8B-shaped layer's E8 indices "
                         "(seven calls, %d tiles)" % tiles,
             "us": round(ms * 1e3, 2), "algorithmic_gbs": round(alg / (ms * 1e-3) / 1e9, 1),
+            "us_encoder_rate_given": round(ms_gv * 1e3, 2),
+            "given_algorithmic_gbs": round(alg_g / (ms_gv * 1e-3) / 1e9, 1),
+            "given_stream_identical": bool(same_g),
             "stream_bits_per_weight": round(32.0 * words / (tiles * 256), 4)}
 
     # the stream decoder on the same streams

@@ -74,9 +74,12 @@ enum {
   HQ_SCALE_AUTO = 1u,   /* encode computes the scales (else reads them)    */
   HQ_DITHER = 2u,       /* subtractive dither (E8 only; KV encode/decode)  */
   HQ_WANT_COORDS = 4u,  /* encode also writes full lattice coordinates     */
-  HQ_RATE_CONTROL = 8u  /* encode: per-tile scales by bisection so that each
+  HQ_RATE_CONTROL = 8u, /* encode: per-tile scales by bisection so that each
                            tile fits floor(bps * tile) bits (see below);
                            requires HQ_SCALE_AUTO; not with HQ_DITHER       */
+  HQ_RATE_GIVEN = 16u   /* hq_rate: rice_k and tile_bits are inputs (the
+                           values hq_encode_tiles wrote for these indices);
+                           other calls ignore it                           */
 };
 
 /* Device status bits (OR-ed into *status by kernels). */
@@ -176,8 +179,17 @@ hq_status hq_decode_tiles(const hq_params* p, const int8_t* idx,
  * ceil(tile_bits/32), tile_word_offset[n_tiles] = total words.  A tile that
  * does not fit in capacity_words is not written and sets HQ_ST_STREAM_FULL.
  *
- * idx [n_tiles * tile] int8; coset as for encode (used only when packing);
- * rice_k [n_tiles] uint8, tile_bits [n_tiles] uint32, total_bits: 1 uint64;
+ * With HQ_RATE_GIVEN, rice_k and tile_bits are read instead of computed:
+ * the rate pass then reads 4 bytes per tile instead of the tile's indices,
+ * and the indices are read once, by the packing.  They must be the values
+ * the encoder wrote for these indices; otherwise the stream contents are
+ * unspecified (nothing is accessed outside the buffers, and a tile past
+ * capacity_words still sets HQ_ST_STREAM_FULL).
+ *
+ * idx [n_tiles * tile] int8 (may be NULL with HQ_RATE_GIVEN when not
+ * packing); coset as for encode (used only when packing);
+ * rice_k [n_tiles] uint8, tile_bits [n_tiles] uint32 (outputs, or inputs
+ * with HQ_RATE_GIVEN), total_bits: 1 uint64;
  * tile_word_offset [n_tiles + 1] uint64 (required when packing);
  * workspace: device scratch of at least hq_rate_workspace_bytes(n_tiles)
  * bytes, 8-byte aligned (required when packing; optional otherwise, where it

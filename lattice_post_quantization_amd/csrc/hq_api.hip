@@ -22,7 +22,8 @@ namespace {
 
 using namespace hq;
 
-constexpr uint32_t kKnownFlags = HQ_SCALE_AUTO | HQ_DITHER | HQ_WANT_COORDS | HQ_RATE_CONTROL;
+constexpr uint32_t kKnownFlags =
+    HQ_SCALE_AUTO | HQ_DITHER | HQ_WANT_COORDS | HQ_RATE_CONTROL | HQ_RATE_GIVEN;
 
 bool lattice_ok(int32_t l) { return l == HQ_E8 || l == HQ_D4 || l == HQ_A2 || l == HQ_Z; }
 
@@ -404,10 +405,13 @@ hq_status hq_rate(const hq_params* p, const int8_t* idx, const uint32_t* coset, 
   if (st != HQ_OK) return st;
   if (n_tiles < 0) return HQ_EINVAL;
   if (n_tiles == 0) return HQ_OK;   // zero tiles: a no-op (nothing is written)
-  if (idx == nullptr || rice_k == nullptr || tile_bits == nullptr || total_bits == nullptr)
-    return HQ_EINVAL;
-  if (!aligned16(idx) || ((uintptr_t)total_bits & 7u)) return HQ_EINVAL;
+  const bool given = (p->flags & HQ_RATE_GIVEN) != 0;
   const bool pack = stream_words != nullptr;
+  if ((idx == nullptr && (pack || !given)) || rice_k == nullptr || tile_bits == nullptr ||
+      total_bits == nullptr)
+    return HQ_EINVAL;
+  if (!aligned16(idx) || ((uintptr_t)total_bits & 7u) || ((uintptr_t)tile_bits & 3u))
+    return HQ_EINVAL;
   if (pack) {
     if (tile_word_offset == nullptr || workspace == nullptr) return HQ_EINVAL;
     if (coset_words(p) > 0 && coset == nullptr) return HQ_EINVAL;
@@ -416,8 +420,8 @@ hq_status hq_rate(const hq_params* p, const int8_t* idx, const uint32_t* coset, 
   }
   if (n_tiles > INT64_MAX / p->tile) return HQ_EINVAL;
   if (n_tiles == 0) return HQ_OK;
-  if (!on_device(idx) || !on_device(rice_k) || !on_device(tile_bits) || !on_device(total_bits) ||
-      (status != nullptr && !on_device(status)))
+  if ((idx != nullptr && !on_device(idx)) || !on_device(rice_k) || !on_device(tile_bits) ||
+      !on_device(total_bits) || (status != nullptr && !on_device(status)))
     return HQ_EINVAL;
   if (pack && (!on_device(stream_words) || !on_device(tile_word_offset) ||
                !on_device(workspace) || (coset_words(p) > 0 && !on_device(coset))))
@@ -445,6 +449,7 @@ hq_status hq_rate(const hq_params* p, const int8_t* idx, const uint32_t* coset, 
   a.block_bits = ws ? static_cast<uint64_t*>(workspace) + nb : nullptr;
   a.wave_words = ws ? static_cast<uint64_t*>(workspace) + 2 * nb : nullptr;
   a.status = status;
+  a.given = given ? 1 : 0;
   return launched(launch_rate(a, stream));
 }
 

@@ -73,6 +73,7 @@ struct RateLaunch {
   uint64_t* block_bits;    // workspace: bits per rate block
   uint64_t* wave_words;    // workspace: words per rate wave
   uint32_t* status;
+  int given;               // rice_k and tile_bits are inputs (the encoder's)
 };
 
 struct UnpackLaunch {

@@ -8,7 +8,9 @@
 // packed, Rice-coded lattice-index checkpoint format).
 //
 // Three kernels, each wave owning a contiguous span of tiles (the rate and
-// pack kernels use the same partition):
+// pack kernels use the same partition; with the encoder's rice_k and
+// tile_bits given, a rate kernel that reads only tile_bits replaces the
+// first):
 //   rate_kernel  per tile (16 indices per lane): zigzag bytewise, k from
 //                byte sums over three candidates, tile_bits; per wave the
 //                sum of ceil(tile_bits/32), per block the sums of
@@ -151,6 +153,37 @@ __device__ inline uint64_t wave_sum_u64(uint64_t x) {
   return x;
 }
 
+// A wave's word and bit totals (summed over its lanes) into the workspace:
+// its word count, and its block's word and bit sums (without a workspace,
+// the bit total through one 64-bit atomic per block).  Every thread of the
+// block calls it.
+__device__ inline void rate_sums(const RateLaunch& a, uint64_t words, uint64_t bits,
+                                 int64_t wave, int wl, int lane,
+                                 uint64_t (*blk)[kBlock / 64]) {
+  words = wave_sum_u64(words);
+  bits = wave_sum_u64(bits);
+  if (lane == 0) {
+    if (a.wave_words != nullptr) a.wave_words[wave] = words;
+    blk[0][wl] = words;
+    blk[1][wl] = bits;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t w = 0, b = 0;
+#pragma unroll
+    for (int i = 0; i < kBlock / 64; ++i) {
+      w += blk[0][i];
+      b += blk[1][i];
+    }
+    if (a.block_words != nullptr) {
+      a.block_words[blockIdx.x] = w;
+      a.block_bits[blockIdx.x] = b;
+    } else {
+      atomicAdd((unsigned long long*)a.total_bits, (unsigned long long)b);
+    }
+  }
+}
+
 template <int N>
 __global__ __launch_bounds__(kBlock) void rate_kernel(RateLaunch a) {
   constexpr int G = N / kElemsPerLane;
@@ -188,28 +221,27 @@ __global__ __launch_bounds__(kBlock) void rate_kernel(RateLaunch a) {
       bits += tb;
     }
   }
-  words = wave_sum_u64(words);
-  bits = wave_sum_u64(bits);
-  if (lane == 0) {
-    if (a.wave_words != nullptr) a.wave_words[wave] = words;
-    blk[0][wl] = words;
-    blk[1][wl] = bits;
+  rate_sums(a, words, bits, wave, wl, lane, blk);
+}
+
+// Rate pass with the encoder's rice_k and tile_bits given: the same spans
+// and sums, from tile_bits alone (lanes stride over the wave's tiles).
+template <int N>
+__global__ __launch_bounds__(kBlock) void rate_given_kernel(RateLaunch a) {
+  __shared__ uint64_t blk[2][kBlock / 64];
+  const int lane = threadIdx.x & 63;
+  const int wl = threadIdx.x >> 6;
+  const int64_t wave = (int64_t)blockIdx.x * (kBlock / 64) + wl;
+  const int64_t span = wave_span<N>(a.n_tiles);
+  const int64_t first = wave < rate_waves<N>(a.n_tiles) ? wave * span : a.n_tiles;
+  const int64_t end = first + span < a.n_tiles ? first + span : a.n_tiles;
+  uint64_t words = 0, bits = 0;
+  for (int64_t t = first + lane; t < end; t += 64) {
+    const uint32_t tb = a.tile_bits[t];
+    words += (tb + 31u) / 32u;
+    bits += tb;
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint64_t w = 0, b = 0;
-#pragma unroll
-    for (int i = 0; i < kBlock / 64; ++i) {
-      w += blk[0][i];
-      b += blk[1][i];
-    }
-    if (a.block_words != nullptr) {
-      a.block_words[blockIdx.x] = w;
-      a.block_bits[blockIdx.x] = b;
-    } else {
-      atomicAdd((unsigned long long*)a.total_bits, (unsigned long long)b);
-    }
-  }
+  rate_sums(a, words, bits, wave, wl, lane, blk);
 }
 
 __global__ void zero_u64_kernel(uint64_t* p) { *p = 0; }
@@ -447,7 +479,10 @@ hipError_t launch_n(const RateLaunch& a, hipStream_t s) {
   const int64_t blocks = (waves + kBlock / 64 - 1) / (kBlock / 64);
   if (a.block_words == nullptr)
     hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(1), 0, s, a.total_bits);
-  hipLaunchKernelGGL(rate_kernel<N>, dim3((unsigned)blocks), dim3(kBlock), 0, s, a);
+  if (a.given)
+    hipLaunchKernelGGL(rate_given_kernel<N>, dim3((unsigned)blocks), dim3(kBlock), 0, s, a);
+  else
+    hipLaunchKernelGGL(rate_kernel<N>, dim3((unsigned)blocks), dim3(kBlock), 0, s, a);
   if (a.block_words != nullptr)
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a.block_words, blocks,
                        a.block_bits, a.total_bits);

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libhq.so")
 HQ_OK, HQ_EINVAL, HQ_ERANGE, HQ_EDEVICE, HQ_EUNSUPPORTED = 0, -1, -2, -3, -4
 HQ_Z, HQ_A2, HQ_D4, HQ_E8 = 1, 2, 4, 8
 HQ_F32, HQ_BF16 = 0, 1
-HQ_SCALE_AUTO, HQ_DITHER, HQ_WANT_COORDS, HQ_RATE_CONTROL = 1, 2, 4, 8
+HQ_SCALE_AUTO, HQ_DITHER, HQ_WANT_COORDS, HQ_RATE_CONTROL, HQ_RATE_GIVEN = 1, 2, 4, 8, 16
 HQ_ST_NONFINITE, HQ_ST_OVERFLOW, HQ_ST_STREAM_FULL, HQ_ST_CORRUPT = 1, 2, 4, 8
 
 LATTICES = {"E8": HQ_E8, "D4": HQ_D4, "A2": HQ_A2, "Z": HQ_Z}
@@ -251,15 +251,20 @@ def hq_decode_tiles(idx, coset, scale, lattice="E8", tile=256, rht_seed=0,
 
 
 def hq_rate(idx, coset, lattice="E8", tile=256, pack=False, capacity_words=None,
-            status=None, out=None):
+            status=None, out=None, given=None):
     """Rice parameters and bit lengths per tile; optionally the packed stream.
 
+    given: the encoder's result for these indices (a dict with rice_k and
+    tile_bits, as hq_encode_tiles returns): HQ_RATE_GIVEN, the rate pass
+    then reads tile_bits instead of recomputing both from the indices.
     Returns dict: rice_k, tile_bits, total_bits (int64 device scalar) and, when
     packing, stream (int32 words), tile_word_offset (int64, n_tiles + 1)."""
     _device_tensor(idx, "idx")
     dev = idx.device
     n_tiles = idx.numel() // tile
     o = dict(out or {})
+    if given is not None:
+        o["rice_k"], o["tile_bits"] = given["rice_k"], given["tile_bits"]
     rice_k = o.get("rice_k")
     if rice_k is None:
         rice_k = torch.empty(n_tiles, dtype=torch.uint8, device=dev)
@@ -283,7 +288,7 @@ def hq_rate(idx, coset, lattice="E8", tile=256, pack=False, capacity_words=None,
     ws = o.get("workspace")
     if ws is None:
         ws = torch.empty(max(rate_workspace_bytes(n_tiles), 8), dtype=torch.uint8, device=dev)
-    p = make_params(lattice, tile, 4.0)
+    p = make_params(lattice, tile, 4.0, flags=HQ_RATE_GIVEN if given is not None else 0)
     code = lib().hq_rate(ctypes.byref(p), _ptr(idx), _ptr(coset), n_tiles, _ptr(rice_k),
                          _ptr(tile_bits), _ptr(total), _ptr(stream),
                          int(capacity_words or 0), _ptr(offs), _ptr(ws),

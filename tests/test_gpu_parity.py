@@ -108,6 +108,14 @@ def check_rate(ora, lattice, n, label=""):
     goff = T.host(r["tile_word_offset"])
     assert np.array_equal(goff, off), label + " offsets"
     assert np.array_equal(T.u32(r["stream"])[:off[-1]], words), label + " stream"
+    # the same with the oracle's rice_k and tile_bits given (HQ_RATE_GIVEN)
+    given = {"rice_k": torch.from_numpy(k.astype(np.uint8)).cuda(),
+             "tile_bits": torch.from_numpy(tb.astype(np.uint32).view(np.int32)).cuda()}
+    r = hq.hq_rate(idx, coset, lattice, n, pack=True, given=given)
+    torch.cuda.synchronize()
+    assert int(T.host(r["total_bits"])[0]) == total, label + " total (given)"
+    assert np.array_equal(T.host(r["tile_word_offset"]), off), label + " offsets (given)"
+    assert np.array_equal(T.u32(r["stream"])[:off[-1]], words), label + " stream (given)"
 
 
 # ------------------------------------------------------------------ tests
