@@ -313,19 +313,16 @@ struct BitWriter {
   uint32_t an;
   uint32_t wp;
 
-  __device__ inline void drain() {
-    while (an >= 32u) {
+  // nbits <= 32 bits of v (higher bits zero); an < 32 on entry and exit
+  __device__ inline void put(uint32_t v, uint32_t nbits) {
+    acc |= (uint64_t)v << an;
+    an += nbits;
+    if (an >= 32u) {
       atomicOr(&w[wp], (uint32_t)acc);
       acc >>= 32;
       an -= 32u;
       ++wp;
     }
-  }
-  // nbits <= 32 bits of v (higher bits zero)
-  __device__ inline void put(uint32_t v, uint32_t nbits) {
-    acc |= (uint64_t)v << an;
-    an += nbits;
-    drain();
   }
   __device__ inline void flush() {
     if (an > 0u) atomicOr(&w[wp], (uint32_t)acc);
@@ -378,7 +375,9 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(RateLaunch a) {
     const bool live = tile < end;
     const uint4 cq = in.q;
     const uint32_t ck = in.k, tb = live ? in.tb : 0u;
-    const uint32_t nwords = (tb + 31u) / 32u;
+    // (given tile_bits past the tile's LDS words are clamped there; the
+    // codes of such a tile are not written, see below)
+    const uint32_t nwords = (tb + 31u) / 32u < (uint32_t)W ? (tb + 31u) / 32u : (uint32_t)W;
     // word offsets of the pass's tiles: group g's count sits in lane g G
     uint64_t off = base, pass_words = 0;
 #pragma unroll
@@ -397,7 +396,7 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(RateLaunch a) {
     uint32_t k = 0;
     uint32_t zz[4] = {0u, 0u, 0u, 0u};
     if (live) {
-      k = ck;
+      k = ck < 8u ? ck : 8u;   // (a given k above 8 marks the tile corrupt below)
       zeta4(cq, zz);
     }
     // this lane's payload bits: sum floor(zeta / 2^k) + 16 (1 + k)
@@ -407,6 +406,11 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(RateLaunch a) {
     for (int j = 0; j < 4; ++j) qs = byte_sum((zz[j] >> k) & m, qs);
     const uint32_t T = live ? qs + 16u * (1u + k) : 0u;
     const uint32_t pos = 4u + (uint32_t)a.coset_bits + row_incl_scan<G>(T, r) - T;
+    // rice_k and tile_bits computed here always hold the codes; given ones
+    // that do not (k > 8, or codes past tile_bits or past the tile's LDS
+    // words) leave the lane's codes unwritten and mark the tile corrupt
+    const bool fits = !a.given || (ck <= 8u && pos + T <= tb && tb <= 32u * (uint32_t)W);
+    if (live && !fits) set_status(a.status, HQ_ST_CORRUPT);
     if (live) {
       if (r == 0) {
         // header: k (4 bits), then the coset bits
@@ -418,31 +422,38 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(RateLaunch a) {
         }
         h.flush();
       }
-      const uint32_t rmask = (1u << k) - 1u;
-      uint32_t pb = pos;
+      // the lane's 16 codes through one 64-bit accumulator: a word leaves
+      // (OR-ed into LDS) once full, so a lane issues about one LDS operation
+      // per 32 bits; its first and last words may be shared with its
+      // neighbours, which the OR allows
+      if (fits) {
+        const uint32_t rmask = (1u << k) - 1u;
+        uint32_t pb = pos;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t zeta = __builtin_amdgcn_ubfe(zz[i >> 2], 8 * (i & 3), 8);
-        const uint32_t q = zeta >> k, rem = zeta & rmask, len = q + 1u + k;
-        if (len <= 32u) {
-          // q ones, a zero, the k low bits: ((2 rem + 1) << q) - 1, at bit pb
-          const uint32_t c = (((rem << 1) | 1u) << q) - 1u;
-          const uint64_t v = (uint64_t)c << (pb & 31u);
-          uint32_t* w = tw + (pb >> 5);
-          atomicOr(w, (uint32_t)v);
-          atomicOr(w + 1, (uint32_t)(v >> 32));
-        } else {
-          BitWriter bw{tw, 0, pb & 31u, pb >> 5};
-          uint32_t qq = q;
-          while (qq > 0u) {
-            const uint32_t t = qq < 32u ? qq : 32u;
-            bw.put(t == 32u ? 0xFFFFFFFFu : (1u << t) - 1u, t);
-            qq -= t;
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t zeta = __builtin_amdgcn_ubfe(zz[i >> 2], 8 * (i & 3), 8);
+          const uint32_t q = zeta >> k, rem = zeta & rmask, len = q + 1u + k;
+          if (len <= 32u) {
+            // q ones, a zero, the k low bits: ((2 rem + 1) << q) - 1, at bit
+            // pb, OR-ed into the (at most two) words it touches
+            const uint32_t c = (((rem << 1) | 1u) << q) - 1u;
+            const uint64_t v = (uint64_t)c << (pb & 31u);
+            uint32_t* w = tw + (pb >> 5);
+            atomicOr(w, (uint32_t)v);
+            atomicOr(w + 1, (uint32_t)(v >> 32));
+          } else {
+            BitWriter bw{tw, 0, pb & 31u, pb >> 5};
+            uint32_t qq = q;
+            while (qq > 0u) {
+              const uint32_t t = qq < 32u ? qq : 32u;
+              bw.put(t == 32u ? 0xFFFFFFFFu : (1u << t) - 1u, t);
+              qq -= t;
+            }
+            bw.put(rem << 1, 1u + k);
+            bw.flush();
           }
-          bw.put(rem << 1, 1u + k);
-          bw.flush();
+          pb += len;
         }
-        pb += len;
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

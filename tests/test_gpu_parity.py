@@ -498,6 +498,42 @@ def test_unpack_any_k_long_codes_and_corrupt_tiles():
     assert np.array_equal(T.host(g["idx"]).astype(np.int64)[good], idx[good])
 
 
+def test_rate_given_values_that_do_not_hold_the_codes():
+    """HQ_RATE_GIVEN with rice_k / tile_bits that are not the encoder's: a k
+    above 8, a k one below the optimum (longer codes than tile_bits), and
+    tile_bits past what a tile can need.  Those tiles set HQ_ST_CORRUPT and
+    leave their codes unwritten; every other tile's words are the oracle's."""
+    rng = np.random.default_rng(47)
+    n, nt = 256, 60
+    x = rng.standard_normal((nt, n))
+    bits = workloads.f32_to_bf16_bits(x.astype(np.float32))
+    ora = codec.encode(workloads.bf16_bits_to_f64(bits), "E8", n, 4.0, rht_seed=2)
+    k, tb, total, words, off = codec.rate(ora["idx"], ora["coset"], "E8", n)
+    gk, gtb = k.copy(), tb.copy()
+    j = int(np.nonzero(k >= 1)[0][3])
+    gk[7] = 12                                   # k above 8
+    gk[j] = k[j] - 1                             # first minimum: k - 1 costs more
+    gtb[40] = 1 << 20                            # past any tile's words
+    idx = torch.from_numpy(ora["idx"].astype(np.int8)).cuda()
+    coset = torch.from_numpy(ora["coset"].astype(np.uint32).view(np.int32)).cuda()
+    given = {"rice_k": torch.from_numpy(gk.astype(np.uint8)).cuda(),
+             "tile_bits": torch.from_numpy(gtb.astype(np.uint32).view(np.int32)).cuda()}
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    say("case: rate with given values that do not hold the codes")
+    r = hq.hq_rate(idx, coset, "E8", n, pack=True, given=given, status=st,
+                   capacity_words=int(off[-1]) + (1 << 16))
+    torch.cuda.synchronize()
+    assert int(st.item()) & hq.HQ_ST_CORRUPT
+    goff = T.host(r["tile_word_offset"])
+    gw = T.u32(r["stream"])
+    bad = {7, j, 40}
+    for t in range(nt):
+        if t in bad:
+            continue
+        w = gw[goff[t]:goff[t] + (off[t + 1] - off[t])]
+        assert np.array_equal(w, words[off[t]:off[t + 1]]), t
+
+
 @pytest.mark.parametrize("m", [1, 3, 8])
 def test_gemv_parity(m):
     """hq_gemv against the oracle: y = W x with W the oracle's fp64 decode of
