@@ -90,7 +90,9 @@ enum {
                              index that would leave int8)                 */
   HQ_ST_STREAM_FULL = 4u, /* hq_rate: packed stream exceeded capacity     */
   HQ_ST_CORRUPT = 8u      /* hq_unpack: a tile's codes overran its words,
-                             or decoded to a value outside int8           */
+                             or decoded to a value outside int8; hq_rate
+                             with HQ_RATE_GIVEN: given values that cannot
+                             hold a tile's codes                          */
 };
 
 typedef struct {
@@ -183,8 +185,10 @@ hq_status hq_decode_tiles(const hq_params* p, const int8_t* idx,
  * the rate pass then reads 4 bytes per tile instead of the tile's indices,
  * and the indices are read once, by the packing.  They must be the values
  * the encoder wrote for these indices; otherwise the stream contents are
- * unspecified (nothing is accessed outside the buffers, and a tile past
- * capacity_words still sets HQ_ST_STREAM_FULL).
+ * unspecified, nothing is accessed outside the buffers, a tile whose given
+ * k exceeds 8 or whose codes do not fit its given tile_bits sets
+ * HQ_ST_CORRUPT (its codes are not written), and a tile past
+ * capacity_words still sets HQ_ST_STREAM_FULL.
  *
  * idx [n_tiles * tile] int8 (may be NULL with HQ_RATE_GIVEN when not
  * packing); coset as for encode (used only when packing);
