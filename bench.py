@@ -340,8 +340,9 @@ def secondary(layer0, bps, dev):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(tiles are independent; see DESIGN.md for how it would shard)", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (tiles are "
+              "independent, so a stack shards by layer or row block with no exchange)",
+              file=sys.stderr)
         sys.exit(2)
 
     cpu = cpu_baseline(args.cpu_sample_stride, args.bps) if args.cpu_baseline else None

@@ -60,7 +60,7 @@ enum {
   HQ_EINVAL = -1,       /* bad argument (null pointer, size, tile, dtype)  */
   HQ_ERANGE = -2,       /* auto scale cannot keep indices inside int8      */
   HQ_EDEVICE = -3,      /* a HIP call or kernel launch failed              */
-  HQ_EUNSUPPORTED = -4  /* a valid combination this build does not offer   */
+  HQ_EUNSUPPORTED = -4  /* a valid combination the library does not offer */
 };
 
 /* Lattice; the value is the lattice dimension. [arXiv abstract] item (ii). */
