@@ -234,6 +234,28 @@ hq_status hq_unpack(const hq_params* p, const uint32_t* stream_words,
                     uint32_t* status, hipStream_t stream);
 
 /*
+ * hq_unpack_batch - hq_unpack for `count` packed matrices that share p (a
+ * layer's projections), enqueued as one launch per group of up to eight.
+ * The decoder runs one lane per tile, so a single small matrix occupies a
+ * fraction of the GPU; a layer's matrices decoded together fill it.  Same
+ * passages, arguments per item and results (bit for bit) as one hq_unpack
+ * call per item.  `items` is a host array read during the call; every item
+ * is validated and nothing is enqueued unless all pass; an item with
+ * n_tiles 0 is skipped.
+ */
+typedef struct {
+  const uint32_t* stream_words;        /* device, read only in the ranges  */
+  const uint64_t* tile_word_offset;    /* [n_tiles + 1]                    */
+  int64_t n_tiles;
+  int8_t* idx;                         /* [n_tiles * tile], 16-byte aligned */
+  uint32_t* coset;                     /* [n_tiles * hq_coset_words(p)]    */
+  uint8_t* rice_k;                     /* [n_tiles] or NULL                */
+} hq_unpack_item;
+
+hq_status hq_unpack_batch(const hq_params* p, int32_t count, const hq_unpack_item* items,
+                          uint32_t* status, hipStream_t stream);
+
+/*
  * hq_gemv - y = W x for E8-coded weights, without forming W: the consumer
  * of the format ([issue] "Is your feature request related to a problem?":
  * decode must be usable at inference; [ICLR abstract]: algebraic decoding).

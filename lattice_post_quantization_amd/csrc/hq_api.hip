@@ -453,6 +453,67 @@ hq_status hq_rate(const hq_params* p, const int8_t* idx, const uint32_t* coset, 
   return launched(launch_rate(a, stream));
 }
 
+namespace {
+
+// Validation of one packed matrix (n_tiles > 0).
+hq_status check_unpack(const hq_params* p, const hq_unpack_item& it) {
+  if (it.stream_words == nullptr || it.tile_word_offset == nullptr || it.idx == nullptr)
+    return HQ_EINVAL;
+  if (coset_words(p) > 0 && it.coset == nullptr) return HQ_EINVAL;
+  if (!aligned16(it.idx) || ((uintptr_t)it.tile_word_offset & 7u) ||
+      ((uintptr_t)it.stream_words & 3u) || ((uintptr_t)it.coset & 3u))
+    return HQ_EINVAL;
+  if (it.n_tiles > INT64_MAX / p->tile) return HQ_EINVAL;
+  if (!on_device(it.stream_words) || !on_device(it.tile_word_offset) || !on_device(it.idx) ||
+      (coset_words(p) > 0 && !on_device(it.coset)) ||
+      (it.rice_k != nullptr && !on_device(it.rice_k)))
+    return HQ_EINVAL;
+  return HQ_OK;
+}
+
+}  // namespace
+
+hq_status hq_unpack_batch(const hq_params* p, int32_t count, const hq_unpack_item* items,
+                          uint32_t* status, hipStream_t stream) {
+  hq_status st = check_params(p);
+  if (st != HQ_OK) return st;
+  if (count < 0 || (count > 0 && items == nullptr)) return HQ_EINVAL;
+  for (int32_t i = 0; i < count; ++i) {
+    if (items[i].n_tiles < 0) return HQ_EINVAL;
+    if (items[i].n_tiles == 0) continue;   // skipped: nothing is read or written
+    st = check_unpack(p, items[i]);
+    if (st != HQ_OK) return st;
+  }
+  if (status != nullptr && !on_device(status)) return HQ_EINVAL;
+  // launches of up to kUnpackMaxItems matrices, waves numbered across them
+  UnpackLaunch a;
+  memset(&a, 0, sizeof(a));
+  a.tile = p->tile;
+  a.coset_bits = coset_bits(p);
+  a.coset_words = coset_words(p);
+  a.status = status;
+  for (int32_t i = 0; i <= count; ++i) {
+    if ((i == count || a.n == kUnpackMaxItems) && a.n > 0) {
+      if (launch_unpack(a, stream) != hipSuccess) return HQ_EDEVICE;
+      a.n = 0;
+      a.n_waves = 0;
+    }
+    if (i == count) break;
+    const hq_unpack_item& it = items[i];
+    if (it.n_tiles == 0) continue;
+    UnpackItem& u = a.it[a.n++];
+    u.stream = it.stream_words;
+    u.tile_word_offset = it.tile_word_offset;
+    u.n_tiles = it.n_tiles;
+    u.idx = it.idx;
+    u.coset = a.coset_words > 0 ? it.coset : nullptr;
+    u.rice_k = it.rice_k;
+    u.wave0 = a.n_waves;
+    a.n_waves += (it.n_tiles + 63) / 64;
+  }
+  return HQ_OK;
+}
+
 hq_status hq_unpack(const hq_params* p, const uint32_t* stream_words,
                     const uint64_t* tile_word_offset, int64_t n_tiles, int8_t* idx,
                     uint32_t* coset, uint8_t* rice_k, uint32_t* status, hipStream_t stream) {
@@ -460,29 +521,8 @@ hq_status hq_unpack(const hq_params* p, const uint32_t* stream_words,
   if (st != HQ_OK) return st;
   if (n_tiles < 0) return HQ_EINVAL;
   if (n_tiles == 0) return HQ_OK;   // zero tiles: a no-op (nothing is read or written)
-  if (stream_words == nullptr || tile_word_offset == nullptr || idx == nullptr) return HQ_EINVAL;
-  if (coset_words(p) > 0 && coset == nullptr) return HQ_EINVAL;
-  if (!aligned16(idx) || ((uintptr_t)tile_word_offset & 7u) || ((uintptr_t)stream_words & 3u) ||
-      ((uintptr_t)coset & 3u))
-    return HQ_EINVAL;
-  if (n_tiles > INT64_MAX / p->tile) return HQ_EINVAL;
-  if (!on_device(stream_words) || !on_device(tile_word_offset) || !on_device(idx) ||
-      (coset_words(p) > 0 && !on_device(coset)) || (rice_k != nullptr && !on_device(rice_k)) ||
-      (status != nullptr && !on_device(status)))
-    return HQ_EINVAL;
-  UnpackLaunch a;
-  memset(&a, 0, sizeof(a));
-  a.stream = stream_words;
-  a.tile_word_offset = tile_word_offset;
-  a.n_tiles = n_tiles;
-  a.tile = p->tile;
-  a.coset_bits = coset_bits(p);
-  a.coset_words = coset_words(p);
-  a.idx = idx;
-  a.coset = coset_words(p) > 0 ? coset : nullptr;
-  a.rice_k = rice_k;
-  a.status = status;
-  return launched(launch_unpack(a, stream));
+  const hq_unpack_item it{stream_words, tile_word_offset, n_tiles, idx, coset, rice_k};
+  return hq_unpack_batch(p, 1, &it, status, stream);
 }
 
 size_t hq_gemv_workspace_bytes(int64_t rows, int64_t cols, int32_t m) {

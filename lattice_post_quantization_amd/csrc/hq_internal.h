@@ -76,17 +76,28 @@ struct RateLaunch {
   int given;               // rice_k and tile_bits are inputs (the encoder's)
 };
 
-struct UnpackLaunch {
+// One packed matrix of an unpack launch; wave0 numbers its first wave (64
+// tiles per wave) among the launch's waves.
+struct UnpackItem {
   const uint32_t* stream;
   const uint64_t* tile_word_offset;
   int64_t n_tiles;
-  int tile;
-  int coset_bits;       // per tile
-  int coset_words;      // per tile
   int8_t* idx;
   uint32_t* coset;      // nullptr iff coset_words == 0
   uint8_t* rice_k;      // may be nullptr
+  int64_t wave0;
+};
+
+constexpr int kUnpackMaxItems = 8;
+
+struct UnpackLaunch {
+  int n;                // items in use
+  int tile;
+  int coset_bits;       // per tile
+  int coset_words;      // per tile
   uint32_t* status;     // may be nullptr
+  int64_t n_waves;      // waves of all items
+  UnpackItem it[kUnpackMaxItems];
 };
 
 // One matrix of an hq_gemv batch.  The workspace pointers and the plan are

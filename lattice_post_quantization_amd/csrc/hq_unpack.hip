@@ -15,7 +15,9 @@
 // into LDS with coalesced loads and decodes from there with branch-free
 // refills; otherwise it reads global memory.  Decoded bytes go to a 4 KB LDS
 // buffer (64 bytes of each tile) that is written back 64 contiguous bytes
-// per tile, sixteen tiles per store instruction.
+// per tile, sixteen tiles per store instruction.  One launch covers up to
+// eight packed matrices (a layer's projections), its waves running over
+// them in order, so that small matrices together fill the GPU.
 #include "hq.h"
 #include "hq_device.h"
 #include "hq_internal.h"
@@ -252,9 +254,9 @@ constexpr int kSegWords = 2560;       // staged stream words per wave (10 KB)
 // (64 bytes of each tile at a time; writer lane L keeps chunk c at slot
 // 4 L + ((c ^ (L >> 2)) & 3), so each 16-lane group writes 16 bank groups).
 template <int N, typename Reader>
-__device__ inline void decode_tiles(const UnpackLaunch& a, Reader& br, int64_t tile, bool live,
-                                    int64_t wave_tile0, uint32_t live_in_wave, int lane,
-                                    uint4* st, bool& bad) {
+__device__ inline void decode_tiles(const UnpackLaunch& a, const UnpackItem& it, Reader& br,
+                                    int64_t tile, bool live, int64_t wave_tile0,
+                                    uint32_t live_in_wave, int lane, uint4* st, bool& bad) {
   br.refill();
   bad |= br.nb < 4u;
   const uint32_t k = br.take(4);
@@ -263,11 +265,11 @@ __device__ inline void decode_tiles(const UnpackLaunch& a, Reader& br, int64_t t
     br.refill();
     bad |= br.nb < (uint32_t)nbits;
     const uint32_t cw = br.take((uint32_t)nbits);
-    if (live) a.coset[tile * a.coset_words + j] = cw;
+    if (live) it.coset[tile * a.coset_words + j] = cw;
   }
-  if (live && a.rice_k != nullptr) a.rice_k[tile] = (uint8_t)k;
+  if (live && it.rice_k != nullptr) it.rice_k[tile] = (uint8_t)k;
 
-  const auto rs = out_rsrc(a.idx + wave_tile0 * N, live_in_wave * (uint32_t)N);
+  const auto rs = out_rsrc(it.idx + wave_tile0 * N, live_in_wave * (uint32_t)N);
 #pragma unroll 1
   for (int part = 0; part < N / 64; ++part) {
 #pragma unroll 1
@@ -302,18 +304,26 @@ __global__ __launch_bounds__(kUnpackBlock) void unpack_kernel(UnpackLaunch a) {
   __shared__ uint4 stage[kUnpackBlock / 64][256];   // per wave: 4 chunks of 64 tiles
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t wave_tile0 = ((int64_t)blockIdx.x * kUnpackBlock) + (int64_t)wave * 64;
-  if (wave_tile0 >= a.n_tiles) return;   // whole waves only
+  // the launch's waves run over its items in order, 64 tiles each
+  const int64_t gw = (int64_t)blockIdx.x * (kUnpackBlock / 64) + wave;
+  if (gw >= a.n_waves) return;   // whole waves only
+  int item = 0;
+#pragma unroll
+  for (int k = 1; k < kUnpackMaxItems; ++k)
+    if (k < a.n && gw >= a.it[k].wave0) item = k;
+  item = __builtin_amdgcn_readfirstlane(item);
+  const UnpackItem& it = a.it[item];
+  const int64_t wave_tile0 = (gw - it.wave0) * 64;
   const int64_t tile = wave_tile0 + lane;
-  const bool live = tile < a.n_tiles;
-  const int64_t rem_tiles = a.n_tiles - wave_tile0;
+  const bool live = tile < it.n_tiles;
+  const int64_t rem_tiles = it.n_tiles - wave_tile0;
   const uint32_t live_in_wave = (uint32_t)(rem_tiles < 64 ? rem_tiles : 64);
 
   bool bad = false;
   uint64_t w0 = 0, w1 = 0;
   if (live) {
-    w0 = a.tile_word_offset[tile];
-    w1 = a.tile_word_offset[tile + 1];
+    w0 = it.tile_word_offset[tile];
+    w1 = it.tile_word_offset[tile + 1];
     if (w1 < w0) {
       bad = true;
       w1 = w0;
@@ -322,14 +332,14 @@ __global__ __launch_bounds__(kUnpackBlock) void unpack_kernel(UnpackLaunch a) {
   // When every range is in order, the wave's words [first start, last end)
   // are exactly the union of its tiles' ranges; if they fit, they are staged
   // in LDS and the whole wave decodes from there.
-  const uint64_t seg_base = a.tile_word_offset[wave_tile0];
-  const uint64_t seg_end = a.tile_word_offset[wave_tile0 + live_in_wave];
+  const uint64_t seg_base = it.tile_word_offset[wave_tile0];
+  const uint64_t seg_end = it.tile_word_offset[wave_tile0 + live_in_wave];
   const bool staged = !__any(bad) && seg_end >= seg_base &&
                       seg_end - seg_base <= (uint64_t)kSegWords;   // uniform
   const lds_u32* sw = (const lds_u32*)seg[wave];
   const uint32_t nw = staged ? (uint32_t)(seg_end - seg_base) : 0u;
   if (staged) {
-    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(a.stream) + seg_base,
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(it.stream) + seg_base,
                                                       (short)0, (int)(nw * 4u), 0x00020000);
     for (uint32_t j = 0; j < nw; j += 64)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(seg[wave] + j), 4,
@@ -339,11 +349,11 @@ __global__ __launch_bounds__(kUnpackBlock) void unpack_kernel(UnpackLaunch a) {
     wave_lds_sync();
     LdsReader br;
     br.init(sw, (uint32_t)(w0 - seg_base), (uint32_t)(w1 - seg_base), nw > 0 ? nw : 1u);
-    decode_tiles<N>(a, br, tile, live, wave_tile0, live_in_wave, lane, stage[wave], bad);
+    decode_tiles<N>(a, it, br, tile, live, wave_tile0, live_in_wave, lane, stage[wave], bad);
   } else {
     BitReader<false> br;
-    br.init(a.stream, sw, seg_base, w0, w1);
-    decode_tiles<N>(a, br, tile, live, wave_tile0, live_in_wave, lane, stage[wave], bad);
+    br.init(it.stream, sw, seg_base, w0, w1);
+    decode_tiles<N>(a, it, br, tile, live, wave_tile0, live_in_wave, lane, stage[wave], bad);
   }
   if (live && bad) set_status(a.status, HQ_ST_CORRUPT);
 }
@@ -351,7 +361,7 @@ __global__ __launch_bounds__(kUnpackBlock) void unpack_kernel(UnpackLaunch a) {
 }  // namespace
 
 hipError_t launch_unpack(const UnpackLaunch& a, hipStream_t s) {
-  const int64_t blocks = (a.n_tiles + kUnpackBlock - 1) / kUnpackBlock;
+  const int64_t blocks = (a.n_waves + kUnpackBlock / 64 - 1) / (kUnpackBlock / 64);
   switch (a.tile) {
     case 64:
       hipLaunchKernelGGL(unpack_kernel<64>, dim3((unsigned)blocks), dim3(kUnpackBlock), 0, s, a);

@@ -80,6 +80,7 @@ _SIGNATURES = {
     "hq_decode_tiles": (_I32, [_PP, _P, _P, _P, _I64, _I64, _P, _I32, _P, _P]),
     "hq_rate": (_I32, [_PP, _P, _P, _I64, _P, _P, _P, _P, _U64, _P, _P, _SZ, _P, _P]),
     "hq_unpack": (_I32, [_PP, _P, _P, _I64, _P, _P, _P, _P, _P]),
+    "hq_unpack_batch": (_I32, [_PP, _I32, _P, _P, _P]),
     "hq_gemv": (_I32, [_PP, _P, _P, _P, _I64, _I64, _P, _I32, _P, _P, _SZ, _P, _P]),
     "hq_gemv_workspace_bytes": (_SZ, [_I64, _I64, _I32]),
     "hq_gemv_batch": (_I32, [_PP, _I32, _P, _I32, _P, _SZ, _P, _P]),
@@ -326,6 +327,47 @@ def hq_unpack(stream, tile_word_offset, lattice="E8", tile=256, status=None, out
                            _stream(dev))
     _check(code, "hq_unpack")
     return {"idx": idx, "coset": coset if nw else None, "rice_k": rice_k}
+
+
+class UnpackItem(ctypes.Structure):
+    _fields_ = [("stream_words", ctypes.c_void_p), ("tile_word_offset", ctypes.c_void_p),
+                ("n_tiles", ctypes.c_int64), ("idx", ctypes.c_void_p),
+                ("coset", ctypes.c_void_p), ("rice_k", ctypes.c_void_p)]
+
+
+def hq_unpack_batch(packs, lattice="E8", tile=256, status=None, outs=None):
+    """hq_unpack for several packed matrices sharing lattice and tile, in one
+    call (one launch per group of eight).  packs: dicts with "stream" and
+    "tile_word_offset" (as hq_rate returns).  Returns a list of dicts like
+    hq_unpack's; outs may supply their tensors."""
+    nw = coset_words(lattice, tile)
+    res, items = [], []
+    dev = None
+    for i, pk in enumerate(packs):
+        stream = _device_tensor(pk["stream"], "stream")
+        offs = _device_tensor(pk["tile_word_offset"], "tile_word_offset")
+        dev = stream.device
+        n_tiles = offs.numel() - 1
+        o = dict((outs[i] if outs is not None else None) or {})
+        idx = o.get("idx")
+        if idx is None:
+            idx = torch.empty((n_tiles, tile), dtype=torch.int8, device=dev)
+        coset = o.get("coset")
+        if coset is None and nw:
+            coset = torch.empty((n_tiles, nw), dtype=torch.int32, device=dev)
+        rice_k = o.get("rice_k")
+        if rice_k is None:
+            rice_k = torch.empty(n_tiles, dtype=torch.uint8, device=dev)
+        items.append(UnpackItem(stream.data_ptr(), offs.data_ptr(), n_tiles, idx.data_ptr(),
+                                coset.data_ptr() if nw else None, rice_k.data_ptr()))
+        res.append({"idx": idx, "coset": coset if nw else None, "rice_k": rice_k})
+    if not items:
+        return res
+    arr = (UnpackItem * len(items))(*items)
+    p = make_params(lattice, tile, 4.0)
+    code = lib().hq_unpack_batch(ctypes.byref(p), len(items), arr, _ptr(status), _stream(dev))
+    _check(code, "hq_unpack_batch")
+    return res
 
 
 def hq_gemv(idx, coset, scale, x, rht_seed=0, out=None, workspace=None):

@@ -230,6 +230,17 @@ def test_unpack_validation_codes():
     bad = hq.make_params("E8", 100, 4.0)
     assert lib.hq_unpack(ctypes.byref(bad), FAKE, FAKE, 1, FAKE, FAKE, None, None,
                          None) == hq.HQ_EINVAL
+    # the batch form: empty items are skipped, a bad item refuses the call
+    Item = hq.UnpackItem
+    empty = (Item * 2)(Item(None, None, 0, None, None, None), Item(None, None, 0, None, None, None))
+    assert lib.hq_unpack_batch(ctypes.byref(p), 2, empty, None, None) == hq.HQ_OK
+    assert lib.hq_unpack_batch(ctypes.byref(p), 0, None, None, None) == hq.HQ_OK
+    assert lib.hq_unpack_batch(ctypes.byref(p), -1, empty, None, None) == hq.HQ_EINVAL
+    assert lib.hq_unpack_batch(ctypes.byref(p), 1, None, None, None) == hq.HQ_EINVAL
+    mixed = (Item * 2)(Item(None, None, 0, None, None, None), Item(None, FAKE, 3, FAKE, FAKE, None))
+    assert lib.hq_unpack_batch(ctypes.byref(p), 2, mixed, None, None) == hq.HQ_EINVAL
+    neg = (Item * 1)(Item(FAKE, FAKE, -2, FAKE, FAKE, None))
+    assert lib.hq_unpack_batch(ctypes.byref(p), 1, neg, None, None) == hq.HQ_EINVAL
 
 
 def test_gemv_validation_codes():

@@ -445,6 +445,48 @@ def test_unpack_parity(lattice, n):
         _check_unpacked(g2, ref_idx, ref_cos, ref_k, lattice, n, label + " (gpu pack)")
 
 
+@pytest.mark.parametrize("lattice,n", [("E8", 256), ("A2", 128)])
+def test_unpack_batch_matches_oracle_and_single_calls(lattice, n):
+    """hq_unpack_batch over eleven packed matrices (more than one launch of
+    eight, one empty, ragged tile counts from 1 to 1300): each item gives
+    the oracle's indices, coset bits and k, the same bytes as one hq_unpack
+    call, and an empty item is skipped."""
+    from oracle import rice
+    rng = np.random.default_rng(53)
+    cb = codec.coset_bits_per_tile(lattice, n)
+    counts = [7, 0, 64, 65, 300, 1, 129, 1300, 33, 200, 2]
+    packs, refs = [], []
+    for i, nt in enumerate(counts):
+        if nt == 0:
+            refs.append(None)
+            packs.append({"stream": torch.zeros(1, dtype=torch.int32, device="cuda"),
+                          "tile_word_offset": torch.zeros(1, dtype=torch.int64, device="cuda")})
+            continue
+        w = rng.standard_normal((nt, n)) * 0.02
+        w[:, 5] *= 100.0
+        xh = workloads.bf16_bits_to_f64(workloads.f32_to_bf16_bits(w.astype(np.float32)))
+        ora = codec.encode(xh, lattice, n, 3.0 + (i % 3), rht_seed=i)
+        k, tb, total, words, off = codec.rate(ora["idx"], ora["coset"], lattice, n)
+        refs.append(rice.unpack(words, off, n, cb))
+        wd, od = _stream_dev(words, off)
+        packs.append({"stream": wd, "tile_word_offset": od})
+    say("case: unpack batch of %d matrices, %s/%d" % (len(counts), lattice, n))
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    got = hq.hq_unpack_batch(packs, lattice, n, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    for i, (g, ref) in enumerate(zip(got, refs)):
+        if ref is None:
+            assert g["idx"].numel() == 0
+            continue
+        _check_unpacked(g, ref[0], ref[1], ref[2], lattice, n, "batch item %d" % i)
+        one = hq.hq_unpack(packs[i]["stream"], packs[i]["tile_word_offset"], lattice, n)
+        torch.cuda.synchronize()
+        assert torch.equal(one["idx"], g["idx"]) and torch.equal(one["rice_k"], g["rice_k"]), i
+        if cb:
+            assert torch.equal(one["coset"], g["coset"]), i
+
+
 def _forced_k_stream(idx, coset_rows, ks):
     """Packed words of tiles coded with the given k (not the optimal one),
     through the oracle's own tile bit-string writer."""
