@@ -314,6 +314,37 @@ hq_status hq_gemv_batch(const hq_params* p, int32_t count, const hq_gemv_item* i
 size_t hq_gemv_batch_workspace_bytes(int32_t count, const hq_gemv_item* items, int32_t m);
 
 /*
+ * hq_gemm - Y = W X^T for many vectors on the bf16 matrix cores, from the
+ * stored indices of W: the GEMM counterpart of hq_gemv (same passages,
+ * same W).  Per 256-column slice, (Delta / 32) <P, H (s (.) x)>: the lattice
+ * points |P| <= 255 are exact in bf16, the rotated inputs H (s (.) x) are
+ * formed in fp64 and held as two bf16 terms (their rounding and the
+ * rounding of the rest, |error| <= 2^-17 of each value), the products are
+ * exact and accumulate in fp32 inside the MFMA; each slice's sum is scaled
+ * by its tile's Delta / 32 and added in fp32.  Deterministic.
+ *
+ * p: lattice E8, tile 256, rht_seed of the encode; no dither.
+ * idx [rows*cols] int8 (16-byte aligned), coset [n_tiles] words, scale
+ * [n_tiles] fp32 as for hq_gemv; cols a multiple of 256 and at most 2^22,
+ * rows at most 2^23; x [m][cols] fp32 (16-byte aligned), 1 <= m <= 65536
+ * with m cols and m rows at most 2^31; y [m][rows] fp32 out; workspace:
+ * device scratch of at least hq_gemm_workspace_bytes(rows, cols, m) bytes,
+ * 16-byte aligned.  Errors as for hq_gemv (HQ_EINVAL for sizes out of
+ * range).
+ */
+hq_status hq_gemm(const hq_params* p, const int8_t* idx, const uint32_t* coset,
+                  const float* scale, int64_t rows, int64_t cols, const float* x,
+                  int32_t m, float* y, void* workspace, size_t workspace_bytes,
+                  uint32_t* status, hipStream_t stream);
+
+/* Device workspace bytes hq_gemm needs: the rotated inputs as two bf16
+   terms (4 m cols bytes) and, when a small matrix splits its slices over
+   several blocks, their partial sums (4 m rows bytes per range, added in
+   range order; the split is a function of the sizes alone, so results
+   repeat bit for bit); 0 for invalid sizes. */
+size_t hq_gemm_workspace_bytes(int64_t rows, int64_t cols, int32_t m);
+
+/*
  * hq_kv_scores - attention scores of queries against one head's compressed
  * keys: scores[j][k] = q_j . khat_k, khat_k the key hq_decode_tiles would
  * reconstruct (dither subtracted), without forming khat.

@@ -554,6 +554,53 @@ bool gemv_on_device(const hq_gemv_item& it) {
 
 }  // namespace
 
+size_t hq_gemm_workspace_bytes(int64_t rows, int64_t cols, int32_t m) {
+  if (rows <= 0 || rows > kGemmMaxRows || cols <= 0 || cols % 256 != 0 || cols > kGemmMaxCols ||
+      m < 1 || m > kGemmMaxVecs || m * cols > kGemmMaxProduct || m * rows > kGemmMaxProduct)
+    return 0;
+  return gemm_workspace(rows, cols, m);
+}
+
+hq_status hq_gemm(const hq_params* p, const int8_t* idx, const uint32_t* coset, const float* scale,
+                  int64_t rows, int64_t cols, const float* x, int32_t m, float* y,
+                  void* workspace, size_t workspace_bytes, uint32_t* status, hipStream_t stream) {
+  (void)status;
+  hq_status st = check_params(p);
+  if (st != HQ_OK) return st;
+  if (p->lattice != HQ_E8 || p->tile != 256 || (p->flags & HQ_DITHER)) return HQ_EUNSUPPORTED;
+  if (rows < 0 || cols < 0 || cols % 256 != 0 || m < 1) return HQ_EINVAL;
+  if (rows > kGemmMaxRows || cols > kGemmMaxCols || m > kGemmMaxVecs ||
+      m * cols > kGemmMaxProduct || m * rows > kGemmMaxProduct)
+    return HQ_EINVAL;
+  if (rows == 0 || cols == 0) return HQ_OK;
+  if (idx == nullptr || coset == nullptr || scale == nullptr || x == nullptr || y == nullptr ||
+      workspace == nullptr)
+    return HQ_EINVAL;
+  if (!aligned16(idx) || !aligned16(x) || !aligned16(workspace) || ((uintptr_t)y & 3u) ||
+      ((uintptr_t)coset & 3u) || ((uintptr_t)scale & 3u))
+    return HQ_EINVAL;
+  if (workspace_bytes < gemm_workspace(rows, cols, m)) return HQ_EINVAL;
+  if (!on_device(idx) || !on_device(coset) || !on_device(scale) || !on_device(x) ||
+      !on_device(y) || !on_device(workspace))
+    return HQ_EINVAL;
+  GemmLaunch a;
+  memset(&a, 0, sizeof(a));
+  a.idx = idx;
+  a.coset = coset;
+  a.scale = scale;
+  a.rows = rows;
+  a.cols = cols;
+  a.x = x;
+  a.m = m;
+  a.y = y;
+  a.xh = static_cast<uint16_t*>(workspace);
+  a.xl = a.xh + (size_t)m * (size_t)cols;
+  gemm_plan(rows, cols, m, a.kchunks, a.spc);
+  a.part = a.kchunks > 1 ? reinterpret_cast<float*>(a.xl + (size_t)m * (size_t)cols) : nullptr;
+  make_signs(p->rht_seed, p->tile, a.signs);
+  return launched(launch_gemm(a, stream));
+}
+
 size_t hq_gemv_batch_workspace_bytes(int32_t count, const hq_gemv_item* items, int32_t m) {
   if (count < 0 || (count > 0 && items == nullptr) || m < 1 || m > 8) return 0;
   size_t total = 0;

@@ -90,6 +90,36 @@ struct UnpackItem {
 
 constexpr int kUnpackMaxItems = 8;
 
+// hq_gemm: the matrix, the m input vectors and the workspace halves that hold
+// their rotations as bf16 hi / lo terms ([m][cols] each).
+struct GemmLaunch {
+  const int8_t* idx;
+  const uint32_t* coset;
+  const float* scale;
+  int64_t rows, cols;
+  const float* x;       // [m][cols]
+  int32_t m;
+  float* y;             // [m][rows]
+  uint16_t* xh;
+  uint16_t* xl;
+  float* part;          // [kchunks][m][rows] partial sums when kchunks > 1
+  int64_t kchunks;      // slice ranges summed by separate blocks
+  int64_t spc;          // slices per range
+  uint32_t signs[kMaxTile / 32];
+};
+
+// limits that keep the kernels' 32-bit buffer offsets in range
+constexpr int64_t kGemmMaxCols = (int64_t)1 << 22;
+constexpr int64_t kGemmMaxRows = (int64_t)1 << 23;
+// limits that keep the launch grids within 2^32 work-items
+constexpr int64_t kGemmMaxVecs = 65536;
+constexpr int64_t kGemmMaxProduct = (int64_t)1 << 31;   // m cols and m rows
+// The slice ranges of a product (a function of the sizes only, so results
+// do not depend on the device): enough ranges for about 1024 blocks.
+void gemm_plan(int64_t rows, int64_t cols, int32_t m, int64_t& kchunks, int64_t& spc);
+size_t gemm_workspace(int64_t rows, int64_t cols, int32_t m);
+hipError_t launch_gemm(const GemmLaunch& a, hipStream_t s);
+
 struct UnpackLaunch {
   int n;                // items in use
   int tile;

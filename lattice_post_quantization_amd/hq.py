@@ -83,6 +83,8 @@ _SIGNATURES = {
     "hq_unpack_batch": (_I32, [_PP, _I32, _P, _P, _P]),
     "hq_gemv": (_I32, [_PP, _P, _P, _P, _I64, _I64, _P, _I32, _P, _P, _SZ, _P, _P]),
     "hq_gemv_workspace_bytes": (_SZ, [_I64, _I64, _I32]),
+    "hq_gemm": (_I32, [_PP, _P, _P, _P, _I64, _I64, _P, _I32, _P, _P, _SZ, _P, _P]),
+    "hq_gemm_workspace_bytes": (_SZ, [_I64, _I64, _I32]),
     "hq_gemv_batch": (_I32, [_PP, _I32, _P, _I32, _P, _SZ, _P, _P]),
     "hq_gemv_batch_workspace_bytes": (_SZ, [_I32, _P, _I32]),
     "hq_kv_scores": (_I32, [_PP, _P, _I64, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
@@ -389,6 +391,26 @@ def hq_gemv(idx, coset, scale, x, rht_seed=0, out=None, workspace=None):
                          _ptr(xv), m, _ptr(y), _ptr(ws), ws.numel(), None, _stream(dev))
     _check(code, "hq_gemv")
     return y.reshape(-1) if x.dim() == 1 else y
+
+
+def hq_gemm(idx, coset, scale, x, rht_seed=0, out=None, workspace=None):
+    """Y = W X^T on the matrix cores for E8/256-coded weights W (rows, cols)
+    given by idx, coset and scale; x: fp32 (m, cols), any m >= 1; returns
+    fp32 (m, rows)."""
+    for t, name in ((idx, "idx"), (coset, "coset"), (scale, "scale"), (x, "x")):
+        _device_tensor(t, name)
+    rows, cols = idx.shape
+    m = x.shape[0]
+    dev = idx.device
+    y = out if out is not None else torch.empty((m, rows), dtype=torch.float32, device=dev)
+    nb = lib().hq_gemm_workspace_bytes(rows, cols, m)
+    ws = workspace if workspace is not None else torch.empty(max(nb, 16), dtype=torch.uint8,
+                                                             device=dev)
+    p = make_params("E8", 256, 4.0, rht_seed)
+    code = lib().hq_gemm(ctypes.byref(p), _ptr(idx), _ptr(coset), _ptr(scale), rows, cols,
+                         _ptr(x), m, _ptr(y), _ptr(ws), ws.numel(), None, _stream(dev))
+    _check(code, "hq_gemm")
+    return y
 
 
 def hq_gemv_batch(mats, xs, rht_seed=0, outs=None, workspace=None):

@@ -295,6 +295,38 @@ def test_gemv_validation_codes():
     assert lib.hq_gemv_batch(ctypes.byref(p), 1, items, 1, FAKE, 10, None, None) == hq.HQ_EINVAL
 
 
+def test_gemm_validation_codes():
+    lib = hq.lib()
+    p = hq.make_params("E8", 256, 4.0, 3)
+    # the two bf16 terms of the rotated inputs at least; partial sums only
+    # where the slices are split, which a small matrix does
+    for m in (1, 33, 300):
+        assert lib.hq_gemm_workspace_bytes(14336, 4096, m) >= 4 * m * 4096
+        assert lib.hq_gemm_workspace_bytes(37, 4096, m) >= 4 * m * 4096 + 4 * 2 * m * 37
+    for rows, cols, m in ((4, 4000, 1), (4, (1 << 22) + 256, 1), ((1 << 23) + 1, 256, 1),
+                          (4, 256, 0), (4, 256, 65537), (1 << 16, 256, 1 << 16),
+                          (4, 1 << 16, 1 << 16), (0, 256, 1)):
+        assert lib.hq_gemm_workspace_bytes(rows, cols, m) == 0, (rows, cols, m)
+    assert lib.hq_gemm_workspace_bytes(1 << 15, 1 << 15, 1 << 16) > 0
+    # nothing to compute: a no-op
+    assert lib.hq_gemm(ctypes.byref(p), None, None, None, 0, 256, None, 1, None, None, 0, None,
+                       None) == hq.HQ_OK
+    # E8 with tile 256 only; no dither
+    for q in (hq.make_params("A2", 256, 4.0), hq.make_params("E8", 128, 4.0),
+              hq.make_params("E8", 256, 4.0, 0, hq.HQ_DITHER, 1)):
+        assert lib.hq_gemm(ctypes.byref(q), FAKE, FAKE, FAKE, 4, 256, FAKE, 1, FAKE, FAKE, 1 << 20,
+                           None, None) == hq.HQ_EUNSUPPORTED
+    # sizes out of range, workspace too small, null buffers
+    for rows, cols, m in ((4, 384, 1), (4, 256, 0), (4, 256, 65537), (1 << 16, 256, 1 << 16),
+                          (4, (1 << 22) + 256, 1), (-1, 256, 1)):
+        assert lib.hq_gemm(ctypes.byref(p), FAKE, FAKE, FAKE, rows, cols, FAKE, m, FAKE, FAKE,
+                           1 << 40, None, None) == hq.HQ_EINVAL, (rows, cols, m)
+    assert lib.hq_gemm(ctypes.byref(p), FAKE, FAKE, FAKE, 4, 512, FAKE, 2, FAKE, FAKE, 100,
+                       None, None) == hq.HQ_EINVAL
+    assert lib.hq_gemm(ctypes.byref(p), FAKE, None, FAKE, 4, 512, FAKE, 1, FAKE, FAKE, 1 << 20,
+                       None, None) == hq.HQ_EINVAL
+
+
 def test_kv_scores_validation_codes():
     lib = hq.lib()
     p = hq.make_params("E8", 128, 4.0, 1, hq.HQ_DITHER, 2, 0)

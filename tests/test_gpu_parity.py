@@ -621,6 +621,49 @@ def test_gemv_parity(m):
         assert np.all(np.abs(T.host(y1) - y_ref[0]) <= tol[0]), label + " 1-D"
 
 
+@pytest.mark.parametrize("m", [1, 5, 32, 33, 64, 100])
+def test_gemm_parity(m):
+    """hq_gemm against the oracle: Y = X W^T with W the oracle's fp64 decode
+    of the oracle's own encode (ragged 37 x 1536, 300 x 768 and a Llama-shaped
+    k projection 1024 x 4096, RHT seed 5), X seeded N(0, 1) in fp32, m
+    vectors (one and two 32-vector fragments per block, several vector
+    blocks).  Bound: the two bf16 terms of a rotated input miss it by at
+    most 2^-16 of its size; the exact products accumulate in fp32 inside the
+    matrix core (at most 64 roundings per slice: 32 products of the slice per
+    output pass through two chains of 16 steps), then one rounding of the
+    scale and one per slice sum, so |y - y_ref| <= (2^-16 + (slices + 80)
+    2^-24) B with B = sum_t Delta/32 sum_j |P_j| |(H (s . x_t))_j| in fp64.
+    Two calls give the same bits."""
+    from oracle import hadamard, splitmix
+    rng = np.random.default_rng(61 + m)
+    for rows, cols in ((37, 1536), (300, 768), (1024, 4096)):
+        label = "gemm %dx%d m=%d" % (rows, cols, m)
+        say("case:", label)
+        w = rng.standard_normal((rows, cols)) * 0.02
+        w[:, 7] *= 50.0
+        xh = workloads.bf16_bits_to_f64(workloads.f32_to_bf16_bits(w.astype(np.float32)))
+        ora = codec.encode(xh, "E8", 256, 4.0, rht_seed=5)
+        W = codec.decode(ora["idx"], ora["coset"], ora["scale"], "E8", 256, 5).reshape(rows, cols)
+        x = rng.standard_normal((m, cols)).astype(np.float32)
+        y_ref = x.astype(np.float64) @ W.T                                  # (m, rows)
+        T_ = cols // 256
+        P = np.abs(ora["coords"].reshape(rows, T_, 256).astype(np.float64))
+        xr = np.abs(hadamard.unnormalized_forward(x.astype(np.float64).reshape(m * T_, 256),
+                                                  splitmix.rht_signs(5, 256))).reshape(m, T_, 256)
+        B = np.einsum("rt,rtj,vtj->vr", ora["scale"].reshape(rows, T_) / 32.0, P, xr)
+        tol = (2.0 ** -16 + (T_ + 80) * 2.0 ** -24) * B
+        idx = torch.from_numpy(ora["idx"].astype(np.int8).reshape(rows, cols)).cuda()
+        cw = torch.from_numpy(ora["coset"].astype(np.uint32).view(np.int32)).cuda()
+        sc = torch.from_numpy(ora["scale"].astype(np.float32)).cuda()
+        xd = torch.from_numpy(x).cuda()
+        y = hq.hq_gemm(idx, cw, sc, xd, rht_seed=5)
+        y2 = hq.hq_gemm(idx, cw, sc, xd, rht_seed=5)
+        torch.cuda.synchronize()
+        err = np.abs(T.host(y).astype(np.float64) - y_ref)
+        assert np.all(err <= tol), "%s: max err/tol %.3g" % (label, np.max(err / tol))
+        assert torch.equal(y, y2), label + " determinism"
+
+
 @pytest.mark.parametrize("m", [1, 2, 3])
 def test_gemv_batch_matches_single_calls(m):
     """hq_gemv_batch on ten matrices of mixed shapes (ragged row counts, one
