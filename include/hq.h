@@ -345,6 +345,23 @@ hq_status hq_gemm(const hq_params* p, const int8_t* idx, const uint32_t* coset,
 size_t hq_gemm_workspace_bytes(int64_t rows, int64_t cols, int32_t m);
 
 /*
+ * hq_gemm_batch - hq_gemm for `count` matrices with the same m and the same
+ * p (a layer's projections), enqueued as three kernel launches per group of
+ * up to eight matrices instead of up to three per matrix.  Same passages,
+ * arguments per item (hq_gemv_item) and results (bit for bit) as one
+ * hq_gemm call per item.  The workspace (device, 16-byte aligned, at least
+ * hq_gemm_batch_workspace_bytes(count, items, m) bytes) is divided among the
+ * items in order; an item with rows or cols 0 is skipped.
+ */
+hq_status hq_gemm_batch(const hq_params* p, int32_t count, const hq_gemv_item* items,
+                        int32_t m, void* workspace, size_t workspace_bytes,
+                        uint32_t* status, hipStream_t stream);
+
+/* Device workspace bytes hq_gemm_batch needs (the sum over the items of
+   hq_gemm_workspace_bytes); 0 for invalid arguments. */
+size_t hq_gemm_batch_workspace_bytes(int32_t count, const hq_gemv_item* items, int32_t m);
+
+/*
  * hq_kv_scores - attention scores of queries against one head's compressed
  * keys: scores[j][k] = q_j . khat_k, khat_k the key hq_decode_tiles would
  * reconstruct (dither subtracted), without forming khat.

@@ -554,51 +554,106 @@ bool gemv_on_device(const hq_gemv_item& it) {
 
 }  // namespace
 
+// Sizes hq_gemm accepts (m checked separately).
+static bool gemm_sizes_ok(int64_t rows, int64_t cols, int32_t m) {
+  return rows >= 0 && cols >= 0 && cols % 256 == 0 && rows <= kGemmMaxRows &&
+         cols <= kGemmMaxCols && m * cols <= kGemmMaxProduct && m * rows <= kGemmMaxProduct;
+}
+
 size_t hq_gemm_workspace_bytes(int64_t rows, int64_t cols, int32_t m) {
-  if (rows <= 0 || rows > kGemmMaxRows || cols <= 0 || cols % 256 != 0 || cols > kGemmMaxCols ||
-      m < 1 || m > kGemmMaxVecs || m * cols > kGemmMaxProduct || m * rows > kGemmMaxProduct)
+  if (m < 1 || m > kGemmMaxVecs || rows <= 0 || cols <= 0 || !gemm_sizes_ok(rows, cols, m))
     return 0;
   return gemm_workspace(rows, cols, m);
+}
+
+size_t hq_gemm_batch_workspace_bytes(int32_t count, const hq_gemv_item* items, int32_t m) {
+  if (count < 0 || (count > 0 && items == nullptr) || m < 1 || m > kGemmMaxVecs) return 0;
+  size_t total = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const hq_gemv_item& it = items[i];
+    if (!gemm_sizes_ok(it.rows, it.cols, m)) return 0;
+    if (it.rows > 0 && it.cols > 0) total += gemm_workspace(it.rows, it.cols, m);
+  }
+  return total;
+}
+
+hq_status hq_gemm_batch(const hq_params* p, int32_t count, const hq_gemv_item* items, int32_t m,
+                        void* workspace, size_t workspace_bytes, uint32_t* status,
+                        hipStream_t stream) {
+  (void)status;
+  hq_status st = check_params(p);
+  if (st != HQ_OK) return st;
+  if (p->lattice != HQ_E8 || p->tile != 256 || (p->flags & HQ_DITHER)) return HQ_EUNSUPPORTED;
+  if (count < 0 || (count > 0 && items == nullptr) || m < 1 || m > kGemmMaxVecs)
+    return HQ_EINVAL;
+  bool any = false;
+  for (int32_t i = 0; i < count; ++i) {
+    const hq_gemv_item& it = items[i];
+    if (!gemm_sizes_ok(it.rows, it.cols, m)) return HQ_EINVAL;
+    if (it.rows == 0 || it.cols == 0) continue;
+    if (it.idx == nullptr || it.coset == nullptr || it.scale == nullptr || it.x == nullptr ||
+        it.y == nullptr)
+      return HQ_EINVAL;
+    if (!aligned16(it.idx) || !aligned16(it.x) || ((uintptr_t)it.y & 3u) ||
+        ((uintptr_t)it.coset & 3u) || ((uintptr_t)it.scale & 3u))
+      return HQ_EINVAL;
+    any = true;
+  }
+  if (!any) return HQ_OK;
+  if (workspace == nullptr || !aligned16(workspace) ||
+      workspace_bytes < hq_gemm_batch_workspace_bytes(count, items, m))
+    return HQ_EINVAL;
+  for (int32_t i = 0; i < count; ++i) {
+    const hq_gemv_item& it = items[i];
+    if (it.rows == 0 || it.cols == 0) continue;
+    if (!on_device(it.idx) || !on_device(it.coset) || !on_device(it.scale) || !on_device(it.x) ||
+        !on_device(it.y))
+      return HQ_EINVAL;
+  }
+  if (!on_device(workspace)) return HQ_EINVAL;
+  // launches of up to kGemmMaxItems matrices, each with its own workspace
+  // slice in item order
+  GemmBatch b;
+  memset(&b, 0, sizeof(b));
+  b.m = m;
+  make_signs(p->rht_seed, p->tile, b.signs);
+  char* ws = static_cast<char*>(workspace);
+  for (int32_t i = 0; i <= count; ++i) {
+    if ((i == count || b.n == kGemmMaxItems) && b.n > 0) {
+      char* base = ws;
+      for (int k = 0; k < b.n; ++k) ws += gemm_workspace(b.it[k].rows, b.it[k].cols, m);
+      gemm_layout(b, base);
+      if (launch_gemm(b, stream) != hipSuccess) return HQ_EDEVICE;
+      b.n = 0;
+    }
+    if (i == count) break;
+    const hq_gemv_item& it = items[i];
+    if (it.rows == 0 || it.cols == 0) continue;
+    GemmItem& g = b.it[b.n++];
+    memset(&g, 0, sizeof(g));
+    g.idx = it.idx;
+    g.coset = it.coset;
+    g.scale = it.scale;
+    g.rows = it.rows;
+    g.cols = it.cols;
+    g.x = it.x;
+    g.y = it.y;
+  }
+  return HQ_OK;
 }
 
 hq_status hq_gemm(const hq_params* p, const int8_t* idx, const uint32_t* coset, const float* scale,
                   int64_t rows, int64_t cols, const float* x, int32_t m, float* y,
                   void* workspace, size_t workspace_bytes, uint32_t* status, hipStream_t stream) {
-  (void)status;
-  hq_status st = check_params(p);
-  if (st != HQ_OK) return st;
-  if (p->lattice != HQ_E8 || p->tile != 256 || (p->flags & HQ_DITHER)) return HQ_EUNSUPPORTED;
-  if (rows < 0 || cols < 0 || cols % 256 != 0 || m < 1) return HQ_EINVAL;
-  if (rows > kGemmMaxRows || cols > kGemmMaxCols || m > kGemmMaxVecs ||
-      m * cols > kGemmMaxProduct || m * rows > kGemmMaxProduct)
-    return HQ_EINVAL;
-  if (rows == 0 || cols == 0) return HQ_OK;
-  if (idx == nullptr || coset == nullptr || scale == nullptr || x == nullptr || y == nullptr ||
-      workspace == nullptr)
-    return HQ_EINVAL;
-  if (!aligned16(idx) || !aligned16(x) || !aligned16(workspace) || ((uintptr_t)y & 3u) ||
-      ((uintptr_t)coset & 3u) || ((uintptr_t)scale & 3u))
-    return HQ_EINVAL;
-  if (workspace_bytes < gemm_workspace(rows, cols, m)) return HQ_EINVAL;
-  if (!on_device(idx) || !on_device(coset) || !on_device(scale) || !on_device(x) ||
-      !on_device(y) || !on_device(workspace))
-    return HQ_EINVAL;
-  GemmLaunch a;
-  memset(&a, 0, sizeof(a));
-  a.idx = idx;
-  a.coset = coset;
-  a.scale = scale;
-  a.rows = rows;
-  a.cols = cols;
-  a.x = x;
-  a.m = m;
-  a.y = y;
-  a.xh = static_cast<uint16_t*>(workspace);
-  a.xl = a.xh + (size_t)m * (size_t)cols;
-  gemm_plan(rows, cols, m, a.kchunks, a.spc);
-  a.part = a.kchunks > 1 ? reinterpret_cast<float*>(a.xl + (size_t)m * (size_t)cols) : nullptr;
-  make_signs(p->rht_seed, p->tile, a.signs);
-  return launched(launch_gemm(a, stream));
+  hq_gemv_item it;
+  it.idx = idx;
+  it.coset = coset;
+  it.scale = scale;
+  it.rows = rows;
+  it.cols = cols;
+  it.x = x;
+  it.y = y;
+  return hq_gemm_batch(p, 1, &it, m, workspace, workspace_bytes, status, stream);
 }
 
 size_t hq_gemv_batch_workspace_bytes(int32_t count, const hq_gemv_item* items, int32_t m) {

@@ -15,19 +15,27 @@
 // is two bf16 MFMA products with fp32 accumulation, scaled by the row's
 // Delta / 32 and added to the output accumulator.
 //
+// One launch of each kernel covers up to kGemmMaxItems matrices that share
+// m (a layer's projections); each matrix keeps its own plan, so a batch
+// gives the bits of one call per matrix.
+//
 // split_kernel: one wave per (vector, slice) rotates in fp64 (as hq_gemv)
 // and writes xh, xl [m][cols] bf16.
-// gemm_kernel: a block of 4 waves owns 128 rows x 32 NF vectors and a range
-// of slices (a small matrix splits its slices over several blocks, whose
-// partial sums sum_kernel adds in range order); per slice
-// it stages the 256 x 32 NF hi and lo inputs in LDS (direct-to-LDS loads in
-// a swizzled order so that the fragment reads hit distinct banks), each wave
+// gemm_kernel: a block of W waves owns 32 W rows x 32 NF vectors and a
+// range of slices (a small matrix splits its slices over several blocks,
+// whose partial sums sum_kernel adds in range order); per slice the
+// 256 x 32 NF hi and lo inputs go through registers (loaded one slice
+// ahead) into LDS in a swizzled order so that the fragment reads hit
+// distinct banks (two buffers, one barrier per slice), and each wave
 // decodes its 32 rows' index bytes (one E8 block per lane and step: z7 from
 // the parity of z0..z6, P = 2 z + c) into bf16 A fragments and runs
 // v_mfma_f32_32x32x16_bf16 over the 16 steps of the slice.  The K order
-// within a slice is permuted so that a lane's 16 blocks are its row's
-// contiguous 128 bytes: step s, lane half h covers block 16 h + s (B uses
-// the same permutation).
+// within a slice is permuted so that a lane reads its row's bytes 16 at a
+// time next to the other half's: step s, lane half h covers block
+// 4 (s / 2) + 2 h + s % 2 (B uses the same permutation).  Blocks go to the
+// eight XCDs in turn; the numbering puts the blocks that share a row range
+// (one per 32 NF vectors) on one XCD, one after the other, so the index
+// bytes they all read come from that XCD's L2 after the first.
 #include "hq.h"
 #include "hq_device.h"
 #include "hq_internal.h"
@@ -39,24 +47,36 @@ namespace {
 using namespace fastlib;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kGemmRows = 128;      // rows per block (4 waves x 32)
 constexpr int kSliceK = 256;
+
+// Matrix of the batch that holds index g of a numbering (wave-uniform).
+template <typename F>
+__device__ inline int item_at(const GemmBatch& b, int64_t g, F first) {
+  int i = 0;
+#pragma unroll
+  for (int k = 1; k < kGemmMaxItems; ++k)
+    if (k < b.n && g >= first(b.it[k])) i = k;
+  return i;
+}
 
 // xh / xl [v][c] for c in slice t: one wave per (vector, slice), lane l
 // holding elements 4 l .. 4 l + 3; fp64 butterflies as in hq_gemv's rotation.
-__global__ __launch_bounds__(256) void split_kernel(GemmLaunch a) {
+__global__ __launch_bounds__(256) void split_kernel(GemmBatch bt) {
   __shared__ double v[4][256];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t slices = a.cols / kSliceK;
   const int64_t g = (int64_t)blockIdx.x * 4 + w;
-  if (g >= (int64_t)a.m * slices) return;
-  const int64_t vec = g / slices, t = g % slices;
+  if (g >= bt.n_split) return;
+  const GemmItem& a = bt.it[item_at(bt, g, [](const GemmItem& t) { return t.split0; })];
+  const int64_t slices = a.cols / kSliceK;
+  const int64_t vec = (g - a.split0) / slices, t = (g - a.split0) % slices;
   const int64_t c0 = vec * a.cols + t * kSliceK + 4 * lane;
   const float4 xv = *reinterpret_cast<const float4*>(a.x + c0);
-  const uint32_t sg = a.signs[lane >> 3] >> (4 * (lane & 7));
+  const uint32_t sg = bt.signs[lane >> 3] >> (4 * (lane & 7));
   double e[4] = {(double)xv.x, (double)xv.y, (double)xv.z, (double)xv.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -108,10 +128,11 @@ __device__ inline bf16x8 a_fragment(uint32_t d0, uint32_t d1, uint32_t c) {
     f[4 + i] = fmaf((float)(int32_t)(int8_t)(d1 >> (8 * i)), i == 3 ? 4.0f : 2.0f,
                     i == 3 ? c7 : cf);
   }
-  bf16x8 r;
+  u32x4 r;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = (__bf16)f[i];
-  return r;
+  for (int i = 0; i < 4; ++i)
+    r[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){f[2 * i], f[2 * i + 1]}, bf16x2));
+  return __builtin_bit_cast(bf16x8, r);
 }
 
 // One 32 x 32 x 16 bf16 matrix-core product accumulated into c.
@@ -119,46 +140,60 @@ __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// 16 bytes per lane from offset goff of rs into LDS at dst + 16 lane (a
-// plain function: written directly in the kernel template, the builtin keeps
-// the host pass from instantiating the template's launch stub).
-__device__ inline void to_lds16(__amdgpu_buffer_rsrc_t rs, uint4* dst, int goff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr(dst), 16, goff, 0, 0, 0);
-}
-
-// A lane's 128 index bytes of one slice (its row, its half), from offset off.
+// A lane's 128 index bytes of one slice: 16 bytes (two blocks) out of every
+// 32 of its row, from offset off (the two lanes of a row read neighbouring
+// 16 bytes, so an instruction touches 32 B of each of 32 rows).
 __device__ inline void load_a(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t* d) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(off + 16 * i), 0, 0);
+    const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(off + 32 * i), 0, 0);
     d[4 * i] = q[0]; d[4 * i + 1] = q[1]; d[4 * i + 2] = q[2]; d[4 * i + 3] = q[3];
   }
 }
 
-template <int NF>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmLaunch a) {
-  // per slice: NF fragments of 32 vectors x 256 k, hi and lo, 16-byte chunks;
-  // chunk (j, q) of vector j (0 .. 32 NF) sits at slot j * 32 + (q ^ (j & 31))
-  __shared__ uint4 bh[NF * 32 * 32];
-  __shared__ uint4 bl[NF * 32 * 32];
-  __shared__ float dsc[4][32];
+// NF fragments of 32 vectors; W waves of 32 rows each.
+template <int NF, int W>
+__global__ __launch_bounds__(64 * W, 2) void gemm_kernel(GemmBatch bt) {
+  // a slice's inputs: NF x 32 vectors x 256 k, hi and lo, as 16-byte chunks;
+  // chunk (j, q) of vector j sits at slot j * 32 + (q ^ (j & 31)); two
+  // buffers: the next slice's inputs, loaded into registers while this
+  // slice computes, are written to one while the other is read
+  constexpr int kSlots = NF * 32 * 32;
+  constexpr int kPerWave = kSlots / (64 * W);   // chunks per array and lane
+  __shared__ uint4 bh[2][kSlots];
+  __shared__ uint4 bl[2][kSlots];
+  __shared__ float dsc[W][32];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5, li = lane & 31;
-  const int64_t row0 = (int64_t)blockIdx.x * kGemmRows + 32 * w;
-  const int64_t vec0 = (int64_t)blockIdx.y * (32 * NF);
+  // the block's matrix, then (XCD, position on it) -> (row range, slice
+  // range, vector block); numbers past the matrix's blocks end at once
+  const int64_t g = blockIdx.x;
+  const GemmItem& a = bt.it[item_at(bt, g, [](const GemmItem& t) { return t.blk0; })];
+  const int64_t local = g - a.blk0;
+  const int64_t vblocks = (bt.m + 32 * NF - 1) / (32 * NF);
+  const int64_t rblocks = (a.rows + 32 * W - 1) / (32 * W);
+  const int64_t k = local >> 3;
+  const int64_t rt = (k / vblocks) * 8 + (local & 7);
+  if (rt >= rblocks * a.kchunks) return;
+  const int64_t chunk = rt / rblocks;
+  const int64_t row0 = (rt % rblocks) * (32 * W) + 32 * w;
+  const int64_t vec0 = (k % vblocks) * (32 * NF);
   const int64_t slices = a.cols / kSliceK;
   // this block's slice range
-  const int64_t t_begin = (int64_t)blockIdx.z * a.spc;
+  const int64_t t_begin = chunk * a.spc;
   const int64_t t_end = t_begin + a.spc < slices ? t_begin + a.spc : slices;
 
   // inputs of this block's vectors (zeros past m), indices of this wave's
   // rows (zeros past rows), per-tile words and scales
+  const int64_t live_vecs = bt.m - vec0 < 32 * NF ? bt.m - vec0 : 32 * NF;
   const auto xh_rs = out_rsrc(const_cast<uint16_t*>(a.xh) + vec0 * a.cols,
-                              (uint32_t)((a.m - vec0 < 32 * NF ? a.m - vec0 : 32 * NF) * a.cols * 2));
+                              (uint32_t)(live_vecs * a.cols * 2));
   const auto xl_rs = out_rsrc(const_cast<uint16_t*>(a.xl) + vec0 * a.cols,
-                              (uint32_t)((a.m - vec0 < 32 * NF ? a.m - vec0 : 32 * NF) * a.cols * 2));
-  const int64_t live_rows = a.rows - row0 < 32 ? a.rows - row0 : 32;
+                              (uint32_t)(live_vecs * a.cols * 2));
+  // a wave wholly past the matrix (small matrices) gets empty ranges
+  const int64_t rest = a.rows - row0;
+  const int64_t live_rows = rest < 0 ? 0 : (rest < 32 ? rest : 32);
   const auto idx_rs = out_rsrc(const_cast<int8_t*>(a.idx) + row0 * a.cols,
                                (uint32_t)(live_rows * a.cols));
   const auto cw_rs = out_rsrc(const_cast<uint32_t*>(a.coset) + row0 * slices,
@@ -166,61 +201,84 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmLaunch a) {
   const auto sc_rs = out_rsrc(const_cast<float*>(a.scale) + row0 * slices,
                               (uint32_t)(live_rows * slices * 4));
 
+  // chunk i of lane (w, lane) is slot 64 (kPerWave w + i) + lane
+  u32x4 nh[kPerWave], nl[kPerWave];
+  auto fetch = [&](int64_t t) {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int S = 64 * (kPerWave * w + i) + lane;
+      const int j = S >> 5, q = (S & 31) ^ (j & 31);
+      const int goff = (int)((j * a.cols + t * kSliceK + 8 * q) * 2);
+      nh[i] = __builtin_amdgcn_raw_buffer_load_b128(xh_rs, goff, 0, 0);
+      nl[i] = __builtin_amdgcn_raw_buffer_load_b128(xl_rs, goff, 0, 0);
+    }
+  };
+  auto put = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int S = 64 * (kPerWave * w + i) + lane;
+      bh[b][S] = __builtin_bit_cast(uint4, nh[i]);
+      bl[b][S] = __builtin_bit_cast(uint4, nl[i]);
+    }
+  };
+  auto tile_word = [&](__amdgpu_buffer_rsrc_t rs, int64_t t) {
+    return __builtin_amdgcn_raw_buffer_load_b32(rs, (int)((li * slices + t) * 4), 0, 0);
+  };
+
   f32x16 out[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) out[f] = (f32x16){};
 
+  // the first slice's loads
   uint32_t dn[32];
-  load_a(idx_rs, (uint32_t)(li * a.cols + t_begin * kSliceK + 128 * h), dn);
+  fetch(t_begin);
+  put(0);
+  uint32_t cw_n = tile_word(cw_rs, t_begin), sc_n = tile_word(sc_rs, t_begin);
+  load_a(idx_rs, (uint32_t)(li * a.cols + t_begin * kSliceK + 16 * h), dn);
 
   for (int64_t t = t_begin; t < t_end; ++t) {
-    // ---- stage the slice's inputs: instruction i of wave w fills slots
-    // 64 (4 NF w + i) + lane (4 NF instructions per array and wave)
-    __syncthreads();   // the previous slice's fragments have been read
-#pragma unroll
-    for (int i = 0; i < NF * 4; ++i) {
-      const int S = 64 * (NF * 4 * w + i) + lane;   // slot
-      const int j = S >> 5, q = (S & 31) ^ (j & 31);
-      const int goff = (int)((j * a.cols + t * kSliceK + 8 * q) * 2);
-      to_lds16(xh_rs, bh + 64 * (NF * 4 * w + i), goff);
-      to_lds16(xl_rs, bl + 64 * (NF * 4 * w + i), goff);
-    }
-    const uint32_t cw = __builtin_amdgcn_raw_buffer_load_b32(cw_rs, (int)((li * slices + t) * 4), 0, 0);
-    const float sc = __uint_as_float(
-        __builtin_amdgcn_raw_buffer_load_b32(sc_rs, (int)((li * slices + t) * 4), 0, 0));
+    const int b = (int)((t - t_begin) & 1);
+    // this slice's inputs are in buffer b, and every wave has read the other
+    // buffer's previous slice
+    __syncthreads();
+    const uint32_t cw = cw_n;
+    const float sc = __uint_as_float(sc_n);
     uint32_t d[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) d[i] = dn[i];
     __builtin_amdgcn_sched_barrier(0);
-    // the next slice's index bytes are the last loads issued: the wait below
-    // leaves them in flight during this slice
-    if (t + 1 < t_end) load_a(idx_rs, (uint32_t)(li * a.cols + (t + 1) * kSliceK + 128 * h), dn);
+    if (t + 1 < t_end) {
+      fetch(t + 1);
+      cw_n = tile_word(cw_rs, t + 1);
+      sc_n = tile_word(sc_rs, t + 1);
+      load_a(idx_rs, (uint32_t)(li * a.cols + (t + 1) * kSliceK + 16 * h), dn);
+    }
     __builtin_amdgcn_sched_barrier(0);
-    if (t + 1 < t_end)
-      __asm__ volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else
-      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // the rows' Delta / 32, for the transpose into the output layout below
     if (h == 0) dsc[w][li] = sc * 0.03125f;
-    __syncthreads();
 
+    const uint4* Bh = bh[b];
+    const uint4* Bl = bl[b];
     f32x16 acc[NF];
 #pragma unroll
     for (int f = 0; f < NF; ++f) acc[f] = (f32x16){};
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
-      const uint32_t c = (cw >> (16 * h + s)) & 1u;
+      // block of step s for this lane half
+      const int q = 4 * (s >> 1) + 2 * h + (s & 1);
+      const uint32_t c = (cw >> q) & 1u;
       const bf16x8 af = a_fragment(d[2 * s], d[2 * s + 1], c);
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
-        const int j = 32 * f + li, q = 16 * h + s;
+        const int j = 32 * f + li;
         const int slot = j * 32 + (q ^ (j & 31));
-        const bf16x8 b_hi = __builtin_bit_cast(bf16x8, bh[slot]);
-        const bf16x8 b_lo = __builtin_bit_cast(bf16x8, bl[slot]);
-        acc[f] = mfma32(af, b_hi, acc[f]);
-        acc[f] = mfma32(af, b_lo, acc[f]);
+        acc[f] = mfma32(af, __builtin_bit_cast(bf16x8, Bh[slot]), acc[f]);
+        acc[f] = mfma32(af, __builtin_bit_cast(bf16x8, Bl[slot]), acc[f]);
       }
     }
+    if (t + 1 < t_end) put(b ^ 1);
     // ---- out += (Delta / 32) acc; register r holds row 8 (r / 4) + 4 h + r % 4
+    wave_lds_sync();
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const float4 ds = *reinterpret_cast<const float4*>(&dsc[w][8 * g4 + 4 * h]);
@@ -232,11 +290,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmLaunch a) {
     }
   }
 
-  // ---- y[vec][row]: four consecutive rows per 16-byte store (dropped past
-  // the matrix: rows past a.rows, vectors past m)
-  // y, or this range's partial sums
-  const int64_t live_vecs = a.m - vec0 < 32 * NF ? a.m - vec0 : 32 * NF;
-  float* dst = a.kchunks > 1 ? a.part + (int64_t)blockIdx.z * a.m * a.rows : a.y;
+  // ---- y[vec][row] (or this range's partial sums), one element per store;
+  // rows past the matrix go to an offset the hardware drops
+  float* dst = a.kchunks > 1 ? a.part + chunk * bt.m * a.rows : a.y;
   const auto y_rs = out_rsrc(dst + vec0 * a.rows, (uint32_t)(live_vecs * a.rows * 4));
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
@@ -246,7 +302,6 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmLaunch a) {
       const int64_t r0 = row0 + 8 * g4 + 4 * h;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        // rows past the matrix go to an offset the hardware drops
         const uint32_t off = r0 + r < a.rows ? (uint32_t)((j * a.rows + r0 + r) * 4) : 0x80000000u;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out[f][4 * g4 + r]), y_rs, (int)off,
                                               0, 0);
@@ -255,32 +310,43 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmLaunch a) {
   }
 }
 
-// y = the sum of the ranges' partial sums, in range order
-__global__ __launch_bounds__(256) void sum_kernel(GemmLaunch a) {
-  const int64_t n = (int64_t)a.m * a.rows;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
+// y = the sum of the ranges' partial sums, in range order (matrices with
+// more than one range)
+__global__ __launch_bounds__(256) void sum_kernel(GemmBatch bt) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= bt.n_sum) return;
+  // the element's matrix (lanes may differ: a plain scan)
+  int k = 0;
+  for (int j = 1; j < bt.n; ++j)
+    if (bt.it[j].kchunks > 1 && g >= bt.it[j].sum0) k = j;
+  const GemmItem& a = bt.it[k];
+  const int64_t n = (int64_t)bt.m * a.rows;
+  const int64_t i = g - a.sum0;
   float s = a.part[i];
   for (int64_t c = 1; c < a.kchunks; ++c) s += a.part[c * n + i];
   a.y[i] = s;
 }
 
-template <int NF>
-void launch_nf(const GemmLaunch& a, hipStream_t s) {
-  const int64_t row_blocks = (a.rows + kGemmRows - 1) / kGemmRows;
-  const int64_t vec_blocks = (a.m + 32 * NF - 1) / (32 * NF);
-  hipLaunchKernelGGL((gemm_kernel<NF>),
-                     dim3((unsigned)row_blocks, (unsigned)vec_blocks, (unsigned)a.kchunks),
-                     dim3(256), 0, s, a);
+template <int NF, int W>
+void launch_nf(const GemmBatch& b, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_kernel<NF, W>), dim3((unsigned)b.n_blocks), dim3(64 * W), 0, s, b);
 }
+
+// one 32-vector fragment per block for m <= 32 (4 waves, two blocks per
+// CU), else two (8 waves, one block per CU: the double-buffered inputs take
+// 128 KiB of LDS)
+int nf_for(int32_t m) { return m <= 32 ? 1 : 2; }
+int waves_for(int nf) { return nf == 1 ? 4 : 8; }
 
 }  // namespace
 
 void gemm_plan(int64_t rows, int64_t cols, int32_t m, int64_t& kchunks, int64_t& spc) {
-  const int nf = m <= 32 ? 1 : 2;
-  const int64_t base = ((rows + kGemmRows - 1) / kGemmRows) * ((m + 32 * nf - 1) / (32 * nf));
+  const int nf = nf_for(m), waves = waves_for(nf);
+  const int64_t base = ((rows + 32 * waves - 1) / (32 * waves)) * ((m + 32 * nf - 1) / (32 * nf));
   const int64_t slices = cols / kSliceK;
-  int64_t k = (1024 + base - 1) / base;
+  // about two blocks per CU slot
+  const int64_t target = nf == 1 ? 1024 : 512;
+  int64_t k = (target + base - 1) / base;
   k = k < 1 ? 1 : (k > slices ? slices : k);
   spc = (slices + k - 1) / k;
   kchunks = (slices + spc - 1) / spc;
@@ -293,17 +359,39 @@ size_t gemm_workspace(int64_t rows, int64_t cols, int32_t m) {
          (kchunks > 1 ? (size_t)4 * (size_t)kchunks * (size_t)m * (size_t)rows : 0);
 }
 
-hipError_t launch_gemm(const GemmLaunch& a, hipStream_t s) {
-  const int64_t splits = (int64_t)a.m * (a.cols / kSliceK);
-  hipLaunchKernelGGL(split_kernel, dim3((unsigned)((splits + 3) / 4)), dim3(256), 0, s, a);
-  if (a.m <= 32)
-    launch_nf<1>(a, s);
-  else
-    launch_nf<2>(a, s);
-  if (a.kchunks > 1) {
-    const int64_t n = (int64_t)a.m * a.rows;
-    hipLaunchKernelGGL(sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+void gemm_layout(GemmBatch& b, char* workspace) {
+  const int nf = nf_for(b.m), waves = waves_for(nf);
+  const int64_t vblocks = (b.m + 32 * nf - 1) / (32 * nf);
+  b.n_blocks = b.n_split = b.n_sum = 0;
+  for (int i = 0; i < b.n; ++i) {
+    GemmItem& it = b.it[i];
+    gemm_plan(it.rows, it.cols, b.m, it.kchunks, it.spc);
+    const size_t half = (size_t)2 * (size_t)b.m * (size_t)it.cols;
+    it.xh = reinterpret_cast<uint16_t*>(workspace);
+    it.xl = reinterpret_cast<uint16_t*>(workspace + half);
+    it.part = it.kchunks > 1 ? reinterpret_cast<float*>(workspace + 2 * half) : nullptr;
+    workspace += gemm_workspace(it.rows, it.cols, b.m);
+    // blocks: (row ranges x slice ranges) rounded up to the eight XCDs,
+    // times the vector blocks
+    const int64_t tasks = (it.rows + 32 * waves - 1) / (32 * waves) * it.kchunks;
+    it.blk0 = b.n_blocks;
+    it.split0 = b.n_split;
+    it.sum0 = b.n_sum;
+    b.n_blocks += (tasks + 7) / 8 * 8 * vblocks;
+    b.n_split += (int64_t)b.m * (it.cols / kSliceK);
+    if (it.kchunks > 1) b.n_sum += (int64_t)b.m * it.rows;
   }
+  for (int i = b.n; i < kGemmMaxItems; ++i) b.it[i] = b.it[0];
+}
+
+hipError_t launch_gemm(const GemmBatch& b, hipStream_t s) {
+  hipLaunchKernelGGL(split_kernel, dim3((unsigned)((b.n_split + 3) / 4)), dim3(256), 0, s, b);
+  if (nf_for(b.m) == 1)
+    launch_nf<1, 4>(b, s);
+  else
+    launch_nf<2, 8>(b, s);
+  if (b.n_sum > 0)
+    hipLaunchKernelGGL(sum_kernel, dim3((unsigned)((b.n_sum + 255) / 256)), dim3(256), 0, s, b);
   return hipGetLastError();
 }
 

@@ -90,22 +90,37 @@ struct UnpackItem {
 
 constexpr int kUnpackMaxItems = 8;
 
-// hq_gemm: the matrix, the m input vectors and the workspace halves that hold
-// their rotations as bf16 hi / lo terms ([m][cols] each).
-struct GemmLaunch {
+// One matrix of an hq_gemm batch.  The workspace pointers and the plan are
+// filled in by gemm_layout; blk0 / split0 / sum0 number the matrix's GEMM
+// blocks, split waves and summed elements across the batch.
+struct GemmItem {
   const int8_t* idx;
   const uint32_t* coset;
   const float* scale;
-  int64_t rows, cols;
+  int64_t rows;
+  int64_t cols;         // multiple of 256 (E8, tile 256), at most kGemmMaxCols
   const float* x;       // [m][cols]
-  int32_t m;
   float* y;             // [m][rows]
-  uint16_t* xh;
+  uint16_t* xh;         // workspace: the rotated inputs' bf16 terms, [m][cols]
   uint16_t* xl;
-  float* part;          // [kchunks][m][rows] partial sums when kchunks > 1
+  float* part;          // workspace: [kchunks][m][rows] partial sums (kchunks > 1)
   int64_t kchunks;      // slice ranges summed by separate blocks
   int64_t spc;          // slices per range
-  uint32_t signs[kMaxTile / 32];
+  int64_t blk0;
+  int64_t split0;
+  int64_t sum0;
+};
+
+constexpr int kGemmMaxItems = 8;   // matrices per launch
+
+struct GemmBatch {
+  int32_t n;            // matrices, 1..kGemmMaxItems
+  int32_t m;            // vectors
+  int64_t n_blocks;     // GEMM blocks of the batch
+  int64_t n_split;      // split waves
+  int64_t n_sum;        // summed elements
+  uint32_t signs[8];
+  GemmItem it[kGemmMaxItems];
 };
 
 // limits that keep the kernels' 32-bit buffer offsets in range
@@ -115,10 +130,13 @@ constexpr int64_t kGemmMaxRows = (int64_t)1 << 23;
 constexpr int64_t kGemmMaxVecs = 65536;
 constexpr int64_t kGemmMaxProduct = (int64_t)1 << 31;   // m cols and m rows
 // The slice ranges of a product (a function of the sizes only, so results
-// do not depend on the device): enough ranges for about 1024 blocks.
+// do not depend on the device or the batch): enough ranges for about two
+// blocks per CU slot.
 void gemm_plan(int64_t rows, int64_t cols, int32_t m, int64_t& kchunks, int64_t& spc);
 size_t gemm_workspace(int64_t rows, int64_t cols, int32_t m);
-hipError_t launch_gemm(const GemmLaunch& a, hipStream_t s);
+// Fills the workspace pointers, the plan and the numbering of b.it[0 .. b.n).
+void gemm_layout(GemmBatch& b, char* workspace);
+hipError_t launch_gemm(const GemmBatch& b, hipStream_t s);
 
 struct UnpackLaunch {
   int n;                // items in use

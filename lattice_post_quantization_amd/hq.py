@@ -85,6 +85,8 @@ _SIGNATURES = {
     "hq_gemv_workspace_bytes": (_SZ, [_I64, _I64, _I32]),
     "hq_gemm": (_I32, [_PP, _P, _P, _P, _I64, _I64, _P, _I32, _P, _P, _SZ, _P, _P]),
     "hq_gemm_workspace_bytes": (_SZ, [_I64, _I64, _I32]),
+    "hq_gemm_batch": (_I32, [_PP, _I32, _P, _I32, _P, _SZ, _P, _P]),
+    "hq_gemm_batch_workspace_bytes": (_SZ, [_I32, _P, _I32]),
     "hq_gemv_batch": (_I32, [_PP, _I32, _P, _I32, _P, _SZ, _P, _P]),
     "hq_gemv_batch_workspace_bytes": (_SZ, [_I32, _P, _I32]),
     "hq_kv_scores": (_I32, [_PP, _P, _I64, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
@@ -446,6 +448,40 @@ def hq_gemv_batch(mats, xs, rht_seed=0, outs=None, workspace=None):
                                ws.numel(), None, _stream(dev))
     _check(code, "hq_gemv_batch")
     return [y.reshape(-1) for y in ys] if one_d else ys
+
+
+def hq_gemm_batch(mats, xs, rht_seed=0, outs=None, workspace=None):
+    """hq_gemm for several E8/256-coded matrices in one call: mats is a list
+    of dicts with idx, coset and scale, xs the matching fp32 inputs (m, cols)
+    with one m.  Returns the list of fp32 (m, rows) outputs."""
+    if len(mats) != len(xs):
+        raise ValueError("one input per matrix")
+    if not mats:
+        return []
+    dev = mats[0]["idx"].device
+    m = xs[0].shape[0]
+    items = (GemvItem * len(mats))()
+    ys = []
+    for i, (e, x) in enumerate(zip(mats, xs)):
+        for name in ("idx", "coset", "scale"):
+            _device_tensor(e[name], name)
+        _device_tensor(x, "x")
+        if x.dim() != 2 or x.shape[0] != m:
+            raise ValueError("inputs must all be (m, cols) with the same m")
+        rows, cols = e["idx"].shape
+        y = outs[i] if outs is not None else torch.empty((m, rows), dtype=torch.float32,
+                                                          device=dev)
+        ys.append(y)
+        items[i] = GemvItem(_addr(e["idx"]), _addr(e["coset"]), _addr(e["scale"]), rows, cols,
+                            _addr(x), _addr(y))
+    nb = lib().hq_gemm_batch_workspace_bytes(len(mats), ctypes.byref(items), m)
+    ws = workspace if workspace is not None else torch.empty(max(nb, 16), dtype=torch.uint8,
+                                                             device=dev)
+    p = make_params("E8", 256, 4.0, rht_seed)
+    code = lib().hq_gemm_batch(ctypes.byref(p), len(mats), ctypes.byref(items), m, _ptr(ws),
+                               ws.numel(), None, _stream(dev))
+    _check(code, "hq_gemm_batch")
+    return ys
 
 
 def hq_kv_scores(q, enc, rht_seed=0, dither_seed=None, dither_base=0, out=None,

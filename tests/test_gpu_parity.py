@@ -664,6 +664,29 @@ def test_gemm_parity(m):
         assert torch.equal(y, y2), label + " determinism"
 
 
+@pytest.mark.parametrize("m", [3, 40])
+def test_gemm_batch_matches_single_calls(m):
+    """hq_gemm_batch on ten matrices of mixed shapes (ragged row counts, one
+    and many slices, split and unsplit slice ranges; more than one launch
+    group) gives each matrix's hq_gemm result bit for bit."""
+    rng = np.random.default_rng(71 + m)
+    shapes = [(37, 1536), (64, 4096), (5, 256), (300, 14336), (129, 2048), (1, 768),
+              (4096, 512), (256, 1024), (3, 4096), (90, 512)]
+    mats, xs = [], []
+    for i, (rows, cols) in enumerate(shapes):
+        w = (rng.standard_normal((rows, cols)) * 0.02).astype(np.float32)
+        bits = workloads.f32_to_bf16_bits(w)
+        say("case: gemm batch m=%d item %d %dx%d" % (m, i, rows, cols))
+        mats.append(hq.hq_encode_tiles(T.bf16_device(bits, (rows, cols)), "E8", 256, 4.0, 9))
+        xs.append(torch.from_numpy(rng.standard_normal((m, cols)).astype(np.float32)).cuda())
+    ys = hq.hq_gemm_batch(mats, xs, rht_seed=9)
+    torch.cuda.synchronize()
+    for i, (e, x) in enumerate(zip(mats, xs)):
+        y1 = hq.hq_gemm(e["idx"], e["coset"], e["scale"], x, rht_seed=9)
+        torch.cuda.synchronize()
+        assert torch.equal(ys[i], y1), "item %d %s" % (i, shapes[i])
+
+
 @pytest.mark.parametrize("m", [1, 2, 3])
 def test_gemv_batch_matches_single_calls(m):
     """hq_gemv_batch on ten matrices of mixed shapes (ragged row counts, one
