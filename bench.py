@@ -37,9 +37,9 @@ DEC_BYTES_PER_TILE = 256 + 4 + 4 + 512
 # sources still match.
 KERNEL_SOURCES = ("hq_e8fast.hip", "hq_lanes.h", "hq_device.h", "hq_internal.h")
 MEASURED_TRAFFIC = {
-    "sources_sha256": "4f5fa13dbdfa996a43adaa744cf960a553d7ade3a4eb4794749fa29dce362165",
-    "encode": {"read": 513.87, "write": 269.33},
-    "decode": {"read": 264.27, "write": 512.00},
+    "sources_sha256": "9b7c684a93d7e4c51a5a2a043a7ac95646a6eb0e2cd404fa9fce1072f87acb88",
+    "encode": {"read": 513.84, "write": 269.33},
+    "decode": {"read": 264.32, "write": 512.00},
     "valu_lane_ops_per_weight": {"encode": 36.51, "decode": 11.92},
 }
 # VALU issue roof: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (a wave64 instruction
@@ -255,6 +255,38 @@ def secondary(layer0, bps, dev):
             "speedup_vs_bf16": round(ms_b / ms_g, 3),
             "algorithmic_gbs": round(alg_g / (ms_g * 1e-3) / 1e9, 1)}
 
+    # Y = W X^T for many vectors on the matrix cores, one batched call for
+    # the layer, beside torch.matmul on the decoded bf16 weights
+    gemm = {"workload": "Y = W X^T (m fp32 vectors) for the same layer's seven matrices, from "
+                        "the E8 indices, one batched call; beside torch.matmul of bf16 X on "
+                        "the decoded bf16 weights",
+            "by_m": {}}
+    for m in (32, 128):
+        xm = [torch.randn(m, e["idx"].shape[1], device=dev) for e in encs]
+        ym = [torch.empty(m, e["idx"].shape[0], device=dev) for e in encs]
+        items = (hq.GemvItem * len(encs))()
+        for i, (e, x, y) in enumerate(zip(encs, xm, ym)):
+            items[i] = hq.GemvItem(e["idx"].data_ptr(), e["coset"].data_ptr(),
+                                   e["scale"].data_ptr(), e["idx"].shape[0], e["idx"].shape[1],
+                                   x.data_ptr(), y.data_ptr())
+        wsg = torch.empty(max(16, hq.lib().hq_gemm_batch_workspace_bytes(len(encs), items, m)),
+                          dtype=torch.uint8, device=dev)
+
+        def gemm_layer():
+            hq.hq_gemm_batch(encs, xm, rht_seed=0, outs=ym, workspace=wsg)
+
+        xmb = [x.to(torch.bfloat16) for x in xm]
+
+        def bf16_gemm_layer():
+            for wm, x in zip(ys, xmb):
+                torch.matmul(x, wm.t())
+
+        ms_m = time_calls(gemm_layer, 10)
+        ms_t = time_calls(bf16_gemm_layer, 10)
+        gemm["by_m"][str(m)] = {"us": round(ms_m * 1e3, 2), "bf16_matmul_us": round(ms_t * 1e3, 2),
+                                "speedup_vs_bf16": round(ms_t / ms_m, 3),
+                                "tflops": round(2.0 * m * w_total / (ms_m * 1e-3) / 1e12, 2)}
+
     # variants on the same layer's weights: per-tile rate control (the
     # generic kernel searches about a dozen scales per tile) and tile 512
     xs0, _, _ = layer0
@@ -344,7 +376,8 @@ def secondary(layer0, bps, dev):
                              "one call (dither regenerated per key)" % (nq, heads, seq),
           "scores_us": round(ms_s * 1e3, 2),
           "scores_gflops": round(2.0 * nq * heads * seq * 128 / (ms_s * 1e-3) / 1e9, 1)}
-    return {"pack": pack, "unpack": unpack, "gemv": gemv, "kv": kv, "variants": variants,
+    return {"pack": pack, "unpack": unpack, "gemv": gemv, "gemm": gemm, "kv": kv,
+            "variants": variants,
             "lattice_sweep": sweep}
 
 
