@@ -560,21 +560,58 @@ static bool gemm_sizes_ok(int64_t rows, int64_t cols, int32_t m) {
          cols <= kGemmMaxCols && m * cols <= kGemmMaxProduct && m * rows <= kGemmMaxProduct;
 }
 
-size_t hq_gemm_workspace_bytes(int64_t rows, int64_t cols, int32_t m) {
-  if (m < 1 || m > kGemmMaxVecs || rows <= 0 || cols <= 0 || !gemm_sizes_ok(rows, cols, m))
-    return 0;
-  return gemm_workspace(rows, cols, m);
+extern "C++" {
+// The launch groups of a batch (up to kGemmMaxItems non-empty matrices
+// each, in item order): fn(group) for each, planned.
+template <typename F>
+static void gemm_groups(int32_t count, const hq_gemv_item* items, int32_t m, F fn) {
+  GemmBatch b;
+  memset(&b, 0, sizeof(b));
+  b.m = m;
+  for (int32_t i = 0; i <= count; ++i) {
+    if ((i == count || b.n == kGemmMaxItems) && b.n > 0) {
+      gemm_plan(b);
+      fn(b);
+      b.n = 0;
+    }
+    if (i == count) break;
+    const hq_gemv_item& it = items[i];
+    if (it.rows == 0 || it.cols == 0) continue;
+    GemmItem& g = b.it[b.n++];
+    memset(&g, 0, sizeof(g));
+    g.idx = it.idx;
+    g.coset = it.coset;
+    g.scale = it.scale;
+    g.rows = it.rows;
+    g.cols = it.cols;
+    g.x = it.x;
+    g.y = it.y;
+  }
 }
+
+static size_t gemm_group_workspace(const GemmBatch& b) {
+  size_t total = 0;
+  for (int k = 0; k < b.n; ++k) total += gemm_item_workspace(b.it[k], b.m);
+  return total;
+}
+}  // extern "C++"
 
 size_t hq_gemm_batch_workspace_bytes(int32_t count, const hq_gemv_item* items, int32_t m) {
   if (count < 0 || (count > 0 && items == nullptr) || m < 1 || m > kGemmMaxVecs) return 0;
+  for (int32_t i = 0; i < count; ++i)
+    if (!gemm_sizes_ok(items[i].rows, items[i].cols, m)) return 0;
   size_t total = 0;
-  for (int32_t i = 0; i < count; ++i) {
-    const hq_gemv_item& it = items[i];
-    if (!gemm_sizes_ok(it.rows, it.cols, m)) return 0;
-    if (it.rows > 0 && it.cols > 0) total += gemm_workspace(it.rows, it.cols, m);
-  }
+  gemm_groups(count, items, m, [&](const GemmBatch& b) { total += gemm_group_workspace(b); });
   return total;
+}
+
+size_t hq_gemm_workspace_bytes(int64_t rows, int64_t cols, int32_t m) {
+  if (rows <= 0 || cols <= 0) return 0;
+  hq_gemv_item it;
+  memset(&it, 0, sizeof(it));
+  it.rows = rows;
+  it.cols = cols;
+  return hq_gemm_batch_workspace_bytes(1, &it, m);
 }
 
 hq_status hq_gemm_batch(const hq_params* p, int32_t count, const hq_gemv_item* items, int32_t m,
@@ -611,35 +648,22 @@ hq_status hq_gemm_batch(const hq_params* p, int32_t count, const hq_gemv_item* i
       return HQ_EINVAL;
   }
   if (!on_device(workspace)) return HQ_EINVAL;
-  // launches of up to kGemmMaxItems matrices, each with its own workspace
-  // slice in item order
-  GemmBatch b;
-  memset(&b, 0, sizeof(b));
-  b.m = m;
-  make_signs(p->rht_seed, p->tile, b.signs);
+  // launches of up to kGemmMaxItems matrices, each group with its own
+  // workspace slice in item order
+  uint32_t signs[8];
+  make_signs(p->rht_seed, p->tile, signs);
   char* ws = static_cast<char*>(workspace);
-  for (int32_t i = 0; i <= count; ++i) {
-    if ((i == count || b.n == kGemmMaxItems) && b.n > 0) {
-      char* base = ws;
-      for (int k = 0; k < b.n; ++k) ws += gemm_workspace(b.it[k].rows, b.it[k].cols, m);
-      gemm_layout(b, base);
-      if (launch_gemm(b, stream) != hipSuccess) return HQ_EDEVICE;
-      b.n = 0;
-    }
-    if (i == count) break;
-    const hq_gemv_item& it = items[i];
-    if (it.rows == 0 || it.cols == 0) continue;
-    GemmItem& g = b.it[b.n++];
-    memset(&g, 0, sizeof(g));
-    g.idx = it.idx;
-    g.coset = it.coset;
-    g.scale = it.scale;
-    g.rows = it.rows;
-    g.cols = it.cols;
-    g.x = it.x;
-    g.y = it.y;
-  }
-  return HQ_OK;
+  bool ok = true;
+  gemm_groups(count, items, m, [&](const GemmBatch& planned) {
+    if (!ok) return;
+    GemmBatch b = planned;
+    memcpy(b.signs, signs, sizeof(signs));
+    const size_t bytes = gemm_group_workspace(b);
+    gemm_layout(b, ws);
+    ws += bytes;
+    ok = launch_gemm(b, stream) == hipSuccess;
+  });
+  return ok ? HQ_OK : HQ_EDEVICE;
 }
 
 hq_status hq_gemm(const hq_params* p, const int8_t* idx, const uint32_t* coset, const float* scale,

@@ -16,14 +16,14 @@
 // Delta / 32 and added to the output accumulator.
 //
 // One launch of each kernel covers up to kGemmMaxItems matrices that share
-// m (a layer's projections); each matrix keeps its own plan, so a batch
-// gives the bits of one call per matrix.
+// m (a layer's projections).
 //
 // split_kernel: one wave per (vector, slice) rotates in fp64 (as hq_gemv)
 // and writes xh, xl [m][cols] bf16.
 // gemm_kernel: a block of W waves owns 32 W rows x 32 NF vectors and a
 // range of slices (a small matrix splits its slices over several blocks,
-// whose partial sums sum_kernel adds in range order); per slice the
+// whose partial sums sum_kernel adds in range order; the ranges depend on
+// the sizes of the whole batch); per slice the
 // 256 x 32 NF hi and lo inputs go through registers (loaded one slice
 // ahead) into LDS in a swizzled order so that the fragment reads hit
 // distinct banks (two buffers, one barrier per slice), and each wave
@@ -340,37 +340,50 @@ int waves_for(int nf) { return nf == 1 ? 4 : 8; }
 
 }  // namespace
 
-void gemm_plan(int64_t rows, int64_t cols, int32_t m, int64_t& kchunks, int64_t& spc) {
-  const int nf = nf_for(m), waves = waves_for(nf);
-  const int64_t base = ((rows + 32 * waves - 1) / (32 * waves)) * ((m + 32 * nf - 1) / (32 * nf));
-  const int64_t slices = cols / kSliceK;
-  // about two blocks per CU slot
-  const int64_t target = nf == 1 ? 1024 : 512;
-  int64_t k = (target + base - 1) / base;
-  k = k < 1 ? 1 : (k > slices ? slices : k);
-  spc = (slices + k - 1) / k;
-  kchunks = (slices + spc - 1) / spc;
+// Slice ranges of a group: one length L (at most 16 slices) for the whole
+// group, the longest that still gives every CU slot a block (512 slots of
+// 4 waves, 256 of 8); a matrix with more slices than L splits them into
+// ceil(slices / L) ranges of near-equal length.  Few ranges keep the
+// partial sums (written and read back once) small next to the index bytes.
+void gemm_plan(GemmBatch& b) {
+  const int nf = nf_for(b.m), waves = waves_for(nf);
+  const int64_t vblocks = (b.m + 32 * nf - 1) / (32 * nf);
+  const int64_t slots = nf == 1 ? 512 : 256;
+  int64_t len = 16;
+  for (; len > 1; --len) {
+    int64_t blocks = 0;
+    for (int i = 0; i < b.n; ++i) {
+      const int64_t slices = b.it[i].cols / kSliceK;
+      blocks += (b.it[i].rows + 32 * waves - 1) / (32 * waves) * vblocks * ((slices + len - 1) / len);
+    }
+    if (blocks >= slots) break;
+  }
+  for (int i = 0; i < b.n; ++i) {
+    GemmItem& it = b.it[i];
+    const int64_t slices = it.cols / kSliceK;
+    it.kchunks = (slices + len - 1) / len;
+    it.spc = (slices + it.kchunks - 1) / it.kchunks;
+    it.kchunks = (slices + it.spc - 1) / it.spc;
+  }
 }
 
-size_t gemm_workspace(int64_t rows, int64_t cols, int32_t m) {
-  int64_t kchunks, spc;
-  gemm_plan(rows, cols, m, kchunks, spc);
-  return (size_t)4 * (size_t)m * (size_t)cols +
-         (kchunks > 1 ? (size_t)4 * (size_t)kchunks * (size_t)m * (size_t)rows : 0);
+size_t gemm_item_workspace(const GemmItem& it, int32_t m) {
+  return (size_t)4 * (size_t)m * (size_t)it.cols +
+         (it.kchunks > 1 ? (size_t)4 * (size_t)it.kchunks * (size_t)m * (size_t)it.rows : 0);
 }
 
 void gemm_layout(GemmBatch& b, char* workspace) {
   const int nf = nf_for(b.m), waves = waves_for(nf);
   const int64_t vblocks = (b.m + 32 * nf - 1) / (32 * nf);
+  gemm_plan(b);
   b.n_blocks = b.n_split = b.n_sum = 0;
   for (int i = 0; i < b.n; ++i) {
     GemmItem& it = b.it[i];
-    gemm_plan(it.rows, it.cols, b.m, it.kchunks, it.spc);
     const size_t half = (size_t)2 * (size_t)b.m * (size_t)it.cols;
     it.xh = reinterpret_cast<uint16_t*>(workspace);
     it.xl = reinterpret_cast<uint16_t*>(workspace + half);
     it.part = it.kchunks > 1 ? reinterpret_cast<float*>(workspace + 2 * half) : nullptr;
-    workspace += gemm_workspace(it.rows, it.cols, b.m);
+    workspace += gemm_item_workspace(it, b.m);
     // blocks: (row ranges x slice ranges) rounded up to the eight XCDs,
     // times the vector blocks
     const int64_t tasks = (it.rows + 32 * waves - 1) / (32 * waves) * it.kchunks;

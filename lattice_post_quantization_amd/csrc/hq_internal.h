@@ -129,12 +129,14 @@ constexpr int64_t kGemmMaxRows = (int64_t)1 << 23;
 // limits that keep the launch grids within 2^32 work-items
 constexpr int64_t kGemmMaxVecs = 65536;
 constexpr int64_t kGemmMaxProduct = (int64_t)1 << 31;   // m cols and m rows
-// The slice ranges of a product (a function of the sizes only, so results
-// do not depend on the device or the batch): enough ranges for about two
-// blocks per CU slot.
-void gemm_plan(int64_t rows, int64_t cols, int32_t m, int64_t& kchunks, int64_t& spc);
-size_t gemm_workspace(int64_t rows, int64_t cols, int32_t m);
-// Fills the workspace pointers, the plan and the numbering of b.it[0 .. b.n).
+// The slice ranges of every matrix of b (kchunks, spc), a function of the
+// group's sizes and m alone, so a call repeats its bits on any device.
+void gemm_plan(GemmBatch& b);
+// Workspace of one planned matrix: the inputs' bf16 terms, then the partial
+// sums when its slices are split.
+size_t gemm_item_workspace(const GemmItem& it, int32_t m);
+// Plans b, then fills the workspace pointers and the numbering of
+// b.it[0 .. b.n).
 void gemm_layout(GemmBatch& b, char* workspace);
 hipError_t launch_gemm(const GemmBatch& b, hipStream_t s);
 

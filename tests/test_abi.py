@@ -325,15 +325,18 @@ def test_gemm_validation_codes():
                        None, None) == hq.HQ_EINVAL
     assert lib.hq_gemm(ctypes.byref(p), FAKE, None, FAKE, 4, 512, FAKE, 1, FAKE, FAKE, 1 << 20,
                        None, None) == hq.HQ_EINVAL
-    # the batch form: workspace is the sum over the items; the same checks
-    # per item; nothing for an empty batch
+    # the batch form: the bf16 terms of every item's inputs at least (the
+    # partial sums depend on the group's plan), a batch of one as hq_gemm;
+    # the same checks per item; nothing for an empty batch
     shapes = ((4096, 4096), (1024, 4096), (4096, 14336), (37, 1536))
     items = (hq.GemvItem * len(shapes))()
     for i, (r, c) in enumerate(shapes):
         items[i] = hq.GemvItem(FAKE, FAKE, FAKE, r, c, FAKE, FAKE)
     for m in (1, 40, 300):
-        assert lib.hq_gemm_batch_workspace_bytes(len(shapes), items, m) == sum(
-            lib.hq_gemm_workspace_bytes(r, c, m) for r, c in shapes)
+        assert lib.hq_gemm_batch_workspace_bytes(len(shapes), items, m) >= sum(
+            4 * m * c for r, c in shapes)
+        assert lib.hq_gemm_batch_workspace_bytes(1, items, m) == lib.hq_gemm_workspace_bytes(
+            4096, 4096, m)
     assert lib.hq_gemm_batch_workspace_bytes(len(shapes), items, 65537) == 0
     items[3].cols = 1000
     assert lib.hq_gemm_batch_workspace_bytes(len(shapes), items, 1) == 0
