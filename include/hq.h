@@ -60,7 +60,11 @@ enum {
   HQ_EINVAL = -1,       /* bad argument (null pointer, size, tile, dtype)  */
   HQ_ERANGE = -2,       /* auto scale cannot keep indices inside int8      */
   HQ_EDEVICE = -3,      /* a HIP call or kernel launch failed              */
-  HQ_EUNSUPPORTED = -4  /* a valid combination the library does not offer */
+  HQ_EUNSUPPORTED = -4, /* a valid combination the library does not offer */
+  HQ_EIO = -5,          /* checkpoint file: cannot open, write or read     */
+  HQ_EFORMAT = -6,      /* checkpoint file: not one, truncated, or a record
+                           whose checksum or offsets do not hold          */
+  HQ_ENOTFOUND = -7     /* checkpoint file: no record of that name        */
 };
 
 /* Lattice; the value is the lattice dimension. [arXiv abstract] item (ii). */
@@ -338,9 +342,9 @@ hq_status hq_gemm(const hq_params* p, const int8_t* idx, const uint32_t* coset,
                   uint32_t* status, hipStream_t stream);
 
 /* Device workspace bytes hq_gemm needs: the rotated inputs as two bf16
-   terms (4 m cols bytes) and, when a small matrix splits its slices over
-   several blocks, their partial sums (4 m rows bytes per range, added in
-   range order; the split is a function of the sizes alone, so results
+   terms (4 m cols bytes) and, when the slices are split over several blocks
+   to occupy the device, their partial sums (4 m rows bytes per range, added
+   in range order; the split is a function of the sizes alone, so results
    repeat bit for bit); 0 for invalid sizes. */
 size_t hq_gemm_workspace_bytes(int64_t rows, int64_t cols, int32_t m);
 
@@ -348,17 +352,20 @@ size_t hq_gemm_workspace_bytes(int64_t rows, int64_t cols, int32_t m);
  * hq_gemm_batch - hq_gemm for `count` matrices with the same m and the same
  * p (a layer's projections), enqueued as three kernel launches per group of
  * up to eight matrices instead of up to three per matrix.  Same passages,
- * arguments per item (hq_gemv_item) and results (bit for bit) as one
- * hq_gemm call per item.  The workspace (device, 16-byte aligned, at least
- * hq_gemm_batch_workspace_bytes(count, items, m) bytes) is divided among the
- * items in order; an item with rows or cols 0 is skipped.
+ * arguments per item (hq_gemv_item) and error bound as hq_gemm.  The slice
+ * ranges summed by separate blocks are chosen for each group of eight as a
+ * whole, so an item may round differently than in a call of its own; the
+ * same call repeats its bits.  The workspace (device, 16-byte aligned, at
+ * least hq_gemm_batch_workspace_bytes(count, items, m) bytes) is divided
+ * among the groups in order; an item with rows or cols 0 is skipped.
  */
 hq_status hq_gemm_batch(const hq_params* p, int32_t count, const hq_gemv_item* items,
                         int32_t m, void* workspace, size_t workspace_bytes,
                         uint32_t* status, hipStream_t stream);
 
-/* Device workspace bytes hq_gemm_batch needs (the sum over the items of
-   hq_gemm_workspace_bytes); 0 for invalid arguments. */
+/* Device workspace bytes hq_gemm_batch needs (each item's input terms and,
+   where its group's plan splits its slices, its partial sums); 0 for
+   invalid arguments. */
 size_t hq_gemm_batch_workspace_bytes(int32_t count, const hq_gemv_item* items, int32_t m);
 
 /*
@@ -466,6 +473,56 @@ hq_status hq_scale_constant(const hq_params* p, double* out);
 
 /* Library version as 10000*major + 100*minor + patch. */
 int32_t hq_version(void);
+
+/*
+ * Checkpoint files - the packed, Rice-coded lattice-index format on disk
+ * ([issue] "Additional context": a packed, Rice-coded lattice-index
+ * checkpoint format, to be read back; [arXiv abstract] item (iii)).  Host
+ * code only: every array below is host memory, and no device call is made.
+ *
+ * A file holds records, one per packed matrix, each named.  Layout (host
+ * byte order; little-endian on every supported host): the file magic
+ * "HQCKPT" 0 1, then per record a 136-byte header (magic "HQRE", header
+ * size, the hq_ckpt_entry below, payload bytes, FNV-1a 64 checksum of the
+ * payload) and the payload: scale[n_tiles] fp32, padded to 8 bytes;
+ * tile_word_offset[n_tiles + 1] uint64; words[n_words] uint32, padded to 8
+ * bytes.  The stream is the one hq_rate packs and hq_unpack decodes (each
+ * tile's k and coset bits inline), so loading a matrix is: read the record,
+ * copy the three arrays to the device, hq_unpack (or hq_unpack_batch).
+ */
+typedef struct {
+  char name[64];          /* NUL-terminated, 1..63 bytes, unique per file   */
+  int32_t lattice;        /* hq_lattice of the encode                       */
+  int32_t tile;           /* 64, 128, 256 or 512                            */
+  float bps;              /* rate R of the encode, 0 < R <= 8               */
+  uint32_t rht_seed;      /* RHT seed of the encode                         */
+  int64_t rows, cols;     /* the matrix; rows * cols = n_tiles * tile       */
+  int64_t n_tiles;
+  uint64_t n_words;       /* stream words, tile_word_offset[n_tiles]        */
+} hq_ckpt_entry;
+
+/* Appends one record to `path` (created with the file magic if missing).
+ * scale [n_tiles], tile_word_offset [n_tiles + 1] (starting at 0, never
+ * decreasing, ending at n_words) and words [n_words] are host arrays.
+ * HQ_EINVAL: an invalid entry or offsets, a NULL array, or a name the file
+ * already holds; HQ_EFORMAT: the file exists but is not a checkpoint;
+ * HQ_EIO: the file cannot be opened or written. */
+hq_status hq_ckpt_append(const char* path, const hq_ckpt_entry* e, const float* scale,
+                         const uint64_t* tile_word_offset, const uint32_t* words);
+
+/* Number of records in `path` (HQ_EIO / HQ_EFORMAT as above). */
+hq_status hq_ckpt_count(const char* path, int32_t* count);
+
+/* The entry of record i (0-based, file order); HQ_ENOTFOUND past the end. */
+hq_status hq_ckpt_entry_at(const char* path, int32_t i, hq_ckpt_entry* e);
+
+/* Reads the record named `name` into e and the host arrays (capacities in
+ * tiles and words; HQ_EINVAL if too small).  HQ_ENOTFOUND: no such record;
+ * HQ_EFORMAT: a truncated record, a checksum mismatch or offsets that do
+ * not hold (the arrays' contents are then unspecified). */
+hq_status hq_ckpt_read(const char* path, const char* name, hq_ckpt_entry* e, float* scale,
+                       uint64_t* tile_word_offset, uint32_t* words, int64_t capacity_tiles,
+                       uint64_t capacity_words);
 
 #ifdef __cplusplus
 }

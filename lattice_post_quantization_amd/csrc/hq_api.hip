@@ -808,6 +808,9 @@ const char* hq_status_string(hq_status s) {
     case HQ_ERANGE: return "auto scale would overflow the int8 indices";
     case HQ_EDEVICE: return "HIP call or kernel launch failed";
     case HQ_EUNSUPPORTED: return "unsupported parameter combination";
+    case HQ_EIO: return "checkpoint file cannot be opened, written or read";
+    case HQ_EFORMAT: return "not a checkpoint file, or a damaged record";
+    case HQ_ENOTFOUND: return "no checkpoint record of that name";
     default: return "unknown status";
   }
 }

@@ -17,6 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhq.so")
 
 HQ_OK, HQ_EINVAL, HQ_ERANGE, HQ_EDEVICE, HQ_EUNSUPPORTED = 0, -1, -2, -3, -4
+HQ_EIO, HQ_EFORMAT, HQ_ENOTFOUND = -5, -6, -7
 HQ_Z, HQ_A2, HQ_D4, HQ_E8 = 1, 2, 4, 8
 HQ_F32, HQ_BF16 = 0, 1
 HQ_SCALE_AUTO, HQ_DITHER, HQ_WANT_COORDS, HQ_RATE_CONTROL, HQ_RATE_GIVEN = 1, 2, 4, 8, 16
@@ -64,6 +65,13 @@ class GemvItem(ctypes.Structure):
                 ("y", ctypes.c_void_p)]
 
 
+class CkptEntry(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 64), ("lattice", ctypes.c_int32),
+                ("tile", ctypes.c_int32), ("bps", ctypes.c_float), ("rht_seed", ctypes.c_uint32),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("n_tiles", ctypes.c_int64),
+                ("n_words", ctypes.c_uint64)]
+
+
 class DecodeItem(ctypes.Structure):
     _fields_ = [("idx", ctypes.c_void_p), ("coset", ctypes.c_void_p), ("scale", ctypes.c_void_p),
                 ("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("y", ctypes.c_void_p)]
@@ -76,6 +84,10 @@ _I32, _I64, _U32, _U64, _SZ = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32,
 _PP = ctypes.POINTER(Params)
 
 _SIGNATURES = {
+    "hq_ckpt_append": (_I32, [ctypes.c_char_p, _P, _P, _P, _P]),
+    "hq_ckpt_count": (_I32, [ctypes.c_char_p, _P]),
+    "hq_ckpt_entry_at": (_I32, [ctypes.c_char_p, _I32, _P]),
+    "hq_ckpt_read": (_I32, [ctypes.c_char_p, ctypes.c_char_p, _P, _P, _P, _P, _I64, _U64]),
     "hq_encode_tiles": (_I32, [_PP, _P, _I32, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P]),
     "hq_decode_tiles": (_I32, [_PP, _P, _P, _P, _I64, _I64, _P, _I32, _P, _P]),
     "hq_rate": (_I32, [_PP, _P, _P, _I64, _P, _P, _P, _P, _U64, _P, _P, _SZ, _P, _P]),
@@ -331,6 +343,67 @@ def hq_unpack(stream, tile_word_offset, lattice="E8", tile=256, status=None, out
                            _stream(dev))
     _check(code, "hq_unpack")
     return {"idx": idx, "coset": coset if nw else None, "rice_k": rice_k}
+
+
+def _entry_dict(e):
+    names = {v: k for k, v in LATTICES.items()}
+    return {"name": e.name.decode(), "lattice": names[e.lattice], "tile": e.tile,
+            "bps": e.bps, "rht_seed": e.rht_seed, "rows": e.rows, "cols": e.cols,
+            "n_tiles": e.n_tiles, "n_words": e.n_words}
+
+
+def ckpt_save(path, name, packed, scale, rows, cols, lattice="E8", tile=256, bps=4.0,
+              rht_seed=0):
+    """Append one packed matrix to the checkpoint file `path`: packed is the
+    dict hq_rate returns with pack=True (stream, tile_word_offset), scale the
+    encode's per-tile scales.  The arrays are copied to host memory."""
+    offs = packed["tile_word_offset"].detach().to("cpu", torch.int64).contiguous()
+    n_tiles = offs.numel() - 1
+    n_words = int(offs[-1])
+    if packed["stream"].numel() < n_words:
+        raise ValueError("stream holds fewer words than tile_word_offset ends at")
+    words = packed["stream"].detach()[:n_words].to("cpu").contiguous()
+    sc = scale.detach().to("cpu", torch.float32).contiguous().reshape(-1)
+    e = CkptEntry(name.encode(), LATTICES[lattice], tile, bps, rht_seed, rows, cols, n_tiles,
+                  n_words)
+    _check(lib().hq_ckpt_append(os.fsencode(path), ctypes.byref(e), sc.data_ptr(),
+                                offs.data_ptr(), words.data_ptr() if n_words else None),
+           "hq_ckpt_append")
+
+
+def ckpt_entries(path):
+    """The entries of a checkpoint file, in file order (list of dicts)."""
+    n = ctypes.c_int32()
+    _check(lib().hq_ckpt_count(os.fsencode(path), ctypes.byref(n)), "hq_ckpt_count")
+    out = []
+    for i in range(n.value):
+        e = CkptEntry()
+        _check(lib().hq_ckpt_entry_at(os.fsencode(path), i, ctypes.byref(e)), "hq_ckpt_entry_at")
+        out.append(_entry_dict(e))
+    return out
+
+
+def ckpt_load(path, name, device=None):
+    """Read the record `name`: a dict with the entry's fields plus stream
+    (int32 words), tile_word_offset (int64) and scale (fp32) on `device`
+    (host tensors if None), ready for hq_unpack."""
+    meta = {e["name"]: e for e in ckpt_entries(path)}
+    if name not in meta:
+        raise HQError(HQ_ENOTFOUND, "hq_ckpt_read")
+    m = meta[name]
+    sc = torch.empty(max(m["n_tiles"], 1), dtype=torch.float32)
+    offs = torch.empty(m["n_tiles"] + 1, dtype=torch.int64)
+    words = torch.empty(max(m["n_words"], 1), dtype=torch.int32)
+    e = CkptEntry()
+    _check(lib().hq_ckpt_read(os.fsencode(path), name.encode(), ctypes.byref(e), sc.data_ptr(),
+                              offs.data_ptr(), words.data_ptr(), m["n_tiles"], m["n_words"]),
+           "hq_ckpt_read")
+    res = _entry_dict(e)
+    res.update(stream=words, tile_word_offset=offs, scale=sc[:m["n_tiles"]])
+    if device is not None:
+        for k in ("stream", "tile_word_offset", "scale"):
+            res[k] = res[k].to(device)
+    return res
 
 
 class UnpackItem(ctypes.Structure):

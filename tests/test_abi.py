@@ -71,7 +71,7 @@ def test_coset_words_and_workspace():
 
 
 def test_status_strings():
-    for code in (0, -1, -2, -3, -4, 5):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, 5):
         assert hq.status_string(code)
 
 
