@@ -366,6 +366,28 @@ def secondary(layer0, bps, dev):
         hq.hq_kv_scores(qv, encs_kv[0], 1, dither_seed=2, dither_base=0, out=sc, workspace=wsq)
 
     ms_s = time_calls(kv_scores, 10)
+    # decode attention: 4 queries per KV head (grouped queries) over each of
+    # the 8 heads' compressed K and V, one call per head; beside torch's
+    # scaled_dot_product_attention on the decoded bf16 caches
+    qa = torch.randn(heads, 4, 128, device=dev)
+    oa = torch.empty(heads, 4, 128, device=dev)
+    wsa = torch.empty(hq.lib().hq_kv_attention_workspace_bytes(heads, 4, seq), dtype=torch.uint8,
+                      device=dev)
+    cache = dict(rht_seed=1, dither_seed=2, dither_base=0)
+
+    def kv_attention():
+        hq.hq_kv_attention(qa, encs_kv[0], encs_kv[1], k_cache=cache, v_cache=cache, out=oa,
+                           workspace=wsa)
+
+    kd = ys[0].view(heads, seq, 128)
+    vd = ys[1].view(heads, seq, 128)
+    qab = qa.to(torch.bfloat16)
+
+    def bf16_attention():
+        torch.nn.functional.scaled_dot_product_attention(qab, kd, vd)
+
+    ms_a = time_calls(kv_attention, 10)
+    ms_ab = time_calls(bf16_attention, 10)
     # per 128-vector: 256 B in / 128 B idx + 4 coset + 1 k + 4 bits + 4 scale
     kv = {"workload": "dithered E8 encode and decode of K and V [8, 32768, 128] bf16 "
                       "(%d vectors of 128, 4 bps)" % n_vec,
@@ -375,7 +397,14 @@ def secondary(layer0, bps, dev):
           "scores_workload": "%d queries against all %d x %d compressed keys of the K cache, "
                              "one call (dither regenerated per key)" % (nq, heads, seq),
           "scores_us": round(ms_s * 1e3, 2),
-          "scores_gflops": round(2.0 * nq * heads * seq * 128 / (ms_s * 1e-3) / 1e9, 1)}
+          "scores_gflops": round(2.0 * nq * heads * seq * 128 / (ms_s * 1e-3) / 1e9, 1),
+          "attention_workload": "decode attention of 4 queries per head over all %d heads x %d "
+                                "compressed K and V vectors (one call), beside "
+                                "scaled_dot_product_attention on the decoded bf16 caches"
+                                % (heads, seq),
+          "attention_us": round(ms_a * 1e3, 2),
+          "attention_bf16_sdpa_us": round(ms_ab * 1e3, 2),
+          "attention_cache_gbs": round(2 * heads * seq * (128 + 8) / (ms_a * 1e-3) / 1e9, 1)}
     return {"pack": pack, "unpack": unpack, "gemv": gemv, "gemm": gemm, "kv": kv,
             "variants": variants,
             "lattice_sweep": sweep}

@@ -397,6 +397,42 @@ hq_status hq_kv_scores(const hq_params* p, const float* q, int64_t n_q,
 size_t hq_kv_scores_workspace_bytes(int64_t n_q);
 
 /*
+ * hq_kv_attention - decode attention over compressed K and V, per head:
+ * out_hj = sum_k a_hjk vhat_hk, a_hjk = softmax over k of tau q_hj . khat_hk,
+ * with khat and vhat the vectors hq_decode_tiles would reconstruct (dither
+ * subtracted), without forming either.
+ *
+ * Passages: as hq_kv_scores.  The pages give no attention procedure; this
+ * is softmax attention of one head over the decoded cache.  Both caches
+ * stay in the lattice domain: scores as in hq_kv_scores (queries rotated
+ * once, scaled by tau log2(e) / sqrt(n), so the softmax runs in base 2), the
+ * weighted sum of the values' yhat = Delta (p - d) is formed per query and
+ * rotated back once: sum_k a_jk vhat_k = s_V (.) H (sum_k a_jk yhatV_k) /
+ * sqrt(n).  Keys are split into ranges; each keeps a running maximum, its
+ * exponent sum and weighted sum (fp32), and the ranges are merged in order
+ * (deterministic).
+ *
+ * pk, pv: the K and V encodes' parameters (lattice E8, tile 128; rht_seed;
+ * HQ_DITHER with dither_seed and dither_base = global index of vector 0, or
+ * no dither).  k_* and v_*: [n_heads][n_keys] vectors as hq_kv_encode writes
+ * them for the whole cache (key k of head h is vector h n_keys + k; idx
+ * 16-byte aligned); n_keys >= 1 when n_q > 0.  q [n_heads][n_q][128] fp32
+ * (16-byte aligned), 1 <= n_heads <= 65535, n_q <= 65536 queries per head
+ * (grouped queries share a head); tau the score scale (finite; 1/sqrt(128)
+ * for standard attention); out [n_heads][n_q][128] fp32; workspace: device
+ * scratch of at least hq_kv_attention_workspace_bytes(n_heads, n_q, n_keys)
+ * bytes, 16-byte aligned.  Errors as hq_kv_scores.
+ */
+hq_status hq_kv_attention(const hq_params* pk, const int8_t* k_idx, const uint32_t* k_coset,
+                          const float* k_scale, const hq_params* pv, const int8_t* v_idx,
+                          const uint32_t* v_coset, const float* v_scale, int64_t n_heads,
+                          int64_t n_keys, const float* q, int64_t n_q, float tau, float* out,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Device workspace bytes hq_kv_attention needs; 0 for invalid sizes. */
+size_t hq_kv_attention_workspace_bytes(int64_t n_heads, int64_t n_q, int64_t n_keys);
+
+/*
  * hq_kv_encode - encode KV-cache vectors ([ICLR abstract]: subtractive
  * dither keeps each cached inner product unbiased per vector; [arXiv
  * abstract] item (iv)).  The vectors are tiles of n = p->tile = head_dim

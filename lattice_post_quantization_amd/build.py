@@ -28,7 +28,7 @@ FLAGS = [
     "-I", INCLUDE, "-I", CSRC,
 ]
 SOURCES = ["hq_encode.hip", "hq_decode.hip", "hq_e8fast.hip", "hq_fast128.hip", "hq_rate.hip", "hq_unpack.hip",
-           "hq_gemv.hip", "hq_gemm.hip", "hq_kvscore.hip", "hq_api.hip", "hq_ckpt.cpp"]
+           "hq_gemv.hip", "hq_gemm.hip", "hq_kvscore.hip", "hq_kvattn.hip", "hq_api.hip", "hq_ckpt.cpp"]
 
 
 def _compile(src):

@@ -14,6 +14,7 @@
 #include "hq.h"
 #include "hq_device.h"
 #include "hq_internal.h"
+#include "hq_kvattn.h"
 
 namespace hq {
 }
@@ -794,6 +795,84 @@ hq_status hq_kv_scores(const hq_params* p, const float* q, int64_t n_q, const in
   a.dither_seed = p->dither_seed;
   a.dither_base = p->dither_base;
   return launched(launch_scores(a, stream));
+}
+
+static bool attn_sizes_ok(int64_t n_heads, int64_t n_q, int64_t n_keys) {
+  return n_heads >= 1 && n_heads <= 65535 && n_q >= 0 && n_q <= 65536 && n_keys >= 0 &&
+         n_heads * n_keys <= ((int64_t)1 << 32) && n_heads * n_q <= ((int64_t)1 << 31);
+}
+
+size_t hq_kv_attention_workspace_bytes(int64_t n_heads, int64_t n_q, int64_t n_keys) {
+  if (!attn_sizes_ok(n_heads, n_q, n_keys) || n_q == 0 || n_keys == 0) return 0;
+  return attn_workspace(n_heads, n_q, n_keys);
+}
+
+// A K or V cache's parameters for hq_kv_attention.
+static hq_status check_cache(const hq_params* p, int64_t n_keys) {
+  hq_status st = check_params(p);
+  if (st != HQ_OK) return st;
+  if (p->lattice != HQ_E8 || p->tile != 128) return HQ_EUNSUPPORTED;
+  if ((p->flags & HQ_DITHER) && p->dither_base + n_keys > ((int64_t)1 << 32)) return HQ_EINVAL;
+  return HQ_OK;
+}
+
+hq_status hq_kv_attention(const hq_params* pk, const int8_t* k_idx, const uint32_t* k_coset,
+                          const float* k_scale, const hq_params* pv, const int8_t* v_idx,
+                          const uint32_t* v_coset, const float* v_scale, int64_t n_heads,
+                          int64_t n_keys, const float* q, int64_t n_q, float tau, float* out,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!attn_sizes_ok(n_heads, n_q, n_keys) || !isfinite(tau)) {
+    if (check_params(pk) != HQ_OK) return check_params(pk);
+    return HQ_EINVAL;
+  }
+  hq_status st = check_cache(pk, n_heads * n_keys);
+  if (st != HQ_OK) return st;
+  st = check_cache(pv, n_heads * n_keys);
+  if (st != HQ_OK) return st;
+  if (n_q == 0) return HQ_OK;
+  if (n_keys == 0) return HQ_EINVAL;              // softmax over no keys
+  if (k_idx == nullptr || k_coset == nullptr || k_scale == nullptr || v_idx == nullptr ||
+      v_coset == nullptr || v_scale == nullptr || q == nullptr || out == nullptr ||
+      workspace == nullptr)
+    return HQ_EINVAL;
+  if (workspace_bytes < attn_workspace(n_heads, n_q, n_keys)) return HQ_EINVAL;
+  if (!aligned16(q) || !aligned16(k_idx) || !aligned16(v_idx) || !aligned16(workspace) ||
+      ((uintptr_t)k_coset & 3u) || ((uintptr_t)k_scale & 3u) || ((uintptr_t)v_coset & 3u) ||
+      ((uintptr_t)v_scale & 3u) || ((uintptr_t)out & 3u))
+    return HQ_EINVAL;
+  if (!on_device(q) || !on_device(k_idx) || !on_device(k_coset) || !on_device(k_scale) ||
+      !on_device(v_idx) || !on_device(v_coset) || !on_device(v_scale) || !on_device(out) ||
+      !on_device(workspace))
+    return HQ_EINVAL;
+  AttnLaunch a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.n_q = n_q;
+  a.k_idx = k_idx;
+  a.k_coset = k_coset;
+  a.k_scale = k_scale;
+  a.v_idx = v_idx;
+  a.v_coset = v_coset;
+  a.v_scale = v_scale;
+  a.n_keys = n_keys;
+  a.n_heads = n_heads;
+  a.out = out;
+  a.qr = static_cast<float*>(workspace);
+  a.part = a.qr + (size_t)(n_heads * n_q) * 128;
+  attn_plan(n_heads, n_q, n_keys, a.keys_per_wave, a.n_ranges);
+  uint32_t sg[8];
+  make_signs(pk->rht_seed, 128, sg);
+  memcpy(a.k_signs, sg, sizeof(a.k_signs));
+  make_signs(pv->rht_seed, 128, sg);
+  memcpy(a.v_signs, sg, sizeof(a.v_signs));
+  a.k_dither = (pk->flags & HQ_DITHER) != 0;
+  a.v_dither = (pv->flags & HQ_DITHER) != 0;
+  a.k_seed = pk->dither_seed;
+  a.v_seed = pv->dither_seed;
+  a.k_base = pk->dither_base;
+  a.v_base = pv->dither_base;
+  a.q_scale = (double)tau * 1.4426950408889634 / sqrt(128.0);   // tau log2(e) / sqrt(n)
+  return launched(launch_attention(a, stream));
 }
 
 int32_t hq_coset_words(const hq_params* p) {

@@ -9,6 +9,7 @@ a missing library raises instead of falling back to anything else.
 """
 
 import ctypes
+import math
 import os
 
 import torch  # loads the HIP runtime first, so libhq.so binds to the same one
@@ -103,6 +104,9 @@ _SIGNATURES = {
     "hq_gemv_batch_workspace_bytes": (_SZ, [_I32, _P, _I32]),
     "hq_kv_scores": (_I32, [_PP, _P, _I64, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
     "hq_kv_scores_workspace_bytes": (_SZ, [_I64]),
+    "hq_kv_attention": (_I32, [_PP, _P, _P, _P, _PP, _P, _P, _P, _I64, _I64, _P, _I64,
+                               ctypes.c_float, _P, _P, _SZ, _P]),
+    "hq_kv_attention_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "hq_kv_encode": (_I32, [_PP, _P, _I32, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "hq_encode_batch": (_I32, [_PP, _I32, _I32, _P, _P, _P]),
     "hq_decode_batch": (_I32, [_PP, _I32, _I32, _P, _P, _P]),
@@ -576,6 +580,42 @@ def hq_kv_scores(q, enc, rht_seed=0, dither_seed=None, dither_base=0, out=None,
                               n_keys, _ptr(sc), _ptr(ws), ws.numel(), _stream(dev))
     _check(code, "hq_kv_scores")
     return sc
+
+
+def hq_kv_attention(q, kenc, venc, tau=None, k_cache=None, v_cache=None, out=None,
+                    workspace=None):
+    """out_hj = softmax_k(tau q_hj . khat_hk) . vhat_h for queries q fp32,
+    (n_q, 128) for one head or (n_heads, n_q, 128), over K and V encoded by
+    hq_kv_encode for the whole cache (kenc, venc: its dicts; n_heads equal
+    runs of keys).  k_cache / v_cache: dicts with the encodes' rht_seed,
+    dither_seed (None: rotation-only) and dither_base.  tau defaults to
+    1 / sqrt(128).  Returns fp32 shaped like q."""
+    _device_tensor(q, "q")
+    n_heads = 1 if q.dim() == 2 else q.shape[0]
+    n_q = q.shape[-2]
+    if kenc["idx"].shape[0] % n_heads:
+        raise ValueError("the cache does not split into n_heads equal runs")
+    n_keys = kenc["idx"].shape[0] // n_heads
+    dev = q.device
+    tau = 1.0 / math.sqrt(128.0) if tau is None else tau
+
+    def params(c):
+        c = dict(c or {})
+        ds = c.get("dither_seed")
+        return make_params("E8", 128, 4.0, c.get("rht_seed", 0), HQ_DITHER if ds is not None else 0,
+                           0 if ds is None else ds, c.get("dither_base", 0))
+
+    pk, pv = params(k_cache), params(v_cache)
+    o = out if out is not None else torch.empty(q.shape, dtype=torch.float32, device=dev)
+    nb = lib().hq_kv_attention_workspace_bytes(n_heads, n_q, n_keys)
+    ws = workspace if workspace is not None else torch.empty(max(nb, 16), dtype=torch.uint8,
+                                                             device=dev)
+    code = lib().hq_kv_attention(ctypes.byref(pk), _ptr(kenc["idx"]), _ptr(kenc["coset"]),
+                                 _ptr(kenc["scale"]), ctypes.byref(pv), _ptr(venc["idx"]),
+                                 _ptr(venc["coset"]), _ptr(venc["scale"]), n_heads, n_keys,
+                                 _ptr(q), n_q, tau, _ptr(o), _ptr(ws), ws.numel(), _stream(dev))
+    _check(code, "hq_kv_attention")
+    return o
 
 
 def hq_kv_encode(kv, bps=4.0, rht_seed=0, dither_seed=None, dither_base=0, status=None,

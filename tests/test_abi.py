@@ -353,6 +353,33 @@ def test_gemm_validation_codes():
     assert lib.hq_gemm_batch(ctypes.byref(p), 1, items, 1, FAKE, 10, None, None) == hq.HQ_EINVAL
 
 
+def test_kv_attention_validation_codes():
+    lib = hq.lib()
+    pk = hq.make_params("E8", 128, 4.0, 1, hq.HQ_DITHER, 2, 0)
+    pv = hq.make_params("E8", 128, 4.0, 7)
+    assert lib.hq_kv_attention_workspace_bytes(8, 4, 32768) >= 8 * 4 * 128 * 4
+    for nh, nq, nk in ((1, 0, 10), (1, 4, 0), (1, 65537, 10), (1, 4, (1 << 32) + 1),
+                       (0, 4, 10), (65536, 1, 10), (8, 4, 1 << 30)):
+        assert lib.hq_kv_attention_workspace_bytes(nh, nq, nk) == 0
+
+    def call(pk=pk, pv=pv, n_heads=2, n_keys=100, n_q=4, tau=0.1, ws=1 << 30, k=FAKE, out=FAKE):
+        return lib.hq_kv_attention(ctypes.byref(pk), k, FAKE, FAKE, ctypes.byref(pv), FAKE, FAKE,
+                                   FAKE, n_heads, n_keys, FAKE, n_q, tau, out, FAKE, ws, None)
+    # nothing to compute; no keys for a query; E8 / 128 only
+    assert call(n_q=0, k=None, out=None) == hq.HQ_OK
+    assert call(n_keys=0) == hq.HQ_EINVAL
+    assert call(pk=hq.make_params("E8", 256, 4.0)) == hq.HQ_EUNSUPPORTED
+    assert call(pv=hq.make_params("D4", 128, 4.0)) == hq.HQ_EUNSUPPORTED
+    # sizes, scale, workspace, nulls, dither range
+    assert call(n_q=65537) == hq.HQ_EINVAL
+    assert call(n_heads=0) == hq.HQ_EINVAL
+    assert call(tau=float("inf")) == hq.HQ_EINVAL
+    assert call(ws=16) == hq.HQ_EINVAL
+    assert call(k=None) == hq.HQ_EINVAL
+    far = hq.make_params("E8", 128, 4.0, 1, hq.HQ_DITHER, 2, (1 << 32) - 10)
+    assert call(pk=far) == hq.HQ_EINVAL
+
+
 def test_kv_scores_validation_codes():
     lib = hq.lib()
     p = hq.make_params("E8", 128, 4.0, 1, hq.HQ_DITHER, 2, 0)

@@ -259,6 +259,107 @@ def test_kv_dither_parity_and_unbiasedness():
     assert abs(stat) <= 4 * se
 
 
+def _attn_tol(q, k_hat, v_hat, tau):
+    """Bound for hq_kv_attention against the fp64 attention of the same
+    decoded cache.  A score (base-2 units, tau log2(e) q . khat) is an fp32
+    sum of 128 products of fp32-rounded factors: its error is at most
+    2^-16 tau log2(e) |q| max|khat| (orthonormal rotation: the rotated
+    factors keep the norms).  An error ds in the scores moves the softmax
+    weights by at most a factor 2^(2 ds), so the output by at most
+    2 ln2 ds max|vhat|; the fp32 running sums over a range and the merge add
+    at most 2^-14 max|vhat|."""
+    ds = 2.0 ** -16 * tau * math.log2(math.e) * np.linalg.norm(q, axis=1) * \
+        np.max(np.linalg.norm(k_hat, axis=1))
+    vmax = np.max(np.abs(v_hat))
+    return ((2 * math.log(2) * ds + 2.0 ** -14) * vmax)[:, None]
+
+
+@pytest.mark.parametrize("dither", [True, False])
+def test_kv_attention_parity(dither):
+    """hq_kv_attention against the oracle's softmax attention over its own
+    dithered (or rotation-only) decode of K and V: 3001 keys (ragged against
+    the key ranges and the four key residues), K with RHT seed 1 and dither
+    seed 2, V with RHT seed 7 and dither seed 3 at global base 3001, the K/V
+    workload's distribution (N(0, 1) with per-channel offsets), 11 queries
+    (three query groups), tau = 1/sqrt(128) and 0.5."""
+    from oracle.attention import attention
+    kb, vb = workloads.kv_layer()
+    n = 3001
+    kx = workloads.bf16_bits_to_f64(kb[0, :n]).reshape(n, 128)
+    vx = workloads.bf16_bits_to_f64(vb[0, :n]).reshape(n, 128)
+    ks = dict(rht_seed=1, dither_seed=2 if dither else None, dither_base=0)
+    vs = dict(rht_seed=7, dither_seed=3 if dither else None, dither_base=n)
+    say("case: kv attention n_keys=%d dither=%s" % (n, dither))
+    ko = codec.encode(kx, "E8", 128, 4.0, rht_seed=1, dither_seed=ks["dither_seed"],
+                      dither_base=0)
+    vo = codec.encode(vx, "E8", 128, 4.0, rht_seed=7, dither_seed=vs["dither_seed"],
+                      dither_base=n)
+    k_hat = codec.decode(ko["idx"], ko["coset"], ko["scale"], "E8", 128, 1,
+                         dither_seed=ks["dither_seed"], dither_base=0).reshape(n, 128)
+    v_hat = codec.decode(vo["idx"], vo["coset"], vo["scale"], "E8", 128, 7,
+                         dither_seed=vs["dither_seed"], dither_base=n).reshape(n, 128)
+
+    def dev_enc(o):
+        return {"idx": torch.from_numpy(o["idx"].astype(np.int8).reshape(n, 128)).cuda(),
+                "coset": torch.from_numpy(o["coset"].astype(np.uint32).view(np.int32).reshape(n)).cuda(),
+                "scale": torch.from_numpy(o["scale"].astype(np.float32)).cuda()}
+
+    kd, vd = dev_enc(ko), dev_enc(vo)
+    q = np.random.default_rng(17).standard_normal((11, 128)).astype(np.float32)
+    qd = torch.from_numpy(q).cuda()
+    for tau in (1.0 / math.sqrt(128.0), 0.5):
+        out = hq.hq_kv_attention(qd, kd, vd, tau=tau, k_cache=ks, v_cache=vs)
+        out2 = hq.hq_kv_attention(qd, kd, vd, tau=tau, k_cache=ks, v_cache=vs)
+        torch.cuda.synchronize()
+        ref = attention(q.astype(np.float64), k_hat, v_hat, tau)
+        tol = _attn_tol(q.astype(np.float64), k_hat, v_hat, tau)
+        err = np.abs(T.host(out).astype(np.float64) - ref)
+        say("  tau %.4f  max err %.3e  max tol %.3e" % (tau, err.max(), tol.max()))
+        assert np.all(err <= tol), "max err/tol %.3g" % np.max(err / tol)
+        assert torch.equal(out, out2)
+
+
+def test_kv_attention_all_heads_against_decoded_cache():
+    """At the workload's size (all heads of [8, 32768, 128], dithered K and
+    V encoded as one cache each, 4 queries per head in one call):
+    hq_kv_attention agrees, within the same bound per head, with fp64
+    attention over the same cache decoded by hq_decode_tiles (the rotated-
+    domain form equals decode-then-attend), and a single key gives that
+    key's decoded value."""
+    kb, vb = workloads.kv_layer()
+    heads, nkeys = kb.shape[0], kb.shape[1]
+    say("case: kv attention %d heads x %d keys" % (heads, nkeys))
+    kd = T.bf16_device(kb, (heads * nkeys, 128))
+    vd = T.bf16_device(vb, (heads * nkeys, 128))
+    ks = dict(rht_seed=1, dither_seed=2, dither_base=0)
+    vs = dict(rht_seed=1, dither_seed=2, dither_base=heads * nkeys)
+    ke = hq.hq_kv_encode(kd, 4.0, 1, dither_seed=2, dither_base=0)
+    ve = hq.hq_kv_encode(vd, 4.0, 1, dither_seed=2, dither_base=heads * nkeys)
+    q = torch.from_numpy(workloads.kv_queries()[:4 * heads].astype(np.float32)
+                         .reshape(heads, 4, 128)).cuda()
+    tau = 1.0 / math.sqrt(128.0)
+    out = hq.hq_kv_attention(q, ke, ve, tau=tau, k_cache=ks, v_cache=vs)
+    k_hat = hq.hq_decode_tiles(ke["idx"], ke["coset"], ke["scale"], "E8", 128, 1, torch.float32,
+                               dither_seed=2, dither_base=0).double().reshape(heads, nkeys, 128)
+    v_hat = hq.hq_decode_tiles(ve["idx"], ve["coset"], ve["scale"], "E8", 128, 1, torch.float32,
+                               dither_seed=2, dither_base=heads * nkeys).double() \
+        .reshape(heads, nkeys, 128)
+    ref = torch.softmax(tau * (q.double() @ k_hat.transpose(1, 2).contiguous()), dim=2) @ v_hat
+    torch.cuda.synchronize()
+    for h in range(heads):
+        tol = _attn_tol(T.host(q[h]).astype(np.float64), T.host(k_hat[h]), T.host(v_hat[h]), tau)
+        err = np.abs(T.host(out[h]).astype(np.float64) - T.host(ref[h]))
+        say("  head %d max err %.3e  max tol %.3e" % (h, err.max(), tol.max()))
+        assert np.all(err <= tol), "head %d" % h
+    one = {k: v[5:6] for k, v in ke.items() if k in ("idx", "coset", "scale")}
+    onev = {k: v[5:6] for k, v in ve.items() if k in ("idx", "coset", "scale")}
+    out1 = hq.hq_kv_attention(q[0], one, onev, tau=tau, k_cache=dict(ks, dither_base=5),
+                              v_cache=dict(vs, dither_base=heads * nkeys + 5))
+    torch.cuda.synchronize()
+    v5 = T.host(v_hat[0, 5]).astype(np.float64)
+    assert np.all(np.abs(T.host(out1).astype(np.float64) - v5[None, :]) <= 2.0 ** -20 * np.abs(v5).max())
+
+
 def test_edge_cases_and_status_bits():
     dev = torch.device("cuda")
     # empty input: no-op
