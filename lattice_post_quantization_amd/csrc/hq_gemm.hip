@@ -262,19 +262,44 @@ __global__ __launch_bounds__(64 * W, 2) void gemm_kernel(GemmBatch bt) {
     f32x16 acc[NF];
 #pragma unroll
     for (int f = 0; f < NF; ++f) acc[f] = (f32x16){};
-#pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      // block of step s for this lane half
+    // step s covers block 4 (s / 2) + 2 h + s % 2 of this lane half; the
+    // next step's inputs and A fragment are formed before this step's
+    // products are issued
+    uint4 cbh[NF], cbl[NF], nbh[NF], nbl[NF];
+    auto ldb = [&](int s, uint4* hh, uint4* ll) {
       const int q = 4 * (s >> 1) + 2 * h + (s & 1);
-      const uint32_t c = (cw >> q) & 1u;
-      const bf16x8 af = a_fragment(d[2 * s], d[2 * s + 1], c);
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
         const int j = 32 * f + li;
         const int slot = j * 32 + (q ^ (j & 31));
-        acc[f] = mfma32(af, __builtin_bit_cast(bf16x8, Bh[slot]), acc[f]);
-        acc[f] = mfma32(af, __builtin_bit_cast(bf16x8, Bl[slot]), acc[f]);
+        hh[f] = Bh[slot];
+        ll[f] = Bl[slot];
       }
+    };
+    auto afr = [&](int s) {
+      const int q = 4 * (s >> 1) + 2 * h + (s & 1);
+      return a_fragment(d[2 * s], d[2 * s + 1], (cw >> q) & 1u);
+    };
+    ldb(0, cbh, cbl);
+    bf16x8 af = afr(0);
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      bf16x8 afn = af;
+      if (s + 1 < 16) {
+        ldb(s + 1, nbh, nbl);
+        afn = afr(s + 1);
+      }
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        acc[f] = mfma32(af, __builtin_bit_cast(bf16x8, cbh[f]), acc[f]);
+        acc[f] = mfma32(af, __builtin_bit_cast(bf16x8, cbl[f]), acc[f]);
+      }
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        cbh[f] = nbh[f];
+        cbl[f] = nbl[f];
+      }
+      af = afn;
     }
     if (t + 1 < t_end) put(b ^ 1);
     // ---- out += (Delta / 32) acc; register r holds row 8 (r / 4) + 4 h + r % 4
