@@ -35,6 +35,7 @@
 #include "hq_device.h"
 #include "hq_internal.h"
 #include "hq_lanes.h"
+#include "hq_dither.h"
 
 namespace hq {
 namespace {
@@ -70,65 +71,6 @@ __device__ inline double pair_sum_f64(double v) {
   double a = v, b = v;
   swap_f64<true>(a, b);
   return a + b;
-}
-
-// d = w - Q_E8(w) for one block, on the 2^-24 grid (W = w 2^24), exact.  The
-// nearest point is decided as in e8_block_fast; with off = [coset a] 2^23 the
-// coordinate's offset from its point is ((W + off) mod 2^24) - 2^23, and the
-// parity flip moves one coordinate's point by one.
-__device__ inline void e8_dither_block(const int32_t* W, int32_t* d24) {
-  uint32_t k1[8], k2[8];
-#define HQ_DITHER_KEYS(i)                                         \
-  {                                                               \
-    const uint32_t F8 = ((uint32_t)W[i] << 3) & 0x07FFFFFFu;      \
-    k1[i] = sad26<i>(F8);                                         \
-    k2[i] = sad26<7 - i>(F8);                                     \
-  }
-  HQ_DITHER_KEYS(0) HQ_DITHER_KEYS(1) HQ_DITHER_KEYS(2) HQ_DITHER_KEYS(3)
-  HQ_DITHER_KEYS(4) HQ_DITHER_KEYS(5) HQ_DITHER_KEYS(6) HQ_DITHER_KEYS(7)
-#undef HQ_DITHER_KEYS
-  const uint32_t kmin = min3u(min3u(k1[0], k1[1], k1[2]), min3u(k1[3], k1[4], k1[5]),
-                              k1[6] < k1[7] ? k1[6] : k1[7]);
-  const uint32_t kmax = max3u(max3u(k2[0], k2[1], k2[2]), max3u(k2[3], k2[4], k2[5]),
-                              k2[6] > k2[7] ? k2[6] : k2[7]);
-  const int32_t bmin = (int32_t)(kmin >> 3), bmax = (int32_t)(kmax >> 3);
-  if (bmin == 0 || bmax == kHalf) {
-    int32_t z[8];
-    const int c = e8_nearest(W, z);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) d24[i] = W[i] - (shl24(z[i]) + (c ? kHalf : 0));
-    return;
-  }
-  const uint32_t sumB =
-      (((k1[0] + k1[1] + k1[2]) + (k1[3] + k1[4] + k1[5]) + (k1[6] + k1[7])) - 28u) >> 3;
-  const uint32_t X = ((uint32_t)W[0] ^ (uint32_t)W[1] ^ (uint32_t)W[2]) ^
-                     ((uint32_t)W[3] ^ (uint32_t)W[4] ^ (uint32_t)W[5]) ^
-                     ((uint32_t)W[6] ^ (uint32_t)W[7]);
-  const int odd_b = (int)((X >> 24) & 1u);
-  const int odd_a = (int)(((X >> 23) ^ (X >> 24)) & 1u);
-  const int32_t D = (1 << 25) - (int32_t)sumB + (odd_a ? 2 * bmin : 0) -
-                    (odd_b ? (1 << 24) - 2 * bmax : 0);
-  const int c = D > 0;
-  const uint32_t jf = c ? 7u - (kmax & 7u) : (kmin & 7u);
-  const int odd = c ? odd_b : odd_a;
-  const uint32_t G0 = third_bytes(W[0], W[1], W[2], W[3]);
-  const uint32_t G1 = third_bytes(W[4], W[5], W[6], W[7]);
-  const uint32_t upj = (uint32_t)((((uint64_t)G1 << 32) | G0) >> (8 * jf + 7)) & 1u;
-  const bool neg = ((uint32_t)c ^ upj) != 0u;   // the flipped point moves by -1
-  const uint32_t off = c ? 0u : (uint32_t)kHalf;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int32_t d = (int32_t)(((uint32_t)W[i] + off) & 0xFFFFFFu) - kHalf;
-    if (odd && (uint32_t)i == jf) d += neg ? kOne : -kOne;
-    d24[i] = d;
-  }
-}
-
-// W = w 2^24 for element e of vector vec: w = 2^-23 h - 1, h the top 24 bits
-// of the counter hash of (seed, vec, e).
-__device__ inline int32_t dither_w(uint32_t seed, uint64_t vec, uint32_t e) {
-  const uint64_t key = ((uint64_t)seed << 40) ^ ((vec << 8) | e);
-  return 2 * (int32_t)(splitmix64(key) >> 40) - kOne;
 }
 
 // ------------------------------------------------- D4, A2 and Z decisions

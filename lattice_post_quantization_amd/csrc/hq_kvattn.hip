@@ -30,6 +30,7 @@
 #include "hq.h"
 #include "hq_device.h"
 #include "hq_kvattn.h"
+#include "hq_dither.h"
 
 namespace hq {
 namespace {
@@ -73,19 +74,13 @@ __device__ inline void block_yhat(uint32_t d0, uint32_t d1, int c, float delta, 
     P[i] = 2 * z + c;
   }
   if (dither) {
-    int32_t W[8], Z[8];
+    int32_t W[8], d24[8];                          // w and d in 2^-24 units
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint64_t j = (uint64_t)(8 * b + i);
-      const uint64_t kk = ((uint64_t)seed << 40) ^ ((vec << 8) | j);
-      W[i] = 2 * (int32_t)(splitmix64(kk) >> 40) - kOne;
-    }
-    const int cz = e8_nearest(W, Z);
+    for (int i = 0; i < 8; ++i) W[i] = dither_w(seed, vec, (uint32_t)(8 * b + i));
+    e8_dither_block(W, d24);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int32_t d24 = W[i] - (shl24(Z[i]) + (cz ? kHalf : 0));   // d in 2^-24 units
-      y[i] = delta * ((float)P[i] * 0.5f - (float)d24 * 5.9604644775390625e-08f);
-    }
+    for (int i = 0; i < 8; ++i)
+      y[i] = delta * ((float)P[i] * 0.5f - (float)d24[i] * 5.9604644775390625e-08f);
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = delta * ((float)P[i] * 0.5f);
