@@ -17,6 +17,7 @@
 #include "hq.h"
 #include "hq_device.h"
 #include "hq_internal.h"
+#include "hq_dither.h"
 
 namespace hq {
 namespace {
@@ -75,19 +76,13 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreLaunch a) {
       if (a.dither) {
         // d = w - Q_E8(w), w = 2^-23 h - 1, h the top 24 bits of the hash
         const uint64_t vec = (uint64_t)(a.dither_base + key);
-        int32_t W[8], Z[8];
+        int32_t W[8], d24[8];                      // w and d in 2^-24 units
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint64_t j = (uint64_t)(8 * blk + i);
-          const uint64_t kk = ((uint64_t)a.dither_seed << 40) ^ ((vec << 8) | j);
-          W[i] = 2 * (int32_t)(splitmix64(kk) >> 40) - kOne;
-        }
-        const int cz = e8_nearest(W, Z);
+        for (int i = 0; i < 8; ++i) W[i] = dither_w(a.dither_seed, vec, (uint32_t)(8 * blk + i));
+        e8_dither_block(W, d24);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int32_t d24 = W[i] - (shl24(Z[i]) + (cz ? kHalf : 0));   // d in 2^-24 units
-          y[8 * blk + i] = delta * ((float)P[i] * 0.5f - (float)d24 * 5.9604644775390625e-08f);
-        }
+        for (int i = 0; i < 8; ++i)
+          y[8 * blk + i] = delta * ((float)P[i] * 0.5f - (float)d24[i] * 5.9604644775390625e-08f);
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) y[8 * blk + i] = delta * ((float)P[i] * 0.5f);
