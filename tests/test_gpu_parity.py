@@ -797,6 +797,46 @@ def test_gemm_batch_parity(m):
         assert torch.equal(ys[i], ys2[i]), "item %d determinism" % i
 
 
+def test_layer_gemm_and_gemv_as_benchmarked():
+    """The Llama-3.1-8B-shaped layer as bench.py runs its products: the seven
+    matrices drawn on the GPU and encoded in one batch (E8/256, 4 bps, RHT
+    seed 0), then hq_gemm_batch at m = 32 and 128 and hq_gemv_batch at m = 1.
+    Property checked at this size: each product equals X W^T for the fp32
+    weights hq_decode_tiles gives, within the GEMM bound
+    (2^-16 + (slices + 80) 2^-24) B plus the fp32 decode's rounding
+    2^-23 |X| |W|^T, where B <= sum_t |w_rt| |x_vt| (per 256-column tile:
+    Delta / 32 <|P|, |H (s . x)|> is at most the product of the tile norms,
+    the rotation being orthonormal up to the factor the norms carry)."""
+    dev = torch.device("cuda")
+    xs = [workloads.llama_stack_torch(0, m, dev) for m in range(len(workloads.LLAMA_LAYER))]
+    encs = hq.hq_encode_batch(xs, "E8", 256, 4.0, 0)
+    del xs
+    ws = [hq.hq_decode_tiles(e["idx"], e["coset"], e["scale"], "E8", 256, 0, torch.float32)
+          for e in encs]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(23)
+    for m in (32, 128, 1):
+        say("case: layer products m=%d" % m)
+        xm = [torch.randn(m, w.shape[1], device=dev, generator=gen) for w in ws]
+        if m == 1:
+            ys = hq.hq_gemv_batch(encs, xm, rht_seed=0)
+        else:
+            ys = hq.hq_gemm_batch(encs, xm, rht_seed=0)
+        torch.cuda.synchronize()
+        for i, (w, x, y) in enumerate(zip(ws, xm, ys)):
+            w64, x64 = w.double(), x.double()
+            ref = x64 @ w64.t()
+            T_ = w.shape[1] // 256
+            wn = w64.view(w.shape[0], T_, 256).norm(dim=2)           # (rows, tiles)
+            xn = x64.view(m, T_, 256).norm(dim=2)                    # (m, tiles)
+            tol = (2.0 ** -16 + (T_ + 80) * 2.0 ** -24) * (xn @ wn.t()) + \
+                2.0 ** -23 * (x64.abs() @ w64.abs().t())
+            err = (y.double().view(m, -1) - ref).abs()
+            worst = float((err / tol).max())
+            say("  matrix %d %s: max err/tol %.3g" % (i, tuple(w.shape), worst))
+            assert worst <= 1.0, "m=%d matrix %d" % (m, i)
+
+
 @pytest.mark.parametrize("m", [1, 2, 3])
 def test_gemv_batch_matches_single_calls(m):
     """hq_gemv_batch on ten matrices of mixed shapes (ragged row counts, one
