@@ -552,8 +552,10 @@ hq_status hq_ckpt_count(const char* path, int32_t* count);
 /* The entry of record i (0-based, file order); HQ_ENOTFOUND past the end. */
 hq_status hq_ckpt_entry_at(const char* path, int32_t i, hq_ckpt_entry* e);
 
-/* Reads the record named `name` into e and the host arrays (capacities in
- * tiles and words; HQ_EINVAL if too small).  HQ_ENOTFOUND: no such record;
+/* Reads the record named `name` into e and the host arrays: scale holds
+ * capacity_tiles values, tile_word_offset capacity_tiles + 1, words
+ * capacity_words (HQ_EINVAL if the record needs more; at most 2^48 weights
+ * per record).  HQ_ENOTFOUND: no such record;
  * HQ_EFORMAT: a truncated record, a checksum mismatch or offsets that do
  * not hold (the arrays' contents are then unspecified). */
 hq_status hq_ckpt_read(const char* path, const char* name, hq_ckpt_entry* e, float* scale,

@@ -69,7 +69,9 @@ hq_status check_entry(const hq_ckpt_entry& e) {
   if (e.tile != 64 && e.tile != 128 && e.tile != 256 && e.tile != 512) return HQ_EINVAL;
   if (!(e.bps > 0.0f && e.bps <= 8.0f)) return HQ_EINVAL;
   if (e.rows < 0 || e.cols < 0 || e.n_tiles < 0) return HQ_EINVAL;
-  if (e.rows > ((int64_t)1 << 40) || e.cols > ((int64_t)1 << 40)) return HQ_EINVAL;
+  // at most 2^48 weights, so the products below stay inside int64
+  if (e.rows > 0 && e.cols > ((int64_t)1 << 48) / e.rows) return HQ_EINVAL;
+  if (e.n_tiles > ((int64_t)1 << 48) / e.tile) return HQ_EINVAL;
   if (e.rows * e.cols != e.n_tiles * (int64_t)e.tile) return HQ_EINVAL;
   if (e.n_words > ((uint64_t)1 << 40)) return HQ_EINVAL;
   return HQ_OK;

@@ -2,6 +2,7 @@
 written and read back through the C ABI, with streams the oracle packs, and
 the error codes of damaged, foreign and missing files."""
 
+import ctypes
 import os
 
 import numpy as np
@@ -77,6 +78,12 @@ def test_error_codes(tmp_path):
     with pytest.raises(hq.HQError) as ex:
         _save(path, "x", words, off, ora["scale"], 8, 500)
     assert ex.value.code == hq.HQ_EINVAL
+    # a shape whose product would leave int64 is refused, not wrapped
+    e = hq.CkptEntry(b"big", hq.HQ_E8, 256, 4.0, 0, 1 << 40, 1 << 40, 16, 0)
+    offs = np.zeros(17, np.int64)
+    sc = np.zeros(16, np.float32)
+    assert hq.lib().hq_ckpt_append(path.encode(), ctypes.byref(e), sc.ctypes.data,
+                                   offs.ctypes.data, None) == hq.HQ_EINVAL
     # a missing record, a missing file, a directory that does not exist
     with pytest.raises(hq.HQError) as ex:
         hq.ckpt_load(path, "nope")
