@@ -6,7 +6,9 @@
 
 namespace hq {
 
-constexpr int kAttnQG = 4;        // queries per wave
+// queries per block: 4 (held in registers) for up to 4 queries per head,
+// else 8 (read from LDS)
+inline int attn_group(int64_t n_q) { return n_q <= 4 ? 4 : 8; }
 
 struct AttnLaunch {
   const float* q;           // [n_heads][n_q][128]

@@ -15,7 +15,8 @@
 // rotate_kernel: qr = H (s_K (.) q) tau log2(e) / sqrt(n) (fp64 butterflies,
 // one fp32 rounding), so scores come out in base-2 exponent units.
 // attn_kernel: a block owns a range of keys of one head and up to 4 of its
-// queries, each wave a quarter of the range; lane
+// queries (8 from LDS when a head has more), each wave a quarter of the
+// range; lane
 // (r, b) = (lane / 16, lane % 16) decodes E8 block b of keys k0 + 4 i + r for
 // K and V (the dither regenerated from the encoder's counter hash and E8
 // decision), the block's partial score is summed over the 16 lanes of its
@@ -93,15 +94,18 @@ __device__ inline float sum16(float x) {
   return x;
 }
 
+template <int QG>
 __global__ __launch_bounds__(256) void attn_kernel(AttnLaunch a) {
-  __shared__ float wm[4][kAttnQG], wl[4][kAttnQG];
-  __shared__ float wacc[4][kAttnQG][kHd];
+  constexpr bool kLdsQ = QG > 4;     // queries read from LDS at each step
+  __shared__ float wm[4][QG], wl[4][QG];
+  __shared__ float wacc[4][QG][kHd];
+  __shared__ float4 qs[kLdsQ ? QG : 1][kHd / 4];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int64_t range = blockIdx.x, head = blockIdx.z;
   const int r = lane >> 4, b = lane & 15;
-  const int64_t q0 = (int64_t)blockIdx.y * kAttnQG;
-  const int nq = (int)(a.n_q - q0 < kAttnQG ? a.n_q - q0 : kAttnQG);
+  const int64_t q0 = (int64_t)blockIdx.y * QG;
+  const int nq = (int)(a.n_q - q0 < QG ? a.n_q - q0 : QG);
   // this wave's keys (possibly none at the end of the head)
   const int64_t k_begin0 = (range * 4 + w) * a.keys_per_wave;
   const int64_t k_begin = k_begin0 < a.n_keys ? k_begin0 : a.n_keys;
@@ -110,18 +114,28 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnLaunch a) {
   const int64_t kv0 = head * a.n_keys;             // the head's first vector
   const float* qr = a.qr + (head * a.n_q + q0) * kHd;
 
-  float qv[kAttnQG][8];
+  // the queries' coordinates of block b: registers, or LDS for 8 queries
+  float qv[kLdsQ ? 1 : QG][8];
+  if constexpr (kLdsQ) {
+    for (int e = threadIdx.x; e < QG * (kHd / 4); e += 256) {
+      const int jj = e / (kHd / 4) < nq ? e / (kHd / 4) : 0;
+      qs[e / (kHd / 4)][e % (kHd / 4)] =
+          reinterpret_cast<const float4*>(qr + jj * kHd)[e % (kHd / 4)];
+    }
+    __syncthreads();
+  } else {
 #pragma unroll
-  for (int j = 0; j < kAttnQG; ++j) {
-    const int jj = j < nq ? j : 0;
-    const float4 lo = *reinterpret_cast<const float4*>(qr + jj * kHd + 8 * b);
-    const float4 hi = *reinterpret_cast<const float4*>(qr + jj * kHd + 8 * b + 4);
-    qv[j][0] = lo.x; qv[j][1] = lo.y; qv[j][2] = lo.z; qv[j][3] = lo.w;
-    qv[j][4] = hi.x; qv[j][5] = hi.y; qv[j][6] = hi.z; qv[j][7] = hi.w;
+    for (int j = 0; j < QG; ++j) {
+      const int jj = j < nq ? j : 0;
+      const float4 lo = *reinterpret_cast<const float4*>(qr + jj * kHd + 8 * b);
+      const float4 hi = *reinterpret_cast<const float4*>(qr + jj * kHd + 8 * b + 4);
+      qv[j][0] = lo.x; qv[j][1] = lo.y; qv[j][2] = lo.z; qv[j][3] = lo.w;
+      qv[j][4] = hi.x; qv[j][5] = hi.y; qv[j][6] = hi.z; qv[j][7] = hi.w;
+    }
   }
-  float m[kAttnQG], l[kAttnQG], acc[kAttnQG][8];
+  float m[QG], l[QG], acc[QG][8];
 #pragma unroll
-  for (int j = 0; j < kAttnQG; ++j) {
+  for (int j = 0; j < QG; ++j) {
     m[j] = -INFINITY;
     l[j] = 0.0f;
 #pragma unroll
@@ -141,10 +155,19 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnLaunch a) {
     block_yhat(vb.x, vb.y, (int)((a.v_coset[key] >> b) & 1u), a.v_scale[key], a.v_dither,
                a.v_seed, (uint64_t)(a.v_base + key), b, yv);
 #pragma unroll
-    for (int j = 0; j < kAttnQG; ++j) {
+    for (int j = 0; j < QG; ++j) {
+      float q8[8];
+      if constexpr (kLdsQ) {
+        const float4 lo = qs[j][2 * b], hi = qs[j][2 * b + 1];
+        q8[0] = lo.x; q8[1] = lo.y; q8[2] = lo.z; q8[3] = lo.w;
+        q8[4] = hi.x; q8[5] = hi.y; q8[6] = hi.z; q8[7] = hi.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q8[i] = qv[j][i];
+      }
       float part = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) part = fmaf(qv[j][i], yk[i], part);
+      for (int i = 0; i < 8; ++i) part = fmaf(q8[i], yk[i], part);
       float s = sum16(part);                       // this key's score (log2 units)
       if (!live) s = -INFINITY;
       float smax = fmaxf(s, __shfl_xor(s, 16, 64));
@@ -160,7 +183,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnLaunch a) {
   }
   // sum the four key residues (a wave without keys has m = -inf, l = 0)
 #pragma unroll
-  for (int j = 0; j < kAttnQG; ++j) {
+  for (int j = 0; j < QG; ++j) {
     l[j] += __shfl_xor(l[j], 16, 64);
     l[j] += __shfl_xor(l[j], 32, 64);
 #pragma unroll
@@ -171,7 +194,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnLaunch a) {
   }
   if (r == 0) {
 #pragma unroll
-    for (int j = 0; j < kAttnQG; ++j) {
+    for (int j = 0; j < QG; ++j) {
       if (b == 0) {
         wm[w][j] = m[j];
         wl[w][j] = l[j];
@@ -184,7 +207,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnLaunch a) {
   // merge the four waves in order: thread (j, d) for j < nq
   const int jt = threadIdx.x >> 7, d = threadIdx.x & 127;
 #pragma unroll
-  for (int jb = 0; jb < kAttnQG; jb += 2) {
+  for (int jb = 0; jb < QG; jb += 2) {
     const int j = jb + jt;
     if (j >= nq) continue;
     float M = wm[0][j];
@@ -243,7 +266,7 @@ __global__ __launch_bounds__(kHd) void combine_kernel(AttnLaunch a) {
 // ranges keep the merge short), a multiple of 4.
 void attn_plan(int64_t n_heads, int64_t n_q, int64_t n_keys, int64_t& keys_per_wave,
                int64_t& n_ranges) {
-  const int64_t groups = (n_q + kAttnQG - 1) / kAttnQG;
+  const int64_t groups = (n_q + attn_group(n_q) - 1) / attn_group(n_q);
   const int64_t per_head = (2048 + n_heads * groups - 1) / (n_heads * groups);   // waves
   int64_t kpw = (n_keys + per_head - 1) / per_head;
   kpw = kpw < 64 ? 64 : kpw;
@@ -260,9 +283,12 @@ size_t attn_workspace(int64_t n_heads, int64_t n_q, int64_t n_keys) {
 
 hipError_t launch_attention(const AttnLaunch& a, hipStream_t s) {
   hipLaunchKernelGGL(rotate_kernel, dim3((unsigned)(a.n_heads * a.n_q)), dim3(kHd), 0, s, a);
-  const int64_t groups = (a.n_q + kAttnQG - 1) / kAttnQG;
-  hipLaunchKernelGGL(attn_kernel, dim3((unsigned)a.n_ranges, (unsigned)groups, (unsigned)a.n_heads),
-                     dim3(256), 0, s, a);
+  const int qg = attn_group(a.n_q);
+  const dim3 grid((unsigned)a.n_ranges, (unsigned)((a.n_q + qg - 1) / qg), (unsigned)a.n_heads);
+  if (qg == 4)
+    hipLaunchKernelGGL((attn_kernel<4>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_kernel<8>), grid, dim3(256), 0, s, a);
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)a.n_q, (unsigned)a.n_heads), dim3(kHd), 0, s,
                      a);
   return hipGetLastError();
