@@ -331,7 +331,9 @@ size_t hq_gemv_batch_workspace_bytes(int32_t count, const hq_gemv_item* items, i
  * idx [rows*cols] int8 (16-byte aligned), coset [n_tiles] words, scale
  * [n_tiles] fp32 as for hq_gemv; cols a multiple of 256 and at most 2^22,
  * rows at most 2^23; x [m][cols] fp32 (16-byte aligned), 1 <= m <= 65536
- * with m cols and m rows at most 2^31; y [m][rows] fp32 out; workspace:
+ * with m cols and m rows at most 2^31 (and each launch's grid below 2^32
+ * work-items, which only the largest of these sizes reach); y [m][rows]
+ * fp32 out; workspace:
  * device scratch of at least hq_gemm_workspace_bytes(rows, cols, m) bytes,
  * 16-byte aligned.  Errors as for hq_gemv (HQ_EINVAL for sizes out of
  * range).

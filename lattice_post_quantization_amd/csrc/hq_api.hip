@@ -602,8 +602,12 @@ size_t hq_gemm_batch_workspace_bytes(int32_t count, const hq_gemv_item* items, i
   for (int32_t i = 0; i < count; ++i)
     if (!gemm_sizes_ok(items[i].rows, items[i].cols, m)) return 0;
   size_t total = 0;
-  gemm_groups(count, items, m, [&](const GemmBatch& b) { total += gemm_group_workspace(b); });
-  return total;
+  bool fits = true;
+  gemm_groups(count, items, m, [&](const GemmBatch& b) {
+    total += gemm_group_workspace(b);
+    fits = fits && gemm_fits_launch(b);
+  });
+  return fits ? total : 0;
 }
 
 size_t hq_gemm_workspace_bytes(int64_t rows, int64_t cols, int32_t m) {
@@ -638,8 +642,8 @@ hq_status hq_gemm_batch(const hq_params* p, int32_t count, const hq_gemv_item* i
     any = true;
   }
   if (!any) return HQ_OK;
-  if (workspace == nullptr || !aligned16(workspace) ||
-      workspace_bytes < hq_gemm_batch_workspace_bytes(count, items, m))
+  const size_t need = hq_gemm_batch_workspace_bytes(count, items, m);   // 0: too large a launch
+  if (need == 0 || workspace == nullptr || !aligned16(workspace) || workspace_bytes < need)
     return HQ_EINVAL;
   for (int32_t i = 0; i < count; ++i) {
     const hq_gemv_item& it = items[i];

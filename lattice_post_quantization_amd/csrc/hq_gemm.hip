@@ -387,9 +387,27 @@ void gemm_plan(GemmBatch& b) {
     GemmItem& it = b.it[i];
     const int64_t slices = it.cols / kSliceK;
     it.kchunks = (slices + len - 1) / len;
+    // at most kGemmMaxRanges ranges (longer ranges for very wide matrices)
+    if (it.kchunks > kGemmMaxRanges) it.kchunks = kGemmMaxRanges;
     it.spc = (slices + it.kchunks - 1) / it.kchunks;
     it.kchunks = (slices + it.spc - 1) / it.spc;
   }
+}
+
+bool gemm_fits_launch(const GemmBatch& b) {
+  const int nf = nf_for(b.m), waves = waves_for(nf);
+  const int64_t vblocks = (b.m + 32 * nf - 1) / (32 * nf);
+  int64_t blocks = 0, split = 0, sum = 0;
+  for (int i = 0; i < b.n; ++i) {
+    const GemmItem& it = b.it[i];
+    const int64_t tasks = (it.rows + 32 * waves - 1) / (32 * waves) * it.kchunks;
+    blocks += (tasks + 7) / 8 * 8 * vblocks;
+    split += (int64_t)b.m * (it.cols / kSliceK);
+    if (it.kchunks > 1) sum += (int64_t)b.m * it.rows;
+  }
+  // every grid below 2^32 work-items
+  const int64_t lim = (int64_t)1 << 32;
+  return blocks * 64 * waves < lim && (split + 3) / 4 * 256 < lim && (sum + 255) / 256 * 256 < lim;
 }
 
 size_t gemm_item_workspace(const GemmItem& it, int32_t m) {

@@ -132,6 +132,9 @@ constexpr int64_t kGemmMaxProduct = (int64_t)1 << 31;   // m cols and m rows
 // The slice ranges of every matrix of b (kchunks, spc), a function of the
 // group's sizes and m alone, so a call repeats its bits on any device.
 void gemm_plan(GemmBatch& b);
+constexpr int64_t kGemmMaxRanges = 64;
+// Whether a planned group's three launches stay within 2^32 work-items.
+bool gemm_fits_launch(const GemmBatch& b);
 // Workspace of one planned matrix: the inputs' bf16 terms, then the partial
 // sums when its slices are split.
 size_t gemm_item_workspace(const GemmItem& it, int32_t m);

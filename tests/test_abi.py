@@ -307,7 +307,13 @@ def test_gemm_validation_codes():
                           (4, 256, 0), (4, 256, 65537), (1 << 16, 256, 1 << 16),
                           (4, 1 << 16, 1 << 16), (0, 256, 1)):
         assert lib.hq_gemm_workspace_bytes(rows, cols, m) == 0, (rows, cols, m)
+    # the largest accepted sizes stay within one launch's grid (or are refused)
     assert lib.hq_gemm_workspace_bytes(1 << 15, 1 << 15, 1 << 16) > 0
+    assert lib.hq_gemm_workspace_bytes(1 << 23, 1 << 22, 256) == 0
+    big = (hq.GemvItem * 8)()
+    for i in range(8):
+        big[i] = hq.GemvItem(FAKE, FAKE, FAKE, 1 << 15, 1 << 15, FAKE, FAKE)
+    assert lib.hq_gemm_batch_workspace_bytes(8, big, 1 << 16) == 0
     # nothing to compute: a no-op
     assert lib.hq_gemm(ctypes.byref(p), None, None, None, 0, 256, None, 1, None, None, 0, None,
                        None) == hq.HQ_OK
