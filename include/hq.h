@@ -387,8 +387,9 @@ size_t hq_gemm_batch_workspace_bytes(int32_t count, const hq_gemv_item* items, i
  * key 0 (as for hq_kv_encode), or no dither (rotation-only keys).
  * q [n_q][128] fp32; idx [n_keys][128] int8, coset [n_keys] uint32 (16 coset
  * bits), scale [n_keys] fp32 as written by hq_kv_encode; scores [n_q][n_keys]
- * fp32 out; workspace: device scratch of at least
- * hq_kv_scores_workspace_bytes(n_q) bytes.  fp32 arithmetic in a fixed order.
+ * fp32 out (n_q < 2^25, n_keys <= 2^32 - 256); workspace: device scratch of
+ * at least hq_kv_scores_workspace_bytes(n_q) bytes.  fp32 arithmetic in a
+ * fixed order.
  */
 hq_status hq_kv_scores(const hq_params* p, const float* q, int64_t n_q,
                        const int8_t* idx, const uint32_t* coset, const float* scale,
@@ -420,7 +421,9 @@ size_t hq_kv_scores_workspace_bytes(int64_t n_q);
  * them for the whole cache (key k of head h is vector h n_keys + k; idx
  * 16-byte aligned); n_keys >= 1 when n_q > 0.  q [n_heads][n_q][128] fp32
  * (16-byte aligned), 1 <= n_heads <= 65535, n_q <= 65536 queries per head
- * (grouped queries share a head); tau the score scale (finite; 1/sqrt(128)
+ * (grouped queries share a head), n_heads n_q < 2^25, n_heads n_keys <= 2^32
+ * (and the launch grid below 2^32 work-items, which only extreme sizes
+ * reach); tau the score scale (finite; 1/sqrt(128)
  * for standard attention); out [n_heads][n_q][128] fp32; workspace: device
  * scratch of at least hq_kv_attention_workspace_bytes(n_heads, n_q, n_keys)
  * bytes, 16-byte aligned.  Errors as hq_kv_scores.

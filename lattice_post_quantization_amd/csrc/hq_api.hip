@@ -773,8 +773,9 @@ hq_status hq_kv_scores(const hq_params* p, const float* q, int64_t n_q, const in
   if (q == nullptr || idx == nullptr || coset == nullptr || scale == nullptr ||
       scores == nullptr || workspace == nullptr)
     return HQ_EINVAL;
-  if (n_q > INT64_MAX / 128 || n_keys > INT64_MAX / n_q || n_q > 0x7FFFFFFF ||
-      workspace_bytes < hq_kv_scores_workspace_bytes(n_q))
+  // grids below 2^32 work-items: n_q blocks of 128, n_keys / 256 blocks of 256
+  if (n_q >= ((int64_t)1 << 25) || n_keys > ((int64_t)1 << 32) - 256 ||
+      n_keys > INT64_MAX / n_q || workspace_bytes < hq_kv_scores_workspace_bytes(n_q))
     return HQ_EINVAL;
   if ((p->flags & HQ_DITHER) && p->dither_base + n_keys > ((int64_t)1 << 32)) return HQ_EINVAL;
   if (!aligned16(q) || !aligned16(idx) || !aligned16(workspace) || ((uintptr_t)coset & 3u) ||
@@ -801,9 +802,14 @@ hq_status hq_kv_scores(const hq_params* p, const float* q, int64_t n_q, const in
   return launched(launch_scores(a, stream));
 }
 
+// Sizes hq_kv_attention takes: every grid below 2^32 work-items (rotation
+// and merge: n_heads n_q blocks of 128; attention: ranges x query groups x
+// heads blocks of 256).
 static bool attn_sizes_ok(int64_t n_heads, int64_t n_q, int64_t n_keys) {
-  return n_heads >= 1 && n_heads <= 65535 && n_q >= 0 && n_q <= 65536 && n_keys >= 0 &&
-         n_heads * n_keys <= ((int64_t)1 << 32) && n_heads * n_q <= ((int64_t)1 << 31);
+  if (n_heads < 1 || n_heads > 65535 || n_q < 0 || n_q > 65536 || n_keys < 0) return false;
+  if (n_heads * n_keys > ((int64_t)1 << 32) || n_heads * n_q >= ((int64_t)1 << 25)) return false;
+  if (n_q == 0 || n_keys == 0) return true;
+  return attn_blocks(n_heads, n_q, n_keys) * 256 < ((int64_t)1 << 32);
 }
 
 size_t hq_kv_attention_workspace_bytes(int64_t n_heads, int64_t n_q, int64_t n_keys) {

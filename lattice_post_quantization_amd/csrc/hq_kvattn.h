@@ -37,6 +37,8 @@ struct AttnLaunch {
 void attn_plan(int64_t n_heads, int64_t n_q, int64_t n_keys, int64_t& keys_per_wave,
                int64_t& n_ranges);
 size_t attn_workspace(int64_t n_heads, int64_t n_q, int64_t n_keys);
+// Blocks of the attention launch (ranges x query groups x heads).
+int64_t attn_blocks(int64_t n_heads, int64_t n_q, int64_t n_keys);
 hipError_t launch_attention(const AttnLaunch& a, hipStream_t s);
 
 }  // namespace hq

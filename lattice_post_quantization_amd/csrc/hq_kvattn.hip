@@ -274,6 +274,12 @@ void attn_plan(int64_t n_heads, int64_t n_q, int64_t n_keys, int64_t& keys_per_w
   n_ranges = (n_keys + 4 * keys_per_wave - 1) / (4 * keys_per_wave);
 }
 
+int64_t attn_blocks(int64_t n_heads, int64_t n_q, int64_t n_keys) {
+  int64_t kpw, nr;
+  attn_plan(n_heads, n_q, n_keys, kpw, nr);
+  return nr * ((n_q + attn_group(n_q) - 1) / attn_group(n_q)) * n_heads;
+}
+
 size_t attn_workspace(int64_t n_heads, int64_t n_q, int64_t n_keys) {
   int64_t kpw, nr;
   attn_plan(n_heads, n_q, n_keys, kpw, nr);

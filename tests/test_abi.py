@@ -365,7 +365,7 @@ def test_kv_attention_validation_codes():
     pv = hq.make_params("E8", 128, 4.0, 7)
     assert lib.hq_kv_attention_workspace_bytes(8, 4, 32768) >= 8 * 4 * 128 * 4
     for nh, nq, nk in ((1, 0, 10), (1, 4, 0), (1, 65537, 10), (1, 4, (1 << 32) + 1),
-                       (0, 4, 10), (65536, 1, 10), (8, 4, 1 << 30)):
+                       (0, 4, 10), (65536, 1, 10), (8, 4, 1 << 30), (4096, 8192, 10)):
         assert lib.hq_kv_attention_workspace_bytes(nh, nq, nk) == 0
 
     def call(pk=pk, pv=pv, n_heads=2, n_keys=100, n_q=4, tau=0.1, ws=1 << 30, k=FAKE, out=FAKE):
@@ -399,6 +399,12 @@ def test_kv_scores_validation_codes():
     for q in (hq.make_params("E8", 256, 4.0), hq.make_params("D4", 128, 4.0)):
         assert lib.hq_kv_scores(ctypes.byref(q), FAKE, 4, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 1 << 20,
                                 None) == hq.HQ_EUNSUPPORTED
+    # query and key counts past one launch's grid
+    p0 = hq.make_params("E8", 128, 4.0, 1)
+    assert lib.hq_kv_scores(ctypes.byref(p0), FAKE, 1 << 25, FAKE, FAKE, FAKE, 4, FAKE, FAKE,
+                            1 << 40, None) == hq.HQ_EINVAL
+    assert lib.hq_kv_scores(ctypes.byref(p0), FAKE, 4, FAKE, FAKE, FAKE, (1 << 32) - 255, FAKE,
+                            FAKE, 1 << 40, None) == hq.HQ_EINVAL
     # null buffers, short workspace, dither index overflow
     assert lib.hq_kv_scores(ctypes.byref(p), FAKE, 4, FAKE, None, FAKE, 4, FAKE, FAKE, 1 << 20,
                             None) == hq.HQ_EINVAL
