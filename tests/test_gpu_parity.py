@@ -319,6 +319,45 @@ def test_kv_attention_parity(dither):
         assert torch.equal(out, out2)
 
 
+@pytest.mark.parametrize("n_keys,n_q", [(1, 5), (3, 1), (257, 8), (1029, 4)])
+def test_kv_attention_small_caches(n_keys, n_q):
+    """Three heads of tiny and ragged caches (fewer keys than a wave's four
+    residues, one key past a range of 256) and query counts on both sides
+    of the 4 / 8 query groups, against the oracle's attention over its own
+    dithered decode of each head (dither index = head x n_keys + key)."""
+    from oracle.attention import attention
+    rng = np.random.default_rng(31 + n_keys)
+    heads = 3
+    x = rng.standard_normal((heads * n_keys, 128))
+    xk = workloads.bf16_bits_to_f64(workloads.f32_to_bf16_bits(x.astype(np.float32)))
+    xv = workloads.bf16_bits_to_f64(workloads.f32_to_bf16_bits(
+        rng.standard_normal((heads * n_keys, 128)).astype(np.float32)))
+    say("case: kv attention %d heads x %d keys, %d queries" % (heads, n_keys, n_q))
+    ko = codec.encode(xk, "E8", 128, 4.0, rht_seed=4, dither_seed=6, dither_base=100)
+    vo = codec.encode(xv, "E8", 128, 4.0, rht_seed=4, dither_seed=6, dither_base=9000)
+    k_hat = codec.decode(ko["idx"], ko["coset"], ko["scale"], "E8", 128, 4, dither_seed=6,
+                         dither_base=100).reshape(heads, n_keys, 128)
+    v_hat = codec.decode(vo["idx"], vo["coset"], vo["scale"], "E8", 128, 4, dither_seed=6,
+                         dither_base=9000).reshape(heads, n_keys, 128)
+    n = heads * n_keys
+
+    def dev_enc(o):
+        return {"idx": torch.from_numpy(o["idx"].astype(np.int8).reshape(n, 128)).cuda(),
+                "coset": torch.from_numpy(o["coset"].astype(np.uint32).view(np.int32).reshape(n)).cuda(),
+                "scale": torch.from_numpy(o["scale"].astype(np.float32)).cuda()}
+
+    q = rng.standard_normal((heads, n_q, 128)).astype(np.float32)
+    out = hq.hq_kv_attention(torch.from_numpy(q).cuda(), dev_enc(ko), dev_enc(vo), tau=0.3,
+                             k_cache=dict(rht_seed=4, dither_seed=6, dither_base=100),
+                             v_cache=dict(rht_seed=4, dither_seed=6, dither_base=9000))
+    torch.cuda.synchronize()
+    for h in range(heads):
+        ref = attention(q[h].astype(np.float64), k_hat[h], v_hat[h], 0.3)
+        tol = _attn_tol(q[h].astype(np.float64), k_hat[h], v_hat[h], 0.3)
+        err = np.abs(T.host(out[h]).astype(np.float64) - ref)
+        assert np.all(err <= tol), "head %d: max err/tol %.3g" % (h, np.max(err / tol))
+
+
 def test_kv_attention_all_heads_against_decoded_cache():
     """At the workload's size (all heads of [8, 32768, 128], dithered K and
     V encoded as one cache each, 4 queries per head in one call):
