@@ -181,9 +181,25 @@ def secondary(layer0, bps, dev):
                              b["stream"][:int(b["tile_word_offset"][-1])])
                  for a, b in zip(outs, outs_g))
     alg_g = tiles * (256 + 4 + 1 + 4) + tiles * 8 + 4 * words
+    # both in one batched call for the layer
+    wsr = torch.empty(max(16, sum(hq.rate_workspace_bytes(e["idx"].numel() // 256)
+                                  for e in encs)), dtype=torch.uint8, device=dev)
+    outs_b = hq.hq_rate_batch(encs, "E8", 256, pack=True, workspace=wsr)
+    outs_bg = hq.hq_rate_batch(encs, "E8", 256, pack=True, given=True, workspace=wsr)
+    ms_b = time_calls(lambda: hq.hq_rate_batch(encs, "E8", 256, pack=True, workspace=wsr,
+                                               outs=outs_b), 10)
+    ms_bg = time_calls(lambda: hq.hq_rate_batch(encs, "E8", 256, pack=True, given=True,
+                                                workspace=wsr, outs=outs_bg), 10)
+    torch.cuda.synchronize()
+    same_b = all(torch.equal(a["stream"][:int(a["tile_word_offset"][-1])],
+                             b["stream"][:int(b["tile_word_offset"][-1])])
+                 for a, b in zip(outs, outs_b))
     pack = {"workload": "rate + pack of one Llama-3.1-8B-shaped layer's E8 indices "
-                        "(seven calls, %d tiles)" % tiles,
+                        "(seven calls, %d tiles; and one batched call)" % tiles,
             "us": round(ms * 1e3, 2), "algorithmic_gbs": round(alg / (ms * 1e-3) / 1e9, 1),
+            "us_batched": round(ms_b * 1e3, 2),
+            "us_batched_encoder_rate_given": round(ms_bg * 1e3, 2),
+            "batched_stream_identical": bool(same_b),
             "us_encoder_rate_given": round(ms_gv * 1e3, 2),
             "given_algorithmic_gbs": round(alg_g / (ms_gv * 1e-3) / 1e9, 1),
             "given_stream_identical": bool(same_g),

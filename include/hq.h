@@ -211,6 +211,35 @@ hq_status hq_rate(const hq_params* p, const int8_t* idx, const uint32_t* coset,
                   hipStream_t stream);
 
 /*
+ * hq_rate_batch - hq_rate for `count` matrices that share p (a layer's
+ * projections), enqueued as at most four kernel launches per group of up to
+ * eight matrices instead of up to four per matrix.  Same passages,
+ * arguments per item and results (bit for bit) as one hq_rate call per item
+ * with a workspace.  The workspace (device, 8-byte aligned, at least
+ * hq_rate_batch_workspace_bytes(count, items) bytes: each item's
+ * hq_rate_workspace_bytes, in item order) is required; an item with
+ * n_tiles 0 is skipped.
+ */
+typedef struct {
+  const int8_t* idx;            /* [n_tiles * tile] (NULL: HQ_RATE_GIVEN, no packing) */
+  const uint32_t* coset;        /* [n_tiles * words] (packing, E8 / A2)           */
+  int64_t n_tiles;
+  uint8_t* rice_k;              /* [n_tiles]                                      */
+  uint32_t* tile_bits;          /* [n_tiles]                                      */
+  uint64_t* total_bits;         /* one value                                      */
+  uint32_t* stream_words;       /* NULL: rate only                                */
+  uint64_t capacity_words;
+  uint64_t* tile_word_offset;   /* [n_tiles + 1] (packing)                        */
+} hq_rate_item;
+
+hq_status hq_rate_batch(const hq_params* p, int32_t count, const hq_rate_item* items,
+                        void* workspace, size_t workspace_bytes, uint32_t* status,
+                        hipStream_t stream);
+
+/* Device workspace bytes hq_rate_batch needs; 0 for invalid arguments. */
+size_t hq_rate_batch_workspace_bytes(int32_t count, const hq_rate_item* items);
+
+/*
  * hq_unpack - decode a packed stream back to stripped indices, coset words
  * and Rice parameters: the inverse of the packing done by hq_rate.
  *

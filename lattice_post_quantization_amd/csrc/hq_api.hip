@@ -15,6 +15,7 @@
 #include "hq_device.h"
 #include "hq_internal.h"
 #include "hq_kvattn.h"
+#include "hq_ratebatch.h"
 
 namespace hq {
 }
@@ -452,6 +453,102 @@ hq_status hq_rate(const hq_params* p, const int8_t* idx, const uint32_t* coset, 
   a.status = status;
   a.given = given ? 1 : 0;
   return launched(launch_rate(a, stream));
+}
+
+// Validation of one hq_rate_batch item with n_tiles > 0 (a workspace is
+// given to the call).
+static hq_status check_rate_item(const hq_params* p, const hq_rate_item& it) {
+  const bool given = (p->flags & HQ_RATE_GIVEN) != 0;
+  const bool pack = it.stream_words != nullptr;
+  if ((it.idx == nullptr && (pack || !given)) || it.rice_k == nullptr ||
+      it.tile_bits == nullptr || it.total_bits == nullptr)
+    return HQ_EINVAL;
+  if (!aligned16(it.idx) || ((uintptr_t)it.total_bits & 7u) || ((uintptr_t)it.tile_bits & 3u))
+    return HQ_EINVAL;
+  if (pack) {
+    if (it.tile_word_offset == nullptr || ((uintptr_t)it.tile_word_offset & 7u)) return HQ_EINVAL;
+    if (coset_words(p) > 0 && it.coset == nullptr) return HQ_EINVAL;
+  }
+  if (it.n_tiles > INT64_MAX / p->tile) return HQ_EINVAL;
+  if ((it.idx != nullptr && !on_device(it.idx)) || !on_device(it.rice_k) ||
+      !on_device(it.tile_bits) || !on_device(it.total_bits))
+    return HQ_EINVAL;
+  if (pack && (!on_device(it.stream_words) || !on_device(it.tile_word_offset) ||
+               (coset_words(p) > 0 && !on_device(it.coset))))
+    return HQ_EINVAL;
+  return HQ_OK;
+}
+
+size_t hq_rate_batch_workspace_bytes(int32_t count, const hq_rate_item* items) {
+  if (count < 0 || (count > 0 && items == nullptr)) return 0;
+  size_t total = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    if (items[i].n_tiles < 0) return 0;
+    total += hq_rate_workspace_bytes(items[i].n_tiles);
+  }
+  return total;
+}
+
+hq_status hq_rate_batch(const hq_params* p, int32_t count, const hq_rate_item* items,
+                        void* workspace, size_t workspace_bytes, uint32_t* status,
+                        hipStream_t stream) {
+  hq_status st = check_params(p);
+  if (st != HQ_OK) return st;
+  if (count < 0 || (count > 0 && items == nullptr)) return HQ_EINVAL;
+  bool any = false;
+  for (int32_t i = 0; i < count; ++i) {
+    if (items[i].n_tiles < 0) return HQ_EINVAL;
+    if (items[i].n_tiles == 0) continue;
+    st = check_rate_item(p, items[i]);
+    if (st != HQ_OK) return st;
+    any = true;
+  }
+  if (!any) return HQ_OK;
+  if (workspace == nullptr || ((uintptr_t)workspace & 7u) ||
+      workspace_bytes < hq_rate_batch_workspace_bytes(count, items) || !on_device(workspace) ||
+      (status != nullptr && !on_device(status)))
+    return HQ_EINVAL;
+  // groups of up to kRateMaxItems matrices, each with its own workspace slice
+  RateBatch b;
+  memset(&b, 0, sizeof(b));
+  char* ws = static_cast<char*>(workspace);
+  for (int32_t i = 0; i <= count; ++i) {
+    if ((i == count || b.n == kRateMaxItems) && b.n > 0) {
+      for (int k = b.n; k < kRateMaxItems; ++k) b.it[k] = b.it[0];
+      for (int k = b.n + 1; k <= kRateMaxItems; ++k) b.block0[k] = b.block0[b.n];
+      if (launch_rate_batch(b, stream) != hipSuccess) return HQ_EDEVICE;
+      memset(&b, 0, sizeof(b));
+    }
+    if (i == count) break;
+    const hq_rate_item& it = items[i];
+    if (it.n_tiles == 0) {
+      ws += hq_rate_workspace_bytes(0);
+      continue;
+    }
+    RateLaunch& a = b.it[b.n];
+    a.idx = it.idx;
+    a.coset = it.coset;
+    a.n_tiles = it.n_tiles;
+    a.tile = p->tile;
+    a.coset_bits = coset_bits(p);
+    a.coset_words = coset_words(p);
+    a.rice_k = it.rice_k;
+    a.tile_bits = it.tile_bits;
+    a.total_bits = it.total_bits;
+    a.stream = it.stream_words;
+    a.capacity = it.capacity_words;
+    a.tile_word_offset = it.tile_word_offset;
+    const int64_t nb = rate_workspace_blocks(it.n_tiles);
+    a.block_words = reinterpret_cast<uint64_t*>(ws);
+    a.block_bits = a.block_words + nb;
+    a.wave_words = a.block_words + 2 * nb;
+    ws += hq_rate_workspace_bytes(it.n_tiles);
+    a.status = status;
+    a.given = (p->flags & HQ_RATE_GIVEN) ? 1 : 0;
+    b.block0[b.n + 1] = b.block0[b.n] + rate_blocks(p->tile, it.n_tiles);
+    ++b.n;
+  }
+  return HQ_OK;
 }
 
 namespace {

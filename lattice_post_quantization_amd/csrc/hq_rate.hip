@@ -26,8 +26,11 @@
 //                its words at the tile's word offset.  Tiles are word
 //                aligned, so no two tiles share a word.  Only wave-level
 //                synchronisation: waves never wait for each other.
+#include <string.h>
+
 #include "hq.h"
 #include "hq_device.h"
+#include "hq_ratebatch.h"
 #include "hq_internal.h"
 
 namespace hq {
@@ -157,7 +160,7 @@ __device__ inline uint64_t wave_sum_u64(uint64_t x) {
 // its word count, and its block's word and bit sums (without a workspace,
 // the bit total through one 64-bit atomic per block).  Every thread of the
 // block calls it.
-__device__ inline void rate_sums(const RateLaunch& a, uint64_t words, uint64_t bits,
+__device__ inline void rate_sums(const RateLaunch& a, int64_t bx, uint64_t words, uint64_t bits,
                                  int64_t wave, int wl, int lane,
                                  uint64_t (*blk)[kBlock / 64]) {
   words = wave_sum_u64(words);
@@ -176,23 +179,35 @@ __device__ inline void rate_sums(const RateLaunch& a, uint64_t words, uint64_t b
       b += blk[1][i];
     }
     if (a.block_words != nullptr) {
-      a.block_words[blockIdx.x] = w;
-      a.block_bits[blockIdx.x] = b;
+      a.block_words[bx] = w;
+      a.block_bits[bx] = b;
     } else {
       atomicAdd((unsigned long long*)a.total_bits, (unsigned long long)b);
     }
   }
 }
 
+// The block's matrix in the batch (block-uniform) and its block index there.
+__device__ inline int rate_item(const RateBatch& b, int64_t& bx) {
+  int i = 0;
+#pragma unroll
+  for (int k = 1; k < kRateMaxItems; ++k)
+    if (k < b.n && (int64_t)blockIdx.x >= b.block0[k]) i = k;
+  bx = (int64_t)blockIdx.x - b.block0[i];
+  return i;
+}
+
 template <int N>
-__global__ __launch_bounds__(kBlock) void rate_kernel(RateLaunch a) {
+__global__ __launch_bounds__(kBlock) void rate_kernel(RateBatch bt) {
+  int64_t bx;
+  const RateLaunch& a = bt.it[rate_item(bt, bx)];
   constexpr int G = N / kElemsPerLane;
   constexpr int TPW = 64 / G;
   __shared__ uint64_t blk[2][kBlock / 64];
   const int lane = threadIdx.x & 63;
   const int r = lane % G;
   const int wl = threadIdx.x >> 6;
-  const int64_t wave = (int64_t)blockIdx.x * (kBlock / 64) + wl;
+  const int64_t wave = bx * (kBlock / 64) + wl;
   // waves past the last one have an empty span (the block still syncs)
   const int64_t span = wave_span<N>(a.n_tiles);
   const int64_t first = wave < rate_waves<N>(a.n_tiles) ? wave * span : a.n_tiles;
@@ -221,17 +236,19 @@ __global__ __launch_bounds__(kBlock) void rate_kernel(RateLaunch a) {
       bits += tb;
     }
   }
-  rate_sums(a, words, bits, wave, wl, lane, blk);
+  rate_sums(a, bx, words, bits, wave, wl, lane, blk);
 }
 
 // Rate pass with the encoder's rice_k and tile_bits given: the same spans
 // and sums, from tile_bits alone (lanes stride over the wave's tiles).
 template <int N>
-__global__ __launch_bounds__(kBlock) void rate_given_kernel(RateLaunch a) {
+__global__ __launch_bounds__(kBlock) void rate_given_kernel(RateBatch bt) {
+  int64_t bx;
+  const RateLaunch& a = bt.it[rate_item(bt, bx)];
   __shared__ uint64_t blk[2][kBlock / 64];
   const int lane = threadIdx.x & 63;
   const int wl = threadIdx.x >> 6;
-  const int64_t wave = (int64_t)blockIdx.x * (kBlock / 64) + wl;
+  const int64_t wave = bx * (kBlock / 64) + wl;
   const int64_t span = wave_span<N>(a.n_tiles);
   const int64_t first = wave < rate_waves<N>(a.n_tiles) ? wave * span : a.n_tiles;
   const int64_t end = first + span < a.n_tiles ? first + span : a.n_tiles;
@@ -241,10 +258,14 @@ __global__ __launch_bounds__(kBlock) void rate_given_kernel(RateLaunch a) {
     words += (tb + 31u) / 32u;
     bits += tb;
   }
-  rate_sums(a, words, bits, wave, wl, lane, blk);
+  rate_sums(a, bx, words, bits, wave, wl, lane, blk);
 }
 
-__global__ void zero_u64_kernel(uint64_t* p) { *p = 0; }
+// total_bits = 0 for the matrices whose bit totals go through atomics
+__global__ void zero_totals_kernel(RateBatch bt) {
+  const int i = threadIdx.x;
+  if (i < bt.n && bt.it[i].block_words == nullptr) *bt.it[i].total_bits = 0;
+}
 
 // Exclusive scan of the n <= kMaxRateWaves / 4 per-block word sums in place,
 // and the total of the per-block bit sums; one block, kScanPer consecutive values
@@ -254,9 +275,14 @@ constexpr int kScanThreads = 1024;
 constexpr int kScanPer = 2;
 static_assert(kScanThreads * kScanPer >= kMaxRateWaves / (kBlock / 64), "scan covers every rate block");
 
-__global__ __launch_bounds__(kScanThreads) void scan_kernel(uint64_t* v, int64_t n,
-                                                            const uint64_t* bits,
-                                                            uint64_t* total_bits) {
+// one block per matrix with a workspace
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(RateBatch bt) {
+  const RateLaunch& a = bt.it[blockIdx.x];
+  if (a.block_words == nullptr) return;     // the whole block
+  uint64_t* v = a.block_words;
+  const int64_t n = bt.block0[blockIdx.x + 1] - bt.block0[blockIdx.x];
+  const uint64_t* bits = a.block_bits;
+  uint64_t* total_bits = a.total_bits;
   __shared__ uint64_t wtot[kScanThreads / 64];
   __shared__ uint64_t btot[kScanThreads / 64];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -337,7 +363,10 @@ constexpr int pack_lds_words() {
 }
 
 template <int N>
-__global__ __launch_bounds__(kBlock) void pack_kernel(RateLaunch a) {
+__global__ __launch_bounds__(kBlock) void pack_kernel(RateBatch bt) {
+  int64_t bx;
+  const RateLaunch& a = bt.it[rate_item(bt, bx)];
+  if (a.stream == nullptr) return;          // the whole block: not packing
   constexpr int G = N / kElemsPerLane;
   constexpr int TPW = 64 / G;
   constexpr int W = PackBound<N>::kWords;
@@ -345,7 +374,7 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(RateLaunch a) {
   const int lane = threadIdx.x & 63;
   const int r = lane % G;
   const int slot = lane / G;
-  const int64_t wave = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+  const int64_t wave = bx * (kBlock / 64) + (threadIdx.x >> 6);
   if (wave >= rate_waves<N>(a.n_tiles)) return;   // whole waves only
   uint32_t* buf = lds[threadIdx.x >> 6];
   const int64_t span = wave_span<N>(a.n_tiles);
@@ -353,8 +382,8 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(RateLaunch a) {
   const int64_t end = first + span < a.n_tiles ? first + span : a.n_tiles;
   // first word of this pass's tiles: the block's offset, then the words of
   // the block's earlier waves
-  uint64_t base = a.block_words[blockIdx.x];
-  for (int i = 0; i < (threadIdx.x >> 6); ++i) base += a.wave_words[(int64_t)blockIdx.x * (kBlock / 64) + i];
+  uint64_t base = a.block_words[bx];
+  for (int i = 0; i < (threadIdx.x >> 6); ++i) base += a.wave_words[bx * (kBlock / 64) + i];
   struct PassIn {
     uint4 q;
     uint32_t k, tb;
@@ -485,32 +514,61 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(RateLaunch a) {
 }
 
 template <int N>
-hipError_t launch_n(const RateLaunch& a, hipStream_t s) {
-  const int64_t waves = rate_waves<N>(a.n_tiles);
-  const int64_t blocks = (waves + kBlock / 64 - 1) / (kBlock / 64);
-  if (a.block_words == nullptr)
-    hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(1), 0, s, a.total_bits);
-  if (a.given)
-    hipLaunchKernelGGL(rate_given_kernel<N>, dim3((unsigned)blocks), dim3(kBlock), 0, s, a);
+hipError_t launch_n(const RateBatch& b, hipStream_t s) {
+  const unsigned blocks = (unsigned)b.block0[b.n];
+  bool atomics = false, given = false, pack = false;
+  for (int i = 0; i < b.n; ++i) {
+    atomics = atomics || b.it[i].block_words == nullptr;
+    given = given || b.it[i].given;
+    pack = pack || b.it[i].stream != nullptr;
+  }
+  if (atomics) hipLaunchKernelGGL(zero_totals_kernel, dim3(1), dim3(64), 0, s, b);
+  if (given)
+    hipLaunchKernelGGL(rate_given_kernel<N>, dim3(blocks), dim3(kBlock), 0, s, b);
   else
-    hipLaunchKernelGGL(rate_kernel<N>, dim3((unsigned)blocks), dim3(kBlock), 0, s, a);
-  if (a.block_words != nullptr)
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a.block_words, blocks,
-                       a.block_bits, a.total_bits);
-  if (a.stream != nullptr)
-    hipLaunchKernelGGL(pack_kernel<N>, dim3((unsigned)blocks), dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL(rate_kernel<N>, dim3(blocks), dim3(kBlock), 0, s, b);
+  hipLaunchKernelGGL(scan_kernel, dim3((unsigned)b.n), dim3(kScanThreads), 0, s, b);
+  if (pack) hipLaunchKernelGGL(pack_kernel<N>, dim3(blocks), dim3(kBlock), 0, s, b);
   return hipGetLastError();
+}
+
+template <int N>
+int64_t blocks_n(int64_t n_tiles) {
+  return (rate_waves<N>(n_tiles) + kBlock / 64 - 1) / (kBlock / 64);
 }
 
 }  // namespace
 
-hipError_t launch_rate(const RateLaunch& a, hipStream_t s) {
-  switch (a.tile) {
-    case 64: return launch_n<64>(a, s);
-    case 128: return launch_n<128>(a, s);
-    case 256: return launch_n<256>(a, s);
-    default: return launch_n<512>(a, s);
+int64_t rate_blocks(int tile, int64_t n_tiles) {
+  switch (tile) {
+    case 64: return blocks_n<64>(n_tiles);
+    case 128: return blocks_n<128>(n_tiles);
+    case 256: return blocks_n<256>(n_tiles);
+    default: return blocks_n<512>(n_tiles);
   }
+}
+
+// The matrices of one launch share the tile and, for a pass with given
+// values, the flag (the API groups them so).
+hipError_t launch_rate_batch(const RateBatch& b, hipStream_t s) {
+  switch (b.it[0].tile) {
+    case 64: return launch_n<64>(b, s);
+    case 128: return launch_n<128>(b, s);
+    case 256: return launch_n<256>(b, s);
+    default: return launch_n<512>(b, s);
+  }
+}
+
+hipError_t launch_rate(const RateLaunch& a, hipStream_t s) {
+  RateBatch b;
+  memset(&b, 0, sizeof(b));
+  b.n = 1;
+  b.it[0] = a;
+  b.block0[0] = 0;
+  b.block0[1] = rate_blocks(a.tile, a.n_tiles);
+  for (int i = 1; i < kRateMaxItems; ++i) b.it[i] = a;
+  for (int i = 2; i <= kRateMaxItems; ++i) b.block0[i] = b.block0[1];
+  return launch_rate_batch(b, s);
 }
 
 int64_t rate_workspace_blocks(int64_t n_tiles) {

@@ -101,6 +101,8 @@ _SIGNATURES = {
     "hq_gemm_batch": (_I32, [_PP, _I32, _P, _I32, _P, _SZ, _P, _P]),
     "hq_gemm_batch_workspace_bytes": (_SZ, [_I32, _P, _I32]),
     "hq_gemv_batch": (_I32, [_PP, _I32, _P, _I32, _P, _SZ, _P, _P]),
+    "hq_rate_batch": (_I32, [_PP, _I32, _P, _P, _SZ, _P, _P]),
+    "hq_rate_batch_workspace_bytes": (_SZ, [_I32, _P]),
     "hq_gemv_batch_workspace_bytes": (_SZ, [_I32, _P, _I32]),
     "hq_kv_scores": (_I32, [_PP, _P, _I64, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
     "hq_kv_scores_workspace_bytes": (_SZ, [_I64]),
@@ -319,6 +321,62 @@ def hq_rate(idx, coset, lattice="E8", tile=256, pack=False, capacity_words=None,
     if pack:
         res["stream"] = stream
         res["tile_word_offset"] = offs
+    return res
+
+
+class RateItem(ctypes.Structure):
+    _fields_ = [("idx", ctypes.c_void_p), ("coset", ctypes.c_void_p), ("n_tiles", ctypes.c_int64),
+                ("rice_k", ctypes.c_void_p), ("tile_bits", ctypes.c_void_p),
+                ("total_bits", ctypes.c_void_p), ("stream_words", ctypes.c_void_p),
+                ("capacity_words", ctypes.c_uint64), ("tile_word_offset", ctypes.c_void_p)]
+
+
+def hq_rate_batch(encs, lattice="E8", tile=256, pack=False, given=False, status=None,
+                  workspace=None, outs=None):
+    """hq_rate for several matrices sharing lattice and tile in one call (one
+    launch group per eight).  encs: dicts with idx and coset (and, with
+    given=True, the encoder's rice_k and tile_bits).  outs: the result of an
+    earlier call to write into.  Returns a list of dicts like hq_rate's."""
+    if not encs:
+        return []
+    dev = encs[0]["idx"].device
+    items = (RateItem * len(encs))()
+    res = []
+    for i, e in enumerate(encs):
+        _device_tensor(e["idx"], "idx")
+        n_tiles = e["idx"].numel() // tile
+        o = outs[i] if outs is not None else {}
+        rk = e["rice_k"] if given else o.get("rice_k")
+        if rk is None:
+            rk = torch.empty(n_tiles, dtype=torch.uint8, device=dev)
+        tb = e["tile_bits"] if given else o.get("tile_bits")
+        if tb is None:
+            tb = torch.empty(n_tiles, dtype=torch.int32, device=dev)
+        total = o.get("total_bits")
+        if total is None:
+            total = torch.empty(1, dtype=torch.int64, device=dev)
+        r = {"rice_k": rk, "tile_bits": tb, "total_bits": total}
+        cap = 0
+        if pack:
+            cap = n_tiles * ((4 + tile // 2 + 9 * tile + 31) // 32)
+            r["stream"] = o.get("stream")
+            if r["stream"] is None:
+                r["stream"] = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+            cap = min(cap, r["stream"].numel())
+            r["tile_word_offset"] = o.get("tile_word_offset")
+            if r["tile_word_offset"] is None:
+                r["tile_word_offset"] = torch.empty(n_tiles + 1, dtype=torch.int64, device=dev)
+        items[i] = RateItem(_addr(e["idx"]), _addr(e["coset"]), n_tiles, _addr(rk), _addr(tb),
+                            _addr(total), _addr(r.get("stream")), cap,
+                            _addr(r.get("tile_word_offset")))
+        res.append(r)
+    nb = lib().hq_rate_batch_workspace_bytes(len(encs), ctypes.byref(items))
+    ws = workspace if workspace is not None else torch.empty(max(nb, 16), dtype=torch.uint8,
+                                                             device=dev)
+    p = make_params(lattice, tile, 4.0, flags=HQ_RATE_GIVEN if given else 0)
+    code = lib().hq_rate_batch(ctypes.byref(p), len(encs), ctypes.byref(items), _ptr(ws),
+                               ws.numel(), _ptr(status), _stream(dev))
+    _check(code, "hq_rate_batch")
     return res
 
 

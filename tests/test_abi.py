@@ -243,6 +243,30 @@ def test_unpack_validation_codes():
     assert lib.hq_unpack_batch(ctypes.byref(p), 1, neg, None, None) == hq.HQ_EINVAL
 
 
+def test_rate_batch_validation_codes():
+    lib = hq.lib()
+    p = hq.make_params("E8", 256, 4.0)
+    items = (hq.RateItem * 3)()
+    for i, n in enumerate((10, 0, 3000)):
+        items[i] = hq.RateItem(FAKE, FAKE, n, FAKE, FAKE, FAKE, None, 0, None)
+    assert lib.hq_rate_batch_workspace_bytes(3, items) == sum(
+        lib.hq_rate_workspace_bytes(n) for n in (10, 0, 3000))
+    # nothing to compute; negative counts; a workspace is required
+    assert lib.hq_rate_batch(ctypes.byref(p), 0, None, None, 0, None, None) == hq.HQ_OK
+    assert lib.hq_rate_batch(ctypes.byref(p), -1, items, FAKE, 1 << 20, None, None) == hq.HQ_EINVAL
+    items[1].n_tiles = -1
+    assert lib.hq_rate_batch_workspace_bytes(3, items) == 0
+    assert lib.hq_rate_batch(ctypes.byref(p), 3, items, FAKE, 1 << 20, None, None) == hq.HQ_EINVAL
+    items[1].n_tiles = 0
+    assert lib.hq_rate_batch(ctypes.byref(p), 3, items, None, 0, None, None) == hq.HQ_EINVAL
+    # missing outputs, packing without offsets
+    items[0].rice_k = None
+    assert lib.hq_rate_batch(ctypes.byref(p), 3, items, FAKE, 1 << 20, None, None) == hq.HQ_EINVAL
+    items[0].rice_k = FAKE
+    items[2].stream_words = FAKE
+    assert lib.hq_rate_batch(ctypes.byref(p), 3, items, FAKE, 1 << 20, None, None) == hq.HQ_EINVAL
+
+
 def test_gemv_validation_codes():
     lib = hq.lib()
     p = hq.make_params("E8", 256, 4.0, 3)

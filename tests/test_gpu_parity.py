@@ -680,6 +680,37 @@ def test_unpack_any_k_long_codes_and_corrupt_tiles():
     assert np.array_equal(T.host(g["idx"]).astype(np.int64)[good], idx[good])
 
 
+@pytest.mark.parametrize("lattice,n", [("E8", 256), ("A2", 128), ("D4", 64)])
+def test_rate_batch_matches_single_calls(lattice, n):
+    """hq_rate_batch on ten matrices of mixed sizes (one tile, ragged counts,
+    more than one launch group), rate only, packing, and packing with the
+    encoder's values given: every output equals one hq_rate call per
+    matrix, bit for bit (streams up to their last word)."""
+    rng = np.random.default_rng(91 + n)
+    shapes = [(1, n), (37, 1536), (300, 4096), (5, 768), (129, 2048), (64, 512), (2, 4096),
+              (1000, 1024), (3, 256), (90, 2560)]
+    encs = []
+    for i, (rows, cols) in enumerate(shapes):
+        bits = workloads.f32_to_bf16_bits((rng.standard_normal((rows, cols)) * 0.02)
+                                          .astype(np.float32))
+        encs.append(hq.hq_encode_tiles(T.bf16_device(bits, (rows, cols)), lattice, n, 4.0, 3))
+    for pack, given in ((False, False), (True, False), (True, True)):
+        say("case: rate batch %s/%d pack=%s given=%s" % (lattice, n, pack, given))
+        batch = hq.hq_rate_batch(encs, lattice, n, pack=pack, given=given)
+        for i, e in enumerate(encs):
+            one = hq.hq_rate(e["idx"], e["coset"], lattice, n, pack=pack,
+                             given=e if given else None)
+            torch.cuda.synchronize()
+            b = batch[i]
+            assert torch.equal(b["rice_k"], one["rice_k"]), i
+            assert torch.equal(b["tile_bits"], one["tile_bits"]), i
+            assert int(b["total_bits"].item()) == int(one["total_bits"].item()), i
+            if pack:
+                assert torch.equal(b["tile_word_offset"], one["tile_word_offset"]), i
+                nw = int(one["tile_word_offset"][-1].item())
+                assert torch.equal(b["stream"][:nw], one["stream"][:nw]), i
+
+
 def test_rate_given_values_that_do_not_hold_the_codes():
     """HQ_RATE_GIVEN with rice_k / tile_bits that are not the encoder's: a k
     above 8, a k one below the optimum (longer codes than tile_bits), and
