@@ -38,8 +38,8 @@ DEC_BYTES_PER_TILE = 256 + 4 + 4 + 512
 KERNEL_SOURCES = ("hq_e8fast.hip", "hq_lanes.h", "hq_device.h", "hq_internal.h")
 MEASURED_TRAFFIC = {
     "sources_sha256": "aecf7cb8364cdf9ce554d40ee42718e6255ee38f73e15f73f785749b1b9b001a",
-    "encode": {"read": 513.85, "write": 269.33},
-    "decode": {"read": 264.30, "write": 512.00},
+    "encode": {"read": 513.87, "write": 269.32},
+    "decode": {"read": 264.28, "write": 512.00},
     "valu_lane_ops_per_weight": {"encode": 36.51, "decode": 11.92},
 }
 # VALU issue roof: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (a wave64 instruction
