@@ -19,7 +19,10 @@
  * Conventions for every entry point
  *   - All array arguments are caller-allocated DEVICE pointers (hipMalloc or
  *     equivalent) on the current HIP device; `p` is host memory read during
- *     the call only.  The library allocates nothing on any path.
+ *     the call only.  The library allocates nothing on any path.  The
+ *     exceptions are the host helpers and the checkpoint-file calls
+ *     (hq_ckpt_*), whose arrays are host memory and which make no device
+ *     call (their status codes add HQ_EIO, HQ_EFORMAT and HQ_ENOTFOUND).
  *   - Calls enqueue kernels on `stream` and return without synchronising.
  *     The return code reports argument validation (HQ_EINVAL,
  *     HQ_EUNSUPPORTED), the auto-scale index range bound (HQ_ERANGE) and
