@@ -163,3 +163,28 @@ def test_device_pack_file_unpack_round_trip(tmp_path):
                             torch.bfloat16)
     torch.cuda.synchronize()
     assert torch.equal(y0, y1)
+
+
+@pytest.mark.gpu
+def test_layer_checkpoint_round_trip(tmp_path):
+    """A Llama-3.1-8B-shaped layer as the benchmark draws it: seven matrices
+    encoded and packed in one batched call each, written as seven records of
+    one file, read back onto the device and decoded by one batched
+    hq_unpack: every index and coset equals the encoder's."""
+    dev = torch.device("cuda")
+    xs = [workloads.llama_stack_torch(0, m, dev) for m in range(len(workloads.LLAMA_LAYER))]
+    print("case: layer checkpoint (seven matrices)", flush=True)
+    encs = hq.hq_encode_batch(xs, "E8", 256, 4.0, 0)
+    packs = hq.hq_rate_batch(encs, "E8", 256, pack=True, given=True)
+    path = str(tmp_path / "layer0.hqckpt")
+    names = [name for name, _, _ in workloads.LLAMA_LAYER]
+    for name, x, e, pk in zip(names, xs, encs, packs):
+        hq.ckpt_save(path, name, pk, e["scale"], x.shape[0], x.shape[1])
+    assert [e["name"] for e in hq.ckpt_entries(path)] == names
+    loaded = [hq.ckpt_load(path, name, device=dev) for name in names]
+    outs = hq.hq_unpack_batch(loaded, "E8", 256)
+    torch.cuda.synchronize()
+    for name, e, got, u in zip(names, encs, loaded, outs):
+        assert torch.equal(u["idx"].reshape(-1), e["idx"].reshape(-1)), name
+        assert torch.equal(u["coset"].reshape(-1), e["coset"].reshape(-1)), name
+        assert torch.equal(got["scale"].reshape(-1), e["scale"].reshape(-1)), name
