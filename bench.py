@@ -421,6 +421,23 @@ def secondary(layer0, bps, dev):
           "attention_us": round(ms_a * 1e3, 2),
           "attention_bf16_sdpa_us": round(ms_ab * 1e3, 2),
           "attention_cache_gbs": round(2 * heads * seq * (128 + 8) / (ms_a * 1e-3) / 1e9, 1)}
+    # bias of the cached inner products at this scale, dither against the
+    # rotation-only control: per query q_j, b_j = q_j . mean over the cache
+    # of (khat - k), as a z-score against its spread under independent errors
+    qb = torch.from_numpy(workloads.kv_queries().astype(np.float32)).to(dev).double()
+    bias = {"workload": "K cache [8, 32768, 128] at 4 bps, 4096 queries: z_j = q_j . mean(khat - k) "
+                        "/ its standard error; mean and max |z| over the queries"}
+    for mode, ds in (("dither", 2), ("rotation_only", None)):
+        ek = hq.hq_kv_encode(kvs[0], bps, 1, dither_seed=ds)
+        kh = hq.hq_decode_tiles(ek["idx"], ek["coset"], ek["scale"], "E8", 128, 1, torch.float32,
+                                dither_seed=ds)
+        err = kh.double() - kvs[0].double()
+        b = qb @ err.mean(0)
+        sd = torch.sqrt((qb * qb) @ (err.var(0) / err.shape[0]))
+        z = (b / sd).abs()
+        bias[mode] = {"z_mean": round(float(z.mean()), 3), "z_max": round(float(z.max()), 3)}
+        del ek, kh, err
+    kv["bias"] = bias
     return {"pack": pack, "unpack": unpack, "gemv": gemv, "gemm": gemm, "kv": kv,
             "variants": variants,
             "lattice_sweep": sweep}
