@@ -355,15 +355,34 @@ def rate(idx, coset_words, lattice, n):
     return k, tb, int(np.sum(tb)), words, off
 
 
-def itemized_rate(tile_bits_arr, lattice, n, scale_bits=16):
-    """Itemized accounting in bits: payload, coset, k field, scale, padding."""
+def itemized_rate(tile_bits_arr, lattice, n, scale_bits=16, offset_bits=0):
+    """Itemized rate accounting in bits ([ICLR abstract]: one itemized rate
+    accounting), every item part of the total:
+
+      payload   the Rice codes of the stored indices (tile_bits minus the k
+                field and the coset bits);
+      coset     one bit per E8 block (A2: per pair; D4, Z: none);
+      k_field   4 bits per tile;
+      scale     scale_bits per tile (16: the bf16 value of reading R2 is
+                lossless in 16 bits; a store that keeps fp32 passes 32);
+      padding   the zero bits that start every tile on a 32-bit word;
+      offsets   offset_bits per entry of the (n_tiles + 1)-entry tile word
+                offset table, for a store that keeps one (0: the stream is
+                self-delimiting tile after tile).
+
+    bps = total / weights; bps_stream counts the packed stream alone
+    (payload + coset + k field + padding); bps_payload the Rice codes."""
     tb = np.asarray(tile_bits_arr, np.int64)
     T = tb.size
     cb = coset_bits_per_tile(lattice, n) * T
     kb = rice.K_FIELD_BITS * T
     payload = int(tb.sum()) - cb - kb
     pad = int((((tb + 31) // 32) * 32 - tb).sum())
-    total = payload + cb + kb + scale_bits * T
-    return {"payload": payload, "coset": cb, "k_field": kb,
-            "scale": scale_bits * T, "padding": pad,
-            "bps": total / (T * n), "bps_payload": payload / (T * n)}
+    sb = scale_bits * T
+    ob = offset_bits * (T + 1) if offset_bits else 0
+    stream = payload + cb + kb + pad
+    total = stream + sb + ob
+    w = T * n
+    return {"payload": payload, "coset": cb, "k_field": kb, "scale": sb, "padding": pad,
+            "offsets": ob, "total": total, "bps": total / w, "bps_stream": stream / w,
+            "bps_payload": payload / w}

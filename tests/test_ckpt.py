@@ -60,6 +60,25 @@ def test_round_trip_of_oracle_streams(tmp_path):
             assert np.array_equal(cos, rice.coset_bit_rows(ora["coset"], cb))
 
 
+def test_record_size_is_the_itemized_stored_rate(tmp_path):
+    """A record's bytes are the oracle's itemized accounting of what it
+    stores (fp32 scales, a uint64 tile word offset table, the packed stream
+    with its word padding) plus the fixed 136-byte header and the zero bytes
+    that align the scale and word arrays to 8 bytes."""
+    rng = np.random.default_rng(8)
+    path = str(tmp_path / "one.hqckpt")
+    for name, rows, cols in (("even", 16, 512), ("odd", 7, 768)):
+        ora, idx, words, off = _oracle_packed(rng, rows, cols)
+        before = os.path.getsize(path) if os.path.exists(path) else 8   # file magic
+        _save(path, name, words, off, ora["scale"], rows, cols)
+        grown = os.path.getsize(path) - before
+        it = codec.itemized_rate(ora["tile_bits"], "E8", 256, scale_bits=32, offset_bits=64)
+        T, W = idx.shape[0], len(words)
+        align = 8 * ((4 * T) % 8 + (4 * W) % 8)
+        assert 8 * grown == it["total"] + 8 * 136 + align
+        assert it["bps"] > codec.itemized_rate(ora["tile_bits"], "E8", 256)["bps"]
+
+
 def test_error_codes(tmp_path):
     rng = np.random.default_rng(6)
     ora, idx, words, off = _oracle_packed(rng, 8, 512)

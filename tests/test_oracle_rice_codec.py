@@ -194,13 +194,42 @@ def test_e8_decode_exact_in_fp32():
     assert np.array_equal(xh.astype(np.float32).astype(np.float64), xh)
 
 
+def test_itemized_rate_items_on_a_hand_computed_case():
+    """Two E8/256 tiles worked by hand.  Tile 0 stores 256 zeros: zeta = 0,
+    L(k) = 256 (1 + k), so k = 0 and the payload is 256 bits; tile_bits =
+    4 + 32 + 256 = 292, 10 words, 28 padding bits.  Tile 1 stores 256 ones:
+    zeta = 2, L(0) = L(1) = L(2) = 768, the smallest k (0) is taken; tile_bits
+    = 4 + 32 + 768 = 804, 26 words, 28 padding bits."""
+    idx = np.zeros((2, 256), np.int64)
+    idx[1] = 1
+    k, tb = rice.tile_bits(idx, codec.coset_bits_per_tile("E8", 256))
+    assert k.tolist() == [0, 0] and tb.tolist() == [292, 804]
+    r = codec.itemized_rate(tb, "E8", 256)
+    assert r["payload"] == 256 + 768
+    assert r["coset"] == 2 * 32
+    assert r["k_field"] == 2 * 4
+    assert r["scale"] == 2 * 16
+    assert r["padding"] == 28 + 28
+    assert r["offsets"] == 0
+    assert r["total"] == 1024 + 64 + 8 + 32 + 56 == 1184
+    assert r["bps"] == 1184 / 512 and r["bps_stream"] == 1152 / 512 and r["bps_payload"] == 2.0
+    # the stream items are the packer's word count, bit for bit
+    _, _, words, _ = rice.pack(idx, np.zeros((2, 1), np.uint32), 32)
+    assert 32 * len(words) == r["payload"] + r["coset"] + r["k_field"] + r["padding"]
+    # a store that keeps fp32 scales and a uint64 table of the 3 tile offsets
+    s = codec.itemized_rate(tb, "E8", 256, scale_bits=32, offset_bits=64)
+    assert s["scale"] == 64 and s["offsets"] == 3 * 64 and s["total"] == 1152 + 64 + 192
+
+
 def test_itemized_rate_matches_pages_compression():
-    """About 3.9x compression of bf16 weights at 4 bps means about 4.1 bits
-    per weight all-in; the itemized E8 rate lands there."""
+    """About 3.9x compression of bf16 weights at 4 bps ([ICLR abstract]) means
+    about 4.1 bits per weight all-in; the itemized E8 rate, word padding
+    included, lands there."""
     x = workloads.bf16_bits_to_f64(workloads.llama_matrix(1, shape=(256, 4096)))
     e = codec.encode(x, "E8", 256, 4.0, rht_seed=0)
     r = codec.itemized_rate(e["tile_bits"], "E8", 256)
-    assert 4.05 < r["bps"] < 4.35
+    assert r["total"] == sum(r[k] for k in ("payload", "coset", "k_field", "scale", "padding"))
+    assert 4.05 < r["bps"] < 4.45
     assert 3.6 < 16 / r["bps"] < 4.0
 
 
