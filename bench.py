@@ -64,9 +64,11 @@ def parse():
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--bps", type=float, default=4.0)
     ap.add_argument("--cpu-baseline", type=int, default=1,
-                    help="time the oracle on a sample of the workload (rank 0, N=1)")
-    ap.add_argument("--cpu-sample-stride", type=int, default=4,
-                    help="oracle sample: every k-th tile of layer 0")
+                    help="time the oracle on the 1024x1024 matrix and one whole layer "
+                         "(rank 0, N=1), and compare it with the GPU's results")
+    ap.add_argument("--cold-steps", type=int, default=2,
+                    help="also time this many cache-cold steps (all encodes, then all "
+                         "decodes; reported beside the headline)")
     ap.add_argument("--secondary", type=int, default=1,
                     help="after the timed steps, also time the pack pass and the KV path "
                          "(reported beside the headline, never in it)")
@@ -77,49 +79,116 @@ def parse():
 
 
 # ------------------------------------------------------------ CPU baseline
+#
+# The oracle (fp64 NumPy, unmodified) timed on the host cores on the two
+# workloads it finishes in seconds: the 1024x1024 fp32 matrix (E8, 4 bps,
+# tile 256, RHT seed 1) and one whole layer of the stack (the benchmarked
+# layer 0, copied from the GPU; E8, 4 bps, tile 256, RHT seed 0).  Work:
+# encode (rotation, nearest point, strip, Rice k and bits) and decode.  One
+# untimed warm-up pass, which also compares the oracle with the GPU's own
+# results of the same inputs (the parity record of the line), then three
+# timed passes; the median is reported.  Tile chunks are spread over a pool
+# of forked single-threaded processes.
 
-def _oracle_chunk(args):
-    tiles, seed, bps = args
+_CPU = {}     # inputs and GPU results, set before the pool forks
+
+
+def _oracle_chunk(task):
+    """One chunk of tiles: oracle encode + decode; with compare=True also
+    the comparison against the GPU's results of the same tiles."""
     from threadpoolctl import threadpool_limits
+
+    import numpy as np
+
     from oracle import codec
+    key, t0, t1, compare = task
+    w = _CPU[key]
     with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        e = codec.encode(tiles, "E8", 256, bps, rht_seed=seed)
-        codec.decode(e["idx"], e["coset"], e["scale"], "E8", 256, seed)
-        return time.perf_counter() - t0
+        X = w["x"](t0, t1)
+        e = codec.encode(X, "E8", 256, w["bps"], rht_seed=w["seed"])
+        codec.decode(e["idx"], e["coset"], e["scale"], "E8", 256, w["seed"])
+        if not compare:
+            return None
+        g = w["gpu"]
+        gs = g["scale"][t0:t1].astype(np.float64)
+        keep = gs == e["scale"]
+        gi = g["idx"][t0:t1].astype(np.int64)
+        bad = np.any((gi[keep] != e["idx"][keep]).reshape(-1, 32, 8), axis=-1)
+        gc = codec.unpack_cosets(g["coset"][t0:t1][keep], "E8", 256)
+        bad |= gc != codec.unpack_cosets(e["coset"][keep], "E8", 256)
+        near = e["margin"][keep] < 1e-6
+        ok = ~np.any(bad, axis=1)
+        # decoded weights: the oracle's decode of the GPU's own indices
+        yd = codec.bf16_bits(codec.bf16_rne(codec.decode(gi, g["coset"][t0:t1], gs, "E8", 256,
+                                                         w["seed"])))
+        return {"tiles": t1 - t0, "scale_differs": int(np.sum(~keep)),
+                "blocks": int(bad.size), "mismatches": int(bad.sum()),
+                "mismatches_outside_near_ties": int(np.sum(bad & ~near)),
+                "near_ties": int(near.sum()),
+                "rate_differs": int(np.sum(g["rice_k"][t0:t1][keep][ok] != e["rice_k"][keep][ok]) +
+                                    np.sum(g["tile_bits"][t0:t1][keep][ok] != e["tile_bits"][keep][ok])),
+                "decode_bf16_differs": int(np.sum(g["y"][t0:t1] != yd))}
 
 
-def cpu_baseline(stride, bps):
-    """The oracle (fp64 NumPy, unmodified) on every stride-th tile of a
-    host-drawn layer of the same shapes and distribution, spread over the
-    host's cores (one single-threaded process each)."""
+def cpu_baseline(layer0_host, small_host, bps, runs=3):
+    """Times the oracle on the host cores (see above); returns (cpu_baseline
+    object, parity record)."""
     import multiprocessing as mp
+    import statistics
 
     import numpy as np
 
     import workloads
-    chunks = []
-    n_w = 0
-    for m in range(7):
-        bits = workloads.llama_matrix(m, layer=0)
-        t = workloads.bf16_bits_to_f64(bits.reshape(-1, 256)[::stride])
-        n_w += t.size
-        chunks.extend(np.array_split(t, max(1, len(t) // 2048)))
-    procs = min(os.cpu_count() or 1, 16)
+    from oracle import codec
+
+    _CPU.clear()
+    _CPU["small"] = {"x": lambda a, b: codec.tiles(small_host["x"], 256)[a:b], "bps": bps,
+                     "seed": 1, "gpu": small_host, "tiles": small_host["x"].size // 256}
+    lb = layer0_host["bits"]
+    _CPU["layer"] = {"x": lambda a, b: workloads.bf16_bits_to_f64(lb[a:b]), "bps": bps,
+                     "seed": 0, "gpu": layer0_host, "tiles": len(lb)}
+    host_cpus = os.cpu_count() or 1
+    procs = min(host_cpus, 16)          # the CPU share of one GPU on the box
     ctx = mp.get_context("fork")
-    with ctx.Pool(procs) as pool:
-        t0 = time.perf_counter()
-        pool.map(_oracle_chunk, [(c, 0, bps) for c in chunks], chunksize=1)
-        wall = time.perf_counter() - t0
-    return {
+    pool = ctx.Pool(procs)
+    out, parity = {}, {}
+    try:
+        for key, chunk in (("small", 256), ("layer", 4096)):
+            n_t = _CPU[key]["tiles"]
+            tasks = [(key, a, min(a + chunk, n_t)) for a in range(0, n_t, chunk)]
+            parts = pool.map(_oracle_chunk, [t + (True,) for t in tasks], chunksize=1)
+            rec = {k: sum(p[k] for p in parts) for k in parts[0]}
+            rec["near_tie_fraction"] = rec["near_ties"] / max(rec["blocks"], 1)
+            rec["mismatch_fraction"] = rec["mismatches"] / max(rec["blocks"], 1)
+            parity[key] = rec
+            walls = []
+            for _ in range(runs):
+                t0 = time.perf_counter()
+                pool.map(_oracle_chunk, [t + (False,) for t in tasks], chunksize=1)
+                walls.append(time.perf_counter() - t0)
+            print("cpu baseline %s: %s s" % (key, ", ".join("%.2f" % w for w in walls)),
+                  file=sys.stderr, flush=True)
+            out[key] = (statistics.median(walls), n_t * 256)
+    finally:
+        pool.close()
+        pool.join()
+        _CPU.clear()
+    wall, n_w = out["layer"]
+    base = {
         "value": round(2.0 * n_w / wall / 1e9, 6),
         "unit": "GB/s (bf16 in)",
         "cores": procs,
+        "host_cpu_count": host_cpus,
         "kind": "oracle",
-        "sample": "every %dth 256-weight tile of one host-drawn layer of the same "
-                  "shapes and distribution (%d weights), E8 4 bps encode + decode, "
-                  "%d single-threaded processes, %.1f s wall" % (stride, n_w, procs, wall),
+        "sample": "one whole layer of the stack (layer 0, %d weights, copied from the GPU), "
+                  "E8 4 bps tile 256, oracle encode (rotation, nearest point with margins, "
+                  "strip, Rice k and bits) + decode; median of %d passes after a warm-up, "
+                  "%.2f s; %d single-threaded processes on a host reporting %d CPUs"
+                  % (n_w, runs, wall, procs, host_cpus),
+        "small_fp32_1024x1024": {"median_s": round(out["small"][0], 4),
+                                 "gbs_in": round(4.0 * out["small"][1] / out["small"][0] / 1e9, 6)},
     }
+    return base, parity
 
 
 # ------------------------------------------------------------------- GPU
@@ -451,8 +520,6 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    cpu = cpu_baseline(args.cpu_sample_stride, args.bps) if args.cpu_baseline else None
-
     import torch
 
     import workloads
@@ -550,7 +617,81 @@ def main():
                "unit": "T VALU lane-ops/s (issued)", "frac": round(achieved / VALU_PEAK_LANE_OPS, 4),
                "lane_ops_per_weight": MEASURED_TRAFFIC["valu_lane_ops_per_weight"][dom_name]}
 
+    # cache-cold form of the same work: every layer's encode, then every
+    # layer's decode, so no decode finds its indices in the 256 MB Infinity
+    # Cache (the headline decodes each layer right after its encode)
+    cold = None
+    if args.cold_steps > 0:
+        def cold_step():
+            for layer, (xs, encs, ys) in enumerate(layers):
+                hq.hq_encode_batch(xs, "E8", 256, args.bps, layer, outs=encs)
+            for layer, (xs, encs, ys) in enumerate(layers):
+                hq.hq_decode_batch(encs, "E8", 256, layer, torch.bfloat16, outs=ys)
+        cold_step()
+        torch.cuda.synchronize()
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(args.cold_steps):
+            cold_step()
+        c1.record()
+        torch.cuda.synchronize()
+        cms = c0.elapsed_time(c1) / args.cold_steps
+        cold = {"workload": "the same stack, all 32 encodes then all 32 decodes per step",
+                "steps": args.cold_steps, "ms_per_step": round(cms, 4),
+                "value": round(2.0 * n_weights / (cms * 1e-3) / 1e9, 3),
+                "pct_hbm_peak_algorithmic": round(100.0 * (ENC_BYTES_PER_TILE + DEC_BYTES_PER_TILE)
+                                                  * n_tiles / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)}
+
+    # the achievable-bandwidth reference: a plain device copy of 4 GiB
+    src = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    copy_ms = time_calls(lambda: dst.copy_(src), 5)
+    copy_gbs = 2.0 * src.numel() / (copy_ms * 1e-3) / 1e9
+    del src, dst
+
     extra = secondary(layers[0], args.bps, dev) if args.secondary else None
+
+    cpu = parity = None
+    if args.cpu_baseline:
+        import numpy as np
+        xs0, encs0, ys0 = layers[0]
+        # the last timed step's results for layer 0, and its inputs, on the host
+        layer0_host = {
+            "bits": np.concatenate([x.view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1, 256)
+                                    for x in xs0]),
+            "scale": np.concatenate([e["scale"].cpu().numpy() for e in encs0]),
+            "idx": np.concatenate([e["idx"].cpu().numpy().reshape(-1, 256) for e in encs0]),
+            "coset": np.concatenate([e["coset"].cpu().numpy().view(np.uint32).reshape(-1, 1)
+                                     for e in encs0]),
+            "rice_k": np.concatenate([e["rice_k"].cpu().numpy() for e in encs0]).astype(np.int64),
+            "tile_bits": np.concatenate([e["tile_bits"].cpu().numpy().view(np.uint32)
+                                         for e in encs0]).astype(np.int64),
+            "y": np.concatenate([y.view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1, 256)
+                                 for y in ys0]),
+        }
+        sx = workloads.small_fp32()
+        sxd = torch.from_numpy(sx).to(dev)
+        se = hq.hq_encode_tiles(sxd, "E8", 256, args.bps, 1)
+        sy = hq.hq_decode_tiles(se["idx"], se["coset"], se["scale"], "E8", 256, 1, torch.bfloat16)
+        torch.cuda.synchronize()
+        small_host = {
+            "x": sx, "scale": se["scale"].cpu().numpy(),
+            "idx": se["idx"].cpu().numpy().reshape(-1, 256),
+            "coset": se["coset"].cpu().numpy().view(np.uint32).reshape(-1, 1),
+            "rice_k": se["rice_k"].cpu().numpy().astype(np.int64),
+            "tile_bits": se["tile_bits"].cpu().numpy().view(np.uint32).astype(np.int64),
+            "y": sy.view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1, 256)}
+        del sxd, se, sy
+        cpu, par = cpu_baseline(layer0_host, small_host, args.bps)
+        parity = {
+            "rule": "indices and coset bits equal the oracle's on every block except oracle "
+                    "near-ties (margin < 1e-6), scales equal except on bf16-midpoint tiles, "
+                    "k and bits equal on matching tiles, bf16 decode of the GPU's indices "
+                    "equal to the oracle's",
+            "small_fp32_1024x1024": par["small"],
+            "llama_layer0_all_seven": par["layer"]}
 
     value = 2.0 * n_weights / (ms_per_step * 1e-3) / 1e9
     alg = (ENC_BYTES_PER_TILE + DEC_BYTES_PER_TILE) * n_tiles / (ms_per_step * 1e-3) / 1e9
@@ -594,7 +735,10 @@ def main():
         },
         "host_wall_ms_per_step": round(wall * 1e3 / args.steps, 3),
         "gpu_event_ms_per_step": round(gpu_ms / args.steps, 3),
+        "cache_cold": cold,
+        "device_copy_gbs": round(copy_gbs, 1),
         "cpu_baseline": cpu,
+        "parity": parity,
         "secondary": extra,
     }
     print(json.dumps(out), flush=True)
