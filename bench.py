@@ -29,18 +29,15 @@ HBM_PEAK_GBS = 8000.0
 ENC_BYTES_PER_TILE = 512 + 256 + 4 + 1 + 4 + 4
 DEC_BYTES_PER_TILE = 256 + 4 + 4 + 512
 
-# Measured HBM bytes per tile (rocprofv3 FETCH_SIZE and WRITE_SIZE per
-# dispatch, each scaled by what the same counter reads for a copy of known
-# size) and VALU lane-operations per weight (SQ_INSTS_VALU per dispatch x 64
-# lanes); the runs are summarised in profiles/.  They describe the kernels
-# built from the sources with this sha256 and are reported only while the
-# sources still match.
+# Measured per kernel (rocprofv3, summarised in profiles/): HBM bytes per
+# algorithmic byte (FETCH_SIZE + WRITE_SIZE per dispatch, each scaled by
+# what the same counter reads for a copy of known size, over the dispatch's
+# algorithmic bytes) and VALU lane-operations (SQ_INSTS_VALU x 64 lanes) per
+# algorithmic byte and per weight.  They describe the kernels built from the
+# sources with this sha256 and are reported only while the sources match.
 KERNEL_SOURCES = ("hq_e8fast.hip", "hq_lanes.h", "hq_device.h", "hq_internal.h")
 MEASURED_TRAFFIC = {
-    "sources_sha256": "aecf7cb8364cdf9ce554d40ee42718e6255ee38f73e15f73f785749b1b9b001a",
-    "encode": {"read": 513.87, "write": 269.32},
-    "decode": {"read": 264.28, "write": 512.00},
-    "valu_lane_ops_per_weight": {"encode": 36.51, "decode": 11.92},
+    "sources_sha256": None,
 }
 # VALU issue roof: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (a wave64 instruction
 # occupies a SIMD for 4 cycles; fp64 add / mul / fma issue at the same rate)
@@ -66,6 +63,9 @@ def parse():
     ap.add_argument("--cpu-baseline", type=int, default=1,
                     help="time the oracle on the 1024x1024 matrix and one whole layer "
                          "(rank 0, N=1), and compare it with the GPU's results")
+    ap.add_argument("--pipeline", type=int, default=1,
+                    help="also time the pipelined form of the step (one launch encodes layer "
+                         "l and decodes layer l - 1) and report it as the headline")
     ap.add_argument("--cold-steps", type=int, default=2,
                     help="also time this many cache-cold steps (all encodes, then all "
                          "decodes; reported beside the headline)")
@@ -545,77 +545,110 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # events for the timed region are created up front (creation is a host
-    # call that would otherwise sit between kernel launches)
-    n_ev = 2 * len(layers) * args.steps
-    ev = {"enc": [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)],
-          "dec": [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)],
-          "enc_tiles": [], "dec_tiles": []}
-    cursor = {"enc": 0, "dec": 0}
+    L = len(layers)
 
-    def mark(kind):
-        ev[kind][cursor[kind]].record()
-        cursor[kind] += 1
+    class Launches:
+        """HIP events recorded around each launch of one kind, on the current
+        stream (every call of the library enqueues on it), created up front
+        so that no host call sits between launches of the timed region."""
 
-    def step(timed):
+        def __init__(self, n):
+            self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+            self.k = 0
+            self.bytes = []
+
+        def begin(self):
+            self.ev[self.k].record()
+
+        def end(self, nbytes):
+            self.ev[self.k + 1].record()
+            self.k += 2
+            self.bytes.append(nbytes)
+
+        def stats(self, steps):
+            durs = [self.ev[2 * i].elapsed_time(self.ev[2 * i + 1]) for i in range(self.k // 2)]
+            tot_ms = sum(durs)
+            return {"launches": len(durs), "avg_us": 1e3 * tot_ms / len(durs),
+                    "sum_ms_per_step": tot_ms / steps,
+                    "bytes_per_launch": sum(self.bytes) / len(self.bytes),
+                    "gbs": sum(self.bytes) / (tot_ms * 1e-3) / 1e9}
+
+    enc_bytes = [t * ENC_BYTES_PER_TILE for t in tiles_per_layer]
+    dec_bytes = [t * DEC_BYTES_PER_TILE for t in tiles_per_layer]
+
+    def step_sequential(timers):
         # one launch encodes a layer's seven projections, one launch decodes them
         for layer, (xs, encs, ys) in enumerate(layers):
-            if timed:
-                mark("enc")
+            if timers:
+                timers["encode"].begin()
             hq.hq_encode_batch(xs, "E8", 256, args.bps, layer, outs=encs)
-            if timed:
-                mark("enc")
-                ev["enc_tiles"].append(tiles_per_layer[layer])
-                mark("dec")
+            if timers:
+                timers["encode"].end(enc_bytes[layer])
+                timers["decode"].begin()
             hq.hq_decode_batch(encs, "E8", 256, layer, torch.bfloat16, outs=ys)
-            if timed:
-                mark("dec")
-                ev["dec_tiles"].append(tiles_per_layer[layer])
+            if timers:
+                timers["decode"].end(dec_bytes[layer])
 
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
+    def step_pipelined(timers):
+        # launch l encodes layer l and decodes layer l - 1 (L + 1 launches)
+        for layer in range(L + 1):
+            xs, encs, _ = layers[layer] if layer < L else ([], None, None)
+            dsrc, ys = (layers[layer - 1][1], layers[layer - 1][2]) if layer > 0 else ([], None)
+            if timers:
+                timers["codec"].begin()
+            hq.hq_encode_decode_batch(xs, dsrc, "E8", 256, args.bps, enc_seed=layer,
+                                      dec_seed=layer - 1, enc_outs=encs, dec_outs=ys)
+            if timers:
+                timers["codec"].end((enc_bytes[layer] if layer < L else 0) +
+                                    (dec_bytes[layer - 1] if layer > 0 else 0))
 
-    # timed region: whole steps, bracketed by synchronisation
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    t_start.record()
-    for _ in range(args.steps):
-        step(True)
-    t_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    gpu_ms = t_start.elapsed_time(t_end)
-    ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
+    def run(step, kinds):
+        for _ in range(args.warmup):
+            step(None)
+        torch.cuda.synchronize()
+        timers = {k: Launches(args.steps * (L + 1)) for k in kinds}
+        # timed region: whole steps, bracketed by synchronisation
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        t_start.record()
+        for _ in range(args.steps):
+            step(timers)
+        t_end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        gpu_ms = t_start.elapsed_time(t_end)
+        return {"ms_per_step": max(gpu_ms, wall * 1e3) / args.steps,
+                "host_wall_ms_per_step": wall * 1e3 / args.steps,
+                "gpu_event_ms_per_step": gpu_ms / args.steps,
+                "kernels": {k: t.stats(args.steps) for k, t in timers.items()}}
 
-    def kernel_stats(name, tiles_key, bytes_per_tile):
-        evs = ev[name][:cursor[name]]
-        durs = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(len(evs) // 2)]
-        tiles = ev[tiles_key]
-        tot_ms = sum(durs)
-        tot_bytes = sum(t * bytes_per_tile for t in tiles)
-        return {"launches": len(durs), "avg_us": 1e3 * tot_ms / len(durs),
-                "sum_ms_per_step": tot_ms / args.steps,
-                "gbs": tot_bytes / (tot_ms * 1e-3) / 1e9}
-
-    enc = kernel_stats("enc", "enc_tiles", ENC_BYTES_PER_TILE)
-    dec = kernel_stats("dec", "dec_tiles", DEC_BYTES_PER_TILE)
-    dominant = enc if enc["sum_ms_per_step"] >= dec["sum_ms_per_step"] else dec
-    dom_name = "encode" if dominant is enc else "decode"
-
-    tiles_per_launch = sum(ev["enc_tiles"]) / len(ev["enc_tiles"])
+    seq = run(step_sequential, ("encode", "decode"))
+    ref_y = [layers[i][2][m].clone() for i in (0, L - 1) for m in (0, 6)]
+    pipe = run(step_pipelined, ("codec",)) if args.pipeline else None
+    same = None
+    if pipe is not None:
+        got = [layers[i][2][m] for i in (0, L - 1) for m in (0, 6)]
+        same = all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip(ref_y, got))
+    del ref_y
+    head = pipe if pipe is not None else seq
+    ms_per_step = head["ms_per_step"]
+    kern = dict(seq["kernels"])
+    if pipe is not None:
+        kern.update(pipe["kernels"])
+    dom_name = max(head["kernels"], key=lambda k: head["kernels"][k]["sum_ms_per_step"])
+    dominant = kern[dom_name]
     traffic = alu = None
-    if kernel_sources_sha256() == MEASURED_TRAFFIC["sources_sha256"]:
-        t = MEASURED_TRAFFIC[dom_name]
-        traffic = round((t["read"] + t["write"]) * tiles_per_launch)
-        # the same launches against the VALU issue roof
-        ops = MEASURED_TRAFFIC["valu_lane_ops_per_weight"][dom_name] * 256 * tiles_per_launch
+    meas = MEASURED_TRAFFIC.get(dom_name)
+    if isinstance(meas, dict) and kernel_sources_sha256() == MEASURED_TRAFFIC["sources_sha256"]:
+        # measured HBM bytes per launch: per-tile figures times the tiles of an average launch
+        traffic = round(meas["bytes_per_byte"] * dominant["bytes_per_launch"])
+        ops = meas["valu_lane_ops_per_byte"] * dominant["bytes_per_launch"]
         achieved = ops / (dominant["avg_us"] * 1e-6)
         alu = {"achieved": round(achieved / 1e12, 2), "peak": round(VALU_PEAK_LANE_OPS / 1e12, 2),
                "unit": "T VALU lane-ops/s (issued)", "frac": round(achieved / VALU_PEAK_LANE_OPS, 4),
-               "lane_ops_per_weight": MEASURED_TRAFFIC["valu_lane_ops_per_weight"][dom_name]}
+               "lane_ops_per_weight": meas["valu_lane_ops_per_weight"]}
 
     # cache-cold form of the same work: every layer's encode, then every
     # layer's decode, so no decode finds its indices in the 256 MB Infinity
@@ -693,6 +726,11 @@ def main():
             "small_fp32_1024x1024": par["small"],
             "llama_layer0_all_seven": par["layer"]}
 
+    # the dominant kernel's limiter: HBM when its traffic fraction is the
+    # larger one, else VALU issue (when measured)
+    bound = "hbm"
+    if alu is not None and alu["frac"] > dominant["gbs"] / HBM_PEAK_GBS:
+        bound = "alu"
     value = 2.0 * n_weights / (ms_per_step * 1e-3) / 1e9
     alg = (ENC_BYTES_PER_TILE + DEC_BYTES_PER_TILE) * n_tiles / (ms_per_step * 1e-3) / 1e9
     out = {
@@ -713,28 +751,33 @@ def main():
                         "then decode (E8, tile 256, auto scale)",
             "layers": args.layers, "weights": n_weights, "bps": args.bps, "tile": 256,
             "lattice": "E8", "input": "bf16", "output": "bf16",
+            "schedule": ("pipelined: launch l encodes layer l and decodes layer l - 1 "
+                         "(hq_encode_decode_batch, %d launches)" % (L + 1)) if pipe is not None
+            else "sequential: per layer one encode launch, then one decode launch",
         },
         "pct_hbm_peak_algorithmic": round(100.0 * alg / HBM_PEAK_GBS, 3),
         "algorithmic_gbs": round(alg, 2),
         "roofline": {
             "kernel": dom_name,
-            "bound": "hbm",
+            "bound": bound,
             "achieved": round(dominant["gbs"], 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dominant["gbs"] / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "traffic_unit": "HBM bytes per launch (null: kernel changed since the counters)",
-            "algorithmic_bytes_per_launch": round(
-                (ENC_BYTES_PER_TILE if dom_name == "encode" else DEC_BYTES_PER_TILE) * tiles_per_launch),
+            "traffic_unit": "measured HBM bytes per launch (null: kernel changed since the counters)",
+            "algorithmic_bytes_per_launch": round(dominant["bytes_per_launch"]),
             "alu_issue": alu,
         },
-        "kernels": {
-            "encode": {k: round(v, 3) for k, v in enc.items()},
-            "decode": {k: round(v, 3) for k, v in dec.items()},
-        },
-        "host_wall_ms_per_step": round(wall * 1e3 / args.steps, 3),
-        "gpu_event_ms_per_step": round(gpu_ms / args.steps, 3),
+        "kernels": {k: {q: round(v, 3) for q, v in st.items()} for k, st in kern.items()},
+        "host_wall_ms_per_step": round(head["host_wall_ms_per_step"], 3),
+        "gpu_event_ms_per_step": round(head["gpu_event_ms_per_step"], 3),
+        "sequential": {"ms_per_step": round(seq["ms_per_step"], 4),
+                       "value": round(2.0 * n_weights / (seq["ms_per_step"] * 1e-3) / 1e9, 3),
+                       "pct_hbm_peak_algorithmic": round(
+                           100.0 * (ENC_BYTES_PER_TILE + DEC_BYTES_PER_TILE) * n_tiles /
+                           (seq["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)},
+        "pipelined_outputs_identical": same,
         "cache_cold": cold,
         "device_copy_gbs": round(copy_gbs, 1),
         "cpu_baseline": cpu,

@@ -523,6 +523,31 @@ hq_status hq_decode_batch(const hq_params* p, int32_t y_dtype, int32_t count,
                           const hq_decode_item* items, uint32_t* status,
                           hipStream_t stream);
 
+/*
+ * Encode one batch and decode another, independent batch in one call: the
+ * results are exactly those of hq_encode_batch(enc_p, x_dtype, enc_count,
+ * enc_items) followed by hq_decode_batch(dec_p, y_dtype, dec_count,
+ * dec_items), with the same validation of every item.  For a model streamed
+ * through the codec ([arXiv abstract] "HyperQuant: A Rate-Distortion-Optimal
+ * Quantization Pipeline ..." ideas (i)-(iii), [ICLR abstract] "HyperQuant: A
+ * Near-Entropy-Optimal Lattice Quantization Pipeline ...": rotation, lattice
+ * point, strip and Rice rate, then the algebraic decode) the caller encodes
+ * layer l + 1 while it decodes layer l.  On the E8 / tile 256 / bf16-input
+ * path, with at most 8 non-empty matrices on each side, one launch runs both
+ * (each wave alternates an encode group and a decode group, so the encoder's
+ * arithmetic overlaps the decoder's memory traffic); otherwise the two
+ * batches are enqueued one after the other.  The batches must be
+ * independent: HQ_EINVAL when an encode output (idx, scale, coset, rice_k,
+ * tile_bits) overlaps a decode input or output, or a decode output overlaps
+ * an encode input.  `status` (optional device word) collects both sides'
+ * status bits.
+ */
+hq_status hq_encode_decode_batch(const hq_params* enc_p, int32_t x_dtype,
+                                 int32_t enc_count, const hq_encode_item* enc_items,
+                                 const hq_params* dec_p, int32_t y_dtype,
+                                 int32_t dec_count, const hq_decode_item* dec_items,
+                                 uint32_t* status, hipStream_t stream);
+
 /* Coset words per tile: E8 ceil(n/256), A2 ceil(n/64), D4 and Z 0;
  * -1 on an invalid p. */
 int32_t hq_coset_words(const hq_params* p);

@@ -257,8 +257,13 @@ hq_status hq_decode_tiles(const hq_params* p, const int8_t* idx, const uint32_t*
   return launched(launch_decode(a, stream));
 }
 
-hq_status hq_encode_batch(const hq_params* p, int32_t x_dtype, int32_t count,
-                          const hq_encode_item* items, uint32_t* status, hipStream_t stream) {
+extern "C++" {
+namespace {
+
+// Validation of an encode batch: every item as hq_encode_tiles would check
+// it, and device residence of every pointer.
+hq_status check_encode_batch(const hq_params* p, int32_t x_dtype, int32_t count,
+                             const hq_encode_item* items, uint32_t* status) {
   hq_status st = check_params(p);
   if (st != HQ_OK) return st;
   if (p->flags & (HQ_WANT_COORDS | HQ_DITHER)) return HQ_EUNSUPPORTED;
@@ -277,6 +282,10 @@ hq_status hq_encode_batch(const hq_params* p, int32_t x_dtype, int32_t count,
       return HQ_EINVAL;
   }
   if (status != nullptr && !on_device(status)) return HQ_EINVAL;
+  return HQ_OK;
+}
+
+EncodeLaunch encode_launch(const hq_params* p, int32_t x_dtype, uint32_t* status) {
   EncodeLaunch a;
   memset(&a, 0, sizeof(a));
   a.in_bf16 = x_dtype == HQ_BF16;
@@ -288,26 +297,42 @@ hq_status hq_encode_batch(const hq_params* p, int32_t x_dtype, int32_t count,
   a.c = scale_constant(p);
   a.sqrt_n = sqrt((double)p->tile);
   set_rate_control(p, a);
-  if (!a.rate_control && e8_fast_encode_ok(a)) {
-    EncBatch b;
-    memset(&b, 0, sizeof(b));
-    for (int32_t i = 0; i <= count; ++i) {
-      const bool flush = (i == count) || b.n == kMaxItems;
-      if (flush && b.n > 0) {
-        for (int k = b.n; k < kMaxItems; ++k) b.it[k] = b.it[0];
-        if (launch_encode_e8_fast(a, b, stream) != hipSuccess) return HQ_EDEVICE;
-        memset(&b, 0, sizeof(b));
-      }
-      if (i == count) break;
-      const hq_encode_item& it = items[i];
-      const int64_t nt = it.rows * it.cols / p->tile;
-      if (nt == 0) continue;
-      b.it[b.n] = EncItem{it.x, it.idx, it.scale, it.coset, it.rice_k, it.tile_bits, nt,
-                          b.n_groups};
-      b.n_groups += (nt + 15) / 16;
-      b.n += 1;
+  return a;
+}
+
+bool encode_batch_fast(const EncodeLaunch& a) { return !a.rate_control && e8_fast_encode_ok(a); }
+
+// Launch groups of the fast encoder: up to kMaxItems non-empty matrices each.
+// Calls emit(batch) per group; returns false when a launch fails.
+template <typename F>
+bool encode_groups(const hq_params* p, int32_t count, const hq_encode_item* items, F emit) {
+  EncBatch b;
+  memset(&b, 0, sizeof(b));
+  for (int32_t i = 0; i <= count; ++i) {
+    const bool flush = (i == count) || b.n == kMaxItems;
+    if (flush && b.n > 0) {
+      for (int k = b.n; k < kMaxItems; ++k) b.it[k] = b.it[0];
+      if (!emit(b)) return false;
+      memset(&b, 0, sizeof(b));
     }
-    return HQ_OK;
+    if (i == count) break;
+    const hq_encode_item& it = items[i];
+    const int64_t nt = it.rows * it.cols / p->tile;
+    if (nt == 0) continue;
+    b.it[b.n] = EncItem{it.x, it.idx, it.scale, it.coset, it.rice_k, it.tile_bits, nt, b.n_groups};
+    b.n_groups += (nt + 15) / 16;
+    b.n += 1;
+  }
+  return true;
+}
+
+hq_status enqueue_encode_batch(const hq_params* p, EncodeLaunch a, int32_t count,
+                               const hq_encode_item* items, hipStream_t stream) {
+  if (encode_batch_fast(a)) {
+    const bool ok = encode_groups(p, count, items, [&](const EncBatch& b) {
+      return launch_encode_e8_fast(a, b, stream) == hipSuccess;
+    });
+    return ok ? HQ_OK : HQ_EDEVICE;
   }
   for (int32_t i = 0; i < count; ++i) {
     const hq_encode_item& it = items[i];
@@ -326,8 +351,8 @@ hq_status hq_encode_batch(const hq_params* p, int32_t x_dtype, int32_t count,
   return HQ_OK;
 }
 
-hq_status hq_decode_batch(const hq_params* p, int32_t y_dtype, int32_t count,
-                          const hq_decode_item* items, uint32_t* status, hipStream_t stream) {
+hq_status check_decode_batch(const hq_params* p, int32_t y_dtype, int32_t count,
+                             const hq_decode_item* items, uint32_t* status) {
   hq_status st = check_params(p);
   if (st != HQ_OK) return st;
   if (p->flags & (HQ_WANT_COORDS | HQ_DITHER)) return HQ_EUNSUPPORTED;
@@ -350,6 +375,10 @@ hq_status hq_decode_batch(const hq_params* p, int32_t y_dtype, int32_t count,
       return HQ_EINVAL;
   }
   if (status != nullptr && !on_device(status)) return HQ_EINVAL;
+  return HQ_OK;
+}
+
+DecodeLaunch decode_launch(const hq_params* p, int32_t y_dtype, uint32_t* status) {
   DecodeLaunch a;
   memset(&a, 0, sizeof(a));
   a.lattice = p->lattice;
@@ -358,25 +387,38 @@ hq_status hq_decode_batch(const hq_params* p, int32_t y_dtype, int32_t count,
   a.status = status;
   make_signs(p->rht_seed, p->tile, a.signs);
   a.inv_sqrt_n = 1.0 / sqrt((double)p->tile);
-  if (e8_fast_decode_ok(a)) {
-    DecBatch b;
-    memset(&b, 0, sizeof(b));
-    for (int32_t i = 0; i <= count; ++i) {
-      const bool flush = (i == count) || b.n == kMaxItems;
-      if (flush && b.n > 0) {
-        for (int k = b.n; k < kMaxItems; ++k) b.it[k] = b.it[0];
-        if (launch_decode_e8_fast(a, b, stream) != hipSuccess) return HQ_EDEVICE;
-        memset(&b, 0, sizeof(b));
-      }
-      if (i == count) break;
-      const hq_decode_item& it = items[i];
-      const int64_t nt = it.rows * it.cols / p->tile;
-      if (nt == 0) continue;
-      b.it[b.n] = DecItem{it.idx, it.coset, it.scale, it.y, nt, b.n_groups};
-      b.n_groups += (nt + 15) / 16;
-      b.n += 1;
+  return a;
+}
+
+template <typename F>
+bool decode_groups(const hq_params* p, int32_t count, const hq_decode_item* items, F emit) {
+  DecBatch b;
+  memset(&b, 0, sizeof(b));
+  for (int32_t i = 0; i <= count; ++i) {
+    const bool flush = (i == count) || b.n == kMaxItems;
+    if (flush && b.n > 0) {
+      for (int k = b.n; k < kMaxItems; ++k) b.it[k] = b.it[0];
+      if (!emit(b)) return false;
+      memset(&b, 0, sizeof(b));
     }
-    return HQ_OK;
+    if (i == count) break;
+    const hq_decode_item& it = items[i];
+    const int64_t nt = it.rows * it.cols / p->tile;
+    if (nt == 0) continue;
+    b.it[b.n] = DecItem{it.idx, it.coset, it.scale, it.y, nt, b.n_groups};
+    b.n_groups += (nt + 15) / 16;
+    b.n += 1;
+  }
+  return true;
+}
+
+hq_status enqueue_decode_batch(const hq_params* p, DecodeLaunch a, int32_t count,
+                               const hq_decode_item* items, hipStream_t stream) {
+  if (e8_fast_decode_ok(a)) {
+    const bool ok = decode_groups(p, count, items, [&](const DecBatch& b) {
+      return launch_decode_e8_fast(a, b, stream) == hipSuccess;
+    });
+    return ok ? HQ_OK : HQ_EDEVICE;
   }
   for (int32_t i = 0; i < count; ++i) {
     const hq_decode_item& it = items[i];
@@ -390,6 +432,98 @@ hq_status hq_decode_batch(const hq_params* p, int32_t y_dtype, int32_t count,
     if (launch_decode(a, stream) != hipSuccess) return HQ_EDEVICE;
   }
   return HQ_OK;
+}
+
+// Non-empty items of a batch (launch groups hold up to kMaxItems).
+template <typename I>
+int32_t live_items(const hq_params* p, int32_t count, const I* items) {
+  int32_t n = 0;
+  for (int32_t i = 0; i < count; ++i)
+    if (items[i].rows * items[i].cols / p->tile > 0) ++n;
+  return n;
+}
+
+struct Span {
+  uintptr_t lo, hi;   // [lo, hi)
+};
+
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+Span span(const void* ptr, int64_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(ptr);
+  return Span{lo, lo + (uintptr_t)(bytes > 0 ? bytes : 0)};
+}
+
+}  // namespace
+}  // extern "C++"
+
+hq_status hq_encode_batch(const hq_params* p, int32_t x_dtype, int32_t count,
+                          const hq_encode_item* items, uint32_t* status, hipStream_t stream) {
+  hq_status st = check_encode_batch(p, x_dtype, count, items, status);
+  if (st != HQ_OK) return st;
+  return enqueue_encode_batch(p, encode_launch(p, x_dtype, status), count, items, stream);
+}
+
+hq_status hq_decode_batch(const hq_params* p, int32_t y_dtype, int32_t count,
+                          const hq_decode_item* items, uint32_t* status, hipStream_t stream) {
+  hq_status st = check_decode_batch(p, y_dtype, count, items, status);
+  if (st != HQ_OK) return st;
+  return enqueue_decode_batch(p, decode_launch(p, y_dtype, status), count, items, stream);
+}
+
+hq_status hq_encode_decode_batch(const hq_params* enc_p, int32_t x_dtype, int32_t enc_count,
+                                 const hq_encode_item* enc_items, const hq_params* dec_p,
+                                 int32_t y_dtype, int32_t dec_count,
+                                 const hq_decode_item* dec_items, uint32_t* status,
+                                 hipStream_t stream) {
+  hq_status st = check_encode_batch(enc_p, x_dtype, enc_count, enc_items, status);
+  if (st != HQ_OK) return st;
+  st = check_decode_batch(dec_p, y_dtype, dec_count, dec_items, status);
+  if (st != HQ_OK) return st;
+  // the two batches must be independent: no buffer the encode writes may be
+  // read or written by the decode, and the decode's outputs may not overlap
+  // the encode's inputs
+  for (int32_t i = 0; i < enc_count; ++i) {
+    const hq_encode_item& e = enc_items[i];
+    const int64_t ne = e.rows * e.cols;
+    if (ne == 0) continue;
+    const int64_t te = ne / enc_p->tile;
+    const int xb = x_dtype == HQ_BF16 ? 2 : 4;
+    const Span ew[5] = {span(e.idx, ne), span(e.scale, 4 * te),
+                        span(e.coset, 4 * te * coset_words(enc_p)), span(e.rice_k, te),
+                        span(e.tile_bits, 4 * te)};
+    const Span ex = span(e.x, ne * xb);
+    for (int32_t j = 0; j < dec_count; ++j) {
+      const hq_decode_item& d = dec_items[j];
+      const int64_t nd = d.rows * d.cols;
+      if (nd == 0) continue;
+      const int64_t td = nd / dec_p->tile;
+      const Span dr[4] = {span(d.idx, nd), span(d.scale, 4 * td),
+                          span(d.coset, 4 * td * coset_words(dec_p)),
+                          span(d.y, nd * (y_dtype == HQ_BF16 ? 2 : 4))};
+      for (const Span& w : ew)
+        for (const Span& r : dr)
+          if (overlap(w, r)) return HQ_EINVAL;
+      if (overlap(ex, dr[3])) return HQ_EINVAL;
+    }
+  }
+  const EncodeLaunch a = encode_launch(enc_p, x_dtype, status);
+  const DecodeLaunch ad = decode_launch(dec_p, y_dtype, status);
+  const int32_t le = live_items(enc_p, enc_count, enc_items);
+  const int32_t ld = live_items(dec_p, dec_count, dec_items);
+  if (encode_batch_fast(a) && e8_fast_decode_ok(ad) && le <= kMaxItems && ld <= kMaxItems &&
+      le + ld > 0) {
+    EncBatch b;
+    DecBatch bd;
+    memset(&b, 0, sizeof(b));
+    memset(&bd, 0, sizeof(bd));
+    encode_groups(enc_p, enc_count, enc_items, [&](const EncBatch& g) { b = g; return true; });
+    decode_groups(dec_p, dec_count, dec_items, [&](const DecBatch& g) { bd = g; return true; });
+    return launch_codec_e8_fast(a, b, ad, bd, stream) == hipSuccess ? HQ_OK : HQ_EDEVICE;
+  }
+  st = enqueue_encode_batch(enc_p, a, enc_count, enc_items, stream);
+  if (st != HQ_OK) return st;
+  return enqueue_decode_batch(dec_p, ad, dec_count, dec_items, stream);
 }
 
 size_t hq_rate_workspace_bytes(int64_t n_tiles) {

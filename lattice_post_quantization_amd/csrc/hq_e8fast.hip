@@ -598,6 +598,95 @@ __global__ __launch_bounds__(kBlock) void decode_e8_fast(DecodeLaunch a, DecBatc
   }
 }
 
+// ---------------------------------------------------------------- pipeline
+// One launch that encodes one batch and decodes another, independent one
+// (a model streamed through the codec: layer l + 1 is encoded while layer l
+// is decoded).  Encode is bound by VALU issue and leaves most of the HBM
+// bandwidth unused; decode is bound by HBM and leaves most of the VALU
+// unused.  Here every wave alternates: slot s = w, w + W, ... is encode
+// group s (if the encode batch has it) followed by decode group s (if the
+// decode batch has it), so the two waves of a SIMD are usually in different
+// phases and both resources stay busy.  The next item streams into the
+// wave's LDS buffer while the current one is computed, as in the separate
+// kernels; the group bodies are the same functions, so the results are bit
+// for bit those of the two separate launches.  The caller guarantees that
+// no decode input is written by the encode.
+struct PipeItem {
+  int64_t slot;
+  int kind;   // 0: encode group `slot`, 1: decode group `slot`, -1: none
+};
+
+__device__ inline PipeItem pipe_first(int64_t s, int64_t ne, int64_t nd) {
+  if (s < ne) return {s, 0};
+  if (s < nd) return {s, 1};
+  return {s, -1};
+}
+
+__device__ inline PipeItem pipe_next(PipeItem c, int64_t stride, int64_t ne, int64_t nd) {
+  if (c.kind == 0 && c.slot < nd) return {c.slot, 1};
+  return pipe_first(c.slot + stride, ne, nd);
+}
+
+// The encode stage (528 uint4 per wave) also holds a decode group (288).
+template <bool OUT_BF16>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void codec_e8_fast(
+    EncodeLaunch a, EncBatch b, DecodeLaunch ad, DecBatch bd) {
+  __shared__ uint32_t sign_enc[128];
+  __shared__ uint32_t sign_dec[128];
+  __shared__ uint4 stage[kBlock / 64][kEncStage];
+  __shared__ uint4 ostage[kBlock / 64][256];
+  fill_sign_table(sign_enc, a.signs);
+  fill_sign_table(sign_dec, ad.signs);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int t = lane & 15, row = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint4* buf = stage[wave];
+  const bool scale_in = !a.auto_scale;
+  const int64_t ne = b.n_groups, nd = bd.n_groups;
+  const int64_t stride = (int64_t)gridDim.x * (kBlock / 64);
+  PipeItem cur = pipe_first((int64_t)blockIdx.x * (kBlock / 64) + wave, ne, nd);
+  if (cur.kind < 0) return;
+  // one register set for either kind: an encode group's 32 dwords of bf16
+  // pairs, or a decode group's 16 dwords of indices
+  uint32_t w[32];
+  float sc = 0.0f;
+  DecIn din;
+  int ic = cur.kind == 0 ? item_of(b, cur.slot) : item_of(bd, cur.slot);
+  if (cur.kind == 0) {
+    enc_prefetch(b.it[ic], cur.slot - b.it[ic].group0, buf, lane, scale_in);
+    enc_take(buf, t, row, w, sc);
+  } else {
+    dec_prefetch(bd.it[ic], cur.slot - bd.it[ic].group0, buf, lane);
+    dec_take(buf, t, row, w, din);
+  }
+  for (;;) {
+    // every lane's reads of the buffer complete before it is refilled
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    PipeItem nx = pipe_next(cur, stride, ne, nd);
+    const bool more = nx.kind >= 0;   // uniform across the wave
+    if (!more) nx = cur;              // the last item prefetches itself again
+    const int ip = nx.kind == 0 ? item_of(b, nx.slot) : item_of(bd, nx.slot);
+    if (nx.kind == 0)
+      enc_prefetch(b.it[ip], nx.slot - b.it[ip].group0, buf, lane, scale_in);
+    else
+      dec_prefetch(bd.it[ip], nx.slot - bd.it[ip].group0, buf, lane);
+    if (cur.kind == 0)
+      enc_group(a, b.it[ic], sign_enc, cur.slot - b.it[ic].group0, t, row, w, sc, ostage[wave]);
+    else
+      dec_group<OUT_BF16>(bd.it[ic], sign_dec, cur.slot - bd.it[ic].group0, t, row, w, din,
+                          ostage[wave]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (nx.kind == 0)
+      enc_take(buf, t, row, w, sc);
+    else
+      dec_take(buf, t, row, w, din);
+    if (!more) break;
+    cur = nx;
+    ic = ip;
+  }
+}
+
 }  // namespace
 
 bool e8_fast_encode_ok(const EncodeLaunch& a) {
@@ -615,6 +704,20 @@ hipError_t launch_encode_e8_fast(const EncodeLaunch& a, const EncBatch& b, hipSt
   static int occ = 0;
   const int64_t blocks = persistent_grid(b.n_groups * 16, resident_blocks(encode_e8_fast, occ));
   hipLaunchKernelGGL(encode_e8_fast, dim3((unsigned)blocks), dim3(kBlock), 0, s, a, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_codec_e8_fast(const EncodeLaunch& a, const EncBatch& b, const DecodeLaunch& ad,
+                               const DecBatch& bd, hipStream_t s) {
+  static int occ_bf16 = 0, occ_f32 = 0;
+  const int64_t slots = b.n_groups > bd.n_groups ? b.n_groups : bd.n_groups;
+  if (ad.out_bf16) {
+    const int64_t blocks = persistent_grid(slots * 16, resident_blocks(codec_e8_fast<true>, occ_bf16));
+    hipLaunchKernelGGL(codec_e8_fast<true>, dim3((unsigned)blocks), dim3(kBlock), 0, s, a, b, ad, bd);
+  } else {
+    const int64_t blocks = persistent_grid(slots * 16, resident_blocks(codec_e8_fast<false>, occ_f32));
+    hipLaunchKernelGGL(codec_e8_fast<false>, dim3((unsigned)blocks), dim3(kBlock), 0, s, a, b, ad, bd);
+  }
   return hipGetLastError();
 }
 

@@ -261,6 +261,11 @@ bool e8_fast_decode_ok(const DecodeLaunch& a);
 // a: shared parameters (its per-matrix fields are ignored); b: the matrices
 hipError_t launch_encode_e8_fast(const EncodeLaunch& a, const EncBatch& b, hipStream_t s);
 hipError_t launch_decode_e8_fast(const DecodeLaunch& a, const DecBatch& b, hipStream_t s);
+// One launch that runs an encode batch and an independent decode batch
+// together (every wave alternates a group of each); same results as the two
+// launches above.
+hipError_t launch_codec_e8_fast(const EncodeLaunch& a, const EncBatch& b, const DecodeLaunch& ad,
+                               const DecBatch& bd, hipStream_t s);
 
 // Fast path for tile 128, every lattice (E8 with or without the KV dither):
 // bf16 input (encode), either output type (decode); groups of 32 tiles.

@@ -112,6 +112,7 @@ _SIGNATURES = {
     "hq_kv_encode": (_I32, [_PP, _P, _I32, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "hq_encode_batch": (_I32, [_PP, _I32, _I32, _P, _P, _P]),
     "hq_decode_batch": (_I32, [_PP, _I32, _I32, _P, _P, _P]),
+    "hq_encode_decode_batch": (_I32, [_PP, _I32, _I32, _P, _PP, _I32, _I32, _P, _P, _P]),
     "hq_coset_words": (_I32, [_PP]),
     "hq_rate_workspace_bytes": (_SZ, [_I64]),
     "hq_status_string": (ctypes.c_char_p, [_I32]),
@@ -715,12 +716,9 @@ def _addr(t):
     return None if t is None else t.data_ptr()
 
 
-def hq_encode_batch(xs, lattice="E8", tile=256, bps=4.0, rht_seed=0, outs=None, status=None):
-    """hq_encode_tiles on every matrix of `xs` (same dtype, device and
-    parameters) in one call; auto scales.  `outs` may give, per matrix, the
-    preallocated dict hq_encode_tiles would return.  Returns a list of dicts."""
-    if not xs:
-        return []
+def _encode_items(xs, lattice, tile, outs):
+    """Output dicts (allocated unless given in `outs`) and the C item array
+    of a batched encode."""
     dev = xs[0].device
     dt = xs[0].dtype
     res = []
@@ -749,19 +747,10 @@ def hq_encode_batch(xs, lattice="E8", tile=256, bps=4.0, rht_seed=0, outs=None, 
     for i, (x, r) in enumerate(zip(xs, res)):
         items[i] = EncodeItem(_addr(x), x.shape[0], x.shape[1], _addr(r["scale"]), _addr(r["idx"]),
                               _addr(r["coset"]), _addr(r["rice_k"]), _addr(r["tile_bits"]))
-    p = make_params(lattice, tile, bps, rht_seed, HQ_SCALE_AUTO)
-    code = lib().hq_encode_batch(ctypes.byref(p), _dtype_code(dt), len(xs), ctypes.byref(items),
-                                 _ptr(status), _stream(dev))
-    _check(code, "hq_encode_batch")
-    return res
+    return res, items
 
 
-def hq_decode_batch(encs, lattice="E8", tile=256, rht_seed=0, out_dtype=torch.bfloat16,
-                    outs=None, status=None):
-    """hq_decode_tiles on every encoded matrix of `encs` (dicts with idx,
-    coset, scale) in one call.  Returns the list of decoded tensors."""
-    if not encs:
-        return []
+def _decode_items(encs, out_dtype, outs):
     dev = encs[0]["idx"].device
     ys = []
     items = (DecodeItem * len(encs))()
@@ -774,8 +763,60 @@ def hq_decode_batch(encs, lattice="E8", tile=256, rht_seed=0, out_dtype=torch.bf
         ys.append(y)
         items[i] = DecodeItem(_addr(e["idx"]), _addr(e["coset"]), _addr(e["scale"]), rows, cols,
                               _addr(y))
+    return ys, items
+
+
+def hq_encode_batch(xs, lattice="E8", tile=256, bps=4.0, rht_seed=0, outs=None, status=None):
+    """hq_encode_tiles on every matrix of `xs` (same dtype, device and
+    parameters) in one call; auto scales.  `outs` may give, per matrix, the
+    preallocated dict hq_encode_tiles would return.  Returns a list of dicts."""
+    if not xs:
+        return []
+    res, items = _encode_items(xs, lattice, tile, outs)
+    p = make_params(lattice, tile, bps, rht_seed, HQ_SCALE_AUTO)
+    code = lib().hq_encode_batch(ctypes.byref(p), _dtype_code(xs[0].dtype), len(xs),
+                                 ctypes.byref(items), _ptr(status), _stream(xs[0].device))
+    _check(code, "hq_encode_batch")
+    return res
+
+
+def hq_decode_batch(encs, lattice="E8", tile=256, rht_seed=0, out_dtype=torch.bfloat16,
+                    outs=None, status=None):
+    """hq_decode_tiles on every encoded matrix of `encs` (dicts with idx,
+    coset, scale) in one call.  Returns the list of decoded tensors."""
+    if not encs:
+        return []
+    ys, items = _decode_items(encs, out_dtype, outs)
     p = make_params(lattice, tile, 4.0, rht_seed, 0)
     code = lib().hq_decode_batch(ctypes.byref(p), _dtype_code(out_dtype), len(encs),
-                                 ctypes.byref(items), _ptr(status), _stream(dev))
+                                 ctypes.byref(items), _ptr(status), _stream(encs[0]["idx"].device))
     _check(code, "hq_decode_batch")
     return ys
+
+
+def hq_encode_decode_batch(xs, encs, lattice="E8", tile=256, bps=4.0, enc_seed=0, dec_seed=0,
+                           out_dtype=torch.bfloat16, enc_outs=None, dec_outs=None, status=None):
+    """hq_encode_batch(xs, ..., rht_seed=enc_seed) and hq_decode_batch(encs,
+    ..., rht_seed=dec_seed) in one call (one launch on the E8 / tile 256
+    path).  `encs` must not share memory with the encode's outputs.
+    Returns (encode result dicts, decoded tensors)."""
+    if not xs and not encs:
+        return [], []
+    dev = (xs[0] if xs else encs[0]["idx"]).device
+    if xs:
+        res, eitems = _encode_items(xs, lattice, tile, enc_outs)
+        x_dt = _dtype_code(xs[0].dtype)
+    else:
+        res, eitems, x_dt = [], None, 1
+    if encs:
+        ys, ditems = _decode_items(encs, out_dtype, dec_outs)
+    else:
+        ys, ditems = [], None
+    pe = make_params(lattice, tile, bps, enc_seed, HQ_SCALE_AUTO)
+    pd = make_params(lattice, tile, 4.0, dec_seed, 0)
+    code = lib().hq_encode_decode_batch(
+        ctypes.byref(pe), x_dt, len(xs), ctypes.byref(eitems) if eitems is not None else None,
+        ctypes.byref(pd), _dtype_code(out_dtype), len(encs),
+        ctypes.byref(ditems) if ditems is not None else None, _ptr(status), _stream(dev))
+    _check(code, "hq_encode_decode_batch")
+    return res, ys

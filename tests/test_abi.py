@@ -211,6 +211,33 @@ def test_batch_validation():
     assert lib.hq_decode_batch(ctypes.byref(p), 5, 1, ctypes.byref(d), None, None) == hq.HQ_EINVAL
 
 
+def test_encode_decode_batch_validation():
+    """The fused call validates both batches as the separate calls do, before
+    anything is enqueued."""
+    lib = hq.lib()
+    p = hq.make_params("E8", 256, 4.0, 0, hq.HQ_SCALE_AUTO)
+    pd = hq.make_params("E8", 256, 4.0, 1, 0)
+    f = lib.hq_encode_decode_batch
+    assert f(ctypes.byref(p), 1, 0, None, ctypes.byref(pd), 1, 0, None, None, None) == hq.HQ_OK
+    assert f(ctypes.byref(p), 1, 1, None, ctypes.byref(pd), 1, 0, None, None, None) == hq.HQ_EINVAL
+    assert f(ctypes.byref(p), 1, 0, None, ctypes.byref(pd), 1, 1, None, None, None) == hq.HQ_EINVAL
+    assert f(None, 1, 0, None, ctypes.byref(pd), 1, 0, None, None, None) == hq.HQ_EINVAL
+    assert f(ctypes.byref(p), 1, 0, None, None, 1, 0, None, None, None) == hq.HQ_EINVAL
+    e = (hq.EncodeItem * 1)()
+    e[0] = hq.EncodeItem(4096, 4, 100, 4096, 4096, 4096, 4096, 4096)      # cols % tile
+    assert f(ctypes.byref(p), 1, 1, ctypes.byref(e), ctypes.byref(pd), 1, 0, None, None,
+             None) == hq.HQ_EINVAL
+    d = (hq.DecodeItem * 1)()
+    d[0] = hq.DecodeItem(4096, 4096, 4096, 4, 256, 4096)                  # host pointers
+    assert f(ctypes.byref(p), 1, 0, None, ctypes.byref(pd), 1, 1, ctypes.byref(d), None,
+             None) == hq.HQ_EINVAL
+    assert f(ctypes.byref(p), 1, 0, None, ctypes.byref(pd), 7, 1, ctypes.byref(d), None,
+             None) == hq.HQ_EINVAL                                          # output dtype
+    pc = hq.make_params("E8", 256, 4.0, 1, hq.HQ_DITHER)
+    assert f(ctypes.byref(p), 1, 0, None, ctypes.byref(pc), 1, 0, None, None,
+             None) == hq.HQ_EUNSUPPORTED
+
+
 def test_unpack_validation_codes():
     lib = hq.lib()
     p = hq.make_params("E8", 256, 4.0)

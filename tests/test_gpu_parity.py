@@ -485,6 +485,78 @@ def test_batched_calls_match_single_calls_and_oracle():
             assert np.array_equal(T.bf16_host_bits(y).reshape(-1, 256), codec.bf16_bits(yo)), i
 
 
+def _pipeline_batches(rng, shapes, seed_bits):
+    mats, hosts = [], []
+    for r, c in shapes:
+        w = rng.standard_normal((r, c)) * 0.02
+        w[:, ::97] *= 400.0                       # a few outlier columns
+        bits = workloads.f32_to_bf16_bits(w.astype(np.float32))
+        hosts.append(workloads.bf16_bits_to_f64(bits))
+        mats.append(T.bf16_device(bits, (r, c)))
+    return mats, hosts
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_encode_decode_batch_matches_separate_calls(out_dtype):
+    """hq_encode_decode_batch (one launch: encode of one batch interleaved
+    with the decode of another) gives exactly the bytes of hq_encode_batch
+    followed by hq_decode_batch: batches of different sizes and group counts
+    (ragged tiles, an empty matrix), one side empty, and more than eight
+    matrices (the two-launch fallback); the encode side also against the
+    oracle on sampled tiles."""
+    rng = np.random.default_rng(47)
+    enc_shapes = [(7, 256), (33, 768), (0, 512), (5, 1024), (64, 256), (3, 2048)]
+    dec_shapes = [(40, 256), (1, 512), (16, 1024), (9, 768)]
+    emats, ehosts = _pipeline_batches(rng, enc_shapes, 0)
+    dmats, _ = _pipeline_batches(rng, dec_shapes, 1)
+    dsrc = hq.hq_encode_batch(dmats, "E8", 256, 4.0, 11)     # the layer to decode
+    torch.cuda.synchronize()
+    cases = [("both", emats, dsrc), ("encode only", emats, []), ("decode only", [], dsrc),
+             ("nine + four (fallback)", emats + emats[:3], dsrc)]
+    for label, em, ds in cases:
+        say("case: pipeline %s, %s out" % (label, out_dtype))
+        res, ys = hq.hq_encode_decode_batch(em, ds, "E8", 256, 4.0, enc_seed=5, dec_seed=11,
+                                            out_dtype=out_dtype)
+        ref_e = hq.hq_encode_batch(em, "E8", 256, 4.0, 5) if em else []
+        ref_y = hq.hq_decode_batch(ds, "E8", 256, 11, out_dtype) if ds else []
+        torch.cuda.synchronize()
+        assert len(res) == len(ref_e) and len(ys) == len(ref_y)
+        for i, (a, b) in enumerate(zip(res, ref_e)):
+            for k in ("scale", "idx", "coset", "rice_k", "tile_bits"):
+                assert torch.equal(a[k], b[k]), (label, i, k)
+        for i, (a, b) in enumerate(zip(ys, ref_y)):
+            assert torch.equal(a.view(torch.int16 if out_dtype == torch.bfloat16 else torch.int32),
+                               b.view(torch.int16 if out_dtype == torch.bfloat16 else torch.int32)), \
+                (label, i)
+    # the encode side against the oracle (tiles every 7th)
+    for i, h in enumerate(ehosts):
+        if h.size == 0:
+            continue
+        tiles = np.arange(0, h.size // 256, 7)
+        ora = codec.encode(codec.tiles(h, 256)[tiles], "E8", 256, 4.0, rht_seed=5)
+        assert np.array_equal(T.host(res[i]["scale"]).reshape(-1)[tiles].astype(np.float64),
+                              ora["scale"])
+        T.compare_indices(T.host(res[i]["idx"]).reshape(-1, 256)[tiles],
+                          T.u32(res[i]["coset"]).reshape(-1, 1)[tiles], ora, "E8", 256,
+                          "pipeline encode item %d" % i)
+
+
+def test_encode_decode_batch_refuses_overlap():
+    """A decode batch that reads what the encode batch writes (or writes over
+    its input) is refused before anything is enqueued."""
+    rng = np.random.default_rng(3)
+    mats, _ = _pipeline_batches(rng, [(8, 512)], 0)
+    enc = hq.hq_encode_batch(mats, "E8", 256, 4.0, 1)
+    torch.cuda.synchronize()
+    with pytest.raises(hq.HQError) as e:          # decode reads the encode's own outputs
+        hq.hq_encode_decode_batch(mats, enc, "E8", 256, 4.0, enc_seed=1, dec_seed=1, enc_outs=enc)
+    assert e.value.code == hq.HQ_EINVAL
+    other = hq.hq_encode_batch(mats, "E8", 256, 4.0, 2)
+    with pytest.raises(hq.HQError) as e:          # decode writes over the encode's input
+        hq.hq_encode_decode_batch(mats, other, "E8", 256, 4.0, dec_outs=[mats[0]])
+    assert e.value.code == hq.HQ_EINVAL
+
+
 def test_stack_sampled_parity_as_benchmarked():
     """The 32-layer Llama-3.1-8B-shaped stack exactly as bench.py runs it:
     each layer drawn on the GPU, one batched encode of its seven matrices and
