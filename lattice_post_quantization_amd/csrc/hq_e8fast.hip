@@ -616,6 +616,14 @@ struct PipeItem {
   int kind;   // 0: encode group `slot`, 1: decode group `slot`, -1: none
 };
 
+// This lane's index in the wave, recomputed where it is called (an asm the
+// compiler may neither hoist nor merge).
+__device__ inline int opaque_lane_id() {
+  int v;
+  __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
+  return v;
+}
+
 __device__ inline PipeItem pipe_first(int64_t s, int64_t ne, int64_t nd) {
   if (s < ne) return {s, 0};
   if (s < nd) return {s, 1};
@@ -667,20 +675,30 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     const bool more = nx.kind >= 0;   // uniform across the wave
     if (!more) nx = cur;              // the last item prefetches itself again
     const int ip = nx.kind == 0 ? item_of(b, nx.slot) : item_of(bd, nx.slot);
-    if (nx.kind == 0)
-      enc_prefetch(b.it[ip], nx.slot - b.it[ip].group0, buf, lane, scale_in);
-    else
-      dec_prefetch(bd.it[ip], nx.slot - bd.it[ip].group0, buf, lane);
-    if (cur.kind == 0)
-      enc_group(a, b.it[ic], sign_enc, cur.slot - b.it[ic].group0, t, row, w, sc, ostage[wave]);
-    else
-      dec_group<OUT_BF16>(bd.it[ic], sign_dec, cur.slot - bd.it[ic].group0, t, row, w, din,
-                          ostage[wave]);
+    // Each kind's per-lane LDS addresses are derived inside its own branch
+    // from a lane id the compiler cannot hoist: kept live across the loop,
+    // both kinds' addresses would not fit the register file next to an
+    // encode group's working set.
+    {
+      const int ln = opaque_lane_id(), tt = ln & 15, rr = ln >> 4;
+      if (nx.kind == 0)
+        enc_prefetch(b.it[ip], nx.slot - b.it[ip].group0, buf, ln, scale_in);
+      else
+        dec_prefetch(bd.it[ip], nx.slot - bd.it[ip].group0, buf, ln);
+      if (cur.kind == 0)
+        enc_group(a, b.it[ic], sign_enc, cur.slot - b.it[ic].group0, tt, rr, w, sc, ostage[wave]);
+      else
+        dec_group<OUT_BF16>(bd.it[ic], sign_dec, cur.slot - bd.it[ic].group0, tt, rr, w, din,
+                            ostage[wave]);
+    }
     __builtin_amdgcn_sched_barrier(0);
-    if (nx.kind == 0)
-      enc_take(buf, t, row, w, sc);
-    else
-      dec_take(buf, t, row, w, din);
+    {
+      const int ln = opaque_lane_id(), tt = ln & 15, rr = ln >> 4;
+      if (nx.kind == 0)
+        enc_take(buf, tt, rr, w, sc);
+      else
+        dec_take(buf, tt, rr, w, din);
+    }
     if (!more) break;
     cur = nx;
     ic = ip;

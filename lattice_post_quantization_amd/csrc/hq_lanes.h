@@ -185,12 +185,31 @@ __device__ inline uint32_t third_bytes(int32_t a, int32_t b, int32_t c, int32_t 
 
 __device__ inline uint32_t pack4(const int32_t* s);
 
+// 8 (U mod 2^24): v_mul_u32_u24 reads only the low 24 bits of U
+__device__ inline uint32_t frac8(int32_t u) {
+  uint32_t r;
+  __asm__("v_mul_u32_u24 %0, 8, %1" : "=v"(r) : "v"(u));
+  return r;
+}
+
+__device__ inline uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  __asm__("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+__device__ inline uint32_t pk_add_u16(uint32_t a, uint32_t b) {
+  uint32_t r;
+  __asm__("v_pk_add_u16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 __device__ inline uint32_t e8_block_fast(const int32_t* U, uint32_t& p0, uint32_t& p1, int& cs) {
   // keys (B << 3) + i and (B << 3) + 7 - i: |8F - 2^26| plus the index
   uint32_t k1[8], k2[8];
 #define HQ_E8_KEYS(i)                                             \
   {                                                               \
-    const uint32_t F8 = ((uint32_t)U[i] << 3) & 0x07FFFFFFu;      \
+    const uint32_t F8 = frac8(U[i]);                              \
     k1[i] = sad26<i>(F8);                                         \
     k2[i] = sad26<7 - i>(F8);                                     \
   }
@@ -201,39 +220,51 @@ __device__ inline uint32_t e8_block_fast(const int32_t* U, uint32_t& p0, uint32_
                               k1[6] < k1[7] ? k1[6] : k1[7]);
   const uint32_t kmax = max3u(max3u(k2[0], k2[1], k2[2]), max3u(k2[3], k2[4], k2[5]),
                               k2[6] > k2[7] ? k2[6] : k2[7]);
-  const int32_t bmin = (int32_t)(kmin >> 3), bmax = (int32_t)(kmax >> 3);
-  const uint32_t tie = (uint32_t)(bmin == 0) | (uint32_t)(bmax == kHalf);
-  const uint32_t sumB =
-      (((k1[0] + k1[1] + k1[2]) + (k1[3] + k1[4] + k1[5]) + (k1[6] + k1[7])) - 28u) >> 3;
-  const uint32_t X = ((uint32_t)U[0] ^ (uint32_t)U[1] ^ (uint32_t)U[2]) ^
-                     ((uint32_t)U[3] ^ (uint32_t)U[4] ^ (uint32_t)U[5]) ^
-                     ((uint32_t)U[6] ^ (uint32_t)U[7]);
+  // min B = 0 or max B = 2^23: a coordinate on a half-integer or an integer
+  const uint32_t tie = (uint32_t)(kmin < 8u) | (uint32_t)(kmax >= (1u << 26));
+  // 8 sum B = sum k1 - 28
+  const uint32_t sumk = (k1[0] + k1[1] + k1[2]) + (k1[3] + k1[4] + k1[5]) + (k1[6] + k1[7]);
+  const uint32_t X = xor3(xor3((uint32_t)U[0], (uint32_t)U[1], (uint32_t)U[2]),
+                          xor3((uint32_t)U[3], (uint32_t)U[4], (uint32_t)U[5]),
+                          (uint32_t)U[6] ^ (uint32_t)U[7]);
   const int odd_b = (int)((X >> 24) & 1u);                 // sum I odd
   const int odd_a = (int)(((X >> 23) ^ (X >> 24)) & 1u);   // sum (I + up) odd
-  const int32_t D = (1 << 25) - (int32_t)sumB + (odd_a ? 2 * bmin : 0) -
-                    (odd_b ? (1 << 24) - 2 * bmax : 0);
-  const int c = D > 0;
+  // 8 D = 2^28 - 8 sum B + [odd a] 16 min B - [odd b] (2^27 - 16 max B)
+  const int32_t D8 = (int32_t)((1u << 28) + 28u - sumk) +
+                     (odd_a ? 2 * (int32_t)(kmin & ~7u) : 0) -
+                     (odd_b ? (1 << 27) - 2 * (int32_t)(kmax & ~7u) : 0);
+  const int c = D8 > 0;
   const uint32_t jf = c ? 7u - (kmax & 7u) : (kmin & 7u);
   const int odd = c ? odd_b : odd_a;
-  // byte k of Gq: byte 2 of U_{4q+k}, whose bit 7 is [F > 2^23]
-  const uint32_t G0 = third_bytes(U[0], U[1], U[2], U[3]);
-  const uint32_t G1 = third_bytes(U[4], U[5], U[6], U[7]);
+  // Q: the high halves (U >> 16) of two coordinates; byte 1 of a half is I,
+  // bit 7 of byte 0 is [F > 2^23]
+  const uint32_t Q0 = __builtin_amdgcn_perm((uint32_t)U[1], (uint32_t)U[0], 0x07060302u);
+  const uint32_t Q1 = __builtin_amdgcn_perm((uint32_t)U[3], (uint32_t)U[2], 0x07060302u);
+  const uint32_t Q2 = __builtin_amdgcn_perm((uint32_t)U[5], (uint32_t)U[4], 0x07060302u);
+  const uint32_t Q3 = __builtin_amdgcn_perm((uint32_t)U[7], (uint32_t)U[6], 0x07060302u);
+  // byte k of Gq: byte 2 of U_{4q+k}
+  const uint32_t G0 = __builtin_amdgcn_perm(Q1, Q0, 0x06040200u);
+  const uint32_t G1 = __builtin_amdgcn_perm(Q3, Q2, 0x06040200u);
   const uint32_t upj = (uint32_t)((((uint64_t)G1 << 32) | G0) >> (8 * jf + 7)) & 1u;
+  // Adding 0x80 to a half carries [F > 2^23] into its high byte (the
+  // integer coset's rounding); 0x8000 adds the bias of 128 to the byte, so
+  // the parity flip below cannot carry into a neighbour (a tile without the
+  // overflow flag has |u_i| < 126, so every biased byte stays in 1..255).
+  const uint32_t cadd = c ? 0x80008000u : 0x80808080u;
+  const uint32_t b0 = __builtin_amdgcn_perm(pk_add_u16(Q1, cadd), pk_add_u16(Q0, cadd), 0x07050301u);
+  const uint32_t b1 = __builtin_amdgcn_perm(pk_add_u16(Q3, cadd), pk_add_u16(Q2, cadd), 0x07050301u);
   // The flipped coordinate moves away from u's rounding in coset a (-1 when
   // rounded up) and towards u in coset b (+1 when u lies above the
   // half-integer).
-  const bool neg = ((uint32_t)c ^ upj) != 0u;
-  const uint32_t jo = odd ? jf : 8u;                       // 8: no flip
-  const int32_t s7 = (int32_t)((uint32_t)U[7] + (c ? 0u : (uint32_t)kHalf) +
-                               (jo == 7u ? (neg ? 0xFF000000u : 0x01000000u) : 0u)) >> 1;
-  const uint32_t d = (neg ? 0xFFFFFFFFu : 1u) << (8u * (jo & 3u));
-  const uint32_t up0 = c ? 0u : (G0 >> 7) & 0x01010101u;
-  const uint32_t up1 = c ? 0u : (G1 >> 7) & 0x00010101u;
+  // +-1 at byte jf of the 8 biased bytes: one 64-bit shift-and-add of the
+  // sign-extended step (no biased byte is 0, so a -1 borrows nothing)
+  const int32_t step = odd ? (((uint32_t)c ^ upj) ? -1 : 1) : 0;
+  const uint64_t bb = ((((uint64_t)b1 << 32) | b0) + ((uint64_t)(int64_t)step << (8u * jf)));
   constexpr uint32_t kBias = 0x80808080u;
-  p0 = ((top_bytes((uint32_t)U[0], (uint32_t)U[1], (uint32_t)U[2], (uint32_t)U[3]) ^ kBias) + up0 +
-        (jo < 4u ? d : 0u)) ^ kBias;
-  p1 = ((top_bytes((uint32_t)U[4], (uint32_t)U[5], (uint32_t)U[6], (uint32_t)s7) ^ kBias) + up1 +
-        (jo - 4u < 3u ? d : 0u)) ^ kBias;
+  p0 = (uint32_t)bb ^ kBias;
+  const uint32_t q1 = (uint32_t)(bb >> 32) ^ kBias;
+  // the last coordinate is stored halved: floor(z7 / 2)
+  p1 = __builtin_amdgcn_perm((uint32_t)((int32_t)q1 >> 25), q1, 0x04020100u);
   cs = c;
   return tie;
 }
