@@ -214,6 +214,27 @@ hq_status hq_rate(const hq_params* p, const int8_t* idx, const uint32_t* coset,
                   hipStream_t stream);
 
 /*
+ * hq_rate_noalloc - hq_rate for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The arguments, checks and results (bit for bit) are those of
+ * hq_rate with a workspace, and it likewise packs when stream_words is
+ * given; there is no workspace argument.  The per-block sums live in a
+ * static device array of the library, 96 KiB per GPU, allocated with the
+ * code object and held until the process ends; it holds the workspace of
+ * any tile count (a size that would need more is refused with HQ_ERANGE).
+ * The first call on a device looks up that array's address there.  The
+ * call allocates nothing.  Every call on one GPU shares the array (each
+ * call writes every word it reads, so nothing needs clearing): calls that
+ * overlap on one GPU, on different streams or from different host threads,
+ * race and leave unspecified results.
+ */
+hq_status hq_rate_noalloc(const hq_params* p, const int8_t* idx, const uint32_t* coset,
+                          int64_t n_tiles, uint8_t* rice_k, uint32_t* tile_bits,
+                          uint64_t* total_bits, uint32_t* stream_words,
+                          uint64_t capacity_words, uint64_t* tile_word_offset,
+                          uint32_t* status, hipStream_t stream);
+
+/*
  * hq_rate_batch - hq_rate for `count` matrices that share p (a layer's
  * projections), enqueued as at most four kernel launches per group of up to
  * eight matrices instead of up to four per matrix.  Same passages,

@@ -11,6 +11,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "hq.h"
 #include "hq_device.h"
 #include "hq_internal.h"
@@ -20,9 +22,40 @@
 namespace hq {
 }
 
+// Scratch of hq_rate_noalloc: the per-block word and bit sums and per-wave
+// word sums that hq_rate keeps in its caller's workspace.  The rate pass
+// runs at most 8192 waves (2048 blocks), so 6 * 2048 uint64 hold the
+// workspace of any tile count.  Each GPU the library runs on holds its own
+// copy until the process ends.
+constexpr size_t kRateScratchWords = 6 * 2048;
+static __device__ __align__(256) uint64_t scratch[kRateScratchWords];
+
 namespace {
 
 using namespace hq;
+
+// Device address of `scratch` on the current device, looked up once per
+// device (the host-side name is not a device address).
+constexpr int kScratchDevices = 64;
+void* g_scratch_ptr[kScratchDevices];
+hipError_t g_scratch_err[kScratchDevices];
+std::once_flag g_scratch_once[kScratchDevices];
+
+hq_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) {
+    (void)hipGetLastError();
+    return HQ_EDEVICE;
+  }
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* q = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = q;
+  });
+  if (g_scratch_err[dev] != hipSuccess || g_scratch_ptr[dev] == nullptr) return HQ_EDEVICE;
+  *out = g_scratch_ptr[dev];
+  return HQ_OK;
+}
 
 constexpr uint32_t kKnownFlags =
     HQ_SCALE_AUTO | HQ_DITHER | HQ_WANT_COORDS | HQ_RATE_CONTROL | HQ_RATE_GIVEN;
@@ -532,11 +565,15 @@ size_t hq_rate_workspace_bytes(int64_t n_tiles) {
   return 6 * (size_t)rate_workspace_blocks(n_tiles) * sizeof(uint64_t);
 }
 
-hq_status hq_rate(const hq_params* p, const int8_t* idx, const uint32_t* coset, int64_t n_tiles,
-                  uint8_t* rice_k, uint32_t* tile_bits, uint64_t* total_bits,
-                  uint32_t* stream_words, uint64_t capacity_words, uint64_t* tile_word_offset,
-                  void* workspace, size_t workspace_bytes, uint32_t* status,
-                  hipStream_t stream) {
+// hq_rate's checks and launch; scratch_ws: the workspace is the library's
+// static scratch (known device memory, not checked by pointer attributes);
+// check_only: return after the checks, launching nothing.
+static hq_status rate_impl(const hq_params* p, const int8_t* idx, const uint32_t* coset,
+                           int64_t n_tiles, uint8_t* rice_k, uint32_t* tile_bits,
+                           uint64_t* total_bits, uint32_t* stream_words, uint64_t capacity_words,
+                           uint64_t* tile_word_offset, void* workspace, size_t workspace_bytes,
+                           uint32_t* status, hipStream_t stream, bool scratch_ws,
+                           bool check_only = false) {
   hq_status st = check_params(p);
   if (st != HQ_OK) return st;
   if (n_tiles < 0) return HQ_EINVAL;
@@ -560,9 +597,11 @@ hq_status hq_rate(const hq_params* p, const int8_t* idx, const uint32_t* coset, 
       !on_device(total_bits) || (status != nullptr && !on_device(status)))
     return HQ_EINVAL;
   if (pack && (!on_device(stream_words) || !on_device(tile_word_offset) ||
-               !on_device(workspace) || (coset_words(p) > 0 && !on_device(coset))))
+               (!scratch_ws && !on_device(workspace)) ||
+               (coset_words(p) > 0 && !on_device(coset))))
     return HQ_EINVAL;
-  if (!pack && workspace != nullptr && !on_device(workspace)) return HQ_EINVAL;
+  if (!pack && workspace != nullptr && !scratch_ws && !on_device(workspace)) return HQ_EINVAL;
+  if (check_only) return HQ_OK;
   RateLaunch a;
   memset(&a, 0, sizeof(a));
   a.idx = idx;
@@ -587,6 +626,36 @@ hq_status hq_rate(const hq_params* p, const int8_t* idx, const uint32_t* coset, 
   a.status = status;
   a.given = given ? 1 : 0;
   return launched(launch_rate(a, stream));
+}
+
+hq_status hq_rate(const hq_params* p, const int8_t* idx, const uint32_t* coset, int64_t n_tiles,
+                  uint8_t* rice_k, uint32_t* tile_bits, uint64_t* total_bits,
+                  uint32_t* stream_words, uint64_t capacity_words, uint64_t* tile_word_offset,
+                  void* workspace, size_t workspace_bytes, uint32_t* status,
+                  hipStream_t stream) {
+  return rate_impl(p, idx, coset, n_tiles, rice_k, tile_bits, total_bits, stream_words,
+                   capacity_words, tile_word_offset, workspace, workspace_bytes, status, stream,
+                   false);
+}
+
+hq_status hq_rate_noalloc(const hq_params* p, const int8_t* idx, const uint32_t* coset,
+                          int64_t n_tiles, uint8_t* rice_k, uint32_t* tile_bits,
+                          uint64_t* total_bits, uint32_t* stream_words, uint64_t capacity_words,
+                          uint64_t* tile_word_offset, uint32_t* status, hipStream_t stream) {
+  // the workspace of any tile count fits the scratch; a size past it (none
+  // exists while the rate pass is capped at 8192 waves) is refused
+  if (n_tiles > 0 && hq_rate_workspace_bytes(n_tiles) > sizeof(scratch)) return HQ_ERANGE;
+  // hq_rate's argument checks first, with the scratch standing in for the
+  // workspace (a placeholder address: nothing is read in the checks)
+  hq_status st = rate_impl(p, idx, coset, n_tiles, rice_k, tile_bits, total_bits, stream_words,
+                           capacity_words, tile_word_offset, reinterpret_cast<void*>(256),
+                           sizeof(scratch), status, stream, true, true);
+  if (st != HQ_OK || n_tiles == 0) return st;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != HQ_OK) return st;
+  return rate_impl(p, idx, coset, n_tiles, rice_k, tile_bits, total_bits, stream_words,
+                   capacity_words, tile_word_offset, ws, sizeof(scratch), status, stream, true);
 }
 
 // Validation of one hq_rate_batch item with n_tiles > 0 (a workspace is

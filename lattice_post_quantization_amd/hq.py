@@ -113,6 +113,7 @@ _SIGNATURES = {
     "hq_encode_batch": (_I32, [_PP, _I32, _I32, _P, _P, _P]),
     "hq_decode_batch": (_I32, [_PP, _I32, _I32, _P, _P, _P]),
     "hq_encode_decode_batch": (_I32, [_PP, _I32, _I32, _P, _PP, _I32, _I32, _P, _P, _P]),
+    "hq_rate_noalloc": (_I32, [_PP, _P, _P, _I64, _P, _P, _P, _P, _U64, _P, _P, _P]),
     "hq_coset_words": (_I32, [_PP]),
     "hq_rate_workspace_bytes": (_SZ, [_I64]),
     "hq_status_string": (ctypes.c_char_p, [_I32]),
@@ -275,8 +276,11 @@ def hq_decode_tiles(idx, coset, scale, lattice="E8", tile=256, rht_seed=0,
 
 
 def hq_rate(idx, coset, lattice="E8", tile=256, pack=False, capacity_words=None,
-            status=None, out=None, given=None):
+            status=None, out=None, given=None, noalloc=False):
     """Rice parameters and bit lengths per tile; optionally the packed stream.
+
+    noalloc: call hq_rate_noalloc (the library's static scratch instead of a
+    workspace; the outputs are still allocated here unless given in `out`).
 
     given: the encoder's result for these indices (a dict with rice_k and
     tile_bits, as hq_encode_tiles returns): HQ_RATE_GIVEN, the rate pass
@@ -309,15 +313,24 @@ def hq_rate(idx, coset, lattice="E8", tile=256, pack=False, capacity_words=None,
         offs = o.get("tile_word_offset")
         if offs is None:
             offs = torch.empty(n_tiles + 1, dtype=torch.int64, device=dev)
-    ws = o.get("workspace")
-    if ws is None:
-        ws = torch.empty(max(rate_workspace_bytes(n_tiles), 8), dtype=torch.uint8, device=dev)
     p = make_params(lattice, tile, 4.0, flags=HQ_RATE_GIVEN if given is not None else 0)
-    code = lib().hq_rate(ctypes.byref(p), _ptr(idx), _ptr(coset), n_tiles, _ptr(rice_k),
-                         _ptr(tile_bits), _ptr(total), _ptr(stream),
-                         int(capacity_words or 0), _ptr(offs), _ptr(ws),
-                         0 if ws is None else ws.numel(), _ptr(status), _stream(dev))
-    _check(code, "hq_rate")
+    if noalloc:
+        # the library's static scratch stands in for the workspace
+        ws = None
+        code = lib().hq_rate_noalloc(ctypes.byref(p), _ptr(idx), _ptr(coset), n_tiles,
+                                     _ptr(rice_k), _ptr(tile_bits), _ptr(total), _ptr(stream),
+                                     int(capacity_words or 0), _ptr(offs), _ptr(status),
+                                     _stream(dev))
+        _check(code, "hq_rate_noalloc")
+    else:
+        ws = o.get("workspace")
+        if ws is None:
+            ws = torch.empty(max(rate_workspace_bytes(n_tiles), 8), dtype=torch.uint8, device=dev)
+        code = lib().hq_rate(ctypes.byref(p), _ptr(idx), _ptr(coset), n_tiles, _ptr(rice_k),
+                             _ptr(tile_bits), _ptr(total), _ptr(stream),
+                             int(capacity_words or 0), _ptr(offs), _ptr(ws),
+                             0 if ws is None else ws.numel(), _ptr(status), _stream(dev))
+        _check(code, "hq_rate")
     res = {"rice_k": rice_k, "tile_bits": tile_bits, "total_bits": total, "workspace": ws}
     if pack:
         res["stream"] = stream
