@@ -26,15 +26,17 @@ namespace {
 
 using namespace fastlib;
 
-// Coalesced store of a group's output.  Lane (t, r) holds CPL 16-byte chunks:
-// chunk k lies at byte r * 16 CPL + 16 k of tile t, and tiles are
-// 64 CPL bytes apart.  The wave writes them, 4 KB (256 chunks) per pass,
+// Coalesced store of a group's output.  Lane (t, r) holds CPL 16-byte chunks
+// of tile t; chunk k belongs at 16-byte slot slot(k) of the tile (tiles are
+// 64 CPL bytes apart).  The wave writes them, 4 KB (256 chunks) per pass,
 // into a 4 KB LDS buffer and reads them back so that each store instruction
 // covers 1 KB of contiguous output.  Chunk c of a pass sits at LDS slot
-// c ^ ((c >> 4) & 15), which keeps both sides free of bank conflicts.
-template <int CPL>
+// c ^ ((c >> 4) & 15), which spreads a pass's writes and reads over the banks.
+// slot() lets a lane keep the element order its transform left: the chunks
+// land at their natural positions without lane exchanges.
+template <int CPL, typename Slot>
 __device__ inline void store_group(__amdgpu_buffer_rsrc_t rs, const uint4* chunk, uint4* ost,
-                                   int t, int row) {
+                                   int t, int row, Slot slot) {
   constexpr int kTilesPerPass = 256 / (4 * CPL);
   const int lane = row * 16 + t;
 #pragma unroll
@@ -43,7 +45,7 @@ __device__ inline void store_group(__amdgpu_buffer_rsrc_t rs, const uint4* chunk
     if (t / kTilesPerPass == h) {
 #pragma unroll
       for (int k = 0; k < CPL; ++k) {
-        const int c = (t % kTilesPerPass) * 4 * CPL + row * CPL + k;
+        const int c = (t % kTilesPerPass) * 4 * CPL + slot(k);
         ost[c ^ ((c >> 4) & 15)] = chunk[k];
       }
     }
@@ -263,19 +265,18 @@ __device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const
     if (L < best) { best = L; bk = kc[j]; }
   }
 
-  // ---- restore natural element order (undo the two swaps) and store
-#pragma unroll
-  for (int q = 0; q < 16; ++q)
-    if (!(q & 4)) swap32(packed[q], packed[q + 4]);
-#pragma unroll
-  for (int q = 0; q < 8; ++q) swap16(packed[q], packed[q + 8]);
+  // ---- store.  Chunk k (blocks 2k, 2k + 1: element bits 0-3 inside) has
+  // element bit 7 = k bit 0, bit 6 = k bit 1, bit 5 = row bit 0 and bit 4 =
+  // row bit 1, i.e. 16-byte slot 8 k0 + 4 k1 + 2 r0 + r1 of the tile.
   const uint32_t live = live_tiles(it.n_tiles, group);
   const int64_t tile0 = group * 16;
   uint4 ch[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k)
     ch[k] = make_uint4(packed[4 * k], packed[4 * k + 1], packed[4 * k + 2], packed[4 * k + 3]);
-  store_group<4>(out_rsrc(it.idx + tile0 * 256, live * 256u), ch, ost, t, row);
+  const int rs0 = 2 * (row & 1) + (row >> 1);
+  store_group<4>(out_rsrc(it.idx + tile0 * 256, live * 256u), ch, ost, t, row,
+                 [rs0](int k) { return 8 * (k & 1) + 4 * (k >> 1) + rs0; });
   if (a.auto_scale)
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(delta), out_rsrc(it.scale + tile0, live * 4u),
                                           (int)row0_offset(t, row, 4), 0, 0);
@@ -385,12 +386,14 @@ __device__ inline void dec_group(const DecItem& it, const uint32_t* sign_tab, in
   const uint32_t cw = in.cw >> (8 * row);        // this lane's 8 blocks
   const float dsc = in.scale * 0.03125f;         // Delta / 32, exact
 
-  // bound for the int16 path: sum |P| <= 4 sum|stored| + 320 (|z7| <= 2|t7| + 1)
-  uint32_t sabs = 0;
+  // bound for the int16 path: sum |P| <= 4 sum|stored| + 320 (|z7| <= 2|t7| + 1).
+  // For a signed byte z held as the unsigned byte u, |u - 128| = 128 - |z|,
+  // so the tile's sum of |u - 128| over its 256 bytes is 32768 - sum |z|.
+  uint32_t sad = 0;
 #pragma unroll
-  for (int q = 0; q < 16; ++q) sabs = __builtin_amdgcn_sad_u8(d[q] ^ 0x80808080u, 0x80808080u, sabs);
-  sabs = tile_sum_u32(sabs);
-  const bool small = sabs <= 8111u;
+  for (int q = 0; q < 16; ++q) sad = __builtin_amdgcn_sad_u8(d[q], 0x80808080u, sad);
+  sad = tile_sum_u32(sad);
+  const bool small = sad >= 32768u - 8111u;
 
   // ---- unstrip into P = 2z + c as int16 pairs: P2[m] = (P_2m, P_2m+1)
   uint32_t P2[32];
@@ -408,13 +411,13 @@ __device__ inline void dec_group(const DecItem& it, const uint32_t* sign_tab, in
     const uint32_t p23 = __builtin_amdgcn_perm(d0, e0, 0x0B070906u);
     const uint32_t p45 = __builtin_amdgcn_perm(d1, e1, 0x0A050804u);
     const uint32_t p67 = __builtin_amdgcn_perm(d1, e1, 0x0B070906u);
-    const s16x2 cc = (s16x2){(short)c, (short)c};
+    const uint32_t cc = c * 0x00010001u;
     // z7 = 2 t7 + par: P7 = 4 t7 + 2 par + c
-    const s16x2 c7 = (s16x2){(short)c, (short)(c + 2 * par)};
-    P2[4 * b] = as_u32(as_s16x2(p01) * (s16x2){2, 2} + cc);
-    P2[4 * b + 1] = as_u32(as_s16x2(p23) * (s16x2){2, 2} + cc);
-    P2[4 * b + 2] = as_u32(as_s16x2(p45) * (s16x2){2, 2} + cc);
-    P2[4 * b + 3] = as_u32(as_s16x2(p67) * (s16x2){2, 4} + c7);
+    const uint32_t c7 = cc + (par << 17);
+    P2[4 * b] = pk_mad_u16(p01, 0x00020002u, cc);
+    P2[4 * b + 1] = pk_mad_u16(p23, 0x00020002u, cc);
+    P2[4 * b + 2] = pk_mad_u16(p45, 0x00020002u, cc);
+    P2[4 * b + 3] = pk_mad_u16(p67, 0x00040002u, c7);
   }
 
   float y[64];
@@ -519,22 +522,25 @@ __device__ inline void dec_group(const DecItem& it, const uint32_t* sign_tab, in
       for (int m = 0; m < 32; ++m)
         o[m] = f64_to_bf16((double)y[2 * m] * dd) | (f64_to_bf16((double)y[2 * m + 1] * dd) << 16);
     }
-    // undo the swaps: dword bit 3 <-> row bit 1, dword bit 4 <-> row bit 0
-#pragma unroll
-    for (int m = 0; m < 32; ++m)
-      if (!(m & 8)) swap32(o[m], o[m + 8]);
-#pragma unroll
-    for (int m = 0; m < 16; ++m) swap16(o[m], o[m + 16]);
+    // Chunk k = o[4k .. 4k + 3] holds element bits 0-2 inside; bit 3 = k
+    // bit 0, bit 7 = k bit 1, bit 6 = k bit 2, bit 5 = row bit 0, bit 4 = row
+    // bit 1: 16-byte slot k0 + 16 k1 + 8 k2 + 4 r0 + 2 r1 of the tile.  The
+    // sign masks of those elements come from the sign table of the natural
+    // layout (row r, chunk j covers elements 64 r + 8 j ...).
     uint4 ch[8];
+    const int rs0 = 4 * (row & 1) + 2 * (row >> 1);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const uint4 sm = st[k];
+      const int sl = (k & 1) + 16 * ((k >> 1) & 1) + 8 * (k >> 2) + rs0;
+      const uint4 sm = reinterpret_cast<const uint4*>(sign_tab)[sl];
       ch[k] = make_uint4(o[4 * k] ^ sm.x, o[4 * k + 1] ^ sm.y, o[4 * k + 2] ^ sm.z,
                          o[4 * k + 3] ^ sm.w);
     }
     store_group<8>(out_rsrc(static_cast<uint16_t*>(it.y) + group * 16 * 256,
                             live_tiles(it.n_tiles, group) * 512u),
-                   ch, ost, t, row);
+                   ch, ost, t, row, [rs0](int k) {
+                     return (k & 1) + 16 * ((k >> 1) & 1) + 8 * (k >> 2) + rs0;
+                   });
   } else {
     uint32_t o[64];
 #pragma unroll
@@ -553,7 +559,7 @@ __device__ inline void dec_group(const DecItem& it, const uint32_t* sign_tab, in
     }
     store_group<16>(out_rsrc(static_cast<float*>(it.y) + group * 16 * 256,
                              live_tiles(it.n_tiles, group) * 1024u),
-                    ch, ost, t, row);
+                    ch, ost, t, row, [row](int k) { return row * 16 + k; });
   }
 }
 

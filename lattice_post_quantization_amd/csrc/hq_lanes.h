@@ -198,6 +198,13 @@ __device__ inline uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
   return r;
 }
 
+// per 16-bit half: a * b + c (mod 2^16)
+__device__ inline uint32_t pk_mad_u16(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  __asm__("v_pk_mad_u16 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ inline uint32_t pk_add_u16(uint32_t a, uint32_t b) {
   uint32_t r;
   __asm__("v_pk_add_u16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
