@@ -27,44 +27,46 @@ namespace {
 using namespace fastlib;
 
 // Coalesced store of a group's output.  Lane (t, r) holds CPL 16-byte chunks
-// of tile t; chunk k belongs at 16-byte slot slot(k) of the tile (tiles are
-// 64 CPL bytes apart).  The wave writes them, 4 KB (256 chunks) per pass,
-// into a 4 KB LDS buffer and reads them back so that each store instruction
-// covers 1 KB of contiguous output.  Chunk c of a pass sits at LDS slot
-// c ^ ((c >> 4) & 15), which spreads a pass's writes and reads over the banks.
-// slot() lets a lane keep the element order its transform left: the chunks
-// land at their natural positions without lane exchanges.
-template <int CPL, typename Slot>
+// of tile t, chunk k at 16-byte slot s_k of its tile (tiles are 64 CPL bytes
+// apart), and the wave writes them, 4 KB (256 chunks) per pass, into a 4 KB
+// LDS buffer, then reads them back so that each store instruction covers
+// 1 KB of contiguous output.  Chunk c of a pass sits at LDS slot
+// c ^ ((c >> 4) & 15), which spreads a pass's accesses over the banks.  With
+// the slots used here that position is a per-lane base XOR a constant of the
+// chunk (write: wb ^ wx(k), passed in), and the read of pass slot 64 i + lane
+// is at rb ^ 68 i with rb = 16 r + (t ^ r): one XOR per access.  The slots
+// let a lane keep the element order its transform left: chunks land at their
+// natural positions without lane exchanges.
+template <int CPL, typename WX>
 __device__ inline void store_group(__amdgpu_buffer_rsrc_t rs, const uint4* chunk, uint4* ost,
-                                   int t, int row, Slot slot) {
+                                   int t, int lane, uint32_t wb, WX wx, uint32_t rb) {
   constexpr int kTilesPerPass = 256 / (4 * CPL);
-  const int lane = row * 16 + t;
 #pragma unroll
   for (int h = 0; h < 16 / kTilesPerPass; ++h) {
     wave_lds_sync();
     if (t / kTilesPerPass == h) {
 #pragma unroll
-      for (int k = 0; k < CPL; ++k) {
-        const int c = (t % kTilesPerPass) * 4 * CPL + slot(k);
-        ost[c ^ ((c >> 4) & 15)] = chunk[k];
-      }
+      for (int k = 0; k < CPL; ++k) ost[wb ^ wx(k)] = chunk[k];
     }
     wave_lds_sync();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int c = 64 * i + lane;
-      const uint4 q = ost[c ^ ((c >> 4) & 15)];
-      store16(rs, (uint32_t)(h * 4096 + 16 * c), q.x, q.y, q.z, q.w);
+      const uint4 q = ost[rb ^ (68u * i)];
+      store16(rs, (uint32_t)(h * 4096 + 1024 * i + 16 * lane), q.x, q.y, q.z, q.w);
     }
   }
+}
+
+__device__ inline uint32_t store_read_base(int t, int row) {
+  return (uint32_t)(16 * row + (t ^ row));
 }
 
 // Staged loads.  A wave's 16 tiles are 8 KB of contiguous bf16, read with
 // eight direct-to-LDS loads of 1 KB each (instruction k covers tiles 2k and
 // 2k + 1, so every load is fully coalesced).  Lane l = 16 r + b of
-// instruction k fetches row r, 16-byte chunk j = (b/2 - k) mod 8 of tile
+// instruction k fetches row r, 16-byte chunk j = (b/2) ^ k of tile
 // 2k + (b & 1) and the hardware stores it at LDS slot 64 k + l; lane (t, r)
-// later finds chunk j of its tile at slot 64 (t/2) + 16 r + ((t + 2j) mod 16),
+// later finds chunk j of its tile at slot e0 ^ 2j, e0 = 64 (t/2) + 16 r + t,
 // so each 16-lane row reads 16 different bank groups.
 // With a caller-supplied scale, a ninth load brings the group's 16 scales to
 // the 256 bytes after the bf16 data (lanes 16-63 repeat them).  Lane offsets
@@ -80,7 +82,7 @@ __device__ inline void enc_prefetch(const EncItem& it, int64_t group, uint4* buf
                            live * 512u);
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const int j = ((b >> 1) - k) & 7;
+    const int j = (b >> 1) ^ k;
     const int off = (2 * k + (b & 1)) * 512 + r * 128 + j * 16;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr(buf + 64 * k), 16, off, 0, 0, 0);
   }
@@ -90,9 +92,10 @@ __device__ inline void enc_prefetch(const EncItem& it, int64_t group, uint4* buf
 }
 
 __device__ inline void enc_take(const uint4* buf, int t, int r, uint32_t* w, float& scale) {
+  const uint32_t e0 = (uint32_t)(64 * (t >> 1) + 16 * r + t);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const uint4 q = buf[64 * (t >> 1) + 16 * r + ((t + 2 * j) & 15)];
+    const uint4 q = buf[e0 ^ (2u * j)];
     w[4 * j] = q.x; w[4 * j + 1] = q.y; w[4 * j + 2] = q.z; w[4 * j + 3] = q.w;
   }
   scale = reinterpret_cast<const float*>(buf + 512)[t];
@@ -274,9 +277,11 @@ __device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const
 #pragma unroll
   for (int k = 0; k < 4; ++k)
     ch[k] = make_uint4(packed[4 * k], packed[4 * k + 1], packed[4 * k + 2], packed[4 * k + 3]);
-  const int rs0 = 2 * (row & 1) + (row >> 1);
-  store_group<4>(out_rsrc(it.idx + tile0 * 256, live * 256u), ch, ost, t, row,
-                 [rs0](int k) { return 8 * (k & 1) + 4 * (k >> 1) + rs0; });
+  // pass slot c = 16 t + s_k, (c >> 4) & 15 = t: position (16 t + ((2 r0 + r1) ^ t)) ^ (8 k0 + 4 k1)
+  const uint32_t wb = (uint32_t)(16 * t + ((2 * (row & 1) + (row >> 1)) ^ t));
+  store_group<4>(out_rsrc(it.idx + tile0 * 256, live * 256u), ch, ost, t, row * 16 + t, wb,
+                 [](int k) { return (uint32_t)(8 * (k & 1) + 4 * (k >> 1)); },
+                 store_read_base(t, row));
   if (a.auto_scale)
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(delta), out_rsrc(it.scale + tile0, live * 4u),
                                           (int)row0_offset(t, row, 4), 0, 0);
@@ -341,8 +346,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
 // Staged loads as in the encoder: a wave's 16 tiles are 4 KB of int8
 // indices, four 1 KB direct-to-LDS loads (instruction k covers tiles 4k ..
 // 4k + 3).  Lane l = 16 r + b of instruction k fetches row r, chunk
-// j = (b/4 - k) mod 4 of tile 4k + (b & 3) into slot 64 k + l; lane (t, r)
-// reads chunk j of its tile from slot 64 (t/4) + 16 r + ((t + 4j) mod 16).
+// j = (b/4) ^ k of tile 4k + (b & 3) into slot 64 k + l; lane (t, r) reads
+// chunk j of its tile from slot d0 ^ 4j, d0 = 64 (t/4) + 16 r + t.
 // Two more loads bring the group's coset words and scales (lanes 0-15; the
 // other lanes repeat them) to the 512 bytes after the indices.
 constexpr int kDecStage = 256 + 32;   // uint4 per wave
@@ -358,7 +363,7 @@ __device__ inline void dec_prefetch(const DecItem& it, int64_t group, uint4* buf
   const auto rs = out_rsrc(const_cast<int8_t*>(it.idx) + group * 16 * 256, live * 256u);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int j = ((b >> 2) - k) & 3;
+    const int j = (b >> 2) ^ k;
     const int off = (4 * k + (b & 3)) * 256 + r * 64 + j * 16;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr(buf + 64 * k), 16, off, 0, 0, 0);
   }
@@ -371,9 +376,10 @@ __device__ inline void dec_prefetch(const DecItem& it, int64_t group, uint4* buf
 }
 
 __device__ inline void dec_take(const uint4* buf, int t, int r, uint32_t* d, DecIn& in) {
+  const uint32_t d0 = (uint32_t)(64 * (t >> 2) + 16 * r + t);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint4 q = buf[64 * (t >> 2) + 16 * r + ((t + 4 * j) & 15)];
+    const uint4 q = buf[d0 ^ (4u * j)];
     d[4 * j] = q.x; d[4 * j + 1] = q.y; d[4 * j + 2] = q.z; d[4 * j + 3] = q.w;
   }
   in.cw = reinterpret_cast<const uint32_t*>(buf + 256)[t];
@@ -536,11 +542,15 @@ __device__ inline void dec_group(const DecItem& it, const uint32_t* sign_tab, in
       ch[k] = make_uint4(o[4 * k] ^ sm.x, o[4 * k + 1] ^ sm.y, o[4 * k + 2] ^ sm.z,
                          o[4 * k + 3] ^ sm.w);
     }
+    // pass slot c = 32 a + s_k (a = t mod 8), (c >> 4) & 15 = 2a + k1:
+    // position (32 a + (rs0 ^ 2a)) ^ (16 k1 + 8 k2 + (k0 ^ k1))
+    const int a8 = t & 7;
+    const uint32_t wb = (uint32_t)(32 * a8 + (rs0 ^ (2 * a8)));
     store_group<8>(out_rsrc(static_cast<uint16_t*>(it.y) + group * 16 * 256,
                             live_tiles(it.n_tiles, group) * 512u),
-                   ch, ost, t, row, [rs0](int k) {
-                     return (k & 1) + 16 * ((k >> 1) & 1) + 8 * (k >> 2) + rs0;
-                   });
+                   ch, ost, t, row * 16 + t, wb, [](int k) {
+                     return (uint32_t)(16 * ((k >> 1) & 1) + 8 * (k >> 2) + ((k & 1) ^ ((k >> 1) & 1)));
+                   }, store_read_base(t, row));
   } else {
     uint32_t o[64];
 #pragma unroll
@@ -559,7 +569,11 @@ __device__ inline void dec_group(const DecItem& it, const uint32_t* sign_tab, in
     }
     store_group<16>(out_rsrc(static_cast<float*>(it.y) + group * 16 * 256,
                              live_tiles(it.n_tiles, group) * 1024u),
-                    ch, ost, t, row, [row](int k) { return row * 16 + k; });
+                    // pass slot c = 64 a + 16 r + k (a = t mod 4), (c >> 4) & 15 = 4a + r:
+                    // position (64 a + 16 r + (4a + r)) ^ k
+                    ch, ost, t, row * 16 + t,
+                    (uint32_t)(64 * (t & 3) + 16 * row + 4 * (t & 3) + row),
+                    [](int k) { return (uint32_t)k; }, store_read_base(t, row));
   }
 }
 
