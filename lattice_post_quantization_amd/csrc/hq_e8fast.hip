@@ -8,22 +8,14 @@
 // rotation per tile, E8 by default, lossless strip, Rice code, algebraic
 // decoding).
 //
-// Work mapping (encode).  A wave holds 16 tiles.  Lane (t, r) = lane t + 16 r
-// holds 64 elements of tile t: those whose element bits 3-4 equal r.  The
-// Walsh-Hadamard transform is a product of one butterfly stage per element
-// bit; the stages on bits 0, 1, 2 and 7 run inside the lane (fp64
-// butterflies), and the four stages on bits 3-6 together are H16 acting on
-// p = bits 3-6, which the matrix cores apply as v_mfma_f64_16x16x4_f64
-// products with the +-1 matrix H16: the 16 tiles are the rows, p's low two
-// bits the lane row and its high two bits the accumulation step.  The
-// products of bf16 values with +-1 and their sums are exact in fp64 (as in
-// the butterflies), so the result is the exact Hadamard sum.  Afterwards lane
-// (t, r) holds output position n = t (element bits 3-6) of tiles 4i + r,
-// i = 0..3, with element bits 0, 1, 2, 7 in registers: an E8 block (bits
-// 0-2) stays inside the lane.
-// Decode keeps the earlier mapping: lane (t, r) holds elements
-// [64 r, 64 r + 64) of tile t; six exact int16 stages run in registers and
-// v_permlane16_swap / v_permlane32_swap exchange the two row bits.
+// Work mapping.  A wave holds 16 tiles.  Lane (t, r) = lane t + 16 r of the
+// wave holds elements [64 r, 64 r + 64) of tile t, so a tile spans the four
+// 16-lane rows and every lane keeps 64 elements in registers.  Element bits
+// 0-5 are register bits: six Walsh-Hadamard stages run inside the lane.
+// Element bits 6 and 7 are the row bits; v_permlane16_swap / v_permlane32_swap
+// exchange a row bit with a register bit (one instruction per dword pair),
+// after which those two stages also run in registers.  Reductions over a tile
+// use the same swaps.  No LDS traffic apart from a 512-byte sign table.
 #include "hq.h"
 #include "hq_device.h"
 #include "hq_internal.h"
@@ -71,13 +63,11 @@ __device__ inline uint32_t store_read_base(int t, int row) {
 
 // Staged loads.  A wave's 16 tiles are 8 KB of contiguous bf16, read with
 // eight direct-to-LDS loads of 1 KB each (instruction k covers tiles 2k and
-// 2k + 1, so every load is fully coalesced).  Lane (t, r)'s chunk j (8
-// elements, bits 0-2) is tile chunk r + 4 (j & 3) + 16 (j >> 2): element bits
-// 3-4 = r, bits 5-6 = j & 3, bit 7 = j >> 2.  Lane l = 16 r + b of
-// instruction k fetches chunk j = (b/2) ^ k of row r of tile 2k + (b & 1) and
-// the hardware stores it at LDS slot 64 k + l; lane (t, r) later finds chunk
-// j of its tile at slot e0 ^ 2j, e0 = 64 (t/2) + 16 r + t, so each 16-lane
-// row reads 16 different bank groups.
+// 2k + 1, so every load is fully coalesced).  Lane l = 16 r + b of
+// instruction k fetches row r, 16-byte chunk j = (b/2) ^ k of tile
+// 2k + (b & 1) and the hardware stores it at LDS slot 64 k + l; lane (t, r)
+// later finds chunk j of its tile at slot e0 ^ 2j, e0 = 64 (t/2) + 16 r + t,
+// so each 16-lane row reads 16 different bank groups.
 // With a caller-supplied scale, a ninth load brings the group's 16 scales to
 // the 256 bytes after the bf16 data (lanes 16-63 repeat them).  Lane offsets
 // are relative to the group's first tile; tiles past the end read as zeros.
@@ -93,7 +83,7 @@ __device__ inline void enc_prefetch(const EncItem& it, int64_t group, uint4* buf
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int j = (b >> 1) ^ k;
-    const int off = (2 * k + (b & 1)) * 512 + 16 * (r + 4 * (j & 3) + 16 * (j >> 2));
+    const int off = (2 * k + (b & 1)) * 512 + r * 128 + j * 16;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr(buf + 64 * k), 16, off, 0, 0, 0);
   }
   if (scale_in)
@@ -117,56 +107,33 @@ __device__ inline uint32_t row0_offset(int t, int row, int size) {
   return row == 0 ? (uint32_t)(t * size) : 0x40000000u;
 }
 
-typedef double f64x4 __attribute__((ext_vector_type(4)));
-
-// Sum over the 16 lanes of a row, in every lane (DPP row rotations).
-__device__ inline uint32_t row_sum_u32(uint32_t x) {
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false);   // row_ror:8
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xF, 0xF, false);   // row_ror:4
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x122, 0xF, 0xF, false);   // row_ror:2
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x121, 0xF, 0xF, false);   // row_ror:1
-  return x;
-}
-
-// Smallest k in [0, 8] with S <= 256 2^(k + 1): the bit length of S - 1
-// minus 9, clamped (S = 0 gives 0).
-__device__ inline int rice_kt(uint32_t S) {
-  const int bl = S == 0u ? 0 : 32 - __clz((int)(S - 1u));
-  const int k = bl - 9;
-  return k < 0 ? 0 : (k > 8 ? 8 : k);
-}
-
 // One group of 16 tiles held by a wave (w: this lane's 64 bf16 of its tile).
-// (scale_in: the caller's scale of this lane's tile when not automatic;
-// kx: 128 bytes of LDS for the exchange of the tiles' grid factors.)
+// (scale_in: the caller's scale of this lane's tile when not automatic.)
 __device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const uint32_t* sign_tab,
                                  int64_t group, int t, int row, const uint32_t* w, float scale_in,
-                                 uint4* kx) {
-  const uint4* st = reinterpret_cast<const uint4*>(sign_tab);
-  const uint32_t live = live_tiles(it.n_tiles, group);
-  const int64_t tile0 = group * 16;
-  // v[16 kk + g]: element bits 0-2 = g & 7, 3-4 = row, 5-6 = kk, 7 = g >> 3
+                                 uint4* ost) {
+
+  const uint4* st = reinterpret_cast<const uint4*>(sign_tab + row * 32);
   double v[64];
   double ss = 0.0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint4 m = st[row + 4 * (j & 3) + 16 * (j >> 2)];
+  for (int k = 0; k < 8; ++k) {
+    const uint4 m = st[k];
     const uint32_t mm[4] = {m.x, m.y, m.z, m.w};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t d = w[4 * j + q] ^ mm[q];
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t d = w[4 * k + j] ^ mm[j];
       const double lo = (double)__uint_as_float(d << 16);
       const double hi = (double)__uint_as_float(d & 0xFFFF0000u);
-      const int base = 16 * (j & 3) + 8 * (j >> 2) + 2 * q;
-      v[base] = lo;
-      v[base + 1] = hi;
+      v[8 * k + 2 * j] = lo;
+      v[8 * k + 2 * j + 1] = hi;
       ss = fma(lo, lo, ss);
       ss = fma(hi, hi, ss);
     }
   }
 
   // ---- scale: bf16_rne(rms * c) (auto) or the caller's; the norm bound
-  // sqrt(sum x^2)/Delta < 124 keeps every grid value in range
+  // sqrt(sum x^2)/Delta < 126 keeps every grid value in range
   ss = tile_sum_f64(ss);
   uint32_t status = 0;
   float delta;
@@ -178,211 +145,153 @@ __device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const
     if (!(delta > 0.0f) || !isfinite(delta)) status |= HQ_ST_NONFINITE;
   }
   if (!isfinite(ss)) status |= HQ_ST_NONFINITE;
+  // |u_i| <= sqrt(sum x^2) / Delta: below 124 no grid value reaches the clamp
   const bool big = !(sqrt(ss) < 124.0 * (double)delta);
-  const double K = 16777216.0 / (a.sqrt_n * (double)delta);
-  if (a.auto_scale)
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(delta), out_rsrc(it.scale + tile0, live * 4u),
-                                          (int)row0_offset(t, row, 4), 0, 0);
-  if (status && (uint32_t)t < live) set_status(a.status, status);
-  status = 0;
-  // The grid factor of tile t moves to the lanes that will hold tile t's
-  // outputs: slot 4 (t mod 4) + t / 4, read back as the four factors of
-  // tiles row, row + 4, row + 8, row + 12.
-  double* kd = reinterpret_cast<double*>(kx);
-  wave_lds_sync();
-  if (row == 0) kd[4 * (t & 3) + (t >> 2)] = K;
-  wave_lds_sync();
-  double Kt[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) Kt[i] = kd[4 * row + i];
+  double K = 16777216.0 / (a.sqrt_n * (double)delta);
 
-  // ---- Walsh-Hadamard stages on element bits 0, 1, 2, 7 (register bits of g)
+  // ---- Walsh-Hadamard: element bits 0-5 in registers
 #pragma unroll
-  for (int h = 1; h < 16; h <<= 1) {
+  for (int h = 1; h < 64; h <<= 1) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-      for (int g = 0; g < 16; ++g) {
-        if (!(g & h)) {
-          const double x = v[16 * kk + g], y = v[16 * kk + g + h];
-          v[16 * kk + g] = x + y;
-          v[16 * kk + g + h] = x - y;
-        }
+    for (int i = 0; i < 64; ++i) {
+      if (!(i & h)) {
+        const double x = v[i], y = v[i + h];
+        v[i] = x + y;
+        v[i + h] = x - y;
       }
     }
   }
-  // ---- stages on bits 3-6: D_g[m][n] = sum_p X_g[m][p] H16[p][n], the
-  // tiles m as rows, p = 4 kk + row (lane row: the step's K index), output
-  // n = t.  B operand of step kk at lane (t, row): H16[4 kk + row][t].
-  double B[4];
+  // element bit 6 (row bit 0) <-> register bit 5, then butterfly
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) B[kk] = (__popc((4 * kk + row) & t) & 1) ? -1.0 : 1.0;
-  double D[16][4];   // D[g][i]: tile 4 i + row, output element (g & 7) + 8 t + 128 (g >> 3)
-#pragma unroll
-  for (int g = 0; g < 16; ++g) {
-    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(v[16 * kk + g], B[kk], acc, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) D[g][i] = acc[i];
+  for (int i = 0; i < 32; ++i) {
+    swap_f64<false>(v[i], v[i + 32]);
+    const double x = v[i], y = v[i + 32];
+    v[i] = x + y;
+    v[i + 32] = x - y;
   }
-  double Ki[4] = {Kt[0], Kt[1], Kt[2], Kt[3]};
+  // element bit 7 (row bit 1) <-> register bit 4, then butterfly
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    if (!(i & 16)) {
+      swap_f64<true>(v[i], v[i + 16]);
+      const double x = v[i], y = v[i + 16];
+      v[i] = x + y;
+      v[i + 16] = x - y;
+    }
+  }
+  // Now register i holds element bits (i0 i1 i2 i3 | i4 = b7 | i5 = b6) and the
+  // lane's row bits hold (r0 = b5, r1 = b4).
 
   // When some tile of the wave may pass the clamp, the generic encoder's
   // clamped rint(S K) replaces S (and K becomes 1).
   if (__builtin_amdgcn_ballot_w64(big) != 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int g = 0; g < 16; ++g) {
-        double q = rint(__dmul_rn(D[g][i], Kt[i]));
-        if (!(fabs(q) <= kUClamp)) {
-          if ((uint32_t)(4 * i + row) < live) status |= HQ_ST_OVERFLOW;
-          q = (q > 0.0) ? kUClamp : -kUClamp;
-        }
-        D[g][i] = q;
+    for (int i = 0; i < 64; ++i) {
+      double q = rint(__dmul_rn(v[i], K));
+      if (!(fabs(q) <= kUClamp)) {
+        status |= HQ_ST_OVERFLOW;
+        q = (q > 0.0) ? kUClamp : -kUClamp;
       }
-      Ki[i] = 1.0;
+      v[i] = q;
     }
+    K = 1.0;
   }
 
-  // ---- quantizer input U = rne(S K) (units of 2^-24), E8 per block
-  // (block g3 of tile 4 i + row: element bit 7 = g3, bits 3-6 = t, so tile
-  // block index t + 16 g3)
-  uint32_t packed[4][4];
-  uint32_t ties = 0, cb = 0;   // bit 2 i + g3
-  int32_t U[64];               // U[16 i + g]
+  // ---- quantizer input U = rne(S K) (units of 2^-24), stored integers
+  uint32_t packed[16];
+  uint32_t cbits = 0, ties = 0;
+  int32_t U[64];
+  const int r0 = row & 1, r1 = row >> 1;
+  // tile block index of register block blk = b3 + 2 b4 + 4 b5 + 8 b6 + 16 b7
+  auto bpos = [&](int blk) {
+    return (blk & 1) + 2 * r1 + 4 * r0 + 8 * (blk >> 2) + 16 * ((blk >> 1) & 1);
+  };
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int blk = 0; blk < 8; ++blk) {
 #pragma unroll
-    for (int g3 = 0; g3 < 2; ++g3) {
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        // two roundings, never fused: q = RN(S K), then RN(q + 1.5 2^52)
-        const double x = __dadd_rn(__dmul_rn(D[8 * g3 + m][i], Ki[i]), kMagic);
-        U[16 * i + 8 * g3 + m] = (int32_t)(uint32_t)(uint64_t)__double_as_longlong(x);
-      }
-      int c;
-      ties |= e8_block_fast(U + 16 * i + 8 * g3, packed[i][2 * g3], packed[i][2 * g3 + 1], c)
-              << (2 * i + g3);
-      cb |= (uint32_t)c << (2 * i + g3);
+    for (int i = 0; i < 8; ++i) {
+      // two roundings, never fused: q = RN(S K), then RN(q + 1.5 2^52)
+      const double m = __dadd_rn(__dmul_rn(v[8 * blk + i], K), kMagic);
+      U[8 * blk + i] = (int32_t)(uint32_t)(uint64_t)__double_as_longlong(m);
     }
+    int c;
+    ties |= e8_block_fast(U + 8 * blk, packed[2 * blk], packed[2 * blk + 1], c) << blk;
+    cbits |= (uint32_t)c << bpos(blk);
   }
   if (ties) {
     // blocks with a coordinate exactly on a rounding boundary
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) {
       if ((ties >> blk) & 1u) {
-        const int i = blk >> 1, g3 = blk & 1;
-        const int c = e8_block_exact(U + 16 * i + 8 * g3, packed[i][2 * g3], packed[i][2 * g3 + 1]);
-        cb = (cb & ~(1u << blk)) | ((uint32_t)c << blk);
+        const int c = e8_block_exact(U + 8 * blk, packed[2 * blk], packed[2 * blk + 1]);
+        cbits = (cbits & ~(1u << bpos(blk))) | ((uint32_t)c << bpos(blk));
       }
     }
   }
+  const uint32_t coset_word = tile_or_u32(cbits);
 
-  // ---- per tile: coset word (bit t + 16 g3 from lane t of the tile's row),
-  // Rice parameter and bit length.  k = argmin_k L(k), L(k) = Q_k + 256 (1 +
-  // k), Q_k = sum floor(zeta / 2^k).  L is convex: L(k+1) - L(k) = 256 - D_k
-  // with D_k = Q_k - Q_{k+1} = sum floor((zeta + 2^k) / 2^(k+1)), which
-  // falls with k, so the first minimum is the smallest k with D_k <= 256.
-  // D_k lies within 128 of S / 2^(k+1) (S = sum zeta), so with kt the
-  // smallest k with S <= 256 * 2^(k+1): D_{kt+1} <= 256, and D_k > 256 for k
-  // <= kt - 2 (strictly, so no smaller k ties).  Only kt - 1, kt, kt + 1
-  // remain.  A tile's 256 indices sit in the 16 lanes of one row; sums of two
-  // tiles share a dword (each below 2^16).
-  uint32_t zz[4][4];
-  uint32_t s2[2] = {0u, 0u};
+  // ---- Rice parameter: k = argmin_k L(k), L(k) = Q_k + 256 (1 + k),
+  // Q_k = sum floor(zeta / 2^k).  L is convex: L(k+1) - L(k) = 256 - D_k with
+  // D_k = Q_k - Q_{k+1} = sum floor((zeta + 2^k) / 2^(k+1)), which falls
+  // with k, so the first minimum is the smallest k with D_k <= 256.  D_k lies
+  // within 128 of S / 2^(k+1) (S = sum zeta), so with kt the smallest k with
+  // S <= 256 * 2^(k+1): D_{kt+1} <= 256, and D_k > 256 for k <= kt - 2
+  // (strictly, so no smaller k ties).  Only kt - 1, kt, kt + 1 remain.
+  uint32_t zz[16];
+  uint32_t S = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t s1 = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      zz[i][q] = zigzag4(packed[i][q]);
-      s1 = byte_sum(zz[i][q], s1);
-    }
-    s2[i >> 1] += s1 << (16 * (i & 1));
+  for (int q = 0; q < 16; ++q) {
+    zz[q] = zigzag4(packed[q]);
+    S = byte_sum(zz[q], S);
   }
-  uint32_t S[4];
+  S = tile_sum_u32(S);
+  int kt = 0;
+  while (kt < 8 && S > (256u << (kt + 1))) ++kt;
+  int kc[3];
+  uint32_t R[3];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const uint32_t x = row_sum_u32(s2[h]);
-    S[2 * h] = x & 0xFFFFu;
-    S[2 * h + 1] = x >> 16;
+  for (int j = 0; j < 3; ++j) {
+    int k = kt - 1 + j;
+    kc[j] = k < 0 ? 0 : (k > 8 ? 8 : k);
+    const uint32_t mask = ((1u << kc[j]) - 1u) * 0x01010101u;
+    uint32_t r = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) r = byte_sum(zz[q] & mask, r);
+    R[j] = r;
   }
-  int kc[4][3];
-  uint32_t R2[3][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}};
+  uint32_t best = 0xFFFFFFFFu;
+  int bk = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int kt = rice_kt(S[i]);
-#pragma unroll
-    for (int jc = 0; jc < 3; ++jc) {
-      const int k = kt - 1 + jc;
-      kc[i][jc] = k < 0 ? 0 : (k > 8 ? 8 : k);
-      const uint32_t mask = ((1u << kc[i][jc]) - 1u) * 0x01010101u;
-      uint32_t r = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) r = byte_sum(zz[i][q] & mask, r);
-      R2[jc][i >> 1] += r << (16 * (i & 1));
-    }
-  }
-  uint32_t best[4], bk[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    best[i] = 0xFFFFFFFFu;
-    bk[i] = 0;
-  }
-#pragma unroll
-  for (int jc = 0; jc < 3; ++jc) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t x = row_sum_u32(R2[jc][h]);
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int i = 2 * h + e;
-        const uint32_t Rk = e ? (x >> 16) : (x & 0xFFFFu);
-        const uint32_t L = ((S[i] - Rk) >> kc[i][jc]) + 256u * (uint32_t)(1 + kc[i][jc]);
-        if (L < best[i]) {
-          best[i] = L;
-          bk[i] = (uint32_t)kc[i][jc];
-        }
-      }
-    }
+  for (int j = 0; j < 3; ++j) {
+    const uint32_t Rk = tile_sum_u32(R[j]);
+    const uint32_t L = ((S - Rk) >> kc[j]) + 256u * (uint32_t)(1 + kc[j]);
+    if (L < best) { best = L; bk = kc[j]; }
   }
 
-  // ---- stores.  Lane (t, row) holds, for tile 4 i + row, the indices of
-  // elements 8 t .. 8 t + 7 (block t) and 128 + 8 t .. (block t + 16): two
-  // 8-byte pieces; per (i, g3) the 16 lanes of a row write 128 contiguous
-  // bytes of one tile.
-  const auto ri = out_rsrc(it.idx + tile0 * 256, live * 256u);
+  // ---- store.  Chunk k (blocks 2k, 2k + 1: element bits 0-3 inside) has
+  // element bit 7 = k bit 0, bit 6 = k bit 1, bit 5 = row bit 0 and bit 4 =
+  // row bit 1, i.e. 16-byte slot 8 k0 + 4 k1 + 2 r0 + r1 of the tile.
+  const uint32_t live = live_tiles(it.n_tiles, group);
+  const int64_t tile0 = group * 16;
+  uint4 ch[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int g3 = 0; g3 < 2; ++g3) {
-      typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-      __builtin_amdgcn_raw_buffer_store_b64((u32x2){packed[i][2 * g3], packed[i][2 * g3 + 1]}, ri,
-                                            (int)(256 * (4 * i + row) + 128 * g3 + 8 * t), 0, 0);
-    }
-  }
-  // coset words from ballots of the coset bits (the same in every lane)
-  const auto rc = out_rsrc(it.coset + tile0, live * 4u);
-  const auto rk = out_rsrc(it.rice_k + tile0, live);
-  const auto rb = out_rsrc(it.tile_bits + tile0, live * 4u);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint64_t m0 = __builtin_amdgcn_ballot_w64(((cb >> (2 * i)) & 1u) != 0u);
-    const uint64_t m1 = __builtin_amdgcn_ballot_w64(((cb >> (2 * i + 1)) & 1u) != 0u);
-    const uint32_t word = (uint32_t)((m0 >> (16 * row)) & 0xFFFFu) |
-                          ((uint32_t)((m1 >> (16 * row)) & 0xFFFFu) << 16);
-    // lane 0 of each row writes the row's tile; other lanes fall outside
-    const uint32_t tl = (uint32_t)(4 * i + row);
-    const int o4 = t == 0 ? (int)(4 * tl) : 0x40000000;
-    const int o1 = t == 0 ? (int)tl : 0x40000000;
-    __builtin_amdgcn_raw_buffer_store_b32(word, rc, o4, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)bk[i], rk, o1, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b32(4u + 32u + best[i], rb, o4, 0, 0);
-  }
-  if (status) set_status(a.status, status);
+  for (int k = 0; k < 4; ++k)
+    ch[k] = make_uint4(packed[4 * k], packed[4 * k + 1], packed[4 * k + 2], packed[4 * k + 3]);
+  // pass slot c = 16 t + s_k, (c >> 4) & 15 = t: position (16 t + ((2 r0 + r1) ^ t)) ^ (8 k0 + 4 k1)
+  const uint32_t wb = (uint32_t)(16 * t + ((2 * (row & 1) + (row >> 1)) ^ t));
+  store_group<4>(out_rsrc(it.idx + tile0 * 256, live * 256u), ch, ost, t, row * 16 + t, wb,
+                 [](int k) { return (uint32_t)(8 * (k & 1) + 4 * (k >> 1)); },
+                 store_read_base(t, row));
+  if (a.auto_scale)
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(delta), out_rsrc(it.scale + tile0, live * 4u),
+                                          (int)row0_offset(t, row, 4), 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b32(coset_word, out_rsrc(it.coset + tile0, live * 4u),
+                                        (int)row0_offset(t, row, 4), 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b8((uint8_t)bk, out_rsrc(it.rice_k + tile0, live),
+                                       (int)row0_offset(t, row, 1), 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b32(4u + 32u + best, out_rsrc(it.tile_bits + tile0, live * 4u),
+                                        (int)row0_offset(t, row, 4), 0, 0);
+  if (status && (uint32_t)t < live) set_status(a.status, status);
 }
 
 // Persistent waves: each wave walks groups of 16 tiles with a grid-wide
