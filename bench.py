@@ -210,6 +210,45 @@ def time_calls(fn, reps, warm=2):
     return e0.elapsed_time(e1) / reps
 
 
+def kv_per_vector(kcache, bps, dev, n_vec=64, n_seeds=1024):
+    """Per-vector bias of the reconstruction, dither against rotation-only:
+    n_vec fixed K vectors (every 4096th of the cache) through encode and
+    fp32 decode under n_seeds dither seeds.  With the dither the error is
+    uniform on the E8 cell scaled by Delta: z = mean error / (Delta
+    sqrt(G / S)) is standard per coordinate and MSE / (G Delta^2) = 1;
+    rotation-only errors stay fixed, so their z grows as sqrt(S)."""
+    g_e8 = 929.0 / 12960.0            # normalized second moment of E8 (Conway-Sloane)
+    xd = kcache[torch.arange(n_vec, device=dev) * 4096].contiguous()
+    x = xd.double()
+    o = hq.hq_kv_encode(xd, bps, 1, dither_seed=1)
+    delta = o["scale"].double()[:, None]
+    y = torch.empty(xd.shape, dtype=torch.float32, device=dev)
+    acc = torch.zeros_like(x)
+    acc2 = torch.zeros_like(x)
+    for s in range(1, n_seeds + 1):
+        hq.hq_kv_encode(xd, bps, 1, dither_seed=s, out=o)
+        hq.hq_decode_tiles(o["idx"], o["coset"], o["scale"], "E8", 128, 1, torch.float32,
+                           dither_seed=s, out=y)
+        e = y.double() - x
+        acc += e
+        acc2 += e * e
+    unit = delta * math.sqrt(g_e8 / n_seeds)
+    z = acc / n_seeds / unit
+    o0 = hq.hq_kv_encode(xd, bps, 1)
+    e0 = hq.hq_decode_tiles(o0["idx"], o0["coset"], o0["scale"], "E8", 128, 1,
+                            torch.float32).double() - x
+    z0 = e0 / unit
+    return {"workload": "%d K vectors (every 4096th of the cache), %d dither seeds, fp32 decode; "
+                        "z = per-coordinate mean error over the seeds / (Delta sqrt(G(E8) / S))"
+                        % (n_vec, n_seeds),
+            "dither": {"z_rms": round(float(torch.sqrt((z * z).mean())), 4),
+                       "z2_per_vector_max": round(float((z * z).mean(1).max()), 4),
+                       "mse_over_G_delta2": round(float((acc2 / n_seeds / (g_e8 * delta * delta)).mean()), 4)},
+            "rotation_only": {"z_rms": round(float(torch.sqrt((z0 * z0).mean())), 2),
+                              "z_rms_per_vector_min": round(float(torch.sqrt((z0 * z0).mean(1)).min()), 2),
+                              "mse_over_G_delta2": round(float((e0 * e0 / (g_e8 * delta * delta)).mean()), 4)}}
+
+
 def secondary(layer0, bps, dev):
     """Steps outside the headline: the rate + pack pass over one layer's
     indices (its own pass over the encoder's output), the stream decoder on
@@ -507,6 +546,7 @@ def secondary(layer0, bps, dev):
         bias[mode] = {"z_mean": round(float(z.mean()), 3), "z_max": round(float(z.max()), 3)}
         del ek, kh, err
     kv["bias"] = bias
+    kv["per_vector"] = kv_per_vector(kvs[0], bps, dev)
     return {"pack": pack, "unpack": unpack, "gemv": gemv, "gemm": gemm, "kv": kv,
             "variants": variants,
             "lattice_sweep": sweep}

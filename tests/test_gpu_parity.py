@@ -259,6 +259,59 @@ def test_kv_dither_parity_and_unbiasedness():
     assert abs(stat) <= 4 * se
 
 
+def test_kv_dither_unbiased_per_vector_on_the_gpu():
+    """The subtractive dither makes each cached vector's reconstruction
+    unbiased; rotation alone does not.  64 fixed K vectors (bf16, 4 bps,
+    every 4096th vector of the K cache), each encoded and decoded (fp32) by
+    the HIP path under 1024 dither seeds, and once rotation-only.  Under the
+    dither the error is uniform on the E8 Voronoi cell scaled by Delta,
+    independent of the vector: per coordinate mean 0 and variance
+    G(E8) Delta^2, so z = mean over seeds / (Delta sqrt(G / S)) is standard
+    in every coordinate of every vector, and MSE / (G Delta^2) is 1.  The
+    rotation-only error is fixed per vector, of size ~ sqrt(G) Delta: its z
+    grows as sqrt(S) (~32 here)."""
+    g_e8 = 929.0 / 12960.0            # normalized second moment of E8 (Conway-Sloane)
+    kb, _ = workloads.kv_layer()
+    sel = np.arange(64) * 4096
+    bits = kb.reshape(-1, 128)[sel]
+    xd = T.bf16_device(bits, (64, 128))
+    x = xd.double()
+    n_seeds = 1024
+    say("case: kv per-vector unbiasedness, 64 vectors x %d dither seeds" % n_seeds)
+    o = hq.hq_kv_encode(xd, 4.0, 1, dither_seed=1)
+    delta = o["scale"].double()[:, None]
+    y = torch.empty((64, 128), dtype=torch.float32, device=xd.device)
+    acc = torch.zeros_like(x)
+    acc2 = torch.zeros_like(x)
+    for s in range(1, n_seeds + 1):
+        hq.hq_kv_encode(xd, 4.0, 1, dither_seed=s, out=o)
+        hq.hq_decode_tiles(o["idx"], o["coset"], o["scale"], "E8", 128, 1, torch.float32,
+                           dither_seed=s, out=y)
+        e = y.double() - x
+        acc += e
+        acc2 += e * e
+    assert torch.equal(o["scale"].double()[:, None], delta)    # the dither leaves the scale alone
+    unit = delta * math.sqrt(g_e8 / n_seeds)
+    z = acc / n_seeds / unit
+    z2_vec = (z * z).mean(1)
+    mse_d = float((acc2 / n_seeds / (g_e8 * delta * delta)).mean())
+    o0 = hq.hq_kv_encode(xd, 4.0, 1)
+    y0 = hq.hq_decode_tiles(o0["idx"], o0["coset"], o0["scale"], "E8", 128, 1, torch.float32)
+    e0 = y0.double() - x
+    z0 = e0 / unit
+    z0_vec = torch.sqrt((z0 * z0).mean(1))
+    mse_0 = float((e0 * e0 / (g_e8 * delta * delta)).mean())
+    rms_z = float(torch.sqrt((z * z).mean()))
+    say("  dither: rms z %.3f, max per-vector mean z^2 %.3f, MSE/(G D^2) %.4f" %
+        (rms_z, float(z2_vec.max()), mse_d))
+    say("  rotation-only: min per-vector rms z %.1f, MSE/(G D^2) %.4f" %
+        (float(z0_vec.min()), mse_0))
+    assert 0.9 < rms_z < 1.1                  # 8192 coordinates: 1 +- 0.016
+    assert float(z2_vec.max()) < 1.6          # 64 vectors, chi2(128)/128: 1 +- 0.125
+    assert abs(mse_d - 1.0) < 0.01
+    assert float(z0_vec.min()) > 8.0          # every vector keeps a fixed error
+
+
 def _attn_tol(q, k_hat, v_hat, tau):
     """Bound for hq_kv_attention against the fp64 attention of the same
     decoded cache.  A score (base-2 units, tau log2(e) q . khat) is an fp32
