@@ -61,7 +61,8 @@ typedef int32_t hq_status;
 enum {
   HQ_OK = 0,
   HQ_EINVAL = -1,       /* bad argument (null pointer, size, tile, dtype)  */
-  HQ_ERANGE = -2,       /* auto scale cannot keep indices inside int8      */
+  HQ_ERANGE = -2,       /* auto scale cannot keep indices inside int8
+                           (int16 with HQ_IDX16)                           */
   HQ_EDEVICE = -3,      /* a HIP call or kernel launch failed              */
   HQ_EUNSUPPORTED = -4, /* a valid combination the library does not offer */
   HQ_EIO = -5,          /* checkpoint file: cannot open, write or read     */
@@ -84,17 +85,31 @@ enum {
   HQ_RATE_CONTROL = 8u, /* encode: per-tile scales by bisection so that each
                            tile fits floor(bps * tile) bits (see below);
                            requires HQ_SCALE_AUTO; not with HQ_DITHER       */
-  HQ_RATE_GIVEN = 16u   /* hq_rate: rice_k and tile_bits are inputs (the
+  HQ_RATE_GIVEN = 16u,  /* hq_rate: rice_k and tile_bits are inputs (the
                            values hq_encode_tiles wrote for these indices);
                            other calls ignore it                           */
+  HQ_IDX16 = 32u        /* int16 index mode, for bit rates whose indices
+                           leave int8 (R >= 6 at tile 256: the stripped
+                           integers reach |u| + 2 with |u| <= sqrt(n)/c).
+                           Every `int8_t* idx` argument of the call then
+                           points to int16 values (2 bytes per index, the
+                           same count and order); grid values are held in
+                           64 bits and clamped at |u| = 32000; Rice k runs
+                           over [0, 15].  Taken by hq_encode_tiles,
+                           hq_decode_tiles, hq_rate, hq_rate_noalloc,
+                           hq_rate_batch, hq_unpack and hq_unpack_batch
+                           (all on the generic kernels); the other calls,
+                           HQ_DITHER and HQ_RATE_CONTROL refuse it with
+                           HQ_EUNSUPPORTED                                 */
 };
 
 /* Device status bits (OR-ed into *status by kernels). */
 enum {
   HQ_ST_NONFINITE = 1u,   /* NaN or Inf in the input of a tile            */
-  HQ_ST_OVERFLOW = 2u,    /* a grid value |u| passed 124, where encode
-                             clamps it (explicit scale; covers every
-                             index that would leave int8)                 */
+  HQ_ST_OVERFLOW = 2u,    /* a grid value |u| passed 124 (32000 with
+                             HQ_IDX16), where encode clamps it (explicit
+                             scale; covers every index that would leave
+                             int8, or int16)                              */
   HQ_ST_STREAM_FULL = 4u, /* hq_rate: packed stream exceeded capacity     */
   HQ_ST_CORRUPT = 8u      /* hq_unpack: a tile's codes overran its words,
                              or decoded to a value outside int8; hq_rate
@@ -279,9 +294,10 @@ size_t hq_rate_batch_workspace_bytes(int32_t count, const hq_rate_item* items);
  * stream_words: the words (device, read only within the tiles' ranges);
  * tile_word_offset [n_tiles + 1] uint64 (device); idx [n_tiles * tile] int8
  * out; coset [n_tiles * hq_coset_words(p)] uint32 out (NULL iff that is 0);
- * rice_k [n_tiles] uint8 out, or NULL.  Only lattice and tile of p are used.
+ * rice_k [n_tiles] uint8 out, or NULL.  Only lattice, tile and HQ_IDX16 of
+ * p are used (with HQ_IDX16 idx receives int16 values).
  * A tile whose codes run past its words, whose word range is reversed, or
- * that decodes an index outside int8 sets HQ_ST_CORRUPT; its outputs are
+ * that decodes an index outside int8 (int16) sets HQ_ST_CORRUPT; its outputs are
  * unspecified and no word outside its range is read.  idx must be 16-byte
  * aligned.
  */

@@ -58,7 +58,7 @@ hq_status scratch_address(void** out) {
 }
 
 constexpr uint32_t kKnownFlags =
-    HQ_SCALE_AUTO | HQ_DITHER | HQ_WANT_COORDS | HQ_RATE_CONTROL | HQ_RATE_GIVEN;
+    HQ_SCALE_AUTO | HQ_DITHER | HQ_WANT_COORDS | HQ_RATE_CONTROL | HQ_RATE_GIVEN | HQ_IDX16;
 
 bool lattice_ok(int32_t l) { return l == HQ_E8 || l == HQ_D4 || l == HQ_A2 || l == HQ_Z; }
 
@@ -73,6 +73,9 @@ hq_status check_params(const hq_params* p) {
     if (!(p->flags & HQ_SCALE_AUTO)) return HQ_EINVAL;     // the scales are outputs
     if (p->flags & HQ_DITHER) return HQ_EUNSUPPORTED;
   }
+  // the int16 index mode runs on the generic kernels, without dither or
+  // rate control
+  if ((p->flags & HQ_IDX16) && (p->flags & (HQ_DITHER | HQ_RATE_CONTROL))) return HQ_EUNSUPPORTED;
   if (p->flags & HQ_DITHER) {
     if (p->lattice != HQ_E8) return HQ_EUNSUPPORTED;
     if (p->tile > 256) return HQ_EUNSUPPORTED;   // the dither key holds coordinates < 256
@@ -95,10 +98,15 @@ double scale_constant(const hq_params* p) {
   return sqrt(2.0 * M_PI * M_E) * pow(2.0, -(double)p->bps) / vol_root(p->lattice);
 }
 
-// Auto scale keeps |index| <= sqrt(n)/c + 2 inside int8.
+// Auto scale keeps |index| <= sqrt(n)/c + 2 inside int8, or in the int16
+// index mode within the 64-bit grid's clamp (|u| <= 32000, inside int16).
 bool range_ok(const hq_params* p) {
-  return sqrt((double)p->tile) / scale_constant(p) + 2.0 <= 127.0;
+  const double bound = (p->flags & HQ_IDX16) ? 32000.0 : 127.0;
+  return sqrt((double)p->tile) / scale_constant(p) + 2.0 <= bound;
 }
+
+// Calls that take int8 indices only.
+bool idx16(const hq_params* p) { return (p->flags & HQ_IDX16) != 0; }
 
 int32_t coset_words(const hq_params* p) {
   if (p->lattice == HQ_E8) return (p->tile / 8 + 31) / 32;
@@ -207,6 +215,7 @@ hq_status hq_encode_tiles(const hq_params* p, const void* x, int32_t x_dtype, in
   a.c = scale_constant(p);
   a.sqrt_n = sqrt((double)p->tile);
   set_rate_control(p, a);
+  a.wide = idx16(p) ? 1 : 0;
   return launched(launch_encode(a, stream));
 }
 
@@ -216,7 +225,7 @@ hq_status hq_kv_encode(const hq_params* p, const void* kv, int32_t kv_dtype, int
   hq_status st = check_params(p);
   if (st != HQ_OK) return st;
   if (p->lattice != HQ_E8) return HQ_EUNSUPPORTED;
-  if (p->flags & HQ_WANT_COORDS) return HQ_EUNSUPPORTED;
+  if (p->flags & (HQ_WANT_COORDS | HQ_IDX16)) return HQ_EUNSUPPORTED;
   if (n_vectors < 0) return HQ_EINVAL;
   st = check_encode(p, kv, kv_dtype, n_vectors, p->tile, scale, idx, coset, rice_k, tile_bits,
                     nullptr);
@@ -287,6 +296,7 @@ hq_status hq_decode_tiles(const hq_params* p, const int8_t* idx, const uint32_t*
   a.dither = (p->flags & HQ_DITHER) != 0;
   a.dither_seed = p->dither_seed;
   a.dither_base = p->dither_base;
+  a.wide = idx16(p) ? 1 : 0;
   return launched(launch_decode(a, stream));
 }
 
@@ -299,7 +309,7 @@ hq_status check_encode_batch(const hq_params* p, int32_t x_dtype, int32_t count,
                              const hq_encode_item* items, uint32_t* status) {
   hq_status st = check_params(p);
   if (st != HQ_OK) return st;
-  if (p->flags & (HQ_WANT_COORDS | HQ_DITHER)) return HQ_EUNSUPPORTED;
+  if (p->flags & (HQ_WANT_COORDS | HQ_DITHER | HQ_IDX16)) return HQ_EUNSUPPORTED;
   if (count < 0 || (count > 0 && items == nullptr)) return HQ_EINVAL;
   for (int32_t i = 0; i < count; ++i) {
     const hq_encode_item& it = items[i];
@@ -388,7 +398,7 @@ hq_status check_decode_batch(const hq_params* p, int32_t y_dtype, int32_t count,
                              const hq_decode_item* items, uint32_t* status) {
   hq_status st = check_params(p);
   if (st != HQ_OK) return st;
-  if (p->flags & (HQ_WANT_COORDS | HQ_DITHER)) return HQ_EUNSUPPORTED;
+  if (p->flags & (HQ_WANT_COORDS | HQ_DITHER | HQ_IDX16)) return HQ_EUNSUPPORTED;
   if (y_dtype != HQ_F32 && y_dtype != HQ_BF16) return HQ_EINVAL;
   if (count < 0 || (count > 0 && items == nullptr)) return HQ_EINVAL;
   for (int32_t i = 0; i < count; ++i) {
@@ -625,6 +635,7 @@ static hq_status rate_impl(const hq_params* p, const int8_t* idx, const uint32_t
   a.wave_words = ws ? static_cast<uint64_t*>(workspace) + 2 * nb : nullptr;
   a.status = status;
   a.given = given ? 1 : 0;
+  a.wide = idx16(p) ? 1 : 0;
   return launched(launch_rate(a, stream));
 }
 
@@ -748,6 +759,7 @@ hq_status hq_rate_batch(const hq_params* p, int32_t count, const hq_rate_item* i
     ws += hq_rate_workspace_bytes(it.n_tiles);
     a.status = status;
     a.given = (p->flags & HQ_RATE_GIVEN) ? 1 : 0;
+    a.wide = idx16(p) ? 1 : 0;
     b.block0[b.n + 1] = b.block0[b.n] + rate_blocks(p->tile, it.n_tiles);
     ++b.n;
   }
@@ -793,6 +805,7 @@ hq_status hq_unpack_batch(const hq_params* p, int32_t count, const hq_unpack_ite
   a.coset_bits = coset_bits(p);
   a.coset_words = coset_words(p);
   a.status = status;
+  a.wide = idx16(p) ? 1 : 0;
   for (int32_t i = 0; i <= count; ++i) {
     if ((i == count || a.n == kUnpackMaxItems) && a.n > 0) {
       if (launch_unpack(a, stream) != hipSuccess) return HQ_EDEVICE;
@@ -925,7 +938,8 @@ hq_status hq_gemm_batch(const hq_params* p, int32_t count, const hq_gemv_item* i
   (void)status;
   hq_status st = check_params(p);
   if (st != HQ_OK) return st;
-  if (p->lattice != HQ_E8 || p->tile != 256 || (p->flags & HQ_DITHER)) return HQ_EUNSUPPORTED;
+  if (p->lattice != HQ_E8 || p->tile != 256 || (p->flags & (HQ_DITHER | HQ_IDX16)))
+    return HQ_EUNSUPPORTED;
   if (count < 0 || (count > 0 && items == nullptr) || m < 1 || m > kGemmMaxVecs)
     return HQ_EINVAL;
   bool any = false;
@@ -1002,7 +1016,8 @@ hq_status hq_gemv_batch(const hq_params* p, int32_t count, const hq_gemv_item* i
   (void)status;
   hq_status st = check_params(p);
   if (st != HQ_OK) return st;
-  if (p->lattice != HQ_E8 || p->tile != 256 || (p->flags & HQ_DITHER)) return HQ_EUNSUPPORTED;
+  if (p->lattice != HQ_E8 || p->tile != 256 || (p->flags & (HQ_DITHER | HQ_IDX16)))
+    return HQ_EUNSUPPORTED;
   if (count < 0 || (count > 0 && items == nullptr) || m < 1 || m > 8) return HQ_EINVAL;
   bool any = false;
   for (int32_t i = 0; i < count; ++i) {
@@ -1067,7 +1082,7 @@ hq_status hq_kv_scores(const hq_params* p, const float* q, int64_t n_q, const in
                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
   hq_status st = check_params(p);
   if (st != HQ_OK) return st;
-  if (p->lattice != HQ_E8 || p->tile != 128) return HQ_EUNSUPPORTED;
+  if (p->lattice != HQ_E8 || p->tile != 128 || idx16(p)) return HQ_EUNSUPPORTED;
   if (n_q < 0 || n_keys < 0) return HQ_EINVAL;
   if (n_q == 0 || n_keys == 0) return HQ_OK;   // nothing to compute
   if (q == nullptr || idx == nullptr || coset == nullptr || scale == nullptr ||
@@ -1121,7 +1136,7 @@ size_t hq_kv_attention_workspace_bytes(int64_t n_heads, int64_t n_q, int64_t n_k
 static hq_status check_cache(const hq_params* p, int64_t n_keys) {
   hq_status st = check_params(p);
   if (st != HQ_OK) return st;
-  if (p->lattice != HQ_E8 || p->tile != 128) return HQ_EUNSUPPORTED;
+  if (p->lattice != HQ_E8 || p->tile != 128 || idx16(p)) return HQ_EUNSUPPORTED;
   if ((p->flags & HQ_DITHER) && p->dither_base + n_keys > ((int64_t)1 << 32)) return HQ_EINVAL;
   return HQ_OK;
 }
@@ -1194,7 +1209,7 @@ const char* hq_status_string(hq_status s) {
   switch (s) {
     case HQ_OK: return "ok";
     case HQ_EINVAL: return "invalid argument";
-    case HQ_ERANGE: return "auto scale would overflow the int8 indices";
+    case HQ_ERANGE: return "auto scale would overflow the indices (int8; int16 with HQ_IDX16)";
     case HQ_EDEVICE: return "HIP call or kernel launch failed";
     case HQ_EUNSUPPORTED: return "unsupported parameter combination";
     case HQ_EIO: return "checkpoint file cannot be opened, written or read";

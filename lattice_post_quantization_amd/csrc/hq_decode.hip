@@ -49,7 +49,8 @@ __device__ inline uint32_t lane_sign_mask(const DecodeLaunch& a, int r) {
   return (s >> (16 * (r & 1))) & 0xFFFFu;
 }
 
-template <int LAT, int N, bool OUT_BF16, bool DITHER>
+// WIDE: the int16 index mode (idx holds int16 values; no dither).
+template <int LAT, int N, bool OUT_BF16, bool DITHER, bool WIDE>
 __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeLaunch a) {
   constexpr int G = N / kElemsPerLane;
   constexpr int TPB = kBlock / G;
@@ -58,11 +59,19 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeLaunch a) {
   if (tile >= a.n_tiles) return;
   const int64_t e0 = tile * N + (int64_t)r * kElemsPerLane;
 
-  const uint4 q = *reinterpret_cast<const uint4*>(a.idx + e0);
-  const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
   int32_t s[16];
+  if constexpr (WIDE) {
+    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const int16_t*>(a.idx) + e0);
+    const uint4 q0 = p[0], q1 = p[1];
+    const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
 #pragma unroll
-  for (int i = 0; i < 16; ++i) s[i] = (int32_t)(int8_t)(qw[i >> 2] >> (8 * (i & 3)));
+    for (int i = 0; i < 16; ++i) s[i] = (int32_t)(int16_t)(qw[i >> 1] >> (16 * (i & 1)));
+  } else {
+    const uint4 q = *reinterpret_cast<const uint4*>(a.idx + e0);
+    const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = (int32_t)(int8_t)(qw[i >> 2] >> (8 * (i & 3)));
+  }
   const double delta = (double)a.scale[tile];
 
   // coset bits of this lane's blocks (E8: 2 per lane, A2: 8 per lane)
@@ -170,20 +179,26 @@ hipError_t launch_lat_n(const DecodeLaunch& a, hipStream_t s) {
   constexpr int TPB = kBlock / (N / kElemsPerLane);
   const int64_t blocks = (a.n_tiles + TPB - 1) / TPB;
   dim3 grid((unsigned)blocks), block(kBlock);
-  if (a.dither) {
+  if (a.wide) {
+    if (a.dither) return hipErrorInvalidValue;
+    if (a.out_bf16)
+      hipLaunchKernelGGL((decode_kernel<LAT, N, true, false, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<LAT, N, false, false, true>), grid, block, 0, s, a);
+  } else if (a.dither) {
     if constexpr (LAT != 8) {
       return hipErrorInvalidValue;
     } else {
       if (a.out_bf16)
-        hipLaunchKernelGGL((decode_kernel<LAT, N, true, true>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((decode_kernel<LAT, N, true, true, false>), grid, block, 0, s, a);
       else
-        hipLaunchKernelGGL((decode_kernel<LAT, N, false, true>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((decode_kernel<LAT, N, false, true, false>), grid, block, 0, s, a);
     }
   } else {
     if (a.out_bf16)
-      hipLaunchKernelGGL((decode_kernel<LAT, N, true, false>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((decode_kernel<LAT, N, true, false, false>), grid, block, 0, s, a);
     else
-      hipLaunchKernelGGL((decode_kernel<LAT, N, false, false>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((decode_kernel<LAT, N, false, false, false>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }

@@ -22,6 +22,9 @@ constexpr int32_t kOne = 1 << 24;    // 1.0 in quantizer-grid units
 constexpr int32_t kHalf = 1 << 23;   // 0.5
 // |U| is clamped here (u = +-124); rne_grid below needs |U| + 2^25 < 2^31.
 constexpr double kUClamp = 2080374784.0;   // 2^31 - 2^26
+// The int16 index mode holds U in 64 bits and clamps at u = +-32000, where
+// every index still fits int16.
+constexpr double kUClamp16 = 536870912000.0;   // 32000 2^24
 
 // SplitMix64 output function (Steele, Lea & Flood, OOPSLA 2014) applied to a
 // counter key: the randomness the method draws (RHT signs, KV dither).
@@ -36,12 +39,15 @@ __device__ inline int32_t shl24(int32_t a) {
   return (int32_t)((uint32_t)a << 24);
 }
 
-// a = rne(U / 2^24) (ties to even), R = U - a 2^24, |R| <= 2^23.
-__device__ inline int32_t rne_grid(int32_t U, int32_t& R) {
-  int32_t t = U + 0x7FFFFF + ((U >> 24) & 1);
-  int32_t a = t >> 24;
-  R = U - shl24(a);
-  return a;
+// a = rne(U / 2^24) (ties to even), R = U - a 2^24, |R| <= 2^23.  GI is the
+// grid's integer type: int32_t, or int64_t in the int16 index mode (a fits
+// int32 either way).
+template <typename GI>
+__device__ inline int32_t rne_grid(GI U, int32_t& R) {
+  const GI t = U + 0x7FFFFF + ((U >> 24) & 1);
+  const GI a = t >> 24;
+  R = (int32_t)(U - (GI)((uint64_t)(int64_t)a << 24));
+  return (int32_t)a;
 }
 
 __device__ inline int32_t iabs(int32_t v) { return v < 0 ? -v : v; }
@@ -49,8 +55,8 @@ __device__ inline int32_t iabs(int32_t v) { return v < 0 ? -v : v; }
 // Nearest point of D_m (m = 4 or 8) to U / 2^24: round half to even; on an
 // odd coordinate sum move the first coordinate of largest residual one step
 // towards U (+1 on a zero residual).  Textbook rule (Conway & Sloane 1982).
-template <int M>
-__device__ inline void d_round(const int32_t* U, int32_t* z) {
+template <int M, typename GI>
+__device__ inline void d_round(const GI* U, int32_t* z) {
   int32_t R[M];
   int32_t sum = 0, amax = -1, j = 0;
 #pragma unroll
@@ -74,7 +80,8 @@ __device__ inline void d_round(const int32_t* U, int32_t* z) {
 //                                 - [odd b](2^24 - 2 max B)
 // in grid units (a parity fix on coordinate j changes the squared distance by
 // 1 - 2|residual_j|).  Ties keep the integer coset.
-__device__ inline int e8_nearest(const int32_t* U, int32_t* z) {
+template <typename GI>
+__device__ inline int e8_nearest(const GI* U, int32_t* z) {
   int32_t a[8], RA[8], b[8], RB[8];
   int32_t sa = 0, sb = 0, sumA = 0, amax = -1, amin = 0x7FFFFFFF, ja = 0, jb = 0;
 #pragma unroll
@@ -106,7 +113,8 @@ __device__ inline int e8_nearest(const int32_t* U, int32_t* z) {
 // integer coset (rne, rne) vs half coset (rne(. - 1/2) + 1/2) under the
 // metric diag(1, 3); ties keep the integer coset.  Returns c; (a, b) are the
 // integer parts, the point is (a + c/2, sqrt3 (b + c/2)).
-__device__ inline int a2_nearest(int32_t U1, int32_t V2, int32_t& a, int32_t& b) {
+template <typename GI>
+__device__ inline int a2_nearest(GI U1, GI V2, int32_t& a, int32_t& b) {
   int32_t r1, r2, s1, s2;
   int32_t a0 = rne_grid(U1, r1), b0 = rne_grid(V2, r2);
   int32_t a1 = rne_grid(U1 - kHalf, s1), b1 = rne_grid(V2 - kHalf, s2);

@@ -727,11 +727,12 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
 }  // namespace
 
 bool e8_fast_encode_ok(const EncodeLaunch& a) {
-  return a.lattice == 8 && a.tile == 256 && a.in_bf16 && !a.dither && a.coords == nullptr;
+  return a.lattice == 8 && a.tile == 256 && a.in_bf16 && !a.dither && !a.wide &&
+         a.coords == nullptr;
 }
 
 bool e8_fast_decode_ok(const DecodeLaunch& a) {
-  return a.lattice == 8 && a.tile == 256 && !a.dither;
+  return a.lattice == 8 && a.tile == 256 && !a.dither && !a.wide;
 }
 
 

@@ -12,6 +12,8 @@
 // covers 64/G whole tiles.  The first four Hadamard stages run inside a lane,
 // the remaining log2(G) across the lane group.  Butterflies run in fp64 and
 // are exact for bf16 tiles (every partial sum fits in 53 bits).
+#include <type_traits>
+
 #include "hq.h"
 #include "hq_device.h"
 #include "hq_internal.h"
@@ -76,26 +78,27 @@ __device__ inline uint32_t lane_sign_mask(const EncodeLaunch& a, int r) {
 }
 
 // Quantizer input on the 2^-24 grid for 16 rotated values: U = rne(S K)
-// (A2: odd coordinates with K3); magnitudes past kUClamp flag an overflow.
-template <int LAT>
-__device__ inline void grid_values(const double* v, double K, double K3, int32_t* U,
-                                   uint32_t& st) {
+// (A2: odd coordinates with K3); magnitudes past the clamp (kUClamp, or
+// kUClamp16 for the 64-bit grid of the int16 index mode) flag an overflow.
+template <int LAT, typename GI>
+__device__ inline void grid_values(const double* v, double K, double K3, GI* U, uint32_t& st) {
+  constexpr double kClamp = sizeof(GI) == 8 ? kUClamp16 : kUClamp;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     double q = rint(__dmul_rn(v[i], (LAT == 2 && (i & 1)) ? K3 : K));
-    if (!(fabs(q) <= kUClamp)) {
+    if (!(fabs(q) <= kClamp)) {
       st |= HQ_ST_OVERFLOW;
-      q = (q > 0.0) ? kUClamp : -kUClamp;
+      q = (q > 0.0) ? kClamp : -kClamp;
     }
-    U[i] = (int32_t)q;
+    U[i] = (GI)q;
   }
 }
 
 // Nearest point and lossless strip of this lane's 16 grid values: stored
 // integers s, full coordinates crd (E8 and A2: 2p), coset bits of the
 // lane's blocks (E8) or pairs (A2).
-template <int LAT>
-__device__ inline void nearest_strip(const int32_t* U, int32_t* s, int16_t* crd, uint32_t& cbits) {
+template <int LAT, typename GI>
+__device__ inline void nearest_strip(const GI* U, int32_t* s, int16_t* crd, uint32_t& cbits) {
   cbits = 0;
   if constexpr (LAT == 8) {
 #pragma unroll
@@ -171,8 +174,47 @@ __device__ inline uint32_t rice_best(const int32_t* s, uint32_t& st, int& bk, ui
   return best;
 }
 
-template <int LAT, int N, bool IN_BF16, bool DITHER>
+// The same for int16 indices (zeta < 2^16, k in [0, 15]): the first minimum
+// is one of kt - 1, kt, kt + 1 with kt the smallest k with S <= N 2^(k+1)
+// (the argument of the int8 case; past k = 15 every zeta >> k is 0, so for
+// S > N 2^16 the minimum is k = 15).  Fills the lane's eight words of packed
+// int16 indices.
+template <int G, int N>
+__device__ inline uint32_t rice_best16(const int32_t* s, uint32_t& st, int& bk, uint32_t* packed) {
+  uint32_t zz[16], S = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (s[i] < -32768 || s[i] > 32767) st |= HQ_ST_OVERFLOW;
+    const int32_t s16 = (int32_t)(int16_t)s[i];
+    if (i & 1) packed[i >> 1] |= (uint32_t)s16 << 16;
+    else packed[i >> 1] = (uint32_t)s16 & 0xFFFFu;
+    zz[i] = zigzag(s16);
+    S += zz[i];
+  }
+  S = group_sum<G>(S);
+  int kt = 0;
+  while (kt < 15 && S > ((uint32_t)N << (kt + 1))) ++kt;
+  uint32_t best = 0xFFFFFFFFu;
+  bk = 0;
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    int k = kt - 1 + c;
+    k = k < 0 ? 0 : (k > 15 ? 15 : k);
+    uint32_t R = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) R += zz[i] & ((1u << k) - 1u);
+    R = group_sum<G>(R);
+    const uint32_t L = ((S - R) >> k) + (uint32_t)N * (uint32_t)(1 + k);
+    if (L < best) { best = L; bk = k; }
+  }
+  return best;
+}
+
+// WIDE: the int16 index mode (64-bit grid values, int16 indices; no dither,
+// no rate control).
+template <int LAT, int N, bool IN_BF16, bool DITHER, bool WIDE>
 __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeLaunch a) {
+  using GI = typename std::conditional<WIDE, int64_t, int32_t>::type;
   constexpr int G = N / kElemsPerLane;
   constexpr int TPB = kBlock / G;
   const int r = threadIdx.x % G;
@@ -228,7 +270,7 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeLaunch a) {
   // ---- per-tile rate control: the finest bf16 scale, by bisection on its
   // bit pattern within eight binades of the automatic one, at which the
   // indices fit int8 and the tile fits the budget (every decision integer)
-  if constexpr (!DITHER) {
+  if constexpr (!DITHER && !WIDE) {
     if (a.rate_control && group_or<G>(st) == 0u && ss > 0.0) {   // group-uniform
       auto feasible = [&](uint32_t code) {
         const double tq = a.sqrt_n * (double)__uint_as_float(code << 16);
@@ -263,10 +305,10 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeLaunch a) {
   const double K3 = 16777216.0 / (t * 1.7320508075688772);
 
   // ---- quantizer input on the 2^-24 grid
-  int32_t U[16];
+  GI U[16];
   grid_values<LAT>(v, K, K3, U, st);
 
-  if constexpr (DITHER) {
+  if constexpr (DITHER && !WIDE) {
     // d = w - Q_E8(w), w = 2^-23 h - 1 with h the top 24 bits of the hash
     const uint64_t vec = (uint64_t)(a.dither_base + tile);
     int32_t W[16], Z[8];
@@ -291,10 +333,19 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeLaunch a) {
   int16_t crd[16];
   uint32_t cbits;
   nearest_strip<LAT>(U, s, crd, cbits);
-  uint32_t packed[4];
   int bk;
-  const uint32_t best = rice_best<G, N>(s, st, bk, packed);
-  *reinterpret_cast<uint4*>(a.idx + e0) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  uint32_t best;
+  if constexpr (WIDE) {
+    uint32_t packed[8];
+    best = rice_best16<G, N>(s, st, bk, packed);
+    uint4* ip = reinterpret_cast<uint4*>(reinterpret_cast<int16_t*>(a.idx) + e0);
+    ip[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    ip[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+  } else {
+    uint32_t packed[4];
+    best = rice_best<G, N>(s, st, bk, packed);
+    *reinterpret_cast<uint4*>(a.idx + e0) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  }
   if (a.coords != nullptr) {
     uint32_t cw[8];
 #pragma unroll
@@ -330,20 +381,26 @@ hipError_t launch_lat_n(const EncodeLaunch& a, hipStream_t s) {
   constexpr int TPB = kBlock / (N / kElemsPerLane);
   const int64_t blocks = (a.n_tiles + TPB - 1) / TPB;
   dim3 grid((unsigned)blocks), block(kBlock);
-  if (a.dither) {
+  if (a.wide) {
+    if (a.dither || a.rate_control) return hipErrorInvalidValue;
+    if (a.in_bf16)
+      hipLaunchKernelGGL((encode_kernel<LAT, N, true, false, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((encode_kernel<LAT, N, false, false, true>), grid, block, 0, s, a);
+  } else if (a.dither) {
     if constexpr (LAT != 8) {
       return hipErrorInvalidValue;
     } else {
       if (a.in_bf16)
-        hipLaunchKernelGGL((encode_kernel<LAT, N, true, true>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((encode_kernel<LAT, N, true, true, false>), grid, block, 0, s, a);
       else
-        hipLaunchKernelGGL((encode_kernel<LAT, N, false, true>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((encode_kernel<LAT, N, false, true, false>), grid, block, 0, s, a);
     }
   } else {
     if (a.in_bf16)
-      hipLaunchKernelGGL((encode_kernel<LAT, N, true, false>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((encode_kernel<LAT, N, true, false, false>), grid, block, 0, s, a);
     else
-      hipLaunchKernelGGL((encode_kernel<LAT, N, false, false>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((encode_kernel<LAT, N, false, false, false>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }

@@ -818,11 +818,12 @@ hipError_t launch_dec_lat(const DecodeLaunch& a, hipStream_t s) {
 }  // namespace
 
 bool fast128_encode_ok(const EncodeLaunch& a) {
-  return a.tile == 128 && a.in_bf16 && a.coords == nullptr && (a.lattice == 8 || !a.dither);
+  return a.tile == 128 && a.in_bf16 && a.coords == nullptr && !a.wide &&
+         (a.lattice == 8 || !a.dither);
 }
 
 bool fast128_decode_ok(const DecodeLaunch& a) {
-  return a.tile == 128 && (a.lattice == 8 || !a.dither);
+  return a.tile == 128 && !a.wide && (a.lattice == 8 || !a.dither);
 }
 
 hipError_t launch_encode_fast128(const EncodeLaunch& a, hipStream_t s) {

@@ -33,6 +33,7 @@ struct EncodeLaunch {
   int64_t dither_base;
   int rate_control;     // per-tile scales by bisection (generic kernel)
   uint32_t rc_budget;   // bits one tile may take: floor(bps * tile)
+  int wide;             // int16 index mode: idx holds int16 values (generic kernel)
 };
 
 // bf16 bit patterns the rate control searches on each side of the
@@ -54,6 +55,7 @@ struct DecodeLaunch {
   int dither;
   uint32_t dither_seed;
   int64_t dither_base;
+  int wide;             // int16 index mode: idx holds int16 values (generic kernel)
 };
 
 struct RateLaunch {
@@ -74,6 +76,7 @@ struct RateLaunch {
   uint64_t* wave_words;    // workspace: words per rate wave
   uint32_t* status;
   int given;               // rice_k and tile_bits are inputs (the encoder's)
+  int wide;                // int16 index mode: idx holds int16 values
 };
 
 // One packed matrix of an unpack launch; wave0 numbers its first wave (64
@@ -150,6 +153,7 @@ struct UnpackLaunch {
   int coset_words;      // per tile
   uint32_t* status;     // may be nullptr
   int64_t n_waves;      // waves of all items
+  int wide;             // int16 index mode: idx receives int16 values
   UnpackItem it[kUnpackMaxItems];
 };
 

@@ -99,6 +99,33 @@ __device__ inline uint4 load16(const int8_t* idx, int64_t e0) {
   return *reinterpret_cast<const uint4*>(idx + e0);
 }
 
+// A lane's 16 indices: 16 bytes (int8) or 32 bytes (int16 index mode).
+template <bool WIDE>
+struct LaneIdx {
+  uint4 q[WIDE ? 2 : 1];
+};
+
+template <bool WIDE>
+__device__ inline LaneIdx<WIDE> load_lane(const int8_t* idx, int64_t e0) {
+  LaneIdx<WIDE> v;
+  if constexpr (WIDE) {
+    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const int16_t*>(idx) + e0);
+    v.q[0] = p[0];
+    v.q[1] = p[1];
+  } else {
+    v.q[0] = load16(idx, e0);
+  }
+  return v;
+}
+
+// Zigzag of the 16 int16 values of a lane, one per dword.
+__device__ inline void zeta16(const LaneIdx<true>& v, uint32_t* zz) {
+  const uint32_t w[8] = {v.q[0].x, v.q[0].y, v.q[0].z, v.q[0].w,
+                         v.q[1].x, v.q[1].y, v.q[1].z, v.q[1].w};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) zz[i] = zigzag((int32_t)(int16_t)(w[i >> 1] >> (16 * (i & 1))));
+}
+
 // k = argmin_k L(k), L(k) = sum floor(zeta / 2^k) + N (1 + k), first minimum.
 // L is convex in k: L(k+1) - L(k) = N - D_k with D_k = sum floor((zeta + 2^k)
 // / 2^(k+1)) non-increasing in k and within N/2 of S / 2^(k+1), S = sum zeta.
@@ -123,6 +150,33 @@ __device__ inline uint32_t best_k(const uint32_t* zz, int& bk) {
     uint32_t R = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) R = byte_sum(zz[j] & mask, R);
+    R = row_sum<G>(R);
+    const uint32_t L = ((S - R) >> k) + (uint32_t)N * (uint32_t)(1 + k);
+    if (L < best) { best = L; bk = k; }
+  }
+  return best;
+}
+
+// The same for int16 indices (zeta < 2^16, one per dword; k in [0, 15]; for
+// S > N 2^16 every candidate clamps to k = 15, where every zeta >> k is 0 or 1
+// and D_15 <= N).
+template <int G, int N>
+__device__ inline uint32_t best_k16(const uint32_t* zz, int& bk) {
+  uint32_t S = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) S += zz[i];
+  S = row_sum<G>(S);
+  int kt = 0;
+  while (kt < 15 && S > ((uint32_t)N << (kt + 1))) ++kt;
+  uint32_t best = 0xFFFFFFFFu;
+  bk = 0;
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    int k = kt - 1 + c;
+    k = k < 0 ? 0 : (k > 15 ? 15 : k);
+    uint32_t R = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) R += zz[i] & ((1u << k) - 1u);
     R = row_sum<G>(R);
     const uint32_t L = ((S - R) >> k) + (uint32_t)N * (uint32_t)(1 + k);
     if (L < best) { best = L; bk = k; }
@@ -197,7 +251,7 @@ __device__ inline int rate_item(const RateBatch& b, int64_t& bx) {
   return i;
 }
 
-template <int N>
+template <int N, bool WIDE>
 __global__ __launch_bounds__(kBlock) void rate_kernel(RateBatch bt) {
   int64_t bx;
   const RateLaunch& a = bt.it[rate_item(bt, bx)];
@@ -217,17 +271,26 @@ __global__ __launch_bounds__(kBlock) void rate_kernel(RateBatch bt) {
   auto fetch = [&](int64_t t0) {
     const int64_t tile = t0 + lane / G;
     const int64_t tl = tile < end ? tile : end - 1;   // whole groups stay convergent
-    return load16(a.idx, tl * N + (int64_t)r * kElemsPerLane);
+    return load_lane<WIDE>(a.idx, tl * N + (int64_t)r * kElemsPerLane);
   };
-  uint4 nxt = first < end ? fetch(first) : make_uint4(0, 0, 0, 0);
+  LaneIdx<WIDE> nxt;
+  if (first < end) nxt = fetch(first);
   for (int64_t t0 = first; t0 < end; t0 += TPW) {
     const int64_t tile = t0 + lane / G;
     const bool live = tile < end;
-    uint32_t zz[4];
-    zeta4(nxt, zz);
-    if (t0 + TPW < end) nxt = fetch(t0 + TPW);
     int bk;
-    const uint32_t pay = best_k<G, N>(zz, bk);
+    uint32_t pay;
+    if constexpr (WIDE) {
+      uint32_t zz[16];
+      zeta16(nxt, zz);
+      if (t0 + TPW < end) nxt = fetch(t0 + TPW);
+      pay = best_k16<G, N>(zz, bk);
+    } else {
+      uint32_t zz[4];
+      zeta4(nxt.q[0], zz);
+      if (t0 + TPW < end) nxt = fetch(t0 + TPW);
+      pay = best_k<G, N>(zz, bk);
+    }
     const uint32_t tb = 4u + (uint32_t)a.coset_bits + pay;
     if (live && r == 0) {
       a.rice_k[tile] = (uint8_t)bk;
@@ -323,10 +386,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(RateBatch bt) {
   }
 }
 
-// Max words one tile can need: 4 + coset bits + 9 N (k = 8 bounds the optimum).
-template <int N>
+// Max words one tile can need: 4 + coset bits + 9 N (k = 8 bounds the
+// optimum: every zeta >> 8 is 0); int16 indices: 17 N (k = 15, zeta >> 15 <= 1).
+template <int N, bool WIDE>
 struct PackBound {
-  static constexpr int kMaxBits = 4 + N / 2 + 9 * N;
+  static constexpr int kMaxBits = 4 + N / 2 + (WIDE ? 17 : 9) * N;
   static constexpr int kWords = (kMaxBits + 31) / 32;
 };
 
@@ -357,20 +421,21 @@ struct BitWriter {
 
 // LDS words of one wave: its TPW tiles of at most W words each, plus a spare
 // word past the last tile (the two-word OR of a code may touch it).
-template <int N>
+template <int N, bool WIDE>
 constexpr int pack_lds_words() {
-  return 64 / (N / kElemsPerLane) * PackBound<N>::kWords + 1;
+  return 64 / (N / kElemsPerLane) * PackBound<N, WIDE>::kWords + 1;
 }
 
-template <int N>
+template <int N, bool WIDE>
 __global__ __launch_bounds__(kBlock) void pack_kernel(RateBatch bt) {
   int64_t bx;
   const RateLaunch& a = bt.it[rate_item(bt, bx)];
   if (a.stream == nullptr) return;          // the whole block: not packing
   constexpr int G = N / kElemsPerLane;
   constexpr int TPW = 64 / G;
-  constexpr int W = PackBound<N>::kWords;
-  __shared__ uint32_t lds[kBlock / 64][pack_lds_words<N>()];
+  constexpr int W = PackBound<N, WIDE>::kWords;
+  constexpr uint32_t kMaxK = WIDE ? 15u : 8u;   // the largest optimal k
+  __shared__ uint32_t lds[kBlock / 64][pack_lds_words<N, WIDE>()];
   const int lane = threadIdx.x & 63;
   const int r = lane % G;
   const int slot = lane / G;
@@ -385,14 +450,14 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(RateBatch bt) {
   uint64_t base = a.block_words[bx];
   for (int i = 0; i < (threadIdx.x >> 6); ++i) base += a.wave_words[bx * (kBlock / 64) + i];
   struct PassIn {
-    uint4 q;
+    LaneIdx<WIDE> q;
     uint32_t k, tb;
   };
   auto fetch = [&](int64_t t0, PassIn& in) {
     if (t0 < end) {   // wave-uniform
       const int64_t tile = t0 + slot;
       if (tile < end) {
-        in.q = load16(a.idx, tile * N + (int64_t)r * kElemsPerLane);
+        in.q = load_lane<WIDE>(a.idx, tile * N + (int64_t)r * kElemsPerLane);
         in.k = a.rice_k[tile];
         in.tb = a.tile_bits[tile];
       }
@@ -402,7 +467,6 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(RateBatch bt) {
     if (t0 >= end) return;   // wave-uniform
     const int64_t tile = t0 + slot;
     const bool live = tile < end;
-    const uint4 cq = in.q;
     const uint32_t ck = in.k, tb = live ? in.tb : 0u;
     // (given tile_bits past the tile's LDS words are clamped there; the
     // codes of such a tile are not written, see below)
@@ -423,22 +487,31 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(RateBatch bt) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // every lane runs the scan (DPP moves read neighbouring lanes)
     uint32_t k = 0;
-    uint32_t zz[4] = {0u, 0u, 0u, 0u};
+    // zigzag values: four per dword (int8) or one per dword (int16)
+    uint32_t zz[WIDE ? 16 : 4];
+#pragma unroll
+    for (int j = 0; j < (WIDE ? 16 : 4); ++j) zz[j] = 0u;
     if (live) {
-      k = ck < 8u ? ck : 8u;   // (a given k above 8 marks the tile corrupt below)
-      zeta4(cq, zz);
+      k = ck < kMaxK ? ck : kMaxK;   // (a given k above it marks the tile corrupt below)
+      if constexpr (WIDE) zeta16(in.q, zz);
+      else zeta4(in.q.q[0], zz);
     }
     // this lane's payload bits: sum floor(zeta / 2^k) + 16 (1 + k)
-    const uint32_t m = (0xFFu >> k) * 0x01010101u;
     uint32_t qs = 0;
+    if constexpr (WIDE) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) qs = byte_sum((zz[j] >> k) & m, qs);
+      for (int j = 0; j < 16; ++j) qs += zz[j] >> k;
+    } else {
+      const uint32_t m = (0xFFu >> k) * 0x01010101u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qs = byte_sum((zz[j] >> k) & m, qs);
+    }
     const uint32_t T = live ? qs + 16u * (1u + k) : 0u;
     const uint32_t pos = 4u + (uint32_t)a.coset_bits + row_incl_scan<G>(T, r) - T;
     // rice_k and tile_bits computed here always hold the codes; given ones
     // that do not (k > 8, or codes past tile_bits or past the tile's LDS
     // words) leave the lane's codes unwritten and mark the tile corrupt
-    const bool fits = !a.given || (ck <= 8u && pos + T <= tb && tb <= 32u * (uint32_t)W);
+    const bool fits = !a.given || (ck <= kMaxK && pos + T <= tb && tb <= 32u * (uint32_t)W);
     if (live && !fits) set_status(a.status, HQ_ST_CORRUPT);
     if (live) {
       if (r == 0) {
@@ -460,7 +533,7 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(RateBatch bt) {
         uint32_t pb = pos;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const uint32_t zeta = __builtin_amdgcn_ubfe(zz[i >> 2], 8 * (i & 3), 8);
+          const uint32_t zeta = WIDE ? zz[i] : __builtin_amdgcn_ubfe(zz[i >> 2], 8 * (i & 3), 8);
           const uint32_t q = zeta >> k, rem = zeta & rmask, len = q + 1u + k;
           if (len <= 32u) {
             // q ones, a zero, the k low bits: ((2 rem + 1) << q) - 1, at bit
@@ -513,8 +586,8 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(RateBatch bt) {
   }
 }
 
-template <int N>
-hipError_t launch_n(const RateBatch& b, hipStream_t s) {
+template <int N, bool WIDE>
+hipError_t launch_nw(const RateBatch& b, hipStream_t s) {
   const unsigned blocks = (unsigned)b.block0[b.n];
   bool atomics = false, given = false, pack = false;
   for (int i = 0; i < b.n; ++i) {
@@ -526,10 +599,16 @@ hipError_t launch_n(const RateBatch& b, hipStream_t s) {
   if (given)
     hipLaunchKernelGGL(rate_given_kernel<N>, dim3(blocks), dim3(kBlock), 0, s, b);
   else
-    hipLaunchKernelGGL(rate_kernel<N>, dim3(blocks), dim3(kBlock), 0, s, b);
+    hipLaunchKernelGGL((rate_kernel<N, WIDE>), dim3(blocks), dim3(kBlock), 0, s, b);
   hipLaunchKernelGGL(scan_kernel, dim3((unsigned)b.n), dim3(kScanThreads), 0, s, b);
-  if (pack) hipLaunchKernelGGL(pack_kernel<N>, dim3(blocks), dim3(kBlock), 0, s, b);
+  if (pack) hipLaunchKernelGGL((pack_kernel<N, WIDE>), dim3(blocks), dim3(kBlock), 0, s, b);
   return hipGetLastError();
+}
+
+// (the matrices of one launch share the index mode)
+template <int N>
+hipError_t launch_n(const RateBatch& b, hipStream_t s) {
+  return b.it[0].wide ? launch_nw<N, true>(b, s) : launch_nw<N, false>(b, s);
 }
 
 template <int N>

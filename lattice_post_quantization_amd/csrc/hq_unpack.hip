@@ -111,7 +111,7 @@ struct BitReader {
 // One Rice code: the zigzag value (garbage, with bad set, when the code runs
 // past the tile or exceeds a byte).
 template <bool FromLds>
-__device__ inline uint32_t read_code(BitReader<FromLds>& br, uint32_t k, bool& bad) {
+__device__ inline uint32_t read_code(BitReader<FromLds>& br, uint32_t k, uint32_t zmax, bool& bad) {
   br.refill();
   // first zero among the valid bits (bits above nb are zero, so ~b has ones
   // there and the count stops at nb at the latest)
@@ -127,7 +127,7 @@ __device__ inline uint32_t read_code(BitReader<FromLds>& br, uint32_t k, bool& b
       br.refill();
       const uint64_t iv = ~br.b;
       z = iv == 0 ? 64u : (uint32_t)__builtin_ctzll(iv);
-      if (br.nb == 0u || q > 255u) {
+      if (br.nb == 0u || q > zmax) {
         bad = true;
         z = 0;
         break;
@@ -142,7 +142,7 @@ __device__ inline uint32_t read_code(BitReader<FromLds>& br, uint32_t k, bool& b
   br.refill();
   bad |= br.nb < k;
   const uint32_t zeta = (q << k) | br.take(k);
-  bad |= zeta > 255u;
+  bad |= zeta > zmax;
   return zeta;
 }
 
@@ -194,7 +194,7 @@ struct LdsReader {
 // trailing zeros of x, 32 for x = 0 (one v_ffbl and a min)
 __device__ inline uint32_t ctz0(uint32_t x) { return x ? (uint32_t)__builtin_ctz(x) : 32u; }
 
-__device__ inline uint32_t read_code_lds(LdsReader& br, uint32_t k, bool& bad) {
+__device__ inline uint32_t read_code_lds(LdsReader& br, uint32_t k, uint32_t zmax, bool& bad) {
   br.refill();
   // the run of ones: the first zero of the 64-bit buffer, without a branch
   const uint32_t zl = ctz0(~(uint32_t)br.b), zh = 32u + ctz0(~(uint32_t)(br.b >> 32));
@@ -206,7 +206,7 @@ __device__ inline uint32_t read_code_lds(LdsReader& br, uint32_t k, bool& bad) {
     br.b = len >= 64u ? 0 : br.b >> len;
     br.nb -= len;
     const uint32_t zeta = (z << k) | rem;
-    bad |= zeta > 255u;
+    bad |= zeta > zmax;
     return zeta;
   }
   // slow path: the unary run or the remainder crosses the buffered bits
@@ -218,7 +218,7 @@ __device__ inline uint32_t read_code_lds(LdsReader& br, uint32_t k, bool& bad) {
     br.refill();
     const uint64_t iv = ~br.b;
     z = iv == 0 ? 64u : (uint32_t)__builtin_ctzll(iv);
-    if (br.nb == 0u || q > 255u) {
+    if (br.nb == 0u || q > zmax) {
       bad = true;
       z = 0;
       break;
@@ -231,29 +231,33 @@ __device__ inline uint32_t read_code_lds(LdsReader& br, uint32_t k, bool& bad) {
   br.refill();
   bad |= br.nb < k;
   const uint32_t zeta = (q << k) | br.take(k);
-  bad |= zeta > 255u;
+  bad |= zeta > zmax;
   return zeta;
 }
 
-__device__ inline uint32_t next_code(LdsReader& br, uint32_t k, bool& bad) {
-  return read_code_lds(br, k, bad);
+__device__ inline uint32_t next_code(LdsReader& br, uint32_t k, uint32_t zmax, bool& bad) {
+  return read_code_lds(br, k, zmax, bad);
 }
-__device__ inline uint32_t next_code(BitReader<false>& br, uint32_t k, bool& bad) {
-  return read_code(br, k, bad);
+__device__ inline uint32_t next_code(BitReader<false>& br, uint32_t k, uint32_t zmax, bool& bad) {
+  return read_code(br, k, zmax, bad);
 }
 
-// int8 index of a zigzag value (as a byte)
+// index of a zigzag value, as a byte (int8) or a half-word (int16)
 __device__ inline uint32_t unzigzag8(uint32_t zeta) {
   return ((zeta >> 1) ^ (0u - (zeta & 1u))) & 0xFFu;
+}
+__device__ inline uint32_t unzigzag16(uint32_t zeta) {
+  return ((zeta >> 1) ^ (0u - (zeta & 1u))) & 0xFFFFu;
 }
 
 constexpr int kUnpackBlock = 128;     // two waves
 constexpr int kSegWords = 2560;       // staged stream words per wave (10 KB)
 
 // Decodes this lane's tile and writes it through the wave's 4 KB LDS buffer
-// (64 bytes of each tile at a time; writer lane L keeps chunk c at slot
-// 4 L + ((c ^ (L >> 2)) & 3), so each 16-lane group writes 16 bank groups).
-template <int N, typename Reader>
+// (64 bytes of each tile at a time: 64 int8 or 32 int16 indices; writer lane
+// L keeps chunk c at slot 4 L + ((c ^ (L >> 2)) & 3), so each 16-lane group
+// writes 16 bank groups).
+template <int N, bool WIDE, typename Reader>
 __device__ inline void decode_tiles(const UnpackLaunch& a, const UnpackItem& it, Reader& br,
                                     int64_t tile, bool live, int64_t wave_tile0,
                                     uint32_t live_in_wave, int lane, uint4* st, bool& bad) {
@@ -269,17 +273,24 @@ __device__ inline void decode_tiles(const UnpackLaunch& a, const UnpackItem& it,
   }
   if (live && it.rice_k != nullptr) it.rice_k[tile] = (uint8_t)k;
 
-  const auto rs = out_rsrc(it.idx + wave_tile0 * N, live_in_wave * (uint32_t)N);
+  constexpr uint32_t kIdxBytes = WIDE ? 2u : 1u;
+  constexpr uint32_t kZmax = WIDE ? 65535u : 255u;
+  const auto rs = out_rsrc(it.idx + wave_tile0 * N * kIdxBytes, live_in_wave * (uint32_t)N * kIdxBytes);
 #pragma unroll 1
-  for (int part = 0; part < N / 64; ++part) {
+  for (int part = 0; part < N * (int)kIdxBytes / 64; ++part) {
 #pragma unroll 1
     for (int c = 0; c < 4; ++c) {
       uint32_t d[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         uint32_t w = 0;
+        if constexpr (WIDE) {
 #pragma unroll
-        for (int bi = 0; bi < 4; ++bi) w |= unzigzag8(next_code(br, k, bad)) << (8 * bi);
+          for (int hi = 0; hi < 2; ++hi) w |= unzigzag16(next_code(br, k, kZmax, bad)) << (16 * hi);
+        } else {
+#pragma unroll
+          for (int bi = 0; bi < 4; ++bi) w |= unzigzag8(next_code(br, k, kZmax, bad)) << (8 * bi);
+        }
         d[j] = w;
       }
       st[4 * lane + ((c ^ (lane >> 2)) & 3)] = make_uint4(d[0], d[1], d[2], d[3]);
@@ -291,14 +302,14 @@ __device__ inline void decode_tiles(const UnpackLaunch& a, const UnpackItem& it,
       const int T = 16 * j + (lane >> 2), cc = lane & 3;
       const uint4 q = st[4 * T + ((cc ^ (T >> 2)) & 3)];
       __builtin_amdgcn_raw_buffer_store_b128((u32x4){q.x, q.y, q.z, q.w}, rs,
-                                             T * N + part * 64 + 16 * cc, 0, 0);
+                                             T * N * (int)kIdxBytes + part * 64 + 16 * cc, 0, 0);
     }
     wave_lds_sync();
   }
   bad |= br.overran();
 }
 
-template <int N>
+template <int N, bool WIDE>
 __global__ __launch_bounds__(kUnpackBlock) void unpack_kernel(UnpackLaunch a) {
   __shared__ uint32_t seg[kUnpackBlock / 64][kSegWords];
   __shared__ uint4 stage[kUnpackBlock / 64][256];   // per wave: 4 chunks of 64 tiles
@@ -349,32 +360,38 @@ __global__ __launch_bounds__(kUnpackBlock) void unpack_kernel(UnpackLaunch a) {
     wave_lds_sync();
     LdsReader br;
     br.init(sw, (uint32_t)(w0 - seg_base), (uint32_t)(w1 - seg_base), nw > 0 ? nw : 1u);
-    decode_tiles<N>(a, it, br, tile, live, wave_tile0, live_in_wave, lane, stage[wave], bad);
+    decode_tiles<N, WIDE>(a, it, br, tile, live, wave_tile0, live_in_wave, lane, stage[wave], bad);
   } else {
     BitReader<false> br;
     br.init(it.stream, sw, seg_base, w0, w1);
-    decode_tiles<N>(a, it, br, tile, live, wave_tile0, live_in_wave, lane, stage[wave], bad);
+    decode_tiles<N, WIDE>(a, it, br, tile, live, wave_tile0, live_in_wave, lane, stage[wave], bad);
   }
   if (live && bad) set_status(a.status, HQ_ST_CORRUPT);
+}
+
+template <bool WIDE>
+void launch_unpack_w(const UnpackLaunch& a, int64_t blocks, hipStream_t s) {
+  switch (a.tile) {
+    case 64:
+      hipLaunchKernelGGL((unpack_kernel<64, WIDE>), dim3((unsigned)blocks), dim3(kUnpackBlock), 0, s, a);
+      break;
+    case 128:
+      hipLaunchKernelGGL((unpack_kernel<128, WIDE>), dim3((unsigned)blocks), dim3(kUnpackBlock), 0, s, a);
+      break;
+    case 256:
+      hipLaunchKernelGGL((unpack_kernel<256, WIDE>), dim3((unsigned)blocks), dim3(kUnpackBlock), 0, s, a);
+      break;
+    default:
+      hipLaunchKernelGGL((unpack_kernel<512, WIDE>), dim3((unsigned)blocks), dim3(kUnpackBlock), 0, s, a);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_unpack(const UnpackLaunch& a, hipStream_t s) {
   const int64_t blocks = (a.n_waves + kUnpackBlock / 64 - 1) / (kUnpackBlock / 64);
-  switch (a.tile) {
-    case 64:
-      hipLaunchKernelGGL(unpack_kernel<64>, dim3((unsigned)blocks), dim3(kUnpackBlock), 0, s, a);
-      break;
-    case 128:
-      hipLaunchKernelGGL(unpack_kernel<128>, dim3((unsigned)blocks), dim3(kUnpackBlock), 0, s, a);
-      break;
-    case 256:
-      hipLaunchKernelGGL(unpack_kernel<256>, dim3((unsigned)blocks), dim3(kUnpackBlock), 0, s, a);
-      break;
-    default:
-      hipLaunchKernelGGL(unpack_kernel<512>, dim3((unsigned)blocks), dim3(kUnpackBlock), 0, s, a);
-  }
+  if (a.wide) launch_unpack_w<true>(a, blocks, s);
+  else launch_unpack_w<false>(a, blocks, s);
   return hipGetLastError();
 }
 

@@ -22,6 +22,7 @@ HQ_EIO, HQ_EFORMAT, HQ_ENOTFOUND = -5, -6, -7
 HQ_Z, HQ_A2, HQ_D4, HQ_E8 = 1, 2, 4, 8
 HQ_F32, HQ_BF16 = 0, 1
 HQ_SCALE_AUTO, HQ_DITHER, HQ_WANT_COORDS, HQ_RATE_CONTROL, HQ_RATE_GIVEN = 1, 2, 4, 8, 16
+HQ_IDX16 = 32
 HQ_ST_NONFINITE, HQ_ST_OVERFLOW, HQ_ST_STREAM_FULL, HQ_ST_CORRUPT = 1, 2, 4, 8
 
 LATTICES = {"E8": HQ_E8, "D4": HQ_D4, "A2": HQ_A2, "Z": HQ_Z}
@@ -201,17 +202,29 @@ def splitmix64(key):
     return int(lib().hq_splitmix64(int(key)))
 
 
+def _idx_flag(idx):
+    """HQ_IDX16 for int16 index tensors (the int16 index mode), else 0."""
+    if idx.dtype == torch.int16:
+        return HQ_IDX16
+    if idx.dtype != torch.int8:
+        raise TypeError("indices must be int8 (or int16 in the int16 index mode)")
+    return 0
+
+
 def hq_encode_tiles(x, lattice="E8", tile=256, bps=4.0, rht_seed=0, scale=None,
-                    want_coords=False, status=None, out=None, rate_control=False):
+                    want_coords=False, status=None, out=None, rate_control=False,
+                    idx16=False):
     """Encode a row-major (rows, cols) bf16/fp32 device matrix.
 
     scale=None selects auto scales (returned); otherwise a float32 device
     tensor of per-tile scales.  Returns a dict of device tensors: scale,
-    idx (int8, like x), coset (int32 words, (n_tiles, w)), rice_k (uint8),
-    tile_bits (int32 holding uint32), coords (int16, if requested).
-    `out` may supply preallocated tensors under the same keys.
+    idx (int8, like x; int16 with idx16), coset (int32 words, (n_tiles, w)),
+    rice_k (uint8), tile_bits (int32 holding uint32), coords (int16, if
+    requested).  `out` may supply preallocated tensors under the same keys.
     rate_control: per-tile scales so that each tile fits floor(bps * tile)
-    bits (auto scales only; the chosen scales are returned)."""
+    bits (auto scales only; the chosen scales are returned).
+    idx16: the int16 index mode (HQ_IDX16), for rates whose indices leave
+    int8."""
     _device_tensor(x, "x")
     if x.dim() != 2:
         raise ValueError("x must be 2-D (rows, cols)")
@@ -221,7 +234,7 @@ def hq_encode_tiles(x, lattice="E8", tile=256, bps=4.0, rht_seed=0, scale=None,
     w = coset_words(lattice, tile)
     o = dict(out or {})
     flags = ((HQ_SCALE_AUTO if scale is None else 0) | (HQ_WANT_COORDS if want_coords else 0) |
-             (HQ_RATE_CONTROL if rate_control else 0))
+             (HQ_RATE_CONTROL if rate_control else 0) | (HQ_IDX16 if idx16 else 0))
     if scale is None:
         scale = o.get("scale")
         if scale is None:
@@ -230,7 +243,9 @@ def hq_encode_tiles(x, lattice="E8", tile=256, bps=4.0, rht_seed=0, scale=None,
         _device_tensor(scale, "scale")
     idx = o.get("idx")
     if idx is None:
-        idx = torch.empty((rows, cols), dtype=torch.int8, device=dev)
+        idx = torch.empty((rows, cols), dtype=torch.int16 if idx16 else torch.int8, device=dev)
+    elif (idx.dtype == torch.int16) != bool(idx16):
+        raise TypeError("out['idx'] must be int16 exactly when idx16 is set")
     coset = o.get("coset")
     if coset is None:
         coset = torch.empty((n_tiles, max(w, 1)), dtype=torch.int32, device=dev)
@@ -259,14 +274,15 @@ def hq_encode_tiles(x, lattice="E8", tile=256, bps=4.0, rht_seed=0, scale=None,
 def hq_decode_tiles(idx, coset, scale, lattice="E8", tile=256, rht_seed=0,
                     out_dtype=torch.bfloat16, dither_seed=None, dither_base=0,
                     status=None, out=None):
-    """Decode stripped indices back to weights (rows, cols) of out_dtype."""
+    """Decode stripped indices back to weights (rows, cols) of out_dtype
+    (int16 indices select the int16 index mode)."""
     _device_tensor(idx, "idx")
     _device_tensor(scale, "scale")
     if coset is not None:
         _device_tensor(coset, "coset")
     rows, cols = idx.shape
     y = out if out is not None else torch.empty((rows, cols), dtype=out_dtype, device=idx.device)
-    flags = HQ_DITHER if dither_seed is not None else 0
+    flags = (HQ_DITHER if dither_seed is not None else 0) | _idx_flag(idx)
     p = make_params(lattice, tile, 4.0, rht_seed, flags,
                     0 if dither_seed is None else dither_seed, dither_base)
     code = lib().hq_decode_tiles(ctypes.byref(p), _ptr(idx), _ptr(coset), _ptr(scale), rows, cols,
@@ -286,7 +302,8 @@ def hq_rate(idx, coset, lattice="E8", tile=256, pack=False, capacity_words=None,
     tile_bits, as hq_encode_tiles returns): HQ_RATE_GIVEN, the rate pass
     then reads tile_bits instead of recomputing both from the indices.
     Returns dict: rice_k, tile_bits, total_bits (int64 device scalar) and, when
-    packing, stream (int32 words), tile_word_offset (int64, n_tiles + 1)."""
+    packing, stream (int32 words), tile_word_offset (int64, n_tiles + 1).
+    int16 indices select the int16 index mode."""
     _device_tensor(idx, "idx")
     dev = idx.device
     n_tiles = idx.numel() // tile
@@ -306,14 +323,17 @@ def hq_rate(idx, coset, lattice="E8", tile=256, pack=False, capacity_words=None,
     if pack:
         if capacity_words is None:
             # the optimal k never costs more than k = 8: 4 + coset + 9 n bits
-            capacity_words = n_tiles * ((4 + tile // 2 + 9 * tile + 31) // 32)
+            # (int16 indices: k = 15, 17 n bits)
+            per = 17 if idx.dtype == torch.int16 else 9
+            capacity_words = n_tiles * ((4 + tile // 2 + per * tile + 31) // 32)
         stream = o.get("stream")
         if stream is None:
             stream = torch.empty(max(int(capacity_words), 1), dtype=torch.int32, device=dev)
         offs = o.get("tile_word_offset")
         if offs is None:
             offs = torch.empty(n_tiles + 1, dtype=torch.int64, device=dev)
-    p = make_params(lattice, tile, 4.0, flags=HQ_RATE_GIVEN if given is not None else 0)
+    p = make_params(lattice, tile, 4.0,
+                    flags=(HQ_RATE_GIVEN if given is not None else 0) | _idx_flag(idx))
     if noalloc:
         # the library's static scratch stands in for the workspace
         ws = None
@@ -372,7 +392,8 @@ def hq_rate_batch(encs, lattice="E8", tile=256, pack=False, given=False, status=
         r = {"rice_k": rk, "tile_bits": tb, "total_bits": total}
         cap = 0
         if pack:
-            cap = n_tiles * ((4 + tile // 2 + 9 * tile + 31) // 32)
+            per = 17 if e["idx"].dtype == torch.int16 else 9
+            cap = n_tiles * ((4 + tile // 2 + per * tile + 31) // 32)
             r["stream"] = o.get("stream")
             if r["stream"] is None:
                 r["stream"] = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
@@ -387,17 +408,20 @@ def hq_rate_batch(encs, lattice="E8", tile=256, pack=False, given=False, status=
     nb = lib().hq_rate_batch_workspace_bytes(len(encs), ctypes.byref(items))
     ws = workspace if workspace is not None else torch.empty(max(nb, 16), dtype=torch.uint8,
                                                              device=dev)
-    p = make_params(lattice, tile, 4.0, flags=HQ_RATE_GIVEN if given else 0)
+    p = make_params(lattice, tile, 4.0,
+                    flags=(HQ_RATE_GIVEN if given else 0) | _idx_flag(encs[0]["idx"]))
     code = lib().hq_rate_batch(ctypes.byref(p), len(encs), ctypes.byref(items), _ptr(ws),
                                ws.numel(), _ptr(status), _stream(dev))
     _check(code, "hq_rate_batch")
     return res
 
 
-def hq_unpack(stream, tile_word_offset, lattice="E8", tile=256, status=None, out=None):
+def hq_unpack(stream, tile_word_offset, lattice="E8", tile=256, status=None, out=None,
+              idx16=False):
     """Decode a packed stream (as written by hq_rate) back to stripped
-    indices (n_tiles, tile) int8, coset words (n_tiles, words) int32 or None,
-    and rice_k (n_tiles,) uint8.  tile_word_offset: int64 (n_tiles + 1)."""
+    indices (n_tiles, tile) int8 (int16 with idx16), coset words
+    (n_tiles, words) int32 or None, and rice_k (n_tiles,) uint8.
+    tile_word_offset: int64 (n_tiles + 1)."""
     _device_tensor(stream, "stream")
     _device_tensor(tile_word_offset, "tile_word_offset")
     dev = stream.device
@@ -405,7 +429,7 @@ def hq_unpack(stream, tile_word_offset, lattice="E8", tile=256, status=None, out
     o = dict(out or {})
     idx = o.get("idx")
     if idx is None:
-        idx = torch.empty((n_tiles, tile), dtype=torch.int8, device=dev)
+        idx = torch.empty((n_tiles, tile), dtype=torch.int16 if idx16 else torch.int8, device=dev)
     nw = coset_words(lattice, tile)
     coset = o.get("coset")
     if coset is None and nw:
@@ -413,7 +437,7 @@ def hq_unpack(stream, tile_word_offset, lattice="E8", tile=256, status=None, out
     rice_k = o.get("rice_k")
     if rice_k is None:
         rice_k = torch.empty(n_tiles, dtype=torch.uint8, device=dev)
-    p = make_params(lattice, tile, 4.0)
+    p = make_params(lattice, tile, 4.0, flags=_idx_flag(idx))
     code = lib().hq_unpack(ctypes.byref(p), _ptr(stream), _ptr(tile_word_offset), n_tiles,
                            _ptr(idx), _ptr(coset if nw else None), _ptr(rice_k), _ptr(status),
                            _stream(dev))
@@ -488,11 +512,11 @@ class UnpackItem(ctypes.Structure):
                 ("coset", ctypes.c_void_p), ("rice_k", ctypes.c_void_p)]
 
 
-def hq_unpack_batch(packs, lattice="E8", tile=256, status=None, outs=None):
+def hq_unpack_batch(packs, lattice="E8", tile=256, status=None, outs=None, idx16=False):
     """hq_unpack for several packed matrices sharing lattice and tile, in one
     call (one launch per group of eight).  packs: dicts with "stream" and
     "tile_word_offset" (as hq_rate returns).  Returns a list of dicts like
-    hq_unpack's; outs may supply their tensors."""
+    hq_unpack's; outs may supply their tensors (int16 indices with idx16)."""
     nw = coset_words(lattice, tile)
     res, items = [], []
     dev = None
@@ -504,7 +528,10 @@ def hq_unpack_batch(packs, lattice="E8", tile=256, status=None, outs=None):
         o = dict((outs[i] if outs is not None else None) or {})
         idx = o.get("idx")
         if idx is None:
-            idx = torch.empty((n_tiles, tile), dtype=torch.int8, device=dev)
+            idx = torch.empty((n_tiles, tile), dtype=torch.int16 if idx16 else torch.int8,
+                              device=dev)
+        elif (idx.dtype == torch.int16) != bool(idx16):
+            raise TypeError("outs[%d]['idx'] must be int16 exactly when idx16 is set" % i)
         coset = o.get("coset")
         if coset is None and nw:
             coset = torch.empty((n_tiles, nw), dtype=torch.int32, device=dev)
@@ -517,7 +544,7 @@ def hq_unpack_batch(packs, lattice="E8", tile=256, status=None, outs=None):
     if not items:
         return res
     arr = (UnpackItem * len(items))(*items)
-    p = make_params(lattice, tile, 4.0)
+    p = make_params(lattice, tile, 4.0, flags=HQ_IDX16 if idx16 else 0)
     code = lib().hq_unpack_batch(ctypes.byref(p), len(items), arr, _ptr(status), _stream(dev))
     _check(code, "hq_unpack_batch")
     return res

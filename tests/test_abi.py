@@ -127,6 +127,49 @@ def test_range_bound_matches_the_oracle():
             assert (code == hq.HQ_ERANGE) == (not codec.index_range_ok(lat, n, bps)), (lat, n, bps)
 
 
+def test_idx16_validation_codes():
+    """The int16 index mode: the auto-scale bound moves to |u| <= 32000, the
+    dither, rate control and the int8-only calls refuse it."""
+    lib = hq.lib()
+    P = hq.make_params
+    auto, w = hq.HQ_SCALE_AUTO, hq.HQ_IDX16
+    # R = 6, 7, 8 pass the bound (validation goes on to the device check)
+    for lat, n in (("E8", 256), ("E8", 512), ("D4", 128), ("A2", 64), ("Z", 256)):
+        for bps in (6.0, 7.0, 8.0):
+            assert _enc(P(lat, n, bps, 0, auto | w), cols=n) == hq.HQ_EINVAL, (lat, n, bps)
+    assert _enc(P("E8", 256, 6.0, 0, auto | w | hq.HQ_DITHER, 1)) == hq.HQ_EUNSUPPORTED
+    assert _enc(P("E8", 256, 6.0, 0, auto | w | hq.HQ_RATE_CONTROL)) == hq.HQ_EUNSUPPORTED
+    pk = P("E8", 128, 6.0, 0, auto | w)
+    assert lib.hq_kv_encode(ctypes.byref(pk), FAKE, 1, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                            None) == hq.HQ_EUNSUPPORTED
+    # batches, GEMV, GEMM and KV scores take int8 indices only
+    items = (hq.EncodeItem * 1)()
+    items[0] = hq.EncodeItem(4096, 4, 256, 4096, 4096, 4096, 4096, 4096)
+    pw = P("E8", 256, 6.0, 0, auto | w)
+    assert lib.hq_encode_batch(ctypes.byref(pw), 1, 1, ctypes.byref(items), None,
+                               None) == hq.HQ_EUNSUPPORTED
+    d = (hq.DecodeItem * 1)()
+    d[0] = hq.DecodeItem(4096, 4096, 4096, 4, 256, 4096)
+    assert lib.hq_decode_batch(ctypes.byref(pw), 1, 1, ctypes.byref(d), None,
+                               None) == hq.HQ_EUNSUPPORTED
+    g = (hq.GemvItem * 1)()
+    g[0] = hq.GemvItem(FAKE, FAKE, FAKE, 256, 256, FAKE, FAKE)
+    assert lib.hq_gemv_batch(ctypes.byref(pw), 1, g, 1, FAKE, 1 << 20, None,
+                             None) == hq.HQ_EUNSUPPORTED
+    assert lib.hq_gemm_batch(ctypes.byref(pw), 1, g, 16, FAKE, 1 << 20, None,
+                             None) == hq.HQ_EUNSUPPORTED
+    ps = P("E8", 128, 6.0, 0, w)
+    assert lib.hq_kv_scores(ctypes.byref(ps), FAKE, 4, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 1 << 20,
+                            None) == hq.HQ_EUNSUPPORTED
+    # decode, rate and unpack accept it (host pointers then fail the device check)
+    assert lib.hq_decode_tiles(ctypes.byref(pw), FAKE, FAKE, FAKE, 2, 256, FAKE, 1, None,
+                               None) == hq.HQ_EINVAL
+    assert lib.hq_rate(ctypes.byref(pw), FAKE, FAKE, 10, FAKE, FAKE, FAKE, None, 0, None, None,
+                       0, None, None) == hq.HQ_EINVAL
+    assert lib.hq_unpack(ctypes.byref(pw), FAKE, FAKE, 4, FAKE, FAKE, None, None,
+                         None) == hq.HQ_EINVAL
+
+
 def test_host_pointers_are_rejected():
     # a well-formed call whose buffers are not device memory returns EINVAL
     host = np.zeros(4096, np.uint8)

@@ -79,9 +79,10 @@ def check_encode(x_host, x_dev, lattice, n, bps, seed, tiles=None, label=""):
     return ora
 
 
-def check_decode(ora, lattice, n, seed, label="", exact=True, dither_seed=None, dither_base=0):
+def check_decode(ora, lattice, n, seed, label="", exact=True, dither_seed=None, dither_base=0,
+                 wide=False):
     Tn = ora["idx"].shape[0]
-    idx = torch.from_numpy(ora["idx"].astype(np.int8)).cuda()
+    idx = torch.from_numpy(ora["idx"].astype(np.int16 if wide else np.int8)).cuda()
     cw = ora["coset"].astype(np.uint32)
     coset = torch.from_numpy(cw.view(np.int32)).cuda() if cw.size else None
     scale = torch.from_numpy(ora["scale"].astype(np.float32)).cuda()
@@ -95,8 +96,8 @@ def check_decode(ora, lattice, n, seed, label="", exact=True, dither_seed=None, 
         T.compare_decoded(g, o, raw, ora["scale"], bf, exact, "%s decode %s" % (label, out_dtype))
 
 
-def check_rate(ora, lattice, n, label=""):
-    idx = torch.from_numpy(ora["idx"].astype(np.int8)).cuda()
+def check_rate(ora, lattice, n, label="", wide=False):
+    idx = torch.from_numpy(ora["idx"].astype(np.int16 if wide else np.int8)).cuda()
     cw = ora["coset"].astype(np.uint32)
     coset = torch.from_numpy(cw.view(np.int32)).cuda() if cw.size else None
     r = hq.hq_rate(idx, coset, lattice, n, pack=True)
@@ -158,6 +159,104 @@ def test_lattices_tile_sizes_ragged(lattice, n, dtype):
         ora = check_encode(xh, xd, lattice, n, bps, 7, label=label)
         check_decode(ora, lattice, n, 7, label, exact=(lattice != "A2"))
         check_rate(ora, lattice, n, label)
+
+
+def _spike_tiles(n, seed, count):
+    """Tiles whose rotation is a single spike of height sqrt(n) (x = s . H
+    row i, so H(s x) = n e_i): the largest |u| the auto scale allows,
+    sqrt(n) / c(L, R), reached by one coordinate."""
+    from oracle import hadamard, splitmix
+    s = splitmix.rht_signs(seed, n)
+    H = hadamard.sylvester(n)
+    rows = [s * H[(37 * i + 5) % n] * (1.0 + 0.25 * i) for i in range(count)]
+    return np.asarray(rows)
+
+
+@pytest.mark.parametrize("lattice,n,bps", [("E8", 256, 6.0), ("E8", 256, 7.0), ("E8", 128, 6.0),
+                                           ("E8", 128, 7.0), ("D4", 128, 6.0), ("A2", 128, 7.0),
+                                           ("Z", 256, 6.0), ("E8", 512, 6.0)])
+def test_idx16_mode_parity(lattice, n, bps):
+    """The int16 index mode (HQ_IDX16) at rates whose indices leave int8:
+    a ragged bf16 matrix with an outlier column and spike tiles (one rotated
+    coordinate at sqrt(n)/c), encode (both kernel paths of the generic
+    encoder), decode, rate + pack and unpack against the oracle."""
+    rows, cols = 37, 6 * n
+    rng = np.random.default_rng(23)
+    w = rng.standard_normal((rows, cols)) * 0.02
+    w[:, 5] *= 300.0
+    w.reshape(-1, n)[:8] = _spike_tiles(n, 9, 8) * 0.02
+    bits = workloads.f32_to_bf16_bits(w.astype(np.float32))
+    xh = workloads.bf16_bits_to_f64(bits)
+    xd = T.bf16_device(bits, (rows, cols))
+    label = "idx16 %s/%d R=%g" % (lattice, n, bps)
+    say("case:", label)
+    X = codec.tiles(xh, n)
+    ora = codec.encode(X, lattice, n, bps, rht_seed=9)
+    assert np.abs(ora["idx"]).max() > 127            # the mode is needed
+    assert np.abs(ora["idx"]).max() <= 32767
+    skip = midpoint_close(oracle_pre_scale(X, lattice, bps))
+    for coords in (False, True):
+        g = hq.hq_encode_tiles(xd, lattice, n, bps, 9, want_coords=coords, idx16=True)
+        torch.cuda.synchronize()
+        assert g["idx"].dtype == torch.int16
+        gs = T.host(g["scale"]).astype(np.float64)
+        assert np.array_equal(gs[~skip], ora["scale"][~skip]), label
+        keep = np.nonzero(gs == ora["scale"])[0]
+        sub = {k: (v[keep] if isinstance(v, np.ndarray) and v.shape[:1] == (len(X),) else v)
+               for k, v in ora.items()}
+        gi = T.host(g["idx"]).reshape(-1, n)[keep]
+        gc = T.u32(g["coset"]).reshape(len(X), -1)[keep]
+        bad, near, total, ok = T.compare_indices(gi, gc, sub, lattice, n, label)
+        assert np.array_equal(T.host(g["rice_k"])[keep][ok], sub["rice_k"][ok]), label
+        assert np.array_equal(T.u32(g["tile_bits"])[keep][ok], sub["tile_bits"][ok]), label
+        if coords:
+            gco = T.host(g["coords"]).reshape(-1, n)[keep]
+            assert np.array_equal(gco[ok], sub["coords"][ok]), label + " coords"
+        say("  %s: blocks %d, mismatches %d, near-ties %d, max |idx| %d"
+            % ("coords" if coords else "plain", total, bad, near, int(np.abs(ora["idx"]).max())))
+    check_decode(ora, lattice, n, 9, label, exact=(lattice != "A2"), wide=True)
+    check_rate(ora, lattice, n, label, wide=True)
+    # the packed stream back through the stream decoder
+    idx = torch.from_numpy(ora["idx"].astype(np.int16)).cuda()
+    cw = ora["coset"].astype(np.uint32)
+    coset = torch.from_numpy(cw.view(np.int32)).cuda() if cw.size else None
+    r = hq.hq_rate(idx, coset, lattice, n, pack=True)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    u = hq.hq_unpack(r["stream"], r["tile_word_offset"], lattice, n, status=st, idx16=True)
+    torch.cuda.synchronize()
+    assert int(T.host(st)[0]) == 0, label + " unpack status"
+    assert np.array_equal(T.host(u["idx"]).astype(np.int64), ora["idx"]), label + " unpack idx"
+    if cw.size:
+        assert np.array_equal(T.u32(u["coset"]), cw), label + " unpack coset"
+    assert np.array_equal(T.host(u["rice_k"]).astype(np.int64), ora["rice_k"]), label + " unpack k"
+
+
+def test_idx16_caller_scale_clamp():
+    """With a caller scale far below the auto one, grid values pass the
+    int16 mode's clamp (|u| = 32000): the tile's status flags the overflow,
+    as the oracle's indices leave int16 there."""
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((4, 256)) * 0.02).astype(np.float32)
+    xd = T.f32_device(w)
+    scale = torch.full((4,), 1e-7, dtype=torch.float32, device="cuda")
+    scale[1:] = 1e-3
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    hq.hq_encode_tiles(xd, "E8", 256, 6.0, 1, scale=scale, status=st, idx16=True)
+    torch.cuda.synchronize()
+    ora = codec.encode(w.astype(np.float64), "E8", 256, 6.0, rht_seed=1,
+                       scale=T.host(scale).astype(np.float64))
+    big = np.abs(ora["idx"]).max(axis=1) > 32767
+    assert big[0] and not big[1:].any()
+    assert int(T.host(st)[0]) & hq.HQ_ST_OVERFLOW
+    # the tiles inside the range match the oracle
+    st.zero_()
+    g = hq.hq_encode_tiles(xd[1:], "E8", 256, 6.0, 1, scale=scale[1:], status=st, idx16=True)
+    torch.cuda.synchronize()
+    assert int(T.host(st)[0]) == 0
+    sub = {k: (v[1:] if isinstance(v, np.ndarray) and v.shape[:1] == (4,) else v)
+           for k, v in ora.items()}
+    T.compare_indices(T.host(g["idx"]).reshape(-1, 256), T.u32(g["coset"]), sub, "E8", 256,
+                      "idx16 caller scale")
 
 
 @pytest.mark.parametrize("bps", [3.0, 4.0, 5.0])
