@@ -217,6 +217,10 @@ def kv_per_vector(kcache, bps, dev, n_vec=64, n_seeds=1024):
     uniform on the E8 cell scaled by Delta: z = mean error / (Delta
     sqrt(G / S)) is standard per coordinate and MSE / (G Delta^2) = 1;
     rotation-only errors stay fixed, so their z grows as sqrt(S)."""
+    import torch
+
+    from lattice_post_quantization_amd import hq
+
     g_e8 = 929.0 / 12960.0            # normalized second moment of E8 (Conway-Sloane)
     xd = kcache[torch.arange(n_vec, device=dev) * 4096].contiguous()
     x = xd.double()
@@ -438,7 +442,8 @@ def secondary(layer0, bps, dev):
 
     ms_e512, ms_d512 = time_calls(enc512, 5), time_calls(dec512, 5)
     variants = {
-        "workload": "the same layer's seven matrices (bf16) through the generic kernels",
+        "workload": "the same layer's seven matrices (bf16): per-tile rate control (fast E8 "
+                    "kernel), tile 512 (generic kernels)",
         "rate_control_encode_us": round(ms_rc * 1e3, 1),
         "rate_control_bits_per_weight": round(rc_bits, 4),
         "tile512_encode_us": round(ms_e512 * 1e3, 1), "tile512_decode_us": round(ms_d512 * 1e3, 1),

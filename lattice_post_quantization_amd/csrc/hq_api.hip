@@ -343,7 +343,8 @@ EncodeLaunch encode_launch(const hq_params* p, int32_t x_dtype, uint32_t* status
   return a;
 }
 
-bool encode_batch_fast(const EncodeLaunch& a) { return !a.rate_control && e8_fast_encode_ok(a); }
+// the fast E8 encoder (with or without the per-tile rate control)
+bool encode_batch_fast(const EncodeLaunch& a) { return e8_fast_encode_ok(a); }
 
 // Launch groups of the fast encoder: up to kMaxItems non-empty matrices each.
 // Calls emit(batch) per group; returns false when a launch fails.
@@ -554,8 +555,9 @@ hq_status hq_encode_decode_batch(const hq_params* enc_p, int32_t x_dtype, int32_
   const DecodeLaunch ad = decode_launch(dec_p, y_dtype, status);
   const int32_t le = live_items(enc_p, enc_count, enc_items);
   const int32_t ld = live_items(dec_p, dec_count, dec_items);
-  if (encode_batch_fast(a) && e8_fast_decode_ok(ad) && le <= kMaxItems && ld <= kMaxItems &&
-      le + ld > 0) {
+  // (the fused kernel encodes without rate control)
+  if (!a.rate_control && encode_batch_fast(a) && e8_fast_decode_ok(ad) && le <= kMaxItems &&
+      ld <= kMaxItems && le + ld > 0) {
     EncBatch b;
     DecBatch bd;
     memset(&b, 0, sizeof(b));

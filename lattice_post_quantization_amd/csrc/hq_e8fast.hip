@@ -107,8 +107,140 @@ __device__ inline uint32_t row0_offset(int t, int row, int size) {
   return row == 0 ? (uint32_t)(t * size) : 0x40000000u;
 }
 
+// E8 decisions of a lane's 64 rotated values (eight blocks) at grid factor
+// K: the stored integers as 16 dwords of int8 (block blk in dwords 2 blk,
+// 2 blk + 1) and the coset bit of block blk at bit blk.  Grid values
+// |S K| <= 124 2^24 (no tile of the wave past the clamp).  Lanes with live
+// false skip the search of boundary blocks (their results are not used).
+__device__ inline uint32_t e8_lane(const double* v, double K, uint32_t* packed, bool live) {
+  uint32_t cb = 0, ties = 0;
+  int32_t U[64];
+#pragma unroll
+  for (int blk = 0; blk < 8; ++blk) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      // two roundings, never fused: q = RN(S K), then RN(q + 1.5 2^52)
+      const double m = __dadd_rn(__dmul_rn(v[8 * blk + i], K), kMagic);
+      U[8 * blk + i] = (int32_t)(uint32_t)(uint64_t)__double_as_longlong(m);
+    }
+    int c;
+    ties |= e8_block_fast(U + 8 * blk, packed[2 * blk], packed[2 * blk + 1], c) << blk;
+    cb |= (uint32_t)c << blk;
+  }
+  if (ties && live) {
+    // blocks with a coordinate exactly on a rounding boundary
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) {
+      if ((ties >> blk) & 1u) {
+        const int c = e8_block_exact(U + 8 * blk, packed[2 * blk], packed[2 * blk + 1]);
+        cb = (cb & ~(1u << blk)) | ((uint32_t)c << blk);
+      }
+    }
+  }
+  return cb;
+}
+
+// Rice parameter and payload bits of the tile whose indices the four rows'
+// lanes hold (16 dwords of int8 each).  k = argmin_k L(k),
+// L(k) = Q_k + 256 (1 + k), Q_k = sum floor(zeta / 2^k).  L is convex:
+// L(k+1) - L(k) = 256 - D_k with D_k = Q_k - Q_{k+1} = sum floor((zeta +
+// 2^k) / 2^(k+1)), which falls with k, so the first minimum is the smallest
+// k with D_k <= 256.  D_k lies within 128 of S / 2^(k+1) (S = sum zeta), so
+// with kt the smallest k with S <= 256 * 2^(k+1): D_{kt+1} <= 256, and
+// D_k > 256 for k <= kt - 2 (strictly, so no smaller k ties).  Only
+// kt - 1, kt, kt + 1 remain.
+__device__ inline uint32_t rice_tile(const uint32_t* packed, int& bk) {
+  uint32_t zz[16];
+  uint32_t S = 0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    zz[q] = zigzag4(packed[q]);
+    S = byte_sum(zz[q], S);
+  }
+  S = tile_sum_u32(S);
+  int kt = 0;
+  while (kt < 8 && S > (256u << (kt + 1))) ++kt;
+  int kc[3];
+  uint32_t R[3];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    int k = kt - 1 + j;
+    kc[j] = k < 0 ? 0 : (k > 8 ? 8 : k);
+    const uint32_t mask = ((1u << kc[j]) - 1u) * 0x01010101u;
+    uint32_t r = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) r = byte_sum(zz[q] & mask, r);
+    R[j] = r;
+  }
+  uint32_t best = 0xFFFFFFFFu;
+  bk = 0;
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const uint32_t Rk = tile_sum_u32(R[j]);
+    const uint32_t L = ((S - Rk) >> kc[j]) + 256u * (uint32_t)(1 + kc[j]);
+    if (L < best) { best = L; bk = kc[j]; }
+  }
+  return best;
+}
+
+__device__ inline double tile_max_f64(double v) {
+  double a = v, b = v;
+  swap_f64<false>(a, b);
+  v = fmax(a, b);
+  a = v;
+  b = v;
+  swap_f64<true>(a, b);
+  return fmax(a, b);
+}
+
+// Per-tile rate control (reading R7: the finest bf16 scale, by bisection on
+// its bit pattern within eight binades of the automatic one, at which the
+// tile's indices stay inside the grid's clamp, hence int8, and its bits fit
+// floor(R n)).  The probes of every tile follow the same rule as the
+// generic kernel's; a probe whose largest grid value would pass the clamp
+// (rint(max|S| K) > 124 2^24, the largest of the generic kernel's clamped
+// values) is infeasible without a decision.  Returns the chosen scale
+// (delta unchanged for a tile that is not searched).
+__device__ inline float rc_search(const EncodeLaunch& a, const double* v, double ss, float delta,
+                                  bool searched) {
+  double m = 0.0;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) m = fmax(m, fabs(v[i]));
+  const double vmax = tile_max_f64(m);
+  const int32_t ac = (int32_t)(__float_as_uint(delta) >> 16);
+  int32_t lo = ac - kRcSpan > 0x0080 ? ac - kRcSpan : 0x0080;
+  int32_t hi = ac + kRcSpan < 0x7F7F ? ac + kRcSpan : 0x7F7F;
+  int32_t probe = hi;
+  bool top = true, active = searched && ss > 0.0;
+  while (__builtin_amdgcn_ballot_w64(active) != 0) {
+    const double tq = a.sqrt_n * (double)__uint_as_float((uint32_t)probe << 16);
+    const double K = 16777216.0 / tq;
+    // (lanes of finished tiles and of probes past the clamp decide on
+    // values whose results are not used)
+    const bool in_range = rint(__dmul_rn(vmax, K)) <= kUClamp;
+    uint32_t packed[16];
+    (void)e8_lane(v, K, packed, active && in_range);
+    int bk;
+    const uint32_t bits = 4u + 32u + rice_tile(packed, bk);
+    const bool f = in_range && bits <= a.rc_budget;
+    if (active) {
+      if (top && !f) {
+        active = false;
+      } else {
+        if (!top) (f ? hi : lo) = probe;
+        if (hi - lo <= 1) active = false;
+        probe = (lo + hi) / 2;
+      }
+      top = false;
+    }
+  }
+  return searched && ss > 0.0 ? __uint_as_float((uint32_t)hi << 16) : delta;
+}
+
 // One group of 16 tiles held by a wave (w: this lane's 64 bf16 of its tile).
 // (scale_in: the caller's scale of this lane's tile when not automatic.)
+// RC: per-tile rate control (auto scales only).
+template <bool RC>
 __device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const uint32_t* sign_tab,
                                  int64_t group, int t, int row, const uint32_t* w, float scale_in,
                                  uint4* ost) {
@@ -146,7 +278,7 @@ __device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const
   }
   if (!isfinite(ss)) status |= HQ_ST_NONFINITE;
   // |u_i| <= sqrt(sum x^2) / Delta: below 124 no grid value reaches the clamp
-  const bool big = !(sqrt(ss) < 124.0 * (double)delta);
+  bool big = !(sqrt(ss) < 124.0 * (double)delta);
   double K = 16777216.0 / (a.sqrt_n * (double)delta);
 
   // ---- Walsh-Hadamard: element bits 0-5 in registers
@@ -181,6 +313,11 @@ __device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const
   }
   // Now register i holds element bits (i0 i1 i2 i3 | i4 = b7 | i5 = b6) and the
   // lane's row bits hold (r0 = b5, r1 = b4).
+  if constexpr (RC) {
+    delta = rc_search(a, v, ss, delta, status == 0u);
+    big = !(sqrt(ss) < 124.0 * (double)delta);
+    K = 16777216.0 / (a.sqrt_n * (double)delta);
+  }
 
   // When some tile of the wave may pass the clamp, the generic encoder's
   // clamped rint(S K) replaces S (and K becomes 1).
@@ -199,35 +336,14 @@ __device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const
 
   // ---- quantizer input U = rne(S K) (units of 2^-24), stored integers
   uint32_t packed[16];
-  uint32_t cbits = 0, ties = 0;
-  int32_t U[64];
+  const uint32_t cb = e8_lane(v, K, packed, true);
   const int r0 = row & 1, r1 = row >> 1;
   // tile block index of register block blk = b3 + 2 b4 + 4 b5 + 8 b6 + 16 b7
-  auto bpos = [&](int blk) {
-    return (blk & 1) + 2 * r1 + 4 * r0 + 8 * (blk >> 2) + 16 * ((blk >> 1) & 1);
-  };
+  uint32_t cbits = 0;
 #pragma unroll
-  for (int blk = 0; blk < 8; ++blk) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      // two roundings, never fused: q = RN(S K), then RN(q + 1.5 2^52)
-      const double m = __dadd_rn(__dmul_rn(v[8 * blk + i], K), kMagic);
-      U[8 * blk + i] = (int32_t)(uint32_t)(uint64_t)__double_as_longlong(m);
-    }
-    int c;
-    ties |= e8_block_fast(U + 8 * blk, packed[2 * blk], packed[2 * blk + 1], c) << blk;
-    cbits |= (uint32_t)c << bpos(blk);
-  }
-  if (ties) {
-    // blocks with a coordinate exactly on a rounding boundary
-#pragma unroll
-    for (int blk = 0; blk < 8; ++blk) {
-      if ((ties >> blk) & 1u) {
-        const int c = e8_block_exact(U + 8 * blk, packed[2 * blk], packed[2 * blk + 1]);
-        cbits = (cbits & ~(1u << bpos(blk))) | ((uint32_t)c << bpos(blk));
-      }
-    }
-  }
+  for (int blk = 0; blk < 8; ++blk)
+    cbits |= ((cb >> blk) & 1u)
+             << ((blk & 1) + 2 * r1 + 4 * r0 + 8 * (blk >> 2) + 16 * ((blk >> 1) & 1));
   const uint32_t coset_word = tile_or_u32(cbits);
 
   // ---- Rice parameter: k = argmin_k L(k), L(k) = Q_k + 256 (1 + k),
@@ -237,36 +353,8 @@ __device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const
   // within 128 of S / 2^(k+1) (S = sum zeta), so with kt the smallest k with
   // S <= 256 * 2^(k+1): D_{kt+1} <= 256, and D_k > 256 for k <= kt - 2
   // (strictly, so no smaller k ties).  Only kt - 1, kt, kt + 1 remain.
-  uint32_t zz[16];
-  uint32_t S = 0;
-#pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    zz[q] = zigzag4(packed[q]);
-    S = byte_sum(zz[q], S);
-  }
-  S = tile_sum_u32(S);
-  int kt = 0;
-  while (kt < 8 && S > (256u << (kt + 1))) ++kt;
-  int kc[3];
-  uint32_t R[3];
-#pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    int k = kt - 1 + j;
-    kc[j] = k < 0 ? 0 : (k > 8 ? 8 : k);
-    const uint32_t mask = ((1u << kc[j]) - 1u) * 0x01010101u;
-    uint32_t r = 0;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) r = byte_sum(zz[q] & mask, r);
-    R[j] = r;
-  }
-  uint32_t best = 0xFFFFFFFFu;
-  int bk = 0;
-#pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    const uint32_t Rk = tile_sum_u32(R[j]);
-    const uint32_t L = ((S - Rk) >> kc[j]) + 256u * (uint32_t)(1 + kc[j]);
-    if (L < best) { best = L; bk = kc[j]; }
-  }
+  int bk;
+  const uint32_t best = rice_tile(packed, bk);
 
   // ---- store.  Chunk k (blocks 2k, 2k + 1: element bits 0-3 inside) has
   // element bit 7 = k bit 0, bit 6 = k bit 1, bit 5 = row bit 0 and bit 4 =
@@ -300,7 +388,9 @@ __device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const
 // The loop body ends with reading the next group from LDS, after this
 // group's stores; the last iteration prefetches its own group again (an L2
 // hit) so that no branch surrounds the memory operations.
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void encode_e8_fast(EncodeLaunch a, EncBatch b) {
+template <bool RC>
+__device__ __attribute__((always_inline)) inline void encode_body(const EncodeLaunch& a,
+                                                                  const EncBatch& b) {
   __shared__ uint32_t sign_tab[128];
   __shared__ uint4 stage[kBlock / 64][kEncStage];
   __shared__ uint4 ostage[kBlock / 64][256];
@@ -327,13 +417,23 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int64_t gp = more ? gn : g;
     const int ip = more ? item_of(b, gn) : ic;
     enc_prefetch(b.it[ip], gp - b.it[ip].group0, buf, lane, scale_in);
-    enc_group(a, b.it[ic], sign_tab, g - b.it[ic].group0, t, row, w, sc, ostage[wave]);
+    enc_group<RC>(a, b.it[ic], sign_tab, g - b.it[ic].group0, t, row, w, sc, ostage[wave]);
     __builtin_amdgcn_sched_barrier(0);
     enc_take(buf, t, row, w, sc);
     if (!more) break;
     g = gn;
     ic = ip;
   }
+}
+
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void encode_e8_fast(EncodeLaunch a, EncBatch b) {
+  encode_body<false>(a, b);
+}
+
+// With the per-tile rate control a lane keeps its 64 rotated values through
+// every probe: one wave per SIMD, so that they stay in registers.
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 1))) void encode_e8_fast_rc(EncodeLaunch a, EncBatch b) {
+  encode_body<true>(a, b);
 }
 
 // ------------------------------------------------------------------ decode
@@ -705,7 +805,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
       else
         dec_prefetch(bd.it[ip], nx.slot - bd.it[ip].group0, buf, ln);
       if (cur.kind == 0)
-        enc_group(a, b.it[ic], sign_enc, cur.slot - b.it[ic].group0, tt, rr, w, sc, ostage[wave]);
+        enc_group<false>(a, b.it[ic], sign_enc, cur.slot - b.it[ic].group0, tt, rr, w, sc,
+                         ostage[wave]);
       else
         dec_group<OUT_BF16>(bd.it[ic], sign_dec, cur.slot - bd.it[ic].group0, tt, rr, w, din,
                             ostage[wave]);
@@ -739,9 +840,16 @@ bool e8_fast_decode_ok(const DecodeLaunch& a) {
 using namespace fastlib;
 
 hipError_t launch_encode_e8_fast(const EncodeLaunch& a, const EncBatch& b, hipStream_t s) {
-  static int occ = 0;
-  const int64_t blocks = persistent_grid(b.n_groups * 16, resident_blocks(encode_e8_fast, occ));
-  hipLaunchKernelGGL(encode_e8_fast, dim3((unsigned)blocks), dim3(kBlock), 0, s, a, b);
+  if (a.rate_control) {
+    static int occ_rc = 0;
+    const int64_t blocks =
+        persistent_grid(b.n_groups * 16, resident_blocks(encode_e8_fast_rc, occ_rc));
+    hipLaunchKernelGGL(encode_e8_fast_rc, dim3((unsigned)blocks), dim3(kBlock), 0, s, a, b);
+  } else {
+    static int occ = 0;
+    const int64_t blocks = persistent_grid(b.n_groups * 16, resident_blocks(encode_e8_fast, occ));
+    hipLaunchKernelGGL(encode_e8_fast, dim3((unsigned)blocks), dim3(kBlock), 0, s, a, b);
+  }
   return hipGetLastError();
 }
 

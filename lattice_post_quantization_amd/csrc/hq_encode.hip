@@ -418,7 +418,8 @@ hipError_t launch_lat(const EncodeLaunch& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_encode(const EncodeLaunch& a, hipStream_t s) {
-  if (!a.rate_control && e8_fast_encode_ok(a)) {
+  // (the fast E8 kernel also runs the per-tile rate control)
+  if (e8_fast_encode_ok(a)) {
     EncBatch b;
     b.n = 1;
     b.pad = 0;

@@ -1216,14 +1216,18 @@ def test_kv_low_rate_parity(bps):
     check_decode(ora, "E8", 128, 1, "kv %g bps" % bps, exact=True, dither_seed=9, dither_base=77)
 
 
-@pytest.mark.parametrize("lattice,n,dtype,bps", [("E8", 256, "bf16", 4.0), ("E8", 128, "f32", 3.0),
+@pytest.mark.parametrize("lattice,n,dtype,bps", [("E8", 256, "bf16", 4.0), ("E8", 256, "bf16", 2.0),
+                                                 ("E8", 256, "bf16", 3.0), ("E8", 256, "bf16", 5.0),
+                                                 ("E8", 128, "f32", 3.0),
                                                  ("D4", 128, "bf16", 4.0), ("A2", 64, "bf16", 3.5),
                                                  ("Z", 512, "f32", 5.0)])
 def test_rate_control_parity(lattice, n, dtype, bps):
     """Per-tile rate control (bisection on bf16 scales to floor(bps n) bits per
     tile) against the oracle on a ragged matrix with outlier columns: the
     chosen scales bit for bit, indices, k and bits, and every tile within
-    its budget; then the decoded values."""
+    its budget; then the decoded values.  E8/256 bf16 runs on the fast
+    kernel, and again on the generic one (a call that exports coordinates),
+    with the same results."""
     rows, cols = 29, 5 * n
     rng = np.random.default_rng(97)
     w = rng.standard_normal((rows, cols)) * 0.02
@@ -1250,6 +1254,11 @@ def test_rate_control_parity(lattice, n, dtype, bps):
     assert np.array_equal(gb, ora["tile_bits"])
     assert np.all(gb <= math.floor(bps * n))
     check_decode(ora, lattice, n, 4, label, exact=(lattice != "A2"))
+    if (lattice, n, dtype) == ("E8", 256, "bf16"):
+        gg = hq.hq_encode_tiles(xd, lattice, n, bps, 4, rate_control=True, want_coords=True)
+        torch.cuda.synchronize()
+        for key in ("scale", "idx", "coset", "rice_k", "tile_bits"):
+            assert torch.equal(gg[key], g[key]), label + " generic vs fast " + key
 
 
 def test_kv_head_dim_64_dither_parity():
