@@ -106,6 +106,7 @@ struct BitReader {
   // this reader stops at the tile's last word, so an overrun shows as
   // missing bits while decoding
   __device__ inline bool overran() const { return false; }
+  __device__ inline bool short_of(uint32_t n) const { return nb < n; }
 };
 
 // One Rice code: the zigzag value (garbage, with bad set, when the code runs
@@ -146,97 +147,112 @@ __device__ inline uint32_t read_code(BitReader<FromLds>& br, uint32_t k, uint32_
   return zeta;
 }
 
-// Tile reader over words staged in LDS: 32-bit word positions relative to
-// the staged segment, a refill that reads the next word unconditionally
-// (clamped into the segment) so that the value is first used one refill
-// later, and a fast path for a code that lies within the buffered bits.
-// The refill does not stop at the tile's last word: the words after it are
-// the wave's next tiles (or the repeated last staged word), so a code that
-// runs past its tile reads staged words only, and overran() reports it
-// once the tile is decoded.
-struct LdsReader {
-  const lds_u32* lds;
-  uint32_t i0, i, iend, last;   // first and next word, end of the tile, last staged word
-  uint64_t b;
-  uint32_t nb;
-  uint32_t ahead;               // lds[min(i, last)]
-
-  __device__ inline void init(const lds_u32* seg, uint32_t w0, uint32_t w1, uint32_t n_staged) {
-    lds = seg;
-    i0 = w0;
-    i = w0;
-    iend = w1;
-    last = n_staged - 1u;
-    b = 0;
-    nb = 0;
-    ahead = lds[w0 < last ? w0 : last];
-  }
-  __device__ inline void refill() {
-    const bool c = nb <= 32u;
-    b |= (uint64_t)(c ? ahead : 0u) << nb;
-    nb += c ? 32u : 0u;
-    i += c ? 1u : 0u;
-    ahead = lds[i < last ? i : last];
-  }
-  // more bits consumed than the tile's words hold
-  __device__ inline bool overran() const {
-    return 32ull * (uint64_t)(i - i0) - nb > 32ull * (uint64_t)(iend - i0);
-  }
-  __device__ inline uint32_t take(uint32_t n) {   // n <= 32, at most nb
-    n = n < nb ? n : nb;
-    const uint32_t v = (uint32_t)b & (n >= 32u ? 0xFFFFFFFFu : (1u << n) - 1u);
-    b >>= n;
-    nb -= n;
-    return v;
-  }
-};
-
 // trailing zeros of x, 32 for x = 0 (one v_ffbl and a min)
 __device__ inline uint32_t ctz0(uint32_t x) { return x ? (uint32_t)__builtin_ctz(x) : 32u; }
 
-__device__ inline uint32_t read_code_lds(LdsReader& br, uint32_t k, uint32_t zmax, bool& bad) {
-  br.refill();
-  // the run of ones: the first zero of the 64-bit buffer, without a branch
-  const uint32_t zl = ctz0(~(uint32_t)br.b), zh = 32u + ctz0(~(uint32_t)(br.b >> 32));
-  uint32_t z = zl < 32u ? zl : zh;
-  if (z + 1u + k <= br.nb) {
-    // common case: the whole code is buffered
-    const uint32_t rem = (uint32_t)(br.b >> (z + 1u)) & ((1u << k) - 1u);
-    const uint32_t len = z + 1u + k;
-    br.b = len >= 64u ? 0 : br.b >> len;
-    br.nb -= len;
-    const uint32_t zeta = (z << k) | rem;
-    bad |= zeta > zmax;
-    return zeta;
+// Tile reader over words staged in LDS, by bit position: the 64-bit window
+// (lo, hi) holds words w and w + 1 of the segment, o < 32 is the position
+// of the next unread bit in lo, and nxt is word w + 2 (read when the window
+// moves on; reads past the staged words repeat the last one).  A code whose
+// unary run and remainder lie in the 32 bits at o (every code shorter than
+// 33 bits) is read from one funnel shift of the window: its run of ones
+// ends at the first zero, then k remainder bits.  The window moves by at
+// most one word per code.  It does not stop at the tile's last word (the
+// words after it are the wave's next tiles, or the repeated last staged
+// word), so a code that runs past its tile reads staged words only; overran() reports a tile whose codes used more bits than its
+// words hold.  zor collects the zigzag values (one of them exceeds zmax iff
+// their OR does, zmax + 1 a power of two).
+struct WinReader {
+  const lds_u32* lds;
+  uint32_t last4;               // byte offset of the last staged word
+  uint32_t w0, wend;            // the tile's words [w0, wend)
+  uint32_t p;                   // byte offset of word w + 2 (w: the word of lo)
+  uint32_t o;
+  uint32_t lo, hi, nxt;
+  uint32_t zor;
+  uint32_t zor_mask;
+
+  __device__ inline uint32_t rd(uint32_t byte_off) const {
+    const uint32_t q = byte_off < last4 ? byte_off : last4;
+    return *reinterpret_cast<const lds_u32*>(reinterpret_cast<const __attribute__((address_space(3))) char*>(lds) + q);
   }
-  // slow path: the unary run or the remainder crosses the buffered bits
-  uint32_t q = 0;
-  while (z >= br.nb) {
-    q += br.nb;
-    br.b = 0;
-    br.nb = 0;
-    br.refill();
-    const uint64_t iv = ~br.b;
-    z = iv == 0 ? 64u : (uint32_t)__builtin_ctzll(iv);
-    if (br.nb == 0u || q > zmax) {
-      bad = true;
-      z = 0;
-      break;
+  __device__ inline uint32_t word() const { return p / 4u - 2u; }
+  __device__ inline void init(const lds_u32* seg, uint32_t a, uint32_t b, uint32_t n_staged) {
+    lds = seg;
+    last4 = 4u * (n_staged - 1u);
+    w0 = a;
+    wend = b;
+    p = 4u * (a + 2u);
+    o = 0;
+    lo = rd(4u * a);
+    hi = rd(4u * a + 4u);
+    nxt = rd(p);
+    zor = 0;
+  }
+  __device__ inline void refill() {}
+  __device__ inline void move() {
+    if (o >= 32u) {
+      o -= 32u;
+      lo = hi;
+      hi = nxt;
+      p += 4u;
+      nxt = rd(p);
     }
   }
-  q += z;
-  const uint32_t used = z + 1u <= br.nb ? z + 1u : br.nb;
-  br.b = used >= 64u ? 0 : br.b >> used;
-  br.nb -= used;
-  br.refill();
-  bad |= br.nb < k;
-  const uint32_t zeta = (q << k) | br.take(k);
-  bad |= zeta > zmax;
-  return zeta;
-}
+  // the window after o moved by at most 32 bits, without a branch (the
+  // read repeats the current word when the window stays)
+  __device__ inline void step() {
+    const bool c = o >= 32u;
+    o &= 31u;
+    lo = c ? hi : lo;
+    hi = c ? nxt : hi;
+    p += c ? 4u : 0u;
+    nxt = rd(p);
+  }
+  // n <= 32 bits
+  __device__ inline uint32_t take(uint32_t n) {
+    const uint32_t x = __builtin_amdgcn_alignbit(hi, lo, o);
+    o += n;
+    move();
+    return n >= 32u ? x : x & ((1u << n) - 1u);
+  }
+  __device__ inline uint32_t code(uint32_t k, uint32_t zmax, bool& bad) {
+    const uint32_t x = __builtin_amdgcn_alignbit(hi, lo, o);
+    const uint32_t z = ctz0(~x);
+    uint32_t zeta;
+    if (z + 1u + k <= 32u) {
+      zeta = (z << k) | __builtin_amdgcn_ubfe(x, z + 1u, k);
+      o += z + 1u + k;
+      move();
+    } else {
+      // a run of ones or a remainder past the 32 bits at o
+      uint32_t q = 0;
+      for (;;) {
+        const uint32_t y = __builtin_amdgcn_alignbit(hi, lo, o);
+        const uint32_t zz = ctz0(~y);
+        q += zz;
+        o += zz < 32u ? zz + 1u : 32u;
+        move();
+        if (zz < 32u) break;
+        if (q > zmax || word() > wend) {   // corrupt: stop here
+          bad = true;
+          break;
+        }
+      }
+      zeta = (q << k) | take(k);
+    }
+    zor |= zeta;
+    return zeta;
+  }
+  __device__ inline bool overran() const {
+    return (zor & ~zor_mask) != 0u || 32u * (word() - w0) + o > 32u * (wend - w0);
+  }
+  // (header bits past the tile show up in overran())
+  __device__ inline bool short_of(uint32_t) const { return false; }
+};
 
-__device__ inline uint32_t next_code(LdsReader& br, uint32_t k, uint32_t zmax, bool& bad) {
-  return read_code_lds(br, k, zmax, bad);
+__device__ inline uint32_t next_code(WinReader& br, uint32_t k, uint32_t zmax, bool& bad) {
+  return br.code(k, zmax, bad);
 }
 __device__ inline uint32_t next_code(BitReader<false>& br, uint32_t k, uint32_t zmax, bool& bad) {
   return read_code(br, k, zmax, bad);
@@ -248,6 +264,94 @@ __device__ inline uint32_t unzigzag8(uint32_t zeta) {
 }
 __device__ inline uint32_t unzigzag16(uint32_t zeta) {
   return ((zeta >> 1) ^ (0u - (zeta & 1u))) & 0xFFFFu;
+}
+
+// The same for the four zigzag bytes (two half-words) of a dword: half the
+// value, complemented where it is odd (all-ones in a field from its low
+// bit l: (l << width) - l).
+// (v_perm selectors 8-11 replicate the sign bits of bytes 1, 3, 5, 7 of
+// {src0, src1}; shifted left by 15, bit 0 of each byte or half-word lands
+// on the sign bit of byte 1 or 3.)
+template <bool WIDE>
+__device__ inline uint32_t unzigzag_packed(uint32_t d) {
+  constexpr uint32_t kHalf = WIDE ? 0x7FFF7FFFu : 0x7F7F7F7Fu;
+  // int8: byte b's low bit sits at bit 7 of byte b of d << 7 (bytes 1, 3
+  // of src0) and of byte b + 1 of d << 15 (bytes 1, 3 of src1)
+  const uint32_t neg = WIDE ? __builtin_amdgcn_perm(0u, d << 15, 0x09090808u)
+                            : __builtin_amdgcn_perm(d << 7, d << 15, 0x0B090A08u);
+  return ((d >> 1) & kHalf) ^ neg;
+}
+
+// One 16-byte chunk of a tile's indices (16 int8 or 8 int16 codes), code
+// by code.
+template <bool WIDE, typename Reader>
+__device__ inline void chunk_by_code(Reader& br, uint32_t k, uint32_t zmax, bool& bad,
+                                     uint32_t* d) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t w = 0;
+    if constexpr (WIDE) {
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) w |= unzigzag16(next_code(br, k, zmax, bad)) << (16 * hi);
+    } else {
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) w |= unzigzag8(next_code(br, k, zmax, bad)) << (8 * bi);
+    }
+    d[j] = w;
+  }
+}
+
+template <bool WIDE>
+__device__ inline void next_chunk(BitReader<false>& br, uint32_t k, uint32_t zmax, bool& bad,
+                                  uint32_t* d) {
+  chunk_by_code<WIDE>(br, k, zmax, bad, d);
+}
+
+// raw v_ffbl_b32: the lowest set bit, 0xFFFFFFFF for 0
+__device__ inline uint32_t ffbl_raw(uint32_t x) {
+  uint32_t r;
+  __asm__("v_ffbl_b32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
+// WinReader: the chunk's codes without a branch, on the assumption that
+// every code of every lane lies in the 32 bits at its position (z + 1 + k
+// <= 32 for its first zero z); a code that does not (its first zero or its
+// remainder past them, or no zero: z = 0xFFFFFFFF) shows as
+// max z > 31 - k, and then the whole wave reads the chunk again code by
+// code from the saved window.
+template <bool WIDE>
+__device__ inline void next_chunk(WinReader& br, uint32_t k, uint32_t zmax, bool& bad,
+                                  uint32_t* d) {
+  const uint32_t so = br.o, sp = br.p, slo = br.lo, shi = br.hi, snx = br.nxt, szor = br.zor;
+  constexpr int kPer = WIDE ? 2 : 4;
+  const uint32_t k1 = k + 1u;
+  uint32_t zmx = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t pk = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const uint32_t x = __builtin_amdgcn_alignbit(br.hi, br.lo, br.o);
+      const uint32_t z = ffbl_raw(~x);
+      zmx = z > zmx ? z : zmx;
+      const uint32_t zeta = (z << k) | __builtin_amdgcn_ubfe(x, z + 1u, k);
+      br.zor |= zeta;
+      pk |= zeta << ((WIDE ? 16 : 8) * i);
+      br.o += z + k1;
+      br.step();
+    }
+    d[j] = unzigzag_packed<WIDE>(pk);
+  }
+  if (__builtin_amdgcn_ballot_w64(zmx > 31u - k) != 0) {
+    br.o = so;
+    br.p = sp;
+    br.lo = slo;
+    br.hi = shi;
+    br.nxt = snx;
+    br.zor = szor;
+    chunk_by_code<WIDE>(br, k, zmax, bad, d);
+  }
 }
 
 constexpr int kUnpackBlock = 128;     // two waves
@@ -262,12 +366,12 @@ __device__ inline void decode_tiles(const UnpackLaunch& a, const UnpackItem& it,
                                     int64_t tile, bool live, int64_t wave_tile0,
                                     uint32_t live_in_wave, int lane, uint4* st, bool& bad) {
   br.refill();
-  bad |= br.nb < 4u;
+  bad |= br.short_of(4u);
   const uint32_t k = br.take(4);
   for (int j = 0; j < a.coset_words; ++j) {
     const int nbits = a.coset_bits - 32 * j < 32 ? a.coset_bits - 32 * j : 32;
     br.refill();
-    bad |= br.nb < (uint32_t)nbits;
+    bad |= br.short_of((uint32_t)nbits);
     const uint32_t cw = br.take((uint32_t)nbits);
     if (live) it.coset[tile * a.coset_words + j] = cw;
   }
@@ -281,18 +385,7 @@ __device__ inline void decode_tiles(const UnpackLaunch& a, const UnpackItem& it,
 #pragma unroll 1
     for (int c = 0; c < 4; ++c) {
       uint32_t d[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint32_t w = 0;
-        if constexpr (WIDE) {
-#pragma unroll
-          for (int hi = 0; hi < 2; ++hi) w |= unzigzag16(next_code(br, k, kZmax, bad)) << (16 * hi);
-        } else {
-#pragma unroll
-          for (int bi = 0; bi < 4; ++bi) w |= unzigzag8(next_code(br, k, kZmax, bad)) << (8 * bi);
-        }
-        d[j] = w;
-      }
+      next_chunk<WIDE>(br, k, kZmax, bad, d);
       st[4 * lane + ((c ^ (lane >> 2)) & 3)] = make_uint4(d[0], d[1], d[2], d[3]);
     }
     wave_lds_sync();
@@ -358,8 +451,9 @@ __global__ __launch_bounds__(kUnpackBlock) void unpack_kernel(UnpackLaunch a) {
     // the copies land in LDS before any lane reads them
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     wave_lds_sync();
-    LdsReader br;
+    WinReader br;
     br.init(sw, (uint32_t)(w0 - seg_base), (uint32_t)(w1 - seg_base), nw > 0 ? nw : 1u);
+    br.zor_mask = WIDE ? 0xFFFFu : 0xFFu;
     decode_tiles<N, WIDE>(a, it, br, tile, live, wave_tile0, live_in_wave, lane, stage[wave], bad);
   } else {
     BitReader<false> br;
