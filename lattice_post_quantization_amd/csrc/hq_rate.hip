@@ -426,6 +426,13 @@ constexpr int pack_lds_words() {
   return 64 / (N / kElemsPerLane) * PackBound<N, WIDE>::kWords + 1;
 }
 
+// The same rounded up to whole 16-byte stores of all 64 lanes (the wave
+// clears its words with them).
+template <int N, bool WIDE>
+constexpr int pack_lds_zero_passes() {
+  return (pack_lds_words<N, WIDE>() + 255) / 256;
+}
+
 template <int N, bool WIDE>
 __global__ __launch_bounds__(kBlock) void pack_kernel(RateBatch bt) {
   int64_t bx;
@@ -435,13 +442,15 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(RateBatch bt) {
   constexpr int TPW = 64 / G;
   constexpr int W = PackBound<N, WIDE>::kWords;
   constexpr uint32_t kMaxK = WIDE ? 15u : 8u;   // the largest optimal k
-  __shared__ uint32_t lds[kBlock / 64][pack_lds_words<N, WIDE>()];
+  constexpr int kZero = pack_lds_zero_passes<N, WIDE>();
+  __shared__ uint4 lds[kBlock / 64][64 * kZero];
   const int lane = threadIdx.x & 63;
   const int r = lane % G;
   const int slot = lane / G;
   const int64_t wave = bx * (kBlock / 64) + (threadIdx.x >> 6);
   if (wave >= rate_waves<N>(a.n_tiles)) return;   // whole waves only
-  uint32_t* buf = lds[threadIdx.x >> 6];
+  uint4* buf4 = lds[threadIdx.x >> 6];
+  uint32_t* buf = reinterpret_cast<uint32_t*>(buf4);
   const int64_t span = wave_span<N>(a.n_tiles);
   const int64_t first = wave * span;
   const int64_t end = first + span < a.n_tiles ? first + span : a.n_tiles;
@@ -451,7 +460,7 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(RateBatch bt) {
   for (int i = 0; i < (threadIdx.x >> 6); ++i) base += a.wave_words[bx * (kBlock / 64) + i];
   struct PassIn {
     LaneIdx<WIDE> q;
-    uint32_t k, tb;
+    uint32_t k, tb, cw0;   // cw0: the tile's first coset word
   };
   auto fetch = [&](int64_t t0, PassIn& in) {
     if (t0 < end) {   // wave-uniform
@@ -460,6 +469,7 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(RateBatch bt) {
         in.q = load_lane<WIDE>(a.idx, tile * N + (int64_t)r * kElemsPerLane);
         in.k = a.rice_k[tile];
         in.tb = a.tile_bits[tile];
+        in.cw0 = a.coset_words > 0 ? a.coset[tile * a.coset_words] : 0u;
       }
     }
   };
@@ -480,8 +490,9 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(RateBatch bt) {
       pass_words += ng;
     }
     uint32_t* tw = buf + slot * W;
-    for (uint32_t j = r; j < nwords; j += G) tw[j] = 0u;
-    if (slot == TPW - 1 && r == 0) buf[TPW * W] = 0u;
+    // every word of the wave's tiles (and the spare word) starts at zero
+#pragma unroll
+    for (int z = 0; z < kZero; ++z) buf4[64 * z + lane] = make_uint4(0u, 0u, 0u, 0u);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -496,39 +507,70 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(RateBatch bt) {
       if constexpr (WIDE) zeta16(in.q, zz);
       else zeta4(in.q.q[0], zz);
     }
-    // this lane's payload bits: sum floor(zeta / 2^k) + 16 (1 + k)
-    uint32_t qs = 0;
-    if constexpr (WIDE) {
+    // The lane's codes by group of four: q per code and the bit length of
+    // each group (sum of q + 1 + k).  When every group of every lane of the
+    // wave spans at most 32 bits, each group is one value of at most 32
+    // bits and leaves with one pair of ORs (the common case: about 17 bits
+    // at 4 bps); otherwise the wave writes code by code.
+    uint32_t qv[16], gl[4], gmax = 0;
+    const uint32_t k1 = k + 1u;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) qs += zz[j] >> k;
-    } else {
-      const uint32_t m = (0xFFu >> k) * 0x01010101u;
+    for (int g = 0; g < 4; ++g) {
+      uint32_t sl = 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) qs = byte_sum((zz[j] >> k) & m, qs);
+      for (int i = 4 * g; i < 4 * g + 4; ++i) {
+        const uint32_t zeta = WIDE ? zz[i] : __builtin_amdgcn_ubfe(zz[i >> 2], 8 * (i & 3), 8);
+        qv[i] = zeta >> k;
+        sl += qv[i] + k1;
+      }
+      gl[g] = sl;
+      gmax = sl > gmax ? sl : gmax;
     }
-    const uint32_t T = live ? qs + 16u * (1u + k) : 0u;
+    // this lane's payload bits: sum floor(zeta / 2^k) + 16 (1 + k)
+    const uint32_t T = live ? (gl[0] + gl[1]) + (gl[2] + gl[3]) : 0u;
     const uint32_t pos = 4u + (uint32_t)a.coset_bits + row_incl_scan<G>(T, r) - T;
     // rice_k and tile_bits computed here always hold the codes; given ones
     // that do not (k > 8, or codes past tile_bits or past the tile's LDS
     // words) leave the lane's codes unwritten and mark the tile corrupt
     const bool fits = !a.given || (ck <= kMaxK && pos + T <= tb && tb <= 32u * (uint32_t)W);
     if (live && !fits) set_status(a.status, HQ_ST_CORRUPT);
+    const bool grouped = __builtin_amdgcn_ballot_w64(live && fits && gmax > 32u) == 0;
     if (live) {
       if (r == 0) {
-        // header: k (4 bits), then the coset bits
-        BitWriter h{tw, (uint64_t)k, 4u, 0u};
+        // header: k (4 bits), then the coset bits (word j at bit 4 + 32 j)
+        if (a.coset_words == 0) atomicOr(tw, k);
         for (int j = 0; j < a.coset_words; ++j) {
           const int nb = a.coset_bits - 32 * j;
-          const uint32_t cw = a.coset[tile * a.coset_words + j];
-          h.put(nb < 32 ? (cw & ((1u << nb) - 1u)) : cw, nb < 32 ? (uint32_t)nb : 32u);
+          uint32_t cw = j == 0 ? in.cw0 : a.coset[tile * a.coset_words + j];
+          if (nb < 32) cw &= (1u << nb) - 1u;
+          atomicOr(tw + j, (cw << 4) | (j == 0 ? k : 0u));
+          atomicOr(tw + j + 1, cw >> 28);
         }
-        h.flush();
       }
-      // the lane's 16 codes through one 64-bit accumulator: a word leaves
-      // (OR-ed into LDS) once full, so a lane issues about one LDS operation
-      // per 32 bits; its first and last words may be shared with its
-      // neighbours, which the OR allows
-      if (fits) {
+      // the lane's 16 codes are OR-ed into the tile's LDS words (a lane's
+      // first and last words may be shared with its neighbours, which the
+      // OR allows)
+      if (fits && grouped) {
+        const uint32_t rmask = (1u << k) - 1u;
+        uint32_t pb = pos;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          // the group's codes, each ((2 rem + 1) << q) - 1 (q ones, a zero,
+          // the k low bits), at their offsets inside the group
+          uint32_t c = 0, sh = 0;
+#pragma unroll
+          for (int i = 4 * g; i < 4 * g + 4; ++i) {
+            const uint32_t zeta = WIDE ? zz[i] : __builtin_amdgcn_ubfe(zz[i >> 2], 8 * (i & 3), 8);
+            c |= (((((zeta & rmask) << 1) | 1u) << qv[i]) - 1u) << sh;
+            sh += qv[i] + k1;
+          }
+          const uint64_t v = (uint64_t)c << (pb & 31u);
+          uint32_t* w = tw + (pb >> 5);
+          atomicOr(w, (uint32_t)v);
+          atomicOr(w + 1, (uint32_t)(v >> 32));
+          pb += gl[g];
+        }
+      } else if (fits) {
         const uint32_t rmask = (1u << k) - 1u;
         uint32_t pb = pos;
 #pragma unroll
