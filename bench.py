@@ -669,7 +669,12 @@ def main():
                 "gpu_event_ms_per_step": gpu_ms / args.steps,
                 "kernels": {k: t.stats(args.steps) for k, t in timers.items()}}
 
+    def progress(msg):
+        print("bench: " + msg, file=sys.stderr, flush=True)
+
+    progress("inputs ready, timing the sequential step")
     seq = run(step_sequential, ("encode", "decode"))
+    progress("timing the pipelined step")
     ref_y = [layers[i][2][m].clone() for i in (0, L - 1) for m in (0, 6)]
     pipe = run(step_pipelined, ("codec",)) if args.pipeline else None
     same = None
@@ -700,6 +705,8 @@ def main():
     # Cache (the headline decodes each layer right after its encode)
     cold = None
     if args.cold_steps > 0:
+        progress("cache-cold steps")
+
         def cold_step():
             for layer, (xs, encs, ys) in enumerate(layers):
                 hq.hq_encode_batch(xs, "E8", 256, args.bps, layer, outs=encs)
@@ -729,6 +736,8 @@ def main():
     copy_gbs = 2.0 * src.numel() / (copy_ms * 1e-3) / 1e9
     del src, dst
 
+    if args.secondary:
+        progress("secondary kernels")
     extra = secondary(layers[0], args.bps, dev) if args.secondary else None
 
     cpu = parity = None
@@ -762,6 +771,7 @@ def main():
             "tile_bits": se["tile_bits"].cpu().numpy().view(np.uint32).astype(np.int64),
             "y": sy.view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1, 256)}
         del sxd, se, sy
+        progress("cpu baseline (oracle on the host)")
         cpu, par = cpu_baseline(layer0_host, small_host, args.bps)
         parity = {
             "rule": "indices and coset bits equal the oracle's on every block except oracle "
