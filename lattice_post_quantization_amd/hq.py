@@ -416,17 +416,53 @@ def hq_rate_batch(encs, lattice="E8", tile=256, pack=False, given=False, status=
     return res
 
 
+def _check_packed(stream, offs, lattice, tile, idx, coset, rice_k, idx16, trusted):
+    """Host-side checks of an unpack call: the kernel reads the offsets as
+    uint64 and the stream words they name on trust, and writes every tile's
+    outputs.  Types and sizes are checked first, then device residence;
+    unless trusted, the last offset is read back (one 8-byte copy) and
+    checked against the stream's length."""
+    for t, name in ((stream, "stream"), (offs, "tile_word_offset")):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a tensor" % name)
+    if stream.dtype not in (torch.int32, torch.uint32) or stream.dim() != 1:
+        raise TypeError("stream must be a 1-D int32 / uint32 tensor of words")
+    if offs.dtype != torch.int64 or offs.dim() != 1 or offs.numel() < 1:
+        raise TypeError("tile_word_offset must be a 1-D int64 tensor of n_tiles + 1 offsets")
+    n_tiles = offs.numel() - 1
+    want = torch.int16 if idx16 else torch.int8
+    nw = coset_words(lattice, tile)
+    if idx is not None and (idx.dtype != want or idx.numel() != n_tiles * tile):
+        raise ValueError("idx must hold n_tiles * tile %s values" % str(want).split(".")[-1])
+    if coset is not None and nw and (coset.dtype not in (torch.int32, torch.uint32) or
+                                     coset.numel() != n_tiles * nw):
+        raise ValueError("coset must hold n_tiles * %d int32 words" % nw)
+    if rice_k is not None and (rice_k.dtype != torch.uint8 or rice_k.numel() != n_tiles):
+        raise ValueError("rice_k must hold n_tiles uint8 values")
+    _device_tensor(stream, "stream")
+    _device_tensor(offs, "tile_word_offset")
+    for t, name in ((idx, "idx"), (coset if nw else None, "coset"), (rice_k, "rice_k")):
+        if t is not None:
+            _device_tensor(t, name)
+    if not trusted and n_tiles > 0:
+        last = int(offs[-1].item())
+        if last < 0 or last > stream.numel():
+            raise ValueError("tile_word_offset[-1] = %d is past the stream's %d words"
+                             % (last, stream.numel()))
+    return n_tiles
+
+
 def hq_unpack(stream, tile_word_offset, lattice="E8", tile=256, status=None, out=None,
-              idx16=False):
+              idx16=False, trusted=False):
     """Decode a packed stream (as written by hq_rate) back to stripped
     indices (n_tiles, tile) int8 (int16 with idx16), coset words
     (n_tiles, words) int32 or None, and rice_k (n_tiles,) uint8.
-    tile_word_offset: int64 (n_tiles + 1)."""
-    _device_tensor(stream, "stream")
-    _device_tensor(tile_word_offset, "tile_word_offset")
-    dev = stream.device
-    n_tiles = tile_word_offset.numel() - 1
+    tile_word_offset: int64 (n_tiles + 1).  trusted=True skips the read-back
+    of the last offset (for offsets known to fit the stream)."""
     o = dict(out or {})
+    n_tiles = _check_packed(stream, tile_word_offset, lattice, tile, o.get("idx"), o.get("coset"),
+                            o.get("rice_k"), idx16, trusted)
+    dev = stream.device
     idx = o.get("idx")
     if idx is None:
         idx = torch.empty((n_tiles, tile), dtype=torch.int16 if idx16 else torch.int8, device=dev)
@@ -512,20 +548,22 @@ class UnpackItem(ctypes.Structure):
                 ("coset", ctypes.c_void_p), ("rice_k", ctypes.c_void_p)]
 
 
-def hq_unpack_batch(packs, lattice="E8", tile=256, status=None, outs=None, idx16=False):
+def hq_unpack_batch(packs, lattice="E8", tile=256, status=None, outs=None, idx16=False,
+                    trusted=False):
     """hq_unpack for several packed matrices sharing lattice and tile, in one
     call (one launch per group of eight).  packs: dicts with "stream" and
     "tile_word_offset" (as hq_rate returns).  Returns a list of dicts like
-    hq_unpack's; outs may supply their tensors (int16 indices with idx16)."""
+    hq_unpack's; outs may supply their tensors (int16 indices with idx16).
+    The same host-side checks as hq_unpack (trusted: no read-back)."""
     nw = coset_words(lattice, tile)
     res, items = [], []
     dev = None
     for i, pk in enumerate(packs):
-        stream = _device_tensor(pk["stream"], "stream")
-        offs = _device_tensor(pk["tile_word_offset"], "tile_word_offset")
-        dev = stream.device
-        n_tiles = offs.numel() - 1
+        stream, offs = pk["stream"], pk["tile_word_offset"]
         o = dict((outs[i] if outs is not None else None) or {})
+        n_tiles = _check_packed(stream, offs, lattice, tile, o.get("idx"), o.get("coset"),
+                                o.get("rice_k"), idx16, trusted)
+        dev = stream.device
         idx = o.get("idx")
         if idx is None:
             idx = torch.empty((n_tiles, tile), dtype=torch.int16 if idx16 else torch.int8,

@@ -313,6 +313,35 @@ def test_unpack_validation_codes():
     assert lib.hq_unpack_batch(ctypes.byref(p), 1, neg, None, None) == hq.HQ_EINVAL
 
 
+def test_unpack_binding_checks_types_and_sizes_first():
+    """The Python binding refuses wrong offset / stream / output types and
+    sizes before any device work (the kernel trusts them): here with host
+    tensors, where the type checks fire before the device check."""
+    import torch
+    words = torch.zeros(64, dtype=torch.int32)
+    offs = torch.zeros(5, dtype=torch.int64)
+    with pytest.raises(TypeError):
+        hq.hq_unpack(words, offs.to(torch.int32))                    # offsets not int64
+    with pytest.raises(TypeError):
+        hq.hq_unpack(words.to(torch.int64), offs)                    # stream not 32-bit words
+    with pytest.raises(TypeError):
+        hq.hq_unpack(words, offs[:0])                                # no offsets at all
+    with pytest.raises(ValueError, match="idx"):
+        hq.hq_unpack(words, offs, out={"idx": torch.zeros((4, 256), dtype=torch.int16)})
+    with pytest.raises(ValueError, match="idx"):
+        hq.hq_unpack(words, offs, out={"idx": torch.zeros((3, 256), dtype=torch.int8)})
+    with pytest.raises(ValueError, match="idx"):
+        hq.hq_unpack(words, offs, idx16=True, out={"idx": torch.zeros((4, 256), dtype=torch.int8)})
+    with pytest.raises(ValueError, match="coset"):
+        hq.hq_unpack(words, offs, out={"coset": torch.zeros((4, 2), dtype=torch.int32)})
+    with pytest.raises(ValueError, match="rice_k"):
+        hq.hq_unpack(words, offs, out={"rice_k": torch.zeros(4, dtype=torch.int32)})
+    with pytest.raises(ValueError, match="CUDA"):                    # well-formed, not on a GPU
+        hq.hq_unpack(words, offs)
+    with pytest.raises(TypeError):
+        hq.hq_unpack_batch([{"stream": words, "tile_word_offset": offs.to(torch.float32)}])
+
+
 def test_rate_batch_validation_codes():
     lib = hq.lib()
     p = hq.make_params("E8", 256, 4.0)
