@@ -524,6 +524,16 @@ def secondary(layer0, bps, dev):
 
     ms_a = time_calls(kv_attention, 10)
     ms_ab = time_calls(bf16_attention, 10)
+    # the same attention on rotation-only caches (no dither to regenerate)
+    encs_rot = [hq.hq_kv_encode(t, bps, 1) for t in kvs]
+    rot_cache = dict(rht_seed=1)
+
+    def kv_attention_rot():
+        hq.hq_kv_attention(qa, encs_rot[0], encs_rot[1], k_cache=rot_cache, v_cache=rot_cache,
+                           out=oa, workspace=wsa)
+
+    ms_ar = time_calls(kv_attention_rot, 10)
+    del encs_rot
     # per 128-vector: 256 B in / 128 B idx + 4 coset + 1 k + 4 bits + 4 scale
     kv = {"workload": "dithered E8 encode and decode of K and V [8, 32768, 128] bf16 "
                       "(%d vectors of 128, 4 bps)" % n_vec,
@@ -539,6 +549,7 @@ def secondary(layer0, bps, dev):
                                 "scaled_dot_product_attention on the decoded bf16 caches"
                                 % (heads, seq),
           "attention_us": round(ms_a * 1e3, 2),
+          "attention_rotation_only_us": round(ms_ar * 1e3, 2),
           "attention_bf16_sdpa_us": round(ms_ab * 1e3, 2),
           "attention_cache_gbs": round(2 * heads * seq * (128 + 8) / (ms_a * 1e-3) / 1e9, 1)}
     # bias of the cached inner products at this scale, dither against the
