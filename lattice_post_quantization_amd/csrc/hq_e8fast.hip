@@ -158,27 +158,39 @@ __device__ inline uint32_t rice_tile(const uint32_t* packed, int& bk) {
     S = byte_sum(zz[q], S);
   }
   S = tile_sum_u32(S);
-  int kt = 0;
-  while (kt < 8 && S > (256u << (kt + 1))) ++kt;
-  int kc[3];
-  uint32_t R[3];
+  // kt = min(8, smallest k with S <= 256 2^(k + 1)); S <= 255 * 256
+  int kt = S <= 512u ? 0 : 23 - (int)__builtin_clz(S - 1u);
+  kt = kt > 8 ? 8 : kt;
+  // The candidates k0, k0 + 1, k0 + 2 with k0 = min(max(kt - 1, 0), 6)
+  // contain kt - 1 .. kt + 1 within [0, 8]; the extra one (k0 + 2 when
+  // kt = 0, k0 when kt = 8) is never strictly better than those.
+  // R_k = sum (zeta mod 2^k): R_k0 directly; with x = zeta & (3 << k0)
+  // bytewise, sum x = 2^k0 (C0 + 2 C1) and popcount x = C0 + C1 (C0, C1 the
+  // counts of set bits k0, k0 + 1), so R_k0+1 = R_k0 + 2^k0 C0 and
+  // R_k0+2 = R_k0+1 + 2^(k0+1) C1.
+  const int k0 = kt - 1 < 0 ? 0 : (kt - 1 > 6 ? 6 : kt - 1);
+  const uint32_t mlo = ((1u << k0) - 1u) * 0x01010101u;
+  const uint32_t m2 = (3u << k0) * 0x01010101u;
+  uint32_t r0 = 0, sx = 0, cx = 0;
 #pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    int k = kt - 1 + j;
-    kc[j] = k < 0 ? 0 : (k > 8 ? 8 : k);
-    const uint32_t mask = ((1u << kc[j]) - 1u) * 0x01010101u;
-    uint32_t r = 0;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) r = byte_sum(zz[q] & mask, r);
-    R[j] = r;
+  for (int q = 0; q < 16; ++q) {
+    r0 = byte_sum(zz[q] & mlo, r0);
+    const uint32_t x = zz[q] & m2;
+    sx = byte_sum(x, sx);
+    cx += (uint32_t)__builtin_popcount(x);
   }
+  r0 = tile_sum_u32(r0);
+  sx = tile_sum_u32(sx);
+  cx = tile_sum_u32(cx);
+  const uint32_t c1 = (sx >> k0) - cx, c0 = cx - c1;
+  const uint32_t R[3] = {r0, r0 + (c0 << k0), r0 + (c0 << k0) + (c1 << (k0 + 1))};
   uint32_t best = 0xFFFFFFFFu;
   bk = 0;
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
-    const uint32_t Rk = tile_sum_u32(R[j]);
-    const uint32_t L = ((S - Rk) >> kc[j]) + 256u * (uint32_t)(1 + kc[j]);
-    if (L < best) { best = L; bk = kc[j]; }
+    const int k = k0 + j;
+    const uint32_t L = ((S - R[j]) >> k) + 256u * (uint32_t)(1 + k);
+    if (L < best) { best = L; bk = k; }
   }
   return best;
 }
@@ -415,7 +427,7 @@ __device__ __attribute__((always_inline)) inline void encode_body(const EncodeLa
     const int64_t gn = g + stride;
     const bool more = gn < b.n_groups;   // uniform across the wave
     const int64_t gp = more ? gn : g;
-    const int ip = more ? item_of(b, gn) : ic;
+    const int ip = more ? item_from(b, ic, gn) : ic;
     enc_prefetch(b.it[ip], gp - b.it[ip].group0, buf, lane, scale_in);
     enc_group<RC>(a, b.it[ic], sign_tab, g - b.it[ic].group0, t, row, w, sc, ostage[wave]);
     __builtin_amdgcn_sched_barrier(0);
@@ -706,7 +718,7 @@ __global__ __launch_bounds__(kBlock) void decode_e8_fast(DecodeLaunch a, DecBatc
     const int64_t gn = g + stride;
     const bool more = gn < b.n_groups;   // uniform across the wave
     const int64_t gp = more ? gn : g;
-    const int ip = more ? item_of(b, gn) : ic;
+    const int ip = more ? item_from(b, ic, gn) : ic;
     dec_prefetch(b.it[ip], gp - b.it[ip].group0, buf, lane);
     dec_group<OUT_BF16>(b.it[ic], sign_tab, g - b.it[ic].group0, t, row, d, in, ostage[wave]);
     __builtin_amdgcn_sched_barrier(0);
@@ -780,6 +792,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
   float sc = 0.0f;
   DecIn din;
   int ic = cur.kind == 0 ? item_of(b, cur.slot) : item_of(bd, cur.slot);
+  // the last item of each batch met so far (the walks only move forward)
+  int ie = cur.kind == 0 ? ic : 0, id = cur.kind == 0 ? 0 : ic;
   if (cur.kind == 0) {
     enc_prefetch(b.it[ic], cur.slot - b.it[ic].group0, buf, lane, scale_in);
     enc_take(buf, t, row, w, sc);
@@ -793,7 +807,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     PipeItem nx = pipe_next(cur, stride, ne, nd);
     const bool more = nx.kind >= 0;   // uniform across the wave
     if (!more) nx = cur;              // the last item prefetches itself again
-    const int ip = nx.kind == 0 ? item_of(b, nx.slot) : item_of(bd, nx.slot);
+    const int ip = nx.kind == 0 ? item_from(b, ie, nx.slot) : item_from(bd, id, nx.slot);
+    if (nx.kind == 0) ie = ip; else id = ip;
     // Each kind's per-lane LDS addresses are derived inside its own branch
     // from a lane id the compiler cannot hoist: kept live across the loop,
     // both kinds' addresses would not fit the register file next to an

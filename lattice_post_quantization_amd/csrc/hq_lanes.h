@@ -325,6 +325,15 @@ __device__ inline int item_of(const B& b, int64_t g) {
   return i;
 }
 
+// Item holding global group g, found from item i, which holds an earlier
+// group of the same walk (groups are visited in increasing order, so the
+// item only moves forward; usually one comparison).
+template <typename B>
+__device__ inline int item_from(const B& b, int i, int64_t g) {
+  while (i + 1 < b.n && g >= b.it[i + 1].group0) ++i;
+  return i;
+}
+
 inline int device_cus() {
   static int cached[64];
   int dev = 0;
