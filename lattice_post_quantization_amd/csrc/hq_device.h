@@ -26,6 +26,17 @@ constexpr double kUClamp = 2080374784.0;   // 2^31 - 2^26
 // every index still fits int16.
 constexpr double kUClamp16 = 536870912000.0;   // 32000 2^24
 
+// rne(x K) of the exact product x K (one rounding, ties to even), as a
+// double holding the integer: the fma adds 1.5 2^52 to the exact product and
+// rounds once at unit spacing.  A product of magnitude >= 2^50, far past
+// every clamp, is rounded twice; it clamps the same way.
+constexpr double kGridMagic = 6755399441055744.0;   // 1.5 2^52
+__device__ inline double rne_product(double x, double K) {
+  const double p = __dmul_rn(x, K);
+  if (!(fabs(p) < 0x1p50)) return rint(p);
+  return __fma_rn(x, K, kGridMagic) - kGridMagic;
+}
+
 // SplitMix64 output function (Steele, Lea & Flood, OOPSLA 2014) applied to a
 // counter key: the randomness the method draws (RHT signs, KV dither).
 __host__ __device__ inline uint64_t splitmix64(uint64_t k) {

@@ -119,8 +119,8 @@ __device__ inline uint32_t e8_lane(const double* v, double K, uint32_t* packed, 
   for (int blk = 0; blk < 8; ++blk) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      // two roundings, never fused: q = RN(S K), then RN(q + 1.5 2^52)
-      const double m = __dadd_rn(__dmul_rn(v[8 * blk + i], K), kMagic);
+      // one rounding of the exact product: RN(S K + 1.5 2^52)
+      const double m = __fma_rn(v[8 * blk + i], K, kMagic);
       U[8 * blk + i] = (int32_t)(uint32_t)(uint64_t)__double_as_longlong(m);
     }
     int c;
@@ -210,7 +210,7 @@ __device__ inline double tile_max_f64(double v) {
 // tile's indices stay inside the grid's clamp, hence int8, and its bits fit
 // floor(R n)).  The probes of every tile follow the same rule as the
 // generic kernel's; a probe whose largest grid value would pass the clamp
-// (rint(max|S| K) > 124 2^24, the largest of the generic kernel's clamped
+// (rne(max|S| K) > 124 2^24, the largest of the generic kernel's clamped
 // values) is infeasible without a decision.  Returns the chosen scale
 // (delta unchanged for a tile that is not searched).
 __device__ inline float rc_search(const EncodeLaunch& a, const double* v, double ss, float delta,
@@ -229,7 +229,7 @@ __device__ inline float rc_search(const EncodeLaunch& a, const double* v, double
     const double K = 16777216.0 / tq;
     // (lanes of finished tiles and of probes past the clamp decide on
     // values whose results are not used)
-    const bool in_range = rint(__dmul_rn(vmax, K)) <= kUClamp;
+    const bool in_range = rne_product(vmax, K) <= kUClamp;
     uint32_t packed[16];
     (void)e8_lane(v, K, packed, active && in_range);
     int bk;
@@ -332,11 +332,11 @@ __device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const
   }
 
   // When some tile of the wave may pass the clamp, the generic encoder's
-  // clamped rint(S K) replaces S (and K becomes 1).
+  // clamped rne(S K) replaces S (and K becomes 1).
   if (__builtin_amdgcn_ballot_w64(big) != 0) {
 #pragma unroll
     for (int i = 0; i < 64; ++i) {
-      double q = rint(__dmul_rn(v[i], K));
+      double q = rne_product(v[i], K);
       if (!(fabs(q) <= kUClamp)) {
         status |= HQ_ST_OVERFLOW;
         q = (q > 0.0) ? kUClamp : -kUClamp;

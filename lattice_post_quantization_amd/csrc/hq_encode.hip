@@ -77,15 +77,15 @@ __device__ inline uint32_t lane_sign_mask(const EncodeLaunch& a, int r) {
   return (s >> (16 * (r & 1))) & 0xFFFFu;
 }
 
-// Quantizer input on the 2^-24 grid for 16 rotated values: U = rne(S K)
-// (A2: odd coordinates with K3); magnitudes past the clamp (kUClamp, or
+// Quantizer input on the 2^-24 grid for 16 rotated values: U = rne(S K) of
+// the exact product (A2: odd coordinates with K3); magnitudes past the clamp (kUClamp, or
 // kUClamp16 for the 64-bit grid of the int16 index mode) flag an overflow.
 template <int LAT, typename GI>
 __device__ inline void grid_values(const double* v, double K, double K3, GI* U, uint32_t& st) {
   constexpr double kClamp = sizeof(GI) == 8 ? kUClamp16 : kUClamp;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    double q = rint(__dmul_rn(v[i], (LAT == 2 && (i & 1)) ? K3 : K));
+    double q = rne_product(v[i], (LAT == 2 && (i & 1)) ? K3 : K);
     if (!(fabs(q) <= kClamp)) {
       st |= HQ_ST_OVERFLOW;
       q = (q > 0.0) ? kClamp : -kClamp;

@@ -138,10 +138,10 @@ __device__ inline uint32_t a2_pair(int32_t U1, int32_t V2, uint32_t& ta, uint32_
   return c ? 1u : 0u;
 }
 
-// Grid value of one rotated coordinate: the low dword of RN(RN(S K) + 1.5 2^52)
-// is rne(S K) for |S K| < 2^31.
+// Grid value of one rotated coordinate: the low dword of RN(S K + 1.5 2^52)
+// (one rounding of the exact product) is rne(S K) for |S K| < 2^31.
 __device__ __attribute__((always_inline)) inline int32_t grid_at(double v, double K) {
-  const double m = __dadd_rn(__dmul_rn(v, K), kMagic);
+  const double m = __fma_rn(v, K, kMagic);
   return (int32_t)(uint32_t)(uint64_t)__double_as_longlong(m);
 }
 
@@ -249,15 +249,15 @@ __device__ inline void enc128_group(const EncodeLaunch& a, const uint32_t* sign_
   }
   // register i now holds element (i mod 32) + 32 r + 64 (i / 32)
 
-  // ---- quantizer grid U = u 2^24 = RN(RN(S K) + 1.5 2^52) - 1.5 2^52 (two
-  // roundings, never fused), formed block by block as the decisions use it.
-  // When some tile of the wave may pass the clamp, the generic encoder's
-  // clamped rint(S K) first replaces S (and K becomes 1).
+  // ---- quantizer grid U = u 2^24 = RN(S K + 1.5 2^52) - 1.5 2^52 (one
+  // rounding of the exact product), formed block by block as the decisions
+  // use it.  When some tile of the wave may pass the clamp, the generic
+  // encoder's clamped rne(S K) first replaces S (and K becomes 1).
   double Kq = K, K3q = K3;
   if (__builtin_amdgcn_ballot_w64(big) != 0) {
 #pragma unroll
     for (int i = 0; i < 64; ++i) {
-      double q = rint(__dmul_rn(v[i], (LAT == 2 && (i & 1)) ? K3 : K));
+      double q = rne_product(v[i], (LAT == 2 && (i & 1)) ? K3 : K);
       if (!(fabs(q) <= kUClamp)) {
         status |= HQ_ST_OVERFLOW;
         q = (q > 0.0) ? kUClamp : -kUClamp;

@@ -17,7 +17,8 @@ R2 Scale, auto mode: Delta_t = bf16_rne(rms_t * c(L, R)) with
 R3 Quantizer input: u = y / Delta with y = H (s x) / sqrt(n), formed as
    S * K_t where S = H (s x) (exact) and K_t = 2^24 / (sqrt(n) * Delta_t)
    (two fp64 roundings: the product sqrt(n)*Delta_t, then the quotient), and
-   held on a 2^-24 grid: U = rne(S * K_t), u = U 2^-24.  On this grid every
+   held on a 2^-24 grid: U = rne(S * K_t), the exact product rounded once to
+   the nearest integer (ties to even), u = U 2^-24.  On this grid every
    nearest-point decision, distance and margin is exact in fp64, so any two
    correct implementations agree bit for bit, ties included.  (For A2 the
    second coordinate of each pair is taken as u2/sqrt3 with
@@ -137,16 +138,42 @@ def auto_scale(X, lattice, bps):
     return np.where(d == 0.0, 1.0, d)
 
 
+def _split(x):
+    """Veltkamp's split of float64 x into hi + lo, each of <= 26 significant
+    bits, so that products of the halves are exact."""
+    c = 134217729.0 * x            # 2^27 + 1
+    hi = c - (c - x)
+    return hi, x - hi
+
+
+def rne_product(a, b):
+    """rne(a b) of the exact product of float64 arrays (one rounding to the
+    nearest integer, ties to even), as float64.  p = RN(a b) and the error
+    e = a b - p are found exactly (Dekker's product, 1971); rint(p) is the
+    answer unless p is a half-integer, where the sign of e decides."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    p = a * b
+    ah, al = _split(a)
+    bh, bl = _split(b)
+    e = ((ah * bh - p) + ah * bl + al * bh) + al * bl
+    r = np.rint(p)
+    half = np.abs(p - r) == 0.5
+    r = np.where(half & (e > 0), np.floor(p) + 1.0, r)
+    r = np.where(half & (e < 0), np.floor(p), r)
+    return r
+
+
 def quantizer_input(S, delta, lattice):
-    """Reading R3: U = rne(S K_t) on the 2^-24 grid; returns u = U 2^-24
-    (for A2, odd coordinates hold u2/sqrt3)."""
+    """Reading R3: U = rne(S K_t) of the exact product on the 2^-24 grid;
+    returns u = U 2^-24 (for A2, odd coordinates hold u2/sqrt3)."""
     n = S.shape[1]
     t = math.sqrt(n) * np.asarray(delta, np.float64)
     K = GRID / t
     Kc = np.repeat(K[:, None], n, axis=1)
     if lattice == "A2":
         Kc[:, 1::2] = (GRID / (t * math.sqrt(3.0)))[:, None]
-    return np.rint(S * Kc) / GRID
+    return rne_product(S, Kc) / GRID
 
 
 def nearest(u, lattice):

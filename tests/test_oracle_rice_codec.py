@@ -156,6 +156,48 @@ def test_quantizer_input_grid_and_formula():
     assert np.max(np.abs(e["u"] - y / e["scale"][:, None])) <= 0.5 / codec.GRID * (1 + 1e-9)
 
 
+def _rne_exact(a, b):
+    """rne of the exact rational product (the definition, with Fractions)."""
+    from fractions import Fraction
+    q = Fraction(float(a)) * Fraction(float(b))
+    f = math.floor(q)
+    r = q - f
+    if r > Fraction(1, 2) or (r == Fraction(1, 2) and f % 2 == 1):
+        f += 1
+    return float(f)
+
+
+def test_grid_rounds_the_exact_product_once():
+    # Reading R3: U = rne(S K) of the exact product.  Checked against the
+    # rational definition on pipeline-sized values and on products whose
+    # fp64 rounding lands exactly on a half-integer while the exact product
+    # does not (there rounding twice, rint(RN(S K)), picks the even neighbour
+    # regardless of the side the product lies on).
+    rng = np.random.default_rng(31)
+    a = rng.normal(0.0, 3.0, 4000) * 2.0 ** rng.integers(-8, 8, 4000)
+    b = rng.uniform(1.0, 2.0, 4000) * 2.0 ** 24
+    got = codec.rne_product(a, b)
+    assert all(g == _rne_exact(x, y) for g, x, y in zip(got, a, b))
+    from fractions import Fraction
+    hard = []
+    for m in rng.integers(2 ** 20, 2 ** 30, 20000):
+        for k in (3.0, 5.0, 7.0, 11.0):
+            x = k
+            y = (float(m) + 0.5) / k
+            if x * y == float(m) + 0.5 and Fraction(x) * Fraction(y) != Fraction(2 * int(m) + 1, 2):
+                hard.append((x, y))
+        if len(hard) >= 40:
+            break
+    assert len(hard) >= 20
+    xs = np.array([h[0] for h in hard])
+    ys = np.array([h[1] for h in hard])
+    got = codec.rne_product(xs, ys)
+    want = np.array([_rne_exact(x, y) for x, y in hard])
+    assert np.array_equal(got, want)
+    # ...where rounding twice would have differed on some of them
+    assert np.any(np.rint(xs * ys) != want)
+
+
 @pytest.mark.parametrize("lat,n", [("E8", 256), ("E8", 128), ("D4", 128), ("A2", 128), ("Z", 128)])
 def test_roundtrip_error_within_covering_radius(lat, n):
     x = workloads.bf16_bits_to_f64(workloads.llama_matrix(0, shape=(16, 4096)))
