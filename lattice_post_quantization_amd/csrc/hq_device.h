@@ -85,7 +85,8 @@ __device__ inline void d_round(const GI* U, int32_t* z) {
 }
 
 // Nearest E8 = D8 u (D8 + 1/2) point.  Returns the coset bit c; z is in D8 and
-// the point is z + c/2.  The coset comparison |u-a|^2 <= |u-b|^2 is evaluated
+// the point is z + c/2.  The half coset's parity fix takes the last
+// coordinate of largest residual (the integer coset's, as d_round, the first).  The coset comparison |u-a|^2 <= |u-b|^2 is evaluated
 // exactly in closed form: with A_i = |u_i - rne(u_i)| and B_i = 1/2 - A_i,
 //   (|u-a|^2 - |u-b|^2) / 2^24 = sum A - 2^25 + [odd a](2^24 - 2 max A)
 //                                 - [odd b](2^24 - 2 max B)
@@ -104,7 +105,7 @@ __device__ inline int e8_nearest(const GI* U, int32_t* z) {
     int32_t A = iabs(RA[i]);
     sumA += A;
     if (A > amax) { amax = A; ja = i; }
-    if (A < amin) { amin = A; jb = i; }   // max |RB| = 2^23 - min |RA|
+    if (A <= amin) { amin = A; jb = i; }  // max |RB| = 2^23 - min |RA|, last on ties
   }
   const bool odd_a = sa & 1, odd_b = sb & 1;
   const int32_t bmax = kHalf - amin;

@@ -20,20 +20,19 @@ using namespace fastlib;
 // coordinate's offset from its point is ((W + off) mod 2^24) - 2^23, and the
 // parity flip moves one coordinate's point by one.
 __device__ inline void e8_dither_block(const int32_t* W, int32_t* d24) {
-  uint32_t k1[8], k2[8];
+  uint32_t k1[8];
 #define HQ_DITHER_KEYS(i)                                         \
   {                                                               \
     const uint32_t F8 = ((uint32_t)W[i] << 3) & 0x07FFFFFFu;      \
     k1[i] = sad26<i>(F8);                                         \
-    k2[i] = sad26<7 - i>(F8);                                     \
   }
   HQ_DITHER_KEYS(0) HQ_DITHER_KEYS(1) HQ_DITHER_KEYS(2) HQ_DITHER_KEYS(3)
   HQ_DITHER_KEYS(4) HQ_DITHER_KEYS(5) HQ_DITHER_KEYS(6) HQ_DITHER_KEYS(7)
 #undef HQ_DITHER_KEYS
   const uint32_t kmin = min3u(min3u(k1[0], k1[1], k1[2]), min3u(k1[3], k1[4], k1[5]),
                               k1[6] < k1[7] ? k1[6] : k1[7]);
-  const uint32_t kmax = max3u(max3u(k2[0], k2[1], k2[2]), max3u(k2[3], k2[4], k2[5]),
-                              k2[6] > k2[7] ? k2[6] : k2[7]);
+  const uint32_t kmax = max3u(max3u(k1[0], k1[1], k1[2]), max3u(k1[3], k1[4], k1[5]),
+                              k1[6] > k1[7] ? k1[6] : k1[7]);
   const int32_t bmin = (int32_t)(kmin >> 3), bmax = (int32_t)(kmax >> 3);
   if (bmin == 0 || bmax == kHalf) {
     int32_t z[8];
@@ -52,7 +51,7 @@ __device__ inline void e8_dither_block(const int32_t* W, int32_t* d24) {
   const int32_t D = (1 << 25) - (int32_t)sumB + (odd_a ? 2 * bmin : 0) -
                     (odd_b ? (1 << 24) - 2 * bmax : 0);
   const int c = D > 0;
-  const uint32_t jf = c ? 7u - (kmax & 7u) : (kmin & 7u);
+  const uint32_t jf = c ? (kmax & 7u) : (kmin & 7u);
   const int odd = c ? odd_b : odd_a;
   const uint32_t G0 = third_bytes(W[0], W[1], W[2], W[3]);
   const uint32_t G1 = third_bytes(W[4], W[5], W[6], W[7]);

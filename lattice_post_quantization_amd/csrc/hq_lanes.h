@@ -133,7 +133,8 @@ __device__ inline void fill_sign_table(uint32_t* tab, const uint32_t* signs) {
 // (distance to the nearest half-integer; the distance to the nearest integer
 // is 2^23 - B_i), and no coordinate exactly on an integer or half-integer:
 //   integer coset a_i = I_i + [F_i > 2^23], half coset b_i = I_i (+ 1/2),
-//   parity fixes on the first max/min of B, coset choice by
+//   parity fixes on the first min of B (coset a) and the last max of B
+//   (coset b), coset choice by
 //   D = 2^25 - sum B + [odd a] 2 min B - [odd b] (2^24 - 2 max B) > 0.
 // Bit 24 of U_i is the parity of I_i and bit 23 is [F_i > 2^23], so both
 // parities come from the XOR of the eight U_i.  The stored integers are
@@ -212,21 +213,22 @@ __device__ inline uint32_t pk_add_u16(uint32_t a, uint32_t b) {
 }
 
 __device__ inline uint32_t e8_block_fast(const int32_t* U, uint32_t& p0, uint32_t& p1, int& cs) {
-  // keys (B << 3) + i and (B << 3) + 7 - i: |8F - 2^26| plus the index
-  uint32_t k1[8], k2[8];
+  // keys (B << 3) + i = |8F - 2^26| plus the index: their minimum is the
+  // integer coset's parity coordinate (smallest B, first on ties), their
+  // maximum the half coset's (largest B, last on ties)
+  uint32_t k1[8];
 #define HQ_E8_KEYS(i)                                             \
   {                                                               \
     const uint32_t F8 = frac8(U[i]);                              \
     k1[i] = sad26<i>(F8);                                         \
-    k2[i] = sad26<7 - i>(F8);                                     \
   }
   HQ_E8_KEYS(0) HQ_E8_KEYS(1) HQ_E8_KEYS(2) HQ_E8_KEYS(3)
   HQ_E8_KEYS(4) HQ_E8_KEYS(5) HQ_E8_KEYS(6) HQ_E8_KEYS(7)
 #undef HQ_E8_KEYS
   const uint32_t kmin = min3u(min3u(k1[0], k1[1], k1[2]), min3u(k1[3], k1[4], k1[5]),
                               k1[6] < k1[7] ? k1[6] : k1[7]);
-  const uint32_t kmax = max3u(max3u(k2[0], k2[1], k2[2]), max3u(k2[3], k2[4], k2[5]),
-                              k2[6] > k2[7] ? k2[6] : k2[7]);
+  const uint32_t kmax = max3u(max3u(k1[0], k1[1], k1[2]), max3u(k1[3], k1[4], k1[5]),
+                              k1[6] > k1[7] ? k1[6] : k1[7]);
   // min B = 0 or max B = 2^23: a coordinate on a half-integer or an integer
   const uint32_t tie = (uint32_t)(kmin < 8u) | (uint32_t)(kmax >= (1u << 26));
   // 8 sum B = sum k1 - 28
@@ -241,7 +243,7 @@ __device__ inline uint32_t e8_block_fast(const int32_t* U, uint32_t& p0, uint32_
                      (odd_a ? 2 * (int32_t)(kmin & ~7u) : 0) -
                      (odd_b ? (1 << 27) - 2 * (int32_t)(kmax & ~7u) : 0);
   const int c = D8 > 0;
-  const uint32_t jf = c ? 7u - (kmax & 7u) : (kmin & 7u);
+  const uint32_t jf = c ? (kmax & 7u) : (kmin & 7u);
   const int odd = c ? odd_b : odd_a;
   // Q: the high halves (U >> 16) of two coordinates; byte 1 of a half is I,
   // bit 7 of byte 0 is [F > 2^23]

@@ -9,8 +9,11 @@ IEEE Trans. IT 28(2), 1982; and "Sphere Packings, Lattices and Groups", ch. 20):
 * D_m = {z in Z^m : sum z even}.  D_m(v): f = rne(v) (round half to even);
   if sum f is odd, move the coordinate with the largest |v_j - f_j| (lowest
   index on ties) one step towards v_j (+1 when v_j - f_j = 0).
-* E8 = D8 u (D8 + 1/2): a = D8(u), b = D8(u - 1/2) + 1/2; keep a when
-  |u - a|^2 <= |u - b|^2 (ties go to the integer coset), else b.
+* E8 = D8 u (D8 + 1/2): a = D8(u), b = D8(u - 1/2) + 1/2, where the half
+  coset's parity fix takes the last coordinate of largest residual (highest
+  index on ties; tie rules are a free choice, and this one lets an
+  implementation rank both cosets' residuals with one key per coordinate);
+  keep a when |u - a|^2 <= |u - b|^2 (ties go to the integer coset), else b.
 * D4: D4(u).
 * A2 (minimum distance 1) = (Z x sqrt3 Z) u ((1/2, sqrt3/2) + Z x sqrt3 Z).
   Decisions are taken in w = (u1, u2/sqrt3), where A2 is Z^2 u ((1/2,1/2)+Z^2)
@@ -30,13 +33,19 @@ import numpy as np
 
 # ----------------------------------------------------------------- D_m / E8
 
-def d_round(v):
-    """Nearest point of D_m to each row of v (float64 (..., m)); float64 out."""
+def d_round(v, last=False):
+    """Nearest point of D_m to each row of v (float64 (..., m)); float64 out.
+    The parity fix goes to the first coordinate of largest residual, or to
+    the last one with last=True."""
     v = np.asarray(v, np.float64)
     f = np.rint(v)
     d = v - f
     odd = (np.sum(f, axis=-1) % 2) != 0
-    j = np.argmax(np.abs(d), axis=-1)
+    if last:
+        m = v.shape[-1]
+        j = m - 1 - np.argmax(np.abs(d)[..., ::-1], axis=-1)
+    else:
+        j = np.argmax(np.abs(d), axis=-1)
     dj = np.take_along_axis(d, j[..., None], axis=-1)[..., 0]
     step = np.where(dj >= 0, 1.0, -1.0)
     fix = np.zeros_like(f)
@@ -60,7 +69,7 @@ def e8_nearest(u):
     """
     u = np.asarray(u, np.float64)
     a = d_round(u)
-    b = d_round(u - 0.5)
+    b = d_round(u - 0.5, last=True)
     da = sqdist(u - a)
     db = sqdist(u - (b + 0.5))
     pick_b = db < da
