@@ -100,6 +100,8 @@ __device__ inline uint4 load16(const int8_t* idx, int64_t e0) {
 }
 
 // A lane's 16 indices: 16 bytes (int8) or 32 bytes (int16 index mode).
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
 template <bool WIDE>
 struct LaneIdx {
   uint4 q[WIDE ? 2 : 1];
@@ -433,6 +435,12 @@ constexpr int pack_lds_zero_passes() {
   return (pack_lds_words<N, WIDE>() + 255) / 256;
 }
 
+// Passes whose loads are in flight ahead of the one being packed.
+#ifndef HQ_PACK_AHEAD
+#define HQ_PACK_AHEAD 3
+#endif
+constexpr int kPackAhead = HQ_PACK_AHEAD;
+
 template <int N, bool WIDE>
 __global__ __launch_bounds__(kBlock) void pack_kernel(RateBatch bt) {
   int64_t bx;
@@ -447,9 +455,10 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(RateBatch bt) {
   const int lane = threadIdx.x & 63;
   const int r = lane % G;
   const int slot = lane / G;
-  const int64_t wave = bx * (kBlock / 64) + (threadIdx.x >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // the wave in the block
+  const int64_t wave = bx * (kBlock / 64) + wv;
   if (wave >= rate_waves<N>(a.n_tiles)) return;   // whole waves only
-  uint4* buf4 = lds[threadIdx.x >> 6];
+  uint4* buf4 = lds[wv];
   uint32_t* buf = reinterpret_cast<uint32_t*>(buf4);
   const int64_t span = wave_span<N>(a.n_tiles);
   const int64_t first = wave * span;
@@ -457,21 +466,36 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(RateBatch bt) {
   // first word of this pass's tiles: the block's offset, then the words of
   // the block's earlier waves
   uint64_t base = a.block_words[bx];
-  for (int i = 0; i < (threadIdx.x >> 6); ++i) base += a.wave_words[bx * (kBlock / 64) + i];
+  for (int i = 0; i < wv; ++i) base += a.wave_words[bx * (kBlock / 64) + i];
   struct PassIn {
     LaneIdx<WIDE> q;
     uint32_t k, tb, cw0;   // cw0: the tile's first coset word
   };
+  // Buffers over the wave's own tiles: 32-bit offsets, and a load past
+  // them reads zeros, so every pass issues the same loads whatever its
+  // place (the compiler then keeps exact wait counts for the loads in
+  // flight; the values of tiles past the wave's are never used).
+  constexpr uint32_t kEsz = WIDE ? 2u : 1u;
+  const uint32_t nt = end > first ? (uint32_t)(end - first) : 0u;
+  const auto rq = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(a.idx) + first * N * (int64_t)kEsz, (short)0, (int)(nt * N * kEsz), 0x00020000);
+  const auto rk = __builtin_amdgcn_make_buffer_rsrc(a.rice_k + first, (short)0, (int)nt, 0x00020000);
+  const auto rt = __builtin_amdgcn_make_buffer_rsrc(a.tile_bits + first, (short)0, (int)(nt * 4u), 0x00020000);
+  const uint32_t cwb = 4u * (uint32_t)a.coset_words;   // coset bytes per tile
+  const auto rc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(a.coset) + (a.coset_words > 0 ? first * a.coset_words : 0), (short)0,
+      (int)(nt * cwb), 0x00020000);
   auto fetch = [&](int64_t t0, PassIn& in) {
-    if (t0 < end) {   // wave-uniform
-      const int64_t tile = t0 + slot;
-      if (tile < end) {
-        in.q = load_lane<WIDE>(a.idx, tile * N + (int64_t)r * kElemsPerLane);
-        in.k = a.rice_k[tile];
-        in.tb = a.tile_bits[tile];
-        in.cw0 = a.coset_words > 0 ? a.coset[tile * a.coset_words] : 0u;
-      }
+    const uint32_t lt = (uint32_t)(t0 - first) + (uint32_t)slot;   // tile, from the wave's first
+    const uint32_t qo = (lt * N + (uint32_t)r * kElemsPerLane) * kEsz;
+#pragma unroll
+    for (int h = 0; h < (WIDE ? 2 : 1); ++h) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(qo + 16u * h), 0, 0);
+      in.q.q[h] = make_uint4(v[0], v[1], v[2], v[3]);
     }
+    in.k = __builtin_amdgcn_raw_buffer_load_b8(rk, (int)lt, 0, 0);
+    in.tb = __builtin_amdgcn_raw_buffer_load_b32(rt, (int)(lt * 4u), 0, 0);
+    in.cw0 = __builtin_amdgcn_raw_buffer_load_b32(rc, (int)(lt * cwb), 0, 0);
   };
   auto pass = [&](const PassIn& in, int64_t t0) {
     if (t0 >= end) return;   // wave-uniform
@@ -537,8 +561,13 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(RateBatch bt) {
     const bool grouped = __builtin_amdgcn_ballot_w64(live && fits && gmax > 32u) == 0;
     if (live) {
       if (r == 0) {
-        // header: k (4 bits), then the coset bits (word j at bit 4 + 32 j)
+        // header: k (4 bits), then the coset bits (word j at bit 4 + 32 j);
+        // one full coset word (E8, tile 256) without the loop
         if (a.coset_words == 0) atomicOr(tw, k);
+        else if (a.coset_bits == 32) {
+          atomicOr(tw, (in.cw0 << 4) | k);
+          atomicOr(tw + 1, in.cw0 >> 28);
+        } else
         for (int j = 0; j < a.coset_words; ++j) {
           const int nb = a.coset_bits - 32 * j;
           uint32_t cw = j == 0 ? in.cw0 : a.coset[tile * a.coset_words + j];
@@ -607,7 +636,18 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(RateBatch bt) {
       if (r == 0) a.tile_word_offset[tile] = off;
       if (tile == a.n_tiles - 1 && r == 0) a.tile_word_offset[a.n_tiles] = off + nwords;
       if (off + nwords <= a.capacity) {
-        for (uint32_t j = r; j < nwords; j += G) a.stream[off + j] = tw[j];
+        // the pass's words are [base, base + pass_words): 32-bit offsets
+        // from there (a pass holds at most 64 / G * W words)
+        const auto rs = __builtin_amdgcn_make_buffer_rsrc(a.stream + base, (short)0,
+                                                          (int)(pass_words * 4u), 0x00020000);
+        const uint32_t o0 = (uint32_t)(off - base);
+        // a fixed count of stores (the wait counts of the loads in flight
+        // stay known to the compiler)
+#pragma unroll
+        for (int s = 0; s < (W + G - 1) / G; ++s) {
+          const uint32_t j = (uint32_t)(r + s * G);
+          if (j < nwords) __builtin_amdgcn_raw_buffer_store_b32(tw[j], rs, (int)((o0 + j) * 4u), 0, 0);
+        }
       } else if (r == 0) {
         set_status(a.status, HQ_ST_STREAM_FULL);
       }
@@ -618,13 +658,26 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(RateBatch bt) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
-  // the next pass's data are loaded while this pass is computed
-  PassIn nxt;
-  fetch(first, nxt);
-  for (int64_t t0 = first; t0 < end; t0 += TPW) {
-    const PassIn cur = nxt;
-    fetch(t0 + TPW, nxt);
-    pass(cur, t0);
+  // the data of the next kPackAhead passes are loaded while this pass is
+  // computed (a pass takes a few VGPRs; the loads are what keeps HBM
+  // busy).  Slot d of the ring serves passes d, d + kPackAhead, ...: it is
+  // refilled right after its pass, so no register is copied while its load
+  // is in flight.
+  // (the prologue issues its loads slot by slot, in the loop's order, so
+  // that the waits at the loop head are the loop's own)
+  PassIn ring[kPackAhead];
+#pragma unroll
+  for (int d = 0; d < kPackAhead; ++d) {
+    fetch(first + (int64_t)d * TPW, ring[d]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int64_t t0 = first; t0 < end; t0 += (int64_t)kPackAhead * TPW) {
+#pragma unroll
+    for (int d = 0; d < kPackAhead; ++d) {
+      const int64_t t = t0 + (int64_t)d * TPW;
+      pass(ring[d], t);
+      fetch(t + (int64_t)kPackAhead * TPW, ring[d]);
+    }
   }
 }
 
