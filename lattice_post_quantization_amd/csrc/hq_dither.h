@@ -67,10 +67,41 @@ __device__ inline void e8_dither_block(const int32_t* W, int32_t* d24) {
 }
 
 // W = w 2^24 for element e of vector vec: w = 2^-23 h - 1, h the top 24 bits
-// of the counter hash of (seed, vec, e).
-__device__ inline int32_t dither_w(uint32_t seed, uint64_t vec, uint32_t e) {
-  const uint64_t key = ((uint64_t)seed << 40) ^ ((vec << 8) | e);
-  return 2 * (int32_t)(splitmix64(key) >> 40) - kOne;
+// of the counter hash (SplitMix64) of the key (seed << 40) ^ (vec << 8 | e).
+//
+// The vector's part is taken once.  With B = (seed << 40 ^ vec << 8) + the
+// additive constant (low byte 0x15), the first state is B + e, and for
+// e <= 0xEA the element moves only the low byte of it (0x15 + e, no carry).
+// So the first xor-shift's high word, and every bit it brings down into the
+// low word, are the vector's: x_lo = q ^ (0x15 + e), x_hi fixed, and of the
+// first 64-bit product only x_lo's terms change (p = lo32(x_hi C1lo) is the
+// vector's).  The last xor-shift leaves the top 24 bits unchanged, so h is
+// bits 40..63 of the second product, whose high word takes three 32-bit
+// products.  Bit-identical to the full hash for every e <= 0xEA (tile and
+// head sizes up to 128 use e < 128).
+struct DitherVec {
+  uint32_t q;   // x_lo ^ (0x15 + e)
+  uint32_t p;   // lo32(x_hi C1lo)
+};
+
+constexpr uint64_t kSmC1 = 0xBF58476D1CE4E5B9ull, kSmC2 = 0x94D049BB133111EBull;
+constexpr uint32_t kSmC1Lo = 0x1CE4E5B9u;
+
+__host__ __device__ inline DitherVec dither_vec(uint32_t seed, uint64_t vec) {
+  const uint64_t B = (((uint64_t)seed << 40) ^ (vec << 8)) + 0x9E3779B97F4A7C15ull;
+  const uint32_t bl = (uint32_t)B, bh = (uint32_t)(B >> 32);
+  const uint32_t xh = bh ^ (bh >> 30);
+  const uint32_t m = (bh << 2) | (bl >> 30);   // low word of B >> 30
+  return DitherVec{(bl & 0xFFFFFF00u) ^ m, xh * kSmC1Lo};
+}
+
+__host__ __device__ inline int32_t dither_w(const DitherVec& k, uint32_t e) {
+  const uint32_t xl = k.q ^ (0x15u + e);
+  // x C1 = x_lo C1 + 2^32 x_hi C1lo; only bits 40..63 of the second product
+  // are kept, so its low word is never formed
+  const uint64_t z1 = (uint64_t)xl * kSmC1 + ((uint64_t)k.p << 32);
+  const uint64_t z2 = z1 ^ (z1 >> 27);
+  return 2 * (int32_t)((z2 * kSmC2) >> 40) - kOne;
 }
 
 }  // namespace

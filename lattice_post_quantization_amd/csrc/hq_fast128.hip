@@ -282,10 +282,12 @@ __device__ inline void enc128_group(const EncodeLaunch& a, const uint32_t* sign_
       // the block's dither first (fewer registers live across the hash)
       int32_t d24[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       if constexpr (DITHER) {
-        const uint32_t e0 = (uint32_t)(8 * (blk & 3) + 32 * r + 64 * (blk >> 2));
+        uint32_t e0 = (uint32_t)(8 * (blk & 3) + 32 * r + 64 * (blk >> 2));
+        asm volatile("" : "+v"(e0));   // formed per block, not held across the loop
         int32_t W[8];
+        const DitherVec dk = dither_vec(a.dither_seed, vec);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) W[i] = dither_w(a.dither_seed, vec, e0 + (uint32_t)i);
+        for (int i = 0; i < 8; ++i) W[i] = dither_w(dk, e0 + (uint32_t)i);
         e8_dither_block(W, d24);
       }
 #pragma unroll
@@ -642,9 +644,11 @@ __device__ inline void dec128_group(const DecodeLaunch& a, const uint32_t* sign_
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
           int32_t W[8], d24[8];
+          uint32_t e0 = (uint32_t)(64 * r + 8 * b);
+          asm volatile("" : "+v"(e0));   // formed per block, not held across the loop
+          const DitherVec dk = dither_vec(a.dither_seed, vec);
 #pragma unroll
-          for (int i = 0; i < 8; ++i)
-            W[i] = dither_w(a.dither_seed, vec, (uint32_t)(64 * r + 8 * b + i));
+          for (int i = 0; i < 8; ++i) W[i] = dither_w(dk, e0 + (uint32_t)i);
           e8_dither_block(W, d24);
 #pragma unroll
           for (int i = 0; i < 8; ++i) {

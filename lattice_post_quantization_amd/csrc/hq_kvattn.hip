@@ -76,8 +76,9 @@ __device__ inline void block_yhat(uint32_t d0, uint32_t d1, int c, float delta, 
   }
   if (dither) {
     int32_t W[8], d24[8];                          // w and d in 2^-24 units
+    const DitherVec dk = dither_vec(seed, vec);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) W[i] = dither_w(seed, vec, (uint32_t)(8 * b + i));
+    for (int i = 0; i < 8; ++i) W[i] = dither_w(dk, (uint32_t)(8 * b + i));
     e8_dither_block(W, d24);
 #pragma unroll
     for (int i = 0; i < 8; ++i)

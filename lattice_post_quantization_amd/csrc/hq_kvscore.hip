@@ -75,10 +75,10 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreLaunch a) {
       }
       if (a.dither) {
         // d = w - Q_E8(w), w = 2^-23 h - 1, h the top 24 bits of the hash
-        const uint64_t vec = (uint64_t)(a.dither_base + key);
         int32_t W[8], d24[8];                      // w and d in 2^-24 units
+        const DitherVec dk = dither_vec(a.dither_seed, (uint64_t)(a.dither_base + key));
 #pragma unroll
-        for (int i = 0; i < 8; ++i) W[i] = dither_w(a.dither_seed, vec, (uint32_t)(8 * blk + i));
+        for (int i = 0; i < 8; ++i) W[i] = dither_w(dk, (uint32_t)(8 * blk + i));
         e8_dither_block(W, d24);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
