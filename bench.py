@@ -37,13 +37,13 @@ DEC_BYTES_PER_TILE = 256 + 4 + 4 + 512
 # sources with this sha256 and are reported only while the sources match.
 KERNEL_SOURCES = ("hq_e8fast.hip", "hq_lanes.h", "hq_device.h", "hq_internal.h")
 MEASURED_TRAFFIC = {
-    "sources_sha256": "9c7c5cc442f3b9dcf7dc4ca11cc61bf2158c80740e64605deabec7cea176b905",
-    "encode": {"bytes_per_byte": 1.0028, "valu_lane_ops_per_byte": 11.12807,
-               "valu_lane_ops_per_weight": 33.95},
-    "decode": {"bytes_per_byte": 1.0011, "valu_lane_ops_per_byte": 3.48047,
-               "valu_lane_ops_per_weight": 10.55},
-    "codec": {"bytes_per_byte": 1.0028, "valu_lane_ops_per_byte": 7.77736,
-              "valu_lane_ops_per_weight": 23.65},
+    "sources_sha256": "d05dd5dff1fa226d344a207a815cbb2289a6c3915919bfe14229a76a61978a07",
+    "encode": {"bytes_per_byte": 1.0027, "valu_lane_ops_per_byte": 10.24419,
+               "valu_lane_ops_per_weight": 31.25},
+    "decode": {"bytes_per_byte": 1.0011, "valu_lane_ops_per_byte": 3.41564,
+               "valu_lane_ops_per_weight": 10.35},
+    "codec": {"bytes_per_byte": 1.0028, "valu_lane_ops_per_byte": 7.27101,
+              "valu_lane_ops_per_weight": 22.11},
 }
 # VALU issue roof: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (a wave64 instruction
 # occupies a SIMD for 4 cycles; fp64 add / mul / fma issue at the same rate)
