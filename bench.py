@@ -396,7 +396,7 @@ def secondary(layer0, bps, dev):
                         "the E8 indices, one batched call; beside torch.matmul of bf16 X on "
                         "the decoded bf16 weights",
             "by_m": {}}
-    for m in (32, 128):
+    for m in (32, 128, 256):
         xm = [torch.randn(m, e["idx"].shape[1], device=dev) for e in encs]
         ym = [torch.empty(m, e["idx"].shape[0], device=dev) for e in encs]
         items = (hq.GemvItem * len(encs))()

@@ -335,6 +335,236 @@ __global__ __launch_bounds__(64 * W, 2) void gemm_kernel(GemmBatch bt) {
   }
 }
 
+// Wide tiles for many vectors: a block of eight waves (two per SIMD) owns
+// 256 rows x 128 vectors; wave w owns rows 32 w .. 32 w + 31 and all 128
+// vectors as four 32-vector fragments, so each step (16 k) forms one A
+// fragment and reads eight B fragments for eight products: half the A
+// decoding per product of gemm_kernel's 32 x 64 wave tile, at the same LDS
+// reads per product.  A slice is staged as four quarters of 64 k: the
+// rotated inputs (128 vectors x 64 k, hi and lo), the index bytes (256 rows
+// x 64 bytes) and the slice's coset words and scales are copied by
+// direct-to-LDS buffer loads into one of three buffers, two quarters ahead
+// of the one computed; one barrier per quarter.  The per-slice products
+// accumulate exactly as in gemm_kernel (32 matrix-core accumulations per
+// slice, then out += (Delta / 32) acc), so the results obey the same bound.
+//
+// LDS layout of a quarter: input chunk q (8 k) of vector j at slot
+// 8 j + (q ^ ((j >> 1) & 7)) of its term; 16-byte chunk c of block-row r's
+// 64 index bytes at slot 4 r + (c ^ ((r >> 2) & 3)): the 16 lanes that a
+// 16-byte fragment read serves together hit the 16 different 16-byte bank
+// groups of gfx950's 64 banks.
+constexpr int kWideRows = 256;
+constexpr int kWideVecs = 128;
+
+// s_waitcnt immediates (gfx9 layout: vmcnt in bits 3:0 and 15:14, expcnt
+// and lgkmcnt at their no-wait values)
+constexpr int kWaitVm0 = 0x0F70, kWaitVm7 = 0x0F77;
+
+typedef uint4 WideB[2][1024];   // a quarter's inputs: [hi, lo][slot]
+typedef uint4 WideA[1024 + 128];  // a quarter's index bytes [slot], then the slice's
+                                  // coset words [256] and scales [256] of the block's rows
+
+__global__ __launch_bounds__(512, 1) void gemm_wide_kernel(GemmBatch bt) {
+  // three buffers as separate objects, so that the compiler sees that a
+  // quarter's fragment reads and the loads filling another buffer do not
+  // overlap
+  __shared__ WideB sb0, sb1, sb2;
+  __shared__ WideA sa0, sa1, sa2;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5, li = lane & 31;
+  const int64_t g = blockIdx.x;
+  const GemmItem& a = bt.it[item_at(bt, g, [](const GemmItem& t) { return t.blk0; })];
+  const int64_t local = g - a.blk0;
+  const int64_t vblocks = (bt.m + kWideVecs - 1) / kWideVecs;
+  const int64_t rblocks = (a.rows + kWideRows - 1) / kWideRows;
+  const int64_t k = local >> 3;
+  const int64_t rt = (k / vblocks) * 8 + (local & 7);
+  if (rt >= rblocks * a.kchunks) return;
+  const int64_t chunk = rt / rblocks;
+  const int64_t rowB = (rt % rblocks) * kWideRows;
+  const int64_t vec0 = (k % vblocks) * kWideVecs;
+  const int64_t slices = a.cols / kSliceK;
+  const int64_t t_begin = chunk * a.spc;
+  const int64_t t_end = t_begin + a.spc < slices ? t_begin + a.spc : slices;
+  const int nq = (int)(4 * (t_end - t_begin));
+
+  const int64_t live_vecs = bt.m - vec0 < kWideVecs ? bt.m - vec0 : kWideVecs;
+  const auto xh_rs = out_rsrc(const_cast<uint16_t*>(a.xh) + vec0 * a.cols,
+                              (uint32_t)(live_vecs * a.cols * 2));
+  const auto xl_rs = out_rsrc(const_cast<uint16_t*>(a.xl) + vec0 * a.cols,
+                              (uint32_t)(live_vecs * a.cols * 2));
+  const int64_t live_block = a.rows - rowB < kWideRows ? a.rows - rowB : kWideRows;
+  const auto idx_rs = out_rsrc(const_cast<int8_t*>(a.idx) + rowB * a.cols,
+                               (uint32_t)(live_block * a.cols));
+  // the words of block rows 64 (w % 4) .. + 63: coset words for waves 0-3,
+  // scales for waves 4-7
+  const int64_t wrow = rowB + 64 * (w & 3);
+  const int64_t wrest = a.rows - wrow;
+  const int64_t wlive = wrest < 0 ? 0 : (wrest < 64 ? wrest : 64);
+  const auto wd_rs = out_rsrc(w < 4 ? (void*)(a.coset + wrow * slices) : (void*)(a.scale + wrow * slices),
+                              (uint32_t)(wlive * slices * 4));
+
+  // Loads of quarter qq (slice t_begin + qq / 4, k offset 64 (qq % 4)), 7
+  // per wave, all into LDS: two 1 KB loads of each input term, two of index
+  // bytes and one of words.  Quarters past the range load the last one
+  // again, so every group has the same size and the waits below are fixed
+  // counts.
+  auto issue = [&](int qq, WideB& B, WideA& A) {
+    qq = qq < nq ? qq : nq - 1;
+    const int64_t t = t_begin + qq / 4;
+    const int64_t kofs = t * kSliceK + 64 * (qq & 3);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int S = 128 * w + 64 * i + lane;
+      const int j = S >> 3, q = (S & 7) ^ ((j >> 1) & 7);
+      const int goff = (int)((j * a.cols + kofs + 8 * q) * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xh_rs, lds_ptr(&B[0][128 * w + 64 * i]), 16,
+                                               goff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xl_rs, lds_ptr(&B[1][128 * w + 64 * i]), 16,
+                                               goff, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int S = 128 * w + 64 * i + lane;
+      const int r = S >> 2, c = (S & 3) ^ ((r >> 2) & 3);
+      const int goff = (int)(r * a.cols + kofs + 16 * c);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(idx_rs, lds_ptr(&A[128 * w + 64 * i]), 16, goff,
+                                               0, 0, 0);
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(wd_rs, lds_ptr(&A[1024 + 16 * w]), 4,
+                                             (int)((lane * slices + t) * 4), 0, 0, 0);
+  };
+
+  f32x16 out[4], acc[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    out[f] = (f32x16){};
+    acc[f] = (f32x16){};
+  }
+
+  // one step's eight B fragments (block q of the quarter: vector fragment f,
+  // hi and lo) and its products with the A fragment af
+  auto ldb = [&](const WideB& B, int q, uint4* bf) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const int j = 32 * f + li;
+      const int slot = 8 * j + (q ^ ((j >> 1) & 7));
+      bf[2 * f] = B[0][slot];
+      bf[2 * f + 1] = B[1][slot];
+    }
+  };
+  auto products = [&](const uint4* bf, bf16x8 af) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      acc[f] = mfma32(af, __builtin_bit_cast(bf16x8, bf[2 * f]), acc[f]);
+      acc[f] = mfma32(af, __builtin_bit_cast(bf16x8, bf[2 * f + 1]), acc[f]);
+    }
+  };
+
+  // quarter qq from buffers (B, A); quarter qq + 2 is loaded into (Bn, An)
+  auto quarter = [&](int qq, const WideB& B, const WideA& A, WideB& Bn, WideA& An) {
+    // this wave's loads of quarter qq are complete (vector memory loads
+    // complete in order; only quarter qq + 1's are younger), then every
+    // wave's are, and every wave has finished quarter qq - 1, whose
+    // buffers quarter qq + 2 refills
+    __builtin_amdgcn_s_waitcnt(kWaitVm7);
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    issue(qq + 2, Bn, An);
+    if (qq >= nq) return;
+    const int u = qq & 3;
+    const uint32_t* wl = reinterpret_cast<const uint32_t*>(&A[1024]);
+    const uint32_t cw = wl[32 * w + li];
+    const int row = 32 * w + li;
+    // this lane half's blocks 4 v + 2 h + {0, 1} for steps 2 v, 2 v + 1
+    // (index chunk 2 v + h of its row)
+    const uint4 ab0 = A[4 * row + ((0 + h) ^ ((row >> 2) & 3))];
+    const uint4 ab1 = A[4 * row + ((2 + h) ^ ((row >> 2) & 3))];
+    uint4 bc[8], bn[8];
+    ldb(B, 2 * h, bc);
+    // steps 0..3: the next step's B fragments are read, and its A fragment
+    // formed, before this step's products are issued
+    bf16x8 af = a_fragment(ab0.x, ab0.y, (cw >> (8 * u + 2 * h)) & 1u);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int qn = 4 * ((s + 1) >> 1) + 2 * h + ((s + 1) & 1);
+      bf16x8 afn = af;
+      if (s < 3) {
+        ldb(B, qn, bn);
+        const uint4& ab = (s + 1) < 2 ? ab0 : ab1;
+        afn = a_fragment((s + 1) & 1 ? ab.z : ab.x, (s + 1) & 1 ? ab.w : ab.y,
+                         (cw >> (8 * u + qn)) & 1u);
+      }
+      products(bc, af);
+      // each product issued with one fragment read and a few of the next A
+      // fragment's instructions, so that the matrix core, the LDS and the
+      // VALU work side by side
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bc[i] = bn[i];
+      af = afn;
+    }
+    if (u == 3) {
+      // ---- out += (Delta / 32) acc; acc register i holds row
+      // 8 (i / 4) + 4 h + i % 4 of the wave
+      const float* sl = reinterpret_cast<const float*>(wl + 256 + 32 * w);
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const float4 ds = *reinterpret_cast<const float4*>(&sl[8 * g4 + 4 * h]);
+        const float dv[4] = {ds.x * 0.03125f, ds.y * 0.03125f, ds.z * 0.03125f, ds.w * 0.03125f};
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            out[f][4 * g4 + i] = fmaf(dv[i], acc[f][4 * g4 + i], out[f][4 * g4 + i]);
+            acc[f][4 * g4 + i] = 0.0f;
+          }
+      }
+    }
+  };
+
+  issue(0, sb0, sa0);
+  issue(1, sb1, sa1);
+  for (int q0 = 0; q0 < nq; q0 += 3) {
+    quarter(q0, sb0, sa0, sb2, sa2);
+    quarter(q0 + 1, sb1, sa1, sb0, sa0);
+    quarter(q0 + 2, sb2, sa2, sb1, sa1);
+  }
+  // no load into this block's LDS may land after the block ends
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+
+  // ---- y[vec][row] (or this range's partial sums); rows past the matrix
+  // go to an offset the hardware drops (one buffer per 32-vector fragment
+  // keeps the 32-bit offsets in range)
+  const int64_t row0 = rowB + 32 * w;
+  float* dst = a.kchunks > 1 ? a.part + chunk * bt.m * a.rows : a.y;
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    const int64_t fv = live_vecs - 32 * f;
+    const auto y_rs = out_rsrc(dst + (vec0 + 32 * f) * a.rows,
+                               (uint32_t)((fv < 0 ? 0 : (fv < 32 ? fv : 32)) * a.rows * 4));
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int64_t r0 = row0 + 8 * g4 + 4 * h;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t off =
+            r0 + i < a.rows ? (uint32_t)((li * a.rows + r0 + i) * 4) : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out[f][4 * g4 + i]), y_rs,
+                                              (int)off, 0, 0);
+      }
+    }
+  }
+}
+
 // y = the sum of the ranges' partial sums, in range order (matrices with
 // more than one range)
 __global__ __launch_bounds__(256) void sum_kernel(GemmBatch bt) {
@@ -357,11 +587,19 @@ void launch_nf(const GemmBatch& b, hipStream_t s) {
   hipLaunchKernelGGL((gemm_kernel<NF, W>), dim3((unsigned)b.n_blocks), dim3(64 * W), 0, s, b);
 }
 
-// one 32-vector fragment per block for m <= 32 (4 waves, two blocks per
-// CU), else two (8 waves, one block per CU: the double-buffered inputs take
-// 128 KiB of LDS)
-int nf_for(int32_t m) { return m <= 32 ? 1 : 2; }
-int waves_for(int nf) { return nf == 1 ? 4 : 8; }
+// Block shapes by m: one 32-vector fragment per block for m <= 32 (4 waves
+// of 32 rows, two blocks per CU); two up to m = 192 (8 waves of 32 rows,
+// one block per CU: the double-buffered inputs take 128 KiB of LDS); above,
+// the wide tiles (8 waves of 32 rows x 128 vectors, one block per CU),
+// which measured faster from m = 256 on (a Llama-shaped layer: 328 against
+// 394 us at m = 256, 618 against 684 us at m = 512) and slower below
+// (264 against 219 us at m = 128).
+constexpr int32_t kWideMinM = 193;
+int shape_for(int32_t m) { return m <= 32 ? 1 : (m < kWideMinM ? 2 : 3); }
+int64_t vecs_per_block(int shape) { return shape == 1 ? 32 : (shape == 2 ? 64 : kWideVecs); }
+int64_t rows_per_block(int shape) { return shape == 1 ? 128 : 256; }
+int64_t threads_per_block(int shape) { return shape == 1 ? 256 : 512; }
+int64_t slots_for(int shape) { return shape == 1 ? 512 : 256; }
 
 }  // namespace
 
@@ -371,15 +609,16 @@ int waves_for(int nf) { return nf == 1 ? 4 : 8; }
 // ceil(slices / L) ranges of near-equal length.  Few ranges keep the
 // partial sums (written and read back once) small next to the index bytes.
 void gemm_plan(GemmBatch& b) {
-  const int nf = nf_for(b.m), waves = waves_for(nf);
-  const int64_t vblocks = (b.m + 32 * nf - 1) / (32 * nf);
-  const int64_t slots = nf == 1 ? 512 : 256;
+  const int shape = shape_for(b.m);
+  const int64_t vpb = vecs_per_block(shape), rpb = rows_per_block(shape);
+  const int64_t vblocks = (b.m + vpb - 1) / vpb;
+  const int64_t slots = slots_for(shape);
   int64_t len = 16;
   for (; len > 1; --len) {
     int64_t blocks = 0;
     for (int i = 0; i < b.n; ++i) {
       const int64_t slices = b.it[i].cols / kSliceK;
-      blocks += (b.it[i].rows + 32 * waves - 1) / (32 * waves) * vblocks * ((slices + len - 1) / len);
+      blocks += (b.it[i].rows + rpb - 1) / rpb * vblocks * ((slices + len - 1) / len);
     }
     if (blocks >= slots) break;
   }
@@ -395,19 +634,21 @@ void gemm_plan(GemmBatch& b) {
 }
 
 bool gemm_fits_launch(const GemmBatch& b) {
-  const int nf = nf_for(b.m), waves = waves_for(nf);
-  const int64_t vblocks = (b.m + 32 * nf - 1) / (32 * nf);
+  const int shape = shape_for(b.m);
+  const int64_t vpb = vecs_per_block(shape), rpb = rows_per_block(shape);
+  const int64_t vblocks = (b.m + vpb - 1) / vpb;
   int64_t blocks = 0, split = 0, sum = 0;
   for (int i = 0; i < b.n; ++i) {
     const GemmItem& it = b.it[i];
-    const int64_t tasks = (it.rows + 32 * waves - 1) / (32 * waves) * it.kchunks;
+    const int64_t tasks = (it.rows + rpb - 1) / rpb * it.kchunks;
     blocks += (tasks + 7) / 8 * 8 * vblocks;
     split += (int64_t)b.m * (it.cols / kSliceK);
     if (it.kchunks > 1) sum += (int64_t)b.m * it.rows;
   }
   // every grid below 2^32 work-items
   const int64_t lim = (int64_t)1 << 32;
-  return blocks * 64 * waves < lim && (split + 3) / 4 * 256 < lim && (sum + 255) / 256 * 256 < lim;
+  return blocks * threads_per_block(shape) < lim && (split + 3) / 4 * 256 < lim &&
+         (sum + 255) / 256 * 256 < lim;
 }
 
 size_t gemm_item_workspace(const GemmItem& it, int32_t m) {
@@ -416,8 +657,9 @@ size_t gemm_item_workspace(const GemmItem& it, int32_t m) {
 }
 
 void gemm_layout(GemmBatch& b, char* workspace) {
-  const int nf = nf_for(b.m), waves = waves_for(nf);
-  const int64_t vblocks = (b.m + 32 * nf - 1) / (32 * nf);
+  const int shape = shape_for(b.m);
+  const int64_t rpb = rows_per_block(shape), vpb = vecs_per_block(shape);
+  const int64_t vblocks = (b.m + vpb - 1) / vpb;
   gemm_plan(b);
   b.n_blocks = b.n_split = b.n_sum = 0;
   for (int i = 0; i < b.n; ++i) {
@@ -429,7 +671,7 @@ void gemm_layout(GemmBatch& b, char* workspace) {
     workspace += gemm_item_workspace(it, b.m);
     // blocks: (row ranges x slice ranges) rounded up to the eight XCDs,
     // times the vector blocks
-    const int64_t tasks = (it.rows + 32 * waves - 1) / (32 * waves) * it.kchunks;
+    const int64_t tasks = (it.rows + rpb - 1) / rpb * it.kchunks;
     it.blk0 = b.n_blocks;
     it.split0 = b.n_split;
     it.sum0 = b.n_sum;
@@ -442,10 +684,13 @@ void gemm_layout(GemmBatch& b, char* workspace) {
 
 hipError_t launch_gemm(const GemmBatch& b, hipStream_t s) {
   hipLaunchKernelGGL(split_kernel, dim3((unsigned)((b.n_split + 3) / 4)), dim3(256), 0, s, b);
-  if (nf_for(b.m) == 1)
+  const int shape = shape_for(b.m);
+  if (shape == 1)
     launch_nf<1, 4>(b, s);
-  else
+  else if (shape == 2)
     launch_nf<2, 8>(b, s);
+  else
+    hipLaunchKernelGGL(gemm_wide_kernel, dim3((unsigned)b.n_blocks), dim3(512), 0, s, b);
   if (b.n_sum > 0)
     hipLaunchKernelGGL(sum_kernel, dim3((unsigned)((b.n_sum + 255) / 256)), dim3(256), 0, s, b);
   return hipGetLastError();

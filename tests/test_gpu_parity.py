@@ -1046,13 +1046,14 @@ def _gemm_case(rng, rows, cols, m, seed):
     return enc, torch.from_numpy(x).cuda(), y_ref, tol
 
 
-@pytest.mark.parametrize("m", [1, 5, 32, 33, 64, 100])
+@pytest.mark.parametrize("m", [1, 5, 32, 33, 64, 100, 200, 300])
 def test_gemm_parity(m):
     """hq_gemm against the oracle: Y = X W^T with W the oracle's fp64 decode
     of the oracle's own encode (ragged 37 x 1536, 300 x 768 and a Llama-shaped
     k projection 1024 x 4096, RHT seed 5), m vectors (one and two 32-vector
-    fragments per block, several vector blocks), within the bound of
-    _gemm_case.  Two calls give the same bits."""
+    fragments per block, the 128-vector wide tiles above 192, several and
+    ragged vector blocks), within the bound of _gemm_case.  Two calls give
+    the same bits."""
     rng = np.random.default_rng(61 + m)
     for rows, cols in ((37, 1536), (300, 768), (1024, 4096)):
         label = "gemm %dx%d m=%d" % (rows, cols, m)
@@ -1066,7 +1067,7 @@ def test_gemm_parity(m):
         assert torch.equal(y, y2), label + " determinism"
 
 
-@pytest.mark.parametrize("m", [3, 40])
+@pytest.mark.parametrize("m", [3, 40, 130, 260])
 def test_gemm_batch_parity(m):
     """hq_gemm_batch on ten oracle-encoded matrices of mixed shapes (ragged
     row counts, one and many slices, split and unsplit slice ranges; two
@@ -1094,7 +1095,8 @@ def test_gemm_batch_parity(m):
 def test_layer_gemm_and_gemv_as_benchmarked():
     """The Llama-3.1-8B-shaped layer as bench.py runs its products: the seven
     matrices drawn on the GPU and encoded in one batch (E8/256, 4 bps, RHT
-    seed 0), then hq_gemm_batch at m = 32 and 128 and hq_gemv_batch at m = 1.
+    seed 0), then hq_gemm_batch at m = 32, 128 and 256 and hq_gemv_batch at
+    m = 1.
     Property checked at this size: each product equals X W^T for the fp32
     weights hq_decode_tiles gives, within the GEMM bound
     (2^-16 + (slices + 80) 2^-24) B plus the fp32 decode's rounding
@@ -1109,7 +1111,7 @@ def test_layer_gemm_and_gemv_as_benchmarked():
           for e in encs]
     gen = torch.Generator(device=dev)
     gen.manual_seed(23)
-    for m in (32, 128, 1):
+    for m in (32, 128, 256, 1):
         say("case: layer products m=%d" % m)
         xm = [torch.randn(m, w.shape[1], device=dev, generator=gen) for w in ws]
         if m == 1:
