@@ -430,9 +430,13 @@ def test_gemm_validation_codes():
                           (4, 256, 0), (4, 256, 65537), (1 << 16, 256, 1 << 16),
                           (4, 1 << 16, 1 << 16), (0, 256, 1)):
         assert lib.hq_gemm_workspace_bytes(rows, cols, m) == 0, (rows, cols, m)
-    # the largest accepted sizes stay within one launch's grid (or are refused)
+    # the largest accepted sizes stay within one launch's grid (or are refused):
+    # one matrix at the row and column limits with 256 vectors takes the wide
+    # tiles (256 rows x 128 vectors per 512-thread block, at most 64 slice
+    # ranges), 2^22 blocks at most, so it is accepted; eight large matrices
+    # at m = 65536 pass 2^32 partial sums and are refused
     assert lib.hq_gemm_workspace_bytes(1 << 15, 1 << 15, 1 << 16) > 0
-    assert lib.hq_gemm_workspace_bytes(1 << 23, 1 << 22, 256) == 0
+    assert lib.hq_gemm_workspace_bytes(1 << 23, 1 << 22, 256) > 0
     big = (hq.GemvItem * 8)()
     for i in range(8):
         big[i] = hq.GemvItem(FAKE, FAKE, FAKE, 1 << 15, 1 << 15, FAKE, FAKE)

@@ -8,7 +8,9 @@ both sides.  Indices must match bit for bit except at oracle near-ties
 (bit-exact where the arithmetic is exact); Rice results exact.
 """
 
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -713,12 +715,14 @@ def test_stack_sampled_parity_as_benchmarked():
     """The 32-layer Llama-3.1-8B-shaped stack exactly as bench.py runs it:
     each layer drawn on the GPU, one batched encode of its seven matrices and
     one batched decode (E8, tile 256, 4 bps, RHT seed = layer index).  Every
-    4099th tile of every matrix is copied to the host and checked against the
+    257th tile of every matrix is copied to the host and checked against the
     oracle: scale, indices and cosets, Rice k and bits, and the decoded bf16
-    of tiles whose indices match."""
+    of tiles whose indices match.  The counts over the 32 layers are printed
+    and, when HQ_PARITY_RECORD names a file, appended to it."""
     dev = torch.device("cuda")
-    stride = 4099
+    stride = 257
     n_checked = 0
+    tot = {"tiles": 0, "scale_skipped": 0, "blocks": 0, "mismatch": 0, "near_ties": 0}
     for layer in range(32):
         say("case: stack layer %d" % layer)
         xs = [workloads.llama_stack_torch(layer, m, dev) for m in range(len(workloads.LLAMA_LAYER))]
@@ -744,8 +748,13 @@ def test_stack_sampled_parity_as_benchmarked():
         keep = np.nonzero(g["scale"].astype(np.float64) == ora["scale"])[0]
         sub = {k: (v[keep] if isinstance(v, np.ndarray) and v.shape[:1] == (len(X),) else v)
                for k, v in ora.items()}
-        _, _, _, ok = T.compare_indices(g["idx"][keep], g["coset"][keep], sub, "E8", 256,
-                                        "stack layer %d" % layer)
+        nbad, nnear, nblk, ok = T.compare_indices(g["idx"][keep], g["coset"][keep], sub, "E8", 256,
+                                                  "stack layer %d" % layer)
+        tot["tiles"] += len(X)
+        tot["scale_skipped"] += int(np.sum(~(g["scale"].astype(np.float64) == ora["scale"])))
+        tot["blocks"] += nblk
+        tot["mismatch"] += nbad
+        tot["near_ties"] += nnear
         assert np.array_equal(g["rice_k"][keep][ok].astype(np.int64), sub["rice_k"][ok]), layer
         assert np.array_equal(g["tile_bits"][keep][ok].astype(np.int64), sub["tile_bits"][ok]), layer
         yo = codec.bf16_rne(codec.decode(sub["idx"][ok], sub["coset"][ok], sub["scale"][ok],
@@ -753,6 +762,17 @@ def test_stack_sampled_parity_as_benchmarked():
         assert np.array_equal(g["y"][keep][ok].reshape(-1, 256), codec.bf16_bits(yo)), layer
         n_checked += len(X)
     say("stack: %d sampled tiles checked" % n_checked)
+    rec = {"workload": "llama3.1-8b-shaped 32-layer stack as benchmarked (drawn on the GPU, "
+                       "batched encode and bf16 decode per layer, RHT seed = layer), every "
+                       "257th tile of every matrix", "lattice": "E8", "tile": 256, "bps": 4.0}
+    rec.update(tot)
+    rec.update({"near_tie_fraction": tot["near_ties"] / tot["blocks"],
+                "mismatch_fraction": tot["mismatch"] / tot["blocks"]})
+    say("  " + json.dumps(rec))
+    path = os.environ.get("HQ_PARITY_RECORD")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(rec) + "\n")
 
 
 def _stream_dev(words, off):
