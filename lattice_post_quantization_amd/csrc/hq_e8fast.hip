@@ -305,19 +305,48 @@ __device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const
       }
     }
   }
-  // element bit 6 (row bit 0) <-> register bit 5, then butterfly
+  // Element bits 4, 5 (register bits 4, 5) trade places with element bits
+  // 6, 7 (the row bits) through the wave's 4 KB output buffer, in eight
+  // rounds of one register pair (element bits 0-3 = 2q, 2q + 1): lane (t, r)
+  // sends register 2q + {0, 1} + 16 i4 + 32 i5 to row i5 + 2 i4 of its tile,
+  // which keeps it as register 2q + {0, 1} + 16 r1 + 32 r0.  16-byte slot
+  // (16 t + 4 (destination row) + (source row)) ^ t: the 16 lanes of a row
+  // hit 16 different bank groups.  LDS instructions take no VALU slots.
+  {
+    const uint32_t ot = (uint32_t)t;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      wave_lds_sync();
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int i4 = x & 1, i5 = x >> 1;
+        const int j = 2 * q + 16 * i4 + 32 * i5;
+        const uint64_t lo = (uint64_t)__double_as_longlong(v[j]);
+        const uint64_t hi = (uint64_t)__double_as_longlong(v[j + 1]);
+        ost[(16 * ot + 4 * (uint32_t)(i5 + 2 * i4) + (uint32_t)row) ^ ot] =
+            make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32));
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int src = 0; src < 4; ++src) {
+        const uint4 d = ost[(16 * ot + 4 * (uint32_t)row + (uint32_t)src) ^ ot];
+        const int j = 2 * q + 16 * (src >> 1) + 32 * (src & 1);
+        v[j] = __longlong_as_double((long long)(((uint64_t)d.y << 32) | d.x));
+        v[j + 1] = __longlong_as_double((long long)(((uint64_t)d.w << 32) | d.z));
+      }
+    }
+    wave_lds_sync();
+  }
+  // butterflies on element bit 6 (register bit 5) and bit 7 (register bit 4)
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    swap_f64<false>(v[i], v[i + 32]);
     const double x = v[i], y = v[i + 32];
     v[i] = x + y;
     v[i + 32] = x - y;
   }
-  // element bit 7 (row bit 1) <-> register bit 4, then butterfly
 #pragma unroll
   for (int i = 0; i < 64; ++i) {
     if (!(i & 16)) {
-      swap_f64<true>(v[i], v[i + 16]);
       const double x = v[i], y = v[i + 16];
       v[i] = x + y;
       v[i + 16] = x - y;
