@@ -556,7 +556,8 @@ hq_status hq_encode_decode_batch(const hq_params* enc_p, int32_t x_dtype, int32_
   const int32_t le = live_items(enc_p, enc_count, enc_items);
   const int32_t ld = live_items(dec_p, dec_count, dec_items);
   // (the fused kernel encodes without rate control)
-  if (!a.rate_control && encode_batch_fast(a) && e8_fast_decode_ok(ad) && le <= kMaxItems &&
+  if (!a.rate_control && a.tile == 256 && ad.tile == 256 && encode_batch_fast(a) &&
+      e8_fast_decode_ok(ad) && le <= kMaxItems &&
       ld <= kMaxItems && le + ld > 0) {
     EncBatch b;
     DecBatch bd;

@@ -149,7 +149,31 @@ __device__ inline uint32_t e8_lane(const double* v, double K, uint32_t* packed, 
 // with kt the smallest k with S <= 256 * 2^(k+1): D_{kt+1} <= 256, and
 // D_k > 256 for k <= kt - 2 (strictly, so no smaller k ties).  Only
 // kt - 1, kt, kt + 1 remain.
+// Value of the lane in the same row with the neighbouring tile index
+// (lane ^ 1): the other half of a 512-element tile.
+__device__ inline uint32_t pair_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);
+}
+
+__device__ inline double pair_f64(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = pair_u32((uint32_t)u), hi = pair_u32((uint32_t)(u >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Sum over the lanes that hold one tile: the four rows of lane t for
+// N = 256, and of lanes t and t ^ 1 for N = 512.
+template <int N>
+__device__ inline uint32_t tile_total_u32(uint32_t v) {
+  v = tile_sum_u32(v);
+  if constexpr (N == 512) v += pair_u32(v);
+  return v;
+}
+
+template <int N>
 __device__ inline uint32_t rice_tile(const uint32_t* packed, int& bk) {
+  static_assert(N == 256 || N == 512, "tile 256 or 512");
+  constexpr int kLog2N = N == 256 ? 8 : 9;
   uint32_t zz[16];
   uint32_t S = 0;
 #pragma unroll
@@ -157,9 +181,9 @@ __device__ inline uint32_t rice_tile(const uint32_t* packed, int& bk) {
     zz[q] = zigzag4(packed[q]);
     S = byte_sum(zz[q], S);
   }
-  S = tile_sum_u32(S);
-  // kt = min(8, smallest k with S <= 256 2^(k + 1)); S <= 255 * 256
-  int kt = S <= 512u ? 0 : 23 - (int)__builtin_clz(S - 1u);
+  S = tile_total_u32<N>(S);
+  // kt = min(8, smallest k with S <= N 2^(k + 1)); S <= 255 N
+  int kt = S <= 2u * N ? 0 : 31 - kLog2N - (int)__builtin_clz(S - 1u);
   kt = kt > 8 ? 8 : kt;
   // The candidates k0, k0 + 1, k0 + 2 with k0 = min(max(kt - 1, 0), 6)
   // contain kt - 1 .. kt + 1 within [0, 8]; the extra one (k0 + 2 when
@@ -179,9 +203,9 @@ __device__ inline uint32_t rice_tile(const uint32_t* packed, int& bk) {
     sx = byte_sum(x, sx);
     cx += (uint32_t)__builtin_popcount(x);
   }
-  r0 = tile_sum_u32(r0);
-  sx = tile_sum_u32(sx);
-  cx = tile_sum_u32(cx);
+  r0 = tile_total_u32<N>(r0);
+  sx = tile_total_u32<N>(sx);
+  cx = tile_total_u32<N>(cx);
   const uint32_t c1 = (sx >> k0) - cx, c0 = cx - c1;
   const uint32_t R[3] = {r0, r0 + (c0 << k0), r0 + (c0 << k0) + (c1 << (k0 + 1))};
   uint32_t best = 0xFFFFFFFFu;
@@ -189,7 +213,7 @@ __device__ inline uint32_t rice_tile(const uint32_t* packed, int& bk) {
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
     const int k = k0 + j;
-    const uint32_t L = ((S - R[j]) >> k) + 256u * (uint32_t)(1 + k);
+    const uint32_t L = ((S - R[j]) >> k) + (uint32_t)N * (uint32_t)(1 + k);
     if (L < best) { best = L; bk = k; }
   }
   return best;
@@ -233,7 +257,7 @@ __device__ inline float rc_search(const EncodeLaunch& a, const double* v, double
     uint32_t packed[16];
     (void)e8_lane(v, K, packed, active && in_range);
     int bk;
-    const uint32_t bits = 4u + 32u + rice_tile(packed, bk);
+    const uint32_t bits = 4u + 32u + rice_tile<256>(packed, bk);
     const bool f = in_range && bits <= a.rc_budget;
     if (active) {
       if (top && !f) {
@@ -252,12 +276,18 @@ __device__ inline float rc_search(const EncodeLaunch& a, const double* v, double
 // One group of 16 tiles held by a wave (w: this lane's 64 bf16 of its tile).
 // (scale_in: the caller's scale of this lane's tile when not automatic.)
 // RC: per-tile rate control (auto scales only).
-template <bool RC>
+// N = 512: the wave holds 8 tiles; tile t / 2 of the group is held as its
+// halves t (elements 256 (t & 1) + [0, 256)), each laid out as a tile of
+// 256, so the loads, the index stores and the coset words (one per half)
+// are those of 16 tiles of 256; element bit 8 is the lane's t & 1, and its
+// butterfly runs between lanes t and t ^ 1.
+template <bool RC, int N = 256>
 __device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const uint32_t* sign_tab,
                                  int64_t group, int t, int row, const uint32_t* w, float scale_in,
                                  uint4* ost) {
-
-  const uint4* st = reinterpret_cast<const uint4*>(sign_tab + row * 32);
+  static_assert(N == 256 || (N == 512 && !RC), "tile 256, or 512 without rate control");
+  const uint4* st = reinterpret_cast<const uint4*>(
+      sign_tab + (N == 512 ? (4 * (t & 1) + row) : row) * 32);
   double v[64];
   double ss = 0.0;
 #pragma unroll
@@ -279,10 +309,11 @@ __device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const
   // ---- scale: bf16_rne(rms * c) (auto) or the caller's; the norm bound
   // sqrt(sum x^2)/Delta < 126 keeps every grid value in range
   ss = tile_sum_f64(ss);
+  if constexpr (N == 512) ss = ss + pair_f64(ss);
   uint32_t status = 0;
   float delta;
   if (a.auto_scale) {
-    delta = bf16_round_to_f32(sqrt(ss / 256.0) * a.c);
+    delta = bf16_round_to_f32(sqrt(ss / (double)N) * a.c);
     if (delta == 0.0f) delta = 1.0f;
   } else {
     delta = scale_in;
@@ -352,6 +383,13 @@ __device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const
       v[i + 16] = x - y;
     }
   }
+  if constexpr (N == 512) {
+    // element bit 8 (the lane's t & 1): x + y in the lower half's lane,
+    // x - y in the upper half's (one rounding each, as the sums)
+    const double sg = (t & 1) ? -1.0 : 1.0;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) v[i] = fma(v[i], sg, pair_f64(v[i]));
+  }
   // Now register i holds element bits (i0 i1 i2 i3 | i4 = b7 | i5 = b6) and the
   // lane's row bits hold (r0 = b5, r1 = b4).
   if constexpr (RC) {
@@ -395,7 +433,7 @@ __device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const
   // S <= 256 * 2^(k+1): D_{kt+1} <= 256, and D_k > 256 for k <= kt - 2
   // (strictly, so no smaller k ties).  Only kt - 1, kt, kt + 1 remain.
   int bk;
-  const uint32_t best = rice_tile(packed, bk);
+  const uint32_t best = rice_tile<N>(packed, bk);
 
   // ---- store.  Chunk k (blocks 2k, 2k + 1: element bits 0-3 inside) has
   // element bit 7 = k bit 0, bit 6 = k bit 1, bit 5 = row bit 0 and bit 4 =
@@ -411,15 +449,29 @@ __device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const
   store_group<4>(out_rsrc(it.idx + tile0 * 256, live * 256u), ch, ost, t, row * 16 + t, wb,
                  [](int k) { return (uint32_t)(8 * (k & 1) + 4 * (k >> 1)); },
                  store_read_base(t, row));
-  if (a.auto_scale)
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(delta), out_rsrc(it.scale + tile0, live * 4u),
-                                          (int)row0_offset(t, row, 4), 0, 0);
   __builtin_amdgcn_raw_buffer_store_b32(coset_word, out_rsrc(it.coset + tile0, live * 4u),
                                         (int)row0_offset(t, row, 4), 0, 0);
-  __builtin_amdgcn_raw_buffer_store_b8((uint8_t)bk, out_rsrc(it.rice_k + tile0, live),
-                                       (int)row0_offset(t, row, 1), 0, 0);
-  __builtin_amdgcn_raw_buffer_store_b32(4u + 32u + best, out_rsrc(it.tile_bits + tile0, live * 4u),
-                                        (int)row0_offset(t, row, 4), 0, 0);
+  if constexpr (N == 256) {
+    if (a.auto_scale)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(delta), out_rsrc(it.scale + tile0, live * 4u),
+                                            (int)row0_offset(t, row, 4), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)bk, out_rsrc(it.rice_k + tile0, live),
+                                         (int)row0_offset(t, row, 1), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(4u + 32u + best, out_rsrc(it.tile_bits + tile0, live * 4u),
+                                          (int)row0_offset(t, row, 4), 0, 0);
+  } else {
+    // per-tile results of tile t / 2, from the lower half's lane of row 0
+    const uint32_t lt = live / 2;
+    const int64_t T0 = tile0 / 2;
+    const int tr = (t & 1) ? 1 : row;
+    if (a.auto_scale)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(delta), out_rsrc(it.scale + T0, lt * 4u),
+                                            (int)row0_offset(t >> 1, tr, 4), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)bk, out_rsrc(it.rice_k + T0, lt),
+                                         (int)row0_offset(t >> 1, tr, 1), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(4u + 64u + best, out_rsrc(it.tile_bits + T0, lt * 4u),
+                                          (int)row0_offset(t >> 1, tr, 4), 0, 0);
+  }
   if (status && (uint32_t)t < live) set_status(a.status, status);
 }
 
@@ -429,13 +481,27 @@ __device__ inline void enc_group(const EncodeLaunch& a, const EncItem& it, const
 // The loop body ends with reading the next group from LDS, after this
 // group's stores; the last iteration prefetches its own group again (an L2
 // hit) so that no branch surrounds the memory operations.
-template <bool RC>
+// Sign table of a 512-element tile: entry i holds the bf16-pair XOR mask
+// of elements 2 i, 2 i + 1 (rows of 32 entries: half h, row r at 4 h + r).
+__device__ inline void fill_sign_table512(uint32_t* tab, const uint32_t* signs) {
+  for (int i = threadIdx.x; i < 256; i += kBlock) {
+    const int e = 2 * i;
+    const uint32_t w0 = signs[e >> 5];
+    const uint32_t b0 = (w0 >> (e & 31)) & 1u, b1 = (w0 >> ((e + 1) & 31)) & 1u;
+    tab[i] = (b0 << 15) | (b1 << 31);
+  }
+}
+
+template <bool RC, int N = 256>
 __device__ __attribute__((always_inline)) inline void encode_body(const EncodeLaunch& a,
                                                                   const EncBatch& b) {
-  __shared__ uint32_t sign_tab[128];
+  __shared__ uint32_t sign_tab[N / 2];
   __shared__ uint4 stage[kBlock / 64][kEncStage];
   __shared__ uint4 ostage[kBlock / 64][256];
-  fill_sign_table(sign_tab, a.signs);
+  if constexpr (N == 512)
+    fill_sign_table512(sign_tab, a.signs);
+  else
+    fill_sign_table(sign_tab, a.signs);
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int t = lane & 15, row = lane >> 4;
@@ -458,7 +524,7 @@ __device__ __attribute__((always_inline)) inline void encode_body(const EncodeLa
     const int64_t gp = more ? gn : g;
     const int ip = more ? item_from(b, ic, gn) : ic;
     enc_prefetch(b.it[ip], gp - b.it[ip].group0, buf, lane, scale_in);
-    enc_group<RC>(a, b.it[ic], sign_tab, g - b.it[ic].group0, t, row, w, sc, ostage[wave]);
+    enc_group<RC, N>(a, b.it[ic], sign_tab, g - b.it[ic].group0, t, row, w, sc, ostage[wave]);
     __builtin_amdgcn_sched_barrier(0);
     enc_take(buf, t, row, w, sc);
     if (!more) break;
@@ -469,6 +535,11 @@ __device__ __attribute__((always_inline)) inline void encode_body(const EncodeLa
 
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void encode_e8_fast(EncodeLaunch a, EncBatch b) {
   encode_body<false>(a, b);
+}
+
+// Tiles of 512 (auto scale): items counted in halves of 256.
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void encode_e8_fast512(EncodeLaunch a, EncBatch b) {
+  encode_body<false, 512>(a, b);
 }
 
 // With the per-tile rate control a lane keeps its 64 rotated values through
@@ -872,8 +943,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
 }  // namespace
 
 bool e8_fast_encode_ok(const EncodeLaunch& a) {
-  return a.lattice == 8 && a.tile == 256 && a.in_bf16 && !a.dither && !a.wide &&
-         a.coords == nullptr;
+  return a.lattice == 8 && (a.tile == 256 || (a.tile == 512 && a.auto_scale && !a.rate_control)) &&
+         a.in_bf16 && !a.dither && !a.wide && a.coords == nullptr;
 }
 
 bool e8_fast_decode_ok(const DecodeLaunch& a) {
@@ -884,6 +955,22 @@ bool e8_fast_decode_ok(const DecodeLaunch& a) {
 using namespace fastlib;
 
 hipError_t launch_encode_e8_fast(const EncodeLaunch& a, const EncBatch& b, hipStream_t s) {
+  if (a.tile == 512) {
+    // the items' tiles of 512 as halves of 256, in groups of 16 halves
+    EncBatch h = b;
+    h.n_groups = 0;
+    for (int i = 0; i < b.n; ++i) {
+      h.it[i].n_tiles = 2 * b.it[i].n_tiles;
+      h.it[i].group0 = h.n_groups;
+      h.n_groups += (h.it[i].n_tiles + 15) / 16;
+    }
+    for (int i = b.n; i < kMaxItems; ++i) h.it[i] = h.it[0];
+    static int occ512 = 0;
+    const int64_t blocks =
+        persistent_grid(h.n_groups * 16, resident_blocks(encode_e8_fast512, occ512));
+    hipLaunchKernelGGL(encode_e8_fast512, dim3((unsigned)blocks), dim3(kBlock), 0, s, a, h);
+    return hipGetLastError();
+  }
   if (a.rate_control) {
     static int occ_rc = 0;
     const int64_t blocks =

@@ -2,8 +2,8 @@
 tile against the oracle, in the calls the benchmark times.
 
 * Sweep: one 4096 x 14336 bf16 N(0, 0.02^2) matrix through D4, A2, Z (tile
-  128) and E8 (tile 256) at 2, 3 and 4 bps (hq_encode_tiles, auto scale, RHT
-  seed 1; hq_decode_tiles to bf16).
+  128) and E8 (tiles 256 and 512) at 2, 3 and 4 bps (hq_encode_tiles, auto
+  scale, RHT seed 1; hq_decode_tiles to bf16).
 * KV: K and V [8 heads, 32768 positions, 128] bf16 with per-channel offsets,
   E8 at 4 bps with the subtractive dither (hq_kv_encode, RHT seed 1, dither
   seed 2, K numbered from 0 and V after it; hq_decode_tiles to bf16 with the
@@ -138,7 +138,8 @@ def _run_case(label, rec_base, bits, g, y, lattice, n, bps, seed, dither_seed=No
     assert tot["decode_bad"] == 0, label
 
 
-@pytest.mark.parametrize("lattice,n", [("D4", 128), ("A2", 128), ("Z", 128), ("E8", 256)])
+@pytest.mark.parametrize("lattice,n", [("D4", 128), ("A2", 128), ("Z", 128), ("E8", 256),
+                                       ("E8", 512)])
 def test_lattice_sweep_full_parity(lattice, n):
     bits = workloads.sweep_matrix()
     rows, cols = bits.shape
