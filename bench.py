@@ -499,7 +499,7 @@ def secondary(layer0, bps, dev):
     ms_e512, ms_d512 = time_calls(enc512, 5), time_calls(dec512, 5)
     variants = {
         "workload": "the same layer's seven matrices (bf16): per-tile rate control (fast E8 "
-                    "kernel), tile 512 (fast E8 encoder, generic decoder)",
+                    "kernel), tile 512 (fast E8 kernels)",
         "rate_control_encode_us": round(ms_rc * 1e3, 1),
         "rate_control_bits_per_weight": round(rc_bits, 4),
         "tile512_encode_us": round(ms_e512 * 1e3, 1), "tile512_decode_us": round(ms_d512 * 1e3, 1),

@@ -569,6 +569,7 @@ struct DecIn {
   float scale;
 };
 
+template <int N = 256>
 __device__ inline void dec_prefetch(const DecItem& it, int64_t group, uint4* buf, int lane) {
   const int r = lane >> 4, b = lane & 15;
   const uint32_t live = live_tiles(it.n_tiles, group);
@@ -582,9 +583,16 @@ __device__ inline void dec_prefetch(const DecItem& it, int64_t group, uint4* buf
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
       out_rsrc(const_cast<uint32_t*>(it.coset) + group * 16, live * 4u), lds_ptr(buf + 256), 4,
       b * 4, 0, 0, 0);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      out_rsrc(const_cast<float*>(it.scale) + group * 16, live * 4u), lds_ptr(buf + 272), 4,
-      b * 4, 0, 0, 0);
+  if constexpr (N == 512) {
+    // one scale per 512-tile (two halves): slot b holds the scale of tile b / 2
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        out_rsrc(const_cast<float*>(it.scale) + group * 8, live * 2u), lds_ptr(buf + 272), 4,
+        (b >> 1) * 4, 0, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        out_rsrc(const_cast<float*>(it.scale) + group * 16, live * 4u), lds_ptr(buf + 272), 4,
+        b * 4, 0, 0, 0);
+  }
 }
 
 __device__ inline void dec_take(const uint4* buf, int t, int r, uint32_t* d, DecIn& in) {
@@ -598,9 +606,15 @@ __device__ inline void dec_take(const uint4* buf, int t, int r, uint32_t* d, Dec
   in.scale = reinterpret_cast<const float*>(buf + 272)[t];
 }
 
-template <bool OUT_BF16>
+// N = 512: the group's 16 tiles are the two halves of 8 tiles of 512 (half
+// h of tile T on lanes t = 2T + h), each half unstripped and transformed
+// as a tile of 256; element bit 8 is then one butterfly with the value of
+// the neighbouring lane (inv = fp64 1/sqrt(512)).
+template <bool OUT_BF16, int N = 256>
 __device__ inline void dec_group(const DecItem& it, const uint32_t* sign_tab, int64_t group, int t,
-                                 int row, const uint32_t* d, const DecIn& in, uint4* ost) {
+                                 int row, const uint32_t* d, const DecIn& in, uint4* ost,
+                                 double inv = 0.0) {
+  static_assert(N == 256 || N == 512, "tile of 256 or 512");
   const uint32_t cw = in.cw >> (8 * row);        // this lane's 8 blocks
   const float dsc = in.scale * 0.03125f;         // Delta / 32, exact
 
@@ -611,7 +625,9 @@ __device__ inline void dec_group(const DecItem& it, const uint32_t* sign_tab, in
 #pragma unroll
   for (int q = 0; q < 16; ++q) sad = __builtin_amdgcn_sad_u8(d[q], 0x80808080u, sad);
   sad = tile_sum_u32(sad);
-  const bool small = sad >= 32768u - 8111u;
+  // N = 512: 64 blocks, sum |P| <= 4 sum |stored| + 640; 65536 - sum |z| over 512 bytes
+  if constexpr (N == 512) sad += pair_u32(sad);
+  const bool small = N == 256 ? sad >= 32768u - 8111u : sad >= 65536u - 8031u;
 
   // ---- unstrip into P = 2z + c as int16 pairs: P2[m] = (P_2m, P_2m+1)
   uint32_t P2[32];
@@ -672,6 +688,13 @@ __device__ inline void dec_group(const DecItem& it, const uint32_t* sign_tab, in
         P2[m + 8] = as_u32(x - z);
       }
     }
+    if constexpr (N == 512) {
+      // element bit 8: half 0 keeps a + b, half 1 keeps a - b (its own value
+      // negated plus its neighbour's); both within int16 by the bound above
+      const uint32_t sg = (t & 1) ? 0xFFFFFFFFu : 0x00010001u;
+#pragma unroll
+      for (int m = 0; m < 32; ++m) P2[m] = pk_mad_u16(P2[m], sg, pair_u32(P2[m]));
+    }
 #pragma unroll
     for (int m = 0; m < 32; ++m) {
       y[2 * m] = (float)(short)(P2[m] & 0xFFFFu);
@@ -712,6 +735,13 @@ __device__ inline void dec_group(const DecItem& it, const uint32_t* sign_tab, in
         y[i + 16] = x - z;
       }
     }
+    if constexpr (N == 512) {
+      // exact: |sums| <= 512 (4 * 128 + 3) < 2^24
+      const float sgf = (t & 1) ? -1.0f : 1.0f;
+#pragma unroll
+      for (int i = 0; i < 64; ++i)
+        y[i] = __builtin_fmaf(y[i], sgf, __uint_as_float(pair_u32(__float_as_uint(y[i]))));
+    }
   }
   // Register i now holds element bits (i0 .. i3, i4 = b7, i5 = b6); rows (b5, b4),
   // as the exact integer (H P)_e.
@@ -722,8 +752,38 @@ __device__ inline void dec_group(const DecItem& it, const uint32_t* sign_tab, in
   // rounding to bf16 follows; a wave with any other scale (fp32 caller
   // scales, outputs that could be subnormal) rounds from the exact fp64
   // product as the generic decoder does.
+  //
+  // N = 512: x = fl64(((H P)_e (Delta / 2)) inv), the first product exact
+  // (an fp32 scale times at most 18 bits), the rounding of the fp64 value
+  // itself.  bf16 output: rounding that fp32 value to bf16 rounds x itself
+  // unless the fp32 value sits exactly on a bf16 midpoint (low 16 bits
+  // 0x8000): a nearer fp32 value cannot lie past a midpoint that fp32
+  // represents.  A wave with such a value, or a scale outside 2^-100 ..
+  // 2^100 (outputs that could leave fp32's normal range), rounds from fp64.
+  const uint32_t* stab = sign_tab + (N == 512 ? 128 * (t & 1) : 0);
+  const double dh = (double)in.scale * 0.5;
   if constexpr (OUT_BF16) {
     uint32_t o[32];
+    if constexpr (N == 512) {
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      uint32_t key = 0xFFFFFFFFu;
+#pragma unroll
+      for (int m = 0; m < 32; ++m) {
+        const float f0 = (float)(((double)y[2 * m] * dh) * inv);
+        const float f1 = (float)(((double)y[2 * m + 1] * dh) * inv);
+        key = min(key, min((__float_as_uint(f0) << 16) + 0x80000000u,
+                           (__float_as_uint(f1) << 16) + 0x80000000u));
+        const bf16x2 pr = {(__bf16)f0, (__bf16)f1};
+        o[m] = __builtin_bit_cast(uint32_t, pr);
+      }
+      const bool fast = key != 0u && in.scale >= 0x1p-100f && in.scale <= 0x1p100f;
+      if (__builtin_amdgcn_ballot_w64(!fast) != 0) {
+#pragma unroll
+        for (int m = 0; m < 32; ++m)
+          o[m] = f64_to_bf16(((double)y[2 * m] * dh) * inv) |
+                 (f64_to_bf16(((double)y[2 * m + 1] * dh) * inv) << 16);
+      }
+    } else {
     const bool exact32 = (__float_as_uint(in.scale) & 0xFFFFu) == 0u && in.scale >= 0x1p-100f &&
                          in.scale <= 0x1p100f;
     if (__builtin_amdgcn_ballot_w64(!exact32) == 0) {
@@ -739,6 +799,7 @@ __device__ inline void dec_group(const DecItem& it, const uint32_t* sign_tab, in
       for (int m = 0; m < 32; ++m)
         o[m] = f64_to_bf16((double)y[2 * m] * dd) | (f64_to_bf16((double)y[2 * m + 1] * dd) << 16);
     }
+    }
     // Chunk k = o[4k .. 4k + 3] holds element bits 0-2 inside; bit 3 = k
     // bit 0, bit 7 = k bit 1, bit 6 = k bit 2, bit 5 = row bit 0, bit 4 = row
     // bit 1: 16-byte slot k0 + 16 k1 + 8 k2 + 4 r0 + 2 r1 of the tile.  The
@@ -749,7 +810,7 @@ __device__ inline void dec_group(const DecItem& it, const uint32_t* sign_tab, in
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int sl = (k & 1) + 16 * ((k >> 1) & 1) + 8 * (k >> 2) + rs0;
-      const uint4 sm = reinterpret_cast<const uint4*>(sign_tab)[sl];
+      const uint4 sm = reinterpret_cast<const uint4*>(stab)[sl];
       ch[k] = make_uint4(o[4 * k] ^ sm.x, o[4 * k + 1] ^ sm.y, o[4 * k + 2] ^ sm.z,
                          o[4 * k + 3] ^ sm.w);
     }
@@ -765,7 +826,9 @@ __device__ inline void dec_group(const DecItem& it, const uint32_t* sign_tab, in
   } else {
     uint32_t o[64];
 #pragma unroll
-    for (int i = 0; i < 64; ++i) o[i] = __float_as_uint(y[i] * dsc);
+    for (int i = 0; i < 64; ++i)
+      o[i] = N == 512 ? __float_as_uint((float)(((double)y[i] * dh) * inv))
+                      : __float_as_uint(y[i] * dsc);
 #pragma unroll
     for (int i = 0; i < 64; ++i)
       if (!(i & 16)) swap32(o[i], o[i + 16]);
@@ -774,7 +837,7 @@ __device__ inline void dec_group(const DecItem& it, const uint32_t* sign_tab, in
     uint4 ch[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      const uint32_t sm = sign_tab[row * 32 + 2 * k], sn = sign_tab[row * 32 + 2 * k + 1];
+      const uint32_t sm = stab[row * 32 + 2 * k], sn = stab[row * 32 + 2 * k + 1];
       ch[k] = make_uint4(o[4 * k] ^ (sm << 16), o[4 * k + 1] ^ (sm & 0x80000000u),
                          o[4 * k + 2] ^ (sn << 16), o[4 * k + 3] ^ (sn & 0x80000000u));
     }
@@ -793,12 +856,15 @@ __device__ inline void dec_group(const DecItem& it, const uint32_t* sign_tab, in
 // prefetch never includes those stores; the last iteration prefetches its
 // own group again (an L2 hit) to keep the loop free of branches around
 // memory operations.
-template <bool OUT_BF16>
+template <bool OUT_BF16, int N = 256>
 __global__ __launch_bounds__(kBlock) void decode_e8_fast(DecodeLaunch a, DecBatch b) {
-  __shared__ uint32_t sign_tab[128];
+  __shared__ uint32_t sign_tab[N / 2];
   __shared__ uint4 stage[kBlock / 64][kDecStage];
   __shared__ uint4 ostage[kBlock / 64][256];
-  fill_sign_table(sign_tab, a.signs);
+  if constexpr (N == 512)
+    fill_sign_table512(sign_tab, a.signs);
+  else
+    fill_sign_table(sign_tab, a.signs);
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int t = lane & 15, row = lane >> 4;
@@ -810,7 +876,7 @@ __global__ __launch_bounds__(kBlock) void decode_e8_fast(DecodeLaunch a, DecBatc
   int ic = item_of(b, g);
   uint32_t d[16];
   DecIn in;
-  dec_prefetch(b.it[ic], g - b.it[ic].group0, buf, lane);
+  dec_prefetch<N>(b.it[ic], g - b.it[ic].group0, buf, lane);
   dec_take(buf, t, row, d, in);
   for (;;) {
     // every lane's reads of the buffer complete before it is refilled
@@ -819,8 +885,9 @@ __global__ __launch_bounds__(kBlock) void decode_e8_fast(DecodeLaunch a, DecBatc
     const bool more = gn < b.n_groups;   // uniform across the wave
     const int64_t gp = more ? gn : g;
     const int ip = more ? item_from(b, ic, gn) : ic;
-    dec_prefetch(b.it[ip], gp - b.it[ip].group0, buf, lane);
-    dec_group<OUT_BF16>(b.it[ic], sign_tab, g - b.it[ic].group0, t, row, d, in, ostage[wave]);
+    dec_prefetch<N>(b.it[ip], gp - b.it[ip].group0, buf, lane);
+    dec_group<OUT_BF16, N>(b.it[ic], sign_tab, g - b.it[ic].group0, t, row, d, in, ostage[wave],
+                           a.inv_sqrt_n);
     __builtin_amdgcn_sched_barrier(0);
     dec_take(buf, t, row, d, in);
     if (!more) break;
@@ -948,7 +1015,7 @@ bool e8_fast_encode_ok(const EncodeLaunch& a) {
 }
 
 bool e8_fast_decode_ok(const DecodeLaunch& a) {
-  return a.lattice == 8 && a.tile == 256 && !a.dither && !a.wide;
+  return a.lattice == 8 && (a.tile == 256 || a.tile == 512) && !a.dither && !a.wide;
 }
 
 
@@ -999,6 +1066,30 @@ hipError_t launch_codec_e8_fast(const EncodeLaunch& a, const EncBatch& b, const 
 }
 
 hipError_t launch_decode_e8_fast(const DecodeLaunch& a, const DecBatch& b, hipStream_t s) {
+  if (a.tile == 512) {
+    // the items' tiles of 512 as halves of 256, in groups of 16 halves
+    DecBatch h = b;
+    h.n_groups = 0;
+    for (int i = 0; i < b.n; ++i) {
+      h.it[i].n_tiles = 2 * b.it[i].n_tiles;
+      h.it[i].group0 = h.n_groups;
+      h.n_groups += (h.it[i].n_tiles + 15) / 16;
+    }
+    for (int i = b.n; i < kMaxItems; ++i) h.it[i] = h.it[0];
+    static int occ512_bf16 = 0, occ512_f32 = 0;
+    if (a.out_bf16) {
+      const int64_t blocks = persistent_grid(
+          h.n_groups * 16, resident_blocks(decode_e8_fast<true, 512>, occ512_bf16));
+      hipLaunchKernelGGL((decode_e8_fast<true, 512>), dim3((unsigned)blocks), dim3(kBlock), 0, s,
+                         a, h);
+    } else {
+      const int64_t blocks = persistent_grid(
+          h.n_groups * 16, resident_blocks(decode_e8_fast<false, 512>, occ512_f32));
+      hipLaunchKernelGGL((decode_e8_fast<false, 512>), dim3((unsigned)blocks), dim3(kBlock), 0,
+                         s, a, h);
+    }
+    return hipGetLastError();
+  }
   static int occ_bf16 = 0, occ_f32 = 0;
   if (a.out_bf16) {
     const int64_t blocks = persistent_grid(b.n_groups * 16, resident_blocks(decode_e8_fast<true>, occ_bf16));

@@ -1426,9 +1426,9 @@ def test_fast_grid_clamp(lattice, n):
 
 
 @pytest.mark.parametrize("lattice,n", [("E8", 128), ("D4", 128), ("A2", 128), ("Z", 128),
-                                       ("E8", 256)])
+                                       ("E8", 256), ("E8", 512)])
 def test_fast_decode_scale_range(lattice, n):
-    """Fast-kernel decode (tile 128, E8 / tile 256) of oracle indices under
+    """Fast-kernel decode (tile 128, E8 / tiles 256 and 512) of oracle indices under
     caller scales: bf16-valued scales within 2^-80 .. 2^80, fp32 scales with
     24 significant bits (the product with the Hadamard sums needs more than
     fp32 holds), and bf16 scales from 2^-112 to 2^104 whose outputs leave the
@@ -1453,3 +1453,12 @@ def test_fast_decode_scale_range(lattice, n):
     ora["scale"] = sc
     say("case: %s/%d decode, bf16, fp32 and extreme scales" % (lattice, n))
     check_decode(ora, lattice, n, 6, "%s/%d scale range" % (lattice, n), exact=(lattice != "A2"))
+    if lattice == "E8" and n >= 256:
+        # every other tile with indices up to +-100, whose sum |P| leaves
+        # int16 (the fast decoders' fp32 Hadamard), beside ordinary tiles
+        big = dict(ora)
+        big["idx"] = np.array(ora["idx"], np.int64).reshape(T, n)
+        big["idx"][::2] = rng.integers(-100, 101, size=((T + 1) // 2, n))
+        big["scale"] = codec.bf16_rne(2.0 ** rng.uniform(-20, 20, T))
+        say("case: %s/%d decode, large indices" % (lattice, n))
+        check_decode(big, lattice, n, 6, "%s/%d large indices" % (lattice, n))
