@@ -37,13 +37,13 @@ DEC_BYTES_PER_TILE = 256 + 4 + 4 + 512
 # sources with this sha256 and are reported only while the sources match.
 KERNEL_SOURCES = ("hq_e8fast.hip", "hq_lanes.h", "hq_device.h", "hq_internal.h")
 MEASURED_TRAFFIC = {
-    "sources_sha256": "db020264cb3f13922b2bd14d0e9aa1948035074a23c0c0c086504aff699beaa4",
-    "encode": {"bytes_per_byte": 1.0041, "valu_lane_ops_per_byte": 9.62225,
-               "valu_lane_ops_per_weight": 29.36},
-    "decode": {"bytes_per_byte": 1.0011, "valu_lane_ops_per_byte": 3.41564,
+    "sources_sha256": "ce14ce5e9bc3682ab36c2e28fd21f04b3100517ac96009e84fb1cb67f95b37ea",
+    "encode": {"bytes_per_byte": 1.0041, "valu_lane_ops_per_byte": 9.65298,
+               "valu_lane_ops_per_weight": 29.45},
+    "decode": {"bytes_per_byte": 1.0009, "valu_lane_ops_per_byte": 3.41564,
                "valu_lane_ops_per_weight": 10.35},
-    "codec": {"bytes_per_byte": 1.003, "valu_lane_ops_per_byte": 6.99343,
-              "valu_lane_ops_per_weight": 21.27},
+    "codec": {"bytes_per_byte": 1.0032, "valu_lane_ops_per_byte": 7.00113,
+              "valu_lane_ops_per_weight": 21.29},
 }
 # VALU issue roof: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (a wave64 instruction
 # occupies a SIMD for 4 cycles; fp64 add / mul / fma issue at the same rate)
