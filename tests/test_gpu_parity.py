@@ -604,13 +604,15 @@ def test_bitwise_determinism():
     assert torch.equal(ya.view(torch.int16), yb.view(torch.int16))
 
 
-def test_batched_calls_match_single_calls_and_oracle():
+@pytest.mark.parametrize("n", [256, 512])
+def test_batched_calls_match_single_calls_and_oracle(n):
     """hq_encode_batch / hq_decode_batch over mixed matrix sizes (more than
     eight, one empty, ragged tile counts) give the same bytes as one call per
-    matrix, and sampled tiles match the oracle."""
+    matrix, and sampled tiles match the oracle (E8, tiles of 256 and 512)."""
     rng = np.random.default_rng(31)
-    shapes = [(7, 256), (1, 512), (0, 256), (33, 768), (16, 256), (5, 1024), (40, 256),
-              (3, 256), (9, 512), (2, 2048), (64, 256)]
+    shapes = [(r, c * n // 256) for r, c in
+              [(7, 256), (1, 512), (0, 256), (33, 768), (16, 256), (5, 1024), (40, 256),
+               (3, 256), (9, 512), (2, 2048), (64, 256)]]
     mats, hosts = [], []
     for r, c in shapes:
         w = rng.standard_normal((r, c)) * 0.02
@@ -619,24 +621,24 @@ def test_batched_calls_match_single_calls_and_oracle():
         mats.append(T.bf16_device(bits, (r, c)))
     say("case: batch of %d matrices" % len(mats))
     for bps in (3.0, 4.0):
-        batch = hq.hq_encode_batch(mats, "E8", 256, bps, 9)
-        ys = hq.hq_decode_batch(batch, "E8", 256, 9, torch.bfloat16)
+        batch = hq.hq_encode_batch(mats, "E8", n, bps, 9)
+        ys = hq.hq_decode_batch(batch, "E8", n, 9, torch.bfloat16)
         torch.cuda.synchronize()
         for i, (x, b, y) in enumerate(zip(mats, batch, ys)):
             if x.numel() == 0:
                 continue
-            s = hq.hq_encode_tiles(x, "E8", 256, bps, 9)
-            ys1 = hq.hq_decode_tiles(s["idx"], s["coset"], s["scale"], "E8", 256, 9)
+            s = hq.hq_encode_tiles(x, "E8", n, bps, 9)
+            ys1 = hq.hq_decode_tiles(s["idx"], s["coset"], s["scale"], "E8", n, 9)
             torch.cuda.synchronize()
             for k in ("scale", "idx", "coset", "rice_k", "tile_bits"):
                 assert torch.equal(b[k], s[k]), (i, k)
             assert torch.equal(y.view(torch.int16), ys1.view(torch.int16)), i
-            ora = codec.encode(hosts[i], "E8", 256, bps, rht_seed=9)
+            ora = codec.encode(hosts[i], "E8", n, bps, rht_seed=9)
             assert np.array_equal(T.host(b["scale"]).astype(np.float64), ora["scale"])
-            T.compare_indices(T.host(b["idx"]).reshape(-1, 256), T.u32(b["coset"]), ora, "E8",
-                              256, "batch item %d" % i)
-            yo = codec.bf16_rne(codec.decode(ora["idx"], ora["coset"], ora["scale"], "E8", 256, 9))
-            assert np.array_equal(T.bf16_host_bits(y).reshape(-1, 256), codec.bf16_bits(yo)), i
+            T.compare_indices(T.host(b["idx"]).reshape(-1, n), T.u32(b["coset"]), ora, "E8",
+                              n, "batch item %d" % i)
+            yo = codec.bf16_rne(codec.decode(ora["idx"], ora["coset"], ora["scale"], "E8", n, 9))
+            assert np.array_equal(T.bf16_host_bits(y).reshape(-1, n), codec.bf16_bits(yo)), i
 
 
 def _pipeline_batches(rng, shapes, seed_bits):
