@@ -571,6 +571,25 @@ def test_edge_cases_and_status_bits():
     hq.hq_encode_tiles(x, "E8", 256, 4.0, 0, status=st)
     torch.cuda.synchronize()
     assert int(st.item()) & hq.HQ_ST_NONFINITE
+    # tile 512 (two halves of 256 on neighbouring lanes): zero tiles, and a
+    # non-finite element in either half flags the call and leaves the
+    # finite tiles beside it as they were
+    x = torch.zeros((3, 512), dtype=torch.bfloat16, device=dev)
+    g = hq.hq_encode_tiles(x, "E8", 512, 4.0, 0)
+    torch.cuda.synchronize()
+    assert np.all(T.host(g["scale"]) == 1.0) and not T.host(g["idx"]).any()
+    for col in (17, 300):
+        st.zero_()
+        x = torch.randn((3, 512), device=dev).to(torch.bfloat16)
+        ref = hq.hq_encode_tiles(x, "E8", 512, 4.0, 0)
+        x[1, col] = float("nan")
+        g = hq.hq_encode_tiles(x, "E8", 512, 4.0, 0, status=st)
+        torch.cuda.synchronize()
+        assert int(st.item()) & hq.HQ_ST_NONFINITE, col
+        for k in ("scale", "rice_k", "tile_bits"):
+            assert torch.equal(g[k][[0, 2]], ref[k][[0, 2]]), (col, k)
+        assert torch.equal(g["idx"].reshape(3, 512)[[0, 2]], ref["idx"].reshape(3, 512)[[0, 2]])
+    st.zero_()
     # an explicit scale far too small overflows the int8 indices
     st.zero_()
     x = torch.randn((1, 256), device=dev).to(torch.bfloat16)
