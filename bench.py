@@ -37,12 +37,12 @@ DEC_BYTES_PER_TILE = 256 + 4 + 4 + 512
 # sources with this sha256 and are reported only while the sources match.
 KERNEL_SOURCES = ("hq_e8fast.hip", "hq_lanes.h", "hq_device.h", "hq_internal.h")
 MEASURED_TRAFFIC = {
-    "sources_sha256": "ce14ce5e9bc3682ab36c2e28fd21f04b3100517ac96009e84fb1cb67f95b37ea",
+    "sources_sha256": "517c6c08f6cdc18e20a475e02dcbfc54f65c7b52939048fedc67442e97b80a4e",
     "encode": {"bytes_per_byte": 1.0041, "valu_lane_ops_per_byte": 9.65298,
                "valu_lane_ops_per_weight": 29.45},
-    "decode": {"bytes_per_byte": 1.0009, "valu_lane_ops_per_byte": 3.41564,
+    "decode": {"bytes_per_byte": 1.0011, "valu_lane_ops_per_byte": 3.41564,
                "valu_lane_ops_per_weight": 10.35},
-    "codec": {"bytes_per_byte": 1.0032, "valu_lane_ops_per_byte": 7.00113,
+    "codec": {"bytes_per_byte": 1.0037, "valu_lane_ops_per_byte": 7.00113,
               "valu_lane_ops_per_weight": 21.29},
 }
 # VALU issue roof: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (a wave64 instruction

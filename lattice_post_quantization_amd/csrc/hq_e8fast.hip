@@ -986,10 +986,16 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         enc_prefetch(b.it[ip], nx.slot - b.it[ip].group0, buf, ln, scale_in);
       else
         dec_prefetch(bd.it[ip], nx.slot - bd.it[ip].group0, buf, ln);
-      if (cur.kind == 0)
+      // An encode group runs at a raised wave priority: when both waves of
+      // a SIMD are ready, the VALU-bound encode issues first and the
+      // decode's memory-bound work fills the gaps (measured: the fused
+      // launch about 5% shorter than with equal priorities).
+      if (cur.kind == 0) {
+        __builtin_amdgcn_s_setprio(1);
         enc_group<false>(a, b.it[ic], sign_enc, cur.slot - b.it[ic].group0, tt, rr, w, sc,
                          ostage[wave]);
-      else
+        __builtin_amdgcn_s_setprio(0);
+      } else
         dec_group<OUT_BF16>(bd.it[ic], sign_dec, cur.slot - bd.it[ic].group0, tt, rr, w, din,
                             ostage[wave]);
     }
